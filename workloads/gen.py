@@ -1,0 +1,411 @@
+"""Seeded synthetic inputs for the paged-attention read path.
+
+This module only *builds inputs*: page pools, block tables, context lengths,
+query tensors and the garbage planted in slots that must never be read.  It
+holds none of the attention arithmetic, and it is the one module that both the
+CPU oracle tests and the GPU path consume.
+
+Layouts follow the paged_attention contract of tiny-llm "Week 3 Day 4: Direct
+Paged Attention" (section "The Paged Attention API", and "How This Maps to
+tiny-llm" for the contiguous pool):
+
+  query        [B, H_q, L, D]
+  key_pages    [num_pages, H_kv, page_size, D]   (value_pages: same shape)
+  block_table  [B, max_pages]  int32, unused entries padded with -1
+  context_lens [B]             int32, visible tokens including the L new rows
+  query_lens   [B] or None     int32, valid query rows per request (<= L)
+
+Floating-point data is stored as float32 arrays for dtype "f32" and as uint16
+bfloat16 bit patterns (round-to-nearest-even from a float32 draw) for "bf16".
+
+Draw order is fixed per workload and stated in each builder; every draw comes
+from one ``numpy.random.default_rng(seed)`` stream, so equal seeds give equal
+bytes on every machine.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence, Union
+
+import numpy as np
+
+GARBAGE_DEFAULT = 1.0e4
+
+# Standard seeds, one per named workload.
+SEEDS = {"C1": 1, "C2": 2, "C3": 3, "C4": 4, "C5": 5}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32 (for test helpers)."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclass
+class PagedInputs:
+    """One call's worth of paged-attention inputs (host arrays)."""
+
+    name: str
+    seed: int
+    dtype: str                      # "f32" or "bf16"
+    B: int
+    H_q: int
+    H_kv: int
+    L: int
+    D: int
+    page_size: int
+    num_pages: int
+    max_pages: int
+    scale: float
+    causal: bool
+    query: np.ndarray               # [B, H_q, L, D] float32 or uint16 (bf16 bits)
+    key_pages: np.ndarray           # [num_pages, H_kv, page_size, D]
+    value_pages: np.ndarray         # same shape
+    block_table: np.ndarray         # [B, max_pages] int32
+    context_lens: np.ndarray        # [B] int32
+    query_lens: Optional[np.ndarray] = None   # [B] int32 or None
+    meta: Dict[str, object] = field(default_factory=dict)
+
+    @property
+    def group(self) -> int:
+        return self.H_q // self.H_kv
+
+    def rows_valid(self) -> np.ndarray:
+        """Valid query rows per request (L where query_lens is absent)."""
+        if self.query_lens is None:
+            return np.full(self.B, self.L, dtype=np.int64)
+        return self.query_lens.astype(np.int64)
+
+    def kv_token_bytes(self) -> int:
+        """Bytes of one token's K plus V across all kv heads."""
+        return self.H_kv * self.D * 2 * (4 if self.dtype == "f32" else 2)
+
+
+@dataclass
+class MixedInputs:
+    """A ragged batch served as one decode call plus one prefill call that
+    read the same page pool (the two share key_pages/value_pages arrays)."""
+
+    name: str
+    seed: int
+    decode: PagedInputs
+    prefill: PagedInputs
+    meta: Dict[str, object] = field(default_factory=dict)
+
+
+# ----------------------------------------------------------------------------
+# helpers
+# ----------------------------------------------------------------------------
+
+def _draw_values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    return f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def _garbage_value(dtype: str, garbage: float) -> Union[np.float32, np.uint16]:
+    g = np.array([garbage], dtype=np.float32)
+    return f32_to_bf16_bits(g)[0] if dtype == "bf16" else g[0]
+
+
+def _fill_pool(rng, dtype, num_pages, H_kv, ps, D, page_order: Sequence[int],
+               valid_slots: Sequence[int], garbage) -> np.ndarray:
+    """Pool whose pages in ``page_order`` get N(0,1) values in their first
+    ``valid_slots[i]`` slots; every other slot and page holds ``garbage``.
+
+    ``garbage`` is a float, or the string "random" (fresh N(0,1)*1e3 draws) or
+    "nan".  Values are drawn page by page in ``page_order``.
+    """
+    np_dtype = np.uint16 if dtype == "bf16" else np.float32
+    pool = np.empty((num_pages, H_kv, ps, D), dtype=np_dtype)
+    if isinstance(garbage, str) and garbage == "random":
+        fill = None
+    elif isinstance(garbage, str) and garbage == "nan":
+        fill = _garbage_value(dtype, float("nan"))
+    else:
+        fill = _garbage_value(dtype, float(garbage))
+    if fill is not None:
+        pool[...] = fill
+    else:
+        # stale data of arbitrary magnitude from a child stream, so the live
+        # values are the same bytes as with a constant garbage fill
+        grng = rng.spawn(1)[0]
+        chunk = max(1, (1 << 22) // (H_kv * ps * D))
+        for s in range(0, num_pages, chunk):
+            e = min(num_pages, s + chunk)
+            g = grng.standard_normal(size=(e - s, H_kv, ps, D), dtype=np.float32) * np.float32(1e3)
+            pool[s:e] = f32_to_bf16_bits(g) if dtype == "bf16" else g
+    order = np.asarray(page_order, dtype=np.int64)
+    vs = np.asarray(valid_slots, dtype=np.int64)
+    slot_idx = np.arange(ps)
+    chunk = max(1, (1 << 22) // (H_kv * ps * D))      # ~4M elements per draw
+    for s in range(0, len(order), chunk):
+        e = min(len(order), s + chunk)
+        vals = _draw_values(rng, (e - s, H_kv, ps, D), dtype)
+        dead = slot_idx[None, :] >= vs[s:e, None]          # [pages, ps] unused slots
+        if dead.any():
+            pg, sl = np.nonzero(dead)
+            if fill is not None:
+                vals[pg, :, sl, :] = fill
+            else:
+                vals[pg, :, sl, :] = pool[order[s:e][pg], :, sl, :]
+        pool[order[s:e]] = vals
+    return pool
+
+
+def _pages_needed(ctx: int, ps: int) -> int:
+    return (ctx + ps - 1) // ps
+
+
+def _tables_from_ids(ctx: Sequence[int], ps: int, max_pages: int,
+                     page_ids: Sequence[Sequence[int]]) -> np.ndarray:
+    bt = np.full((len(ctx), max_pages), -1, dtype=np.int32)
+    for b, ids in enumerate(page_ids):
+        bt[b, :len(ids)] = ids
+    return bt
+
+
+def _valid_slots_per_page(ctx: int, ps: int) -> List[int]:
+    n = _pages_needed(ctx, ps)
+    return [min(ps, ctx - i * ps) for i in range(n)]
+
+
+def _queries(rng, dtype, B, H_q, L, D, query_lens, garbage):
+    q = _draw_values(rng, (B, H_q, L, D), dtype)
+    if query_lens is not None:
+        fill = _garbage_value(dtype, GARBAGE_DEFAULT if isinstance(garbage, str) else float(garbage))
+        for b in range(B):
+            q[b, :, int(query_lens[b]):, :] = fill
+    return q
+
+
+# ----------------------------------------------------------------------------
+# generic builder (tests)
+# ----------------------------------------------------------------------------
+
+def make_random(seed: int, *, B: int, H_q: int, H_kv: int, L: int, D: int,
+                page_size: int, ctx: Union[Sequence[int], tuple], dtype: str = "bf16",
+                causal: bool = True, query_lens: Optional[Sequence[int]] = None,
+                extra_free_pages: int = 3, max_pages: Optional[int] = None,
+                garbage=GARBAGE_DEFAULT, scale: Optional[float] = None,
+                name: str = "random") -> PagedInputs:
+    """Random paged inputs.
+
+    Draw order: context lengths (when ``ctx`` is a (lo, hi) range) ->
+    physical-id permutation -> (random garbage) -> K -> V -> Q.
+    Physical ids are a seeded permutation of the whole pool, so logical pages
+    land at arbitrary physical pages; ``extra_free_pages`` pages stay free and
+    hold garbage, as do unused tail slots of each request's last page.
+    """
+    rng = np.random.default_rng(seed)
+    if isinstance(ctx, tuple):
+        lo, hi = ctx
+        ctx_l = [int(v) for v in rng.integers(lo, hi + 1, size=B)]
+    else:
+        ctx_l = [int(v) for v in ctx]
+        assert len(ctx_l) == B
+    if query_lens is not None:
+        query_lens = np.asarray(query_lens, dtype=np.int32)
+    npg = [_pages_needed(c, page_size) for c in ctx_l]
+    if max_pages is None:
+        max_pages = max(1, max(npg) if npg else 1)
+    live = sum(npg)
+    num_pages = max(1, live + extra_free_pages)
+    perm = rng.permutation(num_pages)
+    ids, cur = [], 0
+    for n in npg:
+        ids.append([int(p) for p in perm[cur:cur + n]])
+        cur += n
+    order = [p for row in ids for p in row]
+    slots = [s for c in ctx_l for s in _valid_slots_per_page(c, page_size)]
+    kp = _fill_pool(rng, dtype, num_pages, H_kv, page_size, D, order, slots, garbage)
+    vp = _fill_pool(rng, dtype, num_pages, H_kv, page_size, D, order, slots, garbage)
+    q = _queries(rng, dtype, B, H_q, L, D, query_lens, garbage)
+    bt = _tables_from_ids(ctx_l, page_size, max_pages, ids)
+    return PagedInputs(
+        name=name, seed=seed, dtype=dtype, B=B, H_q=H_q, H_kv=H_kv, L=L, D=D,
+        page_size=page_size, num_pages=num_pages, max_pages=max_pages,
+        scale=float(scale if scale is not None else 1.0 / math.sqrt(D)), causal=causal,
+        query=q, key_pages=kp, value_pages=vp, block_table=bt,
+        context_lens=np.asarray(ctx_l, dtype=np.int32), query_lens=query_lens,
+        meta={"live_pages": live, "garbage": garbage})
+
+
+# ----------------------------------------------------------------------------
+# the five named workloads
+# ----------------------------------------------------------------------------
+
+def make_c1(seed: int = SEEDS["C1"]) -> PagedInputs:
+    """Tiny fp32 decode: B=2, H_q=H_kv=4, D=64, L=1, page_size=4,
+    context_lens [10, 7], a pool of 16 pages.  Request 0 uses pages [12, 5, 3]
+    (the worked address example of "Why block_table Matters"); request 1 takes
+    two pages from a seeded permutation of the other 13.  Draw order:
+    permutation -> K -> V -> Q."""
+    rng = np.random.default_rng(seed)
+    B, H, D, L, ps, P = 2, 4, 64, 1, 4, 16
+    ctx = [10, 7]
+    others = [p for p in range(P) if p not in (12, 5, 3)]
+    perm = rng.permutation(len(others))
+    ids = [[12, 5, 3], [others[perm[0]], others[perm[1]]]]
+    order = [p for row in ids for p in row]
+    slots = [s for c in ctx for s in _valid_slots_per_page(c, ps)]
+    kp = _fill_pool(rng, "f32", P, H, ps, D, order, slots, GARBAGE_DEFAULT)
+    vp = _fill_pool(rng, "f32", P, H, ps, D, order, slots, GARBAGE_DEFAULT)
+    q = _queries(rng, "f32", B, H, L, D, None, GARBAGE_DEFAULT)
+    bt = _tables_from_ids(ctx, ps, 3, ids)
+    return PagedInputs(
+        name="C1", seed=seed, dtype="f32", B=B, H_q=H, H_kv=H, L=L, D=D,
+        page_size=ps, num_pages=P, max_pages=3, scale=1.0 / math.sqrt(D), causal=True,
+        query=q, key_pages=kp, value_pages=vp, block_table=bt,
+        context_lens=np.asarray(ctx, dtype=np.int32),
+        meta={"workload": "tiny fp32 decode", "live_pages": 5})
+
+
+def _uniform_pool_config(name, seed, *, B, H_q, H_kv, D, L, ps, ctx_lo, ctx_hi,
+                         pool_pages=None, free_frac=None, prefix_lo=None,
+                         prefix_hi=None, causal=True) -> PagedInputs:
+    """Shared builder for C2-C4.  Draw order: contexts (or prefixes) ->
+    physical-id permutation -> K -> V -> Q."""
+    rng = np.random.default_rng(seed)
+    if prefix_lo is not None:
+        prefix = rng.integers(prefix_lo, prefix_hi + 1, size=B)
+        ctx = [int(p) + L for p in prefix]
+        max_ctx = prefix_hi + L
+    else:
+        ctx = [int(c) for c in rng.integers(ctx_lo, ctx_hi + 1, size=B)]
+        max_ctx = ctx_hi
+    max_pages = _pages_needed(max_ctx, ps)
+    npg = [_pages_needed(c, ps) for c in ctx]
+    live = sum(npg)
+    num_pages = pool_pages if pool_pages is not None else int(math.ceil(live * (1.0 + free_frac)))
+    assert num_pages >= live
+    perm = rng.permutation(num_pages)
+    ids, cur = [], 0
+    for n in npg:
+        ids.append([int(p) for p in perm[cur:cur + n]])
+        cur += n
+    order = [p for row in ids for p in row]
+    slots = [s for c in ctx for s in _valid_slots_per_page(c, ps)]
+    kp = _fill_pool(rng, "bf16", num_pages, H_kv, ps, D, order, slots, GARBAGE_DEFAULT)
+    vp = _fill_pool(rng, "bf16", num_pages, H_kv, ps, D, order, slots, GARBAGE_DEFAULT)
+    q = _queries(rng, "bf16", B, H_q, L, D, None, GARBAGE_DEFAULT)
+    bt = _tables_from_ids(ctx, ps, max_pages, ids)
+    return PagedInputs(
+        name=name, seed=seed, dtype="bf16", B=B, H_q=H_q, H_kv=H_kv, L=L, D=D,
+        page_size=ps, num_pages=num_pages, max_pages=max_pages,
+        scale=1.0 / math.sqrt(D), causal=causal, query=q, key_pages=kp,
+        value_pages=vp, block_table=bt, context_lens=np.asarray(ctx, dtype=np.int32),
+        meta={"live_pages": live})
+
+
+def make_c2(seed: int = SEEDS["C2"]) -> PagedInputs:
+    """GQA decode, bf16, Llama-3-8B head shape: B=64, H_q=32, H_kv=8, D=128,
+    L=1, page_size=16, context_lens ~ U{128..4096}, a pool of 20000 pages
+    with shuffled physical ids."""
+    x = _uniform_pool_config("C2", seed, B=64, H_q=32, H_kv=8, D=128, L=1, ps=16,
+                             ctx_lo=128, ctx_hi=4096, pool_pages=20000)
+    x.meta["workload"] = "GQA decode bf16 B64 Hq32 Hkv8 D128 ps16 ctx U[128,4096]"
+    return x
+
+
+def make_c3(seed: int = SEEDS["C3"]) -> PagedInputs:
+    """Chunked causal prefill, bf16, Qwen2.5-7B-like heads: B=4, H_q=28,
+    H_kv=4, D=128, a 512-row query chunk appended after a prefix
+    ~ U{0..2048}; page_size=16; pool = live pages + 10% free pages."""
+    x = _uniform_pool_config("C3", seed, B=4, H_q=28, H_kv=4, D=128, L=512, ps=16,
+                             ctx_lo=None, ctx_hi=None, free_frac=0.10,
+                             prefix_lo=0, prefix_hi=2048)
+    x.meta["workload"] = "chunked causal prefill bf16 B4 Hq28 Hkv4 D128 L512 prefix U[0,2048] ps16"
+    return x
+
+
+def make_c4(seed: int = SEEDS["C4"]) -> PagedInputs:
+    """Long-context split-KV decode, bf16: B=8, H_q=32, H_kv=8, D=128, L=1,
+    context_lens ~ U{32768..131072}, page_size=16, pool = live + 10% free."""
+    x = _uniform_pool_config("C4", seed, B=8, H_q=32, H_kv=8, D=128, L=1, ps=16,
+                             ctx_lo=32768, ctx_hi=131072, free_frac=0.10)
+    x.meta["workload"] = "long-context decode bf16 B8 Hq32 Hkv8 D128 ps16 ctx U[32768,131072]"
+    return x
+
+
+def make_c5(seed: int = SEEDS["C5"]) -> MixedInputs:
+    """Mixed ragged batch, bf16: 48 decode requests (L=1) and 8 prefill
+    requests (L ~ U{64..256}); H_q=32, H_kv=8, D=128, page_size=128, contexts
+    ~ U{256..16384}.  14 requests (25%) share one 2048-token prefix: their
+    first 16 block-table entries name the same 16 physical pages (complete and
+    read-only).  Pool = ceil(used / 0.9) pages, ids shuffled.
+
+    Draw order: prefill query lengths -> sharer choice -> contexts ->
+    physical-id permutation -> K -> V -> Q(decode) -> Q(prefill).
+    """
+    rng = np.random.default_rng(seed)
+    H_q, H_kv, D, ps = 32, 8, 128, 128
+    n_dec, n_pre, shared_tokens = 48, 8, 2048
+    n_req = n_dec + n_pre
+    max_ctx = 16384
+    max_pages = max_ctx // ps
+    qlen_pre = [int(v) for v in rng.integers(64, 256 + 1, size=n_pre)]
+    qlen = [1] * n_dec + qlen_pre
+    sharers = sorted(int(v) for v in rng.choice(n_req, size=n_req // 4, replace=False))
+    ctx = []
+    for r in range(n_req):
+        lo = shared_tokens + qlen[r] if r in sharers else max(256, qlen[r])
+        ctx.append(int(rng.integers(lo, max_ctx + 1)))
+    n_shared_pages = shared_tokens // ps
+    own_pages = []
+    for r in range(n_req):
+        n = _pages_needed(ctx[r], ps)
+        own_pages.append(n - n_shared_pages if r in sharers else n)
+    used = n_shared_pages + sum(own_pages)
+    num_pages = int(math.ceil(used / 0.9))
+    perm = rng.permutation(num_pages)
+    shared_ids = [int(p) for p in perm[:n_shared_pages]]
+    cur = n_shared_pages
+    ids, order, slots = [], list(shared_ids), [ps] * n_shared_pages
+    for r in range(n_req):
+        mine = [int(p) for p in perm[cur:cur + own_pages[r]]]
+        cur += own_pages[r]
+        row = (shared_ids + mine) if r in sharers else mine
+        ids.append(row)
+        vs = _valid_slots_per_page(ctx[r], ps)
+        order.extend(mine)
+        slots.extend(vs[len(vs) - len(mine):])
+    kp = _fill_pool(rng, "bf16", num_pages, H_kv, ps, D, order, slots, GARBAGE_DEFAULT)
+    vp = _fill_pool(rng, "bf16", num_pages, H_kv, ps, D, order, slots, GARBAGE_DEFAULT)
+    q_dec = _queries(rng, "bf16", n_dec, H_q, 1, D, None, GARBAGE_DEFAULT)
+    L_pre = max(qlen_pre)
+    ql_pre = np.asarray(qlen_pre, dtype=np.int32)
+    q_pre = _queries(rng, "bf16", n_pre, H_q, L_pre, D, ql_pre, GARBAGE_DEFAULT)
+    bt = _tables_from_ids(ctx, ps, max_pages, ids)
+    cl = np.asarray(ctx, dtype=np.int32)
+    common = dict(seed=seed, dtype="bf16", H_q=H_q, H_kv=H_kv, D=D, page_size=ps,
+                  num_pages=num_pages, max_pages=max_pages, scale=1.0 / math.sqrt(D),
+                  causal=True, key_pages=kp, value_pages=vp)
+    dec = PagedInputs(name="C5-decode", B=n_dec, L=1, query=q_dec,
+                      block_table=np.ascontiguousarray(bt[:n_dec]),
+                      context_lens=np.ascontiguousarray(cl[:n_dec]), **common)
+    pre = PagedInputs(name="C5-prefill", B=n_pre, L=L_pre, query=q_pre,
+                      block_table=np.ascontiguousarray(bt[n_dec:]),
+                      context_lens=np.ascontiguousarray(cl[n_dec:]),
+                      query_lens=ql_pre, **common)
+    meta = {"workload": "mixed ragged batch bf16 48 decode + 8 prefill, Hq32 Hkv8 D128 ps128, "
+                        "25% share a 2048-token prefix",
+            "sharers": sharers, "shared_page_ids": shared_ids, "used_pages": used}
+    dec.meta.update(meta)
+    pre.meta.update(meta)
+    return MixedInputs(name="C5", seed=seed, decode=dec, prefill=pre, meta=meta)
+
+
+BUILDERS = {"C1": make_c1, "C2": make_c2, "C3": make_c3, "C4": make_c4, "C5": make_c5}
+
+
+def make_config(name: str, seed: Optional[int] = None):
+    """Build one of the five named workloads (C5 returns a MixedInputs)."""
+    fn = BUILDERS[name]
+    return fn() if seed is None else fn(seed)
