@@ -1,0 +1,316 @@
+"""Benchmark of the paged-attention read path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only C2,C3,...]
+                    [--no-cpu-baseline] [--no-flush]
+
+Prints ONE JSON line.  The headline ``value`` is the decode workload "GQA
+decode, bf16, B=64, H_q=32, H_kv=8, D=128, page_size=16, contexts U[128,4096]"
+(seed 2): algorithmic K/V bytes of one step (every visible K and V element
+once) divided by the mean HIP-event time of the step (pa_decode +
+pa_split_reduce), with the inputs resident in HBM and the 256 MB last-level
+cache flushed before every step.  ``roofline`` is for the dominant kernel
+(the decode kernel alone, timed by its own event pair).  Secondary sections
+report the chunked prefill, long-context decode, mixed batch and a
+long-prompt prefill sweep with their own rooflines.  ``cpu_baseline`` times
+the CPU oracle on the host on the full decode workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+FLUSH_BYTES = 1 << 30          # > 256 MB last-level cache
+
+
+# --------------------------------------------------------------------- work
+def decode_kv_bytes(x, unique: bool = False) -> int:
+    """K+V bytes a decode call must read: every visible key and value of
+    every kv head once (unique=True counts shared physical pages once)."""
+    elem = 4 if x.dtype == "f32" else 2
+    per_tok = x.H_kv * x.D * 2 * elem
+    if not unique:
+        return int(x.context_lens.astype(np.int64).sum()) * per_tok
+    seen = {}
+    for b in range(x.B):
+        n = int(x.context_lens[b])
+        for lp in range((n + x.page_size - 1) // x.page_size):
+            p = int(x.block_table[b, lp])
+            seen[p] = max(seen.get(p, 0), min(x.page_size, n - lp * x.page_size))
+    return int(sum(seen.values())) * per_tok
+
+
+def prefill_flops(x) -> float:
+    """4 * D * H_q * (number of visible (query, key) pairs): QK^T and PV,
+    two flops per multiply-add, causal-visible pairs only."""
+    pairs = 0
+    rows = x.rows_valid()
+    for b in range(x.B):
+        ctx, lb = int(x.context_lens[b]), int(rows[b])
+        if x.causal:
+            pairs += sum(ctx - lb + i + 1 for i in range(lb))
+        else:
+            pairs += lb * ctx
+    return 4.0 * x.D * x.H_q * pairs
+
+
+# ------------------------------------------------------------------- timing
+class Runner:
+    def __init__(self, torch, api, flush: bool):
+        self.torch = torch
+        self.api = api
+        self.flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda") if flush else None
+
+    def flush(self):
+        if self.flush_buf is not None:
+            self.flush_buf.fill_(1.0)
+
+    def to_device(self, x, pages=None):
+        from tests._gpu import DeviceInputs
+        return DeviceInputs(x, pages=pages)
+
+    def time_decode(self, d, steps, warmup, partition_tokens=0):
+        torch, api = self.torch, self.api
+        x = d.x
+        out = torch.empty_like(d.q)
+        args = api.make_args(d.q, d.kp, d.vp, d.bt, d.cl, out, scale=x.scale, mask=d.mask,
+                             query_lens=d.ql)
+        S, P, _ = api.pa_decode_plan(args, partition_tokens=partition_tokens)
+        ws = api.Workspace(x.B, x.H_q, x.L, x.D, S, P, d.q.device)
+        for _ in range(warmup):
+            self.flush()
+            api.pa_decode(args, ws)
+            if S > 1:
+                api.pa_split_reduce(args, ws)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            self.flush()
+            ev[k][0].record()
+            api.pa_decode(args, ws)
+            ev[k][1].record()
+            if S > 1:
+                api.pa_split_reduce(args, ws)
+            ev[k][2].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        dec = np.array([e[0].elapsed_time(e[1]) for e in ev])    # ms
+        red = np.array([e[1].elapsed_time(e[2]) for e in ev])
+        return {"S": S, "P": P, "decode_ms": dec, "reduce_ms": red, "step_ms": dec + red,
+                "wall_s": wall, "out": out}
+
+    def time_prefill(self, d, steps, warmup, flush=False):
+        torch, api = self.torch, self.api
+        x = d.x
+        out = torch.empty_like(d.q)
+        args = api.make_args(d.q, d.kp, d.vp, d.bt, d.cl, out, scale=x.scale, mask=d.mask,
+                             query_lens=d.ql)
+        for _ in range(warmup):
+            if flush:
+                self.flush()
+            api.pa_prefill(args)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for k in range(steps):
+            if flush:
+                self.flush()
+            ev[k][0].record()
+            api.pa_prefill(args)
+            ev[k][1].record()
+        torch.cuda.synchronize()
+        return {"ms": np.array([e[0].elapsed_time(e[1]) for e in ev]), "out": out}
+
+
+def _stats(ms):
+    return {"mean_ms": float(np.mean(ms)), "median_ms": float(np.median(ms)),
+            "p10_ms": float(np.percentile(ms, 10)), "p90_ms": float(np.percentile(ms, 90))}
+
+
+def _source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_kv_cache_96_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _counters(name, sha):
+    """HBM traffic per launch from committed rocprofv3 counter summaries, or
+    None when the kernel source changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", f"{name}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("kernel_source_sha") != sha:
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+# --------------------------------------------------------------- cpu oracle
+def cpu_baseline(x, kv_bytes, min_seconds=10.0, max_runs=5):
+    import oracle
+    oracle.load()
+    times, threads = [], 0
+    t_all = time.perf_counter()
+    while len(times) < max_runs and (time.perf_counter() - t_all) < min_seconds:
+        t0 = time.perf_counter()
+        _, threads = oracle.attention_of(x, return_threads=True)
+        times.append(time.perf_counter() - t0)
+    t = float(np.mean(times))
+    return {"value": kv_bytes / t / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"the full decode workload ({x.B} requests, {int(x.context_lens.sum())} "
+                      f"keys), fp64 C oracle, mean of {len(times)} run(s) of {t:.2f} s"}
+
+
+# --------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="C2,C3,C4,C5,long")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--partition-tokens", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_cache_96_amd import api
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    only = set(args.only.split(","))
+    run = Runner(torch, api, flush=not args.no_flush)
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
+
+    # ---- headline: C2 GQA decode
+    x2 = W.make_c2()
+    d2 = run.to_device(x2)
+    kv2 = decode_kv_bytes(x2)
+    log(f"[bench] decode C2: {kv2 / 1e6:.1f} MB of K/V per step")
+    r2 = run.time_decode(d2, args.steps, args.warmup, args.partition_tokens)
+    step_ms = float(np.mean(r2["step_ms"]))
+    dec_ms = float(np.mean(r2["decode_ms"]))
+    value = kv2 / (step_ms * 1e-3) / 1e9
+    achieved = kv2 / (dec_ms * 1e-3) / 1e9
+    sha_dec = _source_sha("pa_decode.hip", "pa_common.hpp")
+    traffic = _counters("decode_c2", sha_dec)
+    log(f"[bench] decode C2: step {step_ms * 1e3:.1f} us (decode {dec_ms * 1e3:.1f} us), "
+        f"{value:.0f} GB/s, S={r2['S']} P={r2['P']}")
+    result = {
+        "metric": "decode K/V HBM GB/s (% of peak) + prefill TFLOP/s (% MFMA peak), 1 MI355X",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "GQA decode bf16 B64 Hq32 Hkv8 D128 L1 page16 ctx U[128,4096] seed2",
+                   "B": x2.B, "H_q": x2.H_q, "H_kv": x2.H_kv, "D": x2.D, "page_size": 16,
+                   "num_splits": r2["S"], "partition_tokens": r2["P"],
+                   "llc_flushed": not args.no_flush, "kv_bytes_per_step": kv2},
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": kv2,
+                     "mean_launch_us": round(dec_ms * 1e3, 2), "source_sha": sha_dec},
+        "step_stats": _stats(r2["step_ms"]),
+        "reduce_mean_us": round(float(np.mean(r2["reduce_ms"])) * 1e3, 2),
+        "wall_s_timed_region": round(r2["wall_s"], 4),
+    }
+    del r2
+
+    sections = {}
+    sha_pre = _source_sha("pa_prefill.hip", "pa_common.hpp")
+    if "C3" in only:
+        x3 = W.make_c3()
+        d3 = run.to_device(x3)
+        fl = prefill_flops(x3)
+        r3 = run.time_prefill(d3, args.steps, args.warmup)
+        ms = float(np.mean(r3["ms"]))
+        tf = fl / (ms * 1e-3) / 1e12
+        log(f"[bench] prefill C3: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+        sections["prefill_C3"] = {
+            "workload": "chunked causal prefill bf16 B4 Hq28 Hkv4 D128 L512 prefix U[0,2048] page16 seed3",
+            "flops": fl, "tflops": round(tf, 2), **_stats(r3["ms"]),
+            "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tf, 2),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                         "traffic": _counters("prefill_c3", sha_pre), "source_sha": sha_pre}}
+        del d3, r3
+    if "long" in only:
+        long = []
+        for L in (4096, 16384):
+            xl = W.make_random(100 + L, B=1, H_q=28, H_kv=4, L=L, D=128, page_size=16, ctx=[L],
+                               dtype="bf16", causal=True, extra_free_pages=16)
+            dl = run.to_device(xl)
+            fl = prefill_flops(xl)
+            rl = run.time_prefill(dl, max(5, args.steps // 6), 2)
+            ms = float(np.mean(rl["ms"]))
+            tf = fl / (ms * 1e-3) / 1e12
+            log(f"[bench] long prefill L={L}: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+            long.append({"workload": f"long-prompt causal prefill bf16 B1 Hq28 Hkv4 D128 L{L} prefix0 page16",
+                         "flops": fl, "tflops": round(tf, 2),
+                         "frac_of_mfma_peak": round(tf / BF16_PEAK_TFLOPS, 4), **_stats(rl["ms"])})
+            del dl, rl
+        sections["prefill_long_prompt"] = long
+    if "C4" in only:
+        x4 = W.make_c4()
+        d4 = run.to_device(x4)
+        kv4 = decode_kv_bytes(x4)
+        r4 = run.time_decode(d4, max(10, args.steps // 3), args.warmup)
+        sm = float(np.mean(r4["step_ms"]))
+        dm = float(np.mean(r4["decode_ms"]))
+        log(f"[bench] decode C4: {sm * 1e3:.1f} us, {kv4 / sm / 1e6:.0f} GB/s, S={r4['S']}")
+        sections["decode_C4"] = {
+            "workload": "long-context decode bf16 B8 Hq32 Hkv8 D128 page16 ctx U[32768,131072] seed4",
+            "kv_bytes": kv4, "gbs_step": round(kv4 / sm / 1e6, 2), "num_splits": r4["S"],
+            "partition_tokens": r4["P"], **_stats(r4["step_ms"]),
+            "roofline": {"bound": "hbm", "kernel": "decode_kernel",
+                         "achieved": round(kv4 / dm / 1e6, 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(kv4 / dm / 1e6 / HBM_PEAK_GBS, 4)}}
+        del d4, r4, x4
+    if "C5" in only:
+        m = W.make_c5()
+        dd = run.to_device(m.decode)
+        dp = run.to_device(m.prefill, pages=(dd.kp, dd.vp))
+        rd = run.time_decode(dd, max(10, args.steps // 3), args.warmup)
+        rp = run.time_prefill(dp, max(10, args.steps // 3), args.warmup, flush=True)
+        logical = decode_kv_bytes(m.decode)
+        unique = decode_kv_bytes(m.decode, unique=True)
+        sm = float(np.mean(rd["step_ms"]))
+        pm = float(np.mean(rp["ms"]))
+        fl = prefill_flops(m.prefill)
+        log(f"[bench] mixed C5: decode {sm * 1e3:.1f} us ({unique / sm / 1e6:.0f} GB/s unique), "
+            f"prefill {pm * 1e3:.1f} us ({fl / pm / 1e9:.1f} TFLOP/s)")
+        sections["mixed_C5"] = {
+            "workload": "mixed ragged batch bf16 48 decode + 8 prefill Hq32 Hkv8 D128 page128, "
+                        "25% share a 2048-token prefix, seed5",
+            "decode_unique_kv_bytes": unique, "decode_logical_kv_bytes": logical,
+            "decode_gbs_unique": round(unique / sm / 1e6, 2),
+            "decode_gbs_logical": round(logical / sm / 1e6, 2), "decode_mean_ms": sm,
+            "prefill_flops": fl, "prefill_tflops": round(fl / pm / 1e9, 2), "prefill_mean_ms": pm,
+            "combined_ms": round(sm + pm, 5)}
+        del dd, dp, rd, rp
+    result["sections"] = sections
+
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline on the decode workload")
+        result["cpu_baseline"] = cpu_baseline(x2, kv2)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

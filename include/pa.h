@@ -1,0 +1,163 @@
+/*
+ * pa.h -- C ABI of the paged-attention read path for AMD Instinct MI355X
+ * (gfx950).  libpa.so implements it with hand-written HIP kernels.
+ *
+ * The operation is the paged_attention contract of tiny-llm "Week 3 Day 4:
+ * Direct Paged Attention" (section "The Paged Attention API"): every query row
+ * attends over the keys/values of its request, which live in a shared page
+ * pool.  Logical key j of request b is found by translating it through the
+ * block table -- logical page j / page_size, physical page
+ * block_table[b][j / page_size], slot j % page_size (sections "Why
+ * block_table Matters" and "How This Maps to tiny-llm") -- and only the first
+ * context_lens[b] keys are visible.  Tiles of K/V are folded into the output
+ * with the online-softmax recurrence of the same page's "Task 2" (running max,
+ * rescaled running sum and output, one division at the end); no dense K/V
+ * tensor is ever built.  The metadata set matches PagedKvMetadata of anllm
+ * "Tutorial 13" (section 6).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All data pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or synchronises.  Work is enqueued on `stream`
+ *    (a hipStream_t; NULL means the null stream) and the call returns at once.
+ *  - Layouts are dense row-major with no padding:
+ *      query, out        [B, H_q, L, D]
+ *      key/value_pages   [num_pages, H_kv, page_size, D]
+ *      block_table       [B, max_pages] int32; entries at or after logical
+ *                        page ceil(context_lens[b] / page_size) are never read
+ *                        (pad them with -1)
+ *      context_lens      [B] int32: visible keys of request b, including the
+ *                        K/V of its own new query rows
+ *      query_lens        [B] int32 or NULL (= L for every request): valid
+ *                        query rows of request b; rows i >= query_lens[b] are
+ *                        written as zeros
+ *  - dtype applies to query, the pages and out alike: PA_DTYPE_F32 or
+ *    PA_DTYPE_BF16 (bfloat16 bits).  Scores, softmax statistics and the
+ *    accumulator are fp32; a bf16 output is rounded to nearest-even once.
+ *  - head_dim must be 64 or 128.  Query head h reads kv head h / (H_q / H_kv).
+ *  - Causal rows are bottom-right aligned: row i of request b is position
+ *    context_lens[b] - query_lens[b] + i and sees keys j <= that position.
+ *    With L = 1 the two masks coincide.
+ *  - A row with no visible key (context 0) is written as zeros.
+ *  - query, the pages, out and the workspace must be 16-byte aligned.
+ *
+ * Errors: arguments are validated synchronously before anything is enqueued.
+ * A rejected call enqueues nothing and returns a negative pa_status.  The
+ * device-side contract (block-table entries that must be read lie in
+ * [0, num_pages); context_lens[b] <= max_pages * page_size; 0 <= query_lens[b]
+ * <= L; with a causal mask query_lens[b] <= context_lens[b]) is taken on trust
+ * and violating it is undefined behaviour.  Kernel faults surface at the
+ * caller's next synchronisation.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,  /* null pointer, bad size, bad scale/mask, misalignment */
+  PA_ERR_UNSUPPORTED = -2,  /* head_dim or dtype outside what the kernels implement */
+  PA_ERR_WORKSPACE = -3,    /* split workspace missing, too small or inconsistent */
+  PA_ERR_HIP = -4           /* the HIP runtime refused a launch */
+} pa_status;
+
+typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
+typedef enum { PA_MASK_NONE = 0, PA_MASK_CAUSAL = 1 } pa_mask;
+
+typedef struct pa_args {
+  const void *query;           /* [B, H_q, L, D] */
+  const void *key_pages;       /* [num_pages, H_kv, page_size, D] */
+  const void *value_pages;     /* [num_pages, H_kv, page_size, D] */
+  const int32_t *block_table;  /* [B, max_pages] */
+  const int32_t *context_lens; /* [B] */
+  const int32_t *query_lens;   /* [B] or NULL */
+  void *out;                   /* [B, H_q, L, D] */
+  int32_t batch;               /* B >= 0 (0: nothing to do) */
+  int32_t num_q_heads;         /* H_q, a multiple of H_kv */
+  int32_t num_kv_heads;        /* H_kv >= 1 */
+  int32_t q_len;               /* L >= 1 */
+  int32_t head_dim;            /* D in {64, 128} */
+  int32_t num_pages;           /* pool size >= 1 */
+  int32_t page_size;           /* tokens per page >= 1 */
+  int32_t max_pages;           /* block-table row length >= 1 */
+  int32_t dtype;               /* pa_dtype */
+  int32_t mask;                /* pa_mask */
+  float scale;                 /* score scale, finite and > 0 (1/sqrt(D) is usual) */
+  /* Debug outputs (NULL in normal use; either one selects the instrumented
+   * kernels).  debug_trace [B, max_pages*page_size, 2] int32 receives, for
+   * every logical key the kernels read, the (physical page, slot) they
+   * computed for it; other entries are left as the caller set them.
+   * debug_visits [B, H_kv, max_pages*page_size] int32 is incremented once
+   * per key each time a workgroup folds it into the softmax state; only the
+   * workgroups whose rows include the last valid query row of the request
+   * count, so a correct walk leaves exactly 1 for j < context_lens[b] and 0
+   * beyond.  The caller zeroes debug_visits. */
+  int32_t *debug_trace;
+  int32_t *debug_visits;
+} pa_args;
+
+/* Split-KV workspace of the decode path ("Reading vLLM's PagedAttention
+ * Kernel", section 3.3: a long context is cut into partitions computed in
+ * parallel and combined afterwards).  Partition s covers keys
+ * [s * partition_tokens, min((s + 1) * partition_tokens, context_len)).
+ *   partial_out  fp32 [B, H_q, L, num_splits, D]  normalised partition outputs
+ *   partial_lse  fp32 [B, H_q, L, num_splits]     natural-log log-sum-exp of
+ *                                                 the scaled scores (-inf: empty)
+ * Both are caller-owned device memory of the size pa_decode_plan reports.
+ * With num_splits == 1 the buffers may be NULL and pa_decode writes `out`. */
+typedef struct pa_workspace {
+  float *partial_out;
+  float *partial_lse;
+  int32_t num_splits;        /* >= 1 */
+  int32_t partition_tokens;  /* > 0, a multiple of page_size */
+} pa_workspace;
+
+/* Choose the split plan of pa_decode for `args` (only the sizes in `args`
+ * are read; no pointer is dereferenced and nothing runs on the GPU).
+ * On input plan->partition_tokens > 0 requests that partition size (rounded
+ * up to a multiple of page_size); 0 lets the library choose from the maximum
+ * context max_pages * page_size and `num_cus` (0: 256, the MI355X CU count).
+ * On return plan->num_splits and plan->partition_tokens are set, the buffer
+ * pointers are left untouched, and *workspace_bytes (if not NULL) is the
+ * total size of partial_out plus partial_lse (0 when num_splits == 1). */
+pa_status pa_decode_plan(const pa_args *args, int32_t num_cus, pa_workspace *plan,
+                         size_t *workspace_bytes);
+
+/* Decode: query rows L <= 8 (one-token decode and short chunks).  Each
+ * workgroup owns one (request, kv head, row block, partition) and walks the
+ * partition's pages with the G * L query rows of that kv head held in
+ * registers, so every K/V byte is read once per row block.  num_splits == 1
+ * writes `out`; num_splits > 1 writes the workspace, and pa_split_reduce
+ * must follow on the same stream. */
+pa_status pa_decode(const pa_args *args, const pa_workspace *ws, void *stream);
+
+/* Log-sum-exp merge of the partition states pa_decode left in `ws` into
+ * `out`: M = max_s lse_s, out = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M),
+ * over the partitions s < ceil(context_lens[b] / partition_tokens); rows with
+ * no visible key get zeros.  `args` must be the arguments of that pa_decode. */
+pa_status pa_split_reduce(const pa_args *args, const pa_workspace *ws, void *stream);
+
+/* Prefill: any L >= 1 (chunked prefill after a cached prefix).  bf16 runs on
+ * the MFMA kernel (K/V tiles staged page by page through LDS, QK^T and PV on
+ * bf16 matrix cores, fp32 statistics); fp32 runs on a vector-ALU kernel. */
+pa_status pa_prefill(const pa_args *args, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *pa_status_string(int32_t status);
+
+/* PA_ABI_VERSION of the built library. */
+int32_t pa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

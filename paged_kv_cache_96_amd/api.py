@@ -1,0 +1,145 @@
+"""Thin Python binding of libpa.so for torch device tensors.
+
+Each function marshals tensors into the C structs of include/pa.h and calls
+the C entry point of the same name on torch's current HIP stream; the
+computation itself happens only in the HIP kernels.  torch provides device
+memory and streams, nothing else.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import PaArgs, PaWorkspace
+
+_DTYPES = {torch.float32: _lib.PA_DTYPE_F32, torch.bfloat16: _lib.PA_DTYPE_BF16}
+_MASKS = {"none": _lib.PA_MASK_NONE, None: _lib.PA_MASK_NONE, "causal": _lib.PA_MASK_CAUSAL}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libpa must be contiguous")
+    return t.data_ptr()
+
+
+def _int32(t: Optional[torch.Tensor], name: str) -> Optional[torch.Tensor]:
+    if t is not None and t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    return t
+
+
+def make_args(query: torch.Tensor, key_pages: torch.Tensor, value_pages: torch.Tensor,
+              block_table: torch.Tensor, context_lens: torch.Tensor, out: torch.Tensor, *,
+              scale: Optional[float] = None, mask: Optional[str] = "causal",
+              query_lens: Optional[torch.Tensor] = None,
+              debug_trace: Optional[torch.Tensor] = None,
+              debug_visits: Optional[torch.Tensor] = None) -> PaArgs:
+    """Fill a pa_args from tensors (shapes as in include/pa.h)."""
+    B, Hq, L, D = query.shape
+    P, Hkv, ps, D2 = key_pages.shape
+    if D2 != D or tuple(value_pages.shape) != tuple(key_pages.shape):
+        raise ValueError("query / key_pages / value_pages head sizes disagree")
+    if tuple(out.shape) != tuple(query.shape) or out.dtype != query.dtype:
+        raise ValueError("out must match query in shape and dtype")
+    if key_pages.dtype != query.dtype or value_pages.dtype != query.dtype:
+        raise ValueError("query and pages must share one dtype")
+    _int32(block_table, "block_table")
+    _int32(context_lens, "context_lens")
+    _int32(query_lens, "query_lens")
+    a = PaArgs()
+    a.query = _ptr(query)
+    a.key_pages = _ptr(key_pages)
+    a.value_pages = _ptr(value_pages)
+    a.block_table = _ptr(block_table)
+    a.context_lens = _ptr(context_lens)
+    a.query_lens = _ptr(query_lens)
+    a.out = _ptr(out)
+    a.batch, a.num_q_heads, a.num_kv_heads, a.q_len, a.head_dim = B, Hq, Hkv, L, D
+    a.num_pages, a.page_size, a.max_pages = P, ps, block_table.shape[1]
+    a.dtype = _DTYPES.get(query.dtype, 99)  # 99: the library rejects it as unsupported
+    a.mask = _MASKS[mask]
+    a.scale = float(scale) if scale is not None else 1.0 / math.sqrt(D)
+    a.debug_trace = _ptr(debug_trace)
+    a.debug_visits = _ptr(debug_visits)
+    return a
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def pa_decode_plan(args: PaArgs, *, num_cus: int = 0, partition_tokens: int = 0) -> Tuple[int, int, int]:
+    """(num_splits, partition_tokens, workspace_bytes) chosen by the library."""
+    ws = PaWorkspace()
+    ws.partition_tokens = int(partition_tokens)
+    nbytes = ctypes.c_size_t(0)
+    _lib.check("pa_decode_plan", _lib.lib().pa_decode_plan(ctypes.byref(args), int(num_cus),
+                                                            ctypes.byref(ws), ctypes.byref(nbytes)))
+    return ws.num_splits, ws.partition_tokens, nbytes.value
+
+
+class Workspace:
+    """Device buffers of a split plan (torch owns the memory)."""
+
+    def __init__(self, B: int, Hq: int, L: int, D: int, num_splits: int, partition_tokens: int,
+                 device):
+        self.num_splits = int(num_splits)
+        self.partition_tokens = int(partition_tokens)
+        if self.num_splits > 1:
+            self.partial_out = torch.empty((B, Hq, L, num_splits, D), dtype=torch.float32,
+                                           device=device)
+            self.partial_lse = torch.empty((B, Hq, L, num_splits), dtype=torch.float32,
+                                           device=device)
+        else:
+            self.partial_out = self.partial_lse = None
+        self.c = PaWorkspace()
+        self.c.partial_out = _ptr(self.partial_out)
+        self.c.partial_lse = _ptr(self.partial_lse)
+        self.c.num_splits = self.num_splits
+        self.c.partition_tokens = self.partition_tokens
+
+
+def pa_decode(args: PaArgs, workspace: Optional[Workspace] = None, stream=None) -> None:
+    ws = ctypes.byref(workspace.c) if workspace is not None else None
+    _lib.check("pa_decode", _lib.lib().pa_decode(ctypes.byref(args), ws, _stream(stream)))
+
+
+def pa_split_reduce(args: PaArgs, workspace: Workspace, stream=None) -> None:
+    _lib.check("pa_split_reduce", _lib.lib().pa_split_reduce(ctypes.byref(args),
+                                                              ctypes.byref(workspace.c),
+                                                              _stream(stream)))
+
+
+def pa_prefill(args: PaArgs, stream=None) -> None:
+    _lib.check("pa_prefill", _lib.lib().pa_prefill(ctypes.byref(args), _stream(stream)))
+
+
+def paged_attention(query: torch.Tensor, key_pages: torch.Tensor, value_pages: torch.Tensor,
+                    block_table: torch.Tensor, context_lens: torch.Tensor, *,
+                    scale: Optional[float] = None, mask: Optional[str] = "causal",
+                    query_lens: Optional[torch.Tensor] = None, partition_tokens: int = 0,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Convenience call: decode (+ merge) for L <= 8, prefill otherwise."""
+    if out is None:
+        out = torch.empty_like(query)
+    args = make_args(query, key_pages, value_pages, block_table, context_lens, out, scale=scale,
+                     mask=mask, query_lens=query_lens)
+    if query.shape[2] <= 8:
+        S, P, _ = pa_decode_plan(args, partition_tokens=partition_tokens)
+        ws = Workspace(query.shape[0], query.shape[1], query.shape[2], query.shape[3], S, P,
+                       query.device)
+        pa_decode(args, ws, stream)
+        if S > 1:
+            pa_split_reduce(args, ws, stream)
+        out._pa_workspace = ws  # keep the buffers alive until the caller is done
+    else:
+        pa_prefill(args, stream)
+    return out

@@ -1,0 +1,57 @@
+"""Build libpa.so in-tree with hipcc for gfx950.
+
+    python -m paged_kv_cache_96_amd.build [-v]
+
+Each HIP source is compiled to an object under ``_build/`` and linked into
+``paged_kv_cache_96_amd/libpa.so``.  Packed-fp32 instructions are disabled
+for all device code (``-packed-fp32-ops``).
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libpa.so")
+ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
+
+SOURCES = ["pa_decode.hip", "pa_reduce.hip", "pa_prefill.hip", "pa_host.cpp"]
+
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-fvisibility=hidden", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+          "-Wno-unused-command-line-argument"]
+
+
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = ["hipcc", *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = ["hipcc", "-x", "hip", *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    with ThreadPoolExecutor(max_workers=min(4, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    tmp = LIB + ".tmp"
+    cmd = ["hipcc", "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv[1:]))

@@ -1,0 +1,87 @@
+// Device helpers shared by the paged-attention kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// ---------------------------------------------------------------- bfloat16
+// bf16 is carried as raw 16-bit patterns; widening to fp32 is exact.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// a.lo*b.lo + a.hi*b.hi + c with bf16 pairs (products exact, fp32 sum).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ------------------------------------------------------------ exponentials
+// Scores are kept in base-2 units (scale already multiplied by log2 e), so
+// every exponential is one hardware exp2.  exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// --------------------------------------------------------------- cross-lane
+// DPP control words (gfx9 encoding).
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i of an 8-lane half row <- lane 7-i
+constexpr int kDppMirror = 0x140;     // lane i of a 16-lane row <- lane 15-i
+constexpr int kDppRor8 = 0x128;       // lane i of a 16-lane row <- lane (i+8)%16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N consecutive lanes; every lane of a group ends
+// with the same value (float addition is commutative, and each step adds the
+// same pair in both lanes).
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "N");
+  if constexpr (N >= 2) x += dpp<kDppXor1>(x);
+  if constexpr (N >= 4) x += dpp<kDppXor2>(x);
+  if constexpr (N >= 8) x += dpp<kDppHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp<kDppMirror>(x);
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Reduce across lanes that differ only in bits >= log2(STRIDE) of the lane
+// id (lanes l, l ^ STRIDE, l ^ 2*STRIDE, ...): combines the per-token-group
+// partial states of one wave.
+template <int STRIDE>
+__device__ __forceinline__ float stride_sum(float x) {
+  if constexpr (STRIDE <= 8) x += dpp<kDppRor8>(x);
+  if constexpr (STRIDE <= 16) x += __shfl_xor(x, 16);
+  if constexpr (STRIDE <= 32) x += __shfl_xor(x, 32);
+  return x;
+}
+template <int STRIDE>
+__device__ __forceinline__ float stride_max(float x) {
+  if constexpr (STRIDE <= 8) x = fmaxf(x, dpp<kDppRor8>(x));
+  if constexpr (STRIDE <= 16) x = fmaxf(x, __shfl_xor(x, 16));
+  if constexpr (STRIDE <= 32) x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+}  // namespace pa

@@ -1,0 +1,197 @@
+// C-ABI host layer of libpa.so: synchronous validation, the split plan, and
+// kernel launches on the caller's stream.  Nothing here allocates device
+// memory or synchronises.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+#define PA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kMinPartitionTokens = 256;  // below this the merge costs more than it buys
+constexpr int kBlocksPerCu = 8;           // decode workgroups wanted per compute unit
+constexpr int kMaxGridYZ = 65535;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Size checks shared by every entry point (no pointer is dereferenced).
+pa_status check_sizes(const pa_args *a) {
+  if (!a) return PA_ERR_INVALID_ARG;
+  if (a->batch < 0 || a->num_q_heads < 1 || a->num_kv_heads < 1 || a->q_len < 1 ||
+      a->head_dim < 1 || a->num_pages < 1 || a->page_size < 1 || a->max_pages < 1)
+    return PA_ERR_INVALID_ARG;
+  if (a->num_q_heads % a->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  if (a->mask != PA_MASK_NONE && a->mask != PA_MASK_CAUSAL) return PA_ERR_INVALID_ARG;
+  if (!(a->scale > 0.f) || !isfinite(a->scale)) return PA_ERR_INVALID_ARG;
+  if ((int64_t)a->max_pages * a->page_size > INT32_MAX / 2) return PA_ERR_INVALID_ARG;
+  if (a->batch > kMaxGridYZ) return PA_ERR_INVALID_ARG;
+  if (a->dtype != PA_DTYPE_F32 && a->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (a->head_dim != 64 && a->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+pa_status check_pointers(const pa_args *a) {
+  if (!a->query || !a->key_pages || !a->value_pages || !a->block_table || !a->context_lens ||
+      !a->out)
+    return PA_ERR_INVALID_ARG;
+  if (!aligned16(a->query) || !aligned16(a->key_pages) || !aligned16(a->value_pages) ||
+      !aligned16(a->out))
+    return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+// Workspace consistency for a decode/merge pair.  S == 1 needs no buffers.
+pa_status check_workspace(const pa_args *a, const pa_workspace *ws, int32_t *S, int32_t *P) {
+  const int32_t cap = a->max_pages * a->page_size;
+  if (!ws || ws->num_splits == 1) {
+    *S = 1;
+    *P = cap;
+    return PA_OK;
+  }
+  if (ws->num_splits < 1 || ws->partition_tokens <= 0 || ws->partition_tokens % a->page_size)
+    return PA_ERR_WORKSPACE;
+  if ((int64_t)ws->num_splits * ws->partition_tokens < cap) return PA_ERR_WORKSPACE;
+  if (!ws->partial_out || !ws->partial_lse || !aligned16(ws->partial_out) ||
+      !aligned16(ws->partial_lse))
+    return PA_ERR_WORKSPACE;
+  *S = ws->num_splits;
+  *P = ws->partition_tokens;
+  return PA_OK;
+}
+
+pa::LaunchParams make_params(const pa_args *a, int32_t S, int32_t P, const pa_workspace *ws) {
+  pa::LaunchParams p;
+  memset(&p, 0, sizeof p);
+  p.q = a->query;
+  p.kp = a->key_pages;
+  p.vp = a->value_pages;
+  p.bt = a->block_table;
+  p.cl = a->context_lens;
+  p.ql = a->query_lens;
+  p.out = a->out;
+  p.ws_o = (S > 1 && ws) ? ws->partial_out : nullptr;
+  p.ws_lse = (S > 1 && ws) ? ws->partial_lse : nullptr;
+  p.dbg_trace = a->debug_trace;
+  p.dbg_visits = a->debug_visits;
+  p.B = a->batch;
+  p.Hq = a->num_q_heads;
+  p.Hkv = a->num_kv_heads;
+  p.L = a->q_len;
+  p.D = a->head_dim;
+  p.num_pages = a->num_pages;
+  p.ps = a->page_size;
+  p.max_pages = a->max_pages;
+  p.causal = a->mask == PA_MASK_CAUSAL;
+  p.num_splits = S;
+  p.part_tokens = P;
+  p.scale_log2 = a->scale * 1.4426950408889634f;
+  return p;
+}
+
+pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+// Grid limits of the vector kernels: gridDim.y = H_kv * row blocks.
+pa_status check_decode_grid(const pa_args *a) {
+  const int64_t rows = (int64_t)(a->num_q_heads / a->num_kv_heads) * a->q_len;
+  const int64_t per = pa::decode_rows_per_block((int)(rows < 8 ? rows : 8));
+  const int64_t blocks_y = (int64_t)a->num_kv_heads * ((rows + per - 1) / per);
+  return blocks_y > kMaxGridYZ ? PA_ERR_INVALID_ARG : PA_OK;
+}
+
+}  // namespace
+
+PA_EXPORT int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+PA_EXPORT const char *pa_status_string(int32_t status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_INVALID_ARG: return "invalid argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported head_dim or dtype";
+    case PA_ERR_WORKSPACE: return "split workspace missing or inconsistent";
+    case PA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+PA_EXPORT pa_status pa_decode_plan(const pa_args *args, int32_t num_cus, pa_workspace *plan,
+                                   size_t *workspace_bytes) {
+  pa_status st = check_sizes(args);
+  if (st != PA_OK) return st;
+  if (!plan) return PA_ERR_INVALID_ARG;
+  if (args->q_len > 8) return PA_ERR_INVALID_ARG;
+  const int32_t ps = args->page_size;
+  const int32_t cap = args->max_pages * ps;
+  int32_t P;
+  if (plan->partition_tokens > 0) {
+    P = (plan->partition_tokens + ps - 1) / ps * ps;
+  } else {
+    const int cus = num_cus > 0 ? num_cus : 256;
+    const int64_t rows = (int64_t)(args->num_q_heads / args->num_kv_heads) * args->q_len;
+    const int64_t per = pa::decode_rows_per_block((int)(rows < 8 ? rows : 8));
+    const int64_t units =
+        (int64_t)(args->batch > 0 ? args->batch : 1) * args->num_kv_heads * ((rows + per - 1) / per);
+    const int64_t want = (int64_t)kBlocksPerCu * cus;
+    const int64_t splits = units >= want ? 1 : (want + units - 1) / units;
+    int64_t tok = (cap + splits - 1) / splits;
+    if (tok < kMinPartitionTokens) tok = kMinPartitionTokens;
+    P = (int32_t)((tok + ps - 1) / ps * ps);
+  }
+  if (P > cap) P = (cap + ps - 1) / ps * ps;
+  const int32_t S = (cap + P - 1) / P;
+  plan->num_splits = S;
+  plan->partition_tokens = P;
+  if (workspace_bytes) {
+    const size_t rows =
+        (size_t)(args->batch > 0 ? args->batch : 0) * args->num_q_heads * args->q_len;
+    *workspace_bytes = S > 1 ? rows * S * (args->head_dim + 1) * sizeof(float) : 0;
+  }
+  return PA_OK;
+}
+
+PA_EXPORT pa_status pa_decode(const pa_args *args, const pa_workspace *ws, void *stream) {
+  pa_status st = check_sizes(args);
+  if (st != PA_OK) return st;
+  if (args->q_len > 8) return PA_ERR_INVALID_ARG;
+  if (args->batch == 0) return PA_OK;
+  if ((st = check_pointers(args)) != PA_OK) return st;
+  if ((st = check_decode_grid(args)) != PA_OK) return st;
+  int32_t S, P;
+  if ((st = check_workspace(args, ws, &S, &P)) != PA_OK) return st;
+  const pa::LaunchParams p = make_params(args, S, P, ws);
+  return hip_status(pa::launch_decode(p, (pa::DType)args->dtype, (hipStream_t)stream));
+}
+
+PA_EXPORT pa_status pa_split_reduce(const pa_args *args, const pa_workspace *ws, void *stream) {
+  pa_status st = check_sizes(args);
+  if (st != PA_OK) return st;
+  if (args->q_len > 8) return PA_ERR_INVALID_ARG;
+  if (args->batch == 0) return PA_OK;
+  if ((st = check_pointers(args)) != PA_OK) return st;
+  int32_t S, P;
+  if ((st = check_workspace(args, ws, &S, &P)) != PA_OK) return st;
+  if (S == 1) return PA_OK;  // pa_decode already wrote `out`
+  const pa::LaunchParams p = make_params(args, S, P, ws);
+  return hip_status(pa::launch_split_reduce(p, (pa::DType)args->dtype, (hipStream_t)stream));
+}
+
+PA_EXPORT pa_status pa_prefill(const pa_args *args, void *stream) {
+  pa_status st = check_sizes(args);
+  if (st != PA_OK) return st;
+  if (args->batch == 0) return PA_OK;
+  if ((st = check_pointers(args)) != PA_OK) return st;
+  const int32_t cap = args->max_pages * args->page_size;
+  const pa::LaunchParams p = make_params(args, 1, cap, nullptr);
+  if (args->dtype == PA_DTYPE_BF16) {
+    const int64_t tiles = ((int64_t)(args->num_q_heads / args->num_kv_heads) * args->q_len + 127) / 128;
+    if (tiles > INT32_MAX || args->num_kv_heads > kMaxGridYZ) return PA_ERR_INVALID_ARG;
+    return hip_status(pa::launch_prefill_mfma(p, (hipStream_t)stream));
+  }
+  if ((st = check_decode_grid(args)) != PA_OK) return st;
+  return hip_status(pa::launch_decode(p, (pa::DType)args->dtype, (hipStream_t)stream));
+}

@@ -1,0 +1,310 @@
+// bf16 paged prefill kernel on gfx950 matrix cores.
+//
+// Work: one workgroup (4 waves) owns BM = 128 packed query rows of one
+// (request b, kv head g); packed row rho is position rho / G of head
+// g*G + rho % G, so the G heads that share a kv head share every K/V tile and
+// the rows of a tile sit at nearly the same causal position.  Keys are walked
+// in tiles of BN = 64 (tiny-llm "Week 3 Day 4", "Task 2": resolve every K/V
+// tile through the block table, fold it in with the online softmax).
+//
+// Per key tile:
+//   1. staging: every thread issues 16-byte loads of the NEXT tile's K and V
+//      rows (address = physical page from the block table, slot, kv head)
+//      into registers while the current tile is computed, then stores them to
+//      the other LDS buffer (double buffering, one barrier per tile);
+//   2. S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: K from LDS is the A
+//      operand, Q (kept in registers for the whole walk) the B operand.  The
+//      result gives every lane the scores of ONE query row (lane % 32) against
+//      16 of the tile's keys; the other 16 sit in lane ^ 32;
+//   3. online softmax in registers (row max over the lane pair with a
+//      permlane32 swap, exp2 of pre-scaled scores, fp32 row sums), P rounded
+//      to bf16 once;
+//   4. O^T += V^T . P^T with the same MFMA: P^T comes straight from the
+//      lane's own registers (B operand); V^T (A operand) is read from the
+//      natural [key][d] LDS tile with ds_read_b64_tr_b16, which hands each
+//      lane four consecutive keys of one head dimension.
+// Keys past a row's causal limit are masked on the diagonal tiles only, and
+// tiles past the last row's limit are never loaded.
+#include "pa_common.hpp"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+constexpr int kBM = 128;   // packed query rows per workgroup (32 per wave)
+constexpr int kBN = 64;    // keys per tile
+
+template <int D>
+struct Tile {
+  static constexpr int kKStride = D + 8;               // shorts per K row (pad 16 B)
+  static constexpr int kVStride = D == 128 ? 160 : 96;  // shorts per V row (320 B / 192 B)
+  static constexpr int kKBytes = kBN * kKStride * 2;
+  static constexpr int kVBytes = kBN * kVStride * 2;
+  static constexpr int kChunks = D / 8;                // 16-byte chunks per row
+  static constexpr int kKeysPerRound = 256 / kChunks;
+  static constexpr int kRounds = kBN / kKeysPerRound;
+  static constexpr int kKSteps = D / 16;               // MFMA k-steps of QK^T
+  static constexpr int kMBlocks = D / 32;              // 32-row blocks of O^T
+};
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));
+}
+
+// Max of a value held by lane l and lane l ^ 32.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D, bool DEBUG>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchParams p, int num_tiles) {
+  using TL = Tile<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kBN * TL::kKStride];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kBN * TL::kVStride];
+
+  const int tile = num_tiles - 1 - (int)blockIdx.x;  // heavy (late) tiles first
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int half = lane >> 5;       // which 8-wide k chunk / key half this lane holds
+  const int ln = lane & 31;         // query row of this lane within the wave
+
+  const int G = p.Hq / p.Hkv;
+  const int ctx = p.cl[b];
+  const int Lb = p.ql ? p.ql[b] : p.L;
+  const int rows_valid = G * Lb;
+  const int rows_all = G * p.L;
+  const int rho0 = tile * kBM;
+
+  // ---- this lane's query row
+  const int rho = rho0 + wave * 32 + ln;
+  const int qi = rho / G;
+  const int qh = g * G + (rho - qi * G);
+  const bool row_valid = rho < rows_valid;
+  const int lim = row_valid ? (p.causal ? ctx - Lb + qi + 1 : ctx) : 0;
+
+  // ---- key ranges: the workgroup's (for staging) and this wave's (compute)
+  const int rho_last_wg = min(rho0 + kBM, rows_valid) - 1;
+  const int kend_wg = rho_last_wg < rho0 ? 0
+                      : (p.causal ? ctx - Lb + rho_last_wg / G + 1 : ctx);
+  const int rho_first_w = rho0 + wave * 32;
+  const int rho_last_w = min(rho_first_w + 32, rows_valid) - 1;
+  const int kend_w = rho_last_w < rho_first_w ? 0
+                     : (p.causal ? ctx - Lb + rho_last_w / G + 1 : ctx);
+  const int kfull_w = rho_last_w < rho_first_w ? 0
+                      : (p.causal ? ctx - Lb + rho_first_w / G + 1 : ctx);  // keys below: unmasked
+  const int ntiles = (kend_wg + kBN - 1) / kBN;
+  const bool counts = DEBUG && rows_valid > 0 && (rows_valid - 1) / kBM == tile;
+
+  // ---- Q as the B operand of S^T = K Q^T: dims kk*16 + half*8 .. +8
+  uint4 q[TL::kKSteps];
+  {
+    const uint16_t *qp = reinterpret_cast<const uint16_t *>(p.q) +
+                         ((size_t)(b * p.Hq + qh) * p.L + qi) * D + half * 8;
+#pragma unroll
+    for (int kk = 0; kk < TL::kKSteps; ++kk)
+      q[kk] = row_valid ? *reinterpret_cast<const uint4 *>(qp + kk * 16) : make_uint4(0, 0, 0, 0);
+  }
+
+  // ---- staging of one K/V tile: thread -> (key kr*KPR + tid / CH, chunk tid % CH)
+  const uint16_t *kp = reinterpret_cast<const uint16_t *>(p.kp);
+  const uint16_t *vp = reinterpret_cast<const uint16_t *>(p.vp);
+  const int32_t *bt = p.bt + (size_t)b * p.max_pages;
+  const int chunk = tid % TL::kChunks;
+  const int key_in_round = tid / TL::kChunks;
+  uint4 kst[TL::kRounds], vst[TL::kRounds];
+
+  auto stage_load = [&](int kt) {
+#pragma unroll
+    for (int r = 0; r < TL::kRounds; ++r) {
+      const int j = kt * kBN + r * TL::kKeysPerRound + key_in_round;
+      if (j < kend_wg) {
+        const int lp = j / p.ps;
+        const int page = bt[lp];
+        const int slot = j - lp * p.ps;
+        const size_t off = (((size_t)page * p.Hkv + g) * p.ps + slot) * D + chunk * 8;
+        kst[r] = *reinterpret_cast<const uint4 *>(kp + off);
+        vst[r] = *reinterpret_cast<const uint4 *>(vp + off);
+        if constexpr (DEBUG) {
+          if (counts && chunk == 0) {
+            const size_t cap = (size_t)p.max_pages * p.ps;
+            if (g == 0) {
+              p.dbg_trace[((size_t)b * cap + j) * 2 + 0] = page;
+              p.dbg_trace[((size_t)b * cap + j) * 2 + 1] = slot;
+            }
+            atomicAdd(&p.dbg_visits[((size_t)b * p.Hkv + g) * cap + j], 1);
+          }
+        }
+      } else {
+        kst[r] = make_uint4(0, 0, 0, 0);  // never loaded: zeros keep masked math finite
+        vst[r] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  auto stage_store = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < TL::kRounds; ++r) {
+      const int key = r * TL::kKeysPerRound + key_in_round;
+      *reinterpret_cast<uint4 *>(&k_lds[buf][key * TL::kKStride + chunk * 8]) = kst[r];
+      *reinterpret_cast<uint4 *>(&v_lds[buf][key * TL::kVStride + chunk * 8]) = vst[r];
+    }
+  };
+
+  // ---- running state of this lane's query row
+  f32x16_t o[TL::kMBlocks];
+#pragma unroll
+  for (int mb = 0; mb < TL::kMBlocks; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[mb][i] = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
+  const float c = p.scale_log2;
+
+  if (ntiles > 0) {
+    stage_load(0);
+    stage_store(0);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    const bool more = kt + 1 < ntiles;
+    if (more) stage_load(kt + 1);
+
+    if (kt * kBN < kend_w) {
+      // -- S^T for the two 32-key blocks of the tile
+      f32x16_t s[2];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[blk][i] = 0.f;
+        const uint16_t *krow = &k_lds[buf][(blk * 32 + ln) * TL::kKStride + half * 8];
+#pragma unroll
+        for (int kk = 0; kk < TL::kKSteps; ++kk) {
+          const uint4 a = *reinterpret_cast<const uint4 *>(krow + kk * 16);
+          s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(q[kk]), s[blk],
+                                                           0, 0, 0);
+        }
+      }
+      // -- mask keys at or past this row's limit (diagonal / tail tiles only)
+      if ((kt + 1) * kBN > kfull_w) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kt * kBN + blk * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+            if (key >= lim) s[blk][i] = kNegInf;
+          }
+      }
+      // -- online softmax update for this row
+      float mx = s[0][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+      mx = pair_max(mx);
+      const float m_new = fmaxf(m_run, mx * c);
+      const bool none = m_new == kNegInf;
+      const float alpha = none ? 1.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      uint32_t pb[2][8];
+      float psum = 0.f;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const float p0 = none ? 0.f : fast_exp2(fmaf(s[blk][i], c, -m_new));
+          const float p1 = none ? 0.f : fast_exp2(fmaf(s[blk][i + 1], c, -m_new));
+          psum += p0 + p1;
+          pb[blk][i >> 1] = cvt_pk_bf16(p0, p1);
+        }
+      l_run = fmaf(l_run, alpha, psum);
+#pragma unroll
+      for (int mb = 0; mb < TL::kMBlocks; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[mb][i] *= alpha;
+
+      // -- O^T += V^T P^T over four 16-key steps
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int blk = ks >> 1, hf = ks & 1;
+        const uint4 bop = make_uint4(pb[blk][hf * 4 + 0], pb[blk][hf * 4 + 1], pb[blk][hf * 4 + 2],
+                                     pb[blk][hf * 4 + 3]);
+        // keys of the two 4-key runs this lane's k slots stand for
+        const int kb = blk * 32 + hf * 16 + half * 4;
+        const int src = lane & 15;  // transpose read: source lane j reads row kb + j/4, cols +4*(j%4)
+#pragma unroll
+        for (int mb = 0; mb < TL::kMBlocks; ++mb) {
+          const int d0 = mb * 32 + ((lane >> 4) & 1) * 16 + 4 * (src & 3);
+          const uint16_t *r1 = &v_lds[buf][(kb + (src >> 2)) * TL::kVStride + d0];
+          const uint16_t *r2 = r1 + 8 * TL::kVStride;
+          const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)r1);
+          const s16x4_t t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)r2);
+          const uint4 aop = make_uint4(
+              (uint32_t)(uint16_t)t1[0] | ((uint32_t)(uint16_t)t1[1] << 16),
+              (uint32_t)(uint16_t)t1[2] | ((uint32_t)(uint16_t)t1[3] << 16),
+              (uint32_t)(uint16_t)t2[0] | ((uint32_t)(uint16_t)t2[1] << 16),
+              (uint32_t)(uint16_t)t2[2] | ((uint32_t)(uint16_t)t2[3] << 16));
+          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop), as_bf16x8(bop), o[mb],
+                                                          0, 0, 0);
+        }
+      }
+    }
+
+    if (more) stage_store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- finalize: O = O^T / l, rounded to bf16; padding rows get zeros
+  const float l_tot = pair_sum(l_run);  // uniform: every lane of the wave takes part
+  if (rho < rows_all) {
+    const float inv = (row_valid && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    uint16_t *op = reinterpret_cast<uint16_t *>(p.out) + ((size_t)(b * p.Hq + qh) * p.L + qi) * D;
+#pragma unroll
+    for (int mb = 0; mb < TL::kMBlocks; ++mb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = mb * 32 + i4 * 8 + half * 4;
+        const uint2 w = make_uint2(cvt_pk_bf16(o[mb][i4 * 4 + 0] * inv, o[mb][i4 * 4 + 1] * inv),
+                                   cvt_pk_bf16(o[mb][i4 * 4 + 2] * inv, o[mb][i4 * 4 + 3] * inv));
+        *reinterpret_cast<uint2 *>(op + d) = w;
+      }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const LaunchParams &p, hipStream_t stream) {
+  const int G = p.Hq / p.Hkv;
+  const int tiles = (G * p.L + kBM - 1) / kBM;
+  dim3 grid(tiles, p.Hkv, p.B);
+  if (p.dbg_trace || p.dbg_visits) {
+    hipLaunchKernelGGL((prefill_kernel<D, true>), grid, dim3(256), 0, stream, p, tiles);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<D, false>), grid, dim3(256), 0, stream, p, tiles);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_mfma(const LaunchParams &p, hipStream_t stream) {
+  return p.D == 64 ? launch_d<64>(p, stream) : launch_d<128>(p, stream);
+}
+
+}  // namespace pa
