@@ -26,11 +26,30 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair (lo, hi) with the hardware converter
+// (v_cvt_pk_bf16_f32, round to nearest even).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 
 // a.lo*b.lo + a.hi*b.hi + c with bf16 pairs (products exact, fp32 sum).
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ----------------------------------------------------------- streaming loads
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load with the non-temporal hint: data read exactly once (paged
+// decode K/V) bypasses normal cache allocation, which on MI355X lifts the
+// sustained HBM read rate well above that of ordinary loads.
+__device__ __forceinline__ uint4 load_stream(const void *p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 // ------------------------------------------------------------ exponentials

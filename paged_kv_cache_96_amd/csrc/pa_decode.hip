@@ -7,18 +7,33 @@
 // operations; "Reading vLLM's PagedAttention Kernel" section 3.3: split long
 // contexts into partitions that are merged afterwards):
 //
-//   grid  = (partition s, kv head g x row block, request b), 256 threads.
+//   grid  = (kv head g x row block, request b, partition s), 256 threads.
 //   A workgroup owns the ROWS packed query rows (row rho -> position
 //   rho / G, head g*G + rho % G) of one kv head, so each K/V byte of the
 //   partition is read once for all of them.  Its 4 waves take interleaved
 //   steps of STEP keys.  In a step every lane issues 16-byte loads: LPT
 //   lanes cover one key's D elements and a wave load covers TPL keys, so the
-//   loads of a page are fully coalesced.  Dot products are summed over the
-//   LPT lanes with DPP; the (max, sum, output) state is kept per row in
-//   registers and rescaled with exp2 (scores are in base-2 units).  At the end
-//   the token groups and the waves are merged through LDS and the partition
-//   state is written (normalised output + log-sum-exp), or the final output
-//   when there is a single partition.
+//   loads of a page are fully coalesced.  K/V are read exactly once, with
+//   non-temporal loads.
+//
+//   Page resolution: when steps never straddle a page (page_size a multiple
+//   of STEP) each wave computes the 64-bit element offset of the page/slot of
+//   each of its steps once, up front, one step per lane; the walk then takes
+//   the offset of step k with a readlane, so the loop issues no memory
+//   operation besides the K/V loads and addresses are formed in scalar
+//   registers.  Other page sizes resolve the page per lane.
+//
+//   Softmax state: every group of LPT lanes (one key of each load) keeps its
+//   own running max / sum / output for every row, so the walk needs no
+//   cross-group exchange.  The max is refreshed lazily: only when a new score
+//   exceeds the reference max by more than 2^8 (the weights then stay below
+//   256 and fp32 sums stay exact to rounding).  Dot products are summed over
+//   the LPT lanes with DPP; scores are kept in base-2 units.  For bf16 the
+//   PV product runs on bf16 dot2 instructions with the weights rounded to
+//   bf16 (two keys per instruction), and the row sums add those same rounded
+//   weights.  At the end the groups and then the
+//   waves are merged and the partition state is written (normalised output
+//   plus log-sum-exp), or the final output when there is one partition.
 #include "pa_common.hpp"
 #include "pa_internal.h"
 
@@ -26,6 +41,9 @@ namespace pa {
 namespace {
 
 using Vec = uint4;  // one 16-byte lane load
+
+constexpr float kMinM = -1.0e30f;  // running-max sentinel: exp2(x - kMinM) never overflows
+constexpr float kLazy = 8.0f;      // refresh the max only when it grows by more than this (log2)
 
 template <typename T>
 struct Elem;
@@ -65,6 +83,10 @@ __device__ __forceinline__ float lane_dot(const Vec &q, const Vec &k) {
   }
 }
 
+__device__ __forceinline__ uint32_t word(const Vec &v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
 template <typename T, int D, int ROWS, bool DEBUG>
 __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blocks) {
   constexpr int kElems = Elem<T>::kPerVec;
@@ -73,21 +95,36 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
   constexpr int kLoads = 4;             // loads in flight per step (each of K and V)
   constexpr int kStep = kTpl * kLoads;  // keys per wave step
   constexpr int kWaves = 4;
+  constexpr bool kBf16 = sizeof(T) == 2;
   static_assert(kLpt * kElems == D && kTpl * kLpt == 64, "layout");
 
-  const int s = blockIdx.x;
-  const int g = blockIdx.y / row_blocks;
-  const int rb = blockIdx.y - g * row_blocks;
-  const int b = blockIdx.z;
+  // Partitions are the slowest grid dimension: every request's first
+  // partition is dispatched before any second one, so the last workgroups
+  // to start are the (short) tail partitions of the longest requests.
+  const int g = blockIdx.x / row_blocks;
+  const int rb = blockIdx.x - g * row_blocks;
+  const int b = blockIdx.y;
+  const int s = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int c = lane % kLpt;            // element chunk of this lane
   const int kl = lane / kLpt;           // key of this lane within a load
 
   const int G = p.Hq / p.Hkv;
+  const int t0 = s * p.part_tokens;
+  const int ps = p.ps;
+  const bool uniform_page = (ps % kStep) == 0;
+  const int32_t *bt = p.bt + (size_t)b * p.max_pages;
+  // Start the block-table fetch for this wave's first 64 steps before the
+  // context length is known (entries past the context are fetched but never
+  // used), so the two loads overlap instead of following one another.
+  int pid_pre = 0;
+  if (uniform_page) {
+    const int lp = (t0 + (wave + kWaves * lane) * kStep) / ps;
+    if (lp < p.max_pages) pid_pre = bt[lp];
+  }
   const int ctx = p.cl[b];
   const int Lb = p.ql ? p.ql[b] : p.L;
-  const int t0 = s * p.part_tokens;
   const bool split = p.num_splits > 1;
   if (split && t0 >= ctx) return;  // empty partition: the merge never reads it
 
@@ -108,21 +145,24 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
     if (valid[r]) kmin = min(kmin, hi[r]);
   }
   const int t1 = split ? min(t0 + p.part_tokens, kmax) : kmax;
-  // last packed row of the request decides which row block counts visits
-  const bool counts = DEBUG && ((Lb * G - 1) / ROWS == rb) && Lb > 0;
+  // the row block holding the last packed row of the request counts visits
+  const bool counts = DEBUG && Lb > 0 && ((Lb * G - 1) / ROWS == rb);
 
   Vec qv[ROWS];
   const T *qbase = reinterpret_cast<const T *>(p.q);
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
-    qv[r] = valid[r] ? *reinterpret_cast<const Vec *>(qbase + qrow[r] * D + c * kElems)
-                     : make_uint4(0, 0, 0, 0);
+    // rows past query_lens are in bounds (i < L): load unconditionally, then drop
+    const bool exists = rb * ROWS + r < G * p.L;
+    const Vec v = exists ? *reinterpret_cast<const Vec *>(qbase + qrow[r] * D + c * kElems)
+                         : make_uint4(0, 0, 0, 0);
+    qv[r] = valid[r] ? v : make_uint4(0, 0, 0, 0);
   }
 
   float m[ROWS], l[ROWS], acc[ROWS][kElems];
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
-    m[r] = kNegInf;
+    m[r] = kMinM;
     l[r] = 0.f;
 #pragma unroll
     for (int e = 0; e < kElems; ++e) acc[r][e] = 0.f;
@@ -130,59 +170,78 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
 
   const T *kp = reinterpret_cast<const T *>(p.kp);
   const T *vp = reinterpret_cast<const T *>(p.vp);
-  const int32_t *bt = p.bt + (size_t)b * p.max_pages;
-  const int ps = p.ps;
-  const bool uniform_page = (ps % kStep) == 0;
   const int nsteps = t1 > t0 ? (t1 - t0 + kStep - 1) / kStep : 0;
+  const int nw = nsteps > wave ? (nsteps - wave + kWaves - 1) / kWaves : 0;  // this wave's steps
   const int tmin = min(t1, kmin);  // keys below this are visible to every valid row
+  const size_t head_stride = (size_t)ps * D;
+  const uint32_t lane_off = (uint32_t)(kl * D + c * kElems);
 
-  auto lane_offset = [&](int base, int n, int &page, int &slot) -> size_t {
-    int j = base + n * kTpl + kl;
-    if (uniform_page) {
+  // Offsets of the page/slot of this wave's steps k0 .. k0+63 (one per lane).
+  uint32_t off_lo = 0, off_hi = 0;
+  auto resolve = [&](int k0) {
+    const int k = k0 + lane;
+    if (k < nw) {
+      const int base = t0 + (wave + kWaves * k) * kStep;
       const int lp = base / ps;
-      page = __builtin_amdgcn_readfirstlane(bt[lp]);
-      slot = base - lp * ps + n * kTpl + kl;
-    } else {
-      j = min(j, t1 - 1);  // keys past the end reuse a valid address; masked below
-      const int lp = j / ps;
-      page = bt[lp];
-      slot = j - lp * ps;
+      const int page = k0 == 0 ? pid_pre : bt[lp];
+      const size_t off = ((size_t)page * p.Hkv + g) * head_stride + (size_t)(base - lp * ps) * D;
+      off_lo = (uint32_t)off;
+      off_hi = (uint32_t)(off >> 32);
     }
-    return ((size_t)page * p.Hkv + g) * ps * D + (size_t)slot * D + c * kElems;
   };
 
-  auto load_step = [&](int step, Vec (&kv)[kLoads], Vec (&vv)[kLoads]) {
-    const int base = t0 + step * kStep;
+  // Element offset of key n*TPL + kl of step (wave-step k, global step st).
+  auto key_offset = [&](int k, int st, int n, int &page, int &slot) -> size_t {
+    if (uniform_page) {
+      const uint32_t lo = __builtin_amdgcn_readlane(off_lo, k & 63);
+      const uint32_t hi2 = __builtin_amdgcn_readlane(off_hi, k & 63);
+      const size_t base = ((size_t)hi2 << 32) | lo;
+      if constexpr (DEBUG) {
+        const int bj = t0 + st * kStep;
+        page = bt[bj / ps];
+        slot = bj % ps + n * kTpl + kl;
+      }
+      return base + lane_off + (size_t)n * kTpl * D;
+    }
+    int j = t0 + st * kStep + n * kTpl + kl;
+    j = min(j, t1 - 1);  // keys past the end reuse a valid address; masked below
+    const int lp = j / ps;
+    page = bt[lp];
+    slot = j - lp * ps;
+    return ((size_t)page * p.Hkv + g) * head_stride + (size_t)slot * D + c * kElems;
+  };
+
+  auto load_step = [&](int k, Vec (&kv)[kLoads], Vec (&vv)[kLoads]) {
+    const int st = wave + kWaves * k;
 #pragma unroll
     for (int n = 0; n < kLoads; ++n) {
-      int page, slot;
-      const size_t off = lane_offset(base, n, page, slot);
-      kv[n] = *reinterpret_cast<const Vec *>(kp + off);
-      vv[n] = *reinterpret_cast<const Vec *>(vp + off);
+      int page = 0, slot = 0;
+      const size_t off = key_offset(k, st, n, page, slot);
+      kv[n] = load_stream(kp + off);
+      vv[n] = load_stream(vp + off);
       if constexpr (DEBUG) {
-        const int j = base + n * kTpl + kl;
+        const int j = t0 + st * kStep + n * kTpl + kl;
         if (counts && c == 0 && j < t1) {
+          const size_t cap = (size_t)p.max_pages * ps;
           if (g == 0) {
-            p.dbg_trace[((size_t)b * p.max_pages * ps + j) * 2 + 0] = page;
-            p.dbg_trace[((size_t)b * p.max_pages * ps + j) * 2 + 1] = slot;
+            p.dbg_trace[((size_t)b * cap + j) * 2 + 0] = page;
+            p.dbg_trace[((size_t)b * cap + j) * 2 + 1] = slot;
           }
-          atomicAdd(&p.dbg_visits[((size_t)b * p.Hkv + g) * p.max_pages * ps + j], 1);
+          atomicAdd(&p.dbg_visits[((size_t)b * p.Hkv + g) * cap + j], 1);
         }
       }
     }
   };
 
-  auto fold_step = [&](int step, const Vec (&kv)[kLoads], const Vec (&vv)[kLoads]) {
-    const int base = t0 + step * kStep;
+  const float cs = p.scale_log2;
+  auto fold_step = [&](int k, const Vec (&kv)[kLoads], const Vec (&vv)[kLoads]) {
+    const int base = t0 + (wave + kWaves * k) * kStep;
     const bool tail = base + kStep > tmin;
     float sc[kLoads][ROWS];
 #pragma unroll
-    for (int n = 0; n < kLoads; ++n) {
+    for (int n = 0; n < kLoads; ++n)
 #pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        sc[n][r] = group_sum<kLpt>(lane_dot<T>(qv[r], kv[n])) * p.scale_log2;
-      }
-    }
+      for (int r = 0; r < ROWS; ++r) sc[n][r] = group_sum<kLpt>(lane_dot<T>(qv[r], kv[n]));
     if (tail) {
 #pragma unroll
       for (int n = 0; n < kLoads; ++n) {
@@ -192,75 +251,118 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
           if (j >= min(hi[r], t1)) sc[n][r] = kNegInf;
       }
     }
+    // lazy refresh of the per-group reference max
+    float mx[ROWS];
+    bool need = false;
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
-      float mx = sc[0][r];
+      float v = sc[0][r];
 #pragma unroll
-      for (int n = 1; n < kLoads; ++n) mx = fmaxf(mx, sc[n][r]);
-      mx = stride_max<kLpt>(mx);
-      const float mnew = fmaxf(m[r], mx);
-      const bool none = mnew == kNegInf;
-      const float alpha = none ? 1.f : fast_exp2(m[r] - mnew);
-      m[r] = mnew;
-      l[r] *= alpha;
+      for (int n = 1; n < kLoads; ++n) v = fmaxf(v, sc[n][r]);
+      mx[r] = v * cs;
+      need |= mx[r] > m[r] + kLazy;
+    }
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
-      for (int e = 0; e < kElems; ++e) acc[r][e] *= alpha;
+      for (int r = 0; r < ROWS; ++r) {
+        const float mn = fmaxf(m[r], mx[r]);
+        const float alpha = fast_exp2(m[r] - mn);
+        m[r] = mn;
+        l[r] *= alpha;
 #pragma unroll
-      for (int n = 0; n < kLoads; ++n) {
-        const float pr = none ? 0.f : fast_exp2(sc[n][r] - mnew);
-        sc[n][r] = pr;
-        l[r] += pr;
+        for (int e = 0; e < kElems; ++e) acc[r][e] *= alpha;
       }
     }
 #pragma unroll
-    for (int n = 0; n < kLoads; ++n) {
-      float vf[kElems];
-      widen<T>(vv[n], vf);
-      if (tail && base + n * kTpl + kl >= t1) {
-        // stale slots past the context may hold anything, NaN included
-#pragma unroll
-        for (int e = 0; e < kElems; ++e) vf[e] = 0.f;
-      }
+    for (int n = 0; n < kLoads; ++n)
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) {
+        const float pr = fast_exp2(fmaf(sc[n][r], cs, -m[r]));
+        sc[n][r] = pr;
+        if constexpr (!kBf16) l[r] += pr;
+      }
+    // stale slots past the context may hold anything, NaN included
+    bool dead[kLoads];
 #pragma unroll
-        for (int e = 0; e < kElems; ++e) acc[r][e] = fmaf(sc[n][r], vf[e], acc[r][e]);
+    for (int n = 0; n < kLoads; ++n) dead[n] = tail && (base + n * kTpl + kl >= t1);
+    if constexpr (kBf16) {
+#pragma unroll
+      for (int n = 0; n < kLoads; n += 2) {
+        uint32_t pk[ROWS];
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+          pk[r] = cvt_pk_bf16(sc[n][r], sc[n + 1][r]);
+          l[r] = dot2_bf16(pk[r], 0x3f803f80u, l[r]);  // + both rounded weights (bf16 1.0 pair)
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t a = dead[n] ? 0u : word(vv[n], w);
+          const uint32_t bb = dead[n + 1] ? 0u : word(vv[n + 1], w);
+          const uint32_t lo = __builtin_amdgcn_perm(bb, a, 0x05040100u);  // dim 2w of keys n, n+1
+          const uint32_t hi2 = __builtin_amdgcn_perm(bb, a, 0x07060302u); // dim 2w+1
+#pragma unroll
+          for (int r = 0; r < ROWS; ++r) {
+            acc[r][2 * w] = dot2_bf16(pk[r], lo, acc[r][2 * w]);
+            acc[r][2 * w + 1] = dot2_bf16(pk[r], hi2, acc[r][2 * w + 1]);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < kLoads; ++n) {
+        float vf[kElems];
+        widen<T>(vv[n], vf);
+#pragma unroll
+        for (int e = 0; e < kElems; ++e) vf[e] = dead[n] ? 0.f : vf[e];
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+          for (int e = 0; e < kElems; ++e) acc[r][e] = fmaf(sc[n][r], vf[e], acc[r][e]);
       }
     }
   };
 
-  // ---- main walk: wave w takes steps w, w + 4, ...; the next step's loads
-  // are issued before the current step is folded.
-  if (wave < nsteps) {
-    Vec kc[kLoads], vc[kLoads];
-    load_step(wave, kc, vc);
-    for (int step = wave; step < nsteps; step += kWaves) {
-      Vec kn[kLoads], vn[kLoads];
-      const bool more = step + kWaves < nsteps;
-      if (more) load_step(step + kWaves, kn, vn);
-      fold_step(step, kc, vc);
-      if (more) {
-#pragma unroll
-        for (int n = 0; n < kLoads; ++n) { kc[n] = kn[n]; vc[n] = vn[n]; }
+  // ---- main walk: wave w takes steps w, w + 4, ...; three register buffers
+  // rotate so that the loads of the next two steps are in flight while a
+  // step is folded (the loop body is unrolled three times for the rotation).
+  if (nw > 0) {
+    if (uniform_page) resolve(0);
+    Vec ka[kLoads], va[kLoads], kb[kLoads], vb[kLoads], kc[kLoads], vc[kLoads];
+    auto fetch = [&](int k, Vec (&kv)[kLoads], Vec (&vv)[kLoads]) {
+      if (k < nw) {
+        if (uniform_page && k > 0 && (k & 63) == 0) resolve(k);
+        load_step(k, kv, vv);
       }
+    };
+    fetch(0, ka, va);
+    fetch(1, kb, vb);
+    for (int k = 0; k < nw; k += 3) {
+      fetch(k + 2, kc, vc);
+      fold_step(k, ka, va);
+      fetch(k + 3, ka, va);
+      if (k + 1 < nw) fold_step(k + 1, kb, vb);
+      fetch(k + 4, kb, vb);
+      if (k + 2 < nw) fold_step(k + 2, kc, vc);
     }
   }
 
-  // ---- merge token groups within the wave, then the waves through LDS
+  // ---- merge the token groups of the wave, then the waves through LDS
   __shared__ float sm_acc[kWaves][ROWS][D];
   __shared__ float sm_m[kWaves][ROWS];
   __shared__ float sm_l[kWaves][ROWS];
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
-    const float lt = stride_sum<kLpt>(l[r]);
+    const float M = stride_max<kLpt>(m[r]);
+    const float f = fast_exp2(m[r] - M);
+    const float lt = stride_sum<kLpt>(l[r] * f);
 #pragma unroll
-    for (int e = 0; e < kElems; ++e) acc[r][e] = stride_sum<kLpt>(acc[r][e]);
+    for (int e = 0; e < kElems; ++e) acc[r][e] = stride_sum<kLpt>(acc[r][e] * f);
     if (lane < kLpt) {
 #pragma unroll
       for (int e = 0; e < kElems; ++e) sm_acc[wave][r][c * kElems + e] = acc[r][e];
     }
     if (lane == 0) {
-      sm_m[wave][r] = m[r];
+      sm_m[wave][r] = M;
       sm_l[wave][r] = lt;
     }
   }
@@ -274,18 +376,18 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
     const int i = rho / G;
     const int h = g * G + (rho - i * G);
     const size_t row = ((size_t)(b * p.Hq + h) * p.L + i);
-    float M = kNegInf;
+    float M = kMinM;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][r]);
     float o = 0.f, lse = kNegInf;
-    if (valid[r] && M != kNegInf) {
-      float wsum = 0.f, osum = 0.f;
+    float wsum = 0.f, osum = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float f = fast_exp2(sm_m[w][r] - M);
-        wsum += f * sm_l[w][r];
-        osum += f * sm_acc[w][r][d];
-      }
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = fast_exp2(sm_m[w][r] - M);
+      wsum += f * sm_l[w][r];
+      osum += f * sm_acc[w][r][d];
+    }
+    if (valid[r] && wsum > 0.f) {
       o = osum / wsum;
       lse = (M + __log2f(wsum)) * kLn2;
     }
@@ -307,7 +409,7 @@ template <typename T, int D, int ROWS>
 hipError_t launch_typed(const LaunchParams &p, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
   const int row_blocks = (G * p.L + ROWS - 1) / ROWS;
-  dim3 grid(p.num_splits, p.Hkv * row_blocks, p.B);
+  dim3 grid(p.Hkv * row_blocks, p.B, p.num_splits);
   const bool debug = p.dbg_trace != nullptr || p.dbg_visits != nullptr;
   if (debug) {
     hipLaunchKernelGGL((decode_kernel<T, D, ROWS, true>), grid, dim3(256), 0, stream, p, row_blocks);

@@ -57,6 +57,7 @@ pa_status check_workspace(const pa_args *a, const pa_workspace *ws, int32_t *S, 
   if (ws->num_splits < 1 || ws->partition_tokens <= 0 || ws->partition_tokens % a->page_size)
     return PA_ERR_WORKSPACE;
   if ((int64_t)ws->num_splits * ws->partition_tokens < cap) return PA_ERR_WORKSPACE;
+  if (ws->num_splits > kMaxGridYZ) return PA_ERR_WORKSPACE;
   if (!ws->partial_out || !ws->partial_lse || !aligned16(ws->partial_out) ||
       !aligned16(ws->partial_lse))
     return PA_ERR_WORKSPACE;
@@ -96,12 +97,12 @@ pa::LaunchParams make_params(const pa_args *a, int32_t S, int32_t P, const pa_wo
 
 pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
-// Grid limits of the vector kernels: gridDim.y = H_kv * row blocks.
+// Grid limits of the vector kernels: gridDim.x = H_kv * row blocks.
 pa_status check_decode_grid(const pa_args *a) {
   const int64_t rows = (int64_t)(a->num_q_heads / a->num_kv_heads) * a->q_len;
   const int64_t per = pa::decode_rows_per_block((int)(rows < 8 ? rows : 8));
-  const int64_t blocks_y = (int64_t)a->num_kv_heads * ((rows + per - 1) / per);
-  return blocks_y > kMaxGridYZ ? PA_ERR_INVALID_ARG : PA_OK;
+  const int64_t blocks_x = (int64_t)a->num_kv_heads * ((rows + per - 1) / per);
+  return blocks_x > INT32_MAX ? PA_ERR_INVALID_ARG : PA_OK;
 }
 
 }  // namespace
@@ -143,6 +144,10 @@ PA_EXPORT pa_status pa_decode_plan(const pa_args *args, int32_t num_cus, pa_work
     P = (int32_t)((tok + ps - 1) / ps * ps);
   }
   if (P > cap) P = (cap + ps - 1) / ps * ps;
+  if ((cap + P - 1) / P > kMaxGridYZ) {  // partitions are a grid dimension
+    const int64_t tok = ((int64_t)cap + kMaxGridYZ - 1) / kMaxGridYZ;
+    P = (int32_t)((tok + ps - 1) / ps * ps);
+  }
   const int32_t S = (cap + P - 1) / P;
   plan->num_splits = S;
   plan->partition_tokens = P;
