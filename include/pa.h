@@ -112,12 +112,22 @@ typedef struct pa_args {
  *   partial_lse  fp32 [B, H_q, L, num_splits]     natural-log log-sum-exp of
  *                                                 the scaled scores (-inf: empty)
  * Both are caller-owned device memory of the size pa_decode_plan reports.
- * With num_splits == 1 the buffers may be NULL and pa_decode writes `out`. */
+ * With num_splits == 1 the buffers may be NULL and pa_decode writes `out`.
+ *
+ *   counters     uint32 [2] or NULL: work-queue counters.  When given (and
+ *                B <= 2048), pa_decode runs as a persistent kernel whose
+ *                workgroups pull (request, partition, kv head) items from a
+ *                queue, which keeps every compute unit busy on ragged
+ *                batches; NULL launches one workgroup per item instead.  The
+ *                caller zeroes them once before first use; every call leaves
+ *                them zero again.  Calls that share one counter pair must not
+ *                overlap in time (same stream, or synchronised). */
 typedef struct pa_workspace {
   float *partial_out;
   float *partial_lse;
   int32_t num_splits;        /* >= 1 */
   int32_t partition_tokens;  /* > 0, a multiple of page_size */
+  uint32_t *counters;
 } pa_workspace;
 
 /* Choose the split plan of pa_decode for `args` (only the sizes in `args`
@@ -127,7 +137,8 @@ typedef struct pa_workspace {
  * context max_pages * page_size and `num_cus` (0: 256, the MI355X CU count).
  * On return plan->num_splits and plan->partition_tokens are set, the buffer
  * pointers are left untouched, and *workspace_bytes (if not NULL) is the
- * total size of partial_out plus partial_lse (0 when num_splits == 1). */
+ * total size of partial_out plus partial_lse (0 when num_splits == 1) plus
+ * 256 bytes for the counters. */
 pa_status pa_decode_plan(const pa_args *args, int32_t num_cus, pa_workspace *plan,
                          size_t *workspace_bytes);
 

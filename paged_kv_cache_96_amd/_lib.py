@@ -57,6 +57,7 @@ class PaWorkspace(ctypes.Structure):
         ("partial_lse", ctypes.c_void_p),
         ("num_splits", ctypes.c_int32),
         ("partition_tokens", ctypes.c_int32),
+        ("counters", ctypes.c_void_p),
     ]
 
 

@@ -90,8 +90,10 @@ class Workspace:
     """Device buffers of a split plan (torch owns the memory)."""
 
     def __init__(self, B: int, Hq: int, L: int, D: int, num_splits: int, partition_tokens: int,
-                 device):
+                 device, queue: bool = True):
         self.num_splits = int(num_splits)
+        # work-queue counters: zeroed once here, left zero by every call
+        self.counters = torch.zeros(64, dtype=torch.int32, device=device) if queue else None
         self.partition_tokens = int(partition_tokens)
         if self.num_splits > 1:
             self.partial_out = torch.empty((B, Hq, L, num_splits, D), dtype=torch.float32,
@@ -105,6 +107,7 @@ class Workspace:
         self.c.partial_lse = _ptr(self.partial_lse)
         self.c.num_splits = self.num_splits
         self.c.partition_tokens = self.partition_tokens
+        self.c.counters = _ptr(self.counters)
 
 
 def pa_decode(args: PaArgs, workspace: Optional[Workspace] = None, stream=None) -> None:

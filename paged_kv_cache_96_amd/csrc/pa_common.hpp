@@ -52,6 +52,17 @@ __device__ __forceinline__ uint4 load_stream(const void *p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Word 3 of a raw (stride 0) buffer resource on gfx9-family GPUs: 32-bit
+// data format, no swizzle.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// 16-byte non-temporal raw buffer load at byte offset `off`; offsets at or
+// past the resource's num_records return zeros without a memory access.
+__device__ __forceinline__ uint4 load_stream_buf(__amdgpu_buffer_rsrc_t r, int off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, /*nt*/ 2);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // ------------------------------------------------------------ exponentials
 // Scores are kept in base-2 units (scale already multiplied by log2 e), so
 // every exponential is one hardware exp2.  exp2(-inf) = 0.

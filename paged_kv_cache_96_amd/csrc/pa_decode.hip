@@ -34,6 +34,8 @@
 //   weights.  At the end the groups and then the
 //   waves are merged and the partition state is written (normalised output
 //   plus log-sum-exp), or the final output when there is one partition.
+#include <type_traits>
+
 #include "pa_common.hpp"
 #include "pa_internal.h"
 
@@ -87,8 +89,13 @@ __device__ __forceinline__ uint32_t word(const Vec &v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-template <typename T, int D, int ROWS, bool DEBUG>
-__global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blocks) {
+// One work item: partition s of the ROWS-row block rb of kv head g of
+// request b.  Walks the partition, merges the waves through LDS and writes
+// the partition state (or the output when there is one partition).
+template <typename T, int D, int ROWS, bool DEBUG, bool UNIFORM>
+__device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g, int rb, int s,
+                                            int ctx, int Lb, float (*sm_acc)[ROWS][D],
+                                            float (*sm_m)[ROWS], float (*sm_l)[ROWS]) {
   constexpr int kElems = Elem<T>::kPerVec;
   constexpr int kLpt = D / kElems;      // lanes per key
   constexpr int kTpl = 64 / kLpt;       // keys per wave load
@@ -97,36 +104,16 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
   constexpr int kWaves = 4;
   constexpr bool kBf16 = sizeof(T) == 2;
   static_assert(kLpt * kElems == D && kTpl * kLpt == 64, "layout");
-
-  // Partitions are the slowest grid dimension: every request's first
-  // partition is dispatched before any second one, so the last workgroups
-  // to start are the (short) tail partitions of the longest requests.
-  const int g = blockIdx.x / row_blocks;
-  const int rb = blockIdx.x - g * row_blocks;
-  const int b = blockIdx.y;
-  const int s = blockIdx.z;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int c = lane % kLpt;            // element chunk of this lane
   const int kl = lane / kLpt;           // key of this lane within a load
 
   const int G = p.Hq / p.Hkv;
   const int t0 = s * p.part_tokens;
   const int ps = p.ps;
-  const bool uniform_page = (ps % kStep) == 0;
   const int32_t *bt = p.bt + (size_t)b * p.max_pages;
-  // Start the block-table fetch for this wave's first 64 steps before the
-  // context length is known (entries past the context are fetched but never
-  // used), so the two loads overlap instead of following one another.
-  int pid_pre = 0;
-  if (uniform_page) {
-    const int lp = (t0 + (wave + kWaves * lane) * kStep) / ps;
-    if (lp < p.max_pages) pid_pre = bt[lp];
-  }
-  const int ctx = p.cl[b];
-  const int Lb = p.ql ? p.ql[b] : p.L;
   const bool split = p.num_splits > 1;
-  if (split && t0 >= ctx) return;  // empty partition: the merge never reads it
 
   // ---- rows of this workgroup
   int hi[ROWS];
@@ -183,7 +170,7 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
     if (k < nw) {
       const int base = t0 + (wave + kWaves * k) * kStep;
       const int lp = base / ps;
-      const int page = k0 == 0 ? pid_pre : bt[lp];
+      const int page = bt[lp];
       const size_t off = ((size_t)page * p.Hkv + g) * head_stride + (size_t)(base - lp * ps) * D;
       off_lo = (uint32_t)off;
       off_hi = (uint32_t)(off >> 32);
@@ -192,7 +179,7 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
 
   // Element offset of key n*TPL + kl of step (wave-step k, global step st).
   auto key_offset = [&](int k, int st, int n, int &page, int &slot) -> size_t {
-    if (uniform_page) {
+    if constexpr (UNIFORM) {
       const uint32_t lo = __builtin_amdgcn_readlane(off_lo, k & 63);
       const uint32_t hi2 = __builtin_amdgcn_readlane(off_hi, k & 63);
       const size_t base = ((size_t)hi2 << 32) | lo;
@@ -226,6 +213,46 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
           if (g == 0) {
             p.dbg_trace[((size_t)b * cap + j) * 2 + 0] = page;
             p.dbg_trace[((size_t)b * cap + j) * 2 + 1] = slot;
+          }
+          atomicAdd(&p.dbg_visits[((size_t)b * p.Hkv + g) * cap + j], 1);
+        }
+      }
+    }
+  };
+
+  // Steps of a uniform walk are fetched through buffer resources whose base
+  // is the step's page/slot: a step past the end gets num_records = 0, so its
+  // loads return zeros without touching memory.  Every fetch is then issued
+  // unconditionally, and the compiler's wait counts see a straight-line
+  // stream of loads (with conditional fetches it must assume the later loads
+  // may be missing and waits for them too, which serialises the pipeline).
+  auto fetch_uniform = [&](auto refresh, int k, Vec (&kv)[kLoads], Vec (&vv)[kLoads]) {
+    const bool ok = k < nw;
+    if constexpr (decltype(refresh)::value) {
+      if (k > 0 && (k & 63) == 0 && ok) resolve(k);
+    }
+    const uint32_t lo = __builtin_amdgcn_readlane(off_lo, k & 63);
+    const uint32_t hi2 = __builtin_amdgcn_readlane(off_hi, k & 63);
+    const size_t base = ((size_t)hi2 << 32) | lo;
+    const int nrec = ok ? kStep * D * (int)sizeof(T) : 0;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T *>(kp + base), (short)0, nrec, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<T *>(vp + base), (short)0, nrec, kBufferRsrcWord3);
+#pragma unroll
+    for (int n = 0; n < kLoads; ++n) {
+      const int boff = (int)((lane_off + n * kTpl * D) * sizeof(T));
+      kv[n] = load_stream_buf(rk, boff);
+      vv[n] = load_stream_buf(rv, boff);
+      if constexpr (DEBUG) {
+        const int st = wave + kWaves * k;
+        const int j = t0 + st * kStep + n * kTpl + kl;
+        if (ok && counts && c == 0 && j < t1) {
+          const int bj = t0 + st * kStep;
+          const size_t cap = (size_t)p.max_pages * ps;
+          if (g == 0) {
+            p.dbg_trace[((size_t)b * cap + j) * 2 + 0] = bt[bj / ps];
+            p.dbg_trace[((size_t)b * cap + j) * 2 + 1] = bj % ps + n * kTpl + kl;
           }
           atomicAdd(&p.dbg_visits[((size_t)b * p.Hkv + g) * cap + j], 1);
         }
@@ -325,14 +352,37 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
   // ---- main walk: wave w takes steps w, w + 4, ...; three register buffers
   // rotate so that the loads of the next two steps are in flight while a
   // step is folded (the loop body is unrolled three times for the rotation).
-  if (nw > 0) {
-    if (uniform_page) resolve(0);
-    Vec ka[kLoads], va[kLoads], kb[kLoads], vb[kLoads], kc[kLoads], vc[kLoads];
-    auto fetch = [&](int k, Vec (&kv)[kLoads], Vec (&vv)[kLoads]) {
-      if (k < nw) {
-        if (uniform_page && k > 0 && (k & 63) == 0) resolve(k);
-        load_step(k, kv, vv);
+  Vec ka[kLoads], va[kLoads], kb[kLoads], vb[kLoads], kc[kLoads], vc[kLoads];
+  if constexpr (UNIFORM) {
+    // A walk of at most 64 steps per wave has every page offset resolved up
+    // front; longer walks (a single partition over a long context) refresh
+    // them every 64 steps.  The two loops are separate so that the refresh,
+    // a vector load that must complete at once, never sits on a path of the
+    // short loop (it would make the compiler wait for the prefetched loads).
+    resolve(0);
+    auto walk = [&](auto refresh) {
+      fetch_uniform(refresh, 0, ka, va);
+      fetch_uniform(refresh, 1, kb, vb);
+      int k = 0;
+      for (; k + 3 <= nw; k += 3) {  // straight-line body: three whole steps
+        fetch_uniform(refresh, k + 2, kc, vc);
+        fold_step(k, ka, va);
+        fetch_uniform(refresh, k + 3, ka, va);
+        fold_step(k + 1, kb, vb);
+        fetch_uniform(refresh, k + 4, kb, vb);
+        fold_step(k + 2, kc, vc);
       }
+      if (k < nw) fold_step(k, ka, va);  // the last one or two steps
+      if (k + 1 < nw) fold_step(k + 1, kb, vb);
+    };
+    if (nw <= 64) {
+      walk(std::integral_constant<bool, false>());
+    } else {
+      walk(std::integral_constant<bool, true>());
+    }
+  } else if (nw > 0) {
+    auto fetch = [&](int k, Vec (&kv)[kLoads], Vec (&vv)[kLoads]) {
+      if (k < nw) load_step(k, kv, vv);
     };
     fetch(0, ka, va);
     fetch(1, kb, vb);
@@ -347,9 +397,6 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
   }
 
   // ---- merge the token groups of the wave, then the waves through LDS
-  __shared__ float sm_acc[kWaves][ROWS][D];
-  __shared__ float sm_m[kWaves][ROWS];
-  __shared__ float sm_l[kWaves][ROWS];
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     const float M = stride_max<kLpt>(m[r]);
@@ -405,18 +452,188 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
   }
 }
 
+
+// Largest batch whose per-request partition counts the persistent schedule
+// keeps in LDS.
+constexpr int kSchedMaxB = kDecodeQueueMaxBatch;
+
+// Decode kernel.  Without a work counter every workgroup runs the one item
+// its block index names (grid = kv head x row block, request, partition;
+// partitions slowest, empty partitions exit at once).  With a work counter
+// the grid is the resident capacity of the GPU and workgroups pull items
+// from a queue until it is exhausted: blocks are dispatched to the XCDs in
+// strict round-robin order, so a plain grid of ragged items leaves slots of
+// fast XCDs idle while a slow XCD is full; the queue keeps every slot busy.
+// Queue order: all full partitions (request-major), then the partial last
+// partitions; empty partitions are never enumerated.  The last workgroup to
+// finish resets the counters to zero for the next call.
+template <typename T, int D, int ROWS, bool DEBUG, bool UNIFORM>
+__global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blocks) {
+  constexpr int kWaves = 4;
+  __shared__ float sm_acc[kWaves][ROWS][D];
+  __shared__ float sm_m[kWaves][ROWS];
+  __shared__ float sm_l[kWaves][ROWS];
+
+  if (p.counters == nullptr) {
+    const int g = blockIdx.x / row_blocks;
+    const int rb = blockIdx.x - g * row_blocks;
+    const int b = blockIdx.y;
+    const int s = blockIdx.z;
+    const int ctx = p.cl[b];
+    const int Lb = p.ql ? p.ql[b] : p.L;
+    if (p.num_splits > 1 && s * p.part_tokens >= ctx) return;  // never read by the merge
+    decode_item<T, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, s, ctx, Lb, sm_acc, sm_m, sm_l);
+    return;
+  }
+
+  // ---- persistent schedule: prefix counts of full / partial partitions
+  __shared__ int s_full[kSchedMaxB + 1];     // exclusive prefix of full partitions
+  __shared__ int s_part[kSchedMaxB + 1];     // exclusive prefix of partial ones
+  __shared__ int s_next[2];
+  const int B = p.B;
+  const int P = p.part_tokens;
+  const int tid = threadIdx.x;
+  // per-thread serial scan over a contiguous slice, then a block scan of sums
+  const int per = (B + 255) / 256;
+  int f_loc = 0, p_loc = 0;
+  for (int k = 0; k < per; ++k) {
+    const int b = tid * per + k;
+    if (b < B) {
+      const int ctx = p.cl[b];
+      const int f = ctx / P;
+      const int q = (ctx % P != 0 || ctx == 0) ? 1 : 0;  // context 0 still gets one item
+      s_full[b] = f;
+      s_part[b] = q;
+      f_loc += f;
+      p_loc += q;
+    }
+  }
+  __shared__ int s_sumf[256], s_sump[256];
+  s_sumf[tid] = f_loc;
+  s_sump[tid] = p_loc;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scan
+    const int a = tid >= off ? s_sumf[tid - off] : 0;
+    const int a2 = tid >= off ? s_sump[tid - off] : 0;
+    __syncthreads();
+    s_sumf[tid] += a;
+    s_sump[tid] += a2;
+    __syncthreads();
+  }
+  int run_f = tid > 0 ? s_sumf[tid - 1] : 0, run_p = tid > 0 ? s_sump[tid - 1] : 0;
+  for (int k = 0; k < per; ++k) {
+    const int b = tid * per + k;
+    if (b < B) {
+      const int f = s_full[b], q = s_part[b];
+      s_full[b] = run_f;
+      s_part[b] = run_p;
+      run_f += f;
+      run_p += q;
+    }
+  }
+  if (tid == 255) {
+    s_full[B] = s_sumf[255];
+    s_part[B] = s_sump[255];
+  }
+  const int U = p.Hkv * row_blocks;
+  __syncthreads();
+  const int F = s_full[B];
+  const long n_items = (long)(F + s_part[B]) * U;
+
+  // Item k of the queue: the first gridDim.x items go to the workgroups by
+  // block index, later ones are claimed through the counter (which counts
+  // claims beyond the first gridDim.x), so the launch starts without a burst
+  // of atomics on one address.
+  uint32_t *work = p.counters;
+  int item = blockIdx.x, parity = 0;
+  while (item < n_items) {
+    // claim the following item now; it is needed only after this one
+    int nxt = 0;
+    if (tid == 0) nxt = (int)(gridDim.x + atomicAdd(work, 1u));
+    const int pair = item / U;
+    const int u = item - pair * U;
+    int b, s;
+    if (pair < F) {  // full partition: largest b with s_full[b] <= pair
+      int lo = 0, hi = B - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_full[mid] <= pair) lo = mid; else hi = mid - 1;
+      }
+      b = lo;
+      s = pair - s_full[b];
+    } else {         // partial last partition of the j-th request that has one
+      const int j = pair - F;
+      int lo = 0, hi = B - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_part[mid] <= j) lo = mid; else hi = mid - 1;
+      }
+      b = lo;
+      s = s_full[b + 1] - s_full[b];
+    }
+    const int g = u / row_blocks;
+    const int rb = u - g * row_blocks;
+    const int ctx = p.cl[b];
+    const int Lb = p.ql ? p.ql[b] : p.L;
+    decode_item<T, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, s, ctx, Lb, sm_acc, sm_m, sm_l);
+    parity ^= 1;
+    if (tid == 0) s_next[parity] = nxt;
+    __syncthreads();  // also orders this item's LDS reads before the next item's writes
+    item = s_next[parity];
+  }
+  if (tid == 0) {
+    if (atomicAdd(work + 1, 1u) == gridDim.x - 1) {  // every workgroup is done claiming
+      work[0] = 0u;
+      work[1] = 0u;
+    }
+  }
+}
+
+// Workgroups of `kernel` that fit on the current device at once (cached per
+// kernel and device).
+template <typename K>
+int resident_blocks(K kernel) {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess ||
+        per_cu < 1)
+      per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+      cus = 256;
+    cached[dev] = per_cu * cus;
+  }
+  return cached[dev];
+}
+
+template <typename T, int D, int ROWS, bool DEBUG, bool UNIFORM>
+hipError_t launch_mode(const LaunchParams &p, int row_blocks, hipStream_t stream) {
+  auto kernel = decode_kernel<T, D, ROWS, DEBUG, UNIFORM>;
+  dim3 grid(p.Hkv * row_blocks, p.B, p.num_splits);
+  if (p.counters) {
+    const long items = (long)p.Hkv * row_blocks * p.B * p.num_splits;  // upper bound
+    const long ctas = resident_blocks(kernel);
+    grid = dim3((unsigned)(items < ctas ? items : ctas), 1, 1);
+  }
+  hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, p, row_blocks);
+  return hipGetLastError();
+}
+
 template <typename T, int D, int ROWS>
 hipError_t launch_typed(const LaunchParams &p, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
   const int row_blocks = (G * p.L + ROWS - 1) / ROWS;
-  dim3 grid(p.Hkv * row_blocks, p.B, p.num_splits);
+  constexpr int kStep = 4 * 64 / (D / (16 / (int)sizeof(T)));  // keys per wave step
+  const bool uniform = p.ps % kStep == 0;
   const bool debug = p.dbg_trace != nullptr || p.dbg_visits != nullptr;
-  if (debug) {
-    hipLaunchKernelGGL((decode_kernel<T, D, ROWS, true>), grid, dim3(256), 0, stream, p, row_blocks);
-  } else {
-    hipLaunchKernelGGL((decode_kernel<T, D, ROWS, false>), grid, dim3(256), 0, stream, p, row_blocks);
-  }
-  return hipGetLastError();
+  if (debug)
+    return uniform ? launch_mode<T, D, ROWS, true, true>(p, row_blocks, stream)
+                   : launch_mode<T, D, ROWS, true, false>(p, row_blocks, stream);
+  return uniform ? launch_mode<T, D, ROWS, false, true>(p, row_blocks, stream)
+                 : launch_mode<T, D, ROWS, false, false>(p, row_blocks, stream);
 }
 
 template <typename T, int D>

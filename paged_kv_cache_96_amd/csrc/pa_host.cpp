@@ -50,6 +50,8 @@ pa_status check_pointers(const pa_args *a) {
 pa_status check_workspace(const pa_args *a, const pa_workspace *ws, int32_t *S, int32_t *P) {
   const int32_t cap = a->max_pages * a->page_size;
   if (!ws || ws->num_splits == 1) {
+    if (ws && ws->counters && (reinterpret_cast<uintptr_t>(ws->counters) & 7u))
+      return PA_ERR_WORKSPACE;
     *S = 1;
     *P = cap;
     return PA_OK;
@@ -61,6 +63,7 @@ pa_status check_workspace(const pa_args *a, const pa_workspace *ws, int32_t *S, 
   if (!ws->partial_out || !ws->partial_lse || !aligned16(ws->partial_out) ||
       !aligned16(ws->partial_lse))
     return PA_ERR_WORKSPACE;
+  if (ws->counters && (reinterpret_cast<uintptr_t>(ws->counters) & 7u)) return PA_ERR_WORKSPACE;
   *S = ws->num_splits;
   *P = ws->partition_tokens;
   return PA_OK;
@@ -80,6 +83,7 @@ pa::LaunchParams make_params(const pa_args *a, int32_t S, int32_t P, const pa_wo
   p.ws_lse = (S > 1 && ws) ? ws->partial_lse : nullptr;
   p.dbg_trace = a->debug_trace;
   p.dbg_visits = a->debug_visits;
+  p.counters = (ws && a->batch <= pa::kDecodeQueueMaxBatch) ? ws->counters : nullptr;
   p.B = a->batch;
   p.Hq = a->num_q_heads;
   p.Hkv = a->num_kv_heads;
@@ -154,7 +158,7 @@ PA_EXPORT pa_status pa_decode_plan(const pa_args *args, int32_t num_cus, pa_work
   if (workspace_bytes) {
     const size_t rows =
         (size_t)(args->batch > 0 ? args->batch : 0) * args->num_q_heads * args->q_len;
-    *workspace_bytes = S > 1 ? rows * S * (args->head_dim + 1) * sizeof(float) : 0;
+    *workspace_bytes = (S > 1 ? rows * S * (args->head_dim + 1) * sizeof(float) : 0) + 256;
   }
   return PA_OK;
 }

@@ -20,6 +20,7 @@ struct LaunchParams {
   float *ws_lse;            // [B, Hq, L, S]   fp32
   int32_t *dbg_trace;       // nullptr unless instrumented
   int32_t *dbg_visits;      // nullptr unless instrumented
+  uint32_t *counters;       // decode work-queue counters [2], or nullptr (plain grid)
   int32_t B, Hq, Hkv, L, D, num_pages, ps, max_pages;
   int32_t causal;
   int32_t num_splits;       // S >= 1
@@ -35,6 +36,10 @@ hipError_t launch_decode(const LaunchParams &p, DType dt, hipStream_t stream);
 hipError_t launch_split_reduce(const LaunchParams &p, DType dt, hipStream_t stream);
 // bf16 MFMA prefill kernel.
 hipError_t launch_prefill_mfma(const LaunchParams &p, hipStream_t stream);
+
+// Largest batch the persistent decode schedule supports (its per-request
+// partition counts live in LDS); larger batches use the plain grid.
+constexpr int kDecodeQueueMaxBatch = 2048;
 
 // Query rows one decode workgroup holds, for a GQA group of `rows_per_head`
 // packed rows (G * L).  Shared by the host (grid sizing) and the launcher.

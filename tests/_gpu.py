@@ -44,7 +44,8 @@ class DeviceInputs:
         return torch.full_like(self.q, float("nan"))
 
 
-def run_decode(api, d: DeviceInputs, *, partition_tokens=0, trace=False, keep_ws=False):
+def run_decode(api, d: DeviceInputs, *, partition_tokens=0, trace=False, keep_ws=False,
+               queue=True):
     """pa_decode (+ pa_split_reduce) through the C ABI.  Returns (out, extras)."""
     out = d.out()
     x = d.x
@@ -57,7 +58,7 @@ def run_decode(api, d: DeviceInputs, *, partition_tokens=0, trace=False, keep_ws
     args = api.make_args(d.q, d.kp, d.vp, d.bt, d.cl, out, scale=x.scale, mask=d.mask,
                          query_lens=d.ql, debug_trace=dbg_t, debug_visits=dbg_v)
     S, P, nbytes = api.pa_decode_plan(args, partition_tokens=partition_tokens)
-    ws = api.Workspace(x.B, x.H_q, x.L, x.D, S, P, d.q.device)
+    ws = api.Workspace(x.B, x.H_q, x.L, x.D, S, P, d.q.device, queue=queue)
     api.pa_decode(args, ws)
     if keep_ws and S > 1:
         torch.cuda.synchronize()

@@ -113,6 +113,8 @@ def test_workspace_validation(L):
     assert _decode(L, a, ws) == -3
     ws.num_splits = 0
     assert _decode(L, a, ws) == -3
+    ws.num_splits, ws.partial_lse, ws.counters = 4, h.p, h.p + 4   # counters not 8-byte aligned
+    assert _decode(L, a, ws) == -3
     assert L.pa_split_reduce(ctypes.byref(a), ctypes.byref(ws), None) == -3
 
 
@@ -144,7 +146,7 @@ def test_plan_covers_capacity_and_sizes_workspace(L):
     a = h.args(batch=64, num_q_heads=32, num_kv_heads=8, max_pages=256, num_pages=20000)
     rc, S, P, nb = _plan(L, a)
     assert rc == 0 and P % 16 == 0 and S * P >= 4096 and S > 1
-    assert nb == 64 * 32 * 1 * S * (128 + 1) * 4
+    assert nb == 64 * 32 * 1 * S * (128 + 1) * 4 + 256
     # long contexts: 8 requests x 8 kv heads up to 131072 keys -> many partitions
     a = h.args(batch=8, num_q_heads=32, num_kv_heads=8, max_pages=8192, num_pages=50000)
     rc, S, P, nb = _plan(L, a)
@@ -154,6 +156,6 @@ def test_plan_covers_capacity_and_sizes_workspace(L):
     assert (rc, P, S) == (0, 1008, -(-131072 // 1008))
     # a single partition needs no workspace
     rc, S, P, nb = _plan(L, h.args(max_pages=4), P=64)
-    assert (rc, S, nb) == (0, 1, 0)
+    assert (rc, S, nb) == (0, 1, 256)
     # decode plans only exist for L <= 8
     assert _plan(L, h.args(q_len=9))[0] == -1

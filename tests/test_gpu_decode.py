@@ -181,3 +181,27 @@ def test_c4_long_context_parity_sampled(api):
     ref = oracle.attention_of(sub)       # requests 0 and 1, every head
     err = assert_parity(g, ref, "bf16", "C4 sample")
     print(f"[C4] max abs err (requests 0-1) {err:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("P", [0, 64, 4096])
+def test_queue_and_grid_schedules_agree_and_reset_counters(api, P):
+    """The persistent work queue and the plain grid run the same items: the
+    outputs are bit-identical, and the queue leaves its counters at zero."""
+    import torch
+    x = make_random(71, B=9, H_q=16, H_kv=4, L=1, D=128, page_size=16,
+                    ctx=[0, 1, 16, 63, 64, 65, 700, 1500, 4000], dtype="bf16", causal=False)
+    d = DeviceInputs(x)
+    a, exa = run_decode(api, d, partition_tokens=P, queue=True)
+    b, exb = run_decode(api, d, partition_tokens=P, queue=False)
+    assert np.array_equal(host_f64(a), host_f64(b))
+    assert int(exa["ws"].counters.abs().sum()) == 0
+    assert_parity(a, oracle.attention_of(x), "bf16", f"queue P={P}")
+    # run the same workspace again: counters were reset by the previous call
+    args = exa["args"]
+    out2 = torch.full_like(d.q, float("nan"))
+    args.out = out2.data_ptr()
+    api.pa_decode(args, exa["ws"])
+    if exa["S"] > 1:
+        api.pa_split_reduce(args, exa["ws"])
+    torch.cuda.synchronize()
+    assert np.array_equal(host_f64(out2), host_f64(a))
