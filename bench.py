@@ -159,7 +159,7 @@ def _counters(name, sha):
 
 
 # --------------------------------------------------------------- cpu oracle
-def cpu_baseline(x, kv_bytes, min_seconds=10.0, max_runs=5):
+def cpu_baseline(x, kv_bytes, min_seconds=10.0, max_runs=2000):
     import oracle
     oracle.load()
     times, threads = [], 0
@@ -184,6 +184,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (3 times): the known "
+                         "byte count that scales the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -191,10 +194,20 @@ def main():
         sys.exit(2)
 
     import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        n = (1 << 30) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30}))
+        return
+
     from paged_kv_cache_96_amd import api
     import workloads as W
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
     only = set(args.only.split(","))
     run = Runner(torch, api, flush=not args.no_flush)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
