@@ -76,6 +76,24 @@ constexpr int kDppHalfMirror = 0x141; // lane i of an 8-lane half row <- lane 7-
 constexpr int kDppMirror = 0x140;     // lane i of a 16-lane row <- lane 15-i
 constexpr int kDppRor8 = 0x128;       // lane i of a 16-lane row <- lane (i+8)%16
 
+// Values of the lane pair {l, l ^ 16} (permlane16 swap) and {l, l ^ 32}
+// (permlane32 swap), lower lane first in every lane of the pair; VALU only,
+// no LDS crossbar.
+__device__ __forceinline__ void pair16(float x, float &lo, float &hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair32(float x, float &lo, float &hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum16(float x) { float a, b; pair16(x, a, b); return a + b; }
+__device__ __forceinline__ float sum32(float x) { float a, b; pair32(x, a, b); return a + b; }
+__device__ __forceinline__ float max16(float x) { float a, b; pair16(x, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float max32(float x) { float a, b; pair32(x, a, b); return fmaxf(a, b); }
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
@@ -91,8 +109,21 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (N >= 4) x += dpp<kDppXor2>(x);
   if constexpr (N >= 8) x += dpp<kDppHalfMirror>(x);
   if constexpr (N >= 16) x += dpp<kDppMirror>(x);
-  if constexpr (N >= 32) x += __shfl_xor(x, 16);
-  if constexpr (N >= 64) x += __shfl_xor(x, 32);
+  if constexpr (N >= 32) x = sum16(x);
+  if constexpr (N >= 64) x = sum32(x);
+  return x;
+}
+
+// Max over aligned groups of N consecutive lanes (every lane gets it).
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "N");
+  if constexpr (N >= 2) x = fmaxf(x, dpp<kDppXor1>(x));
+  if constexpr (N >= 4) x = fmaxf(x, dpp<kDppXor2>(x));
+  if constexpr (N >= 8) x = fmaxf(x, dpp<kDppHalfMirror>(x));
+  if constexpr (N >= 16) x = fmaxf(x, dpp<kDppMirror>(x));
+  if constexpr (N >= 32) x = max16(x);
+  if constexpr (N >= 64) x = max32(x);
   return x;
 }
 
@@ -102,15 +133,15 @@ __device__ __forceinline__ float group_sum(float x) {
 template <int STRIDE>
 __device__ __forceinline__ float stride_sum(float x) {
   if constexpr (STRIDE <= 8) x += dpp<kDppRor8>(x);
-  if constexpr (STRIDE <= 16) x += __shfl_xor(x, 16);
-  if constexpr (STRIDE <= 32) x += __shfl_xor(x, 32);
+  if constexpr (STRIDE <= 16) x = sum16(x);
+  if constexpr (STRIDE <= 32) x = sum32(x);
   return x;
 }
 template <int STRIDE>
 __device__ __forceinline__ float stride_max(float x) {
   if constexpr (STRIDE <= 8) x = fmaxf(x, dpp<kDppRor8>(x));
-  if constexpr (STRIDE <= 16) x = fmaxf(x, __shfl_xor(x, 16));
-  if constexpr (STRIDE <= 32) x = fmaxf(x, __shfl_xor(x, 32));
+  if constexpr (STRIDE <= 16) x = max16(x);
+  if constexpr (STRIDE <= 32) x = max32(x);
   return x;
 }
 

@@ -490,6 +490,8 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
   __shared__ int s_full[kSchedMaxB + 1];     // exclusive prefix of full partitions
   __shared__ int s_part[kSchedMaxB + 1];     // exclusive prefix of partial ones
   __shared__ int s_next[2];
+  __shared__ int s_ctx[kSchedMaxB];          // context_lens, read once per workgroup
+  __shared__ int s_qlen[kSchedMaxB];         // query_lens (or L)
   const int B = p.B;
   const int P = p.part_tokens;
   const int tid = threadIdx.x;
@@ -500,6 +502,8 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
     const int b = tid * per + k;
     if (b < B) {
       const int ctx = p.cl[b];
+      s_ctx[b] = ctx;
+      s_qlen[b] = p.ql ? p.ql[b] : p.L;
       const int f = ctx / P;
       const int q = (ctx % P != 0 || ctx == 0) ? 1 : 0;  // context 0 still gets one item
       s_full[b] = f;
@@ -573,8 +577,8 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
     }
     const int g = u / row_blocks;
     const int rb = u - g * row_blocks;
-    const int ctx = p.cl[b];
-    const int Lb = p.ql ? p.ql[b] : p.L;
+    const int ctx = s_ctx[b];
+    const int Lb = s_qlen[b];
     decode_item<T, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, s, ctx, Lb, sm_acc, sm_m, sm_l);
     parity ^= 1;
     if (tid == 0) s_next[parity] = nxt;

@@ -29,8 +29,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(LaunchParams p, int t
   const float *po = p.ws_o + (size_t)row * S * D;
   float M = kNegInf;
   for (int s = lane; s < n; s += 64) M = fmaxf(M, lse[s]);
-#pragma unroll
-  for (int k = 1; k < 64; k <<= 1) M = fmaxf(M, __shfl_xor(M, k));
+  M = group_max<64>(M);
 
   float o[kPer];
 #pragma unroll
