@@ -79,14 +79,15 @@ class Runner:
         from tests._gpu import DeviceInputs
         return DeviceInputs(x, pages=pages)
 
-    def time_decode(self, d, steps, warmup, partition_tokens=0):
+    def time_decode(self, d, steps, warmup, partition_tokens=0, num_cus=0):
         torch, api = self.torch, self.api
         x = d.x
         out = torch.empty_like(d.q)
         args = api.make_args(d.q, d.kp, d.vp, d.bt, d.cl, out, scale=x.scale, mask=d.mask,
                              query_lens=d.ql)
-        S, P, _ = api.pa_decode_plan(args, partition_tokens=partition_tokens)
-        ws = api.Workspace(x.B, x.H_q, x.L, x.D, S, P, d.q.device)
+        plan = api.pa_decode_plan(args, partition_tokens=partition_tokens, num_cus=num_cus)
+        S, P = plan.num_splits, plan.partition_tokens
+        ws = api.Workspace.for_plan(plan, d.q)
         for _ in range(warmup):
             self.flush()
             api.pa_decode(args, ws)
@@ -107,7 +108,8 @@ class Runner:
         wall = time.perf_counter() - t0
         dec = np.array([e[0].elapsed_time(e[1]) for e in ev])    # ms
         red = np.array([e[1].elapsed_time(e[2]) for e in ev])
-        return {"S": S, "P": P, "decode_ms": dec, "reduce_ms": red, "step_ms": dec + red,
+        return {"S": S, "P": P, "schedule": "balanced" if plan.schedule == api.SCHEDULE_BALANCED
+                else "partitions", "decode_ms": dec, "reduce_ms": red, "step_ms": dec + red,
                 "wall_s": wall, "out": out}
 
     def time_prefill(self, d, steps, warmup, flush=False):
@@ -225,7 +227,7 @@ def main():
     sha_dec = _source_sha("pa_decode.hip", "pa_common.hpp")
     traffic = _counters("decode_c2", sha_dec)
     log(f"[bench] decode C2: step {step_ms * 1e3:.1f} us (decode {dec_ms * 1e3:.1f} us), "
-        f"{value:.0f} GB/s, S={r2['S']} P={r2['P']}")
+        f"{value:.0f} GB/s, {r2['schedule']} S={r2['S']} P={r2['P']}")
     result = {
         "metric": "decode K/V HBM GB/s (% of peak) + prefill TFLOP/s (% MFMA peak), 1 MI355X",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -233,7 +235,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "GQA decode bf16 B64 Hq32 Hkv8 D128 L1 page16 ctx U[128,4096] seed2",
                    "B": x2.B, "H_q": x2.H_q, "H_kv": x2.H_kv, "D": x2.D, "page_size": 16,
-                   "num_splits": r2["S"], "partition_tokens": r2["P"],
+                   "schedule": r2["schedule"], "num_splits": r2["S"], "partition_tokens": r2["P"],
                    "llc_flushed": not args.no_flush, "kv_bytes_per_step": kv2},
         "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -289,7 +291,8 @@ def main():
         log(f"[bench] decode C4: {sm * 1e3:.1f} us, {kv4 / sm / 1e6:.0f} GB/s, S={r4['S']}")
         sections["decode_C4"] = {
             "workload": "long-context decode bf16 B8 Hq32 Hkv8 D128 page16 ctx U[32768,131072] seed4",
-            "kv_bytes": kv4, "gbs_step": round(kv4 / sm / 1e6, 2), "num_splits": r4["S"],
+            "kv_bytes": kv4, "gbs_step": round(kv4 / sm / 1e6, 2), "schedule": r4["schedule"],
+            "num_splits": r4["S"],
             "partition_tokens": r4["P"], **_stats(r4["step_ms"]),
             "roofline": {"bound": "hbm", "kernel": "decode_kernel",
                          "achieved": round(kv4 / dm / 1e6, 2), "peak": HBM_PEAK_GBS,

@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 1
+#define PA_ABI_VERSION 2
 
 typedef enum {
   PA_OK = 0,
@@ -104,56 +104,74 @@ typedef struct pa_args {
   int32_t *debug_visits;
 } pa_args;
 
-/* Split-KV workspace of the decode path ("Reading vLLM's PagedAttention
- * Kernel", section 3.3: a long context is cut into partitions computed in
- * parallel and combined afterwards).  Partition s covers keys
- * [s * partition_tokens, min((s + 1) * partition_tokens, context_len)).
- *   partial_out  fp32 [B, H_q, L, num_splits, D]  normalised partition outputs
- *   partial_lse  fp32 [B, H_q, L, num_splits]     natural-log log-sum-exp of
- *                                                 the scaled scores (-inf: empty)
- * Both are caller-owned device memory of the size pa_decode_plan reports.
- * With num_splits == 1 the buffers may be NULL and pa_decode writes `out`.
- *
- *   counters     uint32 [2] or NULL: work-queue counters.  When given (and
- *                B <= 2048), pa_decode runs as a persistent kernel whose
- *                workgroups pull (request, partition, kv head) items from a
- *                queue, which keeps every compute unit busy on ragged
- *                batches; NULL launches one workgroup per item instead.  The
- *                caller zeroes them once before first use; every call leaves
- *                them zero again.  Calls that share one counter pair must not
- *                overlap in time (same stream, or synchronised). */
+/* How pa_decode divides a call's keys among the waves of the GPU. */
+typedef enum pa_schedule {
+  /* Fixed partitions ("Reading vLLM's PagedAttention Kernel", section 3.3:
+   * a long context is cut into partitions computed in parallel and combined
+   * afterwards).  Partition s covers keys
+   * [s * partition_tokens, min((s + 1) * partition_tokens, context_len)) of
+   * every (request, kv head, row block); one wave walks each.  num_splits ==
+   * 1 is the single-pass decode (no workspace needed). */
+  PA_SCHEDULE_PARTITIONS = 0,
+  /* Equal work per wave: the keys of every (request, kv head, row block),
+   * in steps of STEP keys (16 for bf16 with head_dim 128; 4096 / (head_dim *
+   * element bytes) in general), are laid out request-major and cut into one
+   * contiguous run per wave of a grid that fills the GPU, so ragged context
+   * lengths cost no idle waves.  A row block is R query rows of one kv head
+   * (R = 1, 2, 4 or 8: the smallest that holds G * L, at most 8), and a
+   * request has U = H_kv * ceil(G * L / R) of them.  Row block r of the call
+   * (r = b * U + u) walked in part by wave w leaves its partial state in
+   * piece slot r + w; one walked by a single wave is written to `out`
+   * directly.  num_splits is the number of piece slots: at least B * U + 1
+   * (the library uses at most num_splits - B * U waves), and batch <= 2048. */
+  PA_SCHEDULE_BALANCED = 1
+} pa_schedule;
+
+/* Split-KV workspace of the decode path: normalised partial outputs and the
+ * natural-log log-sum-exp of their scaled scores (-inf: no visible key),
+ *   partitions:  partial_out fp32 [B, H_q, L, num_splits, D],
+ *                partial_lse fp32 [B, H_q, L, num_splits];
+ *   balanced:    partial_out fp32 [num_splits, R, D],
+ *                partial_lse fp32 [num_splits, R].
+ * Both are caller-owned device memory of the size pa_decode_plan reports;
+ * pa_decode overwrites them and pa_split_reduce reads them, so calls that
+ * share one workspace must not overlap in time (same stream, or
+ * synchronised).  With schedule == PA_SCHEDULE_PARTITIONS and num_splits ==
+ * 1 the buffers may be NULL and pa_decode writes `out`. */
 typedef struct pa_workspace {
   float *partial_out;
   float *partial_lse;
-  int32_t num_splits;        /* >= 1 */
-  int32_t partition_tokens;  /* > 0, a multiple of page_size */
-  uint32_t *counters;
+  int32_t num_splits;        /* partitions (>= 1), or piece slots (balanced) */
+  int32_t partition_tokens;  /* partitions: > 0, a multiple of page_size; balanced: ignored */
+  int32_t schedule;          /* pa_schedule */
+  int32_t reserved;          /* 0 */
 } pa_workspace;
 
-/* Choose the split plan of pa_decode for `args` (only the sizes in `args`
- * are read; no pointer is dereferenced and nothing runs on the GPU).
- * On input plan->partition_tokens > 0 requests that partition size (rounded
- * up to a multiple of page_size); 0 lets the library choose from the maximum
- * context max_pages * page_size and `num_cus` (0: 256, the MI355X CU count).
- * On return plan->num_splits and plan->partition_tokens are set, the buffer
- * pointers are left untouched, and *workspace_bytes (if not NULL) is the
- * total size of partial_out plus partial_lse (0 when num_splits == 1) plus
- * 256 bytes for the counters. */
+/* Choose the plan of pa_decode for `args` (only the sizes in `args` are
+ * read; no pointer is dereferenced and nothing runs on the GPU).
+ * On input plan->partition_tokens > 0 requests the partition schedule with
+ * that partition size (rounded up to a multiple of page_size); 0 lets the
+ * library choose: the balanced schedule when batch <= 2048, sized for
+ * `num_cus` compute units (0: 256, the MI355X count), else partitions
+ * chosen from the maximum context max_pages * page_size.
+ * On return plan->schedule, num_splits and partition_tokens are set, the
+ * buffer pointers are left untouched, and *workspace_bytes (if not NULL) is
+ * the total size of partial_out plus partial_lse (0 when no split). */
 pa_status pa_decode_plan(const pa_args *args, int32_t num_cus, pa_workspace *plan,
                          size_t *workspace_bytes);
 
-/* Decode: query rows L <= 8 (one-token decode and short chunks).  Each
- * workgroup owns one (request, kv head, row block, partition) and walks the
- * partition's pages with the G * L query rows of that kv head held in
- * registers, so every K/V byte is read once per row block.  num_splits == 1
- * writes `out`; num_splits > 1 writes the workspace, and pa_split_reduce
- * must follow on the same stream. */
+/* Decode: query rows L <= 8 (one-token decode and short chunks).  A wave
+ * walks the pages of one (request, kv head, row block) at a time with the
+ * G * L query rows of that kv head held in registers, so every K/V byte is
+ * read once per row block.  A single-pass plan writes `out`; otherwise
+ * pa_split_reduce must follow on the same stream. */
 pa_status pa_decode(const pa_args *args, const pa_workspace *ws, void *stream);
 
-/* Log-sum-exp merge of the partition states pa_decode left in `ws` into
+/* Log-sum-exp merge of the partial states pa_decode left in `ws` into
  * `out`: M = max_s lse_s, out = sum_s exp(lse_s - M) o_s / sum_s exp(lse_s - M),
- * over the partitions s < ceil(context_lens[b] / partition_tokens); rows with
- * no visible key get zeros.  `args` must be the arguments of that pa_decode. */
+ * over the partitions s < ceil(context_lens[b] / partition_tokens), or over
+ * the pieces of the balanced schedule; rows with no visible key get zeros.
+ * `args` and `ws` must be those of that pa_decode. */
 pa_status pa_split_reduce(const pa_args *args, const pa_workspace *ws, void *stream);
 
 /* Prefill: any L >= 1 (chunked prefill after a cached prefix).  bf16 runs on

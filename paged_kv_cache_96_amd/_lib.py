@@ -57,8 +57,15 @@ class PaWorkspace(ctypes.Structure):
         ("partial_lse", ctypes.c_void_p),
         ("num_splits", ctypes.c_int32),
         ("partition_tokens", ctypes.c_int32),
-        ("counters", ctypes.c_void_p),
+        ("schedule", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
+
+
+ABI_VERSION = 2  # PA_ABI_VERSION of the structs below
+
+SCHEDULE_PARTITIONS = 0
+SCHEDULE_BALANCED = 1
 
 
 class PaError(RuntimeError):
@@ -92,6 +99,9 @@ def lib() -> ctypes.CDLL:
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_abi_version.argtypes = []
     L.pa_abi_version.restype = ctypes.c_int32
+    if L.pa_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {L.pa_abi_version()}, this binding "
+                          f"expects {ABI_VERSION}; rebuild it")
     _lib = L
     return L
 

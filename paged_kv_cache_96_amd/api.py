@@ -9,12 +9,12 @@ from __future__ import annotations
 
 import ctypes
 import math
-from typing import Optional, Tuple
+from typing import NamedTuple, Optional
 
 import torch
 
 from . import _lib
-from ._lib import PaArgs, PaWorkspace
+from ._lib import PaArgs, PaWorkspace, SCHEDULE_BALANCED, SCHEDULE_PARTITIONS  # noqa: F401
 
 _DTYPES = {torch.float32: _lib.PA_DTYPE_F32, torch.bfloat16: _lib.PA_DTYPE_BF16}
 _MASKS = {"none": _lib.PA_MASK_NONE, None: _lib.PA_MASK_NONE, "causal": _lib.PA_MASK_CAUSAL}
@@ -76,30 +76,46 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def pa_decode_plan(args: PaArgs, *, num_cus: int = 0, partition_tokens: int = 0) -> Tuple[int, int, int]:
-    """(num_splits, partition_tokens, workspace_bytes) chosen by the library."""
+class DecodePlan(NamedTuple):
+    """What pa_decode_plan chose: the schedule (SCHEDULE_PARTITIONS or
+    SCHEDULE_BALANCED), partial states per row block, the partition size
+    (partition schedule only) and the workspace size in bytes."""
+    num_splits: int
+    partition_tokens: int
+    workspace_bytes: int
+    schedule: int
+
+
+def pa_decode_plan(args: PaArgs, *, num_cus: int = 0, partition_tokens: int = 0) -> DecodePlan:
+    """The library's plan for `args`; partition_tokens > 0 asks for the
+    partition schedule with that partition size."""
     ws = PaWorkspace()
     ws.partition_tokens = int(partition_tokens)
     nbytes = ctypes.c_size_t(0)
     _lib.check("pa_decode_plan", _lib.lib().pa_decode_plan(ctypes.byref(args), int(num_cus),
                                                             ctypes.byref(ws), ctypes.byref(nbytes)))
-    return ws.num_splits, ws.partition_tokens, nbytes.value
+    return DecodePlan(ws.num_splits, ws.partition_tokens, nbytes.value, ws.schedule)
 
 
 class Workspace:
-    """Device buffers of a split plan (torch owns the memory)."""
+    """Device buffers of a decode plan (torch owns the memory).  Partition
+    schedule: states [B, H_q, L, num_splits(, D)]; balanced schedule:
+    `block_rows` states per piece slot, [num_splits, block_rows(, D)]."""
 
     def __init__(self, B: int, Hq: int, L: int, D: int, num_splits: int, partition_tokens: int,
-                 device, queue: bool = True):
+                 device, schedule: int = SCHEDULE_PARTITIONS, block_rows: int = 0):
         self.num_splits = int(num_splits)
-        # work-queue counters: zeroed once here, left zero by every call
-        self.counters = torch.zeros(64, dtype=torch.int32, device=device) if queue else None
+        self.schedule = int(schedule)
         self.partition_tokens = int(partition_tokens)
         if self.num_splits > 1:
-            self.partial_out = torch.empty((B, Hq, L, num_splits, D), dtype=torch.float32,
-                                           device=device)
-            self.partial_lse = torch.empty((B, Hq, L, num_splits), dtype=torch.float32,
-                                           device=device)
+            if self.schedule == SCHEDULE_BALANCED:
+                if block_rows < 1:
+                    raise ValueError("the balanced schedule needs block_rows")
+                lead = (self.num_splits, int(block_rows))
+            else:
+                lead = (B, Hq, L, self.num_splits)
+            self.partial_out = torch.empty(lead + (D,), dtype=torch.float32, device=device)
+            self.partial_lse = torch.empty(lead, dtype=torch.float32, device=device)
         else:
             self.partial_out = self.partial_lse = None
         self.c = PaWorkspace()
@@ -107,7 +123,16 @@ class Workspace:
         self.c.partial_lse = _ptr(self.partial_lse)
         self.c.num_splits = self.num_splits
         self.c.partition_tokens = self.partition_tokens
-        self.c.counters = _ptr(self.counters)
+        self.c.schedule = self.schedule
+
+    @classmethod
+    def for_plan(cls, plan: DecodePlan, query: torch.Tensor) -> "Workspace":
+        B, Hq, L, D = query.shape
+        rows = 0
+        if plan.schedule == SCHEDULE_BALANCED and plan.num_splits > 1:
+            rows = plan.workspace_bytes // (plan.num_splits * (D + 1) * 4)
+        return cls(B, Hq, L, D, plan.num_splits, plan.partition_tokens, query.device,
+                   schedule=plan.schedule, block_rows=rows)
 
 
 def pa_decode(args: PaArgs, workspace: Optional[Workspace] = None, stream=None) -> None:
@@ -136,11 +161,10 @@ def paged_attention(query: torch.Tensor, key_pages: torch.Tensor, value_pages: t
     args = make_args(query, key_pages, value_pages, block_table, context_lens, out, scale=scale,
                      mask=mask, query_lens=query_lens)
     if query.shape[2] <= 8:
-        S, P, _ = pa_decode_plan(args, partition_tokens=partition_tokens)
-        ws = Workspace(query.shape[0], query.shape[1], query.shape[2], query.shape[3], S, P,
-                       query.device)
+        plan = pa_decode_plan(args, partition_tokens=partition_tokens)
+        ws = Workspace.for_plan(plan, query)
         pa_decode(args, ws, stream)
-        if S > 1:
+        if plan.num_splits > 1:
             pa_split_reduce(args, ws, stream)
         out._pa_workspace = ws  # keep the buffers alive until the caller is done
     else:

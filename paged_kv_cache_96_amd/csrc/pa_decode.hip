@@ -7,11 +7,12 @@
 // operations; "Reading vLLM's PagedAttention Kernel" section 3.3: split long
 // contexts into partitions that are merged afterwards):
 //
-//   grid  = (kv head g x row block, request b, partition s), 256 threads.
-//   A workgroup owns the ROWS packed query rows (row rho -> position
-//   rho / G, head g*G + rho % G) of one kv head, so each K/V byte of the
-//   partition is read once for all of them.  Its 4 waves take interleaved
-//   steps of STEP keys.  In a step every lane issues 16-byte loads: LPT
+//   Work item = partition s of the ROWS packed query rows (row rho ->
+//   position rho / G, head g*G + rho % G) of kv head g of request b; one
+//   wave owns an item, so each K/V byte of the partition is read once for
+//   all of those rows, and the waves of a workgroup run independently (no
+//   barrier or LDS merge per item).  The wave walks the partition in steps
+//   of STEP keys.  In a step every lane issues 16-byte loads: LPT
 //   lanes cover one key's D elements and a wave load covers TPL keys, so the
 //   loads of a page are fully coalesced.  K/V are read exactly once, with
 //   non-temporal loads.
@@ -31,9 +32,9 @@
 //   the LPT lanes with DPP; scores are kept in base-2 units.  For bf16 the
 //   PV product runs on bf16 dot2 instructions with the weights rounded to
 //   bf16 (two keys per instruction), and the row sums add those same rounded
-//   weights.  At the end the groups and then the
-//   waves are merged and the partition state is written (normalised output
-//   plus log-sum-exp), or the final output when there is one partition.
+//   weights.  At the end the lane groups are merged in registers and the
+//   partition state is written (normalised output plus log-sum-exp), or the
+//   final output when there is one partition.
 #include <type_traits>
 
 #include "pa_common.hpp"
@@ -89,31 +90,29 @@ __device__ __forceinline__ uint32_t word(const Vec &v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// One work item: partition s of the ROWS-row block rb of kv head g of
-// request b.  Walks the partition, merges the waves through LDS and writes
-// the partition state (or the output when there is one partition).
+// One work item, walked by the calling wave alone: keys [t0, tend) of the
+// ROWS-row block rb of kv head g of request b (t0 a multiple of STEP).
+// With `split` it writes the state of that piece to the workspace (slot
+// `slot` of each row under partitions, piece slot `piece` when piece >= 0),
+// otherwise the piece is the whole row range and it writes the output.
 template <typename T, int D, int ROWS, bool DEBUG, bool UNIFORM>
-__device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g, int rb, int s,
-                                            int ctx, int Lb, float (*sm_acc)[ROWS][D],
-                                            float (*sm_m)[ROWS], float (*sm_l)[ROWS]) {
+__device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g, int rb, int t0,
+                                            int tend, int slot, long long piece, bool split,
+                                            int ctx, int Lb) {
   constexpr int kElems = Elem<T>::kPerVec;
   constexpr int kLpt = D / kElems;      // lanes per key
   constexpr int kTpl = 64 / kLpt;       // keys per wave load
   constexpr int kLoads = 4;             // loads in flight per step (each of K and V)
   constexpr int kStep = kTpl * kLoads;  // keys per wave step
-  constexpr int kWaves = 4;
   constexpr bool kBf16 = sizeof(T) == 2;
   static_assert(kLpt * kElems == D && kTpl * kLpt == 64, "layout");
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int c = lane % kLpt;            // element chunk of this lane
   const int kl = lane / kLpt;           // key of this lane within a load
 
   const int G = p.Hq / p.Hkv;
-  const int t0 = s * p.part_tokens;
   const int ps = p.ps;
   const int32_t *bt = p.bt + (size_t)b * p.max_pages;
-  const bool split = p.num_splits > 1;
 
   // ---- rows of this workgroup
   int hi[ROWS];
@@ -131,7 +130,7 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
     kmax = max(kmax, hi[r]);
     if (valid[r]) kmin = min(kmin, hi[r]);
   }
-  const int t1 = split ? min(t0 + p.part_tokens, kmax) : kmax;
+  const int t1 = min(tend, kmax);
   // the row block holding the last packed row of the request counts visits
   const bool counts = DEBUG && Lb > 0 && ((Lb * G - 1) / ROWS == rb);
 
@@ -158,7 +157,7 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
   const T *kp = reinterpret_cast<const T *>(p.kp);
   const T *vp = reinterpret_cast<const T *>(p.vp);
   const int nsteps = t1 > t0 ? (t1 - t0 + kStep - 1) / kStep : 0;
-  const int nw = nsteps > wave ? (nsteps - wave + kWaves - 1) / kWaves : 0;  // this wave's steps
+  const int nw = nsteps;  // steps of this wave
   const int tmin = min(t1, kmin);  // keys below this are visible to every valid row
   const size_t head_stride = (size_t)ps * D;
   const uint32_t lane_off = (uint32_t)(kl * D + c * kElems);
@@ -168,7 +167,7 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
   auto resolve = [&](int k0) {
     const int k = k0 + lane;
     if (k < nw) {
-      const int base = t0 + (wave + kWaves * k) * kStep;
+      const int base = t0 + k * kStep;
       const int lp = base / ps;
       const int page = bt[lp];
       const size_t off = ((size_t)page * p.Hkv + g) * head_stride + (size_t)(base - lp * ps) * D;
@@ -177,7 +176,7 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
     }
   };
 
-  // Element offset of key n*TPL + kl of step (wave-step k, global step st).
+  // Element offset of key n*TPL + kl of step k (st == k).
   auto key_offset = [&](int k, int st, int n, int &page, int &slot) -> size_t {
     if constexpr (UNIFORM) {
       const uint32_t lo = __builtin_amdgcn_readlane(off_lo, k & 63);
@@ -199,7 +198,7 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
   };
 
   auto load_step = [&](int k, Vec (&kv)[kLoads], Vec (&vv)[kLoads]) {
-    const int st = wave + kWaves * k;
+    const int st = k;
 #pragma unroll
     for (int n = 0; n < kLoads; ++n) {
       int page = 0, slot = 0;
@@ -245,7 +244,7 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
       kv[n] = load_stream_buf(rk, boff);
       vv[n] = load_stream_buf(rv, boff);
       if constexpr (DEBUG) {
-        const int st = wave + kWaves * k;
+        const int st = k;
         const int j = t0 + st * kStep + n * kTpl + kl;
         if (ok && counts && c == 0 && j < t1) {
           const int bj = t0 + st * kStep;
@@ -262,7 +261,7 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
 
   const float cs = p.scale_log2;
   auto fold_step = [&](int k, const Vec (&kv)[kLoads], const Vec (&vv)[kLoads]) {
-    const int base = t0 + (wave + kWaves * k) * kStep;
+    const int base = t0 + k * kStep;
     const bool tail = base + kStep > tmin;
     float sc[kLoads][ROWS];
 #pragma unroll
@@ -349,12 +348,12 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
     }
   };
 
-  // ---- main walk: wave w takes steps w, w + 4, ...; three register buffers
+  // ---- main walk over the partition's steps; three register buffers
   // rotate so that the loads of the next two steps are in flight while a
   // step is folded (the loop body is unrolled three times for the rotation).
   Vec ka[kLoads], va[kLoads], kb[kLoads], vb[kLoads], kc[kLoads], vc[kLoads];
   if constexpr (UNIFORM) {
-    // A walk of at most 64 steps per wave has every page offset resolved up
+    // A walk of at most 64 steps has every page offset resolved up
     // front; longer walks (a single partition over a long context) refresh
     // them every 64 steps.  The two loops are separate so that the refresh,
     // a vector load that must complete at once, never sits on a path of the
@@ -396,7 +395,8 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
     }
   }
 
-  // ---- merge the token groups of the wave, then the waves through LDS
+  // ---- merge the lane groups in registers, then write this partition
+  T *out = reinterpret_cast<T *>(p.out);
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     const float M = stride_max<kLpt>(m[r]);
@@ -404,200 +404,163 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
     const float lt = stride_sum<kLpt>(l[r] * f);
 #pragma unroll
     for (int e = 0; e < kElems; ++e) acc[r][e] = stride_sum<kLpt>(acc[r][e] * f);
-    if (lane < kLpt) {
-#pragma unroll
-      for (int e = 0; e < kElems; ++e) sm_acc[wave][r][c * kElems + e] = acc[r][e];
-    }
-    if (lane == 0) {
-      sm_m[wave][r] = M;
-      sm_l[wave][r] = lt;
-    }
-  }
-  __syncthreads();
-
-  T *out = reinterpret_cast<T *>(p.out);
-  for (int t = threadIdx.x; t < ROWS * D; t += 256) {
-    const int r = t / D, d = t - r * D;
     const int rho = rb * ROWS + r;
-    if (rho >= G * p.L) continue;
-    const int i = rho / G;
-    const int h = g * G + (rho - i * G);
-    const size_t row = ((size_t)(b * p.Hq + h) * p.L + i);
-    float M = kMinM;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][r]);
-    float o = 0.f, lse = kNegInf;
-    float wsum = 0.f, osum = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = fast_exp2(sm_m[w][r] - M);
-      wsum += f * sm_l[w][r];
-      osum += f * sm_acc[w][r][d];
-    }
-    if (valid[r] && wsum > 0.f) {
-      o = osum / wsum;
-      lse = (M + __log2f(wsum)) * kLn2;
-    }
+    if (rho >= G * p.L) continue;  // row outside the packed range
+    const bool has = valid[r] && lt > 0.f;
+    const float inv = has ? 1.f / lt : 0.f;
     if (split) {
       if (!valid[r]) continue;  // the merge writes padding rows itself
-      p.ws_o[(row * p.num_splits + s) * D + d] = o;
-      if (d == 0) p.ws_lse[row * p.num_splits + s] = lse;
-    } else {
+      const size_t wi = piece >= 0 ? (size_t)piece * ROWS + r : qrow[r] * p.num_splits + slot;
+      if (lane < kLpt) {
+        float *dst = p.ws_o + wi * D + c * kElems;
+#pragma unroll
+        for (int e = 0; e < kElems; e += 4)
+          *reinterpret_cast<float4 *>(dst + e) =
+              make_float4(acc[r][e] * inv, acc[r][e + 1] * inv, acc[r][e + 2] * inv, acc[r][e + 3] * inv);
+      }
+      if (lane == 0) p.ws_lse[wi] = has ? (M + __log2f(lt)) * kLn2 : kNegInf;
+    } else if (lane < kLpt) {
+      T *dst = out + qrow[r] * D + c * kElems;
       if constexpr (sizeof(T) == 4) {
-        out[row * D + d] = o;
+        *reinterpret_cast<float4 *>(dst) =
+            make_float4(acc[r][0] * inv, acc[r][1] * inv, acc[r][2] * inv, acc[r][3] * inv);
       } else {
-        out[row * D + d] = (uint16_t)f32_to_bf16(o);
+        *reinterpret_cast<uint4 *>(dst) = make_uint4(
+            cvt_pk_bf16(acc[r][0] * inv, acc[r][1] * inv), cvt_pk_bf16(acc[r][2] * inv, acc[r][3] * inv),
+            cvt_pk_bf16(acc[r][4] * inv, acc[r][5] * inv), cvt_pk_bf16(acc[r][6] * inv, acc[r][7] * inv));
       }
     }
   }
 }
 
-
-// Largest batch whose per-request partition counts the persistent schedule
-// keeps in LDS.
-constexpr int kSchedMaxB = kDecodeQueueMaxBatch;
-
-// Decode kernel.  Without a work counter every workgroup runs the one item
-// its block index names (grid = kv head x row block, request, partition;
-// partitions slowest, empty partitions exit at once).  With a work counter
-// the grid is the resident capacity of the GPU and workgroups pull items
-// from a queue until it is exhausted: blocks are dispatched to the XCDs in
-// strict round-robin order, so a plain grid of ragged items leaves slots of
-// fast XCDs idle while a slow XCD is full; the queue keeps every slot busy.
-// Queue order: all full partitions (request-major), then the partial last
-// partitions; empty partitions are never enumerated.  The last workgroup to
-// finish resets the counters to zero for the next call.
+// Decode kernel: four independent waves per workgroup, each walking its own
+// work items.
+//
+// Partition schedule (p.balanced == 0): the grid names the items (x: wave
+// index over partitions x (kv head x row block), the latter fastest; y:
+// request); a wave owns partition s of one row block and exits at once when
+// the partition is empty.
+//
+// Balanced schedule: the steps of every row block of every request are laid
+// out request-major (request b, then unit u = kv head x row block, then the
+// row block's ceil(context_len / STEP) steps) and the W active waves take
+// equal contiguous runs of them: wave w owns [floor(w T / W), floor((w+1) T
+// / W)).  A run crosses row boundaries freely, so the work per wave differs
+// by at most one step whatever the context lengths.  A row block r (counted
+// over the call) covered by waves w0..w1 leaves its piece from wave w in
+// piece slot r + w (unique; see balanced_active_waves), and the merge
+// recomputes w0 and w1 from the same formula; a row block that one wave
+// covers is written to the output directly.
 template <typename T, int D, int ROWS, bool DEBUG, bool UNIFORM>
 __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blocks) {
   constexpr int kWaves = 4;
-  __shared__ float sm_acc[kWaves][ROWS][D];
-  __shared__ float sm_m[kWaves][ROWS];
-  __shared__ float sm_l[kWaves][ROWS];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  if (p.counters == nullptr) {
-    const int g = blockIdx.x / row_blocks;
-    const int rb = blockIdx.x - g * row_blocks;
+  if (!p.balanced) {
+    const int units = p.Hkv * row_blocks;
+    const int idx = blockIdx.x * kWaves + wave;
+    const int s = idx / units;
+    const int u = idx - s * units;
+    const int g = u / row_blocks;
+    const int rb = u - g * row_blocks;
     const int b = blockIdx.y;
-    const int s = blockIdx.z;
+    if (s >= p.num_splits) return;
     const int ctx = p.cl[b];
     const int Lb = p.ql ? p.ql[b] : p.L;
-    if (p.num_splits > 1 && s * p.part_tokens >= ctx) return;  // never read by the merge
-    decode_item<T, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, s, ctx, Lb, sm_acc, sm_m, sm_l);
+    const int t0 = s * p.part_tokens;
+    if (s > 0 && t0 >= ctx) return;  // never read by the merge
+    const bool split = p.num_splits > 1;
+    decode_item<T, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, t0, split ? t0 + p.part_tokens : ctx,
+                                            s, -1, split, ctx, Lb);
     return;
   }
 
-  // ---- persistent schedule: prefix counts of full / partial partitions
-  __shared__ int s_full[kSchedMaxB + 1];     // exclusive prefix of full partitions
-  __shared__ int s_part[kSchedMaxB + 1];     // exclusive prefix of partial ones
-  __shared__ int s_next[2];
-  __shared__ int s_ctx[kSchedMaxB];          // context_lens, read once per workgroup
-  __shared__ int s_qlen[kSchedMaxB];         // query_lens (or L)
+  // ---- balanced schedule: prefix sums of the per-request step counts
+  constexpr int kStep = decode_step_keys(D, (int)sizeof(T));
+  __shared__ long long s_R[kBalancedMaxBatch + 1];  // first step of request b
+  __shared__ int s_ctx[kBalancedMaxBatch];
+  __shared__ long long s_sum[256];
   const int B = p.B;
-  const int P = p.part_tokens;
+  const int U = p.Hkv * row_blocks;
   const int tid = threadIdx.x;
-  // per-thread serial scan over a contiguous slice, then a block scan of sums
+  // per-thread serial sums over a contiguous slice, then a block scan
   const int per = (B + 255) / 256;
-  int f_loc = 0, p_loc = 0;
+  long long loc = 0;
   for (int k = 0; k < per; ++k) {
     const int b = tid * per + k;
     if (b < B) {
       const int ctx = p.cl[b];
       s_ctx[b] = ctx;
-      s_qlen[b] = p.ql ? p.ql[b] : p.L;
-      const int f = ctx / P;
-      const int q = (ctx % P != 0 || ctx == 0) ? 1 : 0;  // context 0 still gets one item
-      s_full[b] = f;
-      s_part[b] = q;
-      f_loc += f;
-      p_loc += q;
+      loc += (long long)U * ((ctx + kStep - 1) / kStep);
     }
   }
-  __shared__ int s_sumf[256], s_sump[256];
-  s_sumf[tid] = f_loc;
-  s_sump[tid] = p_loc;
+  s_sum[tid] = loc;
   __syncthreads();
   for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scan
-    const int a = tid >= off ? s_sumf[tid - off] : 0;
-    const int a2 = tid >= off ? s_sump[tid - off] : 0;
+    const long long a = tid >= off ? s_sum[tid - off] : 0;
     __syncthreads();
-    s_sumf[tid] += a;
-    s_sump[tid] += a2;
+    s_sum[tid] += a;
     __syncthreads();
   }
-  int run_f = tid > 0 ? s_sumf[tid - 1] : 0, run_p = tid > 0 ? s_sump[tid - 1] : 0;
+  long long run = tid > 0 ? s_sum[tid - 1] : 0;
   for (int k = 0; k < per; ++k) {
     const int b = tid * per + k;
     if (b < B) {
-      const int f = s_full[b], q = s_part[b];
-      s_full[b] = run_f;
-      s_part[b] = run_p;
-      run_f += f;
-      run_p += q;
+      const int n = (s_ctx[b] + kStep - 1) / kStep;
+      s_R[b] = run;
+      run += (long long)U * n;
     }
   }
-  if (tid == 255) {
-    s_full[B] = s_sumf[255];
-    s_part[B] = s_sump[255];
-  }
-  const int U = p.Hkv * row_blocks;
+  if (tid == 255) s_R[B] = s_sum[255];
   __syncthreads();
-  const int F = s_full[B];
-  const long n_items = (long)(F + s_part[B]) * U;
 
-  // Item k of the queue: the first gridDim.x items go to the workgroups by
-  // block index, later ones are claimed through the counter (which counts
-  // claims beyond the first gridDim.x), so the launch starts without a burst
-  // of atomics on one address.
-  uint32_t *work = p.counters;
-  int item = blockIdx.x, parity = 0;
-  while (item < n_items) {
-    // claim the following item now; it is needed only after this one
-    int nxt = 0;
-    if (tid == 0) nxt = (int)(gridDim.x + atomicAdd(work, 1u));
-    const int pair = item / U;
-    const int u = item - pair * U;
-    int b, s;
-    if (pair < F) {  // full partition: largest b with s_full[b] <= pair
-      int lo = 0, hi = B - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_full[mid] <= pair) lo = mid; else hi = mid - 1;
-      }
-      b = lo;
-      s = pair - s_full[b];
-    } else {         // partial last partition of the j-th request that has one
-      const int j = pair - F;
-      int lo = 0, hi = B - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_part[mid] <= j) lo = mid; else hi = mid - 1;
-      }
-      b = lo;
-      s = s_full[b + 1] - s_full[b];
+  // Values read from LDS are per-lane to the compiler; everything that shapes
+  // the walk is made wave-uniform (scalar) so that loop bounds and buffer
+  // descriptors stay in scalar registers.
+  auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  auto uni64 = [](long long v) {
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)v >> 32));
+    return (long long)(((unsigned long long)hi << 32) | lo);
+  };
+  const long long Tot = uni64(s_R[B]);
+  const long long Wa = balanced_active_waves(p.grid_waves, Tot, (long long)B * U, p.num_splits);
+  const long long w = (long long)blockIdx.x * kWaves + wave;
+  if (w >= Wa) return;
+  // wave of step t: the largest v with floor(v Tot / Wa) <= t
+  auto wave_of = [&](long long t) { return ((t + 1) * Wa - 1) / Tot; };
+  long long t = w * Tot / Wa;
+  const long long e = (w + 1) * Tot / Wa;
+  while (t < e) {
+    int lo = 0, hi = B - 1;  // request: the largest b with s_R[b] <= t
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_R[mid] <= t) lo = mid; else hi = mid - 1;
     }
+    const int b = uni(lo);
+    const int ctx = uni(s_ctx[b]);
+    const long long n = (ctx + kStep - 1) / kStep;  // > 0: request b holds step t
+    const long long Rb = uni64(s_R[b]);
+    const long long rel = t - Rb;
+    const int u = (int)(rel / n);
+    const long long j0 = rel - (long long)u * n;
+    const long long j1 = min(n, j0 + (e - t));
+    const long long row0 = Rb + (long long)u * n;
+    const long long w0 = wave_of(row0);
+    const bool split = wave_of(row0 + n - 1) > w0;
     const int g = u / row_blocks;
     const int rb = u - g * row_blocks;
-    const int ctx = s_ctx[b];
-    const int Lb = s_qlen[b];
-    decode_item<T, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, s, ctx, Lb, sm_acc, sm_m, sm_l);
-    parity ^= 1;
-    if (tid == 0) s_next[parity] = nxt;
-    __syncthreads();  // also orders this item's LDS reads before the next item's writes
-    item = s_next[parity];
-  }
-  if (tid == 0) {
-    if (atomicAdd(work + 1, 1u) == gridDim.x - 1) {  // every workgroup is done claiming
-      work[0] = 0u;
-      work[1] = 0u;
-    }
+    const int Lb = p.ql ? p.ql[b] : p.L;
+    decode_item<T, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, (int)(j0 * kStep), (int)(j1 * kStep),
+                                            0, (long long)b * U + u + w, split, ctx, Lb);
+    t += j1 - j0;
   }
 }
 
-// Workgroups of `kernel` that fit on the current device at once (cached per
-// kernel and device).
+// Workgroups of `kernel` that fit on the current device at once, cached in
+// `cached` (one array per kernel) per device.
 template <typename K>
-int resident_blocks(K kernel) {
-  static int cached[64] = {0};
+int resident_blocks(K kernel, int (&cached)[64]) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
   if (cached[dev] == 0) {
@@ -613,50 +576,75 @@ int resident_blocks(K kernel) {
   return cached[dev];
 }
 
+// The kernel variant for `p` is chosen once, here; `Fn` either launches it
+// or reports its balanced grid size.
 template <typename T, int D, int ROWS, bool DEBUG, bool UNIFORM>
-hipError_t launch_mode(const LaunchParams &p, int row_blocks, hipStream_t stream) {
-  auto kernel = decode_kernel<T, D, ROWS, DEBUG, UNIFORM>;
-  dim3 grid(p.Hkv * row_blocks, p.B, p.num_splits);
-  if (p.counters) {
-    const long items = (long)p.Hkv * row_blocks * p.B * p.num_splits;  // upper bound
-    const long ctas = resident_blocks(kernel);
-    grid = dim3((unsigned)(items < ctas ? items : ctas), 1, 1);
+struct Variant {
+  static hipError_t launch(const LaunchParams &p, int row_blocks, hipStream_t stream) {
+    auto kernel = decode_kernel<T, D, ROWS, DEBUG, UNIFORM>;
+    dim3 grid;
+    if (p.balanced) {
+      grid = dim3((unsigned)(p.grid_waves / 4), 1, 1);
+    } else {
+      const long per_request = ((long)p.Hkv * row_blocks * p.num_splits + 3) / 4;
+      grid = dim3((unsigned)per_request, p.B, 1);
+    }
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, p, row_blocks);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, p, row_blocks);
-  return hipGetLastError();
-}
+  static int waves() {
+    static int cached[64] = {0};
+    return 4 * resident_blocks(decode_kernel<T, D, ROWS, DEBUG, UNIFORM>, cached);
+  }
+};
 
-template <typename T, int D, int ROWS>
-hipError_t launch_typed(const LaunchParams &p, hipStream_t stream) {
-  const int G = p.Hq / p.Hkv;
-  const int row_blocks = (G * p.L + ROWS - 1) / ROWS;
-  constexpr int kStep = 4 * 64 / (D / (16 / (int)sizeof(T)));  // keys per wave step
+template <typename T, int D, int ROWS, typename Fn>
+auto dispatch_mode(const LaunchParams &p, Fn &&fn) {
+  constexpr int kStep = decode_step_keys(D, (int)sizeof(T));
   const bool uniform = p.ps % kStep == 0;
   const bool debug = p.dbg_trace != nullptr || p.dbg_visits != nullptr;
   if (debug)
-    return uniform ? launch_mode<T, D, ROWS, true, true>(p, row_blocks, stream)
-                   : launch_mode<T, D, ROWS, true, false>(p, row_blocks, stream);
-  return uniform ? launch_mode<T, D, ROWS, false, true>(p, row_blocks, stream)
-                 : launch_mode<T, D, ROWS, false, false>(p, row_blocks, stream);
+    return uniform ? fn(Variant<T, D, ROWS, true, true>()) : fn(Variant<T, D, ROWS, true, false>());
+  return uniform ? fn(Variant<T, D, ROWS, false, true>()) : fn(Variant<T, D, ROWS, false, false>());
 }
 
-template <typename T, int D>
-hipError_t launch_rows(const LaunchParams &p, hipStream_t stream) {
-  switch (decode_rows_per_block((p.Hq / p.Hkv) * p.L)) {
-    case 1: return launch_typed<T, D, 1>(p, stream);
-    case 2: return launch_typed<T, D, 2>(p, stream);
-    case 4: return launch_typed<T, D, 4>(p, stream);
-    default: return launch_typed<T, D, 8>(p, stream);
-  }
+template <typename X>
+struct TypeTag {
+  using type = X;
+};
+
+template <typename Fn>
+auto dispatch(const LaunchParams &p, DType dt, Fn &&fn) {
+  const int rows = decode_rows_per_block((p.Hq / p.Hkv) * p.L);
+  auto by_rows = [&](auto t, auto d) {
+    using TT = typename decltype(t)::type;
+    constexpr int DD = decltype(d)::value;
+    switch (rows) {
+      case 1: return dispatch_mode<TT, DD, 1>(p, fn);
+      case 2: return dispatch_mode<TT, DD, 2>(p, fn);
+      case 4: return dispatch_mode<TT, DD, 4>(p, fn);
+      default: return dispatch_mode<TT, DD, 8>(p, fn);
+    }
+  };
+  using F = TypeTag<float>;
+  using H = TypeTag<uint16_t>;
+  using D64 = std::integral_constant<int, 64>;
+  using D128 = std::integral_constant<int, 128>;
+  if (dt == DType::F32) return p.D == 64 ? by_rows(F(), D64()) : by_rows(F(), D128());
+  return p.D == 64 ? by_rows(H(), D64()) : by_rows(H(), D128());
 }
 
 }  // namespace
 
 hipError_t launch_decode(const LaunchParams &p, DType dt, hipStream_t stream) {
-  if (dt == DType::F32) {
-    return p.D == 64 ? launch_rows<float, 64>(p, stream) : launch_rows<float, 128>(p, stream);
-  }
-  return p.D == 64 ? launch_rows<uint16_t, 64>(p, stream) : launch_rows<uint16_t, 128>(p, stream);
+  const int row_blocks =
+      ((p.Hq / p.Hkv) * p.L + decode_rows_per_block((p.Hq / p.Hkv) * p.L) - 1) /
+      decode_rows_per_block((p.Hq / p.Hkv) * p.L);
+  return dispatch(p, dt, [&](auto v) { return decltype(v)::launch(p, row_blocks, stream); });
+}
+
+int decode_balanced_waves(const LaunchParams &p, DType dt) {
+  return dispatch(p, dt, [](auto v) { return decltype(v)::waves(); });
 }
 
 }  // namespace pa

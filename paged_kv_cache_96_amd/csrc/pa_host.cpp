@@ -15,7 +15,8 @@
 namespace {
 
 constexpr int kMinPartitionTokens = 256;  // below this the merge costs more than it buys
-constexpr int kBlocksPerCu = 8;           // decode workgroups wanted per compute unit
+constexpr int kBlocksPerCu = 8;           // decode work items wanted per compute unit
+constexpr int kWavesPerCu = 8;            // resident decode waves per compute unit
 constexpr int kMaxGridYZ = 65535;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -46,30 +47,64 @@ pa_status check_pointers(const pa_args *a) {
   return PA_OK;
 }
 
-// Workspace consistency for a decode/merge pair.  S == 1 needs no buffers.
-pa_status check_workspace(const pa_args *a, const pa_workspace *ws, int32_t *S, int32_t *P) {
+int elem_bytes(const pa_args *a) { return a->dtype == PA_DTYPE_F32 ? 4 : 2; }
+
+// Query rows of one decode row block.
+int64_t decode_block_rows(const pa_args *a) {
+  const int64_t rows = (int64_t)(a->num_q_heads / a->num_kv_heads) * a->q_len;
+  return pa::decode_rows_per_block((int)(rows < 8 ? rows : 8));
+}
+
+// Row blocks (units of the decode schedule) per request.
+int64_t decode_units(const pa_args *a) {
+  const int64_t rows = (int64_t)(a->num_q_heads / a->num_kv_heads) * a->q_len;
+  const int64_t per = decode_block_rows(a);
+  return (int64_t)a->num_kv_heads * ((rows + per - 1) / per);
+}
+
+// Largest step count a balanced call over `a` can have.
+int64_t balanced_max_steps(const pa_args *a) {
+  const int64_t step = pa::decode_step_keys(a->head_dim, elem_bytes(a));
+  const int64_t cap = (int64_t)a->max_pages * a->page_size;
+  return (int64_t)a->batch * decode_units(a) * ((cap + step - 1) / step);
+}
+
+// Workspace consistency for a decode/merge pair.  A single partition needs
+// no buffers.
+pa_status check_workspace(const pa_args *a, const pa_workspace *ws, int32_t *S, int32_t *P,
+                          bool *balanced) {
   const int32_t cap = a->max_pages * a->page_size;
-  if (!ws || ws->num_splits == 1) {
-    if (ws && ws->counters && (reinterpret_cast<uintptr_t>(ws->counters) & 7u))
-      return PA_ERR_WORKSPACE;
+  *balanced = false;
+  if (ws && ws->schedule != PA_SCHEDULE_PARTITIONS && ws->schedule != PA_SCHEDULE_BALANCED)
+    return PA_ERR_WORKSPACE;
+  if (!ws || (ws->schedule == PA_SCHEDULE_PARTITIONS && ws->num_splits == 1)) {
     *S = 1;
     *P = cap;
     return PA_OK;
   }
-  if (ws->num_splits < 1 || ws->partition_tokens <= 0 || ws->partition_tokens % a->page_size)
-    return PA_ERR_WORKSPACE;
-  if ((int64_t)ws->num_splits * ws->partition_tokens < cap) return PA_ERR_WORKSPACE;
-  if (ws->num_splits > kMaxGridYZ) return PA_ERR_WORKSPACE;
+  if (ws->schedule == PA_SCHEDULE_BALANCED) {
+    // one piece slot per row block plus at least one wave
+    if (a->batch > pa::kBalancedMaxBatch || balanced_max_steps(a) > pa::kBalancedMaxSteps ||
+        (int64_t)ws->num_splits < (int64_t)a->batch * decode_units(a) + 1)
+      return PA_ERR_WORKSPACE;
+    *balanced = true;
+    *P = 0;
+  } else {
+    if (ws->num_splits < 1 || ws->partition_tokens <= 0 || ws->partition_tokens % a->page_size)
+      return PA_ERR_WORKSPACE;
+    if ((int64_t)ws->num_splits * ws->partition_tokens < cap) return PA_ERR_WORKSPACE;
+    if (ws->num_splits > kMaxGridYZ) return PA_ERR_WORKSPACE;
+    *P = ws->partition_tokens;
+  }
   if (!ws->partial_out || !ws->partial_lse || !aligned16(ws->partial_out) ||
       !aligned16(ws->partial_lse))
     return PA_ERR_WORKSPACE;
-  if (ws->counters && (reinterpret_cast<uintptr_t>(ws->counters) & 7u)) return PA_ERR_WORKSPACE;
   *S = ws->num_splits;
-  *P = ws->partition_tokens;
   return PA_OK;
 }
 
-pa::LaunchParams make_params(const pa_args *a, int32_t S, int32_t P, const pa_workspace *ws) {
+pa::LaunchParams make_params(const pa_args *a, int32_t S, int32_t P, bool balanced,
+                             const pa_workspace *ws) {
   pa::LaunchParams p;
   memset(&p, 0, sizeof p);
   p.q = a->query;
@@ -83,7 +118,6 @@ pa::LaunchParams make_params(const pa_args *a, int32_t S, int32_t P, const pa_wo
   p.ws_lse = (S > 1 && ws) ? ws->partial_lse : nullptr;
   p.dbg_trace = a->debug_trace;
   p.dbg_visits = a->debug_visits;
-  p.counters = (ws && a->batch <= pa::kDecodeQueueMaxBatch) ? ws->counters : nullptr;
   p.B = a->batch;
   p.Hq = a->num_q_heads;
   p.Hkv = a->num_kv_heads;
@@ -95,18 +129,21 @@ pa::LaunchParams make_params(const pa_args *a, int32_t S, int32_t P, const pa_wo
   p.causal = a->mask == PA_MASK_CAUSAL;
   p.num_splits = S;
   p.part_tokens = P;
+  p.balanced = balanced ? 1 : 0;
+  p.grid_waves = 0;
   p.scale_log2 = a->scale * 1.4426950408889634f;
+  if (balanced) p.grid_waves = pa::decode_balanced_waves(p, (pa::DType)a->dtype);
   return p;
 }
 
 pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
-// Grid limits of the vector kernels: gridDim.x = H_kv * row blocks.
-pa_status check_decode_grid(const pa_args *a) {
-  const int64_t rows = (int64_t)(a->num_q_heads / a->num_kv_heads) * a->q_len;
-  const int64_t per = pa::decode_rows_per_block((int)(rows < 8 ? rows : 8));
-  const int64_t blocks_x = (int64_t)a->num_kv_heads * ((rows + per - 1) / per);
-  return blocks_x > INT32_MAX ? PA_ERR_INVALID_ARG : PA_OK;
+// Grid limits of the vector kernel under the partition schedule: gridDim.x =
+// ceil(H_kv * row blocks * partitions / 4) (one work item per wave),
+// gridDim.y = batch.
+pa_status check_decode_grid(const pa_args *a, int32_t S) {
+  const int64_t items = decode_units(a) * S;
+  return (items + 3) / 4 > INT32_MAX ? PA_ERR_INVALID_ARG : PA_OK;
 }
 
 }  // namespace
@@ -132,33 +169,45 @@ PA_EXPORT pa_status pa_decode_plan(const pa_args *args, int32_t num_cus, pa_work
   if (args->q_len > 8) return PA_ERR_INVALID_ARG;
   const int32_t ps = args->page_size;
   const int32_t cap = args->max_pages * ps;
-  int32_t P;
-  if (plan->partition_tokens > 0) {
-    P = (plan->partition_tokens + ps - 1) / ps * ps;
+  const int cus = num_cus > 0 ? num_cus : 256;
+  const int64_t units = (int64_t)(args->batch > 0 ? args->batch : 1) * decode_units(args);
+  int32_t S, P;
+  if (plan->partition_tokens <= 0 && args->batch <= pa::kBalancedMaxBatch &&
+      balanced_max_steps(args) <= pa::kBalancedMaxSteps) {
+    // a piece slot per row block plus one per wave of the grid
+    const int64_t slots = units + (int64_t)kWavesPerCu * cus;
+    if (slots > INT32_MAX) return PA_ERR_INVALID_ARG;
+    S = (int32_t)slots;
+    P = 0;
+    plan->schedule = PA_SCHEDULE_BALANCED;
   } else {
-    const int cus = num_cus > 0 ? num_cus : 256;
-    const int64_t rows = (int64_t)(args->num_q_heads / args->num_kv_heads) * args->q_len;
-    const int64_t per = pa::decode_rows_per_block((int)(rows < 8 ? rows : 8));
-    const int64_t units =
-        (int64_t)(args->batch > 0 ? args->batch : 1) * args->num_kv_heads * ((rows + per - 1) / per);
-    const int64_t want = (int64_t)kBlocksPerCu * cus;
-    const int64_t splits = units >= want ? 1 : (want + units - 1) / units;
-    int64_t tok = (cap + splits - 1) / splits;
-    if (tok < kMinPartitionTokens) tok = kMinPartitionTokens;
-    P = (int32_t)((tok + ps - 1) / ps * ps);
+    if (plan->partition_tokens > 0) {
+      P = (plan->partition_tokens + ps - 1) / ps * ps;
+    } else {
+      const int64_t want = (int64_t)kBlocksPerCu * cus;
+      const int64_t splits = units >= want ? 1 : (want + units - 1) / units;
+      int64_t tok = (cap + splits - 1) / splits;
+      if (tok < kMinPartitionTokens) tok = kMinPartitionTokens;
+      P = (int32_t)((tok + ps - 1) / ps * ps);
+    }
+    if (P > cap) P = (cap + ps - 1) / ps * ps;
+    if ((cap + P - 1) / P > kMaxGridYZ) {  // bounds the partition count
+      const int64_t tok = ((int64_t)cap + kMaxGridYZ - 1) / kMaxGridYZ;
+      P = (int32_t)((tok + ps - 1) / ps * ps);
+    }
+    S = (cap + P - 1) / P;
+    plan->schedule = PA_SCHEDULE_PARTITIONS;
   }
-  if (P > cap) P = (cap + ps - 1) / ps * ps;
-  if ((cap + P - 1) / P > kMaxGridYZ) {  // partitions are a grid dimension
-    const int64_t tok = ((int64_t)cap + kMaxGridYZ - 1) / kMaxGridYZ;
-    P = (int32_t)((tok + ps - 1) / ps * ps);
-  }
-  const int32_t S = (cap + P - 1) / P;
   plan->num_splits = S;
   plan->partition_tokens = P;
+  plan->reserved = 0;
   if (workspace_bytes) {
-    const size_t rows =
-        (size_t)(args->batch > 0 ? args->batch : 0) * args->num_q_heads * args->q_len;
-    *workspace_bytes = (S > 1 ? rows * S * (args->head_dim + 1) * sizeof(float) : 0) + 256;
+    // partitions: [B, H_q, L, S] states; balanced: [S, rows per block] states
+    const size_t rows = plan->schedule == PA_SCHEDULE_BALANCED
+                            ? (size_t)decode_block_rows(args)
+                            : (size_t)(args->batch > 0 ? args->batch : 0) * args->num_q_heads *
+                                  args->q_len;
+    *workspace_bytes = S > 1 ? rows * S * (args->head_dim + 1) * sizeof(float) : 0;
   }
   return PA_OK;
 }
@@ -169,10 +218,11 @@ PA_EXPORT pa_status pa_decode(const pa_args *args, const pa_workspace *ws, void 
   if (args->q_len > 8) return PA_ERR_INVALID_ARG;
   if (args->batch == 0) return PA_OK;
   if ((st = check_pointers(args)) != PA_OK) return st;
-  if ((st = check_decode_grid(args)) != PA_OK) return st;
   int32_t S, P;
-  if ((st = check_workspace(args, ws, &S, &P)) != PA_OK) return st;
-  const pa::LaunchParams p = make_params(args, S, P, ws);
+  bool balanced;
+  if ((st = check_workspace(args, ws, &S, &P, &balanced)) != PA_OK) return st;
+  if (!balanced && (st = check_decode_grid(args, S)) != PA_OK) return st;
+  const pa::LaunchParams p = make_params(args, S, P, balanced, ws);
   return hip_status(pa::launch_decode(p, (pa::DType)args->dtype, (hipStream_t)stream));
 }
 
@@ -183,9 +233,10 @@ PA_EXPORT pa_status pa_split_reduce(const pa_args *args, const pa_workspace *ws,
   if (args->batch == 0) return PA_OK;
   if ((st = check_pointers(args)) != PA_OK) return st;
   int32_t S, P;
-  if ((st = check_workspace(args, ws, &S, &P)) != PA_OK) return st;
+  bool balanced;
+  if ((st = check_workspace(args, ws, &S, &P, &balanced)) != PA_OK) return st;
   if (S == 1) return PA_OK;  // pa_decode already wrote `out`
-  const pa::LaunchParams p = make_params(args, S, P, ws);
+  const pa::LaunchParams p = make_params(args, S, P, balanced, ws);
   return hip_status(pa::launch_split_reduce(p, (pa::DType)args->dtype, (hipStream_t)stream));
 }
 
@@ -195,12 +246,12 @@ PA_EXPORT pa_status pa_prefill(const pa_args *args, void *stream) {
   if (args->batch == 0) return PA_OK;
   if ((st = check_pointers(args)) != PA_OK) return st;
   const int32_t cap = args->max_pages * args->page_size;
-  const pa::LaunchParams p = make_params(args, 1, cap, nullptr);
+  const pa::LaunchParams p = make_params(args, 1, cap, false, nullptr);
   if (args->dtype == PA_DTYPE_BF16) {
     const int64_t tiles = ((int64_t)(args->num_q_heads / args->num_kv_heads) * args->q_len + 127) / 128;
     if (tiles > INT32_MAX || args->num_kv_heads > kMaxGridYZ) return PA_ERR_INVALID_ARG;
     return hip_status(pa::launch_prefill_mfma(p, (hipStream_t)stream));
   }
-  if ((st = check_decode_grid(args)) != PA_OK) return st;
+  if ((st = check_decode_grid(args, 1)) != PA_OK) return st;
   return hip_status(pa::launch_decode(p, (pa::DType)args->dtype, (hipStream_t)stream));
 }

@@ -7,6 +7,8 @@
 
 namespace pa {
 
+enum class DType { F32 = 0, BF16 = 1 };
+
 // Everything a paged-attention launch needs, already validated by the host.
 struct LaunchParams {
   const void *q;
@@ -16,19 +18,18 @@ struct LaunchParams {
   const int32_t *cl;
   const int32_t *ql;        // nullptr: every request has L rows
   void *out;
-  float *ws_o;              // [B, Hq, L, S, D] fp32 (decode with S > 1)
-  float *ws_lse;            // [B, Hq, L, S]   fp32
+  float *ws_o;              // partitions: [B, Hq, L, S, D]; balanced: [S, ROWS, D] fp32
+  float *ws_lse;            // partitions: [B, Hq, L, S];    balanced: [S, ROWS]    fp32
   int32_t *dbg_trace;       // nullptr unless instrumented
   int32_t *dbg_visits;      // nullptr unless instrumented
-  uint32_t *counters;       // decode work-queue counters [2], or nullptr (plain grid)
   int32_t B, Hq, Hkv, L, D, num_pages, ps, max_pages;
   int32_t causal;
-  int32_t num_splits;       // S >= 1
-  int32_t part_tokens;      // keys per partition, multiple of ps
+  int32_t num_splits;       // S >= 1: partitions, or piece slots when balanced
+  int32_t part_tokens;      // keys per partition, multiple of ps (partition schedule)
+  int32_t balanced;         // 1: equal runs of steps per wave (see decode_balanced_waves)
+  int32_t grid_waves;       // balanced: waves of the decode grid
   float scale_log2;         // scale * log2(e): scores are kept in base-2 units
 };
-
-enum class DType { F32 = 0, BF16 = 1 };
 
 // Vector-ALU paged decode kernel (also the fp32 prefill path, with S == 1).
 hipError_t launch_decode(const LaunchParams &p, DType dt, hipStream_t stream);
@@ -37,13 +38,42 @@ hipError_t launch_split_reduce(const LaunchParams &p, DType dt, hipStream_t stre
 // bf16 MFMA prefill kernel.
 hipError_t launch_prefill_mfma(const LaunchParams &p, hipStream_t stream);
 
-// Largest batch the persistent decode schedule supports (its per-request
-// partition counts live in LDS); larger batches use the plain grid.
-constexpr int kDecodeQueueMaxBatch = 2048;
+// Largest batch the balanced decode schedule supports (its per-request
+// prefix sums live in LDS); larger batches use the partition schedule.
+constexpr int kBalancedMaxBatch = 2048;
+// Bound on the total number of steps of a balanced call, so that products of
+// a step index and a wave count stay far inside 64 bits.
+constexpr int64_t kBalancedMaxSteps = int64_t(1) << 40;
+// Shortest run of steps a balanced schedule hands to one wave.
+constexpr int kBalancedMinSteps = 4;
+
+// Keys per decode step (one 16-byte load per lane, four loads per step):
+// 16 for bf16 with D = 128.
+__host__ __device__ constexpr int decode_step_keys(int D, int elem_bytes) {
+  return 4096 / (D * elem_bytes);
+}
+
+// Waves of the balanced decode grid for `p` (the resident capacity of the
+// kernel variant that would run it).
+int decode_balanced_waves(const LaunchParams &p, DType dt);
+
+// Waves that take part in a balanced schedule of T steps over `units` row
+// blocks with S piece slots.  The piece of row block r (counted over the
+// whole call) walked by wave w lives in slot r + w: rows and wave runs are
+// both consecutive intervals of the step order, so a later row block never
+// meets an earlier wave and r + w is unique; slots < units + waves - 1.
+__host__ __device__ inline int64_t balanced_active_waves(int64_t grid_waves, int64_t T,
+                                                         int64_t units, int64_t S) {
+  int64_t w = grid_waves;
+  const int64_t by_len = (T + kBalancedMinSteps - 1) / kBalancedMinSteps;
+  if (by_len < w) w = by_len;
+  if (S - units < w) w = S - units;  // S >= units + 1 is checked by the host
+  return w;
+}
 
 // Query rows one decode workgroup holds, for a GQA group of `rows_per_head`
 // packed rows (G * L).  Shared by the host (grid sizing) and the launcher.
-inline int decode_rows_per_block(int rows) {
+__host__ __device__ inline int decode_rows_per_block(int rows) {
   if (rows <= 1) return 1;
   if (rows <= 2) return 2;
   if (rows <= 4) return 4;

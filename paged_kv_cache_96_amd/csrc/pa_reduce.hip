@@ -2,8 +2,12 @@
 // PagedAttention Kernel", section 3.3: partitions computed in parallel are
 // combined afterwards).  One wave per query row:
 //   M = max_s lse_s,  w_s = exp(lse_s - M),  out = sum_s w_s o_s / sum_s w_s
-// over the partitions s < ceil(ctx / partition_tokens) that the decode
-// kernel wrote.  Rows past query_lens[b], and requests with no keys, get 0.
+// over the states the decode kernel wrote: partitions s < ceil(ctx /
+// partition_tokens) under the partition schedule; under the balanced
+// schedule the pieces w0..w1 of the row block, recomputed from the same
+// formula the decode kernel used (a row block that one wave covered was
+// written by the decode kernel and is left alone).  Rows past query_lens[b],
+// and requests with no keys, get 0.
 #include "pa_common.hpp"
 #include "pa_internal.h"
 
@@ -11,6 +15,37 @@ namespace pa {
 namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
+
+// Sum over the 64 lanes of a wave.
+__device__ __forceinline__ long long wave_sum(long long v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Waves w0..w1 of the balanced decode schedule that walked unit u of
+// request b (units per request); count 0 when the request has no keys.
+template <int kStep>
+__device__ void balanced_waves(const LaunchParams &p, int b, int u, int units, long long &w0,
+                               int &count) {
+  const int lane = threadIdx.x & 63;
+  long long tot = 0, before = 0;
+  for (int c = lane; c < p.B; c += 64) {
+    const long long steps = (long long)units * ((p.cl[c] + kStep - 1) / kStep);
+    tot += steps;
+    if (c < b) before += steps;
+  }
+  tot = wave_sum(tot);
+  before = wave_sum(before);
+  const long long n = (p.cl[b] + kStep - 1) / kStep;
+  w0 = 0;
+  count = 0;
+  if (n == 0) return;
+  const long long Wa = balanced_active_waves(p.grid_waves, tot, (long long)p.B * units, p.num_splits);
+  const long long row0 = before + (long long)u * n;
+  w0 = ((row0 + 1) * Wa - 1) / tot;
+  count = (int)(((row0 + n) * Wa - 1) / tot - w0 + 1);
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void split_reduce_kernel(LaunchParams p, int total_rows) {
@@ -23,12 +58,37 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(LaunchParams p, int t
   const int ctx = p.cl[b];
   const int Lb = p.ql ? p.ql[b] : p.L;
   const int S = p.num_splits;
-  const int n = (i < Lb && ctx > 0) ? min(S, (ctx + p.part_tokens - 1) / p.part_tokens) : 0;
+  int n;
+  // state s of this row: lse[s * stride], po[s * stride * D]
+  const float *lse;
+  const float *po;
+  size_t stride;
+  if (p.balanced) {
+    const int h = (row / p.L) % p.Hq;
+    const int G = p.Hq / p.Hkv;
+    const int g = h / G;
+    const int rows = decode_rows_per_block(G * p.L);
+    const int row_blocks = (G * p.L + rows - 1) / rows;
+    const int rho = i * G + (h - g * G);
+    const int u = g * row_blocks + rho / rows;
+    long long w0;
+    int pieces;
+    balanced_waves<decode_step_keys(D, (int)sizeof(T))>(p, b, u, p.Hkv * row_blocks, w0, pieces);
+    if (pieces == 1) return;  // the decode kernel wrote this row
+    n = i < Lb ? pieces : 0;
+    const size_t first = ((size_t)b * p.Hkv * row_blocks + u + w0) * rows + rho % rows;
+    lse = p.ws_lse + first;
+    po = p.ws_o + first * D;
+    stride = rows;
+  } else {
+    n = (i < Lb && ctx > 0) ? min(S, (ctx + p.part_tokens - 1) / p.part_tokens) : 0;
+    lse = p.ws_lse + (size_t)row * S;
+    po = p.ws_o + (size_t)row * S * D;
+    stride = 1;
+  }
 
-  const float *lse = p.ws_lse + (size_t)row * S;
-  const float *po = p.ws_o + (size_t)row * S * D;
   float M = kNegInf;
-  for (int s = lane; s < n; s += 64) M = fmaxf(M, lse[s]);
+  for (int s = lane; s < n; s += 64) M = fmaxf(M, lse[s * stride]);
   M = group_max<64>(M);
 
   float o[kPer];
@@ -37,10 +97,10 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(LaunchParams p, int t
   if (M != kNegInf) {
     float wsum = 0.f;
     for (int s = 0; s < n; ++s) {
-      const float w = fast_exp2((lse[s] - M) * kLog2e);
+      const float w = fast_exp2((lse[s * stride] - M) * kLog2e);
       wsum += w;
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) o[e] = fmaf(w, po[(size_t)s * D + e * 64 + lane], o[e]);
+      for (int e = 0; e < kPer; ++e) o[e] = fmaf(w, po[s * stride * D + e * 64 + lane], o[e]);
     }
     const float inv = 1.f / wsum;
 #pragma unroll

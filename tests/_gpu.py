@@ -45,8 +45,10 @@ class DeviceInputs:
 
 
 def run_decode(api, d: DeviceInputs, *, partition_tokens=0, trace=False, keep_ws=False,
-               queue=True):
-    """pa_decode (+ pa_split_reduce) through the C ABI.  Returns (out, extras)."""
+               num_cus=0):
+    """pa_decode (+ pa_split_reduce) through the C ABI with the library's
+    plan (partition_tokens > 0: the partition schedule with that size; else
+    the balanced schedule, sized for `num_cus`).  Returns (out, extras)."""
     out = d.out()
     x = d.x
     extras = {}
@@ -57,8 +59,9 @@ def run_decode(api, d: DeviceInputs, *, partition_tokens=0, trace=False, keep_ws
         dbg_v = torch.zeros((x.B, x.H_kv, cap), dtype=torch.int32, device=d.q.device)
     args = api.make_args(d.q, d.kp, d.vp, d.bt, d.cl, out, scale=x.scale, mask=d.mask,
                          query_lens=d.ql, debug_trace=dbg_t, debug_visits=dbg_v)
-    S, P, nbytes = api.pa_decode_plan(args, partition_tokens=partition_tokens)
-    ws = api.Workspace(x.B, x.H_q, x.L, x.D, S, P, d.q.device, queue=queue)
+    plan = api.pa_decode_plan(args, partition_tokens=partition_tokens, num_cus=num_cus)
+    S, P, nbytes = plan.num_splits, plan.partition_tokens, plan.workspace_bytes
+    ws = api.Workspace.for_plan(plan, d.q)
     api.pa_decode(args, ws)
     if keep_ws and S > 1:
         torch.cuda.synchronize()
@@ -67,7 +70,7 @@ def run_decode(api, d: DeviceInputs, *, partition_tokens=0, trace=False, keep_ws
     if S > 1:
         api.pa_split_reduce(args, ws)
     torch.cuda.synchronize()
-    extras.update(S=S, P=P, ws_bytes=nbytes, ws=ws, args=args)
+    extras.update(S=S, P=P, ws_bytes=nbytes, ws=ws, args=args, schedule=plan.schedule)
     if trace:
         extras["trace"] = dbg_t.cpu().numpy()
         extras["visits"] = dbg_v.cpu().numpy()

@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 from paged_kv_cache_96_amd import _lib
-from paged_kv_cache_96_amd._lib import PaArgs, PaWorkspace
+from paged_kv_cache_96_amd._lib import (PaArgs, PaWorkspace, SCHEDULE_BALANCED,
+                                        SCHEDULE_PARTITIONS)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pa.h")
@@ -40,7 +41,7 @@ def test_header_and_library_exports_agree(L):
     assert exported == declared
     for name in declared:
         assert hasattr(L, name)
-    assert L.pa_abi_version() == 1
+    assert L.pa_abi_version() == 2
 
 
 def test_status_strings(L):
@@ -113,9 +114,17 @@ def test_workspace_validation(L):
     assert _decode(L, a, ws) == -3
     ws.num_splits = 0
     assert _decode(L, a, ws) == -3
-    ws.num_splits, ws.partial_lse, ws.counters = 4, h.p, h.p + 4   # counters not 8-byte aligned
+    ws.num_splits, ws.partial_lse, ws.schedule = 4, h.p, 7       # unknown schedule
     assert _decode(L, a, ws) == -3
     assert L.pa_split_reduce(ctypes.byref(a), ctypes.byref(ws), None) == -3
+    ws.schedule, ws.num_splits = SCHEDULE_BALANCED, 4             # needs 2 x 2 row blocks + 1 slots
+    assert _decode(L, a, ws) == -3
+    ws.num_splits = 5000
+    big = h.args(batch=2049)                                      # past the balanced batch limit
+    assert _decode(L, big, ws) == -3
+    assert L.pa_split_reduce(ctypes.byref(big), ctypes.byref(ws), None) == -3
+    ws.partial_out = None                                         # missing buffer
+    assert _decode(L, a, ws) == -3
 
 
 def test_batch_zero_is_a_no_op(L):
@@ -132,30 +141,41 @@ def test_prefill_accepts_long_queries_but_checks_sizes(L):
     assert L.pa_prefill(ctypes.byref(h.args(num_q_heads=3)), None) == -1
 
 
-def _plan(L, a, num_cus=0, P=0):
+def _plan(L, a, num_cus=0, P=0, full=False):
     ws = PaWorkspace()
     ws.partition_tokens = P
     nb = ctypes.c_size_t(0)
     rc = L.pa_decode_plan(ctypes.byref(a), num_cus, ctypes.byref(ws), ctypes.byref(nb))
+    if full:
+        return rc, ws.num_splits, ws.partition_tokens, nb.value, ws.schedule
     return rc, ws.num_splits, ws.partition_tokens, nb.value
 
 
 def test_plan_covers_capacity_and_sizes_workspace(L):
     h = HostBuffers()
-    # GQA decode, 64 requests x 8 kv heads, contexts up to 4096 keys (page 16)
+    # GQA decode, 64 requests x 8 kv heads (4 query rows each), contexts up to
+    # 4096 keys: balanced, a slot per row block (512) plus 8 waves x 256 CUs
     a = h.args(batch=64, num_q_heads=32, num_kv_heads=8, max_pages=256, num_pages=20000)
-    rc, S, P, nb = _plan(L, a)
-    assert rc == 0 and P % 16 == 0 and S * P >= 4096 and S > 1
-    assert nb == 64 * 32 * 1 * S * (128 + 1) * 4 + 256
-    # long contexts: 8 requests x 8 kv heads up to 131072 keys -> many partitions
+    rc, S, P, nb, sched = _plan(L, a, full=True)
+    assert (rc, S, P, sched) == (0, 512 + 2048, 0, SCHEDULE_BALANCED)
+    assert nb == S * 4 * (128 + 1) * 4
+    assert _plan(L, a, num_cus=1)[1] == 512 + 8
+    # long contexts: 8 requests x 8 kv heads
     a = h.args(batch=8, num_q_heads=32, num_kv_heads=8, max_pages=8192, num_pages=50000)
-    rc, S, P, nb = _plan(L, a)
-    assert rc == 0 and S >= 16 and S * P >= 8192 * 16
-    # an explicit request is honoured, rounded up to whole pages
-    rc, S, P, nb = _plan(L, a, P=1000)
-    assert (rc, P, S) == (0, 1008, -(-131072 // 1008))
+    rc, S, P, nb, sched = _plan(L, a, full=True)
+    assert (rc, S, sched) == (0, 64 + 2048, SCHEDULE_BALANCED)
+    # 8 query rows per block (G * L = 16): 2 row blocks per kv head
+    rc, S, P, nb, sched = _plan(L, h.args(batch=3, num_q_heads=8, num_kv_heads=2, q_len=4),
+                                full=True)
+    assert (rc, S, nb) == (0, 3 * 2 * 2 + 2048, S * 8 * (128 + 1) * 4)
+    # an explicit partition size selects partitions, rounded up to whole pages
+    rc, S, P, nb, sched = _plan(L, a, P=1000, full=True)
+    assert (rc, P, S, sched) == (0, 1008, -(-131072 // 1008), SCHEDULE_PARTITIONS)
     # a single partition needs no workspace
     rc, S, P, nb = _plan(L, h.args(max_pages=4), P=64)
-    assert (rc, S, nb) == (0, 1, 256)
+    assert (rc, S, nb) == (0, 1, 0)
+    # past the balanced batch limit the library picks partitions
+    rc, S, P, nb, sched = _plan(L, h.args(batch=4096, max_pages=256, num_pages=4096), full=True)
+    assert rc == 0 and sched == SCHEDULE_PARTITIONS and S * P >= 256 * 16
     # decode plans only exist for L <= 8
     assert _plan(L, h.args(q_len=9))[0] == -1

@@ -141,14 +141,15 @@ def test_split_reduce_alone_on_oracle_partials(api):
     assert_parity(out, oracle.merge(po, pl), "f32", "merge")
 
 
-def test_physical_relabel_and_stale_data_bit_identical(api):
+@pytest.mark.parametrize("P", [32, 0])
+def test_physical_relabel_and_stale_data_bit_identical(api, P):
     kw = dict(B=4, H_q=8, H_kv=2, L=1, D=128, page_size=16, ctx=[5, 33, 100, 250],
               dtype="bf16", causal=True, extra_free_pages=6)
     x = make_random(51, garbage=1e4, **kw)
-    base, _ = run_decode(api, DeviceInputs(x), partition_tokens=32)
+    base, _ = run_decode(api, DeviceInputs(x), partition_tokens=P)
     for garbage in (-1e4, 0.0, "nan"):
         y = make_random(51, garbage=garbage, **kw)
-        o, _ = run_decode(api, DeviceInputs(y), partition_tokens=32)
+        o, _ = run_decode(api, DeviceInputs(y), partition_tokens=P)
         assert np.array_equal(host_f64(o), host_f64(base)), f"garbage={garbage}"
     rng = np.random.default_rng(9)
     pi = rng.permutation(x.num_pages)
@@ -157,7 +158,7 @@ def test_physical_relabel_and_stale_data_bit_identical(api):
     kp2[pi], vp2[pi] = x.key_pages, x.value_pages
     x.key_pages, x.value_pages = kp2, vp2
     x.block_table = np.where(x.block_table >= 0, pi[np.maximum(x.block_table, 0)], -1).astype(np.int32)
-    o, _ = run_decode(api, DeviceInputs(x), partition_tokens=32)
+    o, _ = run_decode(api, DeviceInputs(x), partition_tokens=P)
     assert np.array_equal(host_f64(o), host_f64(base))
 
 
@@ -183,25 +184,37 @@ def test_c4_long_context_parity_sampled(api):
     print(f"[C4] max abs err (requests 0-1) {err:.3e}", flush=True)
 
 
-@pytest.mark.parametrize("P", [0, 64, 4096])
-def test_queue_and_grid_schedules_agree_and_reset_counters(api, P):
-    """The persistent work queue and the plain grid run the same items: the
-    outputs are bit-identical, and the queue leaves its counters at zero."""
+@pytest.mark.parametrize("num_cus", [1, 3, 16, 0])
+def test_balanced_schedule_parity_and_repeat(api, num_cus):
+    """The balanced schedule (equal runs of steps per wave, rows spread over
+    up to num_splits pieces) matches the oracle whatever the plan's piece
+    bound, visits every key exactly once, and a second call on the same
+    workspace gives the same bits (stale partial states are never read)."""
     import torch
     x = make_random(71, B=9, H_q=16, H_kv=4, L=1, D=128, page_size=16,
                     ctx=[0, 1, 16, 63, 64, 65, 700, 1500, 4000], dtype="bf16", causal=False)
     d = DeviceInputs(x)
-    a, exa = run_decode(api, d, partition_tokens=P, queue=True)
-    b, exb = run_decode(api, d, partition_tokens=P, queue=False)
-    assert np.array_equal(host_f64(a), host_f64(b))
-    assert int(exa["ws"].counters.abs().sum()) == 0
-    assert_parity(a, oracle.attention_of(x), "bf16", f"queue P={P}")
-    # run the same workspace again: counters were reset by the previous call
-    args = exa["args"]
+    a, ex = run_decode(api, d, num_cus=num_cus, trace=True)
+    print(f"[balanced] num_cus={num_cus} S={ex['S']}", flush=True)
+    assert ex["schedule"] == api.SCHEDULE_BALANCED and ex["S"] >= 2
+    assert_parity(a, oracle.attention_of(x), "bf16", f"balanced cus={num_cus}")
+    assert np.array_equal(ex["visits"], _expect_visits(x))
+    args = ex["args"]
+    args.debug_trace = args.debug_visits = None
     out2 = torch.full_like(d.q, float("nan"))
     args.out = out2.data_ptr()
-    api.pa_decode(args, exa["ws"])
-    if exa["S"] > 1:
-        api.pa_split_reduce(args, exa["ws"])
+    api.pa_decode(args, ex["ws"])
+    api.pa_split_reduce(args, ex["ws"])
     torch.cuda.synchronize()
     assert np.array_equal(host_f64(out2), host_f64(a))
+
+
+def test_balanced_and_partition_schedules_agree(api):
+    x = make_random(72, B=5, H_q=32, H_kv=8, L=2, D=128, page_size=16,
+                    ctx=[2, 300, 1025, 77, 2048], dtype="bf16", causal=True,
+                    query_lens=[2, 1, 2, 0, 2])
+    d = DeviceInputs(x)
+    ref = oracle.attention_of(x)
+    for kw in (dict(num_cus=2), dict(partition_tokens=128), dict()):
+        out, ex = run_decode(api, d, **kw)
+        assert_parity(out, ref, "bf16", f"{kw} S={ex['S']}")
