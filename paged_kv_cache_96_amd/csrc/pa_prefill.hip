@@ -1,24 +1,40 @@
 // bf16 paged prefill kernel on gfx950 matrix cores.
 //
-// Work: one workgroup (4 waves) owns BM = 128 packed query rows of one
+// Work: one workgroup (4 waves) owns BM = 128 * RB packed query rows of one
 // (request b, kv head g); packed row rho is position rho / G of head
 // g*G + rho % G, so the G heads that share a kv head share every K/V tile and
-// the rows of a tile sit at nearly the same causal position.  Keys are walked
+// the rows of a tile sit at nearly the same causal position.  A wave owns RB
+// blocks of 32 rows: every K and V operand it reads from LDS feeds RB matrix
+// instructions (the launcher uses RB = 1; see launch_d).  Keys are walked
 // in tiles of BN = 64 (tiny-llm "Week 3 Day 4", "Task 2": resolve every K/V
 // tile through the block table, fold it in with the online softmax).
 //
 // Per key tile:
-//   1. staging: every thread issues 16-byte loads of the NEXT tile's K and V
-//      rows (address = physical page from the block table, slot, kv head)
-//      into registers while the current tile is computed, then stores them to
-//      the other LDS buffer (double buffering, one barrier per tile);
+//   1. staging: every thread issues 16-byte loads of the K and V rows of the
+//      tile TWO ahead (address = physical page from the block table, slot, kv
+//      head) into one of two register sets while the current tile is
+//      computed, and stores the set loaded one tile earlier (the next tile)
+//      to the other LDS buffer, so a load has a whole tile of compute to
+//      arrive (two LDS buffers, one barrier per tile).  When
+//      page_size is a multiple of 16, each 16-key staging round lies in one
+//      page: its block-table entry is a scalar load (SGPR) and the round is a
+//      buffer load from that page with a per-thread offset fixed for the
+//      whole walk, so staging costs no per-lane address arithmetic;
 //   2. S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: K from LDS is the A
 //      operand, Q (kept in registers for the whole walk) the B operand.  The
 //      result gives every lane the scores of ONE query row (lane % 32) against
 //      16 of the tile's keys; the other 16 sit in lane ^ 32;
-//   3. online softmax in registers (row max over the lane pair with a
-//      permlane32 swap, exp2 of pre-scaled scores, fp32 row sums), P rounded
-//      to bf16 once;
+//   3. softmax in registers (row max over the lane pair with a permlane32
+//      swap, exp2 of pre-scaled scores, fp32 row sums), P rounded to bf16
+//      once.  The weights of a row are taken relative to a reference max
+//      fixed by the row's first key block (key 0 is visible to every row),
+//      so O is never rescaled inside the walk and stays in accumulation
+//      registers that only the matrix instructions touch.  Softmax does not
+//      depend on the reference; bf16 and fp32 hold weights up to 2^16 with
+//      the same relative precision as weights <= 1.  The true running max
+//      is tracked, and if any row of the workgroup exceeds its reference by
+//      more than 2^16 the workgroup walks its keys again with the exact max
+//      as reference (weights <= 1), which keeps every input finite;
 //   4. O^T += V^T . P^T with the same MFMA: P^T comes straight from the
 //      lane's own registers (B operand); V^T (A operand) is read from the
 //      natural [key][d] LDS tile with ds_read_b64_tr_b16, which hands each
@@ -36,8 +52,12 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-constexpr int kBM = 128;   // packed query rows per workgroup (32 per wave)
 constexpr int kBN = 64;    // keys per tile
+constexpr float kMinM = -1.0e30f;  // reference sentinel: exp2(-inf - kMinM) = 0
+constexpr float kRefSlack = 16.0f; // largest row max above the reference (log2) a walk accepts
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= 8 (the eight loads of one
+// staging set may stay in flight), expcnt and lgkmcnt not waited for.
+constexpr int kWaitVmcntOlderThan8 = 8 | (0x7 << 4) | (0xF << 8);
 
 template <int D>
 struct Tile {
@@ -65,8 +85,20 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, bool DEBUG>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchParams p, int num_tiles) {
+// Staging modes.  kStageLanes: every lane resolves its own key (any page
+// size; debug trace).  kStageRun: page_size a multiple of the run length, one
+// buffer resource per run.  kStagePool: the same runs, with one resource for
+// the whole K (V) pool and the run's position in the SGPR offset (pools
+// under 2 GiB, so that offsets stay below 2^31 and an offset of 2^31 is
+// always out of range).
+enum StageMode { kStageLanes = 0, kStageRun = 1, kStagePool = 2 };
+
+template <int D, bool DEBUG, int MODE, int RB>
+__global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchParams p,
+                                                                       int num_tiles) {
+  constexpr bool UNIFORM = MODE != kStageLanes;
+  constexpr int kRW = 32 * RB;     // packed rows per wave
+  constexpr int kBM = 4 * kRW;     // packed rows per workgroup
   using TL = Tile<D>;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kBN * TL::kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kBN * TL::kVStride];
@@ -87,19 +119,24 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchParams p, int num
   const int rows_all = G * p.L;
   const int rho0 = tile * kBM;
 
-  // ---- this lane's query row
-  const int rho = rho0 + wave * 32 + ln;
-  const int qi = rho / G;
-  const int qh = g * G + (rho - qi * G);
-  const bool row_valid = rho < rows_valid;
-  const int lim = row_valid ? (p.causal ? ctx - Lb + qi + 1 : ctx) : 0;
+  // ---- this lane's query rows (one per row block)
+  int rho[RB], qi[RB], qh[RB], lim[RB];
+  bool row_valid[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    rho[rb] = rho0 + wave * kRW + rb * 32 + ln;
+    qi[rb] = rho[rb] / G;
+    qh[rb] = g * G + (rho[rb] - qi[rb] * G);
+    row_valid[rb] = rho[rb] < rows_valid;
+    lim[rb] = row_valid[rb] ? (p.causal ? ctx - Lb + qi[rb] + 1 : ctx) : 0;
+  }
 
   // ---- key ranges: the workgroup's (for staging) and this wave's (compute)
   const int rho_last_wg = min(rho0 + kBM, rows_valid) - 1;
   const int kend_wg = rho_last_wg < rho0 ? 0
                       : (p.causal ? ctx - Lb + rho_last_wg / G + 1 : ctx);
-  const int rho_first_w = rho0 + wave * 32;
-  const int rho_last_w = min(rho_first_w + 32, rows_valid) - 1;
+  const int rho_first_w = rho0 + wave * kRW;
+  const int rho_last_w = min(rho_first_w + kRW, rows_valid) - 1;
   const int kend_w = rho_last_w < rho_first_w ? 0
                      : (p.causal ? ctx - Lb + rho_last_w / G + 1 : ctx);
   const int kfull_w = rho_last_w < rho_first_w ? 0
@@ -108,13 +145,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchParams p, int num
   const bool counts = DEBUG && rows_valid > 0 && (rows_valid - 1) / kBM == tile;
 
   // ---- Q as the B operand of S^T = K Q^T: dims kk*16 + half*8 .. +8
-  uint4 q[TL::kKSteps];
-  {
+  uint4 q[RB][TL::kKSteps];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
     const uint16_t *qp = reinterpret_cast<const uint16_t *>(p.q) +
-                         ((size_t)(b * p.Hq + qh) * p.L + qi) * D + half * 8;
+                         ((size_t)(b * p.Hq + qh[rb]) * p.L + qi[rb]) * D + half * 8;
 #pragma unroll
     for (int kk = 0; kk < TL::kKSteps; ++kk)
-      q[kk] = row_valid ? *reinterpret_cast<const uint4 *>(qp + kk * 16) : make_uint4(0, 0, 0, 0);
+      q[rb][kk] = row_valid[rb] ? *reinterpret_cast<const uint4 *>(qp + kk * 16)
+                                : make_uint4(0, 0, 0, 0);
   }
 
   // ---- staging of one K/V tile: thread -> (key kr*KPR + tid / CH, chunk tid % CH)
@@ -123,9 +162,80 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchParams p, int num
   const int32_t *bt = p.bt + (size_t)b * p.max_pages;
   const int chunk = tid % TL::kChunks;
   const int key_in_round = tid / TL::kChunks;
-  uint4 kst[TL::kRounds], vst[TL::kRounds];
+  struct Stage {
+    uint4 k[TL::kRounds], v[TL::kRounds];
+  };
 
-  auto stage_load = [&](int kt) {
+  // The block table is read-only for the whole call: reading it through the
+  // constant address space lets wave-uniform entries come in by scalar loads.
+  typedef const __attribute__((address_space(4))) int32_t *const_i32_ptr;
+  const const_i32_ptr btc = (const_i32_ptr)bt;
+  // page-uniform rounds: per-thread byte offset within a 16-key run of a page
+  const int run_off = (key_in_round * D + chunk * 8) * 2;
+  // Every load is issued unconditionally: a run past the workgroup's last
+  // key gets a resource of size 0 (its loads return zeros without touching
+  // memory), so no register is ever written conditionally and the compiler's
+  // wait counts only ever wait for the set that is about to be stored.
+  // Runs are loaded strictly in key order, so the run's logical page and
+  // slot are advanced incrementally (scalar registers): a new block-table
+  // entry is read only when a run starts a page.
+  const long long page_bytes = (long long)p.Hkv * p.ps * D * 2;
+  const long long head_bytes = (long long)g * p.ps * D * 2;
+  const char *kp_bytes = reinterpret_cast<const char *>(p.kp);
+  const char *vp_bytes = reinterpret_cast<const char *>(p.vp);
+  int run_j0 = 0, run_lp = 0, run_slot = 0, run_page = 0;
+  int pass = 0;  // 1: the walk again with exact row maxima
+  const int pool_bytes = (int)((long long)p.num_pages * page_bytes);  // kStagePool only
+  const __amdgpu_buffer_rsrc_t pool_k = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char *>(kp_bytes), (short)0, pool_bytes, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t pool_v = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char *>(vp_bytes), (short)0, pool_bytes, kBufferRsrcWord3);
+  auto stage_load_uniform = [&](int kt, Stage &st) {
+    (void)kt;  // runs follow run_j0, which tracks kt * BN
+#pragma unroll
+    for (int r = 0; r < TL::kRounds; ++r) {
+      const bool live = run_j0 < kend_wg;                 // wave-uniform
+      if (run_slot == 0) run_page = live ? btc[min(run_lp, p.max_pages - 1)] : 0;
+      if constexpr (MODE == kStagePool) {
+        const int soff = run_page * (int)page_bytes + (int)head_bytes + run_slot * (D * 2);
+        const int voff = run_j0 + key_in_round < kend_wg ? run_off : (int)0x80000000u;
+        const u32x4_t kv = __builtin_amdgcn_raw_buffer_load_b128(pool_k, voff, soff, 0);
+        const u32x4_t vv = __builtin_amdgcn_raw_buffer_load_b128(pool_v, voff, soff, 0);
+        st.k[r] = make_uint4(kv[0], kv[1], kv[2], kv[3]);
+        st.v[r] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+        run_j0 += TL::kKeysPerRound;
+        run_slot += TL::kKeysPerRound;
+        if (run_slot == p.ps) {
+          run_slot = 0;
+          ++run_lp;
+        }
+        continue;
+      }
+      const long long off = (long long)run_page * page_bytes + head_bytes + run_slot * (D * 2);
+      const int nrec = live ? (p.ps - run_slot) * D * 2 : 0;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char *>(kp_bytes + off), (short)0, nrec, kBufferRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char *>(vp_bytes + off), (short)0, nrec, kBufferRsrcWord3);
+      // keys at or past kend_wg read as zeros (offset past the resource)
+      const int voff = run_j0 + key_in_round < kend_wg ? run_off : 0x40000000;
+      const u32x4_t kv = __builtin_amdgcn_raw_buffer_load_b128(rk, voff, 0, 0);
+      const u32x4_t vv = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0);
+      st.k[r] = make_uint4(kv[0], kv[1], kv[2], kv[3]);
+      st.v[r] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+      run_j0 += TL::kKeysPerRound;
+      run_slot += TL::kKeysPerRound;
+      if (run_slot == p.ps) {
+        run_slot = 0;
+        ++run_lp;
+      }
+    }
+  };
+  auto stage_load = [&](int kt, Stage &st) {
+    if constexpr (UNIFORM) {
+      stage_load_uniform(kt, st);
+      return;
+    }
 #pragma unroll
     for (int r = 0; r < TL::kRounds; ++r) {
       const int j = kt * kBN + r * TL::kKeysPerRound + key_in_round;
@@ -134,10 +244,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchParams p, int num
         const int page = bt[lp];
         const int slot = j - lp * p.ps;
         const size_t off = (((size_t)page * p.Hkv + g) * p.ps + slot) * D + chunk * 8;
-        kst[r] = *reinterpret_cast<const uint4 *>(kp + off);
-        vst[r] = *reinterpret_cast<const uint4 *>(vp + off);
+        st.k[r] = *reinterpret_cast<const uint4 *>(kp + off);
+        st.v[r] = *reinterpret_cast<const uint4 *>(vp + off);
         if constexpr (DEBUG) {
-          if (counts && chunk == 0) {
+          if (counts && chunk == 0 && pass == 0) {
             const size_t cap = (size_t)p.max_pages * p.ps;
             if (g == 0) {
               p.dbg_trace[((size_t)b * cap + j) * 2 + 0] = page;
@@ -147,152 +257,223 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(LaunchParams p, int num
           }
         }
       } else {
-        kst[r] = make_uint4(0, 0, 0, 0);  // never loaded: zeros keep masked math finite
-        vst[r] = make_uint4(0, 0, 0, 0);
+        st.k[r] = make_uint4(0, 0, 0, 0);  // never loaded: zeros keep masked math finite
+        st.v[r] = make_uint4(0, 0, 0, 0);
       }
     }
   };
-  auto stage_store = [&](int buf) {
+  auto stage_store = [&](int buf, const Stage &st) {
 #pragma unroll
     for (int r = 0; r < TL::kRounds; ++r) {
       const int key = r * TL::kKeysPerRound + key_in_round;
-      *reinterpret_cast<uint4 *>(&k_lds[buf][key * TL::kKStride + chunk * 8]) = kst[r];
-      *reinterpret_cast<uint4 *>(&v_lds[buf][key * TL::kVStride + chunk * 8]) = vst[r];
+      *reinterpret_cast<uint4 *>(&k_lds[buf][key * TL::kKStride + chunk * 8]) = st.k[r];
+      *reinterpret_cast<uint4 *>(&v_lds[buf][key * TL::kVStride + chunk * 8]) = st.v[r];
     }
   };
 
-  // ---- running state of this lane's query row
-  f32x16_t o[TL::kMBlocks];
+  // ---- state of this lane's query rows
+  f32x16_t o[RB][TL::kMBlocks];
+  float m_ref[RB], m_seen[RB], l_run[RB];
 #pragma unroll
-  for (int mb = 0; mb < TL::kMBlocks; ++mb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[mb][i] = 0.f;
-  float m_run = kNegInf, l_run = 0.f;
+  for (int rb = 0; rb < RB; ++rb) {
+    m_ref[rb] = kMinM;
+    m_seen[rb] = kMinM;
+  }
   const float c = p.scale_log2;
 
-  if (ntiles > 0) {
-    stage_load(0);
-    stage_store(0);
+  // Register staging: with one row block per wave, two sets (set A holds
+  // even tiles, set B odd ones) so that loads run two tiles ahead; with two
+  // row blocks a tile is long enough for loads one tile ahead, in one set.
+  constexpr bool kTwoSets = RB == 1;
+  Stage sa, sb;
+ for (; pass < 2; ++pass) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int mb = 0; mb < TL::kMBlocks; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[rb][mb][i] = 0.f;
+    l_run[rb] = 0.f;
   }
+  run_j0 = run_lp = run_slot = 0;
+  if (ntiles > 0) {
+    stage_load(0, sa);
+    stage_store(0, sa);
+  }
+  if (kTwoSets && (UNIFORM || ntiles > 1)) stage_load(1, sb);
+  // the query and tile-0 loads are complete here; tile 1 stays in flight
+  __builtin_amdgcn_s_waitcnt(kWaitVmcntOlderThan8);
   __syncthreads();
 
-  for (int kt = 0; kt < ntiles; ++kt) {
+  // One tile: prefetch tile kt + 2 into `ld` (its set is free: tile kt was
+  // stored to LDS one tile ago), compute tile kt, then store tile kt + 1
+  // (loaded into `st` one tile ago) to the other LDS buffer.
+  auto tile_step = [&](int kt, Stage &ld, const Stage &st) {
     const int buf = kt & 1;
     const bool more = kt + 1 < ntiles;
-    if (more) stage_load(kt + 1);
+    if constexpr (kTwoSets) {
+      if (UNIFORM || kt + 2 < ntiles) stage_load(kt + 2, ld);
+    } else {
+      if (UNIFORM || more) stage_load(kt + 1, ld);
+    }
 
     if (kt * kBN < kend_w) {
-      // -- S^T for the two 32-key blocks of the tile
-      f32x16_t s[2];
+      // The tile's two 32-key blocks are processed one after the other
+      // (scores, softmax, PV), which keeps the score and P registers of a
+      // single block live.
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
+        // -- S^T of this block; each K operand read from LDS feeds the RB
+        //    row blocks
+        f32x16_t s[RB];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[blk][i] = 0.f;
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[rb][i] = 0.f;
         const uint16_t *krow = &k_lds[buf][(blk * 32 + ln) * TL::kKStride + half * 8];
 #pragma unroll
         for (int kk = 0; kk < TL::kKSteps; ++kk) {
           const uint4 a = *reinterpret_cast<const uint4 *>(krow + kk * 16);
-          s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(q[kk]), s[blk],
-                                                           0, 0, 0);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(q[rb][kk]),
+                                                            s[rb], 0, 0, 0);
         }
-      }
-      // -- mask keys at or past this row's limit (diagonal / tail tiles only)
-      if ((kt + 1) * kBN > kfull_w) {
+        // -- mask keys at or past each row's limit (diagonal / tail blocks only)
+        if (kt * kBN + (blk + 1) * 32 > kfull_w) {
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+          for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kt * kBN + blk * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-            if (key >= lim) s[blk][i] = kNegInf;
+            for (int i = 0; i < 16; ++i) {
+              const int key = kt * kBN + blk * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+              if (key >= lim[rb]) s[rb][i] = kNegInf;
+            }
+        }
+        // -- online softmax update of each row
+        uint32_t pb[RB][8];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          float mx = s[rb][0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[rb][i]);
+          mx = pair_max(mx) * c;
+          if (pass == 0 && kt == 0 && blk == 0) m_ref[rb] = fmaxf(mx, kMinM);
+          m_seen[rb] = fmaxf(m_seen[rb], mx);
+          float psum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) {
+            const float p0 = fast_exp2(fmaf(s[rb][i], c, -m_ref[rb]));  // masked -> 0
+            const float p1 = fast_exp2(fmaf(s[rb][i + 1], c, -m_ref[rb]));
+            psum += p0 + p1;
+            pb[rb][i >> 1] = cvt_pk_bf16(p0, p1);
           }
-      }
-      // -- online softmax update for this row
-      float mx = s[0][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-      mx = pair_max(mx);
-      const float m_new = fmaxf(m_run, mx * c);
-      const bool none = m_new == kNegInf;
-      const float alpha = none ? 1.f : fast_exp2(m_run - m_new);
-      m_run = m_new;
-      uint32_t pb[2][8];
-      float psum = 0.f;
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) {
-          const float p0 = none ? 0.f : fast_exp2(fmaf(s[blk][i], c, -m_new));
-          const float p1 = none ? 0.f : fast_exp2(fmaf(s[blk][i + 1], c, -m_new));
-          psum += p0 + p1;
-          pb[blk][i >> 1] = cvt_pk_bf16(p0, p1);
+          l_run[rb] += psum;
         }
-      l_run = fmaf(l_run, alpha, psum);
-#pragma unroll
-      for (int mb = 0; mb < TL::kMBlocks; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[mb][i] *= alpha;
 
-      // -- O^T += V^T P^T over four 16-key steps
+        // -- O^T += V^T P^T over the block's two 16-key steps; each V^T
+        //    operand feeds the RB row blocks
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int blk = ks >> 1, hf = ks & 1;
-        const uint4 bop = make_uint4(pb[blk][hf * 4 + 0], pb[blk][hf * 4 + 1], pb[blk][hf * 4 + 2],
-                                     pb[blk][hf * 4 + 3]);
-        // keys of the two 4-key runs this lane's k slots stand for
-        const int kb = blk * 32 + hf * 16 + half * 4;
-        const int src = lane & 15;  // transpose read: source lane j reads row kb + j/4, cols +4*(j%4)
+        for (int hf = 0; hf < 2; ++hf) {
+          uint4 bop[RB];
 #pragma unroll
-        for (int mb = 0; mb < TL::kMBlocks; ++mb) {
-          const int d0 = mb * 32 + ((lane >> 4) & 1) * 16 + 4 * (src & 3);
-          const uint16_t *r1 = &v_lds[buf][(kb + (src >> 2)) * TL::kVStride + d0];
-          const uint16_t *r2 = r1 + 8 * TL::kVStride;
-          const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)r1);
-          const s16x4_t t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)r2);
-          const uint4 aop = make_uint4(
-              (uint32_t)(uint16_t)t1[0] | ((uint32_t)(uint16_t)t1[1] << 16),
-              (uint32_t)(uint16_t)t1[2] | ((uint32_t)(uint16_t)t1[3] << 16),
-              (uint32_t)(uint16_t)t2[0] | ((uint32_t)(uint16_t)t2[1] << 16),
-              (uint32_t)(uint16_t)t2[2] | ((uint32_t)(uint16_t)t2[3] << 16));
-          o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(aop), as_bf16x8(bop), o[mb],
-                                                          0, 0, 0);
+          for (int rb = 0; rb < RB; ++rb)
+            bop[rb] = make_uint4(pb[rb][hf * 4 + 0], pb[rb][hf * 4 + 1], pb[rb][hf * 4 + 2],
+                                 pb[rb][hf * 4 + 3]);
+          // keys of the two 4-key runs this lane's k slots stand for
+          const int kb = blk * 32 + hf * 16 + half * 4;
+          const int src = lane & 15;  // transpose read: source lane j reads row kb + j/4, cols +4*(j%4)
+#pragma unroll
+          for (int mb = 0; mb < TL::kMBlocks; ++mb) {
+            const int d0 = mb * 32 + ((lane >> 4) & 1) * 16 + 4 * (src & 3);
+            const uint16_t *r1 = &v_lds[buf][(kb + (src >> 2)) * TL::kVStride + d0];
+            const uint16_t *r2 = r1 + 8 * TL::kVStride;
+            const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)r1);
+            const s16x4_t t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)r2);
+            const uint4 aop = make_uint4(
+                (uint32_t)(uint16_t)t1[0] | ((uint32_t)(uint16_t)t1[1] << 16),
+                (uint32_t)(uint16_t)t1[2] | ((uint32_t)(uint16_t)t1[3] << 16),
+                (uint32_t)(uint16_t)t2[0] | ((uint32_t)(uint16_t)t2[1] << 16),
+                (uint32_t)(uint16_t)t2[2] | ((uint32_t)(uint16_t)t2[3] << 16));
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              o[rb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  as_bf16x8(aop), as_bf16x8(bop[rb]), o[rb][mb], 0, 0, 0);
+          }
         }
       }
     }
 
-    if (more) stage_store(buf ^ 1);
+    if (more) stage_store(buf ^ 1, st);
     __syncthreads();
+  };
+  if constexpr (kTwoSets) {
+    for (int kt = 0; kt < ntiles; kt += 2) {  // unrolled by two so the sets stay in registers
+      tile_step(kt, sa, sb);
+      if (kt + 1 < ntiles) tile_step(kt + 1, sb, sa);
+    }
+  } else {
+    for (int kt = 0; kt < ntiles; ++kt) tile_step(kt, sa, sa);
   }
+  // weights past 2^16 anywhere in the workgroup: walk again from the exact maxima
+  bool over = false;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) over |= m_seen[rb] > m_ref[rb] + kRefSlack;
+  if (pass == 1 || !__syncthreads_or(over)) break;
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) m_ref[rb] = m_seen[rb];
+ }
 
   // ---- finalize: O = O^T / l, rounded to bf16; padding rows get zeros
-  const float l_tot = pair_sum(l_run);  // uniform: every lane of the wave takes part
-  if (rho < rows_all) {
-    const float inv = (row_valid && l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    uint16_t *op = reinterpret_cast<uint16_t *>(p.out) + ((size_t)(b * p.Hq + qh) * p.L + qi) * D;
 #pragma unroll
-    for (int mb = 0; mb < TL::kMBlocks; ++mb)
+  for (int rb = 0; rb < RB; ++rb) {
+    const float l_tot = pair_sum(l_run[rb]);  // uniform: every lane of the wave takes part
+    if (rho[rb] < rows_all) {
+      const float inv = (row_valid[rb] && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+      uint16_t *op = reinterpret_cast<uint16_t *>(p.out) +
+                     ((size_t)(b * p.Hq + qh[rb]) * p.L + qi[rb]) * D;
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = mb * 32 + i4 * 8 + half * 4;
-        const uint2 w = make_uint2(cvt_pk_bf16(o[mb][i4 * 4 + 0] * inv, o[mb][i4 * 4 + 1] * inv),
-                                   cvt_pk_bf16(o[mb][i4 * 4 + 2] * inv, o[mb][i4 * 4 + 3] * inv));
-        *reinterpret_cast<uint2 *>(op + d) = w;
-      }
+      for (int mb = 0; mb < TL::kMBlocks; ++mb)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = mb * 32 + i4 * 8 + half * 4;
+          const f32x16_t &om = o[rb][mb];
+          const uint2 w = make_uint2(cvt_pk_bf16(om[i4 * 4 + 0] * inv, om[i4 * 4 + 1] * inv),
+                                     cvt_pk_bf16(om[i4 * 4 + 2] * inv, om[i4 * 4 + 3] * inv));
+          *reinterpret_cast<uint2 *>(op + d) = w;
+        }
+    }
   }
 }
 
-template <int D>
-hipError_t launch_d(const LaunchParams &p, hipStream_t stream) {
+template <int D, int RB>
+hipError_t launch_rb(const LaunchParams &p, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
-  const int tiles = (G * p.L + kBM - 1) / kBM;
+  const int bm = 128 * RB;
+  const int tiles = (G * p.L + bm - 1) / bm;
   dim3 grid(tiles, p.Hkv, p.B);
+  const long long pool = (long long)p.num_pages * p.Hkv * p.ps * D * 2;
   if (p.dbg_trace || p.dbg_visits) {
-    hipLaunchKernelGGL((prefill_kernel<D, true>), grid, dim3(256), 0, stream, p, tiles);
+    hipLaunchKernelGGL((prefill_kernel<D, true, kStageLanes, RB>), grid, dim3(256), 0, stream, p,
+                       tiles);
+  } else if (p.ps % Tile<D>::kKeysPerRound != 0) {  // runs would straddle pages
+    hipLaunchKernelGGL((prefill_kernel<D, false, kStageLanes, RB>), grid, dim3(256), 0, stream, p,
+                       tiles);
+  } else if (pool < (1ll << 31)) {
+    hipLaunchKernelGGL((prefill_kernel<D, false, kStagePool, RB>), grid, dim3(256), 0, stream, p,
+                       tiles);
   } else {
-    hipLaunchKernelGGL((prefill_kernel<D, false>), grid, dim3(256), 0, stream, p, tiles);
+    hipLaunchKernelGGL((prefill_kernel<D, false, kStageRun, RB>), grid, dim3(256), 0, stream, p,
+                       tiles);
   }
   return hipGetLastError();
+}
+
+// One row block per wave: two row blocks halve the LDS traffic per flop but
+// need the accumulation registers of 64 rows, which leaves one wave per SIMD
+// and measured slower than two waves of one row block each.
+template <int D>
+hipError_t launch_d(const LaunchParams &p, hipStream_t stream) {
+  return launch_rb<D, 1>(p, stream);
 }
 
 }  // namespace

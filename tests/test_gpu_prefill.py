@@ -60,6 +60,9 @@ def test_prefill_parity_random_shapes(api, case):
             v[b] = 0
     assert np.array_equal(ex["trace"], tr)
     assert np.array_equal(ex["visits"], v)
+    # the same inputs through the fast staging paths (no trace)
+    out2, _ = run_prefill(api, DeviceInputs(x))
+    assert_parity(out2, ref, dt, f"prefill case{seed} fast path")
 
 
 def test_prefill_stale_data_and_relabel_bit_identical(api):
@@ -112,3 +115,47 @@ def test_c5_mixed_batch_full_size(api):
     err_d = assert_parity(out_d, oracle.attention_of(m.decode), "bf16", "C5 decode")
     err_p = assert_parity(out_p, oracle.attention_of(m.prefill), "bf16", "C5 prefill")
     print(f"[C5] decode S={ex['S']} err {err_d:.3e}; prefill err {err_p:.3e}", flush=True)
+
+
+def _plant_spike(x, b, j, coef):
+    """Make logical key j of request b score far above every other key for
+    the query rows of the kv head that share it: K[j] = coef * (sum of that
+    group's last-row queries).  With coef 16 the row maxima sit about 2^200
+    above the first key block's (base-2 units), past the fp32 range, so
+    only an exact reference gives finite weights."""
+    from workloads import bf16_bits_to_f32, f32_to_bf16_bits
+    G = x.H_q // x.H_kv
+    ps = x.page_size
+    page, slot = int(x.block_table[b, j // ps]), j % ps
+    q = x.query if x.dtype == "f32" else bf16_bits_to_f32(x.query)
+    for g in range(x.H_kv):
+        lb = x.L - 1 if x.query_lens is None else int(x.query_lens[b]) - 1
+        d = q[b, g * G:(g + 1) * G, lb, :].astype(np.float64).sum(axis=0)
+        k = (coef * d).astype(np.float32)
+        x.key_pages[page, g, slot, :] = k if x.dtype == "f32" else f32_to_bf16_bits(k)
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_late_score_spike_is_exact(api, dtype):
+    """A key past the first block that scores more than 2^16 above the first
+    block's maximum (in the base-2 units the kernel uses) must give the same
+    result as any other input: the walk is redone from the exact maxima."""
+    x = make_random(81, B=2, H_q=8, H_kv=2, L=130, D=128, page_size=16, ctx=[400, 200],
+                    dtype=dtype, causal=True)
+    x = _plant_spike(x, 0, 300, 16.0)
+    x = _plant_spike(x, 1, 150, 16.0)
+    ref = oracle.attention_of(x)
+    out, _ = run_prefill(api, DeviceInputs(x))
+    assert_parity(out, ref, dtype, "prefill spike")
+
+
+def test_decode_late_score_spike_is_exact(api):
+    x = make_random(82, B=3, H_q=16, H_kv=4, L=1, D=128, page_size=16, ctx=[900, 300, 2000],
+                    dtype="bf16", causal=True)
+    for b, j in ((0, 700), (1, 299), (2, 1999)):
+        x = _plant_spike(x, b, j, 16.0)
+    ref = oracle.attention_of(x)
+    for kw in (dict(), dict(partition_tokens=64)):
+        out, _ = run_decode(api, DeviceInputs(x), **kw)
+        assert_parity(out, ref, "bf16", f"decode spike {kw}")
