@@ -79,7 +79,11 @@ class Runner:
         from tests._gpu import DeviceInputs
         return DeviceInputs(x, pages=pages)
 
-    def time_decode(self, d, steps, warmup, partition_tokens=0, num_cus=0):
+    def time_decode(self, d, steps, warmup, partition_tokens=0, num_cus=0, fused=True):
+        """Times `steps` decode steps (pa_decode + pa_split_reduce, one event
+        pair around both), then `steps` launches of pa_decode alone (its own
+        event pair) for the kernel figure; the last-level cache is flushed
+        before each."""
         torch, api = self.torch, self.api
         x = d.x
         out = torch.empty_like(d.q)
@@ -87,30 +91,40 @@ class Runner:
                              query_lens=d.ql)
         plan = api.pa_decode_plan(args, partition_tokens=partition_tokens, num_cus=num_cus)
         S, P = plan.num_splits, plan.partition_tokens
-        ws = api.Workspace.for_plan(plan, d.q)
-        for _ in range(warmup):
-            self.flush()
+        ws = api.Workspace.for_plan(plan, d.q, fused=fused)
+
+        def step():
             api.pa_decode(args, ws)
             if S > 1:
                 api.pa_split_reduce(args, ws)
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+
+        for _ in range(warmup):
+            self.flush()
+            step()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for k in range(steps):
             self.flush()
             ev[k][0].record()
-            api.pa_decode(args, ws)
+            step()
             ev[k][1].record()
-            if S > 1:
-                api.pa_split_reduce(args, ws)
-            ev[k][2].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        dec = np.array([e[0].elapsed_time(e[1]) for e in ev])    # ms
-        red = np.array([e[1].elapsed_time(e[2]) for e in ev])
-        return {"S": S, "P": P, "schedule": "balanced" if plan.schedule == api.SCHEDULE_BALANCED
-                else "partitions", "decode_ms": dec, "reduce_ms": red, "step_ms": dec + red,
-                "wall_s": wall, "out": out}
+        step_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for k in range(steps):
+            self.flush()
+            kev[k][0].record()
+            api.pa_decode(args, ws)
+            kev[k][1].record()
+        if S > 1:
+            api.pa_split_reduce(args, ws)  # leave `out` complete
+        torch.cuda.synchronize()
+        dec = np.array([e[0].elapsed_time(e[1]) for e in kev])
+        sched = "balanced" if plan.schedule == api.SCHEDULE_BALANCED else "partitions"
+        return {"S": S, "P": P, "schedule": sched, "fused": bool(ws.counters is not None),
+                "decode_ms": dec, "step_ms": step_ms, "wall_s": wall, "out": out}
 
     def time_prefill(self, d, steps, warmup, flush=False):
         torch, api = self.torch, self.api
@@ -224,7 +238,7 @@ def main():
     dec_ms = float(np.mean(r2["decode_ms"]))
     value = kv2 / (step_ms * 1e-3) / 1e9
     achieved = kv2 / (dec_ms * 1e-3) / 1e9
-    sha_dec = _source_sha("pa_decode.hip", "pa_common.hpp")
+    sha_dec = _source_sha("pa_decode.hip", "pa_common.hpp", "pa_merge.hpp", "pa_internal.h")
     traffic = _counters("decode_c2", sha_dec)
     log(f"[bench] decode C2: step {step_ms * 1e3:.1f} us (decode {dec_ms * 1e3:.1f} us), "
         f"{value:.0f} GB/s, {r2['schedule']} S={r2['S']} P={r2['P']}")
@@ -242,13 +256,13 @@ def main():
                      "traffic": traffic, "algorithmic_bytes_per_launch": kv2,
                      "mean_launch_us": round(dec_ms * 1e3, 2), "source_sha": sha_dec},
         "step_stats": _stats(r2["step_ms"]),
-        "reduce_mean_us": round(float(np.mean(r2["reduce_ms"])) * 1e3, 2),
+        "merge": "fused into pa_decode" if r2["fused"] else "pa_split_reduce kernel",
         "wall_s_timed_region": round(r2["wall_s"], 4),
     }
     del r2
 
     sections = {}
-    sha_pre = _source_sha("pa_prefill.hip", "pa_common.hpp")
+    sha_pre = _source_sha("pa_prefill.hip", "pa_common.hpp", "pa_internal.h")
     if "C3" in only:
         x3 = W.make_c3()
         d3 = run.to_device(x3)

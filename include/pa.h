@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 2
+#define PA_ABI_VERSION 3
 
 typedef enum {
   PA_OK = 0,
@@ -123,7 +123,10 @@ typedef enum pa_schedule {
    * (r = b * U + u) walked in part by wave w leaves its partial state in
    * piece slot r + w; one walked by a single wave is written to `out`
    * directly.  num_splits is the number of piece slots: at least B * U + 1
-   * (the library uses at most num_splits - B * U waves), and batch <= 2048. */
+   * (the library uses at most num_splits - B * U waves), and batch <= 2048.
+   * With `counters` (B * U of them) the merge is fused into pa_decode: the
+   * last wave to finish a row block's piece merges its pieces, and
+   * pa_split_reduce has nothing left to do. */
   PA_SCHEDULE_BALANCED = 1
 } pa_schedule;
 
@@ -144,7 +147,12 @@ typedef struct pa_workspace {
   int32_t num_splits;        /* partitions (>= 1), or piece slots (balanced) */
   int32_t partition_tokens;  /* partitions: > 0, a multiple of page_size; balanced: ignored */
   int32_t schedule;          /* pa_schedule */
-  int32_t reserved;          /* 0 */
+  int32_t num_counters;      /* balanced: B * U (set by pa_decode_plan); partitions: 0 */
+  /* Balanced only, optional: uint32 [num_counters] counters in device
+   * memory (one arrival counter per row block).  The
+   * caller zeroes them once before first use; every call leaves them zero.
+   * NULL: no run-time chunks, and pa_split_reduce merges. */
+  uint32_t *counters;
 } pa_workspace;
 
 /* Choose the plan of pa_decode for `args` (only the sizes in `args` are
@@ -154,9 +162,10 @@ typedef struct pa_workspace {
  * library choose: the balanced schedule when batch <= 2048, sized for
  * `num_cus` compute units (0: 256, the MI355X count), else partitions
  * chosen from the maximum context max_pages * page_size.
- * On return plan->schedule, num_splits and partition_tokens are set, the
- * buffer pointers are left untouched, and *workspace_bytes (if not NULL) is
- * the total size of partial_out plus partial_lse (0 when no split). */
+ * On return plan->schedule, num_splits, partition_tokens and num_counters
+ * are set, the buffer pointers are left untouched, and *workspace_bytes (if
+ * not NULL) is the total size of partial_out plus partial_lse (0 when no
+ * split); the counters take num_counters * 4 bytes more. */
 pa_status pa_decode_plan(const pa_args *args, int32_t num_cus, pa_workspace *plan,
                          size_t *workspace_bytes);
 

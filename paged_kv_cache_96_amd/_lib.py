@@ -58,11 +58,12 @@ class PaWorkspace(ctypes.Structure):
         ("num_splits", ctypes.c_int32),
         ("partition_tokens", ctypes.c_int32),
         ("schedule", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("num_counters", ctypes.c_int32),
+        ("counters", ctypes.c_void_p),
     ]
 
 
-ABI_VERSION = 2  # PA_ABI_VERSION of the structs below
+ABI_VERSION = 3  # PA_ABI_VERSION of the structs below
 
 SCHEDULE_PARTITIONS = 0
 SCHEDULE_BALANCED = 1

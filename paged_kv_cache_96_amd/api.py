@@ -78,12 +78,14 @@ def _stream(stream) -> int:
 
 class DecodePlan(NamedTuple):
     """What pa_decode_plan chose: the schedule (SCHEDULE_PARTITIONS or
-    SCHEDULE_BALANCED), partial states per row block, the partition size
-    (partition schedule only) and the workspace size in bytes."""
+    SCHEDULE_BALANCED), partitions or piece slots, the partition size
+    (partition schedule only), the size of the partial states in bytes and
+    the number of arrival counters of a fused merge (balanced only)."""
     num_splits: int
     partition_tokens: int
     workspace_bytes: int
     schedule: int
+    num_counters: int
 
 
 def pa_decode_plan(args: PaArgs, *, num_cus: int = 0, partition_tokens: int = 0) -> DecodePlan:
@@ -94,7 +96,8 @@ def pa_decode_plan(args: PaArgs, *, num_cus: int = 0, partition_tokens: int = 0)
     nbytes = ctypes.c_size_t(0)
     _lib.check("pa_decode_plan", _lib.lib().pa_decode_plan(ctypes.byref(args), int(num_cus),
                                                             ctypes.byref(ws), ctypes.byref(nbytes)))
-    return DecodePlan(ws.num_splits, ws.partition_tokens, nbytes.value, ws.schedule)
+    return DecodePlan(ws.num_splits, ws.partition_tokens, nbytes.value, ws.schedule,
+                      ws.num_counters)
 
 
 class Workspace:
@@ -103,10 +106,14 @@ class Workspace:
     `block_rows` states per piece slot, [num_splits, block_rows(, D)]."""
 
     def __init__(self, B: int, Hq: int, L: int, D: int, num_splits: int, partition_tokens: int,
-                 device, schedule: int = SCHEDULE_PARTITIONS, block_rows: int = 0):
+                 device, schedule: int = SCHEDULE_PARTITIONS, block_rows: int = 0,
+                 num_counters: int = 0):
         self.num_splits = int(num_splits)
         self.schedule = int(schedule)
         self.partition_tokens = int(partition_tokens)
+        # arrival counters of the fused merge: zeroed once, left zero by every call
+        self.counters = (torch.zeros(int(num_counters), dtype=torch.int32, device=device)
+                         if num_counters > 0 else None)
         if self.num_splits > 1:
             if self.schedule == SCHEDULE_BALANCED:
                 if block_rows < 1:
@@ -124,15 +131,20 @@ class Workspace:
         self.c.num_splits = self.num_splits
         self.c.partition_tokens = self.partition_tokens
         self.c.schedule = self.schedule
+        self.c.num_counters = int(num_counters)
+        self.c.counters = _ptr(self.counters)
 
     @classmethod
-    def for_plan(cls, plan: DecodePlan, query: torch.Tensor) -> "Workspace":
+    def for_plan(cls, plan: DecodePlan, query: torch.Tensor, fused: bool = True) -> "Workspace":
+        """Buffers for `plan`; `fused` (balanced schedule) adds the arrival
+        counters, so that pa_decode merges the pieces itself."""
         B, Hq, L, D = query.shape
         rows = 0
         if plan.schedule == SCHEDULE_BALANCED and plan.num_splits > 1:
             rows = plan.workspace_bytes // (plan.num_splits * (D + 1) * 4)
         return cls(B, Hq, L, D, plan.num_splits, plan.partition_tokens, query.device,
-                   schedule=plan.schedule, block_rows=rows)
+                   schedule=plan.schedule, block_rows=rows,
+                   num_counters=plan.num_counters if fused else 0)
 
 
 def pa_decode(args: PaArgs, workspace: Optional[Workspace] = None, stream=None) -> None:

@@ -47,9 +47,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // 16-byte load with the non-temporal hint: data read exactly once (paged
 // decode K/V) bypasses normal cache allocation, which on MI355X lifts the
 // sustained HBM read rate well above that of ordinary loads.
-__device__ __forceinline__ uint4 load_stream(const void *p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
-  return make_uint4(v[0], v[1], v[2], v[3]);
+__device__ __forceinline__ u32x4_t load_stream(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
 }
 
 // Word 3 of a raw (stride 0) buffer resource on gfx9-family GPUs: 32-bit
@@ -58,9 +57,8 @@ constexpr int kBufferRsrcWord3 = 0x00020000;
 
 // 16-byte non-temporal raw buffer load at byte offset `off`; offsets at or
 // past the resource's num_records return zeros without a memory access.
-__device__ __forceinline__ uint4 load_stream_buf(__amdgpu_buffer_rsrc_t r, int off) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, /*nt*/ 2);
-  return make_uint4(v[0], v[1], v[2], v[3]);
+__device__ __forceinline__ u32x4_t load_stream_buf(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, /*nt*/ 2);
 }
 
 // ------------------------------------------------------------ exponentials

@@ -39,13 +39,20 @@
 
 #include "pa_common.hpp"
 #include "pa_internal.h"
+#include "pa_merge.hpp"
 
 namespace pa {
 namespace {
 
-using Vec = uint4;  // one 16-byte lane load
+using Vec = u32x4_t;  // one 16-byte lane load (the type buffer loads return)
+
 
 constexpr float kMinM = -1.0e30f;  // running-max sentinel: exp2(x - kMinM) never overflows
+// Register buffers of the page-uniform walk (kDecodeBuffers - 1 steps in
+// flight while one is folded).
+constexpr int kDecodeBuffers = 3;
+
+
 constexpr float kLazy = 8.0f;      // refresh the max only when it grows by more than this (log2)
 
 template <typename T>
@@ -90,20 +97,33 @@ __device__ __forceinline__ uint32_t word(const Vec &v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+// Where a work item's state goes.  Partition schedule: slot `slot` of each
+// row.  Balanced schedule: piece slot `piece` of the row block, whose
+// `pieces` pieces occupy slots first, first + 1, ...; with arrival counters
+// the last piece to finish merges them (counter `unit`).
+struct ItemOut {
+  int slot;
+  long long piece;  // < 0: partition schedule
+  long long first;
+  int pieces;
+  long long unit;
+};
+
 // One work item, walked by the calling wave alone: keys [t0, tend) of the
 // ROWS-row block rb of kv head g of request b (t0 a multiple of STEP).
-// With `split` it writes the state of that piece to the workspace (slot
-// `slot` of each row under partitions, piece slot `piece` when piece >= 0),
-// otherwise the piece is the whole row range and it writes the output.
+// With `split` it writes the state of that piece to the workspace (see
+// ItemOut), otherwise the piece is the whole row range and it writes the
+// output.
 template <typename T, int D, int ROWS, bool DEBUG, bool UNIFORM>
 __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g, int rb, int t0,
-                                            int tend, int slot, long long piece, bool split,
-                                            int ctx, int Lb) {
+                                            int tend, const ItemOut &io, bool split, int ctx,
+                                            int Lb) {
   constexpr int kElems = Elem<T>::kPerVec;
   constexpr int kLpt = D / kElems;      // lanes per key
   constexpr int kTpl = 64 / kLpt;       // keys per wave load
   constexpr int kLoads = 4;             // loads in flight per step (each of K and V)
   constexpr int kStep = kTpl * kLoads;  // keys per wave step
+  constexpr int kBuf = kDecodeBuffers;  // rotating register buffers of the walk
   constexpr bool kBf16 = sizeof(T) == 2;
   static_assert(kLpt * kElems == D && kTpl * kLpt == 64, "layout");
   const int lane = threadIdx.x & 63;
@@ -141,8 +161,8 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
     // rows past query_lens are in bounds (i < L): load unconditionally, then drop
     const bool exists = rb * ROWS + r < G * p.L;
     const Vec v = exists ? *reinterpret_cast<const Vec *>(qbase + qrow[r] * D + c * kElems)
-                         : make_uint4(0, 0, 0, 0);
-    qv[r] = valid[r] ? v : make_uint4(0, 0, 0, 0);
+                         : Vec{0u, 0u, 0u, 0u};
+    qv[r] = valid[r] ? v : Vec{0u, 0u, 0u, 0u};
   }
 
   float m[ROWS], l[ROWS], acc[ROWS][kElems];
@@ -348,10 +368,10 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
     }
   };
 
-  // ---- main walk over the partition's steps; three register buffers
-  // rotate so that the loads of the next two steps are in flight while a
-  // step is folded (the loop body is unrolled three times for the rotation).
-  Vec ka[kLoads], va[kLoads], kb[kLoads], vb[kLoads], kc[kLoads], vc[kLoads];
+  // ---- main walk over the partition's steps; kBuf register buffers
+  // rotate so that the loads of the next kBuf - 1 steps are in flight while
+  // a step is folded (the loop body is unrolled kBuf times for the rotation).
+  Vec kbuf[kBuf][kLoads], vbuf[kBuf][kLoads];
   if constexpr (UNIFORM) {
     // A walk of at most 64 steps has every page offset resolved up
     // front; longer walks (a single partition over a long context) refresh
@@ -360,19 +380,20 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
     // short loop (it would make the compiler wait for the prefetched loads).
     resolve(0);
     auto walk = [&](auto refresh) {
-      fetch_uniform(refresh, 0, ka, va);
-      fetch_uniform(refresh, 1, kb, vb);
+#pragma unroll
+      for (int i = 0; i < kBuf - 1; ++i) fetch_uniform(refresh, i, kbuf[i], vbuf[i]);
       int k = 0;
-      for (; k + 3 <= nw; k += 3) {  // straight-line body: three whole steps
-        fetch_uniform(refresh, k + 2, kc, vc);
-        fold_step(k, ka, va);
-        fetch_uniform(refresh, k + 3, ka, va);
-        fold_step(k + 1, kb, vb);
-        fetch_uniform(refresh, k + 4, kb, vb);
-        fold_step(k + 2, kc, vc);
+      for (; k + kBuf <= nw; k += kBuf) {  // straight-line body: kBuf whole steps
+#pragma unroll
+        for (int i = 0; i < kBuf; ++i) {
+          fetch_uniform(refresh, k + i + kBuf - 1, kbuf[(i + kBuf - 1) % kBuf],
+                        vbuf[(i + kBuf - 1) % kBuf]);
+          fold_step(k + i, kbuf[i], vbuf[i]);
+        }
       }
-      if (k < nw) fold_step(k, ka, va);  // the last one or two steps
-      if (k + 1 < nw) fold_step(k + 1, kb, vb);
+#pragma unroll
+      for (int i = 0; i < kBuf - 1; ++i)  // the last (at most kBuf - 1) steps
+        if (k + i < nw) fold_step(k + i, kbuf[i], vbuf[i]);
     };
     if (nw <= 64) {
       walk(std::integral_constant<bool, false>());
@@ -383,6 +404,9 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
     auto fetch = [&](int k, Vec (&kv)[kLoads], Vec (&vv)[kLoads]) {
       if (k < nw) load_step(k, kv, vv);
     };
+    Vec (&ka)[kLoads] = kbuf[0], (&va)[kLoads] = vbuf[0];
+    Vec (&kb)[kLoads] = kbuf[1], (&vb)[kLoads] = vbuf[1];
+    Vec (&kc)[kLoads] = kbuf[2], (&vc)[kLoads] = vbuf[2];
     fetch(0, ka, va);
     fetch(1, kb, vb);
     for (int k = 0; k < nw; k += 3) {
@@ -410,15 +434,26 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
     const float inv = has ? 1.f / lt : 0.f;
     if (split) {
       if (!valid[r]) continue;  // the merge writes padding rows itself
-      const size_t wi = piece >= 0 ? (size_t)piece * ROWS + r : qrow[r] * p.num_splits + slot;
+      const size_t wi = io.piece >= 0 ? (size_t)io.piece * ROWS + r
+                                      : qrow[r] * p.num_splits + io.slot;
+      // written through to memory: a merging wave on another XCD reads them
+      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+          p.ws_o + wi * D, (short)0, D * 4, kBufferRsrcWord3);
       if (lane < kLpt) {
-        float *dst = p.ws_o + wi * D + c * kElems;
 #pragma unroll
-        for (int e = 0; e < kElems; e += 4)
-          *reinterpret_cast<float4 *>(dst + e) =
-              make_float4(acc[r][e] * inv, acc[r][e + 1] * inv, acc[r][e + 2] * inv, acc[r][e + 3] * inv);
+        for (int e = 0; e < kElems; e += 4) {
+          const u32x4_t v = {__float_as_uint(acc[r][e] * inv), __float_as_uint(acc[r][e + 1] * inv),
+                             __float_as_uint(acc[r][e + 2] * inv),
+                             __float_as_uint(acc[r][e + 3] * inv)};
+          __builtin_amdgcn_raw_buffer_store_b128(v, ro, (c * kElems + e) * 4, 0, kSysScope);
+        }
       }
-      if (lane == 0) p.ws_lse[wi] = has ? (M + __log2f(lt)) * kLn2 : kNegInf;
+      if (lane == 0) {
+        const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+            p.ws_lse + wi, (short)0, 4, kBufferRsrcWord3);
+        __builtin_amdgcn_raw_buffer_store_b32(
+            __float_as_uint(has ? (M + __log2f(lt)) * kLn2 : kNegInf), rl, 0, 0, kSysScope);
+      }
     } else if (lane < kLpt) {
       T *dst = out + qrow[r] * D + c * kElems;
       if constexpr (sizeof(T) == 4) {
@@ -429,6 +464,24 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
             cvt_pk_bf16(acc[r][0] * inv, acc[r][1] * inv), cvt_pk_bf16(acc[r][2] * inv, acc[r][3] * inv),
             cvt_pk_bf16(acc[r][4] * inv, acc[r][5] * inv), cvt_pk_bf16(acc[r][6] * inv, acc[r][7] * inv));
       }
+    }
+  }
+
+  // ---- fused merge (balanced schedule with arrival counters): the last
+  // piece of the row block to arrive merges all of them into the output.
+  // No wave waits for another: the arrival count decides who merges.
+  if (split && io.piece >= 0 && p.counters != nullptr) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the states are in memory
+    uint32_t *cnt = p.counters + io.unit;
+    uint32_t old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old == (uint32_t)(io.pieces - 1)) {
+      asm volatile("" ::: "memory");
+      const size_t wi = (size_t)io.first * ROWS;
+      merge_block<T, D, ROWS>(p.ws_lse + wi, p.ws_o + wi * D, io.pieces, valid, qrow,
+                              min(ROWS, G * p.L - rb * ROWS), out);
+      if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -448,14 +501,13 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
 // / W)).  A run crosses row boundaries freely, so the work per wave differs
 // by at most one step whatever the context lengths.  A row block r (counted
 // over the call) covered by waves w0..w1 leaves its piece from wave w in
-// piece slot r + w (unique; see balanced_active_waves), and the merge
-// recomputes w0 and w1 from the same formula; a row block that one wave
-// covers is written to the output directly.
+// piece slot r + w (see BalancedSplit), and the merge recomputes w0 and w1
+// from the same formula; a row block that one wave covers is written to the
+// output directly.
 template <typename T, int D, int ROWS, bool DEBUG, bool UNIFORM>
 __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blocks) {
   constexpr int kWaves = 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
   if (!p.balanced) {
     const int units = p.Hkv * row_blocks;
     const int idx = blockIdx.x * kWaves + wave;
@@ -470,8 +522,9 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
     const int t0 = s * p.part_tokens;
     if (s > 0 && t0 >= ctx) return;  // never read by the merge
     const bool split = p.num_splits > 1;
-    decode_item<T, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, t0, split ? t0 + p.part_tokens : ctx,
-                                            s, -1, split, ctx, Lb);
+    const ItemOut io{s, -1, 0, 0, 0};
+    decode_item<T, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, t0, split ? t0 + p.part_tokens : ctx, io,
+                                            split, ctx, Lb);
     return;
   }
 
@@ -524,37 +577,56 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
     return (long long)(((unsigned long long)hi << 32) | lo);
   };
   const long long Tot = uni64(s_R[B]);
-  const long long Wa = balanced_active_waves(p.grid_waves, Tot, (long long)B * U, p.num_splits);
+  const long long units_all = (long long)B * U;
+  const BalancedSplit bs = balanced_split(p.grid_waves, Tot, units_all, p.num_splits);
   const long long w = (long long)blockIdx.x * kWaves + wave;
-  if (w >= Wa) return;
-  // wave of step t: the largest v with floor(v Tot / Wa) <= t
-  auto wave_of = [&](long long t) { return ((t + 1) * Wa - 1) / Tot; };
-  long long t = w * Tot / Wa;
-  const long long e = (w + 1) * Tot / Wa;
-  while (t < e) {
-    int lo = 0, hi = B - 1;  // request: the largest b with s_R[b] <= t
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_R[mid] <= t) lo = mid; else hi = mid - 1;
+  const int lane = threadIdx.x & 63;
+  // A request without keys has no steps: wave (b mod grid waves) writes its
+  // (zero) output rows.
+  {
+    const size_t row_elems = (size_t)p.Hq * p.L * D;
+    for (int b = (int)w; b < B; b += (int)gridDim.x * kWaves) {
+      if (uni(s_ctx[b]) != 0) continue;
+      uint4 *dst = reinterpret_cast<uint4 *>(reinterpret_cast<T *>(p.out) + (size_t)b * row_elems);
+      const size_t n16 = row_elems * sizeof(T) / 16;
+      for (size_t i = lane; i < n16; i += 64) dst[i] = make_uint4(0, 0, 0, 0);
     }
-    const int b = uni(lo);
-    const int ctx = uni(s_ctx[b]);
-    const long long n = (ctx + kStep - 1) / kStep;  // > 0: request b holds step t
-    const long long Rb = uni64(s_R[b]);
-    const long long rel = t - Rb;
-    const int u = (int)(rel / n);
-    const long long j0 = rel - (long long)u * n;
-    const long long j1 = min(n, j0 + (e - t));
-    const long long row0 = Rb + (long long)u * n;
-    const long long w0 = wave_of(row0);
-    const bool split = wave_of(row0 + n - 1) > w0;
-    const int g = u / row_blocks;
-    const int rb = u - g * row_blocks;
-    const int Lb = p.ql ? p.ql[b] : p.L;
-    decode_item<T, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, (int)(j0 * kStep), (int)(j1 * kStep),
-                                            0, (long long)b * U + u + w, split, ctx, Lb);
-    t += j1 - j0;
   }
+
+  // The steps of virtual wave v (its static run, or dynamic chunk v - Wa),
+  // piece by piece: a piece is the part of one row block inside the run.
+  auto run_segment = [&](long long v) {
+    long long t = bs.begin(v);
+    const long long e = bs.begin(v + 1);
+    while (t < e) {
+      int lo = 0, hi = B - 1;  // request: the largest b with s_R[b] <= t
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_R[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      const int b = uni(lo);
+      const int ctx = uni(s_ctx[b]);
+      const long long n = (ctx + kStep - 1) / kStep;  // > 0: request b holds step t
+      const long long Rb = uni64(s_R[b]);
+      const long long rel = t - Rb;
+      const int u = (int)(rel / n);
+      const long long j0 = rel - (long long)u * n;
+      const long long j1 = min(n, j0 + (e - t));
+      const long long row0 = Rb + (long long)u * n;
+      const long long w0 = bs.wave_of(row0);
+      const long long w1 = bs.wave_of(row0 + n - 1);
+      const int g = u / row_blocks;
+      const int rb = u - g * row_blocks;
+      const int Lb = p.ql ? p.ql[b] : p.L;
+      const long long unit = (long long)b * U + u;  // row block over the call
+      const ItemOut io{0, unit + v, unit + w0, (int)(w1 - w0 + 1), unit};
+      decode_item<T, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, (int)(j0 * kStep), (int)(j1 * kStep),
+                                              io, w1 > w0, ctx, Lb);
+      t += j1 - j0;
+    }
+  };
+
+  if (w < bs.Wa) run_segment(w);
 }
 
 // Workgroups of `kernel` that fit on the current device at once, cached in

@@ -16,7 +16,9 @@ namespace {
 
 constexpr int kMinPartitionTokens = 256;  // below this the merge costs more than it buys
 constexpr int kBlocksPerCu = 8;           // decode work items wanted per compute unit
-constexpr int kWavesPerCu = 8;            // resident decode waves per compute unit
+constexpr int kWavesPerCu = 4;            // balanced decode: active waves per compute unit
+                                          // (one per SIMD keeps enough loads in flight and
+                                          // halves the pieces to merge; measured faster)
 constexpr int kMaxGridYZ = 65535;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -99,6 +101,9 @@ pa_status check_workspace(const pa_args *a, const pa_workspace *ws, int32_t *S, 
   if (!ws->partial_out || !ws->partial_lse || !aligned16(ws->partial_out) ||
       !aligned16(ws->partial_lse))
     return PA_ERR_WORKSPACE;
+  if (ws->counters && (!*balanced || (int64_t)ws->num_counters < (int64_t)a->batch * decode_units(a) ||
+                       (reinterpret_cast<uintptr_t>(ws->counters) & 3u)))
+    return PA_ERR_WORKSPACE;
   *S = ws->num_splits;
   return PA_OK;
 }
@@ -118,6 +123,7 @@ pa::LaunchParams make_params(const pa_args *a, int32_t S, int32_t P, bool balanc
   p.ws_lse = (S > 1 && ws) ? ws->partial_lse : nullptr;
   p.dbg_trace = a->debug_trace;
   p.dbg_visits = a->debug_visits;
+  p.counters = (balanced && ws) ? ws->counters : nullptr;
   p.B = a->batch;
   p.Hq = a->num_q_heads;
   p.Hkv = a->num_kv_heads;
@@ -180,6 +186,7 @@ PA_EXPORT pa_status pa_decode_plan(const pa_args *args, int32_t num_cus, pa_work
     S = (int32_t)slots;
     P = 0;
     plan->schedule = PA_SCHEDULE_BALANCED;
+    plan->num_counters = (int32_t)units;  // one arrival counter per row block
   } else {
     if (plan->partition_tokens > 0) {
       P = (plan->partition_tokens + ps - 1) / ps * ps;
@@ -197,10 +204,10 @@ PA_EXPORT pa_status pa_decode_plan(const pa_args *args, int32_t num_cus, pa_work
     }
     S = (cap + P - 1) / P;
     plan->schedule = PA_SCHEDULE_PARTITIONS;
+    plan->num_counters = 0;
   }
   plan->num_splits = S;
   plan->partition_tokens = P;
-  plan->reserved = 0;
   if (workspace_bytes) {
     // partitions: [B, H_q, L, S] states; balanced: [S, rows per block] states
     const size_t rows = plan->schedule == PA_SCHEDULE_BALANCED
@@ -235,7 +242,8 @@ PA_EXPORT pa_status pa_split_reduce(const pa_args *args, const pa_workspace *ws,
   int32_t S, P;
   bool balanced;
   if ((st = check_workspace(args, ws, &S, &P, &balanced)) != PA_OK) return st;
-  if (S == 1) return PA_OK;  // pa_decode already wrote `out`
+  if (S == 1) return PA_OK;                  // pa_decode already wrote `out`
+  if (balanced && ws->counters) return PA_OK;  // pa_decode merged the pieces itself
   const pa::LaunchParams p = make_params(args, S, P, balanced, ws);
   return hip_status(pa::launch_split_reduce(p, (pa::DType)args->dtype, (hipStream_t)stream));
 }

@@ -22,6 +22,7 @@ struct LaunchParams {
   float *ws_lse;            // partitions: [B, Hq, L, S];    balanced: [S, ROWS]    fp32
   int32_t *dbg_trace;       // nullptr unless instrumented
   int32_t *dbg_visits;      // nullptr unless instrumented
+  uint32_t *counters;       // balanced: per row block arrival counters (fused merge), or nullptr
   int32_t B, Hq, Hkv, L, D, num_pages, ps, max_pages;
   int32_t causal;
   int32_t num_splits;       // S >= 1: partitions, or piece slots when balanced
@@ -57,18 +58,30 @@ __host__ __device__ constexpr int decode_step_keys(int D, int elem_bytes) {
 // kernel variant that would run it).
 int decode_balanced_waves(const LaunchParams &p, DType dt);
 
-// Waves that take part in a balanced schedule of T steps over `units` row
-// blocks with S piece slots.  The piece of row block r (counted over the
-// whole call) walked by wave w lives in slot r + w: rows and wave runs are
-// both consecutive intervals of the step order, so a later row block never
-// meets an earlier wave and r + w is unique; slots < units + waves - 1.
-__host__ __device__ inline int64_t balanced_active_waves(int64_t grid_waves, int64_t T,
-                                                         int64_t units, int64_t S) {
+// How a balanced call splits its T steps: wave v < Wa owns the steps
+// [begin(v), begin(v + 1)), equal shares in step order.  The piece of row
+// block r (counted over the call) walked by wave v lives in slot r + v: row
+// blocks and waves' runs are both consecutive intervals of the step order,
+// so a later row block never meets an earlier wave and r + v is unique;
+// slots stay below units + Wa.
+struct BalancedSplit {
+  int64_t T = 0, Wa = 0;
+  __host__ __device__ int64_t begin(int64_t v) const { return Wa > 0 ? v * T / Wa : 0; }
+  // wave of step t < T: the largest v with begin(v) <= t
+  __host__ __device__ int64_t wave_of(int64_t t) const { return ((t + 1) * Wa - 1) / T; }
+};
+
+__host__ __device__ inline BalancedSplit balanced_split(int64_t grid_waves, int64_t T, int64_t units,
+                                                        int64_t S) {
+  BalancedSplit s;
+  s.T = T;
+  if (T <= 0) return s;
   int64_t w = grid_waves;
   const int64_t by_len = (T + kBalancedMinSteps - 1) / kBalancedMinSteps;
   if (by_len < w) w = by_len;
   if (S - units < w) w = S - units;  // S >= units + 1 is checked by the host
-  return w;
+  s.Wa = w;
+  return s;
 }
 
 // Query rows one decode workgroup holds, for a GQA group of `rows_per_head`

@@ -1,0 +1,149 @@
+// Log-sum-exp merge of split-KV partial states for one query row ("Reading
+// vLLM's PagedAttention Kernel", section 3.3: partial results computed in
+// parallel are combined afterwards):
+//   M = max_s lse_s,  w_s = exp(lse_s - M),  out = sum_s w_s o_s / sum_s w_s,
+// zeros when no state saw a key (every lse_s = -inf).  Used by the merge
+// kernel and by the decode kernel's fused merge.  The states are read with
+// system-scope loads, which bypass the (per-XCD, non-coherent) L2: a merging
+// wave may read states that waves on other XCDs wrote moments before.
+#pragma once
+
+#include "pa_common.hpp"
+
+namespace pa {
+
+// Cache-policy bits of buffer instructions on gfx94x/gfx950: sc0 | sc1
+// (system scope: stores write through to memory, loads miss every cache).
+constexpr int kSysScope = 1 | 16;
+
+// Natural-log -> base-2 factor for the exponent weights.
+constexpr float kMergeLog2e = 1.44269504088896340736f;
+
+// Merge n states of one row.  State s lives at element offset s * stride of
+// `lse` and at row (s * stride) of `po` (rows of D floats).  Every lane of
+// the wave takes part; lane l writes output elements e * 64 + l.
+template <typename T, int D>
+__device__ __forceinline__ void merge_row(const float *lse, const float *po, int stride, int n,
+                                          T *out_row) {
+  constexpr int kPer = D / 64;
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(lse), (short)0, 0x7fffffff, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(po), (short)0, 0x7fffffff, kBufferRsrcWord3);
+  // the loads return raw 32-bit words: reinterpret, never convert
+  auto load_f32 = [](__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, kSysScope));
+  };
+  float M = kNegInf;
+  for (int s = lane; s < n; s += 64) M = fmaxf(M, load_f32(rl, s * stride * 4));
+  M = group_max<64>(M);
+  float o[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) o[e] = 0.f;
+  if (M != kNegInf) {
+    float wsum = 0.f;
+    for (int s = 0; s < n; ++s) {
+      const float ls = load_f32(rl, s * stride * 4);
+      const float w = fast_exp2((ls - M) * kMergeLog2e);
+      wsum += w;
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) {
+        const float v = load_f32(ro, (s * stride * D + e * 64 + lane) * 4);
+        o[e] = fmaf(w, v, o[e]);
+      }
+    }
+    const float inv = 1.f / wsum;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) o[e] *= inv;
+  }
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    if constexpr (sizeof(T) == 4) {
+      out_row[e * 64 + lane] = o[e];
+    } else {
+      out_row[e * 64 + lane] = (uint16_t)f32_to_bf16(o[e]);
+    }
+  }
+}
+
+}  // namespace pa
+
+namespace pa {
+
+// Merge the n pieces of a block of R rows in one pass, all rows at once:
+// 64 / R lanes per row, each owning D * R / 64 consecutive elements.  Piece s
+// of row r has its state at lse[s * R + r] and po[(s * R + r) * D ...]; rows
+// with valid[r] false get zeros.  A running (max, sum, acc) keeps every load
+// independent of the previous piece's arithmetic, so the loads of several
+// pieces are in flight together.
+template <typename T, int D, int R>
+__device__ __forceinline__ void merge_block(const float *lse, const float *po, int n,
+                                            const bool (&valid)[R], const size_t (&qrow)[R],
+                                            int rows_in_range, T *out) {
+  constexpr int kLanes = 64 / R;       // lanes per row
+  constexpr int kE = D / kLanes;       // elements per lane
+  static_assert(kLanes * R == 64 && kE * kLanes == D && kE % 4 == 0 || kE < 4, "layout");
+  const int lane = threadIdx.x & 63;
+  const int r = lane / kLanes;
+  const int e0 = (lane % kLanes) * kE;
+  bool ok = false;
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (i == r) ok = valid[i] && i < rows_in_range;
+  const int cnt = ok ? n : 0;
+  const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(lse), (short)0, 0x7fffffff, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(po), (short)0, 0x7fffffff, kBufferRsrcWord3);
+  float m = kNegInf, l = 0.f, acc[kE];
+#pragma unroll
+  for (int e = 0; e < kE; ++e) acc[e] = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < cnt; ++s) {
+    const float ls = __uint_as_float(
+        (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rl, (s * R + r) * 4, 0, kSysScope));
+    float v[kE];
+    const int base = ((s * R + r) * D + e0) * 4;
+    if constexpr (kE >= 4) {
+#pragma unroll
+      for (int e = 0; e < kE; e += 4) {
+        const u32x4_t q = __builtin_amdgcn_raw_buffer_load_b128(ro, base + e * 4, 0, kSysScope);
+        v[e] = __uint_as_float(q[0]);
+        v[e + 1] = __uint_as_float(q[1]);
+        v[e + 2] = __uint_as_float(q[2]);
+        v[e + 3] = __uint_as_float(q[3]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kE; ++e)
+        v[e] = __uint_as_float(
+            (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ro, base + e * 4, 0, kSysScope));
+    }
+    const float mn = fmaxf(m, ls);
+    if (mn == kNegInf) continue;  // nothing seen yet
+    const float a = fast_exp2((m - mn) * kMergeLog2e);   // m = -inf -> 0
+    const float w = fast_exp2((ls - mn) * kMergeLog2e);
+    m = mn;
+    l = fmaf(l, a, w);
+#pragma unroll
+    for (int e = 0; e < kE; ++e) acc[e] = fmaf(acc[e], a, w * v[e]);
+  }
+  if (r >= rows_in_range) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  size_t row = 0;
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (i == r) row = qrow[i];
+  T *dst = out + row * D + e0;
+#pragma unroll
+  for (int e = 0; e < kE; ++e) {
+    if constexpr (sizeof(T) == 4) {
+      dst[e] = acc[e] * inv;
+    } else {
+      dst[e] = (uint16_t)f32_to_bf16(acc[e] * inv);
+    }
+  }
+}
+
+}  // namespace pa

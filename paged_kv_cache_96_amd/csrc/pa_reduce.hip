@@ -10,11 +10,10 @@
 // and requests with no keys, get 0.
 #include "pa_common.hpp"
 #include "pa_internal.h"
+#include "pa_merge.hpp"
 
 namespace pa {
 namespace {
-
-constexpr float kLog2e = 1.44269504088896340736f;
 
 // Sum over the 64 lanes of a wave.
 __device__ __forceinline__ long long wave_sum(long long v) {
@@ -41,16 +40,14 @@ __device__ void balanced_waves(const LaunchParams &p, int b, int u, int units, l
   w0 = 0;
   count = 0;
   if (n == 0) return;
-  const long long Wa = balanced_active_waves(p.grid_waves, tot, (long long)p.B * units, p.num_splits);
+  const BalancedSplit bs = balanced_split(p.grid_waves, tot, (long long)p.B * units, p.num_splits);
   const long long row0 = before + (long long)u * n;
-  w0 = ((row0 + 1) * Wa - 1) / tot;
-  count = (int)(((row0 + n) * Wa - 1) / tot - w0 + 1);
+  w0 = bs.wave_of(row0);
+  count = (int)(bs.wave_of(row0 + n - 1) - w0 + 1);
 }
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void split_reduce_kernel(LaunchParams p, int total_rows) {
-  constexpr int kPer = D / 64;  // output elements per lane
-  const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= total_rows) return;
   const int i = row % p.L;
@@ -87,34 +84,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(LaunchParams p, int t
     stride = 1;
   }
 
-  float M = kNegInf;
-  for (int s = lane; s < n; s += 64) M = fmaxf(M, lse[s * stride]);
-  M = group_max<64>(M);
-
-  float o[kPer];
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) o[e] = 0.f;
-  if (M != kNegInf) {
-    float wsum = 0.f;
-    for (int s = 0; s < n; ++s) {
-      const float w = fast_exp2((lse[s * stride] - M) * kLog2e);
-      wsum += w;
-#pragma unroll
-      for (int e = 0; e < kPer; ++e) o[e] = fmaf(w, po[s * stride * D + e * 64 + lane], o[e]);
-    }
-    const float inv = 1.f / wsum;
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) o[e] *= inv;
-  }
-  T *out = reinterpret_cast<T *>(p.out) + (size_t)row * D;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    if constexpr (sizeof(T) == 4) {
-      out[e * 64 + lane] = o[e];
-    } else {
-      out[e * 64 + lane] = (uint16_t)f32_to_bf16(o[e]);
-    }
-  }
+  merge_row<T, D>(lse, po, (int)stride, n, reinterpret_cast<T *>(p.out) + (size_t)row * D);
 }
 
 template <typename T, int D>

@@ -45,7 +45,7 @@ class DeviceInputs:
 
 
 def run_decode(api, d: DeviceInputs, *, partition_tokens=0, trace=False, keep_ws=False,
-               num_cus=0):
+               num_cus=0, fused=True):
     """pa_decode (+ pa_split_reduce) through the C ABI with the library's
     plan (partition_tokens > 0: the partition schedule with that size; else
     the balanced schedule, sized for `num_cus`).  Returns (out, extras)."""
@@ -61,7 +61,7 @@ def run_decode(api, d: DeviceInputs, *, partition_tokens=0, trace=False, keep_ws
                          query_lens=d.ql, debug_trace=dbg_t, debug_visits=dbg_v)
     plan = api.pa_decode_plan(args, partition_tokens=partition_tokens, num_cus=num_cus)
     S, P, nbytes = plan.num_splits, plan.partition_tokens, plan.workspace_bytes
-    ws = api.Workspace.for_plan(plan, d.q)
+    ws = api.Workspace.for_plan(plan, d.q, fused=fused)
     api.pa_decode(args, ws)
     if keep_ws and S > 1:
         torch.cuda.synchronize()

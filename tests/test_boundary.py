@@ -41,7 +41,7 @@ def test_header_and_library_exports_agree(L):
     assert exported == declared
     for name in declared:
         assert hasattr(L, name)
-    assert L.pa_abi_version() == 2
+    assert L.pa_abi_version() == 3
 
 
 def test_status_strings(L):
@@ -125,6 +125,13 @@ def test_workspace_validation(L):
     assert L.pa_split_reduce(ctypes.byref(big), ctypes.byref(ws), None) == -3
     ws.partial_out = None                                         # missing buffer
     assert _decode(L, a, ws) == -3
+    ws.partial_out, ws.num_counters, ws.counters = h.p, 3, h.p     # 2 x 2 row blocks need 4
+    assert _decode(L, a, ws) == -3
+    ws.num_counters, ws.counters = 4, h.p + 2                     # misaligned counters
+    assert _decode(L, a, ws) == -3
+    ws.schedule, ws.num_splits, ws.partition_tokens = SCHEDULE_PARTITIONS, 4, 16
+    ws.counters = h.p                                             # counters are balanced-only
+    assert _decode(L, a, ws) == -3
 
 
 def test_batch_zero_is_a_no_op(L):
@@ -147,35 +154,36 @@ def _plan(L, a, num_cus=0, P=0, full=False):
     nb = ctypes.c_size_t(0)
     rc = L.pa_decode_plan(ctypes.byref(a), num_cus, ctypes.byref(ws), ctypes.byref(nb))
     if full:
-        return rc, ws.num_splits, ws.partition_tokens, nb.value, ws.schedule
+        return rc, ws.num_splits, ws.partition_tokens, nb.value, ws.schedule, ws.num_counters
     return rc, ws.num_splits, ws.partition_tokens, nb.value
 
 
 def test_plan_covers_capacity_and_sizes_workspace(L):
     h = HostBuffers()
     # GQA decode, 64 requests x 8 kv heads (4 query rows each), contexts up to
-    # 4096 keys: balanced, a slot per row block (512) plus 8 waves x 256 CUs
+    # 4096 keys: balanced, a slot per row block (512) plus 4 waves x 256 CUs
     a = h.args(batch=64, num_q_heads=32, num_kv_heads=8, max_pages=256, num_pages=20000)
-    rc, S, P, nb, sched = _plan(L, a, full=True)
-    assert (rc, S, P, sched) == (0, 512 + 2048, 0, SCHEDULE_BALANCED)
+    rc, S, P, nb, sched, nc = _plan(L, a, full=True)
+    assert (rc, S, P, sched, nc) == (0, 512 + 1024, 0, SCHEDULE_BALANCED, 512)
     assert nb == S * 4 * (128 + 1) * 4
-    assert _plan(L, a, num_cus=1)[1] == 512 + 8
+    assert _plan(L, a, num_cus=1)[1] == 512 + 4
     # long contexts: 8 requests x 8 kv heads
     a = h.args(batch=8, num_q_heads=32, num_kv_heads=8, max_pages=8192, num_pages=50000)
-    rc, S, P, nb, sched = _plan(L, a, full=True)
-    assert (rc, S, sched) == (0, 64 + 2048, SCHEDULE_BALANCED)
+    rc, S, P, nb, sched, nc = _plan(L, a, full=True)
+    assert (rc, S, sched, nc) == (0, 64 + 1024, SCHEDULE_BALANCED, 64)
     # 8 query rows per block (G * L = 16): 2 row blocks per kv head
-    rc, S, P, nb, sched = _plan(L, h.args(batch=3, num_q_heads=8, num_kv_heads=2, q_len=4),
-                                full=True)
-    assert (rc, S, nb) == (0, 3 * 2 * 2 + 2048, S * 8 * (128 + 1) * 4)
+    rc, S, P, nb, sched, nc = _plan(L, h.args(batch=3, num_q_heads=8, num_kv_heads=2, q_len=4),
+                                    full=True)
+    assert (rc, S, nb) == (0, 3 * 2 * 2 + 1024, S * 8 * (128 + 1) * 4)
     # an explicit partition size selects partitions, rounded up to whole pages
-    rc, S, P, nb, sched = _plan(L, a, P=1000, full=True)
-    assert (rc, P, S, sched) == (0, 1008, -(-131072 // 1008), SCHEDULE_PARTITIONS)
+    rc, S, P, nb, sched, nc = _plan(L, a, P=1000, full=True)
+    assert (rc, P, S, sched, nc) == (0, 1008, -(-131072 // 1008), SCHEDULE_PARTITIONS, 0)
     # a single partition needs no workspace
     rc, S, P, nb = _plan(L, h.args(max_pages=4), P=64)
     assert (rc, S, nb) == (0, 1, 0)
     # past the balanced batch limit the library picks partitions
-    rc, S, P, nb, sched = _plan(L, h.args(batch=4096, max_pages=256, num_pages=4096), full=True)
+    rc, S, P, nb, sched, nc = _plan(L, h.args(batch=4096, max_pages=256, num_pages=4096),
+                                    full=True)
     assert rc == 0 and sched == SCHEDULE_PARTITIONS and S * P >= 256 * 16
     # decode plans only exist for L <= 8
     assert _plan(L, h.args(q_len=9))[0] == -1

@@ -184,8 +184,9 @@ def test_c4_long_context_parity_sampled(api):
     print(f"[C4] max abs err (requests 0-1) {err:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "merge_kernel"])
 @pytest.mark.parametrize("num_cus", [1, 3, 16, 0])
-def test_balanced_schedule_parity_and_repeat(api, num_cus):
+def test_balanced_schedule_parity_and_repeat(api, num_cus, fused):
     """The balanced schedule (equal runs of steps per wave, rows spread over
     up to num_splits pieces) matches the oracle whatever the plan's piece
     bound, visits every key exactly once, and a second call on the same
@@ -194,8 +195,8 @@ def test_balanced_schedule_parity_and_repeat(api, num_cus):
     x = make_random(71, B=9, H_q=16, H_kv=4, L=1, D=128, page_size=16,
                     ctx=[0, 1, 16, 63, 64, 65, 700, 1500, 4000], dtype="bf16", causal=False)
     d = DeviceInputs(x)
-    a, ex = run_decode(api, d, num_cus=num_cus, trace=True)
-    print(f"[balanced] num_cus={num_cus} S={ex['S']}", flush=True)
+    a, ex = run_decode(api, d, num_cus=num_cus, trace=True, fused=fused)
+    print(f"[balanced] num_cus={num_cus} S={ex['S']} fused={fused}", flush=True)
     assert ex["schedule"] == api.SCHEDULE_BALANCED and ex["S"] >= 2
     assert_parity(a, oracle.attention_of(x), "bf16", f"balanced cus={num_cus}")
     assert np.array_equal(ex["visits"], _expect_visits(x))
@@ -207,6 +208,8 @@ def test_balanced_schedule_parity_and_repeat(api, num_cus):
     api.pa_split_reduce(args, ex["ws"])
     torch.cuda.synchronize()
     assert np.array_equal(host_f64(out2), host_f64(a))
+    if fused:  # every call leaves the arrival counters at zero
+        assert int(ex["ws"].counters.abs().sum()) == 0
 
 
 def test_balanced_and_partition_schedules_agree(api):
@@ -218,3 +221,19 @@ def test_balanced_and_partition_schedules_agree(api):
     for kw in (dict(num_cus=2), dict(partition_tokens=128), dict()):
         out, ex = run_decode(api, d, **kw)
         assert_parity(out, ref, "bf16", f"{kw} S={ex['S']}")
+
+
+def test_fused_and_kernel_merge_agree_on_c2(api):
+    """The fused merge (the last piece of a row block merges, one running
+    pass) and the merge kernel (two passes) combine the same piece states:
+    both match the oracle and differ from each other by bf16 rounding only."""
+    x = make_c2()
+    d = DeviceInputs(x)
+    ref = oracle.attention_of(x)
+    a, exa = run_decode(api, d, fused=True)
+    b, exb = run_decode(api, d, fused=False)
+    assert exa["S"] == exb["S"]
+    assert_parity(a, ref, "bf16", "C2 fused merge")
+    assert_parity(b, ref, "bf16", "C2 merge kernel")
+    assert np.abs(host_f64(a) - host_f64(b)).max() <= 2 ** -7
+    assert int(exa["ws"].counters.abs().sum()) == 0
