@@ -126,23 +126,26 @@ class Runner:
         return {"S": S, "P": P, "schedule": sched, "fused": bool(ws.counters is not None),
                 "decode_ms": dec, "step_ms": step_ms, "wall_s": wall, "out": out}
 
-    def time_prefill(self, d, steps, warmup, flush=False):
+    def time_prefill(self, d, steps, warmup, flush=False, split=True):
+        """Times pa_prefill; `split` passes the key-split workspace of the
+        library's plan (allocated outside the timed region)."""
         torch, api = self.torch, self.api
         x = d.x
         out = torch.empty_like(d.q)
         args = api.make_args(d.q, d.kp, d.vp, d.bt, d.cl, out, scale=x.scale, mask=d.mask,
                              query_lens=d.ql)
+        ws = api.PrefillWorkspace.for_args(args, d.q.device) if split else None
         for _ in range(warmup):
             if flush:
                 self.flush()
-            api.pa_prefill(args)
+            api.pa_prefill(args, ws)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         torch.cuda.synchronize()
         for k in range(steps):
             if flush:
                 self.flush()
             ev[k][0].record()
-            api.pa_prefill(args)
+            api.pa_prefill(args, ws)
             ev[k][1].record()
         torch.cuda.synchronize()
         return {"ms": np.array([e[0].elapsed_time(e[1]) for e in ev]), "out": out}
@@ -262,7 +265,7 @@ def main():
     del r2
 
     sections = {}
-    sha_pre = _source_sha("pa_prefill.hip", "pa_common.hpp", "pa_internal.h")
+    sha_pre = _source_sha("pa_prefill.hip", "pa_common.hpp", "pa_merge.hpp", "pa_internal.h")
     if "C3" in only:
         x3 = W.make_c3()
         d3 = run.to_device(x3)

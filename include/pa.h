@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 3
+#define PA_ABI_VERSION 4
 
 typedef enum {
   PA_OK = 0,
@@ -127,7 +127,8 @@ typedef enum pa_schedule {
    * With `counters` (B * U of them) the merge is fused into pa_decode: the
    * last wave to finish a row block's piece merges its pieces, and
    * pa_split_reduce has nothing left to do. */
-  PA_SCHEDULE_BALANCED = 1
+  PA_SCHEDULE_BALANCED = 1,
+  PA_SCHEDULE_KEY_SPLIT = 2  /* bf16 prefill: key ranges split and merged */
 } pa_schedule;
 
 /* Split-KV workspace of the decode path: normalised partial outputs and the
@@ -183,10 +184,32 @@ pa_status pa_decode(const pa_args *args, const pa_workspace *ws, void *stream);
  * `args` and `ws` must be those of that pa_decode. */
 pa_status pa_split_reduce(const pa_args *args, const pa_workspace *ws, void *stream);
 
+/* Plan of pa_prefill for `args` (sizes only; nothing runs on the GPU).
+ * The bf16 prefill can split the key range of a row tile into pieces walked
+ * by separate workgroups and merged with the log-sum-exp rule ("Reading
+ * vLLM's PagedAttention Kernel", section 3.3: partial results combined
+ * afterwards), so that one long context in a batch does not bound the call.
+ * On return plan->schedule = PA_SCHEDULE_KEY_SPLIT and plan->num_splits =
+ * num_counters = the slots of the split (4 per compute unit, `num_cus` 0:
+ * 256), or 0 when the call cannot split (fp32, or batch * ceil(G * L / 128)
+ * above 2048): no workspace then.  *workspace_bytes (if not NULL) is the size
+ * of partial_out plus partial_lse; the counters take num_counters * 4 bytes
+ * more. */
+pa_status pa_prefill_plan(const pa_args *args, int32_t num_cus, pa_workspace *plan,
+                          size_t *workspace_bytes);
+
 /* Prefill: any L >= 1 (chunked prefill after a cached prefix).  bf16 runs on
  * the MFMA kernel (K/V tiles staged page by page through LDS, QK^T and PV on
- * bf16 matrix cores, fp32 statistics); fp32 runs on a vector-ALU kernel. */
-pa_status pa_prefill(const pa_args *args, void *stream);
+ * bf16 matrix cores, fp32 statistics); fp32 runs on a vector-ALU kernel.
+ * `ws` is NULL (no split) or a workspace of pa_prefill_plan: partial_out
+ * fp32 [num_splits, D / 8, 256, 4] and partial_lse fp32 [num_splits, 2, 256]
+ * (the state of a piece: the accumulators, reference maxima and row sums of
+ * the workgroup's 256 threads), counters uint32 [num_counters], zeroed by the
+ * caller once and left zero by every call.  Calls sharing a workspace must
+ * not overlap in time.  PA_ERR_WORKSPACE: a workspace that is inconsistent
+ * (wrong schedule, fewer than 2 slots or counters than slots, missing
+ * buffers or counters, misaligned). */
+pa_status pa_prefill(const pa_args *args, const pa_workspace *ws, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *pa_status_string(int32_t status);

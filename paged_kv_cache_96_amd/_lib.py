@@ -22,7 +22,7 @@ PA_DTYPE_BF16 = 1
 PA_MASK_NONE = 0
 PA_MASK_CAUSAL = 1
 
-EXPORTED = ("pa_decode_plan", "pa_decode", "pa_split_reduce", "pa_prefill",
+EXPORTED = ("pa_decode_plan", "pa_decode", "pa_split_reduce", "pa_prefill_plan", "pa_prefill",
             "pa_status_string", "pa_abi_version")
 
 
@@ -63,10 +63,11 @@ class PaWorkspace(ctypes.Structure):
     ]
 
 
-ABI_VERSION = 3  # PA_ABI_VERSION of the structs below
+ABI_VERSION = 4  # PA_ABI_VERSION of the structs below
 
 SCHEDULE_PARTITIONS = 0
 SCHEDULE_BALANCED = 1
+SCHEDULE_KEY_SPLIT = 2
 
 
 class PaError(RuntimeError):
@@ -94,7 +95,9 @@ def lib() -> ctypes.CDLL:
     L.pa_decode.restype = ctypes.c_int
     L.pa_split_reduce.argtypes = [A, W, ctypes.c_void_p]
     L.pa_split_reduce.restype = ctypes.c_int
-    L.pa_prefill.argtypes = [A, ctypes.c_void_p]
+    L.pa_prefill_plan.argtypes = [A, ctypes.c_int32, W, ctypes.POINTER(ctypes.c_size_t)]
+    L.pa_prefill_plan.restype = ctypes.c_int
+    L.pa_prefill.argtypes = [A, W, ctypes.c_void_p]
     L.pa_prefill.restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int32]
     L.pa_status_string.restype = ctypes.c_char_p

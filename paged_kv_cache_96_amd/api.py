@@ -14,7 +14,8 @@ from typing import NamedTuple, Optional
 import torch
 
 from . import _lib
-from ._lib import PaArgs, PaWorkspace, SCHEDULE_BALANCED, SCHEDULE_PARTITIONS  # noqa: F401
+from ._lib import (PaArgs, PaWorkspace, SCHEDULE_BALANCED, SCHEDULE_KEY_SPLIT,  # noqa: F401
+                   SCHEDULE_PARTITIONS)
 
 _DTYPES = {torch.float32: _lib.PA_DTYPE_F32, torch.bfloat16: _lib.PA_DTYPE_BF16}
 _MASKS = {"none": _lib.PA_MASK_NONE, None: _lib.PA_MASK_NONE, "causal": _lib.PA_MASK_CAUSAL}
@@ -158,8 +159,57 @@ def pa_split_reduce(args: PaArgs, workspace: Workspace, stream=None) -> None:
                                                               _stream(stream)))
 
 
-def pa_prefill(args: PaArgs, stream=None) -> None:
-    _lib.check("pa_prefill", _lib.lib().pa_prefill(ctypes.byref(args), _stream(stream)))
+class PrefillPlan(NamedTuple):
+    """What pa_prefill_plan chose: the slots of the key split (0: the call
+    runs unsplit and needs no workspace), the size of the piece states in
+    bytes and the number of arrival counters."""
+    num_splits: int
+    workspace_bytes: int
+    num_counters: int
+
+
+def pa_prefill_plan(args: PaArgs, *, num_cus: int = 0) -> PrefillPlan:
+    ws = PaWorkspace()
+    nbytes = ctypes.c_size_t(0)
+    _lib.check("pa_prefill_plan", _lib.lib().pa_prefill_plan(ctypes.byref(args), int(num_cus),
+                                                              ctypes.byref(ws), ctypes.byref(nbytes)))
+    return PrefillPlan(ws.num_splits, nbytes.value, ws.num_counters)
+
+
+class PrefillWorkspace:
+    """Device buffers of a prefill plan (torch owns the memory): piece states
+    partial_out [num_splits, D / 8, 256, 4] and partial_lse [num_splits, 2,
+    256] fp32, and the arrival counters (zeroed once, left zero by every
+    call)."""
+
+    def __init__(self, plan: PrefillPlan, D: int, device):
+        self.num_splits = int(plan.num_splits)
+        self.c = PaWorkspace()
+        self.c.schedule = SCHEDULE_KEY_SPLIT
+        self.c.num_splits = self.num_splits
+        self.c.num_counters = int(plan.num_counters)
+        if self.num_splits > 0:
+            self.partial_out = torch.empty((self.num_splits, D // 8, 256, 4),
+                                           dtype=torch.float32, device=device)
+            self.partial_lse = torch.empty((self.num_splits, 2, 256), dtype=torch.float32,
+                                           device=device)
+            self.counters = torch.zeros(int(plan.num_counters), dtype=torch.int32, device=device)
+        else:
+            self.partial_out = self.partial_lse = self.counters = None
+        self.c.partial_out = _ptr(self.partial_out)
+        self.c.partial_lse = _ptr(self.partial_lse)
+        self.c.counters = _ptr(self.counters)
+
+    @classmethod
+    def for_args(cls, args: PaArgs, device, num_cus: int = 0) -> "PrefillWorkspace":
+        return cls(pa_prefill_plan(args, num_cus=num_cus), args.head_dim, device)
+
+
+def pa_prefill(args: PaArgs, workspace: Optional[PrefillWorkspace] = None, stream=None) -> None:
+    """Prefill; with a workspace the bf16 kernel may split long key ranges
+    (see pa_prefill_plan)."""
+    ws = ctypes.byref(workspace.c) if workspace is not None else None
+    _lib.check("pa_prefill", _lib.lib().pa_prefill(ctypes.byref(args), ws, _stream(stream)))
 
 
 def paged_attention(query: torch.Tensor, key_pages: torch.Tensor, value_pages: torch.Tensor,
@@ -180,5 +230,7 @@ def paged_attention(query: torch.Tensor, key_pages: torch.Tensor, value_pages: t
             pa_split_reduce(args, ws, stream)
         out._pa_workspace = ws  # keep the buffers alive until the caller is done
     else:
-        pa_prefill(args, stream)
+        ws = PrefillWorkspace.for_args(args, query.device)
+        pa_prefill(args, ws, stream)
+        out._pa_workspace = ws
     return out

@@ -144,6 +144,9 @@ pa::LaunchParams make_params(const pa_args *a, int32_t S, int32_t P, bool balanc
 
 pa_status hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+// Workspace slots a launch uses (0 without a workspace).
+int64_t ws_slots(const pa::LaunchParams &p) { return p.ws_o ? p.num_splits : 0; }
+
 // Grid limits of the vector kernel under the partition schedule: gridDim.x =
 // ceil(H_kv * row blocks * partitions / 4) (one work item per wave),
 // gridDim.y = batch.
@@ -248,16 +251,67 @@ PA_EXPORT pa_status pa_split_reduce(const pa_args *args, const pa_workspace *ws,
   return hip_status(pa::launch_split_reduce(p, (pa::DType)args->dtype, (hipStream_t)stream));
 }
 
-PA_EXPORT pa_status pa_prefill(const pa_args *args, void *stream) {
+namespace {
+
+// Row tiles (128 packed rows) of one (request, kv head) of the bf16 prefill.
+int64_t prefill_tiles(const pa_args *a) {
+  return ((int64_t)(a->num_q_heads / a->num_kv_heads) * a->q_len + 127) / 128;
+}
+
+// Whether the bf16 prefill of `a` can run the key split.
+bool prefill_splits(const pa_args *a) {
+  return a->dtype == PA_DTYPE_BF16 && (int64_t)a->batch * prefill_tiles(a) <= pa::kSplitMaxPairs;
+}
+
+}  // namespace
+
+PA_EXPORT pa_status pa_prefill_plan(const pa_args *args, int32_t num_cus, pa_workspace *plan,
+                                    size_t *workspace_bytes) {
+  pa_status st = check_sizes(args);
+  if (st != PA_OK) return st;
+  if (!plan) return PA_ERR_INVALID_ARG;
+  plan->schedule = PA_SCHEDULE_KEY_SPLIT;
+  plan->partition_tokens = 0;
+  plan->num_splits = 0;
+  plan->num_counters = 0;
+  if (workspace_bytes) *workspace_bytes = 0;
+  if (!prefill_splits(args)) return PA_OK;  // runs unsplit: no workspace
+  // two workgroups per compute unit are resident; the split aims at half
+  // the slots and uses at most all of them
+  const int cus = num_cus > 0 ? num_cus : 256;
+  plan->num_splits = 4 * cus;
+  plan->num_counters = plan->num_splits;
+  if (workspace_bytes)
+    *workspace_bytes = (size_t)plan->num_splits * (args->head_dim / 2 + 2) * 256 * sizeof(float);
+  return PA_OK;
+}
+
+PA_EXPORT pa_status pa_prefill(const pa_args *args, const pa_workspace *ws, void *stream) {
   pa_status st = check_sizes(args);
   if (st != PA_OK) return st;
   if (args->batch == 0) return PA_OK;
   if ((st = check_pointers(args)) != PA_OK) return st;
   const int32_t cap = args->max_pages * args->page_size;
-  const pa::LaunchParams p = make_params(args, 1, cap, false, nullptr);
+  pa::LaunchParams p = make_params(args, 1, cap, false, nullptr);
+  if (ws && ws->num_splits > 0) {
+    // two slots at least: the pieces of split tiles take fewer than
+    // 2 * floor(num_splits / 2) slots
+    if (ws->schedule != PA_SCHEDULE_KEY_SPLIT || ws->num_splits < 2 || !ws->partial_out ||
+        !ws->partial_lse ||
+        !ws->counters || ws->num_counters < ws->num_splits || !aligned16(ws->partial_out) ||
+        !aligned16(ws->partial_lse) || (reinterpret_cast<uintptr_t>(ws->counters) & 3u))
+      return PA_ERR_WORKSPACE;
+    if (prefill_splits(args)) {  // otherwise the call runs unsplit
+      p.ws_o = ws->partial_out;
+      p.ws_lse = ws->partial_lse;
+      p.counters = ws->counters;
+      p.num_splits = ws->num_splits;
+    }
+  }
   if (args->dtype == PA_DTYPE_BF16) {
-    const int64_t tiles = ((int64_t)(args->num_q_heads / args->num_kv_heads) * args->q_len + 127) / 128;
-    if (tiles > INT32_MAX || args->num_kv_heads > kMaxGridYZ) return PA_ERR_INVALID_ARG;
+    const int64_t tiles = prefill_tiles(args);
+    if (tiles * args->num_kv_heads > INT32_MAX) return PA_ERR_INVALID_ARG;
+    if (tiles * args->num_kv_heads * args->batch + ws_slots(p) > INT32_MAX) return PA_ERR_INVALID_ARG;
     return hip_status(pa::launch_prefill_mfma(p, (hipStream_t)stream));
   }
   if ((st = check_decode_grid(args, 1)) != PA_OK) return st;

@@ -18,8 +18,10 @@ struct LaunchParams {
   const int32_t *cl;
   const int32_t *ql;        // nullptr: every request has L rows
   void *out;
-  float *ws_o;              // partitions: [B, Hq, L, S, D]; balanced: [S, ROWS, D] fp32
-  float *ws_lse;            // partitions: [B, Hq, L, S];    balanced: [S, ROWS]    fp32
+  float *ws_o;              // partitions: [B, Hq, L, S, D]; balanced: [S, ROWS, D] fp32;
+                            // prefill key split: [S, D / 8, 256, 4] (nullptr: no split)
+  float *ws_lse;            // partitions: [B, Hq, L, S];    balanced: [S, ROWS]    fp32;
+                            // prefill key split: [S, 2, 256]
   int32_t *dbg_trace;       // nullptr unless instrumented
   int32_t *dbg_visits;      // nullptr unless instrumented
   uint32_t *counters;       // balanced: per row block arrival counters (fused merge), or nullptr
@@ -47,6 +49,11 @@ constexpr int kBalancedMaxBatch = 2048;
 constexpr int64_t kBalancedMaxSteps = int64_t(1) << 40;
 // Shortest run of steps a balanced schedule hands to one wave.
 constexpr int kBalancedMinSteps = 4;
+
+// Largest number of (request, tile) pairs the key split of the bf16 prefill
+// plans over (the plan's tables live in the kernel's staging buffers);
+// larger calls run unsplit.
+constexpr int kSplitMaxPairs = 2048;
 
 // Keys per decode step (one 16-byte load per lane, four loads per step):
 // 16 for bf16 with D = 128.

@@ -41,8 +41,24 @@
 //      lane four consecutive keys of one head dimension.
 // Keys past a row's causal limit are masked on the diagonal tiles only, and
 // tiles past the last row's limit are never loaded.
+//
+// Key split (with a workspace): a tile whose key range is much longer than
+// the average work of a workgroup slot would bound the whole call (a long
+// prefix in one request of the batch), so its keys are cut into pieces of
+// at most P keys, each walked by its own workgroup, and the pieces are
+// merged with the log-sum-exp rule of split-KV decoding ("Reading vLLM's
+// PagedAttention Kernel", section 3.3).  Every workgroup derives the same
+// plan from the context lengths (P = total work / (0.4 x workspace slots),
+// at least kMinPieceKeys, a multiple of BN) and finds its piece by its
+// index in the dispatch order, longest pieces first (see find_piece).  A split
+// piece writes its state (unnormalised O, reference max and row sums) to
+// its slot and counts its arrival on the tile's counter; the last piece to
+// arrive reads them all back, merges them in piece order (so the result
+// does not depend on the order of arrival) and writes the output.  No
+// workgroup waits for another.
 #include "pa_common.hpp"
 #include "pa_internal.h"
+#include "pa_merge.hpp"
 
 namespace pa {
 namespace {
@@ -58,6 +74,8 @@ constexpr float kRefSlack = 16.0f; // largest row max above the reference (log2)
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= 8 (the eight loads of one
 // staging set may stay in flight), expcnt and lgkmcnt not waited for.
 constexpr int kWaitVmcntOlderThan8 = 8 | (0x7 << 4) | (0xF << 8);
+// Key split: shortest piece.
+constexpr int kMinPieceKeys = 4 * kBN;
 
 template <int D>
 struct Tile {
@@ -85,6 +103,207 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: row shifts
+// within each 16-lane row, then the row totals broadcast to the later rows.
+// Lanes whose source lies outside the row read 0.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ float wave_incl_scan_f(float x) {
+  x = dpp_add<0x111, 0xF>(x);
+  x = dpp_add<0x112, 0xF>(x);
+  x = dpp_add<0x114, 0xF>(x);
+  x = dpp_add<0x118, 0xF>(x);
+  x = dpp_add<0x142, 0xA>(x);
+  x = dpp_add<0x143, 0xC>(x);
+  return x;
+}
+
+// The piece of the key split that workgroup blockIdx.x walks.
+struct Piece {
+  int tile, g, b;
+  int k0, k1;  // keys [k0, k1) of the tile
+  int np;      // pieces of the tile (1: not split)
+  int sp;      // this piece
+  int slot;    // first workspace slot of the tile's pieces (np > 1)
+  int found;
+};
+
+// x / d for 0 <= x < 2^31, 0 < d: float estimate, then exact corrections
+// (one step each way when x < 2^24).
+__device__ __forceinline__ int div_small(int x, int d, float rcp) {
+  long long q = (long long)((float)x * rcp);
+  while (q * d > x) --q;
+  while ((q + 1) * d <= x) ++q;
+  return (int)q;
+}
+
+// Every workgroup computes the same plan (see the header).  Pairs (request,
+// tile) are numbered by request, then tile from the last.  Total work W =
+// H_kv * sum of the pairs' keys (in BN blocks); the work target of a piece
+// is W / (0.4 S) (S workspace slots; measured best between W / (0.5 S) and
+// W / (0.25 S)), and piece lengths are at most P = max(kMinPieceKeys,
+// target) rounded up to BN; a pair with k > P keys splits into as equal
+// pieces as the BN grid allows.  Dispatch order: longest pieces first, in
+// four classes of piece length (>= 3P/4, >= P/2, >= P/4, shorter), each
+// class in pair order; within a pair, kv head then piece.  Split pairs take
+// workspace slots in pair order.  All 256 threads take part: each owns a
+// contiguous slice of pairs, per-thread counts are scanned within waves
+// (DPP) and across the four waves (LDS), and the thread whose slice holds
+// this workgroup's piece publishes it in s_pc.  ta: 3 tables of
+// kSplitMaxPairs ints, tb: 1 table plus 32 ints of scratch; the block
+// synchronises before returning (the tables live in the staging buffers).
+__device__ void find_piece(const LaunchParams &p, int nt, int *ta, int *tb, Piece *s_pc,
+                           Piece &pc) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int G = p.Hq / p.Hkv;
+  int *s_ctx = ta, *s_ql = ta + kSplitMaxPairs, *s_len = ta + 2 * kSplitMaxPairs;
+  int *s_keys = tb;
+  int *s_red = tb + kSplitMaxPairs;  // [5 values][4 waves], then 4 floats
+  for (int b = tid; b < p.B; b += 256) {
+    s_ctx[b] = p.cl[b];
+    s_ql[b] = p.ql ? p.ql[b] : p.L;
+  }
+  if (tid == 0) s_pc->found = 0;
+  __syncthreads();
+  const int NP = p.B * nt;
+  const int per = (NP + 255) / 256;
+  const int q0 = min(NP, tid * per), q1 = min(NP, q0 + per);
+  const float rcpG = 1.0f / (float)G;
+  // keys of this thread's pairs (request and tile stepped along the slice)
+  int w = 0;  // in BN blocks (below 2^29)
+  if (q0 < q1) {
+    int b = q0 / nt;
+    int t = nt - 1 - (q0 - b * nt);
+    int ctx = s_ctx[b], Lb = s_ql[b];
+    for (int q = q0; q < q1; ++q) {
+      const int rho0 = t * 128;
+      const int last = min(rho0 + 128, G * Lb) - 1;
+      const int k = last < rho0 ? 0 : (p.causal ? ctx - Lb + div_small(last, G, rcpG) + 1 : ctx);
+      s_keys[q] = k;
+      w += (k + kBN - 1) / kBN;
+      if (--t < 0 && q + 1 < q1) {
+        t = nt - 1;
+        ++b;
+        ctx = s_ctx[b];
+        Lb = s_ql[b];
+      }
+    }
+  }
+  // total in fp32, summed in one fixed order (every workgroup gets the same
+  // value; P only needs to be the same everywhere and about right)
+  float *s_redf = reinterpret_cast<float *>(s_red + 20);
+  {
+    const float ws = __shfl(wave_incl_scan_f((float)w), 63, 64);
+    if (lane == 0) s_redf[wave] = ws;
+  }
+  __syncthreads();
+  const float work = ((s_redf[0] + s_redf[1]) + (s_redf[2] + s_redf[3])) * (float)p.Hkv;
+  const float target = 0.4f * (float)max(2, p.num_splits);
+  const float blocks = fminf(ceilf(work / target), (float)(1 << 24));  // P / BN
+  const int P = max(kMinPieceKeys, (int)blocks * kBN);
+  auto npieces = [&](int k, int len) { return k > len ? (k + len - 1) / len : 1; };
+  auto cls = [&](int len) {
+    return 4 * (long long)len >= 3LL * P ? 0 : 2 * (long long)len >= P ? 1
+           : 4 * (long long)len >= P ? 2 : 3;
+  };
+  int cnt[5] = {0, 0, 0, 0, 0};  // widths of the four classes, split slots
+  for (int q = q0; q < q1; ++q) {
+    const int k = s_keys[q];
+    int len = k;
+    if (k > P) {
+      const int n0 = (k + P - 1) / P;
+      len = ((k + n0 - 1) / n0 + kBN - 1) / kBN * kBN;
+    }
+    s_len[q] = len;
+    const int n = npieces(k, len);
+    const int c = cls(len);
+    const int wdt = p.Hkv * n;
+    cnt[0] += c == 0 ? wdt : 0;
+    cnt[1] += c == 1 ? wdt : 0;
+    cnt[2] += c == 2 ? wdt : 0;
+    cnt[3] += c == 3 ? wdt : 0;
+    cnt[4] += n > 1 ? wdt : 0;
+  }
+  // exclusive prefix of each count over the block, and the class totals
+  int ex[5];
+#pragma unroll
+  for (int v = 0; v < 5; ++v) {
+    const int inc = wave_incl_scan(cnt[v]);
+    ex[v] = inc - cnt[v];
+    if (lane == 63) s_red[v * 4 + wave] = inc;
+  }
+  __syncthreads();
+  int off[5];
+  off[0] = 0;
+#pragma unroll
+  for (int v = 0; v < 5; ++v) {
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+      const int x = s_red[v * 4 + w2];
+      before += w2 < wave ? x : 0;
+      tot += x;
+    }
+    ex[v] += before;
+    if (v < 4) off[v + 1] = off[v] + tot;
+  }
+  const int i = blockIdx.x;
+  int c = 0;
+  while (c < 4 && i >= off[c + 1]) ++c;
+  if (c < 4) {
+    int cnt_c = 0, ex_c = 0;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+      if (cc == c) {
+        cnt_c = cnt[cc];
+        ex_c = ex[cc];
+      }
+    const int r = i - off[c];
+    if (r >= ex_c && r < ex_c + cnt_c) {  // exactly one thread holds workgroup i
+      int acc = ex_c, sacc = ex[4];
+      for (int q = q0; q < q1; ++q) {
+        const int k = s_keys[q], len = s_len[q];
+        const int n = npieces(k, len);
+        const int wdt = p.Hkv * n;
+        if (cls(len) == c) {
+          if (r < acc + wdt) {
+            const int rr = r - acc;
+            Piece x;
+            x.b = q / nt;
+            x.tile = nt - 1 - (q - x.b * nt);
+            x.g = rr / n;
+            x.sp = rr - x.g * n;
+            x.np = n;
+            x.k0 = x.sp * len;
+            x.k1 = min(k, x.k0 + len);
+            x.slot = sacc + x.g * n;
+            x.found = 1;
+            *s_pc = x;
+            break;
+          }
+          acc += wdt;
+        }
+        sacc += n > 1 ? wdt : 0;
+      }
+    }
+  }
+  __syncthreads();
+  pc = *s_pc;
+  __syncthreads();  // the tables live in the staging buffers
+}
+
 // Staging modes.  kStageLanes: every lane resolves its own key (any page
 // size; debug trace).  kStageRun: page_size a multiple of the run length, one
 // buffer resource per run.  kStagePool: the same runs, with one resource for
@@ -102,10 +321,33 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
   using TL = Tile<D>;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kBN * TL::kKStride];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kBN * TL::kVStride];
+  __shared__ uint32_t s_arrived;
+  __shared__ Piece s_pc;
+  static_assert(sizeof(v_lds) >= 3 * kSplitMaxPairs * 4 &&
+                sizeof(k_lds) >= (kSplitMaxPairs + 32) * 4, "plan tables");
 
-  const int tile = num_tiles - 1 - (int)blockIdx.x;  // heavy (late) tiles first
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  // ---- which keys of which tile: a piece of the key split (workspace
+  // given), else the whole tile (heavy, late tiles first)
+  int tile, g, b, k0 = 0, k1 = 0x7fffffff, np = 1, sp = 0, slot = 0;
+  if (p.ws_o != nullptr) {
+    Piece pc;
+    find_piece(p, num_tiles, reinterpret_cast<int *>(&v_lds[0][0]),
+               reinterpret_cast<int *>(&k_lds[0][0]), &s_pc, pc);
+    if (!pc.found) return;  // block-uniform
+    tile = pc.tile;
+    g = pc.g;
+    b = pc.b;
+    k0 = pc.k0;
+    k1 = pc.k1;
+    np = pc.np;
+    sp = pc.sp;
+    slot = pc.slot;
+  } else {  // x = tile from the last * H_kv + kv head, y = request: longest tiles first
+    const int x = blockIdx.x;
+    tile = num_tiles - 1 - x / p.Hkv;
+    g = x - (num_tiles - 1 - tile) * p.Hkv;
+    b = blockIdx.y;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -131,17 +373,19 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
     lim[rb] = row_valid[rb] ? (p.causal ? ctx - Lb + qi[rb] + 1 : ctx) : 0;
   }
 
-  // ---- key ranges: the workgroup's (for staging) and this wave's (compute)
+  // ---- key ranges within [k0, k1): the workgroup's (for staging) and this
+  // wave's (compute)
   const int rho_last_wg = min(rho0 + kBM, rows_valid) - 1;
-  const int kend_wg = rho_last_wg < rho0 ? 0
-                      : (p.causal ? ctx - Lb + rho_last_wg / G + 1 : ctx);
+  const int kend_wg = min(k1, rho_last_wg < rho0 ? 0
+                              : (p.causal ? ctx - Lb + rho_last_wg / G + 1 : ctx));
   const int rho_first_w = rho0 + wave * kRW;
   const int rho_last_w = min(rho_first_w + kRW, rows_valid) - 1;
-  const int kend_w = rho_last_w < rho_first_w ? 0
-                     : (p.causal ? ctx - Lb + rho_last_w / G + 1 : ctx);
+  const int kend_w = min(k1, rho_last_w < rho_first_w ? 0
+                             : (p.causal ? ctx - Lb + rho_last_w / G + 1 : ctx));
   const int kfull_w = rho_last_w < rho_first_w ? 0
                       : (p.causal ? ctx - Lb + rho_first_w / G + 1 : ctx);  // keys below: unmasked
-  const int ntiles = (kend_wg + kBN - 1) / kBN;
+  const int kt0 = k0 / kBN;  // first tile (k0 is a multiple of BN)
+  const int ntiles = kend_wg > k0 ? (kend_wg - k0 + kBN - 1) / kBN : 0;
   const bool counts = DEBUG && rows_valid > 0 && (rows_valid - 1) / kBM == tile;
 
   // ---- Q as the B operand of S^T = K Q^T: dims kk*16 + half*8 .. +8
@@ -295,12 +539,17 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
       for (int i = 0; i < 16; ++i) o[rb][mb][i] = 0.f;
     l_run[rb] = 0.f;
   }
-  run_j0 = run_lp = run_slot = 0;
+  run_j0 = k0;
+  run_lp = k0 / p.ps;
+  run_slot = k0 - run_lp * p.ps;
+  // a piece may start inside a page: its first entry is read here (later
+  // ones when a run starts a page)
+  if constexpr (UNIFORM) run_page = run_j0 < kend_wg ? btc[min(run_lp, p.max_pages - 1)] : 0;
   if (ntiles > 0) {
-    stage_load(0, sa);
+    stage_load(kt0, sa);
     stage_store(0, sa);
   }
-  if (kTwoSets && (UNIFORM || ntiles > 1)) stage_load(1, sb);
+  if (kTwoSets && (UNIFORM || ntiles > 1)) stage_load(kt0 + 1, sb);
   // the query and tile-0 loads are complete here; tile 1 stays in flight
   __builtin_amdgcn_s_waitcnt(kWaitVmcntOlderThan8);
   __syncthreads();
@@ -308,11 +557,12 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
   // One tile: prefetch tile kt + 2 into `ld` (its set is free: tile kt was
   // stored to LDS one tile ago), compute tile kt, then store tile kt + 1
   // (loaded into `st` one tile ago) to the other LDS buffer.
+  const int kt_end = kt0 + ntiles;
   auto tile_step = [&](int kt, Stage &ld, const Stage &st) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < ntiles;
+    const int buf = (kt - kt0) & 1;
+    const bool more = kt + 1 < kt_end;
     if constexpr (kTwoSets) {
-      if (UNIFORM || kt + 2 < ntiles) stage_load(kt + 2, ld);
+      if (UNIFORM || kt + 2 < kt_end) stage_load(kt + 2, ld);
     } else {
       if (UNIFORM || more) stage_load(kt + 1, ld);
     }
@@ -357,7 +607,7 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
 #pragma unroll
           for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[rb][i]);
           mx = pair_max(mx) * c;
-          if (pass == 0 && kt == 0 && blk == 0) m_ref[rb] = fmaxf(mx, kMinM);
+          if (pass == 0 && kt == kt0 && blk == 0) m_ref[rb] = fmaxf(mx, kMinM);
           m_seen[rb] = fmaxf(m_seen[rb], mx);
           float psum = 0.f;
 #pragma unroll
@@ -407,12 +657,12 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
     __syncthreads();
   };
   if constexpr (kTwoSets) {
-    for (int kt = 0; kt < ntiles; kt += 2) {  // unrolled by two so the sets stay in registers
+    for (int kt = kt0; kt < kt_end; kt += 2) {  // unrolled by two so the sets stay in registers
       tile_step(kt, sa, sb);
-      if (kt + 1 < ntiles) tile_step(kt + 1, sb, sa);
+      if (kt + 1 < kt_end) tile_step(kt + 1, sb, sa);
     }
   } else {
-    for (int kt = 0; kt < ntiles; ++kt) tile_step(kt, sa, sa);
+    for (int kt = kt0; kt < kt_end; ++kt) tile_step(kt, sa, sa);
   }
   // weights past 2^16 anywhere in the workgroup: walk again from the exact maxima
   bool over = false;
@@ -422,6 +672,78 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) m_ref[rb] = m_seen[rb];
  }
+
+  // ---- a piece of a split tile: publish this piece's state; the last piece
+  // to arrive merges all of them and writes the output
+  if (np > 1) {
+    if constexpr (RB == 1) {
+      constexpr int kAcc = TL::kMBlocks * 16;  // accumulators per thread (D / 2)
+      auto slot_o = [&](int s) {
+        return __builtin_amdgcn_make_buffer_rsrc(p.ws_o + (size_t)(slot + s) * kAcc * 256,
+                                                 (short)0, kAcc * 256 * 4, kBufferRsrcWord3);
+      };
+      auto slot_m = [&](int s) {
+        return __builtin_amdgcn_make_buffer_rsrc(p.ws_lse + (size_t)(slot + s) * 2 * 256,
+                                                 (short)0, 2 * 256 * 4, kBufferRsrcWord3);
+      };
+      // [value / 4][thread][4]: every 16-byte store and load of a wave is
+      // one coalesced 1 KiB row; written through to memory for the merging
+      // workgroup, which may run on another XCD
+      auto off4 = [&](int mb, int j) { return ((mb * 4 + j) * 256 + tid) * 16; };
+      {
+        const auto ro = slot_o(sp);
+        const auto rm = slot_m(sp);
+#pragma unroll
+        for (int mb = 0; mb < TL::kMBlocks; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x16_t &om = o[0][mb];
+            const u32x4_t v = {__float_as_uint(om[4 * j]), __float_as_uint(om[4 * j + 1]),
+                               __float_as_uint(om[4 * j + 2]), __float_as_uint(om[4 * j + 3])};
+            __builtin_amdgcn_raw_buffer_store_b128(v, ro, off4(mb, j), 0, kSysScope);
+          }
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_ref[0]), rm, tid * 4, 0, kSysScope);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_run[0]), rm, (256 + tid) * 4, 0,
+                                              kSysScope);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the state is in memory
+      __syncthreads();
+      if (tid == 0)
+        s_arrived = __hip_atomic_fetch_add(p.counters + slot, 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (s_arrived != (uint32_t)(np - 1)) return;  // block-uniform
+      asm volatile("" ::: "memory");
+      auto ld = [](__amdgpu_buffer_rsrc_t r, int off) {
+        return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSysScope));
+      };
+      // every piece, this one included, is read back and summed in piece
+      // order: the result does not depend on which piece arrived last
+      float M = kMinM;
+      for (int s2 = 0; s2 < np; ++s2) M = fmaxf(M, ld(slot_m(s2), tid * 4));
+      l_run[0] = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < TL::kMBlocks; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[0][mb][i] = 0.f;
+      for (int s2 = 0; s2 < np; ++s2) {
+        const auto ro = slot_o(s2);
+        const auto rm = slot_m(s2);
+        const float f = fast_exp2(ld(rm, tid * 4) - M);
+        l_run[0] = fmaf(f, ld(rm, (256 + tid) * 4), l_run[0]);
+#pragma unroll
+        for (int mb = 0; mb < TL::kMBlocks; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(ro, off4(mb, j), 0, kSysScope);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              o[0][mb][4 * j + e] = fmaf(f, __uint_as_float(v[e]), o[0][mb][4 * j + e]);
+          }
+      }
+      if (tid == 0) __hip_atomic_store(p.counters + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 
   // ---- finalize: O = O^T / l, rounded to bf16; padding rows get zeros
 #pragma unroll
@@ -450,7 +772,10 @@ hipError_t launch_rb(const LaunchParams &p, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
   const int bm = 128 * RB;
   const int tiles = (G * p.L + bm - 1) / bm;
-  dim3 grid(tiles, p.Hkv, p.B);
+  // key split: one workgroup per piece, at most one per tile plus half the
+  // slots (see find_piece)
+  dim3 grid = p.ws_o ? dim3((unsigned)((long long)tiles * p.Hkv * p.B + max(1, p.num_splits / 2)))
+                     : dim3((unsigned)((long long)tiles * p.Hkv), p.B);
   const long long pool = (long long)p.num_pages * p.Hkv * p.ps * D * 2;
   if (p.dbg_trace || p.dbg_visits) {
     hipLaunchKernelGGL((prefill_kernel<D, true, kStageLanes, RB>), grid, dim3(256), 0, stream, p,
@@ -468,7 +793,8 @@ hipError_t launch_rb(const LaunchParams &p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// One row block per wave: two row blocks halve the LDS traffic per flop but
+// One row block per wave (the key split assumes it): two row blocks halve
+// the LDS traffic per flop but
 // need the accumulation registers of 64 rows, which leaves one wave per SIMD
 // and measured slower than two waves of one row block each.
 template <int D>

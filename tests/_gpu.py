@@ -77,7 +77,10 @@ def run_decode(api, d: DeviceInputs, *, partition_tokens=0, trace=False, keep_ws
     return out, extras
 
 
-def run_prefill(api, d: DeviceInputs, *, trace=False):
+def run_prefill(api, d: DeviceInputs, *, trace=False, split=True, num_cus=0):
+    """pa_prefill on device inputs; `split` passes the key-split workspace
+    of pa_prefill_plan (for `num_cus` compute units), whose counters must be
+    zero again afterwards (returned in extras["counters"])."""
     out = d.out()
     x = d.x
     extras = {}
@@ -88,8 +91,11 @@ def run_prefill(api, d: DeviceInputs, *, trace=False):
         dbg_v = torch.zeros((x.B, x.H_kv, cap), dtype=torch.int32, device=d.q.device)
     args = api.make_args(d.q, d.kp, d.vp, d.bt, d.cl, out, scale=x.scale, mask=d.mask,
                          query_lens=d.ql, debug_trace=dbg_t, debug_visits=dbg_v)
-    api.pa_prefill(args)
+    ws = api.PrefillWorkspace.for_args(args, d.q.device, num_cus=num_cus) if split else None
+    api.pa_prefill(args, ws)
     torch.cuda.synchronize()
+    if ws is not None and ws.counters is not None:
+        extras["counters"] = ws.counters.cpu().numpy()
     if trace:
         extras["trace"] = dbg_t.cpu().numpy()
         extras["visits"] = dbg_v.cpu().numpy()

@@ -60,9 +60,14 @@ def test_prefill_parity_random_shapes(api, case):
             v[b] = 0
     assert np.array_equal(ex["trace"], tr)
     assert np.array_equal(ex["visits"], v)
-    # the same inputs through the fast staging paths (no trace)
-    out2, _ = run_prefill(api, DeviceInputs(x))
-    assert_parity(out2, ref, dt, f"prefill case{seed} fast path")
+    # the same inputs through the fast staging paths (no trace), with the
+    # key split (default plan, and one with pieces as short as allowed) and
+    # without it; the arrival counters are left at zero
+    for kw in (dict(), dict(num_cus=512), dict(split=False)):
+        out2, ex2 = run_prefill(api, DeviceInputs(x), **kw)
+        assert_parity(out2, ref, dt, f"prefill case{seed} fast path {kw}")
+        if "counters" in ex2:
+            assert not ex2["counters"].any()
 
 
 def test_prefill_stale_data_and_relabel_bit_identical(api):
@@ -98,9 +103,36 @@ def test_prefill_equals_decode_for_short_chunks(api):
 def test_c3_chunked_prefill_full_size(api):
     x = make_c3()
     print(f"[C3] seed={x.seed} ctx={x.context_lens.tolist()}", flush=True)
-    out, _ = run_prefill(api, DeviceInputs(x))
-    err = assert_parity(out, oracle.attention_of(x), "bf16", "C3")
-    print(f"[C3] max abs err {err:.3e}", flush=True)
+    ref = oracle.attention_of(x)
+    d = DeviceInputs(x)
+    for kw in (dict(), dict(split=False)):
+        out, ex = run_prefill(api, d, **kw)
+        err = assert_parity(out, ref, "bf16", f"C3 {kw}")
+        assert "counters" not in ex or not ex["counters"].any()
+        print(f"[C3] {kw} max abs err {err:.3e}", flush=True)
+
+
+def test_key_split_matches_unsplit_and_repeats(api):
+    """Pieces merged by the last one to arrive give the unsplit result to
+    rounding, call after call on one workspace (the counters reset)."""
+    import torch
+    x = make_random(71, B=3, H_q=16, H_kv=2, L=200, D=128, page_size=16,
+                    ctx=[3000, 200, 1500], dtype="bf16", causal=True)
+    d = DeviceInputs(x)
+    ref = oracle.attention_of(x)
+    base, _ = run_prefill(api, d, split=False)
+    out = d.out()
+    args = api.make_args(d.q, d.kp, d.vp, d.bt, d.cl, out, scale=x.scale, mask=d.mask)
+    plan = api.pa_prefill_plan(args, num_cus=512)
+    ws = api.PrefillWorkspace(plan, x.D, d.q.device)
+    for rep in range(3):
+        out.zero_()
+        api.pa_prefill(args, ws)
+        torch.cuda.synchronize()
+        assert_parity(out, ref, "bf16", f"split rep {rep}")
+        assert not ws.counters.any().item()
+        diff = np.abs(host_f64(out) - host_f64(base)).max()
+        assert diff <= 2.0 ** -7, diff
 
 
 def test_c5_mixed_batch_full_size(api):
@@ -146,8 +178,9 @@ def test_prefill_late_score_spike_is_exact(api, dtype):
     x = _plant_spike(x, 0, 300, 16.0)
     x = _plant_spike(x, 1, 150, 16.0)
     ref = oracle.attention_of(x)
-    out, _ = run_prefill(api, DeviceInputs(x))
-    assert_parity(out, ref, dtype, "prefill spike")
+    for kw in (dict(), dict(num_cus=512), dict(split=False)):
+        out, _ = run_prefill(api, DeviceInputs(x), **kw)
+        assert_parity(out, ref, dtype, f"prefill spike {kw}")
 
 
 def test_decode_late_score_spike_is_exact(api):
