@@ -10,16 +10,18 @@
 // tile through the block table, fold it in with the online softmax).
 //
 // Per key tile:
-//   1. staging: every thread issues 16-byte loads of the K and V rows of the
-//      tile TWO ahead (address = physical page from the block table, slot, kv
-//      head) into one of two register sets while the current tile is
-//      computed, and stores the set loaded one tile earlier (the next tile)
-//      to the other LDS buffer, so a load has a whole tile of compute to
-//      arrive (two LDS buffers, one barrier per tile).  When
-//      page_size is a multiple of 16, each 16-key staging round lies in one
-//      page: its block-table entry is a scalar load (SGPR) and the round is a
-//      buffer load from that page with a per-thread offset fixed for the
-//      whole walk, so staging costs no per-lane address arithmetic;
+//   1. staging, with two LDS buffers and one barrier per tile.  When
+//      page_size is a multiple of 16, each 16-key run of a tile lies in one
+//      page: its block-table entry is a scalar load (SGPR) and the run is
+//      read with buffer loads from that page at per-lane offsets fixed for
+//      the whole walk, so staging costs no per-lane address arithmetic.
+//      With D = 128 and a pool under 2 GiB the loads write LDS directly
+//      (kStageDma: wave w loads run w of the next tile into the other
+//      buffer while the current tile is computed; no staging registers, no
+//      LDS stores; rows swizzled so that the operand reads stay
+//      conflict-free).  Otherwise every thread loads the tile TWO ahead
+//      into one of two register sets and stores the set loaded one tile
+//      earlier to the other LDS buffer;
 //   2. S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: K from LDS is the A
 //      operand, Q (kept in registers for the whole walk) the B operand.  The
 //      result gives every lane the scores of ONE query row (lane % 32) against
@@ -160,17 +162,14 @@ __device__ __forceinline__ int div_small(int x, int d, float rcp) {
 // workspace slots in pair order.  All 256 threads take part: each owns a
 // contiguous slice of pairs, per-thread counts are scanned within waves
 // (DPP) and across the four waves (LDS), and the thread whose slice holds
-// this workgroup's piece publishes it in s_pc.  ta: 3 tables of
-// kSplitMaxPairs ints, tb: 1 table plus 32 ints of scratch; the block
+// this workgroup's piece publishes it in s_pc.  s_ctx, s_ql, s_len and
+// s_keys: kSplitMaxPairs ints each, s_red 32 ints of scratch; the block
 // synchronises before returning (the tables live in the staging buffers).
-__device__ void find_piece(const LaunchParams &p, int nt, int *ta, int *tb, Piece *s_pc,
-                           Piece &pc) {
+__device__ void find_piece(const LaunchParams &p, int nt, int *s_ctx, int *s_ql, int *s_len,
+                           int *s_keys, int *s_red, Piece *s_pc, Piece &pc) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int G = p.Hq / p.Hkv;
-  int *s_ctx = ta, *s_ql = ta + kSplitMaxPairs, *s_len = ta + 2 * kSplitMaxPairs;
-  int *s_keys = tb;
-  int *s_red = tb + kSplitMaxPairs;  // [5 values][4 waves], then 4 floats
   for (int b = tid; b < p.B; b += 256) {
     s_ctx[b] = p.cl[b];
     s_ql[b] = p.ql ? p.ql[b] : p.L;
@@ -310,29 +309,59 @@ __device__ void find_piece(const LaunchParams &p, int nt, int *ta, int *tb, Piec
 // the whole K (V) pool and the run's position in the SGPR offset (pools
 // under 2 GiB, so that offsets stay below 2^31 and an offset of 2^31 is
 // always out of range).
-enum StageMode { kStageLanes = 0, kStageRun = 1, kStagePool = 2 };
+// kStageDma: the runs of kStagePool with the K/V rows written straight into
+// LDS by the loads (no staging registers, no LDS stores): D = 128 only.
+enum StageMode { kStageLanes = 0, kStageRun = 1, kStagePool = 2, kStageDma = 3 };
+
+// Swizzle of the 16-byte chunks of K/V row R in the unpadded LDS tile of
+// kStageDma (chunk c of the row lives at position c ^ swz(R)): a bijection
+// on R mod 16, so the K operand reads (16 consecutive rows, one chunk) and
+// the transposed V reads (4 consecutive rows, two adjacent chunks) hit
+// distinct bank groups, as the padded strides do in the other modes.
+__device__ __forceinline__ int swz(int r) {
+  return ((r & 3) << 1) | (((r >> 2) & 1) << 3) | ((r >> 3) & 1);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <int D, bool DEBUG, int MODE, int RB>
 __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchParams p,
                                                                        int num_tiles) {
   constexpr bool UNIFORM = MODE != kStageLanes;
+  constexpr bool DMA = MODE == kStageDma;
   constexpr int kRW = 32 * RB;     // packed rows per wave
   constexpr int kBM = 4 * kRW;     // packed rows per workgroup
   using TL = Tile<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kBN * TL::kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kBN * TL::kVStride];
+  static_assert(!DMA || (D == 128 && RB == 1), "DMA staging: D = 128, one row block per wave");
+  // Tile buffers: padded [key][dim] rows (register staging), or four
+  // separate unpadded, swizzled arrays (DMA staging: separate arrays let the
+  // compiler see that a load into one buffer never feeds reads of the other).
+  constexpr int kKS = DMA ? D : TL::kKStride;   // shorts per K row
+  constexpr int kVS = DMA ? D : TL::kVStride;   // shorts per V row
+  constexpr int kPadBuf = DMA ? 1 : 2;
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kPadBuf][DMA ? 8 : kBN * kKS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kPadBuf][DMA ? 8 : kBN * kVS];
+  __shared__ __attribute__((aligned(16))) uint16_t kd0[DMA ? kBN * D : 8], kd1[DMA ? kBN * D : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t vd0[DMA ? kBN * D : 8], vd1[DMA ? kBN * D : 8];
   __shared__ uint32_t s_arrived;
   __shared__ Piece s_pc;
-  static_assert(sizeof(v_lds) >= 3 * kSplitMaxPairs * 4 &&
-                sizeof(k_lds) >= (kSplitMaxPairs + 32) * 4, "plan tables");
+  uint16_t *const kbuf0 = DMA ? kd0 : k_lds[0], *const kbuf1 = DMA ? kd1 : k_lds[kPadBuf - 1];
+  uint16_t *const vbuf0 = DMA ? vd0 : v_lds[0], *const vbuf1 = DMA ? vd1 : v_lds[kPadBuf - 1];
+  // the planner's tables: two in each of two staging areas, scratch in a third
+  int *const plan_a = reinterpret_cast<int *>(DMA ? kd0 : &k_lds[0][0]);
+  int *const plan_b = reinterpret_cast<int *>(DMA ? kd1 : &v_lds[0][0]);
+  int *const plan_s = DMA ? reinterpret_cast<int *>(vd0) : plan_b + 2 * kSplitMaxPairs;
+  static_assert((DMA ? sizeof(kd0) : sizeof(k_lds)) >= 2 * kSplitMaxPairs * 4 &&
+                (DMA ? sizeof(kd1) : sizeof(v_lds) - 32 * 4) >= 2 * kSplitMaxPairs * 4 &&
+                (DMA ? sizeof(vd0) : 32 * 4) >= 32 * 4, "plan tables");
 
   // ---- which keys of which tile: a piece of the key split (workspace
   // given), else the whole tile (heavy, late tiles first)
   int tile, g, b, k0 = 0, k1 = 0x7fffffff, np = 1, sp = 0, slot = 0;
   if (p.ws_o != nullptr) {
     Piece pc;
-    find_piece(p, num_tiles, reinterpret_cast<int *>(&v_lds[0][0]),
-               reinterpret_cast<int *>(&k_lds[0][0]), &s_pc, pc);
+    find_piece(p, num_tiles, plan_a, plan_a + kSplitMaxPairs, plan_b, plan_b + kSplitMaxPairs,
+               plan_s, &s_pc, pc);
     if (!pc.found) return;  // block-uniform
     tile = pc.tile;
     g = pc.g;
@@ -350,7 +379,7 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
   }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int half = lane >> 5;       // which 8-wide k chunk / key half this lane holds
   const int ln = lane & 31;         // query row of this lane within the wave
 
@@ -407,7 +436,7 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
   const int chunk = tid % TL::kChunks;
   const int key_in_round = tid / TL::kChunks;
   struct Stage {
-    uint4 k[TL::kRounds], v[TL::kRounds];
+    uint4 k[DMA ? 1 : TL::kRounds], v[DMA ? 1 : TL::kRounds];
   };
 
   // The block table is read-only for the whole call: reading it through the
@@ -434,6 +463,40 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
       const_cast<char *>(kp_bytes), (short)0, pool_bytes, kBufferRsrcWord3);
   const __amdgpu_buffer_rsrc_t pool_v = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char *>(vp_bytes), (short)0, pool_bytes, kBufferRsrcWord3);
+  // DMA staging: wave w loads run w (keys 16w .. 16w + 15) of a tile, four
+  // rows per instruction; lane l of instruction j writes LDS position l of
+  // rows 16w + 4j .. 16w + 4j + 3 with the global chunk that the swizzle
+  // puts there.  The per-lane offsets are fixed for the whole walk; the run's
+  // page and slot are advanced by BN keys per tile.
+  int dma_voff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r16 = 4 * j + (lane >> 4);
+    dma_voff[j] = r16 * (D * 2) + (((lane & 15) ^ swz(r16)) * 16);
+  }
+  int dma_lp = 0, dma_slot = 0;
+  auto dma_tile = [&](int T, uint16_t *kdst, uint16_t *vdst) {
+    const int run0 = T * kBN + 16 * wave;      // first key of this wave's run
+    const bool live = run0 < kend_wg;          // wave-uniform
+    const int page = live ? btc[min(dma_lp, p.max_pages - 1)] : 0;
+    const int soff = page * (int)page_bytes + (int)head_bytes + dma_slot * (D * 2);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // rows past the workgroup's last key read as zeros (stale slots may
+      // hold anything, NaN included)
+      const bool row_live = run0 + 4 * j + (lane >> 4) < kend_wg;
+      const int voff = row_live ? dma_voff[j] : (int)0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_k, (lds_void_t *)(kdst + (16 * wave + 4 * j) * D),
+                                               16, voff, soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_v, (lds_void_t *)(vdst + (16 * wave + 4 * j) * D),
+                                               16, voff, soff, 0, 0);
+    }
+    dma_slot += kBN;
+    while (dma_slot >= p.ps) {
+      dma_slot -= p.ps;
+      ++dma_lp;
+    }
+  };
   auto stage_load_uniform = [&](int kt, Stage &st) {
     (void)kt;  // runs follow run_j0, which tracks kt * BN
 #pragma unroll
@@ -506,12 +569,14 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
       }
     }
   };
-  auto stage_store = [&](int buf, const Stage &st) {
+  auto stage_store = [&](uint16_t *kdst, uint16_t *vdst, const Stage &st) {
+    if constexpr (!DMA) {
 #pragma unroll
-    for (int r = 0; r < TL::kRounds; ++r) {
-      const int key = r * TL::kKeysPerRound + key_in_round;
-      *reinterpret_cast<uint4 *>(&k_lds[buf][key * TL::kKStride + chunk * 8]) = st.k[r];
-      *reinterpret_cast<uint4 *>(&v_lds[buf][key * TL::kVStride + chunk * 8]) = st.v[r];
+      for (int r = 0; r < TL::kRounds; ++r) {
+        const int key = r * TL::kKeysPerRound + key_in_round;
+        *reinterpret_cast<uint4 *>(&kdst[key * kKS + chunk * 8]) = st.k[r];
+        *reinterpret_cast<uint4 *>(&vdst[key * kVS + chunk * 8]) = st.v[r];
+      }
     }
   };
 
@@ -542,26 +607,43 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
   run_j0 = k0;
   run_lp = k0 / p.ps;
   run_slot = k0 - run_lp * p.ps;
-  // a piece may start inside a page: its first entry is read here (later
-  // ones when a run starts a page)
-  if constexpr (UNIFORM) run_page = run_j0 < kend_wg ? btc[min(run_lp, p.max_pages - 1)] : 0;
-  if (ntiles > 0) {
-    stage_load(kt0, sa);
-    stage_store(0, sa);
+  if constexpr (DMA) {
+    // tile kt0 goes to buffer 0; the first step waits for it (no load is
+    // issued that the walk does not wait for: LDS must not be written after
+    // the workgroup ends)
+    dma_lp = (k0 + 16 * wave) / p.ps;
+    dma_slot = (k0 + 16 * wave) - dma_lp * p.ps;
+    if (ntiles > 0) dma_tile(kt0, kbuf0, vbuf0);
+  } else {
+    // a piece may start inside a page: its first entry is read here (later
+    // ones when a run starts a page)
+    if constexpr (UNIFORM) run_page = run_j0 < kend_wg ? btc[min(run_lp, p.max_pages - 1)] : 0;
+    if (ntiles > 0) {
+      stage_load(kt0, sa);
+      stage_store(kbuf0, vbuf0, sa);
+    }
+    if (kTwoSets && (UNIFORM || ntiles > 1)) stage_load(kt0 + 1, sb);
+    // the query and tile-0 loads are complete here; tile 1 stays in flight
+    __builtin_amdgcn_s_waitcnt(kWaitVmcntOlderThan8);
+    __syncthreads();
   }
-  if (kTwoSets && (UNIFORM || ntiles > 1)) stage_load(kt0 + 1, sb);
-  // the query and tile-0 loads are complete here; tile 1 stays in flight
-  __builtin_amdgcn_s_waitcnt(kWaitVmcntOlderThan8);
-  __syncthreads();
 
   // One tile: prefetch tile kt + 2 into `ld` (its set is free: tile kt was
   // stored to LDS one tile ago), compute tile kt, then store tile kt + 1
   // (loaded into `st` one tile ago) to the other LDS buffer.
   const int kt_end = kt0 + ntiles;
-  auto tile_step = [&](int kt, Stage &ld, const Stage &st) {
-    const int buf = (kt - kt0) & 1;
+  // kc/vc: the buffers of tile kt; kn/vn: the other pair (tile kt + 1)
+  auto tile_step = [&](int kt, Stage &ld, const Stage &st, const uint16_t *kc, const uint16_t *vc,
+                       uint16_t *kn, uint16_t *vn) {
     const bool more = kt + 1 < kt_end;
-    if constexpr (kTwoSets) {
+    if constexpr (DMA) {
+      // tile kt is in LDS once every wave's loads of it are done; after the
+      // barrier no wave still reads tile kt - 1, whose buffers take tile
+      // kt + 1 (a whole tile of compute to arrive)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (more) dma_tile(kt + 1, kn, vn);
+    } else if constexpr (kTwoSets) {
       if (UNIFORM || kt + 2 < kt_end) stage_load(kt + 2, ld);
     } else {
       if (UNIFORM || more) stage_load(kt + 1, ld);
@@ -580,10 +662,12 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) s[rb][i] = 0.f;
-        const uint16_t *krow = &k_lds[buf][(blk * 32 + ln) * TL::kKStride + half * 8];
+        const int krw = blk * 32 + ln;
+        const uint16_t *krow = kc + krw * kKS;
 #pragma unroll
         for (int kk = 0; kk < TL::kKSteps; ++kk) {
-          const uint4 a = *reinterpret_cast<const uint4 *>(krow + kk * 16);
+          const int kcol = DMA ? (((2 * kk + half) ^ swz(krw)) * 8) : (kk * 16 + half * 8);
+          const uint4 a = *reinterpret_cast<const uint4 *>(krow + kcol);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
             s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(q[rb][kk]),
@@ -635,8 +719,10 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
 #pragma unroll
           for (int mb = 0; mb < TL::kMBlocks; ++mb) {
             const int d0 = mb * 32 + ((lane >> 4) & 1) * 16 + 4 * (src & 3);
-            const uint16_t *r1 = &v_lds[buf][(kb + (src >> 2)) * TL::kVStride + d0];
-            const uint16_t *r2 = r1 + 8 * TL::kVStride;
+            const int vr = kb + (src >> 2);
+            const uint16_t *r1 = vc + vr * kVS + (DMA ? (((d0 >> 3) ^ swz(vr)) * 8 + (d0 & 7)) : d0);
+            const uint16_t *r2 = vc + (vr + 8) * kVS +
+                                 (DMA ? (((d0 >> 3) ^ swz(vr + 8)) * 8 + (d0 & 7)) : d0);
             const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)r1);
             const s16x4_t t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)r2);
             const uint4 aop = make_uint4(
@@ -653,17 +739,18 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
       }
     }
 
-    if (more) stage_store(buf ^ 1, st);
-    __syncthreads();
-  };
-  if constexpr (kTwoSets) {
-    for (int kt = kt0; kt < kt_end; kt += 2) {  // unrolled by two so the sets stay in registers
-      tile_step(kt, sa, sb);
-      if (kt + 1 < kt_end) tile_step(kt + 1, sb, sa);
+    if constexpr (!DMA) {
+      if (more) stage_store(kn, vn, st);
+      __syncthreads();
     }
-  } else {
-    for (int kt = kt0; kt < kt_end; ++kt) tile_step(kt, sa, sa);
+  };
+  // unrolled by two: each half has its own staging set and LDS buffers
+  Stage &s2 = kTwoSets ? sb : sa;
+  for (int kt = kt0; kt < kt_end; kt += 2) {
+    tile_step(kt, sa, s2, kbuf0, vbuf0, kbuf1, vbuf1);
+    if (kt + 1 < kt_end) tile_step(kt + 1, s2, sa, kbuf1, vbuf1, kbuf0, vbuf0);
   }
+  if constexpr (DMA) __syncthreads();  // the last tile is read before a rerun restages
   // weights past 2^16 anywhere in the workgroup: walk again from the exact maxima
   bool over = false;
 #pragma unroll
@@ -784,8 +871,12 @@ hipError_t launch_rb(const LaunchParams &p, hipStream_t stream) {
     hipLaunchKernelGGL((prefill_kernel<D, false, kStageLanes, RB>), grid, dim3(256), 0, stream, p,
                        tiles);
   } else if (pool < (1ll << 31)) {
-    hipLaunchKernelGGL((prefill_kernel<D, false, kStagePool, RB>), grid, dim3(256), 0, stream, p,
-                       tiles);
+    if constexpr (D == 128 && RB == 1)
+      hipLaunchKernelGGL((prefill_kernel<D, false, kStageDma, RB>), grid, dim3(256), 0, stream, p,
+                         tiles);
+    else
+      hipLaunchKernelGGL((prefill_kernel<D, false, kStagePool, RB>), grid, dim3(256), 0, stream,
+                         p, tiles);
   } else {
     hipLaunchKernelGGL((prefill_kernel<D, false, kStageRun, RB>), grid, dim3(256), 0, stream, p,
                        tiles);
