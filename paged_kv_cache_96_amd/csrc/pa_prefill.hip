@@ -95,10 +95,19 @@ struct Tile {
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 
+// max(a, b, c) in one instruction, without the operand quieting that
+// fmaxf adds (the scores are finite or -inf).
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+constexpr uint32_t kBf16OnePair = 0x3f803f80u;  // bf16 (1, 1)
+
 // Max of a value held by lane l and lane l ^ 32.
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max3(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -313,13 +322,22 @@ __device__ void find_piece(const LaunchParams &p, int nt, int *s_ctx, int *s_ql,
 // LDS by the loads (no staging registers, no LDS stores): D = 128 only.
 enum StageMode { kStageLanes = 0, kStageRun = 1, kStagePool = 2, kStageDma = 3 };
 
-// Swizzle of the 16-byte chunks of K/V row R in the unpadded LDS tile of
-// kStageDma (chunk c of the row lives at position c ^ swz(R)): a bijection
-// on R mod 16, so the K operand reads (16 consecutive rows, one chunk) and
-// the transposed V reads (4 consecutive rows, two adjacent chunks) hit
-// distinct bank groups, as the padded strides do in the other modes.
-__device__ __forceinline__ int swz(int r) {
-  return ((r & 3) << 1) | (((r >> 2) & 1) << 3) | ((r >> 3) & 1);
+// LDS tile layout of kStageDma (64 rows x 16 chunks of 16 bytes, D = 128).
+// Rows come in blocks of 4 (b = (r / 4) % 4 within a 16-row group); a block
+// fills 1 KiB = 4 windows of 256 bytes (64 banks each), window w holding
+// chunks 4w .. 4w + 3 of the block's 4 rows: row r % 4 in the window's 64
+// bytes at 16 * (r % 4), chunk c in slot (c % 4) ^ b of them.  In shorts:
+//   (r / 16) * 2048 + b * 512 + (16 * (c / 4) + 4 * (r % 4) + ((c % 4) ^ b)) * 8.
+// - A K operand read (16 consecutive rows, one chunk) and a transposed V read
+//   (4 rows of a block, 4 consecutive chunks) each cover all 64 banks once.
+// - Every operand address is a per-lane base plus a constant: no per-read
+//   address arithmetic.
+// - One load instruction fills one block (4 whole rows, a contiguous 1 KiB of
+//   the page), each group of 4 lanes one aligned 64-byte piece of a row, the
+//   unit in which the vector memory path coalesces (see dma_tile).
+__device__ __forceinline__ int dma_pos(int r, int c) {
+  const int b = (r >> 2) & 3;
+  return (r >> 4) * 2048 + b * 512 + (16 * (c >> 2) + 4 * (r & 3) + ((c & 3) ^ b)) * 8;
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -463,33 +481,37 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
       const_cast<char *>(kp_bytes), (short)0, pool_bytes, kBufferRsrcWord3);
   const __amdgpu_buffer_rsrc_t pool_v = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char *>(vp_bytes), (short)0, pool_bytes, kBufferRsrcWord3);
-  // DMA staging: wave w loads run w (keys 16w .. 16w + 15) of a tile, four
-  // rows per instruction; lane l of instruction j writes LDS position l of
-  // rows 16w + 4j .. 16w + 4j + 3 with the global chunk that the swizzle
-  // puts there.  The per-lane offsets are fixed for the whole walk; the run's
-  // page and slot are advanced by BN keys per tile.
+  // DMA staging: wave w loads run w (keys 16w .. 16w + 15, row group w) of
+  // a tile; instruction j fills block j (rows 4j .. 4j + 3): lane l writes
+  // slot l of that 1 KiB with chunk 4 * (l / 16) + ((l % 4) ^ j) of row
+  // 4j + (l / 4) % 4 (see dma_pos).  The per-lane offsets are fixed for the
+  // whole walk; the run's page and slot are advanced by BN keys per tile.
+  const int dma_row = (lane >> 2) & 3;
   int dma_voff[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r16 = 4 * j + (lane >> 4);
-    dma_voff[j] = r16 * (D * 2) + (((lane & 15) ^ swz(r16)) * 16);
-  }
+  for (int j = 0; j < 4; ++j)
+    dma_voff[j] = (4 * j + dma_row) * (D * 2) + (4 * (lane >> 4) + ((lane & 3) ^ j)) * 16;
   int dma_lp = 0, dma_slot = 0;
   auto dma_tile = [&](int T, uint16_t *kdst, uint16_t *vdst) {
     const int run0 = T * kBN + 16 * wave;      // first key of this wave's run
     const bool live = run0 < kend_wg;          // wave-uniform
     const int page = live ? btc[min(dma_lp, p.max_pages - 1)] : 0;
     const int soff = page * (int)page_bytes + (int)head_bytes + dma_slot * (D * 2);
+    auto load = [&](int j, int voff) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_k, (lds_void_t *)(kdst + wave * 2048 + j * 512),
+                                               16, voff, soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_v, (lds_void_t *)(vdst + wave * 2048 + j * 512),
+                                               16, voff, soff, 0, 0);
+    };
+    if (run0 + 16 <= kend_wg) {  // wave-uniform: the whole run is live
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 4; ++j) load(j, dma_voff[j]);
+    } else {
       // rows past the workgroup's last key read as zeros (stale slots may
       // hold anything, NaN included)
-      const bool row_live = run0 + 4 * j + (lane >> 4) < kend_wg;
-      const int voff = row_live ? dma_voff[j] : (int)0x80000000u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_k, (lds_void_t *)(kdst + (16 * wave + 4 * j) * D),
-                                               16, voff, soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_v, (lds_void_t *)(vdst + (16 * wave + 4 * j) * D),
-                                               16, voff, soff, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        load(j, run0 + 4 * j + dma_row < kend_wg ? dma_voff[j] : (int)0x80000000u);
     }
     dma_slot += kBN;
     while (dma_slot >= p.ps) {
@@ -631,6 +653,18 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
   // One tile: prefetch tile kt + 2 into `ld` (its set is free: tile kt was
   // stored to LDS one tile ago), compute tile kt, then store tile kt + 1
   // (loaded into `st` one tile ago) to the other LDS buffer.
+  // kStageDma operand bases (block 0, first steps): K for even / odd k-steps
+  // (2 kk + half), V rows kb .. kb + 3 and kb + 8 .. kb + 11 of the
+  // transposed reads; every other read adds a constant (see dma_pos)
+  int k_dma[2] = {0, 0}, v_dma[2] = {0, 0};
+  if constexpr (DMA) {
+    k_dma[0] = dma_pos(ln, half);
+    k_dma[1] = dma_pos(ln, 2 + half);
+    const int src = lane & 15;
+    const int d0 = ((lane >> 4) & 1) * 16 + 4 * (src & 3);
+    v_dma[0] = dma_pos(half * 4 + (src >> 2), d0 >> 3) + (d0 & 7);
+    v_dma[1] = dma_pos(half * 4 + (src >> 2) + 8, d0 >> 3) + (d0 & 7);
+  }
   const int kt_end = kt0 + ntiles;
   // kc/vc: the buffers of tile kt; kn/vn: the other pair (tile kt + 1)
   auto tile_step = [&](int kt, Stage &ld, const Stage &st, const uint16_t *kc, const uint16_t *vc,
@@ -662,12 +696,12 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) s[rb][i] = 0.f;
-        const int krw = blk * 32 + ln;
-        const uint16_t *krow = kc + krw * kKS;
+        const uint16_t *krow = kc + (blk * 32 + ln) * kKS;
 #pragma unroll
         for (int kk = 0; kk < TL::kKSteps; ++kk) {
-          const int kcol = DMA ? (((2 * kk + half) ^ swz(krw)) * 8) : (kk * 16 + half * 8);
-          const uint4 a = *reinterpret_cast<const uint4 *>(krow + kcol);
+          const uint16_t *ka = DMA ? kc + k_dma[kk & 1] + blk * 4096 + (kk >> 1) * 128
+                                   : krow + kk * 16 + half * 8;
+          const uint4 a = *reinterpret_cast<const uint4 *>(ka);
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
             s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(q[rb][kk]),
@@ -687,21 +721,26 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
         uint32_t pb[RB][8];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
-          float mx = s[rb][0];
+          float mx = max3(s[rb][0], s[rb][1], s[rb][2]);
 #pragma unroll
-          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[rb][i]);
-          mx = pair_max(mx) * c;
+          for (int i = 3; i < 15; i += 2) mx = max3(mx, s[rb][i], s[rb][i + 1]);
+          mx = pair_max(max3(mx, s[rb][15], s[rb][15])) * c;
           if (pass == 0 && kt == kt0 && blk == 0) m_ref[rb] = fmaxf(mx, kMinM);
           m_seen[rb] = fmaxf(m_seen[rb], mx);
-          float psum = 0.f;
+          // the row sum adds the bf16 weights that PV multiplies (dot2 with
+          // (1, 1): exact products, fp32 sums), in two chains
+          float psum0 = 0.f, psum1 = 0.f;
 #pragma unroll
           for (int i = 0; i < 16; i += 2) {
             const float p0 = fast_exp2(fmaf(s[rb][i], c, -m_ref[rb]));  // masked -> 0
             const float p1 = fast_exp2(fmaf(s[rb][i + 1], c, -m_ref[rb]));
-            psum += p0 + p1;
             pb[rb][i >> 1] = cvt_pk_bf16(p0, p1);
+            if (i & 2)
+              psum1 = dot2_bf16(pb[rb][i >> 1], kBf16OnePair, psum1);
+            else
+              psum0 = dot2_bf16(pb[rb][i >> 1], kBf16OnePair, psum0);
           }
-          l_run[rb] += psum;
+          l_run[rb] += psum0 + psum1;
         }
 
         // -- O^T += V^T P^T over the block's two 16-key steps; each V^T
@@ -720,9 +759,9 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
           for (int mb = 0; mb < TL::kMBlocks; ++mb) {
             const int d0 = mb * 32 + ((lane >> 4) & 1) * 16 + 4 * (src & 3);
             const int vr = kb + (src >> 2);
-            const uint16_t *r1 = vc + vr * kVS + (DMA ? (((d0 >> 3) ^ swz(vr)) * 8 + (d0 & 7)) : d0);
-            const uint16_t *r2 = vc + (vr + 8) * kVS +
-                                 (DMA ? (((d0 >> 3) ^ swz(vr + 8)) * 8 + (d0 & 7)) : d0);
+            const int vo = blk * 4096 + hf * 2048 + mb * 128;  // kStageDma
+            const uint16_t *r1 = DMA ? vc + v_dma[0] + vo : vc + vr * kVS + d0;
+            const uint16_t *r2 = DMA ? vc + v_dma[1] + vo : vc + (vr + 8) * kVS + d0;
             const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)r1);
             const s16x4_t t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)r2);
             const uint4 aop = make_uint4(
