@@ -6,8 +6,9 @@
 // the rows of a tile sit at nearly the same causal position.  A wave owns RB
 // blocks of 32 rows: every K and V operand it reads from LDS feeds RB matrix
 // instructions (the launcher uses RB = 1; see launch_d).  Keys are walked
-// in tiles of BN = 64 (tiny-llm "Week 3 Day 4", "Task 2": resolve every K/V
-// tile through the block table, fold it in with the online softmax).
+// in tiles of BN = 32 (LDS loads, below) or 64 keys (tiny-llm "Week 3 Day
+// 4", "Task 2": resolve every K/V tile through the block table, fold it in
+// with the online softmax).
 //
 // Per key tile:
 //   1. staging, with two LDS buffers and one barrier per tile.  When
@@ -16,12 +17,14 @@
 //      read with buffer loads from that page at per-lane offsets fixed for
 //      the whole walk, so staging costs no per-lane address arithmetic.
 //      With D = 128 and a pool under 2 GiB the loads write LDS directly
-//      (kStageDma: wave w loads run w of the next tile into the other
-//      buffer while the current tile is computed; no staging registers, no
-//      LDS stores; rows swizzled so that the operand reads stay
-//      conflict-free).  Otherwise every thread loads the tile TWO ahead
-//      into one of two register sets and stores the set loaded one tile
-//      earlier to the other LDS buffer;
+//      (kStageDma): 32-key tiles, wave w loads keys 8w .. 8w + 7 of the next
+//      tile into the other buffer once the current tile's scores are
+//      computed; no staging registers and no LDS stores, so a workgroup
+//      needs 33 KiB of LDS and fits three waves per SIMD (the launch
+//      bounds ask for three workgroups per compute unit); the tile layout
+//      (dma_pos) keeps the operand reads conflict-free.  Otherwise 64-key tiles: every thread loads the
+//      tile TWO ahead into one of two register sets and stores the set
+//      loaded one tile earlier to the other LDS buffer;
 //   2. S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: K from LDS is the A
 //      operand, Q (kept in registers for the whole walk) the B operand.  The
 //      result gives every lane the scores of ONE query row (lane % 32) against
@@ -343,10 +346,15 @@ __device__ __forceinline__ int dma_pos(int r, int c) {
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <int D, bool DEBUG, int MODE, int RB>
-__global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchParams p,
-                                                                       int num_tiles) {
+__global__ __launch_bounds__(256, MODE == kStageDma ? 3 : RB == 1 ? 2 : 1) void prefill_kernel(
+    LaunchParams p, int num_tiles) {
   constexpr bool UNIFORM = MODE != kStageLanes;
   constexpr bool DMA = MODE == kStageDma;
+  // keys per tile: DMA staging walks tiles of 32 keys (two 16 KiB buffers,
+  // three workgroups per compute unit); the split plan's 64-key grid is a
+  // multiple of it
+  constexpr int BN = DMA ? 32 : kBN;
+  constexpr int NBLK = BN / 32;    // 32-key blocks per tile
   constexpr int kRW = 32 * RB;     // packed rows per wave
   constexpr int kBM = 4 * kRW;     // packed rows per workgroup
   using TL = Tile<D>;
@@ -359,27 +367,31 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
   constexpr int kPadBuf = DMA ? 1 : 2;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[kPadBuf][DMA ? 8 : kBN * kKS];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[kPadBuf][DMA ? 8 : kBN * kVS];
-  __shared__ __attribute__((aligned(16))) uint16_t kd0[DMA ? kBN * D : 8], kd1[DMA ? kBN * D : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t vd0[DMA ? kBN * D : 8], vd1[DMA ? kBN * D : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t kd0[DMA ? BN * D : 8], kd1[DMA ? BN * D : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t vd0[DMA ? BN * D : 8], vd1[DMA ? BN * D : 8];
+  __shared__ int s_plan_red[DMA ? 32 : 1];
   __shared__ uint32_t s_arrived;
   __shared__ Piece s_pc;
   uint16_t *const kbuf0 = DMA ? kd0 : k_lds[0], *const kbuf1 = DMA ? kd1 : k_lds[kPadBuf - 1];
   uint16_t *const vbuf0 = DMA ? vd0 : v_lds[0], *const vbuf1 = DMA ? vd1 : v_lds[kPadBuf - 1];
-  // the planner's tables: two in each of two staging areas, scratch in a third
+  // the planner's tables (kSplitMaxPairs ints each) live in the staging
+  // buffers: one per buffer with DMA staging, two per buffer otherwise
   int *const plan_a = reinterpret_cast<int *>(DMA ? kd0 : &k_lds[0][0]);
-  int *const plan_b = reinterpret_cast<int *>(DMA ? kd1 : &v_lds[0][0]);
-  int *const plan_s = DMA ? reinterpret_cast<int *>(vd0) : plan_b + 2 * kSplitMaxPairs;
-  static_assert((DMA ? sizeof(kd0) : sizeof(k_lds)) >= 2 * kSplitMaxPairs * 4 &&
-                (DMA ? sizeof(kd1) : sizeof(v_lds) - 32 * 4) >= 2 * kSplitMaxPairs * 4 &&
-                (DMA ? sizeof(vd0) : 32 * 4) >= 32 * 4, "plan tables");
+  int *const plan_b = reinterpret_cast<int *>(DMA ? kd1 : &k_lds[0][0] + kSplitMaxPairs * 2);
+  int *const plan_c = reinterpret_cast<int *>(DMA ? vd0 : &v_lds[0][0]);
+  int *const plan_d = reinterpret_cast<int *>(DMA ? vd1 : &v_lds[0][0] + kSplitMaxPairs * 2);
+  int *const plan_s = DMA ? s_plan_red : plan_d + kSplitMaxPairs;
+  static_assert(DMA ? sizeof(kd0) >= kSplitMaxPairs * 4 && sizeof(vd1) >= kSplitMaxPairs * 4
+                    : sizeof(k_lds) >= 2 * kSplitMaxPairs * 4 &&
+                          sizeof(v_lds) >= 2 * kSplitMaxPairs * 4 + 32 * 4,
+                "plan tables");
 
   // ---- which keys of which tile: a piece of the key split (workspace
   // given), else the whole tile (heavy, late tiles first)
   int tile, g, b, k0 = 0, k1 = 0x7fffffff, np = 1, sp = 0, slot = 0;
   if (p.ws_o != nullptr) {
     Piece pc;
-    find_piece(p, num_tiles, plan_a, plan_a + kSplitMaxPairs, plan_b, plan_b + kSplitMaxPairs,
-               plan_s, &s_pc, pc);
+    find_piece(p, num_tiles, plan_a, plan_b, plan_c, plan_d, plan_s, &s_pc, pc);
     if (!pc.found) return;  // block-uniform
     tile = pc.tile;
     g = pc.g;
@@ -431,8 +443,8 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
                              : (p.causal ? ctx - Lb + rho_last_w / G + 1 : ctx));
   const int kfull_w = rho_last_w < rho_first_w ? 0
                       : (p.causal ? ctx - Lb + rho_first_w / G + 1 : ctx);  // keys below: unmasked
-  const int kt0 = k0 / kBN;  // first tile (k0 is a multiple of BN)
-  const int ntiles = kend_wg > k0 ? (kend_wg - k0 + kBN - 1) / kBN : 0;
+  const int kt0 = k0 / BN;  // first tile (k0 is a multiple of 64)
+  const int ntiles = kend_wg > k0 ? (kend_wg - k0 + BN - 1) / BN : 0;
   const bool counts = DEBUG && rows_valid > 0 && (rows_valid - 1) / kBM == tile;
 
   // ---- Q as the B operand of S^T = K Q^T: dims kk*16 + half*8 .. +8
@@ -481,39 +493,45 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
       const_cast<char *>(kp_bytes), (short)0, pool_bytes, kBufferRsrcWord3);
   const __amdgpu_buffer_rsrc_t pool_v = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char *>(vp_bytes), (short)0, pool_bytes, kBufferRsrcWord3);
-  // DMA staging: wave w loads run w (keys 16w .. 16w + 15, row group w) of
-  // a tile; instruction j fills block j (rows 4j .. 4j + 3): lane l writes
-  // slot l of that 1 KiB with chunk 4 * (l / 16) + ((l % 4) ^ j) of row
-  // 4j + (l / 4) % 4 (see dma_pos).  The per-lane offsets are fixed for the
-  // whole walk; the run's page and slot are advanced by BN keys per tile.
+  // DMA staging: wave w loads keys R*w .. R*w + R - 1 of a tile (R = BN / 4,
+  // within one page), i.e. blocks Bw .. Bw + R/4 - 1 of 4 rows (Bw = R/4 * w);
+  // instruction j fills block B = Bw + j: lane l writes slot l of that 1 KiB
+  // with chunk 4 * (l / 16) + ((l % 4) ^ (B % 4)) of row 4B + (l / 4) % 4
+  // (see dma_pos).  The per-lane offsets are fixed for the whole walk; the
+  // run's page and slot are advanced by BN keys per tile.
+  constexpr int kDmaRows = BN / 4;          // keys per wave and tile
+  constexpr int kDmaBlocks = kDmaRows / 4;  // load instructions per wave, K and V each
   const int dma_row = (lane >> 2) & 3;
-  int dma_voff[4];
+  int dma_voff[kDmaBlocks];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    dma_voff[j] = (4 * j + dma_row) * (D * 2) + (4 * (lane >> 4) + ((lane & 3) ^ j)) * 16;
+  for (int j = 0; j < kDmaBlocks; ++j) {
+    const int blk4 = (kDmaBlocks * wave + j) & 3;
+    dma_voff[j] = (4 * j + dma_row) * (D * 2) + (4 * (lane >> 4) + ((lane & 3) ^ blk4)) * 16;
+  }
   int dma_lp = 0, dma_slot = 0;
   auto dma_tile = [&](int T, uint16_t *kdst, uint16_t *vdst) {
-    const int run0 = T * kBN + 16 * wave;      // first key of this wave's run
-    const bool live = run0 < kend_wg;          // wave-uniform
+    const int run0 = T * BN + kDmaRows * wave;  // first key of this wave's run
+    const bool live = run0 < kend_wg;           // wave-uniform
     const int page = live ? btc[min(dma_lp, p.max_pages - 1)] : 0;
     const int soff = page * (int)page_bytes + (int)head_bytes + dma_slot * (D * 2);
     auto load = [&](int j, int voff) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_k, (lds_void_t *)(kdst + wave * 2048 + j * 512),
-                                               16, voff, soff, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_v, (lds_void_t *)(vdst + wave * 2048 + j * 512),
-                                               16, voff, soff, 0, 0);
+      const int dst = (kDmaBlocks * wave + j) * 512;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_k, (lds_void_t *)(kdst + dst), 16, voff, soff,
+                                               0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_v, (lds_void_t *)(vdst + dst), 16, voff, soff,
+                                               0, 0);
     };
-    if (run0 + 16 <= kend_wg) {  // wave-uniform: the whole run is live
+    if (run0 + kDmaRows <= kend_wg) {  // wave-uniform: the whole run is live
 #pragma unroll
-      for (int j = 0; j < 4; ++j) load(j, dma_voff[j]);
+      for (int j = 0; j < kDmaBlocks; ++j) load(j, dma_voff[j]);
     } else {
       // rows past the workgroup's last key read as zeros (stale slots may
       // hold anything, NaN included)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < kDmaBlocks; ++j)
         load(j, run0 + 4 * j + dma_row < kend_wg ? dma_voff[j] : (int)0x80000000u);
     }
-    dma_slot += kBN;
+    dma_slot += BN;
     while (dma_slot >= p.ps) {
       dma_slot -= p.ps;
       ++dma_lp;
@@ -567,7 +585,7 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
     }
 #pragma unroll
     for (int r = 0; r < TL::kRounds; ++r) {
-      const int j = kt * kBN + r * TL::kKeysPerRound + key_in_round;
+      const int j = kt * BN + r * TL::kKeysPerRound + key_in_round;
       if (j < kend_wg) {
         const int lp = j / p.ps;
         const int page = bt[lp];
@@ -633,8 +651,8 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
     // tile kt0 goes to buffer 0; the first step waits for it (no load is
     // issued that the walk does not wait for: LDS must not be written after
     // the workgroup ends)
-    dma_lp = (k0 + 16 * wave) / p.ps;
-    dma_slot = (k0 + 16 * wave) - dma_lp * p.ps;
+    dma_lp = (k0 + kDmaRows * wave) / p.ps;
+    dma_slot = (k0 + kDmaRows * wave) - dma_lp * p.ps;
     if (ntiles > 0) dma_tile(kt0, kbuf0, vbuf0);
   } else {
     // a piece may start inside a page: its first entry is read here (later
@@ -676,19 +694,18 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
       // kt + 1 (a whole tile of compute to arrive)
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
-      if (more) dma_tile(kt + 1, kn, vn);
     } else if constexpr (kTwoSets) {
       if (UNIFORM || kt + 2 < kt_end) stage_load(kt + 2, ld);
     } else {
       if (UNIFORM || more) stage_load(kt + 1, ld);
     }
 
-    if (kt * kBN < kend_w) {
-      // The tile's two 32-key blocks are processed one after the other
-      // (scores, softmax, PV), which keeps the score and P registers of a
-      // single block live.
+    if (kt * BN < kend_w) {
+      // The tile's 32-key blocks are processed one after the other (scores,
+      // softmax, PV), which keeps the score and P registers of a single
+      // block live.
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
+      for (int blk = 0; blk < NBLK; ++blk) {
         // -- S^T of this block; each K operand read from LDS feeds the RB
         //    row blocks
         f32x16_t s[RB];
@@ -707,13 +724,16 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
             s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(q[rb][kk]),
                                                             s[rb], 0, 0, 0);
         }
+        // DMA staging: the next tile's loads go out once this block's K
+        // operands have been read (they write the other buffer)
+        if (DMA && blk == 0 && more) dma_tile(kt + 1, kn, vn);
         // -- mask keys at or past each row's limit (diagonal / tail blocks only)
-        if (kt * kBN + (blk + 1) * 32 > kfull_w) {
+        if (kt * BN + (blk + 1) * 32 > kfull_w) {
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const int key = kt * kBN + blk * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+              const int key = kt * BN + blk * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
               if (key >= lim[rb]) s[rb][i] = kNegInf;
             }
         }
@@ -778,7 +798,9 @@ __global__ __launch_bounds__(256, RB == 1 ? 2 : 1) void prefill_kernel(LaunchPar
       }
     }
 
-    if constexpr (!DMA) {
+    if constexpr (DMA) {
+      if (kt * BN >= kend_w && more) dma_tile(kt + 1, kn, vn);  // no compute in this tile
+    } else {
       if (more) stage_store(kn, vn, st);
       __syncthreads();
     }
