@@ -126,6 +126,28 @@ class Runner:
         return {"S": S, "P": P, "schedule": sched, "fused": bool(ws.counters is not None),
                 "decode_ms": dec, "step_ms": step_ms, "wall_s": wall, "out": out}
 
+    def time_append(self, a, steps, warmup):
+        """Times pa_append of the write workload `a` (K/V rows and slots on the
+        device); the pool is the same every call (rows land in the same
+        slots), the last-level cache is flushed before each call."""
+        torch, api = self.torch, self.api
+        from tests._gpu import dev
+        p = a.paged
+        kp, vp = dev(p.key_pages), dev(p.value_pages)
+        k, v, sm = dev(a.key), dev(a.value), dev(a.slot_mapping)
+        for _ in range(warmup):
+            self.flush()
+            api.pa_append(k, v, sm, kp, vp)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e in ev:
+            self.flush()
+            e[0].record()
+            api.pa_append(k, v, sm, kp, vp)
+            e[1].record()
+        torch.cuda.synchronize()
+        return {"ms": np.array([e[0].elapsed_time(e[1]) for e in ev])}
+
     def time_prefill(self, d, steps, warmup, flush=False, split=True):
         """Times pa_prefill; `split` passes the key-split workspace of the
         library's plan (allocated outside the timed region)."""
@@ -199,7 +221,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="C2,C3,C4,C5,long")
+    ap.add_argument("--only", default="C2,C3,C4,C5,long,append")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--partition-tokens", type=int, default=0)
@@ -337,6 +359,30 @@ def main():
             "prefill_flops": fl, "prefill_tflops": round(fl / pm / 1e9, 2), "prefill_mean_ms": pm,
             "combined_ms": round(sm + pm, 5)}
         del dd, dp, rd, rp
+    if "append" in only:
+        # the K/V write that precedes attention (pa_append), timed on its own
+        wr = []
+        for name, kw in (
+                ("C2 decode step: 64 requests x 1 token, H_kv 8, D 128, page 16",
+                 dict(seed=2, B=64, H_kv=8, D=128, page_size=16, ctx_old=(127, 4095),
+                      n_new=[1] * 64)),
+                ("C3 chunks: 4 requests x 512 tokens after prefixes U[0,2048], H_kv 4, D 128, page 16",
+                 dict(seed=3, B=4, H_kv=4, D=128, page_size=16, ctx_old=(0, 2048),
+                      n_new=[512] * 4)),
+                ("long chunk: 1 request x 16384 tokens, H_kv 8, D 128, page 16",
+                 dict(seed=9, B=1, H_kv=8, D=128, page_size=16, ctx_old=[0], n_new=[16384]))):
+            a = W.make_append(dtype="bf16", **kw)
+            ra = run.time_append(a, max(10, args.steps // 3), args.warmup)
+            ms = float(np.mean(ra["ms"]))
+            gbs = a.moved_bytes() / (ms * 1e-3) / 1e9
+            log(f"[bench] append {name.split(':')[0]}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s")
+            wr.append({"workload": f"K/V write bf16, {name}", "tokens": a.num_tokens,
+                       "moved_bytes": a.moved_bytes(), "gbs": round(gbs, 2), **_stats(ra["ms"]),
+                       "roofline": {"bound": "hbm", "kernel": "append_kernel",
+                                    "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}})
+            del a
+        sections["append"] = wr
     result["sections"] = sections
 
     if not args.no_cpu_baseline:

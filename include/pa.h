@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 4
+#define PA_ABI_VERSION 5
 
 typedef enum {
   PA_OK = 0,
@@ -210,6 +210,47 @@ pa_status pa_prefill_plan(const pa_args *args, int32_t num_cus, pa_workspace *pl
  * (wrong schedule, fewer than 2 slots or counters than slots, missing
  * buffers or counters, misaligned). */
 pa_status pa_prefill(const pa_args *args, const pa_workspace *ws, void *stream);
+
+/* ---------------------------------------------------------------- write path
+ * The K/V write that precedes attention on every step: each new token's key
+ * and value rows are scattered to their physical slots in the page pool
+ * ("Reading vLLM's PagedAttention Kernel", section 3.2: the write path maps
+ * every token to a flat slot, physical page * page_size + offset in the page,
+ * and the read path gathers the slots back through the block table).  The
+ * runtime chooses the slots -- in tiny-llm "Week 3 Day 4" ("Decode Metadata")
+ * and anllm "Tutorial 13" (section 4, the request cache's append) a request
+ * fills its tail page before a new page is allocated -- and passes them in
+ * slot_mapping.  Every element of every row is copied bit for bit; nothing
+ * else in the pool is written.
+ *
+ * Layouts (dense, row-major, 16-byte aligned):
+ *   key, value            [num_tokens, num_kv_heads, head_dim]   (dtype)
+ *   slot_mapping          [num_tokens] int32; slot s of token t receives its
+ *                         rows in page s / page_size at offset s % page_size
+ *                         of every kv head; s < 0 (padding) or
+ *                         s >= num_pages * page_size skips the token
+ *   key_pages, value_pages [num_pages, num_kv_heads, page_size, head_dim]
+ * Two tokens with the same slot race (which one lands is unspecified).
+ * The pages may be read by attention calls enqueued after this one on the
+ * same stream. */
+typedef struct pa_append_args {
+  const void *key;               /* [num_tokens, num_kv_heads, head_dim] */
+  const void *value;             /* [num_tokens, num_kv_heads, head_dim] */
+  const int32_t *slot_mapping;   /* [num_tokens] */
+  void *key_pages;               /* [num_pages, num_kv_heads, page_size, head_dim] */
+  void *value_pages;             /* [num_pages, num_kv_heads, page_size, head_dim] */
+  int32_t num_tokens;            /* >= 0 (0: nothing to do) */
+  int32_t num_kv_heads;          /* >= 1 */
+  int32_t head_dim;              /* 64 or 128 */
+  int32_t num_pages;             /* >= 1 */
+  int32_t page_size;             /* >= 1 */
+  int32_t dtype;                 /* pa_dtype */
+} pa_append_args;
+
+/* Scatter the rows of `key` and `value` into the page pool.
+ * PA_ERR_INVALID_ARG: a NULL or misaligned pointer, a size out of range, or a
+ * pool of 2^31 slots or more; PA_ERR_UNSUPPORTED: head_dim or dtype. */
+pa_status pa_append(const pa_append_args *args, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *pa_status_string(int32_t status);

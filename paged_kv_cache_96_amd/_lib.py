@@ -23,7 +23,7 @@ PA_MASK_NONE = 0
 PA_MASK_CAUSAL = 1
 
 EXPORTED = ("pa_decode_plan", "pa_decode", "pa_split_reduce", "pa_prefill_plan", "pa_prefill",
-            "pa_status_string", "pa_abi_version")
+            "pa_append", "pa_status_string", "pa_abi_version")
 
 
 class PaArgs(ctypes.Structure):
@@ -63,7 +63,23 @@ class PaWorkspace(ctypes.Structure):
     ]
 
 
-ABI_VERSION = 4  # PA_ABI_VERSION of the structs below
+class PaAppendArgs(ctypes.Structure):
+    _fields_ = [
+        ("key", ctypes.c_void_p),
+        ("value", ctypes.c_void_p),
+        ("slot_mapping", ctypes.c_void_p),
+        ("key_pages", ctypes.c_void_p),
+        ("value_pages", ctypes.c_void_p),
+        ("num_tokens", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+ABI_VERSION = 5  # PA_ABI_VERSION of the structs below
 
 SCHEDULE_PARTITIONS = 0
 SCHEDULE_BALANCED = 1
@@ -99,6 +115,8 @@ def lib() -> ctypes.CDLL:
     L.pa_prefill_plan.restype = ctypes.c_int
     L.pa_prefill.argtypes = [A, W, ctypes.c_void_p]
     L.pa_prefill.restype = ctypes.c_int
+    L.pa_append.argtypes = [ctypes.POINTER(PaAppendArgs), ctypes.c_void_p]
+    L.pa_append.restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int32]
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_abi_version.argtypes = []

@@ -234,3 +234,27 @@ def paged_attention(query: torch.Tensor, key_pages: torch.Tensor, value_pages: t
         pa_prefill(args, ws, stream)
         out._pa_workspace = ws
     return out
+
+
+def pa_append(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,
+              key_pages: torch.Tensor, value_pages: torch.Tensor, stream=None) -> None:
+    """K/V write path: the rows key[t], value[t] ([T, H_kv, D]) go to slot
+    slot_mapping[t] (int32: page * page_size + offset; negative or past the
+    pool: skipped) of key_pages / value_pages ([P, H_kv, page_size, D])."""
+    T, Hkv, D = key.shape
+    P, Hkv2, ps, D2 = key_pages.shape
+    if tuple(value.shape) != tuple(key.shape) or tuple(value_pages.shape) != tuple(key_pages.shape):
+        raise ValueError("key / value or key_pages / value_pages shapes disagree")
+    if Hkv2 != Hkv or D2 != D:
+        raise ValueError("token rows and pages disagree in kv heads or head size")
+    if not (key.dtype == value.dtype == key_pages.dtype == value_pages.dtype):
+        raise ValueError("tokens and pages must share one dtype")
+    _int32(slot_mapping, "slot_mapping")
+    if tuple(slot_mapping.shape) != (T,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    a = _lib.PaAppendArgs()
+    a.key, a.value, a.slot_mapping = _ptr(key), _ptr(value), _ptr(slot_mapping)
+    a.key_pages, a.value_pages = _ptr(key_pages), _ptr(value_pages)
+    a.num_tokens, a.num_kv_heads, a.head_dim, a.num_pages, a.page_size = T, Hkv, D, P, ps
+    a.dtype = _DTYPES.get(key.dtype, 99)
+    _lib.check("pa_append", _lib.lib().pa_append(ctypes.byref(a), _stream(stream)))

@@ -317,3 +317,32 @@ PA_EXPORT pa_status pa_prefill(const pa_args *args, const pa_workspace *ws, void
   if ((st = check_decode_grid(args, 1)) != PA_OK) return st;
   return hip_status(pa::launch_decode(p, (pa::DType)args->dtype, (hipStream_t)stream));
 }
+
+PA_EXPORT pa_status pa_append(const pa_append_args *args, void *stream) {
+  if (!args) return PA_ERR_INVALID_ARG;
+  const pa_append_args *a = args;
+  if (a->num_tokens < 0 || a->num_kv_heads < 1 || a->head_dim < 1 || a->num_pages < 1 ||
+      a->page_size < 1)
+    return PA_ERR_INVALID_ARG;
+  if ((int64_t)a->num_pages * a->page_size > INT32_MAX) return PA_ERR_INVALID_ARG;
+  if (a->dtype != PA_DTYPE_F32 && a->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (a->head_dim != 64 && a->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (!a->key_pages || !a->value_pages || !aligned16(a->key_pages) ||
+      !aligned16(a->value_pages))
+    return PA_ERR_INVALID_ARG;
+  if (a->num_tokens == 0) return PA_OK;
+  if (!a->key || !a->value || !a->slot_mapping || !aligned16(a->key) || !aligned16(a->value))
+    return PA_ERR_INVALID_ARG;
+  pa::AppendParams p{};
+  p.k = a->key;
+  p.v = a->value;
+  p.slots = a->slot_mapping;
+  p.kp = a->key_pages;
+  p.vp = a->value_pages;
+  p.tokens = a->num_tokens;
+  p.Hkv = a->num_kv_heads;
+  p.ps = a->page_size;
+  p.num_slots = a->num_pages * a->page_size;
+  p.row_bytes = a->head_dim * (a->dtype == PA_DTYPE_F32 ? 4 : 2);
+  return hip_status(pa::launch_append(p, (hipStream_t)stream));
+}

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 from paged_kv_cache_96_amd import _lib
-from paged_kv_cache_96_amd._lib import (PaArgs, PaWorkspace, SCHEDULE_BALANCED,
+from paged_kv_cache_96_amd._lib import (PaAppendArgs, PaArgs, PaWorkspace, SCHEDULE_BALANCED,
                                         SCHEDULE_KEY_SPLIT, SCHEDULE_PARTITIONS)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -41,7 +41,7 @@ def test_header_and_library_exports_agree(L):
     assert exported == declared
     for name in declared:
         assert hasattr(L, name)
-    assert L.pa_abi_version() == 4
+    assert L.pa_abi_version() == 5
 
 
 def test_status_strings(L):
@@ -231,3 +231,37 @@ def test_prefill_workspace_validation(L):
     # an empty workspace (num_splits 0) is the unsplit call; batch 0 is a no-op
     w = PaWorkspace()
     assert L.pa_prefill(ctypes.byref(h.args(batch=0)), ctypes.byref(ws), None) == 0
+
+
+def _append_args(h, **kw):
+    a = PaAppendArgs()
+    for f in ("key", "value", "slot_mapping", "key_pages", "value_pages"):
+        setattr(a, f, h.p)
+    a.num_tokens, a.num_kv_heads, a.head_dim, a.num_pages, a.page_size, a.dtype = 8, 2, 128, 16, 16, 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("key", None, -1), ("value", None, -1), ("slot_mapping", None, -1), ("key_pages", None, -1),
+    ("value_pages", None, -1), ("num_tokens", -1, -1), ("num_kv_heads", 0, -1),
+    ("num_pages", 0, -1), ("page_size", 0, -1), ("num_pages", 1 << 20, -1),
+    ("head_dim", 96, -2), ("head_dim", 0, -1), ("dtype", 2, -2)])
+def test_append_rejects_bad_arguments(L, field, value, code):
+    h = HostBuffers()
+    a = _append_args(h, **{field: value})
+    if field == "num_pages" and value == 1 << 20:
+        a.page_size = 4096  # 2^32 slots: past int32
+    assert L.pa_append(ctypes.byref(a), None) == code
+
+
+def test_append_alignment_and_empty_call(L):
+    h = HostBuffers()
+    for f in ("key", "value", "key_pages", "value_pages"):
+        assert L.pa_append(ctypes.byref(_append_args(h, **{f: h.p + 4})), None) == -1
+    # no tokens: nothing to do (token pointers unused), but the pool is still checked
+    a = _append_args(h, num_tokens=0, key=None, value=None, slot_mapping=None)
+    assert L.pa_append(ctypes.byref(a), None) == 0
+    assert L.pa_append(ctypes.byref(_append_args(h, num_tokens=0, key_pages=None)), None) == -1
+    assert L.pa_append(None, None) == -1

@@ -409,3 +409,70 @@ def make_config(name: str, seed: Optional[int] = None):
     """Build one of the five named workloads (C5 returns a MixedInputs)."""
     fn = BUILDERS[name]
     return fn() if seed is None else fn(seed)
+
+
+# ----------------------------------------------------------------------------
+# write path: new tokens appended after each request's cached context
+# ----------------------------------------------------------------------------
+
+@dataclass
+class AppendInputs:
+    """One step's K/V write: ``n_new[b]`` tokens of request b land at
+    positions ctx_old[b] .. ctx_old[b] + n_new[b] - 1 of its block table
+    (``paged`` covers the grown contexts; its pool holds the old tokens and
+    garbage elsewhere).  Token rows are request-major; ``pad_tokens`` extra
+    rows with slot -1 are spread among them (padding the runtime may send)."""
+
+    name: str
+    seed: int
+    paged: PagedInputs
+    ctx_old: np.ndarray             # [B] int32
+    n_new: np.ndarray               # [B] int32
+    key: np.ndarray                 # [T, H_kv, D] float32 or uint16 (bf16 bits)
+    value: np.ndarray               # [T, H_kv, D]
+    slot_mapping: np.ndarray        # [T] int32: page * page_size + offset, or -1
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.slot_mapping.shape[0])
+
+    def moved_bytes(self) -> int:
+        """Bytes an append reads plus writes for the tokens with a slot."""
+        p = self.paged
+        live = int((self.slot_mapping >= 0).sum())
+        return live * p.H_kv * p.D * (4 if p.dtype == "f32" else 2) * 2 * 2
+
+
+def make_append(seed: int, *, B: int, H_kv: int, D: int, page_size: int,
+                ctx_old: Union[Sequence[int], tuple], n_new: Union[Sequence[int], tuple],
+                dtype: str = "bf16", pad_tokens: int = 0, extra_free_pages: int = 3,
+                garbage=GARBAGE_DEFAULT, name: str = "append") -> AppendInputs:
+    """Random write-path inputs.  Draw order: the paged pool of the grown
+    contexts (make_random with this seed) -> old context lengths (when a
+    range) -> new-token counts (when a range) -> pad positions -> K rows ->
+    V rows, from a child stream of the seed."""
+    rng = np.random.default_rng([seed, 1])
+    old = ([int(v) for v in rng.integers(ctx_old[0], ctx_old[1] + 1, size=B)]
+           if isinstance(ctx_old, tuple) else [int(v) for v in ctx_old])
+    new = ([int(v) for v in rng.integers(n_new[0], n_new[1] + 1, size=B)]
+           if isinstance(n_new, tuple) else [int(v) for v in n_new])
+    assert len(old) == B and len(new) == B
+    grown = [o + n for o, n in zip(old, new)]
+    paged = make_random(seed, B=B, H_q=H_kv, H_kv=H_kv, L=1, D=D, page_size=page_size,
+                        ctx=grown, dtype=dtype, causal=False,
+                        extra_free_pages=extra_free_pages, garbage=garbage, name=name)
+    slots = []
+    bt = paged.block_table
+    for b in range(B):
+        for pos in range(old[b], grown[b]):
+            slots.append(int(bt[b, pos // page_size]) * page_size + pos % page_size)
+    T = len(slots) + pad_tokens
+    pad_at = set(int(i) for i in rng.choice(T, size=pad_tokens, replace=False)) if pad_tokens else set()
+    it = iter(slots)
+    slot_mapping = np.array([-1 if t in pad_at else next(it) for t in range(T)], dtype=np.int32)
+    key = _draw_values(rng, (T, H_kv, D), dtype)
+    value = _draw_values(rng, (T, H_kv, D), dtype)
+    return AppendInputs(name=name, seed=seed, paged=paged,
+                        ctx_old=np.asarray(old, dtype=np.int32),
+                        n_new=np.asarray(new, dtype=np.int32), key=key, value=value,
+                        slot_mapping=slot_mapping)
