@@ -359,6 +359,24 @@ def main():
             "prefill_flops": fl, "prefill_tflops": round(fl / pm / 1e9, 2), "prefill_mean_ms": pm,
             "combined_ms": round(sm + pm, 5)}
         del dd, dp, rd, rp
+    if "threshold" in only:
+        # decode vs prefill around the router's threshold (not in the default
+        # run): 64 requests, ctx U[128,4096], H 32/8, D 128, bf16
+        th = []
+        for L in (1, 2, 4, 8, 16, 32):
+            xt = W.make_random(700 + L, B=64, H_q=32, H_kv=8, L=L, D=128, page_size=16,
+                               ctx=(128, 4096), dtype="bf16", causal=True, extra_free_pages=64)
+            dt = run.to_device(xt)
+            row = {"L": L, "rows_per_kv_head": 4 * L}
+            if L <= 8:
+                row["decode_step_us"] = round(float(np.mean(
+                    run.time_decode(dt, 20, 3)["step_ms"])) * 1e3, 2)
+            row["prefill_us"] = round(float(np.mean(
+                run.time_prefill(dt, 20, 3, flush=True)["ms"])) * 1e3, 2)
+            log(f"[bench] threshold L={L}: {row}")
+            th.append(row)
+            del dt, xt
+        sections["route_threshold"] = th
     if "append" in only:
         # the K/V write that precedes attention (pa_append), timed on its own
         wr = []

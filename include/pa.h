@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 5
+#define PA_ABI_VERSION 6
 
 typedef enum {
   PA_OK = 0,
@@ -210,6 +210,32 @@ pa_status pa_prefill_plan(const pa_args *args, int32_t num_cus, pa_workspace *pl
  * (wrong schedule, fewer than 2 slots or counters than slots, missing
  * buffers or counters, misaligned). */
 pa_status pa_prefill(const pa_args *args, const pa_workspace *ws, void *stream);
+
+/* ------------------------------------------------------------------ router
+ * One call for any query length: the shape decision sits at the boundary
+ * (tiny-llm "Week 3 Day 4", "Choose a Schedule for Each Query Shape": one
+ * tile shape cannot serve decode and prefill well, and the choice belongs in
+ * the extension's dispatch).  The decode kernel holds the G * L query rows of
+ * a kv head in one row block of at most 8 rows and reads every K/V byte once
+ * per row block; the prefill kernel reads K/V once per 128-row tile.  So
+ * pa_attention runs the decode path when G * L <= 8 (G = H_q / H_kv) and
+ * the prefill path otherwise.  Measured on MI355X with 64 requests of
+ * U[128, 4096] keys, H_q 32, H_kv 8, D 128, bf16: L = 1 decode 125 us vs
+ * prefill 191 us; L = 2 149 vs 171; L = 4 298 vs 195; L = 8 627 vs 195. */
+typedef enum { PA_ROUTE_DECODE = 0, PA_ROUTE_PREFILL = 1 } pa_route;
+
+/* The plan of pa_attention: *route (if not NULL) receives the path, and
+ * `plan` / *workspace_bytes are those of pa_decode_plan (decode route;
+ * plan->partition_tokens on input as there) or pa_prefill_plan. */
+pa_status pa_attention_plan(const pa_args *args, int32_t num_cus, pa_workspace *plan,
+                            size_t *workspace_bytes, int32_t *route);
+
+/* Attention for any L >= 1 on the route of pa_attention_plan, with that
+ * plan's workspace (or NULL where the route allows it): the decode route
+ * runs pa_decode and, when its pieces are not merged in the kernel (a split
+ * without arrival counters), pa_split_reduce; the prefill route runs
+ * pa_prefill.  Errors as for those calls. */
+pa_status pa_attention(const pa_args *args, const pa_workspace *ws, void *stream);
 
 /* ---------------------------------------------------------------- write path
  * The K/V write that precedes attention on every step: each new token's key

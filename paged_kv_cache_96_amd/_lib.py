@@ -23,7 +23,8 @@ PA_MASK_NONE = 0
 PA_MASK_CAUSAL = 1
 
 EXPORTED = ("pa_decode_plan", "pa_decode", "pa_split_reduce", "pa_prefill_plan", "pa_prefill",
-            "pa_append", "pa_status_string", "pa_abi_version")
+            "pa_attention_plan", "pa_attention", "pa_append", "pa_status_string",
+            "pa_abi_version")
 
 
 class PaArgs(ctypes.Structure):
@@ -79,7 +80,10 @@ class PaAppendArgs(ctypes.Structure):
     ]
 
 
-ABI_VERSION = 5  # PA_ABI_VERSION of the structs below
+ABI_VERSION = 6  # PA_ABI_VERSION of the structs below
+
+ROUTE_DECODE = 0
+ROUTE_PREFILL = 1
 
 SCHEDULE_PARTITIONS = 0
 SCHEDULE_BALANCED = 1
@@ -115,6 +119,11 @@ def lib() -> ctypes.CDLL:
     L.pa_prefill_plan.restype = ctypes.c_int
     L.pa_prefill.argtypes = [A, W, ctypes.c_void_p]
     L.pa_prefill.restype = ctypes.c_int
+    L.pa_attention_plan.argtypes = [A, ctypes.c_int32, W, ctypes.POINTER(ctypes.c_size_t),
+                                    ctypes.POINTER(ctypes.c_int32)]
+    L.pa_attention_plan.restype = ctypes.c_int
+    L.pa_attention.argtypes = [A, W, ctypes.c_void_p]
+    L.pa_attention.restype = ctypes.c_int
     L.pa_append.argtypes = [ctypes.POINTER(PaAppendArgs), ctypes.c_void_p]
     L.pa_append.restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int32]

@@ -212,27 +212,59 @@ def pa_prefill(args: PaArgs, workspace: Optional[PrefillWorkspace] = None, strea
     _lib.check("pa_prefill", _lib.lib().pa_prefill(ctypes.byref(args), ws, _stream(stream)))
 
 
+class AttentionPlan(NamedTuple):
+    """pa_attention_plan's choice: the route (ROUTE_DECODE or ROUTE_PREFILL)
+    and the plan of that route's path."""
+    route: int
+    plan: object  # DecodePlan or PrefillPlan
+
+
+def pa_attention_plan(args: PaArgs, *, num_cus: int = 0,
+                      partition_tokens: int = 0) -> AttentionPlan:
+    ws = PaWorkspace()
+    ws.partition_tokens = int(partition_tokens)
+    nbytes = ctypes.c_size_t(0)
+    route = ctypes.c_int32(-1)
+    _lib.check("pa_attention_plan", _lib.lib().pa_attention_plan(
+        ctypes.byref(args), int(num_cus), ctypes.byref(ws), ctypes.byref(nbytes),
+        ctypes.byref(route)))
+    if route.value == _lib.ROUTE_DECODE:
+        plan = DecodePlan(ws.num_splits, ws.partition_tokens, nbytes.value, ws.schedule,
+                          ws.num_counters)
+    else:
+        plan = PrefillPlan(ws.num_splits, nbytes.value, ws.num_counters)
+    return AttentionPlan(route.value, plan)
+
+
+def attention_workspace(ap: AttentionPlan, args: PaArgs, query: torch.Tensor):
+    """Device buffers for an AttentionPlan (decode: with arrival counters, so
+    the merge runs inside pa_decode)."""
+    if ap.route == _lib.ROUTE_DECODE:
+        return Workspace.for_plan(ap.plan, query, fused=True)
+    return PrefillWorkspace(ap.plan, args.head_dim, query.device)
+
+
+def pa_attention(args: PaArgs, workspace=None, stream=None) -> None:
+    ws = ctypes.byref(workspace.c) if workspace is not None else None
+    _lib.check("pa_attention", _lib.lib().pa_attention(ctypes.byref(args), ws, _stream(stream)))
+
+
 def paged_attention(query: torch.Tensor, key_pages: torch.Tensor, value_pages: torch.Tensor,
                     block_table: torch.Tensor, context_lens: torch.Tensor, *,
                     scale: Optional[float] = None, mask: Optional[str] = "causal",
                     query_lens: Optional[torch.Tensor] = None, partition_tokens: int = 0,
                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Convenience call: decode (+ merge) for L <= 8, prefill otherwise."""
+    """Convenience call through the library's router (pa_attention): the
+    decode path when the query rows of one kv head fit a decode row block,
+    the prefill path otherwise."""
     if out is None:
         out = torch.empty_like(query)
     args = make_args(query, key_pages, value_pages, block_table, context_lens, out, scale=scale,
                      mask=mask, query_lens=query_lens)
-    if query.shape[2] <= 8:
-        plan = pa_decode_plan(args, partition_tokens=partition_tokens)
-        ws = Workspace.for_plan(plan, query)
-        pa_decode(args, ws, stream)
-        if plan.num_splits > 1:
-            pa_split_reduce(args, ws, stream)
-        out._pa_workspace = ws  # keep the buffers alive until the caller is done
-    else:
-        ws = PrefillWorkspace.for_args(args, query.device)
-        pa_prefill(args, ws, stream)
-        out._pa_workspace = ws
+    ap = pa_attention_plan(args, partition_tokens=partition_tokens)
+    ws = attention_workspace(ap, args, query)
+    pa_attention(args, ws, stream)
+    out._pa_workspace = ws  # keep the buffers alive until the caller is done
     return out
 
 

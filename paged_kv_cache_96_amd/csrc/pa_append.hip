@@ -9,7 +9,7 @@
 // The slot of a token is read by the LANES threads of each of its rows (one
 // cached load).  Tokens with a negative or out-of-pool slot are skipped.
 // HBM bound: every byte is read once and written once.
-#include "pa_internal.h"
+#include "pa_write.h"
 
 namespace pa {
 namespace {

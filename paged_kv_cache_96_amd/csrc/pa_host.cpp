@@ -9,6 +9,7 @@
 
 #include "pa.h"
 #include "pa_internal.h"
+#include "pa_write.h"
 
 #define PA_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -316,6 +317,38 @@ PA_EXPORT pa_status pa_prefill(const pa_args *args, const pa_workspace *ws, void
   }
   if ((st = check_decode_grid(args, 1)) != PA_OK) return st;
   return hip_status(pa::launch_decode(p, (pa::DType)args->dtype, (hipStream_t)stream));
+}
+
+namespace {
+
+// pa_attention's route: decode when the query rows of one kv head fit one
+// decode row block (each K/V byte is then read once per kv head), else
+// prefill (K/V read once per 128-row tile).
+bool routes_to_decode(const pa_args *a) {
+  return (int64_t)(a->num_q_heads / a->num_kv_heads) * a->q_len <= 8;
+}
+
+}  // namespace
+
+PA_EXPORT pa_status pa_attention_plan(const pa_args *args, int32_t num_cus, pa_workspace *plan,
+                                      size_t *workspace_bytes, int32_t *route) {
+  pa_status st = check_sizes(args);
+  if (st != PA_OK) return st;
+  if (!plan) return PA_ERR_INVALID_ARG;
+  const bool dec = routes_to_decode(args);
+  if (route) *route = dec ? PA_ROUTE_DECODE : PA_ROUTE_PREFILL;
+  return dec ? pa_decode_plan(args, num_cus, plan, workspace_bytes)
+             : pa_prefill_plan(args, num_cus, plan, workspace_bytes);
+}
+
+PA_EXPORT pa_status pa_attention(const pa_args *args, const pa_workspace *ws, void *stream) {
+  pa_status st = check_sizes(args);
+  if (st != PA_OK) return st;
+  if (!routes_to_decode(args)) return pa_prefill(args, ws, stream);
+  if ((st = pa_decode(args, ws, stream)) != PA_OK) return st;
+  const bool merged = ws && ws->schedule == PA_SCHEDULE_BALANCED && ws->counters;
+  if (ws && ws->num_splits > 1 && !merged) return pa_split_reduce(args, ws, stream);
+  return PA_OK;
 }
 
 PA_EXPORT pa_status pa_append(const pa_append_args *args, void *stream) {

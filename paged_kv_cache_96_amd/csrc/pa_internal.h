@@ -41,21 +41,6 @@ hipError_t launch_split_reduce(const LaunchParams &p, DType dt, hipStream_t stre
 // bf16 MFMA prefill kernel.
 hipError_t launch_prefill_mfma(const LaunchParams &p, hipStream_t stream);
 
-// K/V write path: scatter of token rows to page-pool slots (pa_append).
-struct AppendParams {
-  const void *k;
-  const void *v;
-  const int32_t *slots;
-  void *kp;
-  void *vp;
-  int32_t tokens;
-  int32_t Hkv;
-  int32_t ps;
-  int32_t num_slots;     // num_pages * page_size (< 2^31)
-  int32_t row_bytes;     // head_dim * element bytes: 128, 256 or 512
-};
-hipError_t launch_append(const AppendParams &p, hipStream_t stream);
-
 // Largest batch the balanced decode schedule supports (its per-request
 // prefix sums live in LDS); larger batches use the partition schedule.
 constexpr int kBalancedMaxBatch = 2048;

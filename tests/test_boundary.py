@@ -41,7 +41,7 @@ def test_header_and_library_exports_agree(L):
     assert exported == declared
     for name in declared:
         assert hasattr(L, name)
-    assert L.pa_abi_version() == 5
+    assert L.pa_abi_version() == 6
 
 
 def test_status_strings(L):
@@ -265,3 +265,47 @@ def test_append_alignment_and_empty_call(L):
     assert L.pa_append(ctypes.byref(a), None) == 0
     assert L.pa_append(ctypes.byref(_append_args(h, num_tokens=0, key_pages=None)), None) == -1
     assert L.pa_append(None, None) == -1
+
+
+def _attention_plan(L, a, P=0):
+    ws = PaWorkspace()
+    ws.partition_tokens = P
+    nb = ctypes.c_size_t(0)
+    route = ctypes.c_int32(-1)
+    rc = L.pa_attention_plan(ctypes.byref(a), 0, ctypes.byref(ws), ctypes.byref(nb),
+                             ctypes.byref(route))
+    return rc, route.value, (ws.schedule, ws.num_splits, ws.partition_tokens, ws.num_counters,
+                             nb.value)
+
+
+@pytest.mark.parametrize("Hq,Hkv,Lq,route", [
+    (32, 8, 1, 0), (32, 8, 2, 0), (32, 8, 4, 1), (8, 8, 8, 0), (8, 8, 9, 1), (64, 8, 2, 1),
+    (28, 4, 512, 1), (4, 4, 1, 0)])
+def test_attention_router_picks_by_rows_per_kv_head(L, Hq, Hkv, Lq, route):
+    # decode when G * L query rows fit one decode row block (<= 8), else prefill
+    h = HostBuffers()
+    a = h.args(batch=8, num_q_heads=Hq, num_kv_heads=Hkv, q_len=Lq, max_pages=64, num_pages=600)
+    rc, r, plan = _attention_plan(L, a)
+    assert (rc, r) == (0, route)
+    same = _plan(L, a, full=True) if route == 0 else _prefill_plan(L, a)
+    if route == 0:
+        assert (plan[0], plan[1], plan[2], plan[4], plan[3]) == (same[4], same[1], same[2], same[3],
+                                                                 same[5])
+    else:
+        assert (plan[0], plan[1], plan[3], plan[4]) == same[1:]
+    # an explicit partition size reaches the decode plan
+    if route == 0:
+        rc, r, plan = _attention_plan(L, a, P=64)
+        assert rc == 0 and plan[0] == SCHEDULE_PARTITIONS and plan[2] == 64
+
+
+def test_attention_router_validates(L):
+    h = HostBuffers()
+    assert L.pa_attention(ctypes.byref(h.args(num_q_heads=7)), None, None) == -1
+    assert L.pa_attention(ctypes.byref(h.args(head_dim=96)), None, None) == -2
+    assert L.pa_attention(ctypes.byref(h.args(batch=0)), None, None) == 0
+    assert L.pa_attention(ctypes.byref(h.args(query=None)), None, None) == -1
+    assert L.pa_attention(ctypes.byref(h.args(q_len=64, query=None)), None, None) == -1
+    ws = PaWorkspace()
+    assert L.pa_attention_plan(ctypes.byref(h.args()), 0, None, None, None) == -1
+    assert L.pa_attention_plan(ctypes.byref(h.args()), 0, ctypes.byref(ws), None, None) == 0
