@@ -35,6 +35,11 @@ CASES = [
     (8, "f32", 128, 8, 2, 40, 16, [40, 300], True, None),
     (9, "f32", 64, 4, 4, 12, 3, [12, 13, 40], False, [12, 5, 0]),
     (10, "bf16", 128, 16, 2, 300, 24, [300, 1000], True, None),
+    # page sizes that are multiples of 16: D 64 stages through registers,
+    # D 128 loads straight into LDS (32-key tiles over 48- and 32-key pages)
+    (11, "bf16", 64, 8, 2, 100, 16, [100, 700], True, None),
+    (12, "bf16", 128, 16, 4, 200, 48, [200, 1500, 3001], True, [200, 150, 7]),
+    (13, "bf16", 128, 12, 3, 65, 32, [65, 66, 2000], True, None),
 ]
 
 
