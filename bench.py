@@ -234,6 +234,8 @@ def main():
     ap.add_argument("--only", default="C2,C3,C4,C5,long,append")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="skip the unflushed C2 decode steps (profiling runs)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3 times): the known "
@@ -296,7 +298,7 @@ def main():
         "wall_s_timed_region": round(r2["wall_s"], 4),
     }
     del r2
-    if not args.no_flush:
+    if not args.no_flush and not args.no_warm:
         # the same steps without the cache flush between them (K/V partly in
         # the 256 MB last-level cache): context only, never `value`
         rw = Runner(torch, api, flush=False).time_decode(d2, args.steps, args.warmup,

@@ -544,7 +544,8 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
     if (b < B) {
       const int ctx = p.cl[b];
       s_ctx[b] = ctx;
-      loc += (long long)U * ((ctx + kStep - 1) / kStep);
+      const int n = (ctx + kStep - 1) / kStep;
+      loc += (long long)U * (n > 0 ? n + kUnitSetupSteps : 0);
     }
   }
   s_sum[tid] = loc;
@@ -561,7 +562,7 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
     if (b < B) {
       const int n = (s_ctx[b] + kStep - 1) / kStep;
       s_R[b] = run;
-      run += (long long)U * n;
+      run += (long long)U * (n > 0 ? n + kUnitSetupSteps : 0);
     }
   }
   if (tid == 255) s_R[B] = s_sum[255];
@@ -595,6 +596,8 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
 
   // The steps of virtual wave v (its static run, or dynamic chunk v - Wa),
   // piece by piece: a piece is the part of one row block inside the run.
+  // Positions of the step order: each row block with keys is kUnitSetupSteps
+  // setup positions (no work) followed by its n steps.
   auto run_segment = [&](long long v) {
     long long t = bs.begin(v);
     const long long e = bs.begin(v + 1);
@@ -606,13 +609,18 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
       }
       const int b = uni(lo);
       const int ctx = uni(s_ctx[b]);
-      const long long n = (ctx + kStep - 1) / kStep;  // > 0: request b holds step t
+      const long long n = (ctx + kStep - 1) / kStep;  // > 0: request b holds position t
+      const long long nu = n + kUnitSetupSteps;       // positions per row block
       const long long Rb = uni64(s_R[b]);
       const long long rel = t - Rb;
-      const int u = (int)(rel / n);
-      const long long j0 = rel - (long long)u * n;
+      const int u = (int)(rel / nu);
+      const long long row0 = Rb + (long long)u * nu + kUnitSetupSteps;  // first step
+      if (t < row0) {  // inside the setup positions: the row block starts at row0
+        t = row0;
+        continue;
+      }
+      const long long j0 = t - row0;
       const long long j1 = min(n, j0 + (e - t));
-      const long long row0 = Rb + (long long)u * n;
       const long long w0 = bs.wave_of(row0);
       const long long w1 = bs.wave_of(row0 + n - 1);
       const int g = u / row_blocks;

@@ -69,7 +69,7 @@ int64_t decode_units(const pa_args *a) {
 int64_t balanced_max_steps(const pa_args *a) {
   const int64_t step = pa::decode_step_keys(a->head_dim, elem_bytes(a));
   const int64_t cap = (int64_t)a->max_pages * a->page_size;
-  return (int64_t)a->batch * decode_units(a) * ((cap + step - 1) / step);
+  return (int64_t)a->batch * decode_units(a) * ((cap + step - 1) / step + pa::kUnitSetupSteps);
 }
 
 // Workspace consistency for a decode/merge pair.  A single partition needs

@@ -49,6 +49,13 @@ constexpr int kBalancedMaxBatch = 2048;
 constexpr int64_t kBalancedMaxSteps = int64_t(1) << 40;
 // Shortest run of steps a balanced schedule hands to one wave.
 constexpr int kBalancedMinSteps = 4;
+// Setup cost of a row block in the balanced schedule, in steps: a wave that
+// starts a new row block inside its run pays the previous piece's write and
+// arrival and the new piece's block-table, query and first K/V latencies
+// (measured ~6-7 us, ~5 steps of 1.25 us, on C2-like calls).  Every row
+// block with keys is laid out as kUnitSetupSteps setup positions followed
+// by its steps, so runs are equal in cost rather than in steps.
+constexpr int kUnitSetupSteps = 5;
 
 // Largest number of (request, tile) pairs the key split of the bf16 prefill
 // plans over (the plan's tables live in the kernel's staging buffers);

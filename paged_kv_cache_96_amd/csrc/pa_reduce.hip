@@ -30,7 +30,8 @@ __device__ void balanced_waves(const LaunchParams &p, int b, int u, int units, l
   const int lane = threadIdx.x & 63;
   long long tot = 0, before = 0;
   for (int c = lane; c < p.B; c += 64) {
-    const long long steps = (long long)units * ((p.cl[c] + kStep - 1) / kStep);
+    const long long n = (p.cl[c] + kStep - 1) / kStep;
+    const long long steps = (long long)units * (n > 0 ? n + kUnitSetupSteps : 0);
     tot += steps;
     if (c < b) before += steps;
   }
@@ -41,7 +42,7 @@ __device__ void balanced_waves(const LaunchParams &p, int b, int u, int units, l
   count = 0;
   if (n == 0) return;
   const BalancedSplit bs = balanced_split(p.grid_waves, tot, (long long)p.B * units, p.num_splits);
-  const long long row0 = before + (long long)u * n;
+  const long long row0 = before + (long long)u * (n + kUnitSetupSteps) + kUnitSetupSteps;
   w0 = bs.wave_of(row0);
   count = (int)(bs.wave_of(row0 + n - 1) - w0 + 1);
 }
