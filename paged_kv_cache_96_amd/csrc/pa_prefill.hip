@@ -16,8 +16,8 @@
 //      page: its block-table entry is a scalar load (SGPR) and the run is
 //      read with buffer loads from that page at per-lane offsets fixed for
 //      the whole walk, so staging costs no per-lane address arithmetic.
-//      With D = 128 and a pool under 2 GiB the loads write LDS directly
-//      (kStageDma): 32-key tiles, wave w loads keys 8w .. 8w + 7 of the next
+//      With D = 128 the loads write LDS directly (kStageDma; kStageDmaRun
+//      for pools of 2 GiB and more, with one buffer resource per run): 32-key tiles, wave w loads keys 8w .. 8w + 7 of the next
 //      tile into the other buffer once the current tile's scores are
 //      computed; no staging registers and no LDS stores, so a workgroup
 //      needs 33 KiB of LDS and fits three waves per SIMD (the launch
@@ -323,7 +323,9 @@ __device__ void find_piece(const LaunchParams &p, int nt, int *s_ctx, int *s_ql,
 // always out of range).
 // kStageDma: the runs of kStagePool with the K/V rows written straight into
 // LDS by the loads (no staging registers, no LDS stores): D = 128 only.
-enum StageMode { kStageLanes = 0, kStageRun = 1, kStagePool = 2, kStageDma = 3 };
+// kStageDmaRun: the same with one buffer resource per run (pools of 2 GiB
+// and more, as kStageRun).
+enum StageMode { kStageLanes = 0, kStageRun = 1, kStagePool = 2, kStageDma = 3, kStageDmaRun = 4 };
 
 // LDS tile layout of kStageDma (64 rows x 16 chunks of 16 bytes, D = 128).
 // Rows come in blocks of 4 (b = (r / 4) % 4 within a 16-row group); a block
@@ -346,10 +348,12 @@ __device__ __forceinline__ int dma_pos(int r, int c) {
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <int D, bool DEBUG, int MODE, int RB>
-__global__ __launch_bounds__(256, MODE == kStageDma ? 3 : RB == 1 ? 2 : 1) void prefill_kernel(
-    LaunchParams p, int num_tiles) {
+__global__ __launch_bounds__(256, (MODE == kStageDma || MODE == kStageDmaRun) ? 3
+                                  : RB == 1                                ? 2
+                                                                           : 1) void
+prefill_kernel(LaunchParams p, int num_tiles) {
   constexpr bool UNIFORM = MODE != kStageLanes;
-  constexpr bool DMA = MODE == kStageDma;
+  constexpr bool DMA = MODE == kStageDma || MODE == kStageDmaRun;
   // keys per tile: DMA staging walks tiles of 32 keys (two 16 KiB buffers,
   // three workgroups per compute unit); the split plan's 64-key grid is a
   // multiple of it
@@ -513,13 +517,27 @@ __global__ __launch_bounds__(256, MODE == kStageDma ? 3 : RB == 1 ? 2 : 1) void 
     const int run0 = T * BN + kDmaRows * wave;  // first key of this wave's run
     const bool live = run0 < kend_wg;           // wave-uniform
     const int page = live ? btc[min(dma_lp, p.max_pages - 1)] : 0;
-    const int soff = page * (int)page_bytes + (int)head_bytes + dma_slot * (D * 2);
+    // pool-wide resources with the run in the scalar offset, or (pools of
+    // 2 GiB and more) resources of the run itself, empty past the last key
+    __amdgpu_buffer_rsrc_t rk = pool_k, rv = pool_v;
+    int soff = 0;
+    if constexpr (MODE == kStageDmaRun) {
+      const long long off =
+          (long long)page * page_bytes + head_bytes + (long long)dma_slot * (D * 2);
+      const int nrec = live ? kDmaRows * D * 2 : 0;
+      rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kp_bytes + off), (short)0, nrec,
+                                             kBufferRsrcWord3);
+      rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vp_bytes + off), (short)0, nrec,
+                                             kBufferRsrcWord3);
+    } else {
+      soff = page * (int)page_bytes + (int)head_bytes + dma_slot * (D * 2);
+    }
     auto load = [&](int j, int voff) {
       const int dst = (kDmaBlocks * wave + j) * 512;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_k, (lds_void_t *)(kdst + dst), 16, voff, soff,
-                                               0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_v, (lds_void_t *)(vdst + dst), 16, voff, soff,
-                                               0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t *)(kdst + dst), 16, voff, soff, 0,
+                                               0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t *)(vdst + dst), 16, voff, soff, 0,
+                                               0);
     };
     if (run0 + kDmaRows <= kend_wg) {  // wave-uniform: the whole run is live
 #pragma unroll
@@ -939,8 +957,12 @@ hipError_t launch_rb(const LaunchParams &p, hipStream_t stream) {
       hipLaunchKernelGGL((prefill_kernel<D, false, kStagePool, RB>), grid, dim3(256), 0, stream,
                          p, tiles);
   } else {
-    hipLaunchKernelGGL((prefill_kernel<D, false, kStageRun, RB>), grid, dim3(256), 0, stream, p,
-                       tiles);
+    if constexpr (D == 128 && RB == 1)
+      hipLaunchKernelGGL((prefill_kernel<D, false, kStageDmaRun, RB>), grid, dim3(256), 0, stream,
+                         p, tiles);
+    else
+      hipLaunchKernelGGL((prefill_kernel<D, false, kStageRun, RB>), grid, dim3(256), 0, stream, p,
+                         tiles);
   }
   return hipGetLastError();
 }
