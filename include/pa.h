@@ -115,9 +115,10 @@ typedef enum pa_schedule {
   PA_SCHEDULE_PARTITIONS = 0,
   /* Equal work per wave: the keys of every (request, kv head, row block),
    * in steps of STEP keys (16 for bf16 with head_dim 128; 4096 / (head_dim *
-   * element bytes) in general), are laid out request-major and cut into one
-   * contiguous run per wave of a grid that fills the GPU, so ragged context
-   * lengths cost no idle waves.  A row block is R query rows of one kv head
+   * element bytes) in general), each row block preceded by a few setup
+   * positions that stand for the cost of starting it, are laid out
+   * request-major and cut into one contiguous run per wave of a grid that
+   * fills the GPU, so ragged context lengths cost no idle waves.  A row block is R query rows of one kv head
    * (R = 1, 2, 4 or 8: the smallest that holds G * L, at most 8), and a
    * request has U = H_kv * ceil(G * L / R) of them.  Row block r of the call
    * (r = b * U + u) walked in part by wave w leaves its partial state in
