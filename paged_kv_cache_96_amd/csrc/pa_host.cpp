@@ -277,8 +277,8 @@ PA_EXPORT pa_status pa_prefill_plan(const pa_args *args, int32_t num_cus, pa_wor
   plan->num_counters = 0;
   if (workspace_bytes) *workspace_bytes = 0;
   if (!prefill_splits(args)) return PA_OK;  // runs unsplit: no workspace
-  // two workgroups per compute unit are resident; the split aims at half
-  // the slots and uses at most all of them
+  // four piece slots per compute unit: the split sizes its pieces from the
+  // slot count and launches at most half as many extra workgroups
   const int cus = num_cus > 0 ? num_cus : 256;
   plan->num_splits = 4 * cus;
   plan->num_counters = plan->num_splits;
