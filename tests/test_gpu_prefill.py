@@ -197,3 +197,25 @@ def test_decode_late_score_spike_is_exact(api):
     for kw in (dict(), dict(partition_tokens=64)):
         out, _ = run_decode(api, DeviceInputs(x), **kw)
         assert_parity(out, ref, "bf16", f"decode spike {kw}")
+
+
+@pytest.mark.parametrize("L", [4096, 16384])
+def test_long_prompt_prefill_sampled_rows(api, L):
+    """The long-prompt causal prefill exactly as it is timed (one request,
+    prefix 0, H 28/4, key-split workspace), checked on windows of query rows.
+    Rows [i0, i0 + k) of the call see the same keys as the call with those k
+    rows alone after a context of i0 + k tokens (bottom-right causal
+    alignment), which the oracle finishes in seconds."""
+    x = make_random(100 + L, B=1, H_q=28, H_kv=4, L=L, D=128, page_size=16, ctx=[L],
+                    dtype="bf16", causal=True, extra_free_pages=16)
+    print(f"[long L={L}] seed={x.seed}", flush=True)
+    out, ex = run_prefill(api, DeviceInputs(x))
+    assert not ex["counters"].any()
+    got = host_f64(out)
+    assert np.isfinite(got).all()
+    for i0, k in ((0, 8), (127, 5), (L // 2 - 3, 8), (L - 8, 8)):
+        sub = dataclasses.replace(x, L=k, query=np.ascontiguousarray(x.query[:, :, i0:i0 + k]),
+                                  context_lens=np.array([i0 + k], dtype=np.int32))
+        ref = oracle.attention_of(sub)
+        err = assert_parity(out[:, :, i0:i0 + k], ref, "bf16", f"L={L} rows {i0}..{i0 + k}")
+        print(f"[long L={L}] rows {i0}..{i0 + k} max abs err {err:.3e}", flush=True)
