@@ -1,0 +1,112 @@
+"""Properties of the host-only plan calls over random shapes (no GPU): every
+decode plan covers the whole key capacity with whole pages inside the grid
+limits, or hands every row block a piece slot; prefill and router plans follow
+their documented sizing.  The library is called through the C ABI."""
+import ctypes
+import os
+
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from paged_kv_cache_96_amd import _lib
+from paged_kv_cache_96_amd._lib import (PaArgs, PaWorkspace, SCHEDULE_BALANCED,
+                                        SCHEDULE_KEY_SPLIT, SCHEDULE_PARTITIONS)
+
+MAX_GRID_YZ = 65535
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        import paged_kv_cache_96_amd.build as b
+        b.build()
+    return _lib.lib()
+
+
+def _args(B, Hkv, G, Lq, D, dtype, ps, max_pages):
+    a = PaArgs()
+    a.batch, a.num_q_heads, a.num_kv_heads, a.q_len, a.head_dim = B, G * Hkv, Hkv, Lq, D
+    a.num_pages, a.page_size, a.max_pages = 1 << 20, ps, max_pages
+    a.dtype, a.mask, a.scale = dtype, 1, 0.1
+    return a
+
+
+def _rows_per_block(rows):
+    return 1 if rows <= 1 else 2 if rows <= 2 else 4 if rows <= 4 else 8
+
+
+shapes = dict(
+    B=st.integers(0, 5000), Hkv=st.sampled_from([1, 2, 4, 8]), G=st.integers(1, 8),
+    D=st.sampled_from([64, 128]), dtype=st.sampled_from([0, 1]),
+    ps=st.sampled_from([1, 3, 16, 24, 32, 128, 256]), max_pages=st.integers(1, 20000),
+    cus=st.sampled_from([0, 1, 7, 256, 304]))
+
+
+@settings(max_examples=300, deadline=None)
+@given(Lq=st.integers(1, 8), P_req=st.one_of(st.just(0), st.integers(1, 300000)), **shapes)
+def test_decode_plan_invariants(L, B, Hkv, G, Lq, D, dtype, ps, max_pages, cus, P_req):
+    a = _args(B, Hkv, G, Lq, D, dtype, ps, max_pages)
+    ws = PaWorkspace()
+    ws.partition_tokens = P_req
+    nb = ctypes.c_size_t(0)
+    rc = L.pa_decode_plan(ctypes.byref(a), cus, ctypes.byref(ws), ctypes.byref(nb))
+    assert rc == 0
+    cap = max_pages * ps
+    S, P = ws.num_splits, ws.partition_tokens
+    assert S >= 1
+    rows = G * Lq
+    rpb = _rows_per_block(min(rows, 8))
+    units = max(B, 1) * Hkv * -(-rows // rpb)
+    if ws.schedule == SCHEDULE_BALANCED:
+        # only without an explicit size, for batches up to 2048: a piece slot
+        # per row block plus one per wave of the grid, a counter per row block
+        assert P_req == 0 and B <= 2048 and P == 0
+        assert S == units + 4 * (cus if cus > 0 else 256)
+        assert ws.num_counters == units
+        assert nb.value == S * rpb * (D + 1) * 4
+    else:
+        assert ws.schedule == SCHEDULE_PARTITIONS and ws.num_counters == 0
+        assert P > 0 and P % ps == 0
+        assert S * P >= cap and (S - 1) * P < cap      # covers the capacity, no empty tail
+        assert S <= MAX_GRID_YZ
+        if P_req > 0:
+            want = -(-P_req // ps) * ps
+            if want <= cap and -(-cap // want) <= MAX_GRID_YZ:
+                assert P == want                       # the caller's size, in whole pages
+        else:
+            assert B > 2048
+        assert nb.value == (B * G * Hkv * Lq * S * (D + 1) * 4 if S > 1 else 0)
+
+
+@settings(max_examples=200, deadline=None)
+@given(Lq=st.integers(1, 5000), **shapes)
+def test_prefill_and_router_plans(L, B, Hkv, G, Lq, D, dtype, ps, max_pages, cus):
+    a = _args(B, Hkv, G, Lq, D, dtype, ps, max_pages)
+    ws = PaWorkspace()
+    nb = ctypes.c_size_t(0)
+    assert L.pa_prefill_plan(ctypes.byref(a), cus, ctypes.byref(ws), ctypes.byref(nb)) == 0
+    assert ws.schedule == SCHEDULE_KEY_SPLIT and ws.partition_tokens == 0
+    tiles = -(-(G * Lq) // 128)
+    if dtype == 1 and B * tiles <= 2048:
+        slots = 4 * (cus if cus > 0 else 256)
+        assert (ws.num_splits, ws.num_counters) == (slots, slots)
+        assert nb.value == slots * (D // 2 + 2) * 256 * 4
+    else:
+        assert (ws.num_splits, ws.num_counters, nb.value) == (0, 0, 0)
+    # the router takes the decode plan exactly when G * L <= 8
+    wr = PaWorkspace()
+    nr = ctypes.c_size_t(0)
+    route = ctypes.c_int32(-1)
+    assert L.pa_attention_plan(ctypes.byref(a), cus, ctypes.byref(wr), ctypes.byref(nr),
+                               ctypes.byref(route)) == 0
+    if G * Lq <= 8:
+        assert route.value == _lib.ROUTE_DECODE
+        wd = PaWorkspace()
+        nd = ctypes.c_size_t(0)
+        assert L.pa_decode_plan(ctypes.byref(a), cus, ctypes.byref(wd), ctypes.byref(nd)) == 0
+        assert (wr.schedule, wr.num_splits, wr.partition_tokens, nr.value) == \
+               (wd.schedule, wd.num_splits, wd.partition_tokens, nd.value)
+    else:
+        assert route.value == _lib.ROUTE_PREFILL
+        assert (wr.schedule, wr.num_splits, wr.num_counters, nr.value) == \
+               (ws.schedule, ws.num_splits, ws.num_counters, nb.value)
