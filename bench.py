@@ -1,7 +1,7 @@
 """Benchmark of the paged-attention read path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only C2,C3,...]
-                    [--no-cpu-baseline] [--no-flush]
+                    [--no-cpu-baseline] [--no-flush] [--no-warm] [--no-clocks]
 
 Prints ONE JSON line.  The headline ``value`` is the decode workload "GQA
 decode, bf16, B=64, H_q=32, H_kv=8, D=128, page_size=16, contexts U[128,4096]"
@@ -12,7 +12,9 @@ cache flushed before every step.  ``roofline`` is for the dominant kernel
 (the decode kernel alone, timed by its own event pair).  Secondary sections
 report the chunked prefill, long-context decode, mixed batch and a
 long-prompt prefill sweep with their own rooflines.  ``cpu_baseline`` times
-the CPU oracle on the host on the full decode workload.
+the CPU oracle on the host on the full decode workload.  ``clocks`` holds the
+per-XCD gfx clocks and the memory clock that amd-smi reads while the decode
+and the long-prompt prefill run back to back (outside the timed regions).
 """
 from __future__ import annotations
 
@@ -199,6 +201,55 @@ def _counters(name, sha):
     return c.get("hbm_bytes_per_launch")
 
 
+# ------------------------------------------------------------------- clocks
+def sample_clocks(busy, timeout_s=30.0, lead_s=0.5):
+    """Clocks of the GPU while it runs a workload: keeps calling `busy()`
+    (which enqueues work and synchronises) for `lead_s` seconds, then starts
+    `amd-smi metric -c --json` as a child process and goes on calling it
+    until the child exits.  Returns the gfx clock of every XCD and the memory
+    clock in MHz, or None where amd-smi is missing, fails or sees more than
+    one GPU."""
+    import shutil
+    import subprocess
+    if any(k.startswith("ROCPROF") for k in os.environ):
+        return None  # under a profiler the child would be profiled too
+    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    if not os.path.exists(exe):
+        return None
+    t_lead = time.perf_counter()
+    while time.perf_counter() - t_lead < lead_s:
+        busy()
+    try:
+        proc = subprocess.Popen([exe, "metric", "-c", "--json"], stdout=subprocess.PIPE,
+                                stderr=subprocess.DEVNULL)
+    except OSError:
+        return None
+    t0 = time.perf_counter()
+    calls = 0
+    while proc.poll() is None and time.perf_counter() - t0 < timeout_s:
+        busy()
+        calls += 1
+    try:
+        raw, _ = proc.communicate(timeout=5.0)
+    except subprocess.TimeoutExpired:
+        proc.kill()
+        proc.communicate()
+        return None
+    try:
+        d = json.loads(raw)
+        gpus = d["gpu_data"] if isinstance(d, dict) else d
+        if len(gpus) != 1:
+            return None
+        c = gpus[0]["clock"]
+        gfx = sorted((int(k.split("_")[1]), v["clk"]["value"]) for k, v in c.items()
+                     if k.startswith("gfx_") and isinstance(v, dict))
+        mem = c.get("mem_0", {}).get("clk", {}).get("value")
+    except (ValueError, KeyError, TypeError, AttributeError, IndexError):
+        return None
+    return {"gfx_mhz_per_xcd": [v for _, v in gfx], "mem_mhz": mem,
+            "sample_s": round(time.perf_counter() - t0, 3), "busy_calls": calls}
+
+
 # --------------------------------------------------------------- cpu oracle
 def cpu_baseline(x, kv_bytes, min_seconds=10.0, max_runs=2000):
     import oracle
@@ -225,6 +276,44 @@ def cpu_baseline(x, kv_bytes, min_seconds=10.0, max_runs=2000):
                             "sample": f"mean of {len(t1s)} run(s) of {t1:.2f} s"}}
 
 
+def decode_busy(run, d, n=20):
+    """Back-to-back decode steps (the timed configuration, cache flushed
+    before each) for the clock sample."""
+    torch, api = run.torch, run.api
+    x = d.x
+    out = torch.empty_like(d.q)
+    args = api.make_args(d.q, d.kp, d.vp, d.bt, d.cl, out, scale=x.scale, mask=d.mask,
+                         query_lens=d.ql)
+    plan = api.pa_decode_plan(args)
+    ws = api.Workspace.for_plan(plan, d.q, fused=True)
+
+    def busy():
+        for _ in range(n):
+            run.flush()
+            api.pa_decode(args, ws)
+            if plan.num_splits > 1:
+                api.pa_split_reduce(args, ws)
+        torch.cuda.synchronize()
+    return busy
+
+
+def prefill_busy(run, d, n=2):
+    """Back-to-back prefill calls (with the key-split workspace) for the
+    clock sample."""
+    torch, api = run.torch, run.api
+    x = d.x
+    out = torch.empty_like(d.q)
+    args = api.make_args(d.q, d.kp, d.vp, d.bt, d.cl, out, scale=x.scale, mask=d.mask,
+                         query_lens=d.ql)
+    ws = api.PrefillWorkspace.for_args(args, d.q.device)
+
+    def busy():
+        for _ in range(n):
+            api.pa_prefill(args, ws)
+        torch.cuda.synchronize()
+    return busy
+
+
 # --------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -236,6 +325,8 @@ def main():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-warm", action="store_true",
                     help="skip the unflushed C2 decode steps (profiling runs)")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="skip the amd-smi clock samples (profiling runs)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3 times): the known "
@@ -298,6 +389,11 @@ def main():
         "wall_s_timed_region": round(r2["wall_s"], 4),
     }
     del r2
+    clocks = {"source": "amd-smi metric -c, sampled while the workload runs back to back "
+                        "(outside the timed regions)"}
+    if not args.no_clocks:
+        clocks["decode_C2"] = sample_clocks(decode_busy(run, d2))
+        log(f"[bench] clocks under C2 decode: {clocks['decode_C2']}")
     if not args.no_flush and not args.no_warm:
         # the same steps without the cache flush between them (K/V partly in
         # the 256 MB last-level cache): context only, never `value`
@@ -341,6 +437,9 @@ def main():
             long.append({"workload": f"long-prompt causal prefill bf16 B1 Hq28 Hkv4 D128 L{L} prefix0 page16",
                          "flops": fl, "tflops": round(tf, 2),
                          "frac_of_mfma_peak": round(tf / BF16_PEAK_TFLOPS, 4), **_stats(rl["ms"])})
+            if L == 16384 and not args.no_clocks:
+                clocks["prefill_L16384"] = sample_clocks(prefill_busy(run, dl))
+                log(f"[bench] clocks under L={L} prefill: {clocks['prefill_L16384']}")
             del dl, rl
         sections["prefill_long_prompt"] = long
     if "C4" in only:
@@ -425,6 +524,7 @@ def main():
             del a
         sections["append"] = wr
     result["sections"] = sections
+    result["clocks"] = clocks
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline on the decode workload")
