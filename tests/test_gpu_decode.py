@@ -61,6 +61,9 @@ CASES = [
     (8, "f32", 64, 16, 2, 4, 24, [4, 50, 97], 48, False),
     (9, "bf16", 128, 64, 8, 1, 32, [1, 4097, 2049], 0, True),
     (10, "bf16", 64, 3, 3, 5, 8, [5, 64, 100], 16, True),
+    # pages of 256 keys: many steps per page, partitions inside one page
+    (11, "bf16", 128, 16, 4, 1, 256, [1, 256, 257, 1000], 0, True),
+    (12, "bf16", 128, 8, 2, 2, 256, [2, 600, 2000], 512, True),
 ]
 
 

@@ -40,6 +40,10 @@ CASES = [
     (11, "bf16", 64, 8, 2, 100, 16, [100, 700], True, None),
     (12, "bf16", 128, 16, 4, 200, 48, [200, 1500, 3001], True, [200, 150, 7]),
     (13, "bf16", 128, 12, 3, 65, 32, [65, 66, 2000], True, None),
+    # 64- and 256-key pages: several 32-key tiles per page
+    (14, "bf16", 128, 8, 2, 100, 64, [100, 1000], True, None),
+    (15, "bf16", 128, 28, 4, 130, 256, [130, 300, 2600], True, [130, 64, 1]),
+    (16, "bf16", 64, 8, 2, 70, 256, [70, 900], False, None),
 ]
 
 
