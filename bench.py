@@ -202,33 +202,18 @@ def _counters(name, sha):
 
 
 # ------------------------------------------------------------------- clocks
-def sample_clocks(busy, timeout_s=30.0, lead_s=0.5):
-    """Clocks of the GPU while it runs a workload: keeps calling `busy()`
-    (which enqueues work and synchronises) for `lead_s` seconds, then starts
-    `amd-smi metric -c --json` as a child process and goes on calling it
-    until the child exits.  Returns the gfx clock of every XCD and the memory
-    clock in MHz, or None where amd-smi is missing, fails or sees more than
-    one GPU."""
-    import shutil
+def _amd_smi_clocks(exe, busy, timeout_s):
+    """One `amd-smi metric -c --json` run as a child process while `busy()`
+    keeps the GPU working; (gfx MHz per XCD, memory MHz, seconds) or None."""
     import subprocess
-    if any(k.startswith("ROCPROF") for k in os.environ):
-        return None  # under a profiler the child would be profiled too
-    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
-    if not os.path.exists(exe):
-        return None
-    t_lead = time.perf_counter()
-    while time.perf_counter() - t_lead < lead_s:
-        busy()
     try:
         proc = subprocess.Popen([exe, "metric", "-c", "--json"], stdout=subprocess.PIPE,
                                 stderr=subprocess.DEVNULL)
     except OSError:
         return None
     t0 = time.perf_counter()
-    calls = 0
     while proc.poll() is None and time.perf_counter() - t0 < timeout_s:
         busy()
-        calls += 1
     try:
         raw, _ = proc.communicate(timeout=5.0)
     except subprocess.TimeoutExpired:
@@ -246,8 +231,33 @@ def sample_clocks(busy, timeout_s=30.0, lead_s=0.5):
         mem = c.get("mem_0", {}).get("clk", {}).get("value")
     except (ValueError, KeyError, TypeError, AttributeError, IndexError):
         return None
-    return {"gfx_mhz_per_xcd": [v for _, v in gfx], "mem_mhz": mem,
-            "sample_s": round(time.perf_counter() - t0, 3), "busy_calls": calls}
+    return [v for _, v in gfx], mem, round(time.perf_counter() - t0, 3)
+
+
+def sample_clocks(busy, samples=3, timeout_s=30.0, gap_s=1.0):
+    """Clocks of the GPU while it runs a workload: keeps calling `busy()`
+    (which enqueues work and synchronises) throughout, and reads the clocks
+    with amd-smi `samples` times, each after `gap_s` more seconds of work
+    (the tool reports a snapshot that the driver refreshes; readings taken
+    back to back repeat it).  Each reading is the gfx clock of every XCD and
+    the memory clock in MHz.  None where amd-smi is missing or fails, or
+    under a profiler (the child would be profiled too)."""
+    import shutil
+    if any(k.startswith("ROCPROF") for k in os.environ):
+        return None
+    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    if not os.path.exists(exe):
+        return None
+    out = []
+    for _ in range(samples):
+        t_gap = time.perf_counter()
+        while time.perf_counter() - t_gap < gap_s:
+            busy()
+        r = _amd_smi_clocks(exe, busy, timeout_s)
+        if r is None:
+            return None
+        out.append({"gfx_mhz_per_xcd": r[0], "mem_mhz": r[1], "sample_s": r[2]})
+    return out
 
 
 # --------------------------------------------------------------- cpu oracle
@@ -389,8 +399,9 @@ def main():
         "wall_s_timed_region": round(r2["wall_s"], 4),
     }
     del r2
-    clocks = {"source": "amd-smi metric -c, sampled while the workload runs back to back "
-                        "(outside the timed regions)"}
+    clocks = {"source": "amd-smi metric -c, three readings one second apart while the "
+                        "workload runs back to back (outside the timed regions); driver "
+                        "snapshots, context only"}
     if not args.no_clocks:
         clocks["decode_C2"] = sample_clocks(decode_busy(run, d2))
         log(f"[bench] clocks under C2 decode: {clocks['decode_C2']}")
