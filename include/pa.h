@@ -191,7 +191,7 @@ pa_status pa_split_reduce(const pa_args *args, const pa_workspace *ws, void *str
  * vLLM's PagedAttention Kernel", section 3.3: partial results combined
  * afterwards), so that one long context in a batch does not bound the call.
  * On return plan->schedule = PA_SCHEDULE_KEY_SPLIT and plan->num_splits =
- * num_counters = the slots of the split (4 per compute unit, `num_cus` 0:
+ * num_counters = the slots of the split (5 per compute unit, `num_cus` 0:
  * 256), or 0 when the call cannot split (fp32, or batch * ceil(G * L / 128)
  * above 2048): no workspace then.  *workspace_bytes (if not NULL) is the size
  * of partial_out plus partial_lse; the counters take num_counters * 4 bytes

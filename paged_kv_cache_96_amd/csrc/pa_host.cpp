@@ -277,10 +277,13 @@ PA_EXPORT pa_status pa_prefill_plan(const pa_args *args, int32_t num_cus, pa_wor
   plan->num_counters = 0;
   if (workspace_bytes) *workspace_bytes = 0;
   if (!prefill_splits(args)) return PA_OK;  // runs unsplit: no workspace
-  // four piece slots per compute unit: the split sizes its pieces from the
-  // slot count and launches at most half as many extra workgroups
+  // five piece slots per compute unit: the split sizes its pieces from the
+  // slot count (at most 0.8 of the slots hold split pieces) and launches at
+  // most half as many extra workgroups.  Measured against four: C5-like
+  // prefill -5 to -11%, long prompts of 4096-16384 rows -3 to -5%, short
+  // ones (2048 rows) +3%, chunked prefill within +-2%.
   const int cus = num_cus > 0 ? num_cus : 256;
-  plan->num_splits = 4 * cus;
+  plan->num_splits = 5 * cus;
   plan->num_counters = plan->num_splits;
   if (workspace_bytes)
     *workspace_bytes = (size_t)plan->num_splits * (args->head_dim / 2 + 2) * 256 * sizeof(float);

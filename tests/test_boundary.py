@@ -198,16 +198,16 @@ def _prefill_plan(L, a, num_cus=0):
 
 def test_prefill_plan(L):
     h = HostBuffers()
-    # chunked prefill, 4 requests x 512 rows of G = 7: 4 slots per compute unit
+    # chunked prefill, 4 requests x 512 rows of G = 7: 5 slots per compute unit
     a = h.args(batch=4, num_q_heads=28, num_kv_heads=4, q_len=512, max_pages=160)
-    assert _prefill_plan(L, a) == (0, SCHEDULE_KEY_SPLIT, 1024, 1024, 1024 * (64 + 2) * 256 * 4)
-    assert _prefill_plan(L, a, num_cus=2)[2] == 8
-    assert _prefill_plan(L, h.args(head_dim=64, q_len=64))[4] == 1024 * (32 + 2) * 256 * 4
+    assert _prefill_plan(L, a) == (0, SCHEDULE_KEY_SPLIT, 1280, 1280, 1280 * (64 + 2) * 256 * 4)
+    assert _prefill_plan(L, a, num_cus=2)[2] == 10
+    assert _prefill_plan(L, h.args(head_dim=64, q_len=64))[4] == 1280 * (32 + 2) * 256 * 4
     # fp32 and calls past 2048 (request, tile) pairs run unsplit: no workspace
     assert _prefill_plan(L, h.args(dtype=0, q_len=64))[2:] == (0, 0, 0)
     big = h.args(batch=2049, q_len=16)  # one tile per request
     assert _prefill_plan(L, big)[2:] == (0, 0, 0)
-    assert _prefill_plan(L, h.args(batch=2048, q_len=16))[2] == 1024
+    assert _prefill_plan(L, h.args(batch=2048, q_len=16))[2] == 1280
     assert _prefill_plan(L, h.args(head_dim=96))[0] == -2
 
 

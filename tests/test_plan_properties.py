@@ -88,7 +88,7 @@ def test_prefill_and_router_plans(L, B, Hkv, G, Lq, D, dtype, ps, max_pages, cus
     assert ws.schedule == SCHEDULE_KEY_SPLIT and ws.partition_tokens == 0
     tiles = -(-(G * Lq) // 128)
     if dtype == 1 and B * tiles <= 2048:
-        slots = 4 * (cus if cus > 0 else 256)
+        slots = 5 * (cus if cus > 0 else 256)
         assert (ws.num_splits, ws.num_counters) == (slots, slots)
         assert nb.value == slots * (D // 2 + 2) * 256 * 4
     else:
