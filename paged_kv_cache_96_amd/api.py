@@ -104,7 +104,9 @@ def pa_decode_plan(args: PaArgs, *, num_cus: int = 0, partition_tokens: int = 0)
 class Workspace:
     """Device buffers of a decode plan (torch owns the memory).  Partition
     schedule: states [B, H_q, L, num_splits(, D)]; balanced schedule:
-    `block_rows` states per piece slot, [num_splits, block_rows(, D)]."""
+    `block_rows` states per piece slot, [num_splits, block_rows(, D)].  The
+    buffers are allocated and the counters zeroed on torch's current stream:
+    a call on another stream must first wait for it."""
 
     def __init__(self, B: int, Hq: int, L: int, D: int, num_splits: int, partition_tokens: int,
                  device, schedule: int = SCHEDULE_PARTITIONS, block_rows: int = 0,
@@ -134,6 +136,10 @@ class Workspace:
         self.c.schedule = self.schedule
         self.c.num_counters = int(num_counters)
         self.c.counters = _ptr(self.counters)
+
+    def tensors(self):
+        """The device tensors of the workspace."""
+        return [t for t in (self.partial_out, self.partial_lse, self.counters) if t is not None]
 
     @classmethod
     def for_plan(cls, plan: DecodePlan, query: torch.Tensor, fused: bool = True) -> "Workspace":
@@ -200,6 +206,10 @@ class PrefillWorkspace:
         self.c.partial_lse = _ptr(self.partial_lse)
         self.c.counters = _ptr(self.counters)
 
+    def tensors(self):
+        """The device tensors of the workspace."""
+        return [t for t in (self.partial_out, self.partial_lse, self.counters) if t is not None]
+
     @classmethod
     def for_args(cls, args: PaArgs, device, num_cus: int = 0) -> "PrefillWorkspace":
         return cls(pa_prefill_plan(args, num_cus=num_cus), args.head_dim, device)
@@ -256,15 +266,25 @@ def paged_attention(query: torch.Tensor, key_pages: torch.Tensor, value_pages: t
                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Convenience call through the library's router (pa_attention): the
     decode path when the query rows of one kv head fit a decode row block,
-    the prefill path otherwise."""
+    the prefill path otherwise.  The workspace is allocated (and its
+    counters zeroed) on torch's current stream; when `stream` is another
+    stream it first waits for the current one, and the allocator keeps the
+    workspace until the work queued on `stream` is done."""
     if out is None:
         out = torch.empty_like(query)
     args = make_args(query, key_pages, value_pages, block_table, context_lens, out, scale=scale,
                      mask=mask, query_lens=query_lens)
     ap = pa_attention_plan(args, partition_tokens=partition_tokens)
     ws = attention_workspace(ap, args, query)
+    if stream is not None:
+        if not isinstance(stream, torch.cuda.Stream):
+            stream = torch.cuda.ExternalStream(int(stream))
+        current = torch.cuda.current_stream()
+        if stream != current:
+            stream.wait_stream(current)
+            for t in ws.tensors():
+                t.record_stream(stream)
     pa_attention(args, ws, stream)
-    out._pa_workspace = ws  # keep the buffers alive until the caller is done
     return out
 
 

@@ -65,3 +65,23 @@ def test_decode_route_with_partitions_runs_the_merge(api):
     d = DeviceInputs(x)
     got = _routed(api, d, partition_tokens=256)
     assert_parity(got, oracle.attention_of(x), "bf16", "router partitions")
+
+
+@pytest.mark.parametrize("Lq", [1, 300])
+def test_routed_call_on_a_side_stream(api, Lq):
+    """paged_attention on a stream other than the current one: the call waits
+    for the workspace set-up (zeroed arrival counters) made on the current
+    stream and gives the current-stream result bit for bit, call after call."""
+    import torch
+    x = make_random(410 + Lq, B=4, H_q=32, H_kv=8, L=Lq, D=128, page_size=16, ctx=(Lq, 2500),
+                    dtype="bf16", causal=True, name=f"side_stream{Lq}")
+    d = DeviceInputs(x)
+    base = api.paged_attention(d.q, d.kp, d.vp, d.bt, d.cl, scale=x.scale, mask=d.mask)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for rep in range(3):
+        got = api.paged_attention(d.q, d.kp, d.vp, d.bt, d.cl, scale=x.scale, mask=d.mask,
+                                  stream=side)
+        side.synchronize()
+        assert torch.equal(got.view(torch.int16), base.view(torch.int16)), f"rep {rep}"
+    assert_parity(base, oracle.attention_of(x), "bf16", f"side stream L={Lq}")
