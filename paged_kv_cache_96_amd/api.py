@@ -186,7 +186,8 @@ class PrefillWorkspace:
     """Device buffers of a prefill plan (torch owns the memory): piece states
     partial_out [num_splits, D / 8, 256, 4] and partial_lse [num_splits, 2,
     256] fp32, and the arrival counters (zeroed once, left zero by every
-    call)."""
+    call).  Allocated and zeroed on torch's current stream: a call on
+    another stream must first wait for it."""
 
     def __init__(self, plan: PrefillPlan, D: int, device):
         self.num_splits = int(plan.num_splits)
