@@ -35,6 +35,21 @@ def _int32(t: Optional[torch.Tensor], name: str) -> Optional[torch.Tensor]:
     return t
 
 
+def _same_gpu(ref: torch.Tensor, **tensors) -> None:
+    """The kernels dereference every pointer on the GPU: each tensor must live
+    on the device of `ref`, and that device must be a GPU."""
+    if ref.device.type != "cuda":
+        raise ValueError("tensors passed to libpa must be on the GPU")
+    for name, t in tensors.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, not on {ref.device}")
+
+
+def _shape(t: Optional[torch.Tensor], want: tuple, name: str) -> None:
+    if t is not None and tuple(t.shape) != want:
+        raise ValueError(f"{name} must have shape {list(want)}, not {list(t.shape)}")
+
+
 def make_args(query: torch.Tensor, key_pages: torch.Tensor, value_pages: torch.Tensor,
               block_table: torch.Tensor, context_lens: torch.Tensor, out: torch.Tensor, *,
               scale: Optional[float] = None, mask: Optional[str] = "causal",
@@ -53,6 +68,18 @@ def make_args(query: torch.Tensor, key_pages: torch.Tensor, value_pages: torch.T
     _int32(block_table, "block_table")
     _int32(context_lens, "context_lens")
     _int32(query_lens, "query_lens")
+    _int32(debug_trace, "debug_trace")
+    _int32(debug_visits, "debug_visits")
+    _same_gpu(query, key_pages=key_pages, value_pages=value_pages, block_table=block_table,
+              context_lens=context_lens, out=out, query_lens=query_lens,
+              debug_trace=debug_trace, debug_visits=debug_visits)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [batch, max_pages]")
+    cap = block_table.shape[1] * ps
+    _shape(context_lens, (B,), "context_lens")
+    _shape(query_lens, (B,), "query_lens")
+    _shape(debug_trace, (B, cap, 2), "debug_trace")
+    _shape(debug_visits, (B, Hkv, cap), "debug_visits")
     a = PaArgs()
     a.query = _ptr(query)
     a.key_pages = _ptr(key_pages)
@@ -305,6 +332,7 @@ def pa_append(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor
     _int32(slot_mapping, "slot_mapping")
     if tuple(slot_mapping.shape) != (T,):
         raise ValueError("slot_mapping must be [num_tokens]")
+    _same_gpu(key_pages, value_pages=value_pages, key=key, value=value, slot_mapping=slot_mapping)
     a = _lib.PaAppendArgs()
     a.key, a.value, a.slot_mapping = _ptr(key), _ptr(value), _ptr(slot_mapping)
     a.key_pages, a.value_pages = _ptr(key_pages), _ptr(value_pages)
