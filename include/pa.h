@@ -20,6 +20,10 @@
  *  - All data pointers are DEVICE pointers owned by the caller; the library
  *    never allocates, frees or synchronises.  Work is enqueued on `stream`
  *    (a hipStream_t; NULL means the null stream) and the call returns at once.
+ *    A call enqueues kernel launches only (no memset or copy), and every
+ *    kernel leaves the workspace's arrival counters at zero, so calls can be
+ *    captured into a HIP graph and replayed (plan and workspace set up
+ *    before the capture).
  *  - Layouts are dense row-major with no padding:
  *      query, out        [B, H_q, L, D]
  *      key/value_pages   [num_pages, H_kv, page_size, D]
