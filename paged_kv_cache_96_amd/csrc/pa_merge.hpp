@@ -75,8 +75,11 @@ namespace pa {
 // 64 / R lanes per row, each owning D * R / 64 consecutive elements.  Piece s
 // of row r has its state at lse[s * R + r] and po[(s * R + r) * D ...]; rows
 // with valid[r] false get zeros.  A running (max, sum, acc) keeps every load
-// independent of the previous piece's arithmetic, so the loads of several
-// pieces are in flight together.
+// independent of the previous piece's arithmetic, and the loop body has no
+// branch (an all-empty prefix is carried by selects), so the unrolled loads
+// of up to 16 pieces are in flight together: the states are read past the
+// caches, and a row block split into many pieces (a small batch over long
+// contexts) would otherwise pay one memory round trip per piece.
 template <typename T, int D, int R>
 __device__ __forceinline__ void merge_block(const float *lse, const float *po, int n,
                                             const bool (&valid)[R], const size_t (&qrow)[R],
@@ -99,7 +102,7 @@ __device__ __forceinline__ void merge_block(const float *lse, const float *po, i
   float m = kNegInf, l = 0.f, acc[kE];
 #pragma unroll
   for (int e = 0; e < kE; ++e) acc[e] = 0.f;
-#pragma unroll 4
+#pragma unroll 16
   for (int s = 0; s < cnt; ++s) {
     const float ls = __uint_as_float(
         (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rl, (s * R + r) * 4, 0, kSysScope));
@@ -121,13 +124,13 @@ __device__ __forceinline__ void merge_block(const float *lse, const float *po, i
             (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ro, base + e * 4, 0, kSysScope));
     }
     const float mn = fmaxf(m, ls);
-    if (mn == kNegInf) continue;  // nothing seen yet
-    const float a = fast_exp2((m - mn) * kMergeLog2e);   // m = -inf -> 0
-    const float w = fast_exp2((ls - mn) * kMergeLog2e);
+    const bool none = mn == kNegInf;  // nothing seen yet: the state stays (-inf, 0, 0)
+    const float a = none ? 0.f : fast_exp2((m - mn) * kMergeLog2e);  // m = -inf -> 0
+    const float w = none ? 0.f : fast_exp2((ls - mn) * kMergeLog2e);
     m = mn;
     l = fmaf(l, a, w);
 #pragma unroll
-    for (int e = 0; e < kE; ++e) acc[e] = fmaf(acc[e], a, w * v[e]);
+    for (int e = 0; e < kE; ++e) acc[e] = none ? 0.f : fmaf(acc[e], a, w * v[e]);
   }
   if (r >= rows_in_range) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
