@@ -11,7 +11,8 @@ pa_split_reduce), with the inputs resident in HBM and the 256 MB last-level
 cache flushed before every step.  ``roofline`` is for the dominant kernel
 (the decode kernel alone, timed by its own event pair).  Secondary sections
 report the chunked prefill, long-context decode, mixed batch and a
-long-prompt prefill sweep with their own rooflines.  ``cpu_baseline`` times
+long-prompt prefill sweep with their own rooflines, small-batch decode
+latencies and the K/V write.  ``cpu_baseline`` times
 the CPU oracle on the host on the full decode workload.  ``clocks`` holds the
 per-XCD gfx clocks and the memory clock that amd-smi reads while the decode
 and the long-prompt prefill run back to back (outside the timed regions).
@@ -330,7 +331,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="C2,C3,C4,C5,long,append")
+    ap.add_argument("--only", default="C2,C3,C4,C5,long,small,append")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-warm", action="store_true",
@@ -492,6 +493,25 @@ def main():
             "prefill_flops": fl, "prefill_tflops": round(fl / pm / 1e9, 2), "prefill_mean_ms": pm,
             "combined_ms": round(sm + pm, 5)}
         del dd, dp, rd, rp
+    if "small" in only:
+        # latency-bound decode: one to four requests over long contexts
+        # (H 32/8, D 128, page 16), where the merge of many pieces per row
+        # block is part of the step
+        sb = []
+        for B, ctx in ((1, 4096), (1, 32768), (4, 4096)):
+            xs = W.make_random(800 + B, B=B, H_q=32, H_kv=8, L=1, D=128, page_size=16,
+                               ctx=[ctx] * B, dtype="bf16", causal=True, extra_free_pages=16)
+            ds = run.to_device(xs)
+            kvs = decode_kv_bytes(xs)
+            rs = run.time_decode(ds, max(10, args.steps // 3), args.warmup)
+            sm = float(np.mean(rs["step_ms"]))
+            log(f"[bench] small-batch decode B={B} ctx={ctx}: {sm * 1e3:.1f} us, "
+                f"{kvs / sm / 1e6:.0f} GB/s, S={rs['S']}")
+            sb.append({"workload": f"decode bf16 B{B} Hq32 Hkv8 D128 page16 ctx {ctx}",
+                       "kv_bytes": kvs, "gbs_step": round(kvs / sm / 1e6, 2),
+                       "schedule": rs["schedule"], "num_splits": rs["S"], **_stats(rs["step_ms"])})
+            del ds, rs, xs
+        sections["decode_small_batch"] = sb
     if "threshold" in only:
         # decode vs prefill around the router's threshold (not in the default
         # run): 64 requests, ctx U[128,4096], H 32/8, D 128, bf16
