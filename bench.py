@@ -498,7 +498,7 @@ def main():
         # (H 32/8, D 128, page 16), where the merge of many pieces per row
         # block is part of the step
         sb = []
-        for B, ctx in ((1, 4096), (1, 32768), (4, 4096)):
+        for B, ctx in ((1, 4096), (1, 16384), (1, 32768), (2, 4096), (4, 4096)):
             xs = W.make_random(800 + B, B=B, H_q=32, H_kv=8, L=1, D=128, page_size=16,
                                ctx=[ctx] * B, dtype="bf16", causal=True, extra_free_pages=16)
             ds = run.to_device(xs)

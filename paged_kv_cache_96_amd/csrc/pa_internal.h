@@ -56,6 +56,23 @@ constexpr int kBalancedMinSteps = 4;
 // block with keys is laid out as kUnitSetupSteps setup positions followed
 // by its steps, so runs are equal in cost rather than in steps.
 constexpr int kUnitSetupSteps = 5;
+// Cap on the waves of a balanced call over `units` row blocks and T steps:
+// Wa^2 <= kBalancedWaveFactor * units * T.  With p = Wa / units pieces per row
+// block and s = T / Wa steps per run, that is s >= p / kBalancedWaveFactor: a
+// small batch over long contexts is no longer cut into 100+ pieces of a few
+// steps per row block, whose per-piece costs (setup, state write, merge read)
+// outweigh the extra waves.  Measured best near s = p / 4 for 1-2 requests
+// over 4k-32k keys; large batches are bounded by the slot count first.
+constexpr int kBalancedWaveFactor = 4;
+
+// floor(sqrt(x)) for x >= 0, exact on host and device.
+__host__ __device__ inline int64_t isqrt64(int64_t x) {
+  if (x < 2) return x;
+  int64_t r = (int64_t)sqrt((double)x);
+  while (r * r > x) --r;
+  while ((r + 1) * (r + 1) <= x) ++r;
+  return r;
+}
 
 // Largest number of (request, tile) pairs the key split of the bf16 prefill
 // plans over (the plan's tables live in the kernel's staging buffers);
@@ -93,6 +110,8 @@ __host__ __device__ inline BalancedSplit balanced_split(int64_t grid_waves, int6
   int64_t w = grid_waves;
   const int64_t by_len = (T + kBalancedMinSteps - 1) / kBalancedMinSteps;
   if (by_len < w) w = by_len;
+  const int64_t by_pieces = isqrt64(kBalancedWaveFactor * units * T);
+  if (by_pieces < w) w = by_pieces;
   if (S - units < w) w = S - units;  // S >= units + 1 is checked by the host
   s.Wa = w;
   return s;

@@ -6,6 +6,7 @@ shapes: every step of every row block is walked exactly once, a piece's slot
 (row block + wave) is unique and below the workspace's slots, and the waves
 the merge expects for a row block (w0 .. w1 from the same formulas) are
 exactly the waves that walked it.  The constants are read from the header."""
+import math
 import os
 import re
 
@@ -23,12 +24,14 @@ def _const(name):
 
 SETUP = _const("kUnitSetupSteps")
 MIN_STEPS = _const("kBalancedMinSteps")
+WAVE_FACTOR = _const("kBalancedWaveFactor")
 
 
 def _waves(grid_waves, T, units, S):
     if T <= 0:
         return 0
-    return min(grid_waves, (T + MIN_STEPS - 1) // MIN_STEPS, S - units)
+    return min(grid_waves, (T + MIN_STEPS - 1) // MIN_STEPS, S - units,
+               math.isqrt(WAVE_FACTOR * units * T))
 
 
 def _walk(ctx, U, step, grid_waves, S):
@@ -106,3 +109,21 @@ def test_setup_positions_move_steps_away_from_multi_piece_runs():
     multi = [len(u) for v, u in per_wave.items() if len(set(u)) > 1]
     single = [len(u) for v, u in per_wave.items() if len(set(u)) == 1]
     assert multi and single and max(multi) <= min(single)
+
+
+@pytest.mark.parametrize("B,U,keys", [(1, 8, 16384), (2, 8, 4096), (4, 8, 4096), (1, 8, 32768),
+                                      (3, 16, 9000)])
+def test_piece_cap_bounds_waves_and_pieces_per_row_block(B, U, keys):
+    # a small batch over long contexts: the grid and the slot count would allow
+    # hundreds of pieces per row block; the cap keeps Wa^2 <= factor * units * T
+    # (runs of at least pieces / factor steps) and still walks every step once
+    ctx = [keys - 37 * b for b in range(B)]
+    n, R, Wa, walked, pieces, _ = _walk(ctx, U, 16, 8192, B * U + 1280)
+    units, T = B * U, R[-1]
+    assert Wa == min(math.isqrt(WAVE_FACTOR * units * T), (T + MIN_STEPS - 1) // MIN_STEPS, 1280)
+    assert Wa * Wa <= WAVE_FACTOR * units * T
+    assert len(walked) == U * sum(n)
+    per_unit = sum(len(p) for p in pieces.values()) / units
+    steps_per_run = T / Wa
+    assert per_unit <= WAVE_FACTOR * steps_per_run + 2
+
