@@ -215,6 +215,26 @@ def test_balanced_schedule_parity_and_repeat(api, num_cus, fused):
         assert int(ex["ws"].counters.abs().sum()) == 0
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "merge_kernel"])
+@pytest.mark.parametrize("B,ctx", [(1, [16384]), (2, [4096, 3001]), (1, [32768])])
+def test_small_batch_long_context_wave_cap_parity(api, B, ctx, fused):
+    """One or two requests over long contexts: the balanced split's wave cap
+    (runs of at least pieces / factor steps) is what sizes the grid here.
+    Every key is visited exactly once and the output matches the oracle,
+    with the traced and the production kernel alike."""
+    x = make_random(73 + B, B=B, H_q=32, H_kv=8, L=1, D=128, page_size=16,
+                    ctx=ctx, dtype="bf16", causal=True, extra_free_pages=16)
+    d = DeviceInputs(x)
+    ref = oracle.attention_of(x)
+    a, ex = run_decode(api, d, trace=True, fused=fused)
+    print(f"[wave cap] B={B} ctx={ctx} S={ex['S']} fused={fused}", flush=True)
+    assert ex["schedule"] == api.SCHEDULE_BALANCED
+    assert np.array_equal(ex["visits"], _expect_visits(x))
+    assert_parity(a, ref, "bf16", f"wave cap traced B={B}")
+    b, _ = run_decode(api, d, fused=fused)
+    assert_parity(b, ref, "bf16", f"wave cap B={B}")
+
+
 def test_balanced_and_partition_schedules_agree(api):
     x = make_random(72, B=5, H_q=32, H_kv=8, L=2, D=128, page_size=16,
                     ctx=[2, 300, 1025, 77, 2048], dtype="bf16", causal=True,
