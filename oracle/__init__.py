@@ -4,10 +4,12 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
 leg may import this package.  The product path (``paged_kv_cache_96_amd``)
 never does, and this package imports nothing from it.
 
-The arithmetic lives in ``pa_oracle.c`` (plain C, double precision, OpenMP over
-independent (request, kv head) units); this module builds it with gcc and
-marshals numpy arrays.  ``ledger.py`` models the page pool and per-request
-page lists on the write side.
+The arithmetic lives in ``pa_oracle.c`` (plain C, OpenMP over independent
+(request, kv head) units); this module builds it with gcc twice -- the fp32
+two-pass reference (``precision="f32"``, the default) and the same steps in
+fp64 (``precision="f64"``, the stricter check) -- and marshals numpy arrays.
+``ledger.py`` models the page pool and per-request page lists on the write
+side.
 
 Every function takes plain arrays; ``*_of(inputs)`` helpers accept any object
 with the attributes of ``workloads.PagedInputs`` (duck-typed, no import).
@@ -23,7 +25,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "pa_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+_LIB = os.path.join(_HERE, "liboracle.so")          # fp64 build
+_LIB32 = os.path.join(_HERE, "liboracle_f32.so")    # fp32 build (-DOR_SINGLE)
+_FLAGS = {_LIB: (), _LIB32: ("-DOR_SINGLE",)}
+PRECISIONS = {"f64": _LIB, "f32": _LIB32}
 
 STATUS = {0: "ok", 1: "bad shape", 2: "page id out of range", 3: "bad context length",
           4: "bad query length", 5: "out of memory"}
@@ -46,8 +51,17 @@ def compile_library(src: str = _SRC, out: str = _LIB, extra_flags=()) -> str:
 
 
 def build() -> str:
-    """Rebuild the oracle library unconditionally."""
-    return compile_library()
+    """Rebuild both oracle libraries (fp64 and fp32) unconditionally."""
+    for path, flags in _FLAGS.items():
+        compile_library(out=path, extra_flags=flags)
+    return _LIB
+
+
+def lib_for(precision: str) -> str:
+    """Path of the oracle library of `precision` ("f32" or "f64")."""
+    if precision not in PRECISIONS:
+        raise ValueError(f"precision must be one of {sorted(PRECISIONS)}")
+    return PRECISIONS[precision]
 
 
 _lib_cache = {}
@@ -58,9 +72,9 @@ def load(path: str = _LIB) -> ctypes.CDLL:
     if path in _lib_cache:
         return _lib_cache[path]
     if not os.path.exists(path):
-        if path != _LIB:
+        if path not in _FLAGS:
             raise FileNotFoundError(path)
-        compile_library()
+        compile_library(out=path, extra_flags=_FLAGS[path])
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i = ctypes.c_int
@@ -117,9 +131,11 @@ class _Prepared:
 
 def attention(query, key_pages, value_pages, block_table, context_lens, page_size, *,
               dtype: str, causal: bool, scale: float, query_lens=None,
-              nthreads: Optional[int] = None, lib_path: str = _LIB,
-              return_threads: bool = False):
-    """Paged attention by the plain definition; float64 [B, H_q, L, D]."""
+              nthreads: Optional[int] = None, lib_path: Optional[str] = None,
+              precision: str = "f32", return_threads: bool = False):
+    """Paged attention by the plain definition; float64 array [B, H_q, L, D]
+    holding the results of the `precision` build (`lib_path` overrides it)."""
+    lib_path = lib_path or lib_for(precision)
     prep = _Prepared(query, key_pages, value_pages, block_table, context_lens, query_lens,
                      page_size, dtype, causal, scale)
     B, Hq, Hkv, L, D = prep.dims[:5]
@@ -135,8 +151,11 @@ def attention(query, key_pages, value_pages, block_table, context_lens, page_siz
 def partials(query, key_pages, value_pages, block_table, context_lens, page_size, *,
              dtype: str, causal: bool, scale: float, partition_tokens: int, num_splits: int,
              query_lens=None, nthreads: Optional[int] = None,
-             lib_path: str = _LIB) -> Tuple[np.ndarray, np.ndarray]:
-    """Per-partition (o, lse) states: [B,H_q,L,S,D] and [B,H_q,L,S] (float64)."""
+             lib_path: Optional[str] = None,
+             precision: str = "f32") -> Tuple[np.ndarray, np.ndarray]:
+    """Per-partition (o, lse) states: [B,H_q,L,S,D] and [B,H_q,L,S] (float64
+    arrays of the `precision` build's results)."""
+    lib_path = lib_path or lib_for(precision)
     prep = _Prepared(query, key_pages, value_pages, block_table, context_lens, query_lens,
                      page_size, dtype, causal, scale)
     B, Hq, Hkv, L, D = prep.dims[:5]
@@ -150,8 +169,10 @@ def partials(query, key_pages, value_pages, block_table, context_lens, page_size
     return po, pl
 
 
-def merge(part_o: np.ndarray, part_lse: np.ndarray, lib_path: str = _LIB) -> np.ndarray:
+def merge(part_o: np.ndarray, part_lse: np.ndarray, lib_path: Optional[str] = None,
+          precision: str = "f32") -> np.ndarray:
     """Log-sum-exp merge of partition states over the second-to-last axis."""
+    lib_path = lib_path or lib_for(precision)
     po = np.ascontiguousarray(part_o, dtype=np.float64)
     pl = np.ascontiguousarray(part_lse, dtype=np.float64)
     S, D = po.shape[-2], po.shape[-1]
@@ -164,11 +185,12 @@ def merge(part_o: np.ndarray, part_lse: np.ndarray, lib_path: str = _LIB) -> np.
 
 
 def translate(block_table, context_lens, page_size: int, num_pages: int,
-              lib_path: str = _LIB) -> np.ndarray:
+              lib_path: Optional[str] = None) -> np.ndarray:
     """(physical page, slot) of every logical key: int32 [B, max_pages*page_size, 2]."""
     bt = np.ascontiguousarray(block_table, dtype=np.int32)
     cl = np.ascontiguousarray(context_lens, dtype=np.int32)
     B, mp = bt.shape
+    lib_path = lib_path or _LIB
     tr = np.zeros((B, mp * page_size, 2), dtype=np.int32)
     rc = load(lib_path).or_translate(_ptr(bt), _ptr(cl), B, mp, page_size, num_pages, _ptr(tr))
     if rc:

@@ -17,7 +17,11 @@
  *      s_j = scale * q . k_j, m = max s_j, w_j = exp(s_j - m),
  *      o = sum_j w_j v_j / sum_j w_j  (the dense_attention reference of
  *      "Reading vLLM's PagedAttention Kernel", section 4).
- * All arithmetic is in double precision; bf16 inputs are widened exactly.
+ * Precision: the arithmetic type `real` is float when the file is built
+ * with -DOR_SINGLE (the plain fp32 two-pass reference: fp32 products, sums,
+ * expf and logf) and double otherwise (the stricter check: the same steps
+ * in fp64).  bf16 and fp32 inputs are widened exactly; results are handed
+ * back as double arrays in both builds.
  *
  * Readings where the pages leave a step open:
  *   - query head h reads kv head h / (H_q / H_kv) (contiguous GQA groups);
@@ -48,6 +52,18 @@ enum {
 };
 enum { OR_F32 = 0, OR_BF16 = 1 };
 
+#ifdef OR_SINGLE
+typedef float real;
+#define R_EXP expf
+#define R_LOG logf
+#define R_INF INFINITY
+#else
+typedef double real;
+#define R_EXP exp
+#define R_LOG log
+#define R_INF INFINITY
+#endif
+
 typedef struct {
   const void *q, *kp, *vp;
   const int32_t *bt, *cl, *ql;
@@ -55,12 +71,12 @@ typedef struct {
   double scale;
 } or_args;
 
-static double widen(const void *base, size_t idx, int dtype) {
-  if (dtype == OR_F32) return (double)((const float *)base)[idx];
+static real widen(const void *base, size_t idx, int dtype) {
+  if (dtype == OR_F32) return (real)((const float *)base)[idx];
   uint32_t bits = ((uint32_t)((const uint16_t *)base)[idx]) << 16;
   float f;
   memcpy(&f, &bits, sizeof f);
-  return (double)f;
+  return (real)f;
 }
 
 static int qlen_of(const or_args *a, int b) { return a->ql ? a->ql[b] : a->L; }
@@ -96,7 +112,7 @@ static void translate(const or_args *a, int b, int j, int *page, int *slot) {
 }
 
 /* Step 2: dense copies of the first ctx keys/values of (b, kv head g). */
-static void gather_dense(const or_args *a, int b, int g, double *Kd, double *Vd) {
+static void gather_dense(const or_args *a, int b, int g, real *Kd, real *Vd) {
   const int ctx = a->cl[b], D = a->D;
   for (int j = 0; j < ctx; ++j) {
     int page, slot;
@@ -112,26 +128,27 @@ static void gather_dense(const or_args *a, int b, int g, double *Kd, double *Vd)
 /* Step 3: two-pass softmax attention of one query row over dense keys
  * [lo, hi).  Writes o[D]; returns the log-sum-exp of the scaled scores
  * (-inf when the span is empty, with o = 0). */
-static double dense_attention(const or_args *a, const double *q, const double *Kd,
-                              const double *Vd, int lo, int hi, double *s, double *o) {
+static real dense_attention(const or_args *a, const real *q, const real *Kd, const real *Vd,
+                            int lo, int hi, real *s, real *o) {
   const int D = a->D;
-  for (int d = 0; d < D; ++d) o[d] = 0.0;
-  if (hi <= lo) return -INFINITY;
-  double m = -INFINITY;
+  const real scale = (real)a->scale;
+  for (int d = 0; d < D; ++d) o[d] = 0;
+  if (hi <= lo) return -R_INF;
+  real m = -R_INF;
   for (int j = lo; j < hi; ++j) {
-    double acc = 0.0;
+    real acc = 0;
     for (int d = 0; d < D; ++d) acc += q[d] * Kd[(size_t)j * D + d];
-    s[j] = a->scale * acc;
+    s[j] = scale * acc;
     if (s[j] > m) m = s[j];
   }
-  double Z = 0.0;
+  real Z = 0;
   for (int j = lo; j < hi; ++j) {
-    double w = exp(s[j] - m);
+    real w = R_EXP(s[j] - m);
     Z += w;
     for (int d = 0; d < D; ++d) o[d] += w * Vd[(size_t)j * D + d];
   }
   for (int d = 0; d < D; ++d) o[d] /= Z;
-  return m + log(Z);
+  return m + R_LOG(Z);
 }
 
 /* Visible key limit of row i of request b. */
@@ -165,11 +182,11 @@ static int run(const or_args *a, int P, int S, double *out, double *part_o,
     used = omp_get_num_threads();
 #endif
     size_t n = (size_t)(max_ctx > 0 ? max_ctx : 1);
-    double *Kd = malloc(n * D * sizeof(double));
-    double *Vd = malloc(n * D * sizeof(double));
-    double *s = malloc(n * sizeof(double));
-    double *q = malloc((size_t)D * sizeof(double));
-    double *o = malloc((size_t)D * sizeof(double));
+    real *Kd = malloc(n * D * sizeof(real));
+    real *Vd = malloc(n * D * sizeof(real));
+    real *s = malloc(n * sizeof(real));
+    real *q = malloc((size_t)D * sizeof(real));
+    real *o = malloc((size_t)D * sizeof(real));
     if (!Kd || !Vd || !s || !q || !o) failed = 1;
 #pragma omp for schedule(dynamic, 1)
     for (int u = 0; u < units; ++u) {
@@ -184,14 +201,15 @@ static int run(const or_args *a, int P, int S, double *out, double *part_o,
           for (int d = 0; d < D; ++d) q[d] = widen(a->q, row * D + d, a->dtype);
           const int hi = row_limit(a, b, i);
           if (P <= 0) {
-            dense_attention(a, q, Kd, Vd, 0, hi, s, out + row * D);
+            dense_attention(a, q, Kd, Vd, 0, hi, s, o);
+            for (int d = 0; d < D; ++d) out[row * D + d] = (double)o[d];
           } else {
             for (int sp = 0; sp < S; ++sp) {
               int lo = sp * P, e = lo + P;
               if (e > hi) e = hi;
-              double lse = dense_attention(a, q, Kd, Vd, lo, e, s, o);
-              part_lse[row * S + sp] = lse;
-              memcpy(part_o + (row * S + sp) * D, o, (size_t)D * sizeof(double));
+              real lse = dense_attention(a, q, Kd, Vd, lo, e, s, o);
+              part_lse[row * S + sp] = (double)lse;
+              for (int d = 0; d < D; ++d) part_o[(row * S + sp) * D + d] = (double)o[d];
             }
           }
         }
@@ -230,22 +248,26 @@ int or_partials(ARGS_DECL, int partition_tokens, int num_splits, int nthreads,
  *   out = sum_s w_s o_s; a row whose partitions are all empty gets 0. */
 int or_merge(const double *part_o, const double *part_lse, long rows, int S, int D,
              double *out) {
+  real *o = malloc((size_t)(D > 0 ? D : 1) * sizeof(real));
+  if (!o) return OR_NOMEM;
   for (long r = 0; r < rows; ++r) {
-    double M = -INFINITY;
+    real M = -R_INF;
     for (int s = 0; s < S; ++s)
-      if (part_lse[r * S + s] > M) M = part_lse[r * S + s];
-    double *o = out + (size_t)r * D;
-    for (int d = 0; d < D; ++d) o[d] = 0.0;
-    if (M == -INFINITY) continue;
-    double Z = 0.0;
-    for (int s = 0; s < S; ++s) Z += exp(part_lse[r * S + s] - M);
-    for (int s = 0; s < S; ++s) {
-      double w = exp(part_lse[r * S + s] - M) / Z;
-      if (w == 0.0) continue;
-      const double *os = part_o + ((size_t)r * S + s) * D;
-      for (int d = 0; d < D; ++d) o[d] += w * os[d];
+      if ((real)part_lse[r * S + s] > M) M = (real)part_lse[r * S + s];
+    for (int d = 0; d < D; ++d) o[d] = 0;
+    if (M != -R_INF) {
+      real Z = 0;
+      for (int s = 0; s < S; ++s) Z += R_EXP((real)part_lse[r * S + s] - M);
+      for (int s = 0; s < S; ++s) {
+        real w = R_EXP((real)part_lse[r * S + s] - M) / Z;
+        if (w == 0) continue;
+        const double *os = part_o + ((size_t)r * S + s) * D;
+        for (int d = 0; d < D; ++d) o[d] += w * (real)os[d];
+      }
     }
+    for (int d = 0; d < D; ++d) out[(size_t)r * D + d] = (double)o[d];
   }
+  free(o);
   return OR_OK;
 }
 

@@ -19,10 +19,10 @@ MUTANTS = {
                         "size_t base = (((size_t)page * a->Hkv + 0) * a->page_size + slot) * (size_t)D;"),
     "value_read_from_keys": ("Vd[(size_t)j * D + d] = widen(a->vp, base + d, a->dtype);",
                              "Vd[(size_t)j * D + d] = widen(a->kp, base + d, a->dtype);"),
-    "scale_dropped": ("s[j] = a->scale * acc;", "s[j] = acc;"),
+    "scale_dropped": ("s[j] = scale * acc;", "s[j] = acc;"),
     "dot_misaligned": ("acc += q[d] * Kd[(size_t)j * D + d];",
                        "acc += q[(d + 1) % D] * Kd[(size_t)j * D + d];"),
-    "exp_sign_flipped": ("double w = exp(s[j] - m);", "double w = exp(m - s[j]);"),
+    "exp_sign_flipped": ("real w = R_EXP(s[j] - m);", "real w = R_EXP(m - s[j]);"),
     "not_normalised": ("for (int d = 0; d < D; ++d) o[d] /= Z;",
                        "for (int d = 0; d < D; ++d) o[d] /= 1.0;"),
     "gqa_strided_groups": ("const int h = g * G + hh;", "const int h = hh * a->Hkv + g;"),
@@ -32,8 +32,8 @@ MUTANTS = {
     "query_lens_ignored": ("static int qlen_of(const or_args *a, int b) { return a->ql ? a->ql[b] : a->L; }",
                            "static int qlen_of(const or_args *a, int b) { return a->L; }"),
     "partitions_overlap": ("int lo = sp * P, e = lo + P;", "int lo = sp * P, e = lo + P + 1;"),
-    "lse_missing_log_sum": ("return m + log(Z);", "return m;"),
-    "merge_unweighted": ("Z += exp(part_lse[r * S + s] - M);", "Z += 1.0;"),
+    "lse_missing_log_sum": ("return m + R_LOG(Z);", "return m;"),
+    "merge_unweighted": ("Z += R_EXP((real)part_lse[r * S + s] - M);", "Z += 1;"),
     "bf16_widen_shift": ("<< 16;", "<< 15;"),
     "trace_past_context": ("if ((int)j < cl[b]) {", "if ((int)j <= cl[b]) {"),
 }
