@@ -96,14 +96,17 @@ typedef struct pa_args {
   int32_t mask;                /* pa_mask */
   float scale;                 /* score scale, finite and > 0 (1/sqrt(D) is usual) */
   /* Debug outputs (NULL in normal use; either one selects the instrumented
-   * kernels).  debug_trace [B, max_pages*page_size, 2] int32 receives, for
-   * every logical key the kernels read, the (physical page, slot) they
-   * computed for it; other entries are left as the caller set them.
-   * debug_visits [B, H_kv, max_pages*page_size] int32 is incremented once
-   * per key each time a workgroup folds it into the softmax state; only the
-   * workgroups whose rows include the last valid query row of the request
-   * count, so a correct walk leaves exactly 1 for j < context_lens[b] and 0
-   * beyond.  The caller zeroes debug_visits. */
+   * kernels: the same staging and load code as the production kernels of
+   * the call, plus the records).  debug_trace [B, max_pages*page_size, 2]
+   * int32 receives, for every logical key the kernels read, the (physical
+   * page, slot) decoded from the address that the load of the key actually
+   * used; other entries are left as the caller set them.  debug_visits [B,
+   * H_kv, max_pages*page_size] int32 is incremented once per key each time
+   * a work item loads it for folding into the softmax state, under the kv
+   * head that the load address points at; only the work items whose rows
+   * include the last valid query row of the request count, so a correct
+   * walk leaves exactly 1 for j < context_lens[b] and 0 beyond.  The caller
+   * zeroes debug_visits. */
   int32_t *debug_trace;
   int32_t *debug_visits;
 } pa_args;

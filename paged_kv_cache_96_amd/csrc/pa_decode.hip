@@ -196,46 +196,48 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
     }
   };
 
-  // Element offset of key n*TPL + kl of step k (st == k).
-  auto key_offset = [&](int k, int st, int n, int &page, int &slot) -> size_t {
-    if constexpr (UNIFORM) {
-      const uint32_t lo = __builtin_amdgcn_readlane(off_lo, k & 63);
-      const uint32_t hi2 = __builtin_amdgcn_readlane(off_hi, k & 63);
-      const size_t base = ((size_t)hi2 << 32) | lo;
-      if constexpr (DEBUG) {
-        const int bj = t0 + st * kStep;
-        page = bt[bj / ps];
-        slot = bj % ps + n * kTpl + kl;
+  // Debug record of logical key j, decoded from the element offset `eoff`
+  // that this lane's load of the key actually uses (its first 16-byte chunk:
+  // c == 0): physical page, slot and kv head follow from the pool layout
+  // [num_pages, H_kv, page_size, D] alone, so the trace observes the address
+  // arithmetic of the walk rather than restating it.  The visit is counted
+  // under the kv head the offset points at.
+  auto record = [&](int j, size_t eoff) {
+    if constexpr (DEBUG) {
+      if (counts && c == 0 && j < t1) {
+        const size_t row = eoff / D;            // (page * H_kv + head) * ps + slot
+        const size_t ph = row / (size_t)ps;     // page * H_kv + head
+        const int slot = (int)(row - ph * ps);
+        const int page = (int)(ph / p.Hkv);
+        const int head = (int)(ph - (size_t)page * p.Hkv);
+        const size_t cap = (size_t)p.max_pages * ps;
+        if (g == 0) {
+          p.dbg_trace[((size_t)b * cap + j) * 2 + 0] = page;
+          p.dbg_trace[((size_t)b * cap + j) * 2 + 1] = slot;
+        }
+        atomicAdd(&p.dbg_visits[((size_t)b * p.Hkv + head) * cap + j], 1);
       }
-      return base + lane_off + (size_t)n * kTpl * D;
     }
-    int j = t0 + st * kStep + n * kTpl + kl;
+  };
+
+  // Element offset of key n*TPL + kl of step k, resolved per lane (page
+  // sizes that are not a multiple of the step).
+  auto key_offset = [&](int k, int n) -> size_t {
+    int j = t0 + k * kStep + n * kTpl + kl;
     j = min(j, t1 - 1);  // keys past the end reuse a valid address; masked below
     const int lp = j / ps;
-    page = bt[lp];
-    slot = j - lp * ps;
+    const int page = bt[lp];
+    const int slot = j - lp * ps;
     return ((size_t)page * p.Hkv + g) * head_stride + (size_t)slot * D + c * kElems;
   };
 
   auto load_step = [&](int k, Vec (&kv)[kLoads], Vec (&vv)[kLoads]) {
-    const int st = k;
 #pragma unroll
     for (int n = 0; n < kLoads; ++n) {
-      int page = 0, slot = 0;
-      const size_t off = key_offset(k, st, n, page, slot);
+      const size_t off = key_offset(k, n);
       kv[n] = load_stream(kp + off);
       vv[n] = load_stream(vp + off);
-      if constexpr (DEBUG) {
-        const int j = t0 + st * kStep + n * kTpl + kl;
-        if (counts && c == 0 && j < t1) {
-          const size_t cap = (size_t)p.max_pages * ps;
-          if (g == 0) {
-            p.dbg_trace[((size_t)b * cap + j) * 2 + 0] = page;
-            p.dbg_trace[((size_t)b * cap + j) * 2 + 1] = slot;
-          }
-          atomicAdd(&p.dbg_visits[((size_t)b * p.Hkv + g) * cap + j], 1);
-        }
-      }
+      record(t0 + k * kStep + n * kTpl + kl, off);
     }
   };
 
@@ -263,19 +265,8 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
       const int boff = (int)((lane_off + n * kTpl * D) * sizeof(T));
       kv[n] = load_stream_buf(rk, boff);
       vv[n] = load_stream_buf(rv, boff);
-      if constexpr (DEBUG) {
-        const int st = k;
-        const int j = t0 + st * kStep + n * kTpl + kl;
-        if (ok && counts && c == 0 && j < t1) {
-          const int bj = t0 + st * kStep;
-          const size_t cap = (size_t)p.max_pages * ps;
-          if (g == 0) {
-            p.dbg_trace[((size_t)b * cap + j) * 2 + 0] = bt[bj / ps];
-            p.dbg_trace[((size_t)b * cap + j) * 2 + 1] = bj % ps + n * kTpl + kl;
-          }
-          atomicAdd(&p.dbg_visits[((size_t)b * p.Hkv + g) * cap + j], 1);
-        }
-      }
+      // the resource base plus the lane's byte offset, in elements
+      if (ok) record(t0 + k * kStep + n * kTpl + kl, base + (size_t)boff / sizeof(T));
     }
   };
 

@@ -61,6 +61,8 @@
 // arrive reads them all back, merges them in piece order (so the result
 // does not depend on the order of arrival) and writes the output.  No
 // workgroup waits for another.
+#include <type_traits>
+
 #include "pa_common.hpp"
 #include "pa_internal.h"
 #include "pa_merge.hpp"
@@ -315,8 +317,9 @@ __device__ void find_piece(const LaunchParams &p, int nt, int *s_ctx, int *s_ql,
   __syncthreads();  // the tables live in the staging buffers
 }
 
-// Staging modes.  kStageLanes: every lane resolves its own key (any page
-// size; debug trace).  kStageRun: page_size a multiple of the run length, one
+// Staging modes (each also has an instrumented build that records the
+// page and slot of every key from the address its load uses).  kStageLanes:
+// every lane resolves its own key (any page size).  kStageRun: page_size a multiple of the run length, one
 // buffer resource per run.  kStagePool: the same runs, with one resource for
 // the whole K (V) pool and the run's position in the SGPR offset (pools
 // under 2 GiB, so that offsets stay below 2^31 and an offset of 2^31 is
@@ -492,6 +495,28 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   const char *vp_bytes = reinterpret_cast<const char *>(p.vp);
   int run_j0 = 0, run_lp = 0, run_slot = 0, run_page = 0;
   int pass = 0;  // 1: the walk again with exact row maxima
+  // Debug record of logical key j, decoded from the byte offset into the
+  // pool that this thread's load of the key's first 16-byte chunk actually
+  // uses: page, kv head and slot follow from the layout [num_pages, H_kv,
+  // page_size, D] alone, so the trace observes the staging's own address
+  // arithmetic.  The visit is counted under the kv head the offset points at.
+  auto record = [&](int j, long long byte) {
+    if constexpr (DEBUG) {
+      const long long head_row = (long long)p.ps * D * 2;  // bytes of one page of one head
+      if (counts && pass == 0 && j < kend_wg && byte % (D * 2) == 0) {
+        const long long ph = byte / head_row;              // page * H_kv + head
+        const int slot = (int)((byte - ph * head_row) / (D * 2));
+        const int page = (int)(ph / p.Hkv);
+        const int head = (int)(ph - (long long)page * p.Hkv);
+        const size_t cap = (size_t)p.max_pages * p.ps;
+        if (g == 0) {
+          p.dbg_trace[((size_t)b * cap + j) * 2 + 0] = page;
+          p.dbg_trace[((size_t)b * cap + j) * 2 + 1] = slot;
+        }
+        atomicAdd(&p.dbg_visits[((size_t)b * p.Hkv + head) * cap + j], 1);
+      }
+    }
+  };
   const int pool_bytes = (int)((long long)p.num_pages * page_bytes);  // kStagePool only
   const __amdgpu_buffer_rsrc_t pool_k = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char *>(kp_bytes), (short)0, pool_bytes, kBufferRsrcWord3);
@@ -538,6 +563,15 @@ prefill_kernel(LaunchParams p, int num_tiles) {
                                                0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t *)(vdst + dst), 16, voff, soff, 0,
                                                0);
+      if constexpr (DEBUG) {
+        // byte offset of this lane's chunk from the pool base: the resource
+        // base (per-run resources) or the scalar offset (pool-wide), plus
+        // the lane offset
+        long long base = soff;
+        if constexpr (MODE == kStageDmaRun)
+          base = (long long)page * page_bytes + head_bytes + (long long)dma_slot * (D * 2);
+        if (live && voff >= 0) record(run0 + 4 * j + dma_row, base + voff);
+      }
     };
     if (run0 + kDmaRows <= kend_wg) {  // wave-uniform: the whole run is live
 #pragma unroll
@@ -566,6 +600,7 @@ prefill_kernel(LaunchParams p, int num_tiles) {
         const int voff = run_j0 + key_in_round < kend_wg ? run_off : (int)0x80000000u;
         const u32x4_t kv = __builtin_amdgcn_raw_buffer_load_b128(pool_k, voff, soff, 0);
         const u32x4_t vv = __builtin_amdgcn_raw_buffer_load_b128(pool_v, voff, soff, 0);
+        if (live && voff >= 0) record(run_j0 + key_in_round, (long long)soff + voff);
         st.k[r] = make_uint4(kv[0], kv[1], kv[2], kv[3]);
         st.v[r] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
         run_j0 += TL::kKeysPerRound;
@@ -586,6 +621,7 @@ prefill_kernel(LaunchParams p, int num_tiles) {
       const int voff = run_j0 + key_in_round < kend_wg ? run_off : 0x40000000;
       const u32x4_t kv = __builtin_amdgcn_raw_buffer_load_b128(rk, voff, 0, 0);
       const u32x4_t vv = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0);
+      if (live && voff != 0x40000000) record(run_j0 + key_in_round, off + voff);
       st.k[r] = make_uint4(kv[0], kv[1], kv[2], kv[3]);
       st.v[r] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
       run_j0 += TL::kKeysPerRound;
@@ -611,16 +647,7 @@ prefill_kernel(LaunchParams p, int num_tiles) {
         const size_t off = (((size_t)page * p.Hkv + g) * p.ps + slot) * D + chunk * 8;
         st.k[r] = *reinterpret_cast<const uint4 *>(kp + off);
         st.v[r] = *reinterpret_cast<const uint4 *>(vp + off);
-        if constexpr (DEBUG) {
-          if (counts && chunk == 0 && pass == 0) {
-            const size_t cap = (size_t)p.max_pages * p.ps;
-            if (g == 0) {
-              p.dbg_trace[((size_t)b * cap + j) * 2 + 0] = page;
-              p.dbg_trace[((size_t)b * cap + j) * 2 + 1] = slot;
-            }
-            atomicAdd(&p.dbg_visits[((size_t)b * p.Hkv + g) * cap + j], 1);
-          }
-        }
+        record(j, (long long)off * 2);
       } else {
         st.k[r] = make_uint4(0, 0, 0, 0);  // never loaded: zeros keep masked math finite
         st.v[r] = make_uint4(0, 0, 0, 0);
@@ -943,27 +970,33 @@ hipError_t launch_rb(const LaunchParams &p, hipStream_t stream) {
   dim3 grid = p.ws_o ? dim3((unsigned)((long long)tiles * p.Hkv * p.B + max(1, p.num_splits / 2)))
                      : dim3((unsigned)((long long)tiles * p.Hkv), p.B);
   const long long pool = (long long)p.num_pages * p.Hkv * p.ps * D * 2;
-  if (p.dbg_trace || p.dbg_visits) {
-    hipLaunchKernelGGL((prefill_kernel<D, true, kStageLanes, RB>), grid, dim3(256), 0, stream, p,
-                       tiles);
-  } else if (p.ps % Tile<D>::kKeysPerRound != 0) {  // runs would straddle pages
-    hipLaunchKernelGGL((prefill_kernel<D, false, kStageLanes, RB>), grid, dim3(256), 0, stream, p,
-                       tiles);
-  } else if (pool < (1ll << 31)) {
-    if constexpr (D == 128 && RB == 1)
-      hipLaunchKernelGGL((prefill_kernel<D, false, kStageDma, RB>), grid, dim3(256), 0, stream, p,
+  // the debug outputs select the instrumented build of the same staging mode
+  const bool debug = p.dbg_trace || p.dbg_visits;
+  auto go = [&](auto dbg) {
+    constexpr bool DBG = decltype(dbg)::value;
+    if (p.ps % Tile<D>::kKeysPerRound != 0) {  // runs would straddle pages
+      hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageLanes, RB>), grid, dim3(256), 0, stream, p,
                          tiles);
-    else
-      hipLaunchKernelGGL((prefill_kernel<D, false, kStagePool, RB>), grid, dim3(256), 0, stream,
-                         p, tiles);
-  } else {
-    if constexpr (D == 128 && RB == 1)
-      hipLaunchKernelGGL((prefill_kernel<D, false, kStageDmaRun, RB>), grid, dim3(256), 0, stream,
-                         p, tiles);
-    else
-      hipLaunchKernelGGL((prefill_kernel<D, false, kStageRun, RB>), grid, dim3(256), 0, stream, p,
-                         tiles);
-  }
+    } else if (pool < (1ll << 31)) {
+      if constexpr (D == 128 && RB == 1)
+        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageDma, RB>), grid, dim3(256), 0, stream, p,
+                           tiles);
+      else
+        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStagePool, RB>), grid, dim3(256), 0, stream,
+                           p, tiles);
+    } else {
+      if constexpr (D == 128 && RB == 1)
+        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageDmaRun, RB>), grid, dim3(256), 0, stream,
+                           p, tiles);
+      else
+        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageRun, RB>), grid, dim3(256), 0, stream, p,
+                           tiles);
+    }
+  };
+  if (debug)
+    go(std::integral_constant<bool, true>());
+  else
+    go(std::integral_constant<bool, false>());
   return hipGetLastError();
 }
 

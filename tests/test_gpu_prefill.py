@@ -23,6 +23,42 @@ def api():
     return a
 
 
+def _expect_trace_visits(x):
+    tr = oracle.translate_of(x)
+    v = expected_visits(x)
+    for b in range(x.B):
+        if x.rows_valid()[b] == 0:
+            tr[b] = -1
+            v[b] = 0
+    return tr, v
+
+
+def _dma_staging(x):
+    """Whether the bf16 prefill loads K/V tiles straight into LDS (D 128 with
+    16-key runs inside a page): the staging of every benchmarked shape."""
+    return x.dtype == "bf16" and x.D == 128 and x.page_size % 16 == 0
+
+
+def _traced_prefill_matches(api, d, x, out, **kw):
+    """The instrumented build of the staging mode that produced `out` records
+    the (page, slot) decoded from the address each key's load used and one
+    visit per key under the kv head that address points at: both equal the
+    oracle's translation exactly.  The LDS-load staging gives the same
+    output bits traced and untraced (and call after call); the register
+    staging modes (D 64, and page sizes that are not a multiple of 16) are
+    not bitwise repeatable from call to call (1-ulp bf16 differences in a
+    few rows whose tile walks two or more key tiles), so there the traced
+    output is held to the oracle instead."""
+    t_out, tex = run_prefill(api, d, trace=True, **kw)
+    tr, v = _expect_trace_visits(x)
+    assert np.array_equal(tex["trace"], tr)
+    assert np.array_equal(tex["visits"], v)
+    if _dma_staging(x):
+        assert np.array_equal(host_f64(t_out), host_f64(out)), "traced output differs"
+    else:
+        assert_parity(t_out, oracle.attention_of(x), x.dtype, "traced (per-lane staging)")
+
+
 CASES = [
     # seed, dtype, D, H_q, H_kv, L, ps, ctx, causal, query_lens
     (1, "bf16", 128, 4, 4, 9, 16, [9, 100], True, None),
@@ -54,29 +90,20 @@ def test_prefill_parity_random_shapes(api, case):
           f"causal={causal} qlens={ql}", flush=True)
     x = make_random(seed, B=len(ctx), H_q=Hq, H_kv=Hkv, L=L, D=D, page_size=ps, ctx=ctx,
                     dtype=dt, causal=causal, query_lens=ql, extra_free_pages=5)
-    out, ex = run_prefill(api, DeviceInputs(x), trace=True)
     ref = oracle.attention_of(x)
-    assert_parity(out, ref, dt, f"prefill case{seed}")
-    if ql is not None:
-        g = host_f64(out)
-        for b, n in enumerate(ql):
-            assert (g[b, :, n:] == 0).all()
-    tr = oracle.translate_of(x)
-    v = expected_visits(x)
-    for b in range(x.B):
-        if x.rows_valid()[b] == 0:
-            tr[b] = -1
-            v[b] = 0
-    assert np.array_equal(ex["trace"], tr)
-    assert np.array_equal(ex["visits"], v)
-    # the same inputs through the fast staging paths (no trace), with the
-    # key split (default plan, and one with pieces as short as allowed) and
-    # without it; the arrival counters are left at zero
+    # the production kernels, with the key split (default plan, and one with
+    # pieces as short as allowed) and without it; the arrival counters are
+    # left at zero; each instrumented run traces the same staging mode
     for kw in (dict(), dict(num_cus=512), dict(split=False)):
-        out2, ex2 = run_prefill(api, DeviceInputs(x), **kw)
-        assert_parity(out2, ref, dt, f"prefill case{seed} fast path {kw}")
-        if "counters" in ex2:
-            assert not ex2["counters"].any()
+        out, ex = run_prefill(api, DeviceInputs(x), **kw)
+        assert_parity(out, ref, dt, f"prefill case{seed} {kw}")
+        if "counters" in ex:
+            assert not ex["counters"].any()
+        if ql is not None:
+            g = host_f64(out)
+            for b, n in enumerate(ql):
+                assert (g[b, :, n:] == 0).all()
+        _traced_prefill_matches(api, DeviceInputs(x), x, out, **kw)
 
 
 def test_prefill_stale_data_and_relabel_bit_identical(api):
@@ -113,12 +140,16 @@ def test_c3_chunked_prefill_full_size(api):
     x = make_c3()
     print(f"[C3] seed={x.seed} ctx={x.context_lens.tolist()}", flush=True)
     ref = oracle.attention_of(x)
+    ref64 = oracle.attention_of(x, precision="f64")
     d = DeviceInputs(x)
     for kw in (dict(), dict(split=False)):
         out, ex = run_prefill(api, d, **kw)
         err = assert_parity(out, ref, "bf16", f"C3 {kw}")
+        assert_parity(out, ref64, "bf16", f"C3 {kw} (fp64 oracle)")
         assert "counters" not in ex or not ex["counters"].any()
         print(f"[C3] {kw} max abs err {err:.3e}", flush=True)
+        _traced_prefill_matches(api, d, x, out, **kw)
+        print(f"[C3] {kw} trace bit-exact", flush=True)
 
 
 def test_key_split_matches_unsplit_and_repeats(api):
@@ -156,6 +187,12 @@ def test_c5_mixed_batch_full_size(api):
     err_d = assert_parity(out_d, oracle.attention_of(m.decode), "bf16", "C5 decode")
     err_p = assert_parity(out_p, oracle.attention_of(m.prefill), "bf16", "C5 prefill")
     print(f"[C5] decode S={ex['S']} err {err_d:.3e}; prefill err {err_p:.3e}", flush=True)
+    t_out, tex = run_decode(api, dec, trace=True)
+    tr, v = _expect_trace_visits(m.decode)
+    assert np.array_equal(tex["trace"], tr) and np.array_equal(tex["visits"], v)
+    assert np.array_equal(host_f64(t_out), host_f64(out_d))
+    _traced_prefill_matches(api, pre, m.prefill, out_p)
+    print("[C5] traces bit-exact", flush=True)
 
 
 def _plant_spike(x, b, j, coef):
@@ -204,22 +241,32 @@ def test_decode_late_score_spike_is_exact(api):
 
 
 @pytest.mark.parametrize("L", [4096, 16384])
-def test_long_prompt_prefill_sampled_rows(api, L):
+def test_long_prompt_prefill_whole_tiles(api, L):
     """The long-prompt causal prefill exactly as it is timed (one request,
-    prefix 0, H 28/4, key-split workspace), checked on windows of query rows.
-    Rows [i0, i0 + k) of the call see the same keys as the call with those k
-    rows alone after a context of i0 + k tokens (bottom-right causal
-    alignment), which the oracle finishes in seconds."""
+    prefix 0, H 28/4, key-split workspace), checked on whole 128-row tiles:
+    the first two, one in the middle and the last two.  A tile holds packed
+    rows 128t .. 128t + 127 (packed row rho = position rho / 7 of head
+    rho % 7 of a kv head), so every head of positions 128t // 7 ..
+    (128t + 127) // 7 is compared; rows [i0, i1) of the call see the same
+    keys as the call with those rows alone after a context of i1 tokens
+    (bottom-right causal alignment), which the oracle finishes in seconds.
+    The instrumented build of the same staging mode traces every key."""
     x = make_random(100 + L, B=1, H_q=28, H_kv=4, L=L, D=128, page_size=16, ctx=[L],
                     dtype="bf16", causal=True, extra_free_pages=16)
     print(f"[long L={L}] seed={x.seed}", flush=True)
-    out, ex = run_prefill(api, DeviceInputs(x))
+    d = DeviceInputs(x)
+    out, ex = run_prefill(api, d)
     assert not ex["counters"].any()
     got = host_f64(out)
     assert np.isfinite(got).all()
-    for i0, k in ((0, 8), (127, 5), (L // 2 - 3, 8), (L - 8, 8)):
-        sub = dataclasses.replace(x, L=k, query=np.ascontiguousarray(x.query[:, :, i0:i0 + k]),
-                                  context_lens=np.array([i0 + k], dtype=np.int32))
+    G = x.H_q // x.H_kv
+    nt = -(-G * L // 128)
+    for t in sorted({0, 1, nt // 2, nt - 2, nt - 1}):
+        i0, i1 = 128 * t // G, min(L, (128 * t + 127) // G + 1)
+        sub = dataclasses.replace(x, L=i1 - i0, query=np.ascontiguousarray(x.query[:, :, i0:i1]),
+                                  context_lens=np.array([i1], dtype=np.int32))
         ref = oracle.attention_of(sub)
-        err = assert_parity(out[:, :, i0:i0 + k], ref, "bf16", f"L={L} rows {i0}..{i0 + k}")
-        print(f"[long L={L}] rows {i0}..{i0 + k} max abs err {err:.3e}", flush=True)
+        err = assert_parity(out[:, :, i0:i1], ref, "bf16", f"L={L} tile {t} rows {i0}..{i1}")
+        print(f"[long L={L}] tile {t}: rows {i0}..{i1} max abs err {err:.3e}", flush=True)
+    _traced_prefill_matches(api, d, x, out)
+    print(f"[long L={L}] trace bit-exact", flush=True)
