@@ -65,11 +65,27 @@ int64_t decode_units(const pa_args *a) {
   return (int64_t)a->num_kv_heads * ((rows + per - 1) / per);
 }
 
-// Largest step count a balanced call over `a` can have.
+// a * b for a, b >= 0, saturating at INT64_MAX.
+int64_t sat_mul(int64_t a, int64_t b) {
+  return (b != 0 && a > INT64_MAX / b) ? INT64_MAX : a * b;
+}
+
+// Largest step count a balanced call over `a` can have (saturating).
 int64_t balanced_max_steps(const pa_args *a) {
   const int64_t step = pa::decode_step_keys(a->head_dim, elem_bytes(a));
   const int64_t cap = (int64_t)a->max_pages * a->page_size;
-  return (int64_t)a->batch * decode_units(a) * ((cap + step - 1) / step + pa::kUnitSetupSteps);
+  return sat_mul(sat_mul((int64_t)a->batch, decode_units(a)),
+                 (cap + step - 1) / step + pa::kUnitSetupSteps);
+}
+
+// Whether the balanced schedule can serve `a`: batch, total steps and the
+// product of row blocks and steps (the wave cap's operand) within bounds.
+bool balanced_fits(const pa_args *a) {
+  if (a->batch > pa::kBalancedMaxBatch) return false;
+  const int64_t T = balanced_max_steps(a);
+  if (T > pa::kBalancedMaxSteps) return false;
+  const int64_t units = (int64_t)(a->batch > 0 ? a->batch : 1) * decode_units(a);
+  return T == 0 || units <= pa::kBalancedMaxUnitSteps / T;
 }
 
 // Workspace consistency for a decode/merge pair.  A single partition needs
@@ -87,8 +103,7 @@ pa_status check_workspace(const pa_args *a, const pa_workspace *ws, int32_t *S, 
   }
   if (ws->schedule == PA_SCHEDULE_BALANCED) {
     // one piece slot per row block plus at least one wave
-    if (a->batch > pa::kBalancedMaxBatch || balanced_max_steps(a) > pa::kBalancedMaxSteps ||
-        (int64_t)ws->num_splits < (int64_t)a->batch * decode_units(a) + 1)
+    if (!balanced_fits(a) || (int64_t)ws->num_splits < (int64_t)a->batch * decode_units(a) + 1)
       return PA_ERR_WORKSPACE;
     *balanced = true;
     *P = 0;
@@ -182,8 +197,7 @@ PA_EXPORT pa_status pa_decode_plan(const pa_args *args, int32_t num_cus, pa_work
   const int cus = num_cus > 0 ? num_cus : 256;
   const int64_t units = (int64_t)(args->batch > 0 ? args->batch : 1) * decode_units(args);
   int32_t S, P;
-  if (plan->partition_tokens <= 0 && args->batch <= pa::kBalancedMaxBatch &&
-      balanced_max_steps(args) <= pa::kBalancedMaxSteps) {
+  if (plan->partition_tokens <= 0 && balanced_fits(args)) {
     // a piece slot per row block plus one per wave of the grid
     const int64_t slots = units + (int64_t)kWavesPerCu * cus;
     if (slots > INT32_MAX) return PA_ERR_INVALID_ARG;

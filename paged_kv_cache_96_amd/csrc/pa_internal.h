@@ -47,6 +47,10 @@ constexpr int kBalancedMaxBatch = 2048;
 // Bound on the total number of steps of a balanced call, so that products of
 // a step index and a wave count stay far inside 64 bits.
 constexpr int64_t kBalancedMaxSteps = int64_t(1) << 40;
+// Bound on (row blocks of the call) x (steps of the call) for the balanced
+// schedule, so that the wave cap's product kBalancedWaveFactor * units * T
+// fits in 64 bits.
+constexpr int64_t kBalancedMaxUnitSteps = int64_t(1) << 60;
 // Shortest run of steps a balanced schedule hands to one wave.
 constexpr int kBalancedMinSteps = 4;
 // Setup cost of a row block in the balanced schedule, in steps: a wave that
@@ -110,8 +114,12 @@ __host__ __device__ inline BalancedSplit balanced_split(int64_t grid_waves, int6
   int64_t w = grid_waves;
   const int64_t by_len = (T + kBalancedMinSteps - 1) / kBalancedMinSteps;
   if (by_len < w) w = by_len;
-  const int64_t by_pieces = isqrt64(kBalancedWaveFactor * units * T);
-  if (by_pieces < w) w = by_pieces;
+  // kBalancedWaveFactor * units * T stays below 2^63 (the host keeps units *
+  // T <= 2^60); were it larger, its root would exceed any grid anyway
+  if (units <= (INT64_MAX / kBalancedWaveFactor) / T) {
+    const int64_t by_pieces = isqrt64(kBalancedWaveFactor * units * T);
+    if (by_pieces < w) w = by_pieces;
+  }
   if (S - units < w) w = S - units;  // S >= units + 1 is checked by the host
   s.Wa = w;
   return s;

@@ -309,3 +309,35 @@ def test_attention_router_validates(L):
     ws = PaWorkspace()
     assert L.pa_attention_plan(ctypes.byref(h.args()), 0, None, None, None) == -1
     assert L.pa_attention_plan(ctypes.byref(h.args()), 0, ctypes.byref(ws), None, None) == 0
+
+
+def test_balanced_plan_refused_where_wave_cap_product_could_overflow(L):
+    """The balanced split's wave cap squares (row blocks) x (steps) x 4; the
+    plan keeps that product inside 64 bits by taking the partition schedule
+    for calls whose row blocks times steps pass 2^60 (huge kv-head counts
+    here), and a workspace that asks for the balanced schedule on such a
+    call is refused."""
+    a = PaArgs()
+    a.batch, a.num_q_heads, a.num_kv_heads, a.q_len, a.head_dim = 2048, 1 << 20, 1 << 20, 1, 128
+    a.num_pages, a.page_size, a.max_pages = 1 << 20, 16, 1 << 16
+    a.dtype, a.mask, a.scale = _lib.PA_DTYPE_BF16, _lib.PA_MASK_CAUSAL, 0.1
+    ws = PaWorkspace()
+    nbytes = ctypes.c_size_t(0)
+    assert L.pa_decode_plan(ctypes.byref(a), 0, ctypes.byref(ws), ctypes.byref(nbytes)) == 0
+    assert ws.schedule == SCHEDULE_PARTITIONS
+    # a shape just inside the bound still gets the balanced plan
+    a.num_q_heads = a.num_kv_heads = 8
+    a.max_pages = 256
+    ws = PaWorkspace()
+    assert L.pa_decode_plan(ctypes.byref(a), 0, ctypes.byref(ws), ctypes.byref(nbytes)) == 0
+    assert ws.schedule == SCHEDULE_BALANCED
+    # forcing the balanced schedule onto the huge shape is refused before any launch
+    a.num_q_heads = a.num_kv_heads = 1 << 20
+    a.max_pages = 1 << 16
+    fake = 1 << 20  # aligned, never dereferenced: validation fails first
+    for f in ("query", "key_pages", "value_pages", "block_table", "context_lens", "out"):
+        setattr(a, f, fake)
+    bad = PaWorkspace()
+    bad.schedule, bad.num_splits, bad.partial_out, bad.partial_lse = SCHEDULE_BALANCED, 1 << 30, fake, fake
+    assert L.pa_decode(ctypes.byref(a), ctypes.byref(bad), None) == _lib.PA_ERR_WORKSPACE
+
