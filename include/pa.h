@@ -63,14 +63,16 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 6
+#define PA_ABI_VERSION 7
 
 typedef enum {
   PA_OK = 0,
   PA_ERR_INVALID_ARG = -1,  /* null pointer, bad size, bad scale/mask, misalignment */
   PA_ERR_UNSUPPORTED = -2,  /* head_dim or dtype outside what the kernels implement */
   PA_ERR_WORKSPACE = -3,    /* split workspace missing, too small or inconsistent */
-  PA_ERR_HIP = -4           /* the HIP runtime refused a launch */
+  PA_ERR_HIP = -4,          /* the HIP runtime refused a launch */
+  PA_ERR_SCRATCH = -5       /* pa_decode_noalloc: the call needs more than the
+                               library scratch holds */
 } pa_status;
 
 typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
@@ -285,6 +287,29 @@ typedef struct pa_append_args {
  * PA_ERR_INVALID_ARG: a NULL or misaligned pointer, a size out of range, or a
  * pool of 2^31 slots or more; PA_ERR_UNSUPPORTED: head_dim or dtype. */
 pa_status pa_append(const pa_append_args *args, void *stream);
+
+/* -------------------------------------------------------- no allocation
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * pa_decode_noalloc is pa_decode with the plan pa_decode_plan chooses for
+ * `args` (num_cus 0) -- which must be the balanced schedule -- and the merge
+ * fused in the kernel, but its partial states and arrival counters live in
+ * a library-owned device array of 32 MiB per device, held from the first
+ * call on a device until the process ends.  It allocates nothing, calls no
+ * hipMalloc/hipFree, and enqueues kernels only on `stream`: on the first
+ * call on a device it looks the array up and enqueues a fill kernel that
+ * clears the counters (every call leaves them zero afterwards); then the
+ * decode kernel.  The caller passes inputs and outputs as for pa_decode.
+ * Limits: at most 65536 row blocks (batch * H_kv * ceil(G * L / R), R as
+ * for the balanced schedule) and piece states (num_splits * R * (head_dim
+ * + 1) * 4 bytes, ~3.2 MB for 64 requests with H_q 32, H_kv 8, D 128) that
+ * fit in the rest of the array; a call beyond them, or one whose plan is
+ * the partition schedule (batch above 2048), returns PA_ERR_SCRATCH and
+ * enqueues nothing.  All calls on one GPU share that GPU's array: calls
+ * that overlap in time on one GPU (different streams without ordering, or
+ * different host threads) race and give undefined results. */
+pa_status pa_decode_noalloc(const pa_args *args, void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *pa_status_string(int32_t status);

@@ -16,6 +16,7 @@ PA_ERR_INVALID_ARG = -1
 PA_ERR_UNSUPPORTED = -2
 PA_ERR_WORKSPACE = -3
 PA_ERR_HIP = -4
+PA_ERR_SCRATCH = -5
 
 PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
@@ -23,8 +24,8 @@ PA_MASK_NONE = 0
 PA_MASK_CAUSAL = 1
 
 EXPORTED = ("pa_decode_plan", "pa_decode", "pa_split_reduce", "pa_prefill_plan", "pa_prefill",
-            "pa_attention_plan", "pa_attention", "pa_append", "pa_status_string",
-            "pa_abi_version")
+            "pa_attention_plan", "pa_attention", "pa_append", "pa_decode_noalloc",
+            "pa_status_string", "pa_abi_version")
 
 
 class PaArgs(ctypes.Structure):
@@ -80,7 +81,7 @@ class PaAppendArgs(ctypes.Structure):
     ]
 
 
-ABI_VERSION = 6  # PA_ABI_VERSION of the structs below
+ABI_VERSION = 7  # PA_ABI_VERSION of the structs below
 
 ROUTE_DECODE = 0
 ROUTE_PREFILL = 1
@@ -126,6 +127,8 @@ def lib() -> ctypes.CDLL:
     L.pa_attention.restype = ctypes.c_int
     L.pa_append.argtypes = [ctypes.POINTER(PaAppendArgs), ctypes.c_void_p]
     L.pa_append.restype = ctypes.c_int
+    L.pa_decode_noalloc.argtypes = [A, ctypes.c_void_p]
+    L.pa_decode_noalloc.restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int32]
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_abi_version.argtypes = []

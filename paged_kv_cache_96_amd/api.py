@@ -186,6 +186,13 @@ def pa_decode(args: PaArgs, workspace: Optional[Workspace] = None, stream=None) 
     _lib.check("pa_decode", _lib.lib().pa_decode(ctypes.byref(args), ws, _stream(stream)))
 
 
+def pa_decode_noalloc(args: PaArgs, stream=None) -> None:
+    """pa_decode (balanced schedule, fused merge) with the library's own
+    scratch in place of a workspace: allocates nothing."""
+    _lib.check("pa_decode_noalloc", _lib.lib().pa_decode_noalloc(ctypes.byref(args),
+                                                                  _stream(stream)))
+
+
 def pa_split_reduce(args: PaArgs, workspace: Workspace, stream=None) -> None:
     _lib.check("pa_split_reduce", _lib.lib().pa_split_reduce(ctypes.byref(args),
                                                               ctypes.byref(workspace.c),

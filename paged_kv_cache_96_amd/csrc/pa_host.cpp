@@ -5,7 +5,9 @@
 #include <stdint.h>
 #include <string.h>
 
-#include <hip/hip_runtime_api.h>
+#include <mutex>
+
+#include <hip/hip_runtime.h>
 
 #include "pa.h"
 #include "pa_internal.h"
@@ -182,6 +184,8 @@ PA_EXPORT const char *pa_status_string(int32_t status) {
     case PA_ERR_UNSUPPORTED: return "unsupported head_dim or dtype";
     case PA_ERR_WORKSPACE: return "split workspace missing or inconsistent";
     case PA_ERR_HIP: return "HIP runtime error";
+    case PA_ERR_SCRATCH:
+      return "call needs more than the library scratch of pa_decode_noalloc holds";
     default: return "unknown status";
   }
 }
@@ -395,4 +399,86 @@ PA_EXPORT pa_status pa_append(const pa_append_args *args, void *stream) {
   p.num_slots = a->num_pages * a->page_size;
   p.row_bytes = a->head_dim * (a->dtype == PA_DTYPE_F32 ? 4 : 2);
   return hip_status(pa::launch_append(p, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------------- no allocation
+// pa_decode_noalloc: pa_decode with the balanced schedule and the fused
+// merge, whose partial states and arrival counters live in a library-owned
+// device array instead of a caller workspace.  Layout of `scratch`: the
+// arrival counters (kScratchCounters uint32), then the pieces' log-sum-exps
+// (S x R fp32), then their partial outputs (S x R x D fp32), each region
+// starting on a 256-byte boundary.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(32) << 20;  // 32 MiB per device
+constexpr int64_t kScratchCounters = int64_t(1) << 16;
+constexpr size_t kScratchCounterBytes = size_t(kScratchCounters) * 4;
+
+// In host code `scratch` names a host-side stand-in, not device memory: the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+__global__ void zero_u32(uint32_t *p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {nullptr};
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// The current device's copy of `scratch`.  The first call on a device looks
+// its address up (that device current) and enqueues a fill kernel that
+// clears the counters on `stream` (kernels leave them zero after every
+// call, so one clearing is enough; a fill kernel rather than a memset keeps
+// the call capturable).
+pa_status scratch_of_device(hipStream_t stream, unsigned char **base) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return PA_ERR_HIP;
+    hipLaunchKernelGGL(zero_u32, dim3(64), dim3(256), 0, stream, static_cast<uint32_t *>(p),
+                       kScratchCounters);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *base = static_cast<unsigned char *>(g_scratch[dev]);
+  return PA_OK;
+}
+
+}  // namespace
+
+PA_EXPORT pa_status pa_decode_noalloc(const pa_args *args, void *stream) {
+  pa_status st = check_sizes(args);
+  if (st != PA_OK) return st;
+  if (args->q_len > 8) return PA_ERR_INVALID_ARG;
+  if (args->batch == 0) return PA_OK;
+  if ((st = check_pointers(args)) != PA_OK) return st;
+  pa_workspace ws;
+  memset(&ws, 0, sizeof ws);
+  size_t state_bytes = 0;
+  if ((st = pa_decode_plan(args, 0, &ws, &state_bytes)) != PA_OK) return st;
+  // the balanced schedule with its fused merge is the only plan the scratch
+  // serves; its size must fit
+  if (ws.schedule != PA_SCHEDULE_BALANCED) return PA_ERR_SCRATCH;
+  const size_t rows = (size_t)decode_block_rows(args);
+  const size_t lse_bytes = round256((size_t)ws.num_splits * rows * sizeof(float));
+  const size_t out_bytes = (size_t)ws.num_splits * rows * args->head_dim * sizeof(float);
+  if ((int64_t)ws.num_counters > kScratchCounters ||
+      kScratchCounterBytes + lse_bytes + out_bytes > kScratchBytes)
+    return PA_ERR_SCRATCH;
+  (void)state_bytes;
+  unsigned char *base = nullptr;
+  if ((st = scratch_of_device((hipStream_t)stream, &base)) != PA_OK) return st;
+  ws.counters = reinterpret_cast<uint32_t *>(base);
+  ws.partial_lse = reinterpret_cast<float *>(base + kScratchCounterBytes);
+  ws.partial_out = reinterpret_cast<float *>(base + kScratchCounterBytes + lse_bytes);
+  return pa_decode(args, &ws, stream);
 }

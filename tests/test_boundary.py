@@ -41,7 +41,7 @@ def test_header_and_library_exports_agree(L):
     assert exported == declared
     for name in declared:
         assert hasattr(L, name)
-    assert L.pa_abi_version() == 6
+    assert L.pa_abi_version() == 7
 
 
 def test_status_strings(L):
@@ -341,3 +341,24 @@ def test_balanced_plan_refused_where_wave_cap_product_could_overflow(L):
     bad.schedule, bad.num_splits, bad.partial_out, bad.partial_lse = SCHEDULE_BALANCED, 1 << 30, fake, fake
     assert L.pa_decode(ctypes.byref(a), ctypes.byref(bad), None) == _lib.PA_ERR_WORKSPACE
 
+
+def test_noalloc_refuses_calls_beyond_its_scratch(L):
+    """pa_decode_noalloc checks its scratch bound before touching the GPU:
+    too many row blocks or piece states, or a plan that is not the balanced
+    schedule, return PA_ERR_SCRATCH with nothing enqueued."""
+    a = PaArgs()
+    fake = 1 << 20
+    for f in ("query", "key_pages", "value_pages", "block_table", "context_lens", "out"):
+        setattr(a, f, fake)
+    a.num_pages, a.page_size, a.max_pages = 1 << 16, 16, 4096
+    a.dtype, a.mask, a.scale = _lib.PA_DTYPE_BF16, _lib.PA_MASK_CAUSAL, 0.1
+    # 2048 requests x 64 kv heads = 131072 row blocks > 65536 counters
+    a.batch, a.num_q_heads, a.num_kv_heads, a.q_len, a.head_dim = 2048, 256, 64, 1, 128
+    assert L.pa_decode_noalloc(ctypes.byref(a), None) == _lib.PA_ERR_SCRATCH
+    # more than 2048 requests: the plan is the partition schedule
+    a.batch, a.num_q_heads, a.num_kv_heads = 4096, 8, 1
+    assert L.pa_decode_noalloc(ctypes.byref(a), None) == _lib.PA_ERR_SCRATCH
+    assert "scratch" in _lib.status_string(_lib.PA_ERR_SCRATCH)
+    # argument errors come first, as for pa_decode
+    a.q_len = 9
+    assert L.pa_decode_noalloc(ctypes.byref(a), None) == _lib.PA_ERR_INVALID_ARG
