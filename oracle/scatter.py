@@ -5,7 +5,7 @@ INFRASTRUCTURE ONLY (imported by tests, never by the product path).
 new token a flat physical slot, physical page * page_size + offset in the
 page, and copies the token's key and value rows there; the read path gathers
 them back through the block table.  The slots come from the runtime's page
-ledger (``ledger.PagedCache.slot_mapping``: anllm "Tutorial 13" section 4, the
+ledger (``ledger.RequestPages.slot_mapping``: anllm "Tutorial 13" section 4, the
 request cache's append; tiny-llm "Week 3 Day 4", "Decode Metadata").
 
 This is the definition written out, one token at a time: no batching, no

@@ -7,7 +7,7 @@ page pool driven by the ledger's own placement.
 import numpy as np
 from scipy.special import softmax
 
-from oracle.ledger import PagePool, PagedCache
+from oracle.ledger import PageAllocator, RequestPages
 
 
 def dense_attention_rows(q, K, V, scale, visible):
@@ -29,15 +29,15 @@ def scatter_with_ledger(rng, dense_k, dense_v, page_size, num_pages_extra, garba
                         appends=None):
     """Place per-request dense K/V [B][H_kv, n_b, D] into a page pool.
 
-    Token placement comes from ``PagedCache(policy="fill_tail")`` appends (one
+    Token placement comes from ``RequestPages(policy="fill_tail")`` appends (one
     cache per request, one shared pool); physical ids are then relabelled by a
     seeded permutation of the pool.  Returns (key_pages, value_pages,
     block_table, context_lens) with garbage in every unwritten slot.
     """
     B = len(dense_k)
     Hkv, D = dense_k[0].shape[0], dense_k[0].shape[2]
-    pool = PagePool(page_size)
-    caches = [PagedCache(pool, "fill_tail") for _ in range(B)]
+    pool = PageAllocator(page_size)
+    caches = [RequestPages(pool, "fill_tail") for _ in range(B)]
     placements = [[] for _ in range(B)]
     # interleave requests' appends so their pages are not contiguous
     for b in range(B):
@@ -52,12 +52,12 @@ def scatter_with_ledger(rng, dense_k, dense_v, page_size, num_pages_extra, garba
         for b in range(B):
             if pending[b]:
                 placements[b].extend(caches[b].append(pending[b].pop(0)))
-    used = pool.num_allocated_pages
+    used = pool.fresh_count
     num_pages = used + num_pages_extra
     relabel = rng.permutation(num_pages)
     kp = np.full((num_pages, Hkv, page_size, D), garbage, dtype=np.float64)
     vp = np.full((num_pages, Hkv, page_size, D), garbage, dtype=np.float64)
-    max_pages = max(1, max(len(c.page_ids) for c in caches))
+    max_pages = max(1, max(len(c.pages) for c in caches))
     bt = np.full((B, max_pages), -1, dtype=np.int32)
     for b in range(B):
         for t, (page, slot) in enumerate(placements[b]):

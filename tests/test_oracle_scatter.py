@@ -24,7 +24,7 @@ import numpy as np
 import pytest
 
 from oracle import scatter as oracle_scatter
-from oracle.ledger import PagePool, PagedCache
+from oracle.ledger import PageAllocator, RequestPages
 
 GARBAGE = 1.0e4
 
@@ -40,7 +40,7 @@ def pin_walkthrough_pages(scatter, golden_dir):
     ps, Hkv, D = g["page_size"], 2, 8
     kp = np.full((4, Hkv, ps, D), GARBAGE, np.float32)
     vp = kp.copy()
-    cache = PagedCache(PagePool(ps), policy="walkthrough")
+    cache = RequestPages(PageAllocator(ps), policy="walkthrough")
     rng = np.random.default_rng(11)
     k_all, v_all = [], []
     for n in g["appends"]:
@@ -63,8 +63,8 @@ def pin_walkthrough_pages(scatter, golden_dir):
 def pin_gather_returns_tokens(scatter, seed=0):
     rng = np.random.default_rng(seed)
     ps, Hkv, D, P = 4, 3, 8, 40
-    pool = PagePool(ps)
-    caches = [PagedCache(pool) for _ in range(3)]
+    pool = PageAllocator(ps)
+    caches = [RequestPages(pool) for _ in range(3)]
     kp = np.full((P, Hkv, ps, D), GARBAGE, np.float32)
     vp = kp.copy()
     hist = {i: ([], []) for i in range(3)}
