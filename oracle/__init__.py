@@ -78,7 +78,8 @@ def load(path: str = _LIB) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i = ctypes.c_int
-    common = [P, P, P, P, P, P, i, i, i, i, i, i, i, i, i, i, ctypes.c_double]
+    d = ctypes.c_double
+    common = [P, P, P, P, P, P, i, i, i, i, i, i, i, i, i, i, d, i, d, d]
     lib.or_attention.argtypes = common + [i, P, P]
     lib.or_attention.restype = i
     lib.or_partials.argtypes = common + [i, i, i, P, P]
@@ -87,6 +88,8 @@ def load(path: str = _LIB) -> ctypes.CDLL:
     lib.or_merge.restype = i
     lib.or_translate.argtypes = [P, P, i, i, i, i, P]
     lib.or_translate.restype = i
+    lib.or_e4m3_values.argtypes = [P, ctypes.c_long, P]
+    lib.or_e4m3_values.restype = i
     _lib_cache[path] = lib
     return lib
 
@@ -99,15 +102,27 @@ def default_threads() -> int:
     return max(1, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count() or 1)
 
 
+_DTYPE_CODES = {"f32": 0, "bf16": 1, "fp8_e4m3": 2}
+
+
 class _Prepared:
-    """Contiguous copies of the inputs with the dtypes the C code expects."""
+    """Contiguous copies of the inputs with the dtypes the C code expects.
+    `kv_dtype` (None: the pages share `dtype`) may be "fp8_e4m3": the pages
+    then hold uint8 codes whose values are scaled by k_scale / v_scale."""
 
     def __init__(self, query, key_pages, value_pages, block_table, context_lens,
-                 query_lens, page_size, dtype, causal, scale):
+                 query_lens, page_size, dtype, causal, scale, kv_dtype=None, k_scale=1.0,
+                 v_scale=1.0):
         fp = np.float32 if dtype == "f32" else np.uint16
+        kv_dtype = kv_dtype or dtype
+        if kv_dtype not in _DTYPE_CODES or dtype not in ("f32", "bf16"):
+            raise ValueError(f"unsupported dtype {dtype!r} / kv_dtype {kv_dtype!r}")
+        kfp = {"f32": np.float32, "bf16": np.uint16, "fp8_e4m3": np.uint8}[kv_dtype]
         self.q = np.ascontiguousarray(query, dtype=fp)
-        self.kp = np.ascontiguousarray(key_pages, dtype=fp)
-        self.vp = np.ascontiguousarray(value_pages, dtype=fp)
+        self.kp = np.ascontiguousarray(key_pages, dtype=kfp)
+        self.vp = np.ascontiguousarray(value_pages, dtype=kfp)
+        self.kv_code = _DTYPE_CODES[kv_dtype]
+        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
         self.bt = np.ascontiguousarray(block_table, dtype=np.int32)
         self.cl = np.ascontiguousarray(context_lens, dtype=np.int32)
         self.ql = None if query_lens is None else np.ascontiguousarray(query_lens, dtype=np.int32)
@@ -126,18 +141,20 @@ class _Prepared:
         B, Hq, Hkv, L, D, P, ps, mp = self.dims
         return [_ptr(self.q), _ptr(self.kp), _ptr(self.vp), _ptr(self.bt), _ptr(self.cl),
                 _ptr(self.ql), B, Hq, Hkv, L, D, P, ps, mp, self.dtype_code, self.causal,
-                self.scale]
+                self.scale, self.kv_code, self.k_scale, self.v_scale]
 
 
 def attention(query, key_pages, value_pages, block_table, context_lens, page_size, *,
               dtype: str, causal: bool, scale: float, query_lens=None,
               nthreads: Optional[int] = None, lib_path: Optional[str] = None,
-              precision: str = "f32", return_threads: bool = False):
+              precision: str = "f32", return_threads: bool = False,
+              kv_dtype: Optional[str] = None, k_scale: float = 1.0, v_scale: float = 1.0):
     """Paged attention by the plain definition; float64 array [B, H_q, L, D]
-    holding the results of the `precision` build (`lib_path` overrides it)."""
+    holding the results of the `precision` build (`lib_path` overrides it).
+    kv_dtype "fp8_e4m3": uint8 pages dequantised with k_scale / v_scale."""
     lib_path = lib_path or lib_for(precision)
     prep = _Prepared(query, key_pages, value_pages, block_table, context_lens, query_lens,
-                     page_size, dtype, causal, scale)
+                     page_size, dtype, causal, scale, kv_dtype, k_scale, v_scale)
     B, Hq, Hkv, L, D = prep.dims[:5]
     out = np.zeros((B, Hq, L, D), dtype=np.float64)
     used = ctypes.c_int(0)
@@ -151,13 +168,14 @@ def attention(query, key_pages, value_pages, block_table, context_lens, page_siz
 def partials(query, key_pages, value_pages, block_table, context_lens, page_size, *,
              dtype: str, causal: bool, scale: float, partition_tokens: int, num_splits: int,
              query_lens=None, nthreads: Optional[int] = None,
-             lib_path: Optional[str] = None,
-             precision: str = "f32") -> Tuple[np.ndarray, np.ndarray]:
+             lib_path: Optional[str] = None, precision: str = "f32",
+             kv_dtype: Optional[str] = None, k_scale: float = 1.0,
+             v_scale: float = 1.0) -> Tuple[np.ndarray, np.ndarray]:
     """Per-partition (o, lse) states: [B,H_q,L,S,D] and [B,H_q,L,S] (float64
     arrays of the `precision` build's results)."""
     lib_path = lib_path or lib_for(precision)
     prep = _Prepared(query, key_pages, value_pages, block_table, context_lens, query_lens,
-                     page_size, dtype, causal, scale)
+                     page_size, dtype, causal, scale, kv_dtype, k_scale, v_scale)
     B, Hq, Hkv, L, D = prep.dims[:5]
     S = int(num_splits)
     po = np.zeros((B, Hq, L, S, D), dtype=np.float64)
@@ -198,8 +216,19 @@ def translate(block_table, context_lens, page_size: int, num_pages: int,
     return tr
 
 
+def e4m3_values(codes, lib_path: Optional[str] = None) -> np.ndarray:
+    """Values of fp8 E4M3 codes as the C oracle decodes them (float64)."""
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.zeros(c.shape, dtype=np.float64)
+    load(lib_path or _LIB).or_e4m3_values(_ptr(c), c.size, _ptr(out))
+    return out
+
+
 def _kw(x):
-    return dict(dtype=x.dtype, causal=x.causal, scale=x.scale, query_lens=x.query_lens)
+    kw = dict(dtype=x.dtype, causal=x.causal, scale=x.scale, query_lens=x.query_lens)
+    if getattr(x, "kv_dtype", None):
+        kw.update(kv_dtype=x.kv_dtype, k_scale=x.k_scale, v_scale=x.v_scale)
+    return kw
 
 
 def attention_of(x, **kw):

@@ -50,7 +50,7 @@ enum {
   OR_BAD_QLEN = 4,    /* query_lens[b] < 0, > L, or (causal) > context_lens[b] */
   OR_NOMEM = 5
 };
-enum { OR_F32 = 0, OR_BF16 = 1 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8E4M3 = 2 };
 
 #ifdef OR_SINGLE
 typedef float real;
@@ -69,6 +69,8 @@ typedef struct {
   const int32_t *bt, *cl, *ql;
   int B, Hq, Hkv, L, D, num_pages, page_size, max_pages, dtype, causal;
   double scale;
+  int kv_dtype;            /* element type of the pages: OR_F32, OR_BF16 or OR_FP8E4M3 */
+  double k_scale, v_scale; /* fp8 pages: stored code times scale is the value */
 } or_args;
 
 static real widen(const void *base, size_t idx, int dtype) {
@@ -77,6 +79,29 @@ static real widen(const void *base, size_t idx, int dtype) {
   float f;
   memcpy(&f, &bits, sizeof f);
   return (real)f;
+}
+
+/* Value of an 8-bit float in the OCP E4M3 encoding ("Reading vLLM's
+ * PagedAttention Kernel", section 3.2: the cache write takes a kv-cache dtype
+ * and per-tensor k/v scales; the reading of the fp8 variant is the OCP
+ * 8-bit format with 4 exponent and 3 mantissa bits): bit 7 sign, bits 6..3
+ * exponent e with bias 7, bits 2..0 mantissa m.  e >= 1 is the normal value
+ * (1 + m/8) 2^(e-7); e = 0 is the subnormal value (m/8) 2^-6; the pattern
+ * with every exponent and mantissa bit set is NaN, and there is no
+ * infinity. */
+static real e4m3_value(uint8_t code) {
+  const int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return (real)NAN;
+  const real mag = e == 0 ? (real)ldexp((double)m, -9) : (real)ldexp((double)(8 + m), e - 10);
+  return sign ? -mag : mag;
+}
+
+/* Element idx of a page pool: its stored value, dequantised for fp8 pages
+ * (code value times the pool's scale). */
+static real page_value(const or_args *a, const void *pool, size_t idx, double kv_scale) {
+  if (a->kv_dtype == OR_FP8E4M3)
+    return e4m3_value(((const uint8_t *)pool)[idx]) * (real)kv_scale;
+  return widen(pool, idx, a->kv_dtype);
 }
 
 static int qlen_of(const or_args *a, int b) { return a->ql ? a->ql[b] : a->L; }
@@ -89,6 +114,11 @@ static int check(const or_args *a) {
     return OR_BAD_SHAPE;
   if (a->Hq % a->Hkv != 0) return OR_BAD_SHAPE;
   if (!(a->scale > 0.0) || !isfinite(a->scale)) return OR_BAD_SHAPE;
+  if (a->kv_dtype != OR_F32 && a->kv_dtype != OR_BF16 && a->kv_dtype != OR_FP8E4M3)
+    return OR_BAD_SHAPE;
+  if (a->kv_dtype == OR_FP8E4M3 && (!(a->k_scale > 0.0) || !isfinite(a->k_scale) ||
+                                    !(a->v_scale > 0.0) || !isfinite(a->v_scale)))
+    return OR_BAD_SHAPE;
   for (int b = 0; b < a->B; ++b) {
     int ctx = a->cl[b];
     if (ctx < 0 || (int64_t)ctx > (int64_t)a->max_pages * a->page_size) return OR_BAD_CTX;
@@ -119,8 +149,8 @@ static void gather_dense(const or_args *a, int b, int g, real *Kd, real *Vd) {
     translate(a, b, j, &page, &slot);
     size_t base = (((size_t)page * a->Hkv + g) * a->page_size + slot) * (size_t)D;
     for (int d = 0; d < D; ++d) {
-      Kd[(size_t)j * D + d] = widen(a->kp, base + d, a->dtype);
-      Vd[(size_t)j * D + d] = widen(a->vp, base + d, a->dtype);
+      Kd[(size_t)j * D + d] = page_value(a, a->kp, base + d, a->k_scale);
+      Vd[(size_t)j * D + d] = page_value(a, a->vp, base + d, a->v_scale);
     }
   }
 }
@@ -224,10 +254,11 @@ static int run(const or_args *a, int P, int S, double *out, double *part_o,
 #define ARGS_DECL                                                                      \
   const void *q, const void *kp, const void *vp, const int32_t *bt, const int32_t *cl, \
       const int32_t *ql, int B, int Hq, int Hkv, int L, int D, int num_pages,          \
-      int page_size, int max_pages, int dtype, int causal, double scale
+      int page_size, int max_pages, int dtype, int causal, double scale, int kv_dtype,   \
+      double k_scale, double v_scale
 #define ARGS_INIT                                                                     \
   or_args a = {q, kp, vp, bt, cl, ql, B, Hq, Hkv, L, D, num_pages, page_size, max_pages, \
-               dtype, causal, scale}
+               dtype, causal, scale, kv_dtype, k_scale, v_scale}
 
 /* Full attention: out[B][Hq][L][D] (double). */
 int or_attention(ARGS_DECL, int nthreads, int *threads_used, double *out) {
@@ -279,6 +310,7 @@ int or_translate(const int32_t *bt, const int32_t *cl, int B, int max_pages, int
   memset(&a, 0, sizeof a);
   a.bt = bt; a.cl = cl; a.B = B; a.max_pages = max_pages; a.page_size = page_size;
   a.num_pages = num_pages; a.Hq = a.Hkv = a.L = a.D = 1; a.scale = 1.0;
+  a.kv_dtype = OR_F32;
   int rc = check(&a);
   if (rc) return rc;
   const size_t cap = (size_t)max_pages * page_size;
@@ -293,5 +325,11 @@ int or_translate(const int32_t *bt, const int32_t *cl, int B, int max_pages, int
         t[0] = -1; t[1] = -1;
       }
     }
+  return OR_OK;
+}
+
+/* The value of each of n fp8 E4M3 codes (for pins of the decoder). */
+int or_e4m3_values(const uint8_t *codes, long n, double *out) {
+  for (long i = 0; i < n; ++i) out[i] = (double)e4m3_value(codes[i]);
   return OR_OK;
 }

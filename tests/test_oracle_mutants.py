@@ -8,6 +8,7 @@ import os
 import pytest
 
 import oracle
+from tests import test_oracle_fp8 as fp8
 from tests import test_oracle_pins as pins
 
 MUTANTS = {
@@ -17,8 +18,15 @@ MUTANTS = {
                            "*page = a->bt[(size_t)b * a->max_pages + (lp > 0 ? lp - 1 : 0)];"),
     "kv_head_ignored": ("size_t base = (((size_t)page * a->Hkv + g) * a->page_size + slot) * (size_t)D;",
                         "size_t base = (((size_t)page * a->Hkv + 0) * a->page_size + slot) * (size_t)D;"),
-    "value_read_from_keys": ("Vd[(size_t)j * D + d] = widen(a->vp, base + d, a->dtype);",
-                             "Vd[(size_t)j * D + d] = widen(a->kp, base + d, a->dtype);"),
+    "value_read_from_keys": ("Vd[(size_t)j * D + d] = page_value(a, a->vp, base + d, a->v_scale);",
+                             "Vd[(size_t)j * D + d] = page_value(a, a->kp, base + d, a->v_scale);"),
+    "fp8_bias_off_by_one": ("(real)ldexp((double)(8 + m), e - 10)",
+                            "(real)ldexp((double)(8 + m), e - 9)"),
+    "fp8_subnormal_as_normal": ("e == 0 ? (real)ldexp((double)m, -9)",
+                                "e == 0 ? (real)ldexp((double)(8 + m), -10)"),
+    "fp8_nan_as_number": ("if (e == 15 && m == 7) return (real)NAN;", ""),
+    "fp8_value_scale_swapped": ("Vd[(size_t)j * D + d] = page_value(a, a->vp, base + d, a->v_scale);",
+                                "Vd[(size_t)j * D + d] = page_value(a, a->vp, base + d, a->k_scale);"),
     "scale_dropped": ("s[j] = scale * acc;", "s[j] = acc;"),
     "dot_misaligned": ("acc += q[d] * Kd[(size_t)j * D + d];",
                        "acc += q[(d + 1) % D] * Kd[(size_t)j * D + d];"),
@@ -48,6 +56,8 @@ BATTERY = [
     ("p8_lower_tri", lambda lib, gd: pins.test_p8_full_causal_is_lower_triangular_textbook(lib_path=lib)),
     ("p8_qlen", lambda lib, gd: pins.test_p8_noncausal_rows_see_whole_context_and_qlen_padding_is_zero(lib_path=lib)),
     ("p10_split", lambda lib, gd: pins.test_p10_split_merge_equals_unsplit(12, lib_path=lib)),
+    ("fp8_codes", lambda lib, gd: fp8.test_fp8_decoder_hand_derived_codes(lib_path=lib)),
+    ("fp8_dense", lambda lib, gd: fp8.test_fp8_pages_brute_force_vs_dense(3, lib_path=lib)),
 ]
 
 

@@ -72,6 +72,9 @@ class PagedInputs:
     context_lens: np.ndarray        # [B] int32
     query_lens: Optional[np.ndarray] = None   # [B] int32 or None
     meta: Dict[str, object] = field(default_factory=dict)
+    kv_dtype: Optional[str] = None  # None: pages share `dtype`; "fp8_e4m3": uint8 codes
+    k_scale: float = 1.0            # fp8 pages: value = code value * scale
+    v_scale: float = 1.0
 
     @property
     def group(self) -> int:
@@ -83,9 +86,15 @@ class PagedInputs:
             return np.full(self.B, self.L, dtype=np.int64)
         return self.query_lens.astype(np.int64)
 
+    def kv_elem_bytes(self) -> int:
+        """Bytes of one stored K or V element."""
+        if self.kv_dtype == "fp8_e4m3":
+            return 1
+        return 4 if self.dtype == "f32" else 2
+
     def kv_token_bytes(self) -> int:
         """Bytes of one token's K plus V across all kv heads."""
-        return self.H_kv * self.D * 2 * (4 if self.dtype == "f32" else 2)
+        return self.H_kv * self.D * 2 * self.kv_elem_bytes()
 
 
 @dataclass
@@ -104,12 +113,32 @@ class MixedInputs:
 # helpers
 # ----------------------------------------------------------------------------
 
+# fp8 pages hold 8-bit codes (sign, 4 exponent bits, 3 mantissa bits) drawn
+# directly: sign uniform, exponent field uniform in [4, 8], mantissa uniform,
+# i.e. magnitudes from 2^-3 to 1.875 * 2 before the pool's scale.  Garbage is
+# a fixed code: 0x7E (the largest magnitude) for the default, 0xFE for its
+# negative, 0x00 for zero, 0x7F (NaN) for "nan".
+FP8_GARBAGE_CODES = {GARBAGE_DEFAULT: 0x7E, -GARBAGE_DEFAULT: 0xFE, 0.0: 0x00}
+
+
+def _draw_fp8_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    u = rng.integers(0, 1 << 8, size=shape, dtype=np.uint16)   # sign and mantissa bits
+    e = rng.integers(4, 9, size=shape, dtype=np.uint16)        # exponent field
+    return ((u & 0x80) | (e << 3) | (u & 0x07)).astype(np.uint8)
+
+
 def _draw_values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    if dtype == "fp8_e4m3":
+        return _draw_fp8_codes(rng, shape)
     x = rng.standard_normal(size=shape, dtype=np.float32)
     return f32_to_bf16_bits(x) if dtype == "bf16" else x
 
 
-def _garbage_value(dtype: str, garbage: float) -> Union[np.float32, np.uint16]:
+def _garbage_value(dtype: str, garbage: float) -> Union[np.float32, np.uint16, np.uint8]:
+    if dtype == "fp8_e4m3":
+        if garbage != garbage:  # NaN
+            return np.uint8(0x7F)
+        return np.uint8(FP8_GARBAGE_CODES[float(garbage)])
     g = np.array([garbage], dtype=np.float32)
     return f32_to_bf16_bits(g)[0] if dtype == "bf16" else g[0]
 
@@ -122,7 +151,7 @@ def _fill_pool(rng, dtype, num_pages, H_kv, ps, D, page_order: Sequence[int],
     ``garbage`` is a float, or the string "random" (fresh N(0,1)*1e3 draws) or
     "nan".  Values are drawn page by page in ``page_order``.
     """
-    np_dtype = np.uint16 if dtype == "bf16" else np.float32
+    np_dtype = {"bf16": np.uint16, "f32": np.float32, "fp8_e4m3": np.uint8}[dtype]
     pool = np.empty((num_pages, H_kv, ps, D), dtype=np_dtype)
     if isinstance(garbage, str) and garbage == "random":
         fill = None
@@ -139,6 +168,9 @@ def _fill_pool(rng, dtype, num_pages, H_kv, ps, D, page_order: Sequence[int],
         chunk = max(1, (1 << 22) // (H_kv * ps * D))
         for s in range(0, num_pages, chunk):
             e = min(num_pages, s + chunk)
+            if dtype == "fp8_e4m3":   # any byte, NaN codes included
+                pool[s:e] = grng.integers(0, 256, size=(e - s, H_kv, ps, D), dtype=np.uint16)
+                continue
             g = grng.standard_normal(size=(e - s, H_kv, ps, D), dtype=np.float32) * np.float32(1e3)
             pool[s:e] = f32_to_bf16_bits(g) if dtype == "bf16" else g
     order = np.asarray(page_order, dtype=np.int64)
@@ -194,7 +226,8 @@ def make_random(seed: int, *, B: int, H_q: int, H_kv: int, L: int, D: int,
                 causal: bool = True, query_lens: Optional[Sequence[int]] = None,
                 extra_free_pages: int = 3, max_pages: Optional[int] = None,
                 garbage=GARBAGE_DEFAULT, scale: Optional[float] = None,
-                name: str = "random") -> PagedInputs:
+                name: str = "random", kv_dtype: Optional[str] = None,
+                kv_scales=(0.5, 0.5)) -> PagedInputs:
     """Random paged inputs.
 
     Draw order: context lengths (when ``ctx`` is a (lo, hi) range) ->
@@ -202,6 +235,9 @@ def make_random(seed: int, *, B: int, H_q: int, H_kv: int, L: int, D: int,
     Physical ids are a seeded permutation of the whole pool, so logical pages
     land at arbitrary physical pages; ``extra_free_pages`` pages stay free and
     hold garbage, as do unused tail slots of each request's last page.
+    ``kv_dtype="fp8_e4m3"``: the pages hold random fp8 codes (see
+    _draw_fp8_codes) with k_scale, v_scale = ``kv_scales``; the query and
+    output keep ``dtype``.
     """
     rng = np.random.default_rng(seed)
     if isinstance(ctx, tuple):
@@ -224,17 +260,20 @@ def make_random(seed: int, *, B: int, H_q: int, H_kv: int, L: int, D: int,
         cur += n
     order = [p for row in ids for p in row]
     slots = [s for c in ctx_l for s in _valid_slots_per_page(c, page_size)]
-    kp = _fill_pool(rng, dtype, num_pages, H_kv, page_size, D, order, slots, garbage)
-    vp = _fill_pool(rng, dtype, num_pages, H_kv, page_size, D, order, slots, garbage)
+    pdt = kv_dtype or dtype
+    kp = _fill_pool(rng, pdt, num_pages, H_kv, page_size, D, order, slots, garbage)
+    vp = _fill_pool(rng, pdt, num_pages, H_kv, page_size, D, order, slots, garbage)
     q = _queries(rng, dtype, B, H_q, L, D, query_lens, garbage)
     bt = _tables_from_ids(ctx_l, page_size, max_pages, ids)
+    fp8 = kv_dtype == "fp8_e4m3"
     return PagedInputs(
         name=name, seed=seed, dtype=dtype, B=B, H_q=H_q, H_kv=H_kv, L=L, D=D,
         page_size=page_size, num_pages=num_pages, max_pages=max_pages,
         scale=float(scale if scale is not None else 1.0 / math.sqrt(D)), causal=causal,
         query=q, key_pages=kp, value_pages=vp, block_table=bt,
         context_lens=np.asarray(ctx_l, dtype=np.int32), query_lens=query_lens,
-        meta={"live_pages": live, "garbage": garbage})
+        meta={"live_pages": live, "garbage": garbage}, kv_dtype=kv_dtype,
+        k_scale=float(kv_scales[0]) if fp8 else 1.0, v_scale=float(kv_scales[1]) if fp8 else 1.0)
 
 
 # ----------------------------------------------------------------------------
@@ -269,7 +308,8 @@ def make_c1(seed: int = SEEDS["C1"]) -> PagedInputs:
 
 def _uniform_pool_config(name, seed, *, B, H_q, H_kv, D, L, ps, ctx_lo, ctx_hi,
                          pool_pages=None, free_frac=None, prefix_lo=None,
-                         prefix_hi=None, causal=True) -> PagedInputs:
+                         prefix_hi=None, causal=True, kv_dtype=None,
+                         kv_scales=(0.5, 0.5)) -> PagedInputs:
     """Shared builder for C2-C4.  Draw order: contexts (or prefixes) ->
     physical-id permutation -> K -> V -> Q."""
     rng = np.random.default_rng(seed)
@@ -292,16 +332,19 @@ def _uniform_pool_config(name, seed, *, B, H_q, H_kv, D, L, ps, ctx_lo, ctx_hi,
         cur += n
     order = [p for row in ids for p in row]
     slots = [s for c in ctx for s in _valid_slots_per_page(c, ps)]
-    kp = _fill_pool(rng, "bf16", num_pages, H_kv, ps, D, order, slots, GARBAGE_DEFAULT)
-    vp = _fill_pool(rng, "bf16", num_pages, H_kv, ps, D, order, slots, GARBAGE_DEFAULT)
+    pdt = kv_dtype or "bf16"
+    kp = _fill_pool(rng, pdt, num_pages, H_kv, ps, D, order, slots, GARBAGE_DEFAULT)
+    vp = _fill_pool(rng, pdt, num_pages, H_kv, ps, D, order, slots, GARBAGE_DEFAULT)
     q = _queries(rng, "bf16", B, H_q, L, D, None, GARBAGE_DEFAULT)
     bt = _tables_from_ids(ctx, ps, max_pages, ids)
+    fp8 = kv_dtype == "fp8_e4m3"
     return PagedInputs(
         name=name, seed=seed, dtype="bf16", B=B, H_q=H_q, H_kv=H_kv, L=L, D=D,
         page_size=ps, num_pages=num_pages, max_pages=max_pages,
         scale=1.0 / math.sqrt(D), causal=causal, query=q, key_pages=kp,
         value_pages=vp, block_table=bt, context_lens=np.asarray(ctx, dtype=np.int32),
-        meta={"live_pages": live})
+        meta={"live_pages": live}, kv_dtype=kv_dtype,
+        k_scale=float(kv_scales[0]) if fp8 else 1.0, v_scale=float(kv_scales[1]) if fp8 else 1.0)
 
 
 def make_c2(seed: int = SEEDS["C2"]) -> PagedInputs:
@@ -311,6 +354,16 @@ def make_c2(seed: int = SEEDS["C2"]) -> PagedInputs:
     x = _uniform_pool_config("C2", seed, B=64, H_q=32, H_kv=8, D=128, L=1, ps=16,
                              ctx_lo=128, ctx_hi=4096, pool_pages=20000)
     x.meta["workload"] = "GQA decode bf16 B64 Hq32 Hkv8 D128 ps16 ctx U[128,4096]"
+    return x
+
+
+def make_c2_fp8(seed: int = SEEDS["C2"]) -> PagedInputs:
+    """The GQA decode workload with fp8 (E4M3) K/V pages: the shape, contexts
+    and pool of C2 (same seed, same draw order), page elements drawn as fp8
+    codes (_draw_fp8_codes), k_scale = v_scale = 0.5; query and output bf16."""
+    x = _uniform_pool_config("C2-fp8", seed, B=64, H_q=32, H_kv=8, D=128, L=1, ps=16,
+                             ctx_lo=128, ctx_hi=4096, pool_pages=20000, kv_dtype="fp8_e4m3")
+    x.meta["workload"] = "GQA decode bf16 query, fp8 e4m3 pages, B64 Hq32 Hkv8 D128 ps16 ctx U[128,4096]"
     return x
 
 
