@@ -10,10 +10,13 @@ once) divided by the mean HIP-event time of the step (pa_decode +
 pa_split_reduce), with the inputs resident in HBM and the 256 MB last-level
 cache flushed before every step.  ``roofline`` is for the dominant kernel
 (the decode kernel alone, timed by its own event pair).  Secondary sections
-report the chunked prefill, long-context decode, mixed batch and a
-long-prompt prefill sweep with their own rooflines, small-batch decode
-latencies and the K/V write.  ``cpu_baseline`` times
-the CPU oracle on the host on the full decode workload.  ``clocks`` holds the
+report the same decode with fp8 (E4M3) pages, the chunked prefill,
+long-context decode, mixed batch and a long-prompt prefill sweep, each with
+its own roofline (``traffic`` is the HBM bytes per launch from the committed
+rocprofv3 counter summary of that section while its kernel source is
+unchanged), small-batch decode latencies and the K/V write (bf16 and into an
+fp8 pool).  ``cpu_baseline`` times the fp32 CPU oracle on the host on the
+full decode workload and once on the chunked prefill.  ``clocks`` holds the
 per-XCD gfx clocks and the memory clock that amd-smi reads while the decode
 and the long-prompt prefill run back to back (outside the timed regions).
 """
@@ -40,8 +43,7 @@ FLUSH_BYTES = 1 << 30          # > 256 MB last-level cache
 def decode_kv_bytes(x, unique: bool = False) -> int:
     """K+V bytes a decode call must read: every visible key and value of
     every kv head once (unique=True counts shared physical pages once)."""
-    elem = 4 if x.dtype == "f32" else 2
-    per_tok = x.H_kv * x.D * 2 * elem
+    per_tok = x.kv_token_bytes()
     if not unique:
         return int(x.context_lens.astype(np.int64).sum()) * per_tok
     seen = {}
@@ -90,8 +92,9 @@ class Runner:
         torch, api = self.torch, self.api
         x = d.x
         out = torch.empty_like(d.q)
+        from tests._gpu import kv_scales
         args = api.make_args(d.q, d.kp, d.vp, d.bt, d.cl, out, scale=x.scale, mask=d.mask,
-                             query_lens=d.ql)
+                             query_lens=d.ql, **kv_scales(x))
         plan = api.pa_decode_plan(args, partition_tokens=partition_tokens, num_cus=num_cus)
         S, P = plan.num_splits, plan.partition_tokens
         ws = api.Workspace.for_plan(plan, d.q, fused=fused)
@@ -138,15 +141,16 @@ class Runner:
         p = a.paged
         kp, vp = dev(p.key_pages), dev(p.value_pages)
         k, v, sm = dev(a.key), dev(a.value), dev(a.slot_mapping)
+        sc = dict(k_scale=p.k_scale, v_scale=p.v_scale) if p.kv_dtype else {}
         for _ in range(warmup):
             self.flush()
-            api.pa_append(k, v, sm, kp, vp)
+            api.pa_append(k, v, sm, kp, vp, **sc)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         torch.cuda.synchronize()
         for e in ev:
             self.flush()
             e[0].record()
-            api.pa_append(k, v, sm, kp, vp)
+            api.pa_append(k, v, sm, kp, vp, **sc)
             e[1].record()
         torch.cuda.synchronize()
         return {"ms": np.array([e[0].elapsed_time(e[1]) for e in ev])}
@@ -262,9 +266,25 @@ def sample_clocks(busy, samples=3, timeout_s=30.0, gap_s=1.0):
 
 
 # --------------------------------------------------------------- cpu oracle
-def cpu_baseline(x, kv_bytes, min_seconds=10.0, max_runs=2000):
+def host_cpu_model() -> str:
+    """The host CPU's model name (first "model name" of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(x, kv_bytes, x3=None, flops3=None, min_seconds=10.0, max_runs=2000):
+    """The CPU oracle (fp32 two-pass build, OpenMP over (request, kv head))
+    timed on the host: the full decode workload repeatedly for ~min_seconds
+    on all host cores, a few runs on one core, and one run of the chunked
+    prefill workload `x3` on all cores."""
     import oracle
-    oracle.load()
+    oracle.load(oracle.lib_for("f32"))
     times, threads = [], 0
     t_all = time.perf_counter()
     while len(times) < max_runs and (time.perf_counter() - t_all) < min_seconds:
@@ -280,11 +300,19 @@ def cpu_baseline(x, kv_bytes, min_seconds=10.0, max_runs=2000):
         oracle.attention_of(x, nthreads=1)
         t1s.append(time.perf_counter() - t0)
     t1 = float(np.mean(t1s))
-    return {"value": kv_bytes / t / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"the full decode workload ({x.B} requests, {int(x.context_lens.sum())} "
-                      f"keys), fp64 C oracle, mean of {len(times)} run(s) of {t:.2f} s",
-            "single_core": {"value": kv_bytes / t1 / 1e9, "unit": "GB/s", "cores": 1,
-                            "sample": f"mean of {len(t1s)} run(s) of {t1:.2f} s"}}
+    res = {"value": kv_bytes / t / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+           "host_cpu": host_cpu_model(),
+           "sample": f"the full decode workload ({x.B} requests, {int(x.context_lens.sum())} "
+                     f"keys), fp32 C oracle, mean of {len(times)} run(s) of {t:.2f} s",
+           "single_core": {"value": kv_bytes / t1 / 1e9, "unit": "GB/s", "cores": 1,
+                           "sample": f"mean of {len(t1s)} run(s) of {t1:.2f} s"}}
+    if x3 is not None:
+        t0 = time.perf_counter()
+        _, th3 = oracle.attention_of(x3, return_threads=True)
+        t3 = time.perf_counter() - t0
+        res["prefill_C3"] = {"value": flops3 / t3 / 1e12, "unit": "TFLOP/s", "cores": int(th3),
+                             "sample": f"the chunked prefill workload, one run of {t3:.2f} s"}
+    return res
 
 
 def decode_busy(run, d, n=20):
@@ -331,7 +359,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="C2,C3,C4,C5,long,small,append")
+    ap.add_argument("--only", default="C2,C2fp8,C3,C4,C5,long,small,append",
+                    help="sections to run (C2 is the headline; leaving it out leaves `value` "
+                         "null, for profiling runs): C2, C2fp8, C3, C4, C5, long (= long4096, "
+                         "long16384), small, threshold, append (all write shapes), "
+                         "append_long, append_fp8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-warm", action="store_true",
@@ -364,95 +396,134 @@ def main():
     import workloads as W
 
     only = set(args.only.split(","))
+    if "long" in only:
+        only |= {"long4096", "long16384"}
     run = Runner(torch, api, flush=not args.no_flush)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
-
-    # ---- headline: C2 GQA decode
-    x2 = W.make_c2()
-    d2 = run.to_device(x2)
-    kv2 = decode_kv_bytes(x2)
-    log(f"[bench] decode C2: {kv2 / 1e6:.1f} MB of K/V per step")
-    r2 = run.time_decode(d2, args.steps, args.warmup, args.partition_tokens)
-    step_ms = float(np.mean(r2["step_ms"]))
-    dec_ms = float(np.mean(r2["decode_ms"]))
-    value = kv2 / (step_ms * 1e-3) / 1e9
-    achieved = kv2 / (dec_ms * 1e-3) / 1e9
     sha_dec = _source_sha("pa_decode.hip", "pa_common.hpp", "pa_merge.hpp", "pa_internal.h")
-    traffic = _counters("decode_c2", sha_dec)
-    log(f"[bench] decode C2: step {step_ms * 1e3:.1f} us (decode {dec_ms * 1e3:.1f} us), "
-        f"{value:.0f} GB/s, {r2['schedule']} S={r2['S']} P={r2['P']}")
+    sha_pre = _source_sha("pa_prefill.hip", "pa_common.hpp", "pa_merge.hpp", "pa_internal.h")
+    sha_app = _source_sha("pa_append.hip", "pa_write.h")
+
+    def hbm_roofline(kernel, nbytes, ms, counters, sha):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                "traffic": _counters(counters, sha), "algorithmic_bytes_per_launch": nbytes,
+                "mean_launch_us": round(ms * 1e3, 2), "source_sha": sha}
+
+    def mfma_roofline(flops, ms, counters):
+        tf = flops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tf, 2),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                "traffic": _counters(counters, sha_pre), "algorithmic_flops_per_launch": flops,
+                "mean_launch_us": round(ms * 1e3, 2), "source_sha": sha_pre}
+
     result = {
         "metric": "decode K/V HBM GB/s (% of peak) + prefill TFLOP/s (% MFMA peak), 1 MI355X",
-        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
+        "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "GQA decode bf16 B64 Hq32 Hkv8 D128 L1 page16 ctx U[128,4096] seed2",
-                   "B": x2.B, "H_q": x2.H_q, "H_kv": x2.H_kv, "D": x2.D, "page_size": 16,
-                   "schedule": r2["schedule"], "num_splits": r2["S"], "partition_tokens": r2["P"],
-                   "llc_flushed": not args.no_flush, "kv_bytes_per_step": kv2},
-        "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": round(achieved, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": kv2,
-                     "mean_launch_us": round(dec_ms * 1e3, 2), "source_sha": sha_dec},
-        "step_stats": _stats(r2["step_ms"]),
-        "warm": None,
-        "merge": "fused into pa_decode" if r2["fused"] else "pa_split_reduce kernel",
-        "wall_s_timed_region": round(r2["wall_s"], 4),
+        "config": {"workload": "GQA decode bf16 B64 Hq32 Hkv8 D128 L1 page16 ctx U[128,4096] seed2"},
+        "roofline": None,
     }
-    del r2
     clocks = {"source": "amd-smi metric -c, three readings one second apart while the "
                         "workload runs back to back (outside the timed regions); driver "
                         "snapshots, context only"}
-    if not args.no_clocks:
-        clocks["decode_C2"] = sample_clocks(decode_busy(run, d2))
-        log(f"[bench] clocks under C2 decode: {clocks['decode_C2']}")
-    if not args.no_flush and not args.no_warm:
-        # the same steps without the cache flush between them (K/V partly in
-        # the 256 MB last-level cache): context only, never `value`
-        rw = Runner(torch, api, flush=False).time_decode(d2, args.steps, args.warmup,
-                                                         args.partition_tokens)
-        wm = float(np.mean(rw["step_ms"]))
-        result["warm"] = {"ms_per_step": round(wm, 5), "gbs": round(kv2 / (wm * 1e-3) / 1e9, 2),
-                          "decode_ms": round(float(np.mean(rw["decode_ms"])), 5)}
-        log(f"[bench] decode C2 warm (no flush): step {wm * 1e3:.1f} us")
-        del rw
+
+    # ---- headline: C2 GQA decode
+    x2 = W.make_c2()
+    kv2 = decode_kv_bytes(x2)
+    if "C2" in only:
+        d2 = run.to_device(x2)
+        log(f"[bench] decode C2: {kv2 / 1e6:.1f} MB of K/V per step")
+        r2 = run.time_decode(d2, args.steps, args.warmup, args.partition_tokens)
+        step_ms = float(np.mean(r2["step_ms"]))
+        dec_ms = float(np.mean(r2["decode_ms"]))
+        value = kv2 / (step_ms * 1e-3) / 1e9
+        log(f"[bench] decode C2: step {step_ms * 1e3:.1f} us (decode {dec_ms * 1e3:.1f} us), "
+            f"{value:.0f} GB/s, {r2['schedule']} S={r2['S']} P={r2['P']}")
+        result.update({
+            "value": round(value, 2), "ms_per_step": round(step_ms, 5),
+            "config": {"workload": "GQA decode bf16 B64 Hq32 Hkv8 D128 L1 page16 ctx U[128,4096] seed2",
+                       "B": x2.B, "H_q": x2.H_q, "H_kv": x2.H_kv, "D": x2.D, "page_size": 16,
+                       "schedule": r2["schedule"], "num_splits": r2["S"],
+                       "partition_tokens": r2["P"], "llc_flushed": not args.no_flush,
+                       "kv_bytes_per_step": kv2},
+            "roofline": hbm_roofline("decode_kernel", kv2, dec_ms, "decode_c2", sha_dec),
+            "step_stats": _stats(r2["step_ms"]),
+            "warm": None,
+            "merge": "fused into pa_decode" if r2["fused"] else "pa_split_reduce kernel",
+            "wall_s_timed_region": round(r2["wall_s"], 4),
+        })
+        del r2
+        if not args.no_clocks:
+            clocks["decode_C2"] = sample_clocks(decode_busy(run, d2))
+            log(f"[bench] clocks under C2 decode: {clocks['decode_C2']}")
+        if not args.no_flush and not args.no_warm:
+            # the same steps without the cache flush between them (K/V partly in
+            # the 256 MB last-level cache): context only, never `value`
+            rw = Runner(torch, api, flush=False).time_decode(d2, args.steps, args.warmup,
+                                                             args.partition_tokens)
+            wm = float(np.mean(rw["step_ms"]))
+            result["warm"] = {"ms_per_step": round(wm, 5),
+                              "gbs": round(kv2 / (wm * 1e-3) / 1e9, 2),
+                              "decode_ms": round(float(np.mean(rw["decode_ms"])), 5)}
+            log(f"[bench] decode C2 warm (no flush): step {wm * 1e3:.1f} us")
+            del rw
+        del d2
 
     sections = {}
-    sha_pre = _source_sha("pa_prefill.hip", "pa_common.hpp", "pa_merge.hpp", "pa_internal.h")
-    if "C3" in only:
+    if "C2fp8" in only:
+        # the same decode with fp8 (E4M3) pages: half the K/V bytes per token
+        x8 = W.make_c2_fp8()
+        d8 = run.to_device(x8)
+        kv8 = decode_kv_bytes(x8)
+        r8 = run.time_decode(d8, args.steps, args.warmup)
+        sm = float(np.mean(r8["step_ms"]))
+        dm = float(np.mean(r8["decode_ms"]))
+        log(f"[bench] decode C2 fp8: step {sm * 1e3:.1f} us (decode {dm * 1e3:.1f} us), "
+            f"{kv8 / sm / 1e6:.0f} GB/s of fp8 K/V, S={r8['S']}")
+        sections["decode_C2_fp8"] = {
+            "workload": "GQA decode bf16 query, fp8 e4m3 K/V pages (k/v scale 0.5), B64 Hq32 Hkv8 "
+                        "D128 page16 ctx U[128,4096] seed2",
+            "kv_bytes": kv8, "gbs_step": round(kv8 / sm / 1e6, 2), "schedule": r8["schedule"],
+            "num_splits": r8["S"], **_stats(r8["step_ms"]),
+            "roofline": hbm_roofline("decode_kernel", kv8, dm, "decode_c2_fp8", sha_dec)}
+        del d8, r8, x8
+    x3 = fl3 = None
+    if "C3" in only or not args.no_cpu_baseline:
         x3 = W.make_c3()
+        fl3 = prefill_flops(x3)
+    if "C3" in only:
         d3 = run.to_device(x3)
-        fl = prefill_flops(x3)
         r3 = run.time_prefill(d3, args.steps, args.warmup)
         ms = float(np.mean(r3["ms"]))
-        tf = fl / (ms * 1e-3) / 1e12
-        log(f"[bench] prefill C3: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+        log(f"[bench] prefill C3: {ms * 1e3:.1f} us, {fl3 / ms / 1e9:.1f} TFLOP/s")
         sections["prefill_C3"] = {
             "workload": "chunked causal prefill bf16 B4 Hq28 Hkv4 D128 L512 prefix U[0,2048] page16 seed3",
-            "flops": fl, "tflops": round(tf, 2), **_stats(r3["ms"]),
-            "roofline": {"bound": "mfma", "kernel": "prefill_kernel", "achieved": round(tf, 2),
-                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                         "traffic": _counters("prefill_c3", sha_pre), "source_sha": sha_pre}}
+            "flops": fl3, "tflops": round(fl3 / ms / 1e9, 2), **_stats(r3["ms"]),
+            "roofline": mfma_roofline(fl3, ms, "prefill_c3")}
         del d3, r3
-    if "long" in only:
-        long = []
-        for L in (4096, 16384):
-            xl = W.make_random(100 + L, B=1, H_q=28, H_kv=4, L=L, D=128, page_size=16, ctx=[L],
-                               dtype="bf16", causal=True, extra_free_pages=16)
-            dl = run.to_device(xl)
-            fl = prefill_flops(xl)
-            rl = run.time_prefill(dl, max(5, args.steps // 6), 2)
-            ms = float(np.mean(rl["ms"]))
-            tf = fl / (ms * 1e-3) / 1e12
-            log(f"[bench] long prefill L={L}: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
-            long.append({"workload": f"long-prompt causal prefill bf16 B1 Hq28 Hkv4 D128 L{L} prefix0 page16",
-                         "flops": fl, "tflops": round(tf, 2),
-                         "frac_of_mfma_peak": round(tf / BF16_PEAK_TFLOPS, 4), **_stats(rl["ms"])})
-            if L == 16384 and not args.no_clocks:
-                clocks["prefill_L16384"] = sample_clocks(prefill_busy(run, dl))
-                log(f"[bench] clocks under L={L} prefill: {clocks['prefill_L16384']}")
-            del dl, rl
+    long = []
+    for L in (4096, 16384):
+        if f"long{L}" not in only:
+            continue
+        xl = W.make_random(100 + L, B=1, H_q=28, H_kv=4, L=L, D=128, page_size=16, ctx=[L],
+                           dtype="bf16", causal=True, extra_free_pages=16)
+        dl = run.to_device(xl)
+        fl = prefill_flops(xl)
+        rl = run.time_prefill(dl, max(5, args.steps // 6), 2)
+        ms = float(np.mean(rl["ms"]))
+        tf = fl / (ms * 1e-3) / 1e12
+        log(f"[bench] long prefill L={L}: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
+        long.append({"workload": f"long-prompt causal prefill bf16 B1 Hq28 Hkv4 D128 L{L} prefix0 page16",
+                     "flops": fl, "tflops": round(tf, 2), **_stats(rl["ms"]),
+                     "roofline": mfma_roofline(fl, ms, f"prefill_long{L}")})
+        if L == 16384 and not args.no_clocks:
+            clocks["prefill_L16384"] = sample_clocks(prefill_busy(run, dl))
+            log(f"[bench] clocks under L={L} prefill: {clocks['prefill_L16384']}")
+        del dl, rl
+    if long:
         sections["prefill_long_prompt"] = long
     if "C4" in only:
         x4 = W.make_c4()
@@ -465,11 +536,8 @@ def main():
         sections["decode_C4"] = {
             "workload": "long-context decode bf16 B8 Hq32 Hkv8 D128 page16 ctx U[32768,131072] seed4",
             "kv_bytes": kv4, "gbs_step": round(kv4 / sm / 1e6, 2), "schedule": r4["schedule"],
-            "num_splits": r4["S"],
-            "partition_tokens": r4["P"], **_stats(r4["step_ms"]),
-            "roofline": {"bound": "hbm", "kernel": "decode_kernel",
-                         "achieved": round(kv4 / dm / 1e6, 2), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(kv4 / dm / 1e6 / HBM_PEAK_GBS, 4)}}
+            "num_splits": r4["S"], "partition_tokens": r4["P"], **_stats(r4["step_ms"]),
+            "roofline": hbm_roofline("decode_kernel", kv4, dm, "decode_c4", sha_dec)}
         del d4, r4, x4
     if "C5" in only:
         m = W.make_c5()
@@ -480,6 +548,7 @@ def main():
         logical = decode_kv_bytes(m.decode)
         unique = decode_kv_bytes(m.decode, unique=True)
         sm = float(np.mean(rd["step_ms"]))
+        dm = float(np.mean(rd["decode_ms"]))
         pm = float(np.mean(rp["ms"]))
         fl = prefill_flops(m.prefill)
         log(f"[bench] mixed C5: decode {sm * 1e3:.1f} us ({unique / sm / 1e6:.0f} GB/s unique), "
@@ -491,7 +560,11 @@ def main():
             "decode_gbs_unique": round(unique / sm / 1e6, 2),
             "decode_gbs_logical": round(logical / sm / 1e6, 2), "decode_mean_ms": sm,
             "prefill_flops": fl, "prefill_tflops": round(fl / pm / 1e9, 2), "prefill_mean_ms": pm,
-            "combined_ms": round(sm + pm, 5)}
+            "combined_ms": round(sm + pm, 5),
+            "roofline_decode": hbm_roofline("decode_kernel", unique, dm, "decode_c5", sha_dec),
+            "roofline_prefill": mfma_roofline(fl, pm, "prefill_c5")}
+        sections["mixed_C5"]["roofline_decode"]["note"] = \
+            "achieved on unique K/V bytes (shared prefix pages counted once)"
         del dd, dp, rd, rp
     if "small" in only:
         # latency-bound decode: one to four requests over long contexts
@@ -530,18 +603,26 @@ def main():
             th.append(row)
             del dt, xt
         sections["route_threshold"] = th
+    shapes = []
     if "append" in only:
+        shapes += [
+            ("C2 decode step: 64 requests x 1 token, H_kv 8, D 128, page 16", None,
+             dict(seed=2, B=64, H_kv=8, D=128, page_size=16, ctx_old=(127, 4095), n_new=[1] * 64)),
+            ("C3 chunks: 4 requests x 512 tokens after prefixes U[0,2048], H_kv 4, D 128, page 16",
+             None, dict(seed=3, B=4, H_kv=4, D=128, page_size=16, ctx_old=(0, 2048),
+                        n_new=[512] * 4))]
+    if "append" in only or "append_long" in only:
+        shapes.append(("long chunk: 1 request x 16384 tokens, H_kv 8, D 128, page 16", "append_long",
+                       dict(seed=9, B=1, H_kv=8, D=128, page_size=16, ctx_old=[0], n_new=[16384])))
+    if "append" in only or "append_fp8" in only:
+        shapes.append(("long chunk into an fp8 e4m3 pool (bf16 rows quantised, k/v scale 0.5): "
+                       "1 request x 16384 tokens, H_kv 8, D 128, page 16", "append_fp8_long",
+                       dict(seed=9, B=1, H_kv=8, D=128, page_size=16, ctx_old=[0], n_new=[16384],
+                            kv_dtype="fp8_e4m3")))
+    if shapes:
         # the K/V write that precedes attention (pa_append), timed on its own
         wr = []
-        for name, kw in (
-                ("C2 decode step: 64 requests x 1 token, H_kv 8, D 128, page 16",
-                 dict(seed=2, B=64, H_kv=8, D=128, page_size=16, ctx_old=(127, 4095),
-                      n_new=[1] * 64)),
-                ("C3 chunks: 4 requests x 512 tokens after prefixes U[0,2048], H_kv 4, D 128, page 16",
-                 dict(seed=3, B=4, H_kv=4, D=128, page_size=16, ctx_old=(0, 2048),
-                      n_new=[512] * 4)),
-                ("long chunk: 1 request x 16384 tokens, H_kv 8, D 128, page 16",
-                 dict(seed=9, B=1, H_kv=8, D=128, page_size=16, ctx_old=[0], n_new=[16384]))):
+        for name, counters, kw in shapes:
             a = W.make_append(dtype="bf16", **kw)
             ra = run.time_append(a, max(10, args.steps // 3), args.warmup)
             ms = float(np.mean(ra["ms"]))
@@ -549,19 +630,17 @@ def main():
             log(f"[bench] append {name.split(':')[0]}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s")
             wr.append({"workload": f"K/V write bf16, {name}", "tokens": a.num_tokens,
                        "moved_bytes": a.moved_bytes(), "gbs": round(gbs, 2), **_stats(ra["ms"]),
-                       "roofline": {"bound": "hbm", "kernel": "append_kernel",
-                                    "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}})
+                       "roofline": hbm_roofline("append_kernel", a.moved_bytes(), ms,
+                                                counters or "none", sha_app)})
             del a
         sections["append"] = wr
     result["sections"] = sections
     result["clocks"] = clocks
 
     if not args.no_cpu_baseline:
-        log("[bench] CPU oracle baseline on the decode workload")
-        result["cpu_baseline"] = cpu_baseline(x2, kv2)
+        log("[bench] CPU oracle baseline on the decode and chunked-prefill workloads")
+        result["cpu_baseline"] = cpu_baseline(x2, kv2, x3, fl3)
     print(json.dumps(result), flush=True)
-
 
 if __name__ == "__main__":
     main()

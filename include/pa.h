@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 7
+#define PA_ABI_VERSION 8
 
 typedef enum {
   PA_OK = 0,
@@ -77,6 +77,16 @@ typedef enum {
 
 typedef enum { PA_DTYPE_F32 = 0, PA_DTYPE_BF16 = 1 } pa_dtype;
 typedef enum { PA_MASK_NONE = 0, PA_MASK_CAUSAL = 1 } pa_mask;
+
+/* Element type of the K/V pages ("Reading vLLM's PagedAttention Kernel",
+ * section 3.2: the cache write takes a kv-cache dtype and per-tensor k/v
+ * scales).  PA_KV_SAME: the pages hold `dtype` elements.  PA_KV_FP8_E4M3:
+ * the pages hold one byte per element, an 8-bit float in the OCP E4M3
+ * encoding (bit 7 sign, bits 6..3 exponent with bias 7, bits 2..0
+ * mantissa; exponent 0 subnormal; s.1111.111 NaN; no infinity), and an
+ * element's value is its code's value times k_scale (keys) or v_scale
+ * (values). */
+typedef enum { PA_KV_SAME = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_dtype;
 
 typedef struct pa_args {
   const void *query;           /* [B, H_q, L, D] */
@@ -111,6 +121,14 @@ typedef struct pa_args {
    * zeroes debug_visits. */
   int32_t *debug_trace;
   int32_t *debug_visits;
+  /* Page element type (pa_kv_dtype; 0 = PA_KV_SAME).  PA_KV_FP8_E4M3 needs
+   * dtype PA_DTYPE_BF16 (query and out) and head_dim 128, and is served by
+   * the decode path only (pa_decode, pa_split_reduce, pa_decode_noalloc,
+   * and pa_attention on its decode route); pa_prefill returns
+   * PA_ERR_UNSUPPORTED for it. */
+  int32_t kv_dtype;
+  float k_scale;               /* fp8 pages: finite and > 0 (ignored otherwise) */
+  float v_scale;               /* fp8 pages: finite and > 0 (ignored otherwise) */
 } pa_args;
 
 /* How pa_decode divides a call's keys among the waves of the GPU. */
@@ -280,12 +298,24 @@ typedef struct pa_append_args {
   int32_t head_dim;              /* 64 or 128 */
   int32_t num_pages;             /* >= 1 */
   int32_t page_size;             /* >= 1 */
-  int32_t dtype;                 /* pa_dtype */
+  int32_t dtype;                 /* pa_dtype of key and value (and of the pages when
+                                    cache_dtype is PA_KV_SAME) */
+  /* pa_kv_dtype of the pages (0 = PA_KV_SAME: rows copied bit for bit).
+   * PA_KV_FP8_E4M3 (key/value bf16): each element x is stored as the E4M3
+   * code nearest to x / scale, the division done in fp32 and correctly
+   * rounded, ties to the code with an even mantissa, magnitudes beyond 448
+   * saturated to 448, NaN kept NaN (k_scale for keys, v_scale for values,
+   * both finite and > 0). */
+  int32_t cache_dtype;
+  float k_scale;
+  float v_scale;
 } pa_append_args;
 
-/* Scatter the rows of `key` and `value` into the page pool.
- * PA_ERR_INVALID_ARG: a NULL or misaligned pointer, a size out of range, or a
- * pool of 2^31 slots or more; PA_ERR_UNSUPPORTED: head_dim or dtype. */
+/* Scatter the rows of `key` and `value` into the page pool (quantising
+ * them for an fp8 pool).
+ * PA_ERR_INVALID_ARG: a NULL or misaligned pointer, a size out of range, a
+ * bad scale, or a pool of 2^31 slots or more; PA_ERR_UNSUPPORTED: head_dim,
+ * dtype or cache_dtype. */
 pa_status pa_append(const pa_append_args *args, void *stream);
 
 /* -------------------------------------------------------- no allocation

@@ -38,3 +38,19 @@ def scatter_tokens(key_pages: np.ndarray, value_pages: np.ndarray, key: np.ndarr
             kp[page, h, off, :] = key[t, h, :]
             vp[page, h, off, :] = value[t, h, :]
     return kp, vp
+
+
+def scatter_tokens_fp8(key_pages: np.ndarray, value_pages: np.ndarray, key_bf16: np.ndarray,
+                       value_bf16: np.ndarray, slot_mapping, k_scale: float,
+                       v_scale: float) -> tuple:
+    """The scatter into an fp8 pool: uint8 pools [P, H_kv, page_size, D];
+    token t's bf16 rows (uint16 bit patterns [T, H_kv, D]) are widened to
+    fp32 exactly and stored as the codes of row / scale (fp8.quantize_rows:
+    the write rule of the kv-cache dtype with per-tensor scales), at slot
+    slot_mapping[t] as for scatter_tokens."""
+    from . import fp8
+    k32 = (np.asarray(key_bf16, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    v32 = (np.asarray(value_bf16, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    kq = fp8.quantize_rows(k32, k_scale)
+    vq = fp8.quantize_rows(v32, v_scale)
+    return scatter_tokens(key_pages, value_pages, kq, vq, slot_mapping)

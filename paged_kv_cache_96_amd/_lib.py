@@ -22,6 +22,8 @@ PA_DTYPE_F32 = 0
 PA_DTYPE_BF16 = 1
 PA_MASK_NONE = 0
 PA_MASK_CAUSAL = 1
+PA_KV_SAME = 0
+PA_KV_FP8_E4M3 = 1
 
 EXPORTED = ("pa_decode_plan", "pa_decode", "pa_split_reduce", "pa_prefill_plan", "pa_prefill",
             "pa_attention_plan", "pa_attention", "pa_append", "pa_decode_noalloc",
@@ -50,6 +52,9 @@ class PaArgs(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("debug_trace", ctypes.c_void_p),
         ("debug_visits", ctypes.c_void_p),
+        ("kv_dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -78,10 +83,13 @@ class PaAppendArgs(ctypes.Structure):
         ("num_pages", ctypes.c_int32),
         ("page_size", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("cache_dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
-ABI_VERSION = 7  # PA_ABI_VERSION of the structs below
+ABI_VERSION = 8  # PA_ABI_VERSION of the structs below
 
 ROUTE_DECODE = 0
 ROUTE_PREFILL = 1

@@ -55,16 +55,23 @@ def make_args(query: torch.Tensor, key_pages: torch.Tensor, value_pages: torch.T
               scale: Optional[float] = None, mask: Optional[str] = "causal",
               query_lens: Optional[torch.Tensor] = None,
               debug_trace: Optional[torch.Tensor] = None,
-              debug_visits: Optional[torch.Tensor] = None) -> PaArgs:
-    """Fill a pa_args from tensors (shapes as in include/pa.h)."""
+              debug_visits: Optional[torch.Tensor] = None,
+              k_scale: Optional[float] = None, v_scale: Optional[float] = None) -> PaArgs:
+    """Fill a pa_args from tensors (shapes as in include/pa.h).  uint8 pages
+    are fp8 E4M3 codes (PA_KV_FP8_E4M3) and need k_scale and v_scale."""
     B, Hq, L, D = query.shape
     P, Hkv, ps, D2 = key_pages.shape
     if D2 != D or tuple(value_pages.shape) != tuple(key_pages.shape):
         raise ValueError("query / key_pages / value_pages head sizes disagree")
     if tuple(out.shape) != tuple(query.shape) or out.dtype != query.dtype:
         raise ValueError("out must match query in shape and dtype")
-    if key_pages.dtype != query.dtype or value_pages.dtype != query.dtype:
-        raise ValueError("query and pages must share one dtype")
+    fp8 = key_pages.dtype == torch.uint8
+    if value_pages.dtype != key_pages.dtype:
+        raise ValueError("key_pages and value_pages must share one dtype")
+    if fp8 and (k_scale is None or v_scale is None):
+        raise ValueError("fp8 (uint8) pages need k_scale and v_scale")
+    if not fp8 and key_pages.dtype != query.dtype:
+        raise ValueError("query and pages must share one dtype (or the pages be fp8 codes)")
     _int32(block_table, "block_table")
     _int32(context_lens, "context_lens")
     _int32(query_lens, "query_lens")
@@ -95,6 +102,9 @@ def make_args(query: torch.Tensor, key_pages: torch.Tensor, value_pages: torch.T
     a.scale = float(scale) if scale is not None else 1.0 / math.sqrt(D)
     a.debug_trace = _ptr(debug_trace)
     a.debug_visits = _ptr(debug_visits)
+    a.kv_dtype = _lib.PA_KV_FP8_E4M3 if fp8 else _lib.PA_KV_SAME
+    a.k_scale = float(k_scale) if fp8 else 1.0
+    a.v_scale = float(v_scale) if fp8 else 1.0
     return a
 
 
@@ -298,7 +308,9 @@ def paged_attention(query: torch.Tensor, key_pages: torch.Tensor, value_pages: t
                     block_table: torch.Tensor, context_lens: torch.Tensor, *,
                     scale: Optional[float] = None, mask: Optional[str] = "causal",
                     query_lens: Optional[torch.Tensor] = None, partition_tokens: int = 0,
-                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                    out: Optional[torch.Tensor] = None, stream=None,
+                    k_scale: Optional[float] = None,
+                    v_scale: Optional[float] = None) -> torch.Tensor:
     """Convenience call through the library's router (pa_attention): the
     decode path when the query rows of one kv head fit a decode row block,
     the prefill path otherwise.  The workspace is allocated (and its
@@ -308,7 +320,7 @@ def paged_attention(query: torch.Tensor, key_pages: torch.Tensor, value_pages: t
     if out is None:
         out = torch.empty_like(query)
     args = make_args(query, key_pages, value_pages, block_table, context_lens, out, scale=scale,
-                     mask=mask, query_lens=query_lens)
+                     mask=mask, query_lens=query_lens, k_scale=k_scale, v_scale=v_scale)
     ap = pa_attention_plan(args, partition_tokens=partition_tokens)
     ws = attention_workspace(ap, args, query)
     if stream is not None:
@@ -324,18 +336,26 @@ def paged_attention(query: torch.Tensor, key_pages: torch.Tensor, value_pages: t
 
 
 def pa_append(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor,
-              key_pages: torch.Tensor, value_pages: torch.Tensor, stream=None) -> None:
+              key_pages: torch.Tensor, value_pages: torch.Tensor, stream=None,
+              k_scale: Optional[float] = None, v_scale: Optional[float] = None) -> None:
     """K/V write path: the rows key[t], value[t] ([T, H_kv, D]) go to slot
     slot_mapping[t] (int32: page * page_size + offset; negative or past the
-    pool: skipped) of key_pages / value_pages ([P, H_kv, page_size, D])."""
+    pool: skipped) of key_pages / value_pages ([P, H_kv, page_size, D]).
+    uint8 pages are an fp8 E4M3 pool: bf16 rows are quantised with k_scale /
+    v_scale."""
     T, Hkv, D = key.shape
     P, Hkv2, ps, D2 = key_pages.shape
     if tuple(value.shape) != tuple(key.shape) or tuple(value_pages.shape) != tuple(key_pages.shape):
         raise ValueError("key / value or key_pages / value_pages shapes disagree")
     if Hkv2 != Hkv or D2 != D:
         raise ValueError("token rows and pages disagree in kv heads or head size")
-    if not (key.dtype == value.dtype == key_pages.dtype == value_pages.dtype):
-        raise ValueError("tokens and pages must share one dtype")
+    fp8 = key_pages.dtype == torch.uint8
+    if key.dtype != value.dtype or key_pages.dtype != value_pages.dtype:
+        raise ValueError("key / value or key_pages / value_pages dtypes disagree")
+    if fp8 and (k_scale is None or v_scale is None):
+        raise ValueError("an fp8 (uint8) pool needs k_scale and v_scale")
+    if not fp8 and key.dtype != key_pages.dtype:
+        raise ValueError("tokens and pages must share one dtype (or the pages be fp8 codes)")
     _int32(slot_mapping, "slot_mapping")
     if tuple(slot_mapping.shape) != (T,):
         raise ValueError("slot_mapping must be [num_tokens]")
@@ -345,4 +365,7 @@ def pa_append(key: torch.Tensor, value: torch.Tensor, slot_mapping: torch.Tensor
     a.key_pages, a.value_pages = _ptr(key_pages), _ptr(value_pages)
     a.num_tokens, a.num_kv_heads, a.head_dim, a.num_pages, a.page_size = T, Hkv, D, P, ps
     a.dtype = _DTYPES.get(key.dtype, 99)
+    a.cache_dtype = _lib.PA_KV_FP8_E4M3 if fp8 else _lib.PA_KV_SAME
+    a.k_scale = float(k_scale) if fp8 else 1.0
+    a.v_scale = float(v_scale) if fp8 else 1.0
     _lib.check("pa_append", _lib.lib().pa_append(ctypes.byref(a), _stream(stream)))

@@ -35,6 +35,14 @@
 //   weights.  At the end the lane groups are merged in registers and the
 //   partition state is written (normalised output plus log-sum-exp), or the
 //   final output when there is one partition.
+//
+//   fp8 pages (E4M3 codes with per-tensor k/v scales, bf16 query and output):
+//   a lane's 16-byte load holds 16 elements of one key, so a wave load covers
+//   8 keys (D = 128) and a step 32; every pair of codes is widened exactly
+//   (v_cvt_pk_f32_fp8, then to a bf16 pair) and the arithmetic is that of
+//   bf16 pages.  k_scale folds into the score multiplier, v_scale into the
+//   final division.  A step spans two 16-key halves, each resolved to its
+//   own page, so 16-key pages keep the page-uniform walk.
 #include <type_traits>
 
 #include "pa_common.hpp"
@@ -64,6 +72,10 @@ struct Elem<float> {
 template <>
 struct Elem<uint16_t> {
   static constexpr int kPerVec = 8;
+};
+template <>
+struct Elem<uint8_t> {
+  static constexpr int kPerVec = 16;
 };
 
 template <typename T>
@@ -97,6 +109,29 @@ __device__ __forceinline__ uint32_t word(const Vec &v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+
+// The elements of a lane's page load as bf16 pairs: pair j holds elements
+// 2j and 2j + 1.  bf16 pages: the loaded words.  fp8 pages: every code
+// widened exactly (an E4M3 value is a bf16 value) with the hardware
+// converter, whose results match the format's definition for all 256 codes.
+template <typename KV>
+__device__ __forceinline__ void to_pairs(const Vec &v, uint32_t (&pr)[Elem<KV>::kPerVec / 2]) {
+  if constexpr (sizeof(KV) == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = word(v, i);
+      const f32x2_v lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);  // bytes 0, 1
+      const f32x2_v hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);   // bytes 2, 3
+      pr[2 * i] = cvt_pk_bf16(lo[0], lo[1]);
+      pr[2 * i + 1] = cvt_pk_bf16(hi[0], hi[1]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = word(v, i);
+  }
+}
+
 // Where a work item's state goes.  Partition schedule: slot `slot` of each
 // row.  Balanced schedule: piece slot `piece` of the row block, whose
 // `pieces` pieces occupy slots first, first + 1, ...; with arrival counters
@@ -114,18 +149,26 @@ struct ItemOut {
 // With `split` it writes the state of that piece to the workspace (see
 // ItemOut), otherwise the piece is the whole row range and it writes the
 // output.
-template <typename T, int D, int ROWS, bool DEBUG, bool UNIFORM>
+template <typename T, typename KV, int D, int ROWS, bool DEBUG, bool UNIFORM>
 __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g, int rb, int t0,
                                             int tend, const ItemOut &io, bool split, int ctx,
                                             int Lb) {
-  constexpr int kElems = Elem<T>::kPerVec;
+  constexpr bool kFp8 = sizeof(KV) == 1;  // fp8 E4M3 pages (T: bf16)
+  constexpr int kElems = Elem<KV>::kPerVec;  // page elements per 16-byte lane load
   constexpr int kLpt = D / kElems;      // lanes per key
   constexpr int kTpl = 64 / kLpt;       // keys per wave load
   constexpr int kLoads = 4;             // loads in flight per step (each of K and V)
   constexpr int kStep = kTpl * kLoads;  // keys per wave step
+  constexpr int kResKeys = kFp8 ? 16 : kStep;  // keys resolved to one page at a time
+  constexpr int kRes = kStep / kResKeys;       // page resolutions per step
+  constexpr int kLoadsPerRes = kLoads / kRes;
+  constexpr int kPairs = kElems / 2;    // bf16 pairs per lane load (dot2 paths)
+  constexpr int kQVecs = kElems * (int)sizeof(T) / 16;  // 16-byte query pieces per lane
   constexpr int kBuf = kDecodeBuffers;  // rotating register buffers of the walk
-  constexpr bool kBf16 = sizeof(T) == 2;
+  constexpr bool kBf16 = sizeof(T) == 2;  // bf16 query: dot2 arithmetic
   static_assert(kLpt * kElems == D && kTpl * kLpt == 64, "layout");
+  static_assert(kRes * kResKeys == kStep && kLoadsPerRes * kRes == kLoads, "resolutions");
+  static_assert(!kFp8 || kBf16, "fp8 pages take a bf16 query");
   const int lane = threadIdx.x & 63;
   const int c = lane % kLpt;            // element chunk of this lane
   const int kl = lane / kLpt;           // key of this lane within a load
@@ -154,16 +197,22 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
   // the row block holding the last packed row of the request counts visits
   const bool counts = DEBUG && Lb > 0 && ((Lb * G - 1) / ROWS == rb);
 
-  Vec qv[ROWS];
+  Vec qv[ROWS][kQVecs];
   const T *qbase = reinterpret_cast<const T *>(p.q);
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     // rows past query_lens are in bounds (i < L): load unconditionally, then drop
     const bool exists = rb * ROWS + r < G * p.L;
-    const Vec v = exists ? *reinterpret_cast<const Vec *>(qbase + qrow[r] * D + c * kElems)
-                         : Vec{0u, 0u, 0u, 0u};
-    qv[r] = valid[r] ? v : Vec{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int v = 0; v < kQVecs; ++v) {
+      const Vec x = exists ? *reinterpret_cast<const Vec *>(qbase + qrow[r] * D + c * kElems +
+                                                            v * (16 / (int)sizeof(T)))
+                           : Vec{0u, 0u, 0u, 0u};
+      qv[r][v] = valid[r] ? x : Vec{0u, 0u, 0u, 0u};
+    }
   }
+  // query word j of row r (bf16 pair of elements 2j, 2j + 1 of the lane)
+  auto qword = [&](int r, int j) { return word(qv[r][j / 4], j % 4); };
 
   float m[ROWS], l[ROWS], acc[ROWS][kElems];
 #pragma unroll
@@ -174,25 +223,33 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
     for (int e = 0; e < kElems; ++e) acc[r][e] = 0.f;
   }
 
-  const T *kp = reinterpret_cast<const T *>(p.kp);
-  const T *vp = reinterpret_cast<const T *>(p.vp);
+  const KV *kp = reinterpret_cast<const KV *>(p.kp);
+  const KV *vp = reinterpret_cast<const KV *>(p.vp);
   const int nsteps = t1 > t0 ? (t1 - t0 + kStep - 1) / kStep : 0;
   const int nw = nsteps;  // steps of this wave
   const int tmin = min(t1, kmin);  // keys below this are visible to every valid row
   const size_t head_stride = (size_t)ps * D;
   const uint32_t lane_off = (uint32_t)(kl * D + c * kElems);
 
-  // Offsets of the page/slot of this wave's steps k0 .. k0+63 (one per lane).
-  uint32_t off_lo = 0, off_hi = 0;
+  // Offsets of the page/slot of this wave's steps k0 .. k0+63 (one step per
+  // lane; kRes resolutions of kResKeys keys each per step).  Only keys below
+  // t1 are resolved: block-table entries past the context are never read.
+  uint32_t off_lo[kRes], off_hi[kRes];
+#pragma unroll
+  for (int rr = 0; rr < kRes; ++rr) off_lo[rr] = off_hi[rr] = 0u;
   auto resolve = [&](int k0) {
     const int k = k0 + lane;
-    if (k < nw) {
-      const int base = t0 + k * kStep;
-      const int lp = base / ps;
-      const int page = bt[lp];
-      const size_t off = ((size_t)page * p.Hkv + g) * head_stride + (size_t)(base - lp * ps) * D;
-      off_lo = (uint32_t)off;
-      off_hi = (uint32_t)(off >> 32);
+#pragma unroll
+    for (int rr = 0; rr < kRes; ++rr) {
+      const int base = t0 + k * kStep + rr * kResKeys;
+      if (k < nw && base < t1) {
+        const int lp = base / ps;
+        const int page = bt[lp];
+        const size_t off =
+            ((size_t)page * p.Hkv + g) * head_stride + (size_t)(base - lp * ps) * D;
+        off_lo[rr] = (uint32_t)off;
+        off_hi[rr] = (uint32_t)(off >> 32);
+      }
     }
   };
 
@@ -252,33 +309,52 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
     if constexpr (decltype(refresh)::value) {
       if (k > 0 && (k & 63) == 0 && ok) resolve(k);
     }
-    const uint32_t lo = __builtin_amdgcn_readlane(off_lo, k & 63);
-    const uint32_t hi2 = __builtin_amdgcn_readlane(off_hi, k & 63);
-    const size_t base = ((size_t)hi2 << 32) | lo;
-    const int nrec = ok ? kStep * D * (int)sizeof(T) : 0;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<T *>(kp + base), (short)0, nrec, kBufferRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<T *>(vp + base), (short)0, nrec, kBufferRsrcWord3);
 #pragma unroll
-    for (int n = 0; n < kLoads; ++n) {
-      const int boff = (int)((lane_off + n * kTpl * D) * sizeof(T));
-      kv[n] = load_stream_buf(rk, boff);
-      vv[n] = load_stream_buf(rv, boff);
-      // the resource base plus the lane's byte offset, in elements
-      if (ok) record(t0 + k * kStep + n * kTpl + kl, base + (size_t)boff / sizeof(T));
+    for (int rr = 0; rr < kRes; ++rr) {
+      const uint32_t lo = __builtin_amdgcn_readlane(off_lo[rr], k & 63);
+      const uint32_t hi2 = __builtin_amdgcn_readlane(off_hi[rr], k & 63);
+      const size_t base = ((size_t)hi2 << 32) | lo;
+      const bool live = ok && t0 + k * kStep + rr * kResKeys < t1;  // wave-uniform
+      const int nrec = live ? kResKeys * D * (int)sizeof(KV) : 0;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<KV *>(kp + base), (short)0, nrec, kBufferRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<KV *>(vp + base), (short)0, nrec, kBufferRsrcWord3);
+#pragma unroll
+      for (int nn = 0; nn < kLoadsPerRes; ++nn) {
+        const int n = rr * kLoadsPerRes + nn;
+        const int boff = (int)((lane_off + nn * kTpl * D) * sizeof(KV));
+        kv[n] = load_stream_buf(rk, boff);
+        vv[n] = load_stream_buf(rv, boff);
+        // the resource base plus the lane's byte offset, in elements
+        if (live) record(t0 + k * kStep + n * kTpl + kl, base + (size_t)boff / sizeof(KV));
+      }
     }
   };
 
-  const float cs = p.scale_log2;
+  // score multiplier in base-2 units (fp8 pages: times k_scale)
+  const float cs = kFp8 ? p.scale_log2 * p.k_scale : p.scale_log2;
   auto fold_step = [&](int k, const Vec (&kv)[kLoads], const Vec (&vv)[kLoads]) {
     const int base = t0 + k * kStep;
     const bool tail = base + kStep > tmin;
     float sc[kLoads][ROWS];
 #pragma unroll
-    for (int n = 0; n < kLoads; ++n)
+    for (int n = 0; n < kLoads; ++n) {
+      if constexpr (kBf16) {
+        uint32_t kpr[kPairs];
+        to_pairs<KV>(kv[n], kpr);
 #pragma unroll
-      for (int r = 0; r < ROWS; ++r) sc[n][r] = group_sum<kLpt>(lane_dot<T>(qv[r], kv[n]));
+        for (int r = 0; r < ROWS; ++r) {
+          float a = 0.f;
+#pragma unroll
+          for (int j = 0; j < kPairs; ++j) a = dot2_bf16(qword(r, j), kpr[j], a);
+          sc[n][r] = group_sum<kLpt>(a);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) sc[n][r] = group_sum<kLpt>(lane_dot<T>(qv[r][0], kv[n]));
+      }
+    }
     if (tail) {
 #pragma unroll
       for (int n = 0; n < kLoads; ++n) {
@@ -331,10 +407,13 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
           pk[r] = cvt_pk_bf16(sc[n][r], sc[n + 1][r]);
           l[r] = dot2_bf16(pk[r], 0x3f803f80u, l[r]);  // + both rounded weights (bf16 1.0 pair)
         }
+        uint32_t va[kPairs], vb[kPairs];
+        to_pairs<KV>(vv[n], va);
+        to_pairs<KV>(vv[n + 1], vb);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t a = dead[n] ? 0u : word(vv[n], w);
-          const uint32_t bb = dead[n + 1] ? 0u : word(vv[n + 1], w);
+        for (int w = 0; w < kPairs; ++w) {
+          const uint32_t a = dead[n] ? 0u : va[w];
+          const uint32_t bb = dead[n + 1] ? 0u : vb[w];
           const uint32_t lo = __builtin_amdgcn_perm(bb, a, 0x05040100u);  // dim 2w of keys n, n+1
           const uint32_t hi2 = __builtin_amdgcn_perm(bb, a, 0x07060302u); // dim 2w+1
 #pragma unroll
@@ -422,7 +501,8 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
     const int rho = rb * ROWS + r;
     if (rho >= G * p.L) continue;  // row outside the packed range
     const bool has = valid[r] && lt > 0.f;
-    const float inv = has ? 1.f / lt : 0.f;
+    // fp8 pages: the values carry v_scale, applied once here
+    const float inv = has ? (kFp8 ? p.v_scale / lt : 1.f / lt) : 0.f;
     if (split) {
       if (!valid[r]) continue;  // the merge writes padding rows itself
       const size_t wi = io.piece >= 0 ? (size_t)io.piece * ROWS + r
@@ -451,9 +531,13 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
         *reinterpret_cast<float4 *>(dst) =
             make_float4(acc[r][0] * inv, acc[r][1] * inv, acc[r][2] * inv, acc[r][3] * inv);
       } else {
-        *reinterpret_cast<uint4 *>(dst) = make_uint4(
-            cvt_pk_bf16(acc[r][0] * inv, acc[r][1] * inv), cvt_pk_bf16(acc[r][2] * inv, acc[r][3] * inv),
-            cvt_pk_bf16(acc[r][4] * inv, acc[r][5] * inv), cvt_pk_bf16(acc[r][6] * inv, acc[r][7] * inv));
+#pragma unroll
+        for (int e = 0; e < kElems; e += 8)
+          *reinterpret_cast<uint4 *>(dst + e) =
+              make_uint4(cvt_pk_bf16(acc[r][e] * inv, acc[r][e + 1] * inv),
+                         cvt_pk_bf16(acc[r][e + 2] * inv, acc[r][e + 3] * inv),
+                         cvt_pk_bf16(acc[r][e + 4] * inv, acc[r][e + 5] * inv),
+                         cvt_pk_bf16(acc[r][e + 6] * inv, acc[r][e + 7] * inv));
       }
     }
   }
@@ -495,7 +579,7 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
 // piece slot r + w (see BalancedSplit), and the merge recomputes w0 and w1
 // from the same formula; a row block that one wave covers is written to the
 // output directly.
-template <typename T, int D, int ROWS, bool DEBUG, bool UNIFORM>
+template <typename T, typename KV, int D, int ROWS, bool DEBUG, bool UNIFORM>
 __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blocks) {
   constexpr int kWaves = 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -514,13 +598,13 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
     if (s > 0 && t0 >= ctx) return;  // never read by the merge
     const bool split = p.num_splits > 1;
     const ItemOut io{s, -1, 0, 0, 0};
-    decode_item<T, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, t0, split ? t0 + p.part_tokens : ctx, io,
-                                            split, ctx, Lb);
+    decode_item<T, KV, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, t0, split ? t0 + p.part_tokens : ctx,
+                                                io, split, ctx, Lb);
     return;
   }
 
   // ---- balanced schedule: prefix sums of the per-request step counts
-  constexpr int kStep = decode_step_keys(D, (int)sizeof(T));
+  constexpr int kStep = decode_step_keys(D, (int)sizeof(KV));
   __shared__ long long s_R[kBalancedMaxBatch + 1];  // first step of request b
   __shared__ int s_ctx[kBalancedMaxBatch];
   __shared__ long long s_sum[256];
@@ -619,8 +703,8 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
       const int Lb = p.ql ? p.ql[b] : p.L;
       const long long unit = (long long)b * U + u;  // row block over the call
       const ItemOut io{0, unit + v, unit + w0, (int)(w1 - w0 + 1), unit};
-      decode_item<T, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, (int)(j0 * kStep), (int)(j1 * kStep),
-                                              io, w1 > w0, ctx, Lb);
+      decode_item<T, KV, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, (int)(j0 * kStep),
+                                                  (int)(j1 * kStep), io, w1 > w0, ctx, Lb);
       t += j1 - j0;
     }
   };
@@ -649,10 +733,10 @@ int resident_blocks(K kernel, int (&cached)[64]) {
 
 // The kernel variant for `p` is chosen once, here; `Fn` either launches it
 // or reports its balanced grid size.
-template <typename T, int D, int ROWS, bool DEBUG, bool UNIFORM>
+template <typename T, typename KV, int D, int ROWS, bool DEBUG, bool UNIFORM>
 struct Variant {
   static hipError_t launch(const LaunchParams &p, int row_blocks, hipStream_t stream) {
-    auto kernel = decode_kernel<T, D, ROWS, DEBUG, UNIFORM>;
+    auto kernel = decode_kernel<T, KV, D, ROWS, DEBUG, UNIFORM>;
     dim3 grid;
     if (p.balanced) {
       grid = dim3((unsigned)(p.grid_waves / 4), 1, 1);
@@ -665,18 +749,22 @@ struct Variant {
   }
   static int waves() {
     static int cached[64] = {0};
-    return 4 * resident_blocks(decode_kernel<T, D, ROWS, DEBUG, UNIFORM>, cached);
+    return 4 * resident_blocks(decode_kernel<T, KV, D, ROWS, DEBUG, UNIFORM>, cached);
   }
 };
 
-template <typename T, int D, int ROWS, typename Fn>
+template <typename T, typename KV, int D, int ROWS, typename Fn>
 auto dispatch_mode(const LaunchParams &p, Fn &&fn) {
-  constexpr int kStep = decode_step_keys(D, (int)sizeof(T));
-  const bool uniform = p.ps % kStep == 0;
+  // keys one page resolution covers (the page-uniform walk needs pages made
+  // of whole resolutions): a step, or 16 keys for fp8 pages
+  constexpr int kResKeys = sizeof(KV) == 1 ? 16 : decode_step_keys(D, (int)sizeof(KV));
+  const bool uniform = p.ps % kResKeys == 0;
   const bool debug = p.dbg_trace != nullptr || p.dbg_visits != nullptr;
   if (debug)
-    return uniform ? fn(Variant<T, D, ROWS, true, true>()) : fn(Variant<T, D, ROWS, true, false>());
-  return uniform ? fn(Variant<T, D, ROWS, false, true>()) : fn(Variant<T, D, ROWS, false, false>());
+    return uniform ? fn(Variant<T, KV, D, ROWS, true, true>())
+                   : fn(Variant<T, KV, D, ROWS, true, false>());
+  return uniform ? fn(Variant<T, KV, D, ROWS, false, true>())
+                 : fn(Variant<T, KV, D, ROWS, false, false>());
 }
 
 template <typename X>
@@ -687,22 +775,25 @@ struct TypeTag {
 template <typename Fn>
 auto dispatch(const LaunchParams &p, DType dt, Fn &&fn) {
   const int rows = decode_rows_per_block((p.Hq / p.Hkv) * p.L);
-  auto by_rows = [&](auto t, auto d) {
+  auto by_rows = [&](auto t, auto kv, auto d) {
     using TT = typename decltype(t)::type;
+    using KK = typename decltype(kv)::type;
     constexpr int DD = decltype(d)::value;
     switch (rows) {
-      case 1: return dispatch_mode<TT, DD, 1>(p, fn);
-      case 2: return dispatch_mode<TT, DD, 2>(p, fn);
-      case 4: return dispatch_mode<TT, DD, 4>(p, fn);
-      default: return dispatch_mode<TT, DD, 8>(p, fn);
+      case 1: return dispatch_mode<TT, KK, DD, 1>(p, fn);
+      case 2: return dispatch_mode<TT, KK, DD, 2>(p, fn);
+      case 4: return dispatch_mode<TT, KK, DD, 4>(p, fn);
+      default: return dispatch_mode<TT, KK, DD, 8>(p, fn);
     }
   };
   using F = TypeTag<float>;
   using H = TypeTag<uint16_t>;
+  using E = TypeTag<uint8_t>;  // fp8 E4M3 codes
   using D64 = std::integral_constant<int, 64>;
   using D128 = std::integral_constant<int, 128>;
-  if (dt == DType::F32) return p.D == 64 ? by_rows(F(), D64()) : by_rows(F(), D128());
-  return p.D == 64 ? by_rows(H(), D64()) : by_rows(H(), D128());
+  if (dt == DType::F32) return p.D == 64 ? by_rows(F(), F(), D64()) : by_rows(F(), F(), D128());
+  if (p.kv_fp8) return by_rows(H(), E(), D128());  // the host admits D = 128 only
+  return p.D == 64 ? by_rows(H(), H(), D64()) : by_rows(H(), H(), D128());
 }
 
 }  // namespace

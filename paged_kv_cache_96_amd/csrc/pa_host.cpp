@@ -39,8 +39,17 @@ pa_status check_sizes(const pa_args *a) {
   if (a->batch > kMaxGridYZ) return PA_ERR_INVALID_ARG;
   if (a->dtype != PA_DTYPE_F32 && a->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
   if (a->head_dim != 64 && a->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (a->kv_dtype != PA_KV_SAME && a->kv_dtype != PA_KV_FP8_E4M3) return PA_ERR_INVALID_ARG;
+  if (a->kv_dtype == PA_KV_FP8_E4M3) {
+    if (!(a->k_scale > 0.f) || !isfinite(a->k_scale) || !(a->v_scale > 0.f) ||
+        !isfinite(a->v_scale))
+      return PA_ERR_INVALID_ARG;
+    if (a->dtype != PA_DTYPE_BF16 || a->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  }
   return PA_OK;
 }
+
+bool kv_fp8(const pa_args *a) { return a->kv_dtype == PA_KV_FP8_E4M3; }
 
 pa_status check_pointers(const pa_args *a) {
   if (!a->query || !a->key_pages || !a->value_pages || !a->block_table || !a->context_lens ||
@@ -52,7 +61,10 @@ pa_status check_pointers(const pa_args *a) {
   return PA_OK;
 }
 
-int elem_bytes(const pa_args *a) { return a->dtype == PA_DTYPE_F32 ? 4 : 2; }
+// Bytes of one page element (the decode step depends on it).
+int elem_bytes(const pa_args *a) {
+  return kv_fp8(a) ? 1 : a->dtype == PA_DTYPE_F32 ? 4 : 2;
+}
 
 // Query rows of one decode row block.
 int64_t decode_block_rows(const pa_args *a) {
@@ -156,6 +168,9 @@ pa::LaunchParams make_params(const pa_args *a, int32_t S, int32_t P, bool balanc
   p.balanced = balanced ? 1 : 0;
   p.grid_waves = 0;
   p.scale_log2 = a->scale * 1.4426950408889634f;
+  p.kv_fp8 = kv_fp8(a) ? 1 : 0;
+  p.k_scale = kv_fp8(a) ? a->k_scale : 1.f;
+  p.v_scale = kv_fp8(a) ? a->v_scale : 1.f;
   if (balanced) p.grid_waves = pa::decode_balanced_waves(p, (pa::DType)a->dtype);
   return p;
 }
@@ -289,6 +304,7 @@ PA_EXPORT pa_status pa_prefill_plan(const pa_args *args, int32_t num_cus, pa_wor
   pa_status st = check_sizes(args);
   if (st != PA_OK) return st;
   if (!plan) return PA_ERR_INVALID_ARG;
+  if (kv_fp8(args)) return PA_ERR_UNSUPPORTED;  // fp8 pages: decode path only
   plan->schedule = PA_SCHEDULE_KEY_SPLIT;
   plan->partition_tokens = 0;
   plan->num_splits = 0;
@@ -311,6 +327,7 @@ PA_EXPORT pa_status pa_prefill_plan(const pa_args *args, int32_t num_cus, pa_wor
 PA_EXPORT pa_status pa_prefill(const pa_args *args, const pa_workspace *ws, void *stream) {
   pa_status st = check_sizes(args);
   if (st != PA_OK) return st;
+  if (kv_fp8(args)) return PA_ERR_UNSUPPORTED;  // fp8 pages: decode path only
   if (args->batch == 0) return PA_OK;
   if ((st = check_pointers(args)) != PA_OK) return st;
   const int32_t cap = args->max_pages * args->page_size;
@@ -381,6 +398,14 @@ PA_EXPORT pa_status pa_append(const pa_append_args *args, void *stream) {
   if ((int64_t)a->num_pages * a->page_size > INT32_MAX) return PA_ERR_INVALID_ARG;
   if (a->dtype != PA_DTYPE_F32 && a->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
   if (a->head_dim != 64 && a->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (a->cache_dtype != PA_KV_SAME && a->cache_dtype != PA_KV_FP8_E4M3) return PA_ERR_INVALID_ARG;
+  const bool fp8 = a->cache_dtype == PA_KV_FP8_E4M3;
+  if (fp8) {
+    if (!(a->k_scale > 0.f) || !isfinite(a->k_scale) || !(a->v_scale > 0.f) ||
+        !isfinite(a->v_scale))
+      return PA_ERR_INVALID_ARG;
+    if (a->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  }
   if (!a->key_pages || !a->value_pages || !aligned16(a->key_pages) ||
       !aligned16(a->value_pages))
     return PA_ERR_INVALID_ARG;
@@ -398,6 +423,9 @@ PA_EXPORT pa_status pa_append(const pa_append_args *args, void *stream) {
   p.ps = a->page_size;
   p.num_slots = a->num_pages * a->page_size;
   p.row_bytes = a->head_dim * (a->dtype == PA_DTYPE_F32 ? 4 : 2);
+  p.fp8 = fp8 ? 1 : 0;
+  p.k_scale = fp8 ? a->k_scale : 1.f;
+  p.v_scale = fp8 ? a->v_scale : 1.f;
   return hip_status(pa::launch_append(p, (hipStream_t)stream));
 }
 

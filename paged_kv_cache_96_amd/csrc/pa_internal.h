@@ -32,6 +32,8 @@ struct LaunchParams {
   int32_t balanced;         // 1: equal runs of steps per wave (see decode_balanced_waves)
   int32_t grid_waves;       // balanced: waves of the decode grid
   float scale_log2;         // scale * log2(e): scores are kept in base-2 units
+  int32_t kv_fp8;           // 1: the pages hold fp8 E4M3 codes (query and out bf16)
+  float k_scale, v_scale;   // fp8 pages: element value = code value * scale (else 1)
 };
 
 // Vector-ALU paged decode kernel (also the fp32 prefill path, with S == 1).
@@ -84,7 +86,8 @@ __host__ __device__ inline int64_t isqrt64(int64_t x) {
 constexpr int kSplitMaxPairs = 2048;
 
 // Keys per decode step (one 16-byte load per lane, four loads per step):
-// 16 for bf16 with D = 128.
+// 16 for bf16 with D = 128, 32 for fp8 pages with D = 128.  elem_bytes is
+// the byte size of a page element.
 __host__ __device__ constexpr int decode_step_keys(int D, int elem_bytes) {
   return 4096 / (D * elem_bytes);
 }

@@ -47,7 +47,9 @@ __device__ void balanced_waves(const LaunchParams &p, int b, int u, int units, l
   count = (int)(bs.wave_of(row0 + n - 1) - w0 + 1);
 }
 
-template <typename T, int D>
+// KVB: bytes of a page element (the decode step, and so the balanced split,
+// depends on it).
+template <typename T, int D, int KVB>
 __global__ __launch_bounds__(256) void split_reduce_kernel(LaunchParams p, int total_rows) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= total_rows) return;
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(LaunchParams p, int t
     const int u = g * row_blocks + rho / rows;
     long long w0;
     int pieces;
-    balanced_waves<decode_step_keys(D, (int)sizeof(T))>(p, b, u, p.Hkv * row_blocks, w0, pieces);
+    balanced_waves<decode_step_keys(D, KVB)>(p, b, u, p.Hkv * row_blocks, w0, pieces);
     if (pieces == 1) return;  // the decode kernel wrote this row
     n = i < Lb ? pieces : 0;
     const size_t first = ((size_t)b * p.Hkv * row_blocks + u + w0) * rows + rho % rows;
@@ -88,11 +90,11 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(LaunchParams p, int t
   merge_row<T, D>(lse, po, (int)stride, n, reinterpret_cast<T *>(p.out) + (size_t)row * D);
 }
 
-template <typename T, int D>
+template <typename T, int D, int KVB = (int)sizeof(T)>
 hipError_t launch(const LaunchParams &p, hipStream_t stream) {
   const int rows = p.B * p.Hq * p.L;
-  hipLaunchKernelGGL((split_reduce_kernel<T, D>), dim3((rows + 3) / 4), dim3(256), 0, stream, p,
-                     rows);
+  hipLaunchKernelGGL((split_reduce_kernel<T, D, KVB>), dim3((rows + 3) / 4), dim3(256), 0, stream,
+                     p, rows);
   return hipGetLastError();
 }
 
@@ -100,6 +102,7 @@ hipError_t launch(const LaunchParams &p, hipStream_t stream) {
 
 hipError_t launch_split_reduce(const LaunchParams &p, DType dt, hipStream_t stream) {
   if (dt == DType::F32) return p.D == 64 ? launch<float, 64>(p, stream) : launch<float, 128>(p, stream);
+  if (p.kv_fp8) return launch<uint16_t, 128, 1>(p, stream);  // fp8 pages: D = 128 only
   return p.D == 64 ? launch<uint16_t, 64>(p, stream) : launch<uint16_t, 128>(p, stream);
 }
 

@@ -19,7 +19,9 @@ struct AppendParams {
   int32_t Hkv;
   int32_t ps;
   int32_t num_slots;     // num_pages * page_size (< 2^31)
-  int32_t row_bytes;     // head_dim * element bytes: 128, 256 or 512
+  int32_t row_bytes;     // head_dim * source element bytes: 128, 256 or 512
+  int32_t fp8;           // 1: bf16 rows quantised into fp8 E4M3 pages
+  float k_scale, v_scale;
 };
 hipError_t launch_append(const AppendParams &p, hipStream_t stream);
 

@@ -44,6 +44,13 @@ class DeviceInputs:
         return torch.full_like(self.q, float("nan"))
 
 
+def kv_scales(x) -> dict:
+    """make_args keywords for fp8 pages (empty otherwise)."""
+    if getattr(x, "kv_dtype", None) == "fp8_e4m3":
+        return dict(k_scale=x.k_scale, v_scale=x.v_scale)
+    return {}
+
+
 def run_decode(api, d: DeviceInputs, *, partition_tokens=0, trace=False, keep_ws=False,
                num_cus=0, fused=True):
     """pa_decode (+ pa_split_reduce) through the C ABI with the library's
@@ -58,7 +65,8 @@ def run_decode(api, d: DeviceInputs, *, partition_tokens=0, trace=False, keep_ws
         dbg_t = torch.full((x.B, cap, 2), -1, dtype=torch.int32, device=d.q.device)
         dbg_v = torch.zeros((x.B, x.H_kv, cap), dtype=torch.int32, device=d.q.device)
     args = api.make_args(d.q, d.kp, d.vp, d.bt, d.cl, out, scale=x.scale, mask=d.mask,
-                         query_lens=d.ql, debug_trace=dbg_t, debug_visits=dbg_v)
+                         query_lens=d.ql, debug_trace=dbg_t, debug_visits=dbg_v,
+                         **kv_scales(x))
     plan = api.pa_decode_plan(args, partition_tokens=partition_tokens, num_cus=num_cus)
     S, P, nbytes = plan.num_splits, plan.partition_tokens, plan.workspace_bytes
     ws = api.Workspace.for_plan(plan, d.q, fused=fused)

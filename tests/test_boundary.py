@@ -41,7 +41,7 @@ def test_header_and_library_exports_agree(L):
     assert exported == declared
     for name in declared:
         assert hasattr(L, name)
-    assert L.pa_abi_version() == 7
+    assert L.pa_abi_version() == 8
 
 
 def test_status_strings(L):
@@ -362,3 +362,47 @@ def test_noalloc_refuses_calls_beyond_its_scratch(L):
     # argument errors come first, as for pa_decode
     a.q_len = 9
     assert L.pa_decode_noalloc(ctypes.byref(a), None) == _lib.PA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kv_dtype=2), -1),                                     # unknown page type
+    (dict(kv_dtype=1, k_scale=0.0, v_scale=1.0), -1),           # scales finite and > 0
+    (dict(kv_dtype=1, k_scale=1.0, v_scale=float("nan")), -1),
+    (dict(kv_dtype=1, k_scale=-1.0, v_scale=1.0), -1),
+    (dict(kv_dtype=1, k_scale=1.0, v_scale=1.0, dtype=0), -2),  # fp8 pages need a bf16 query
+    (dict(kv_dtype=1, k_scale=1.0, v_scale=1.0, head_dim=64), -2),  # and head_dim 128
+])
+def test_fp8_pages_validation(L, kw, code):
+    h = HostBuffers()
+    assert _decode(L, h.args(**kw)) == code
+
+
+def test_fp8_pages_are_decode_only(L):
+    """fp8 pages go through the decode path (and the router's decode route);
+    the prefill path refuses them before any launch."""
+    h = HostBuffers()
+    a = h.args(kv_dtype=1, k_scale=0.5, v_scale=0.5, q_len=64)
+    assert L.pa_prefill(ctypes.byref(a), None, None) == -2
+    ws = PaWorkspace()
+    n = ctypes.c_size_t(0)
+    assert L.pa_prefill_plan(ctypes.byref(a), 0, ctypes.byref(ws), ctypes.byref(n)) == -2
+    assert L.pa_attention(ctypes.byref(a), None, None) == -2
+    a.q_len = 1
+    assert L.pa_decode_plan(ctypes.byref(a), 0, ctypes.byref(ws), ctypes.byref(n)) == 0
+    assert ws.schedule == SCHEDULE_BALANCED
+    # a bf16 call with the same step budget: fp8 steps hold 32 keys, not 16
+    b = h.args(q_len=1)
+    wb = PaWorkspace()
+    assert L.pa_decode_plan(ctypes.byref(b), 0, ctypes.byref(wb), ctypes.byref(n)) == 0
+    assert wb.num_splits == ws.num_splits
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cache_dtype=2), -1),
+    (dict(cache_dtype=1, k_scale=0.0, v_scale=1.0), -1),
+    (dict(cache_dtype=1, k_scale=1.0, v_scale=float("inf")), -1),
+    (dict(cache_dtype=1, k_scale=1.0, v_scale=1.0, dtype=0), -2),   # fp32 rows: not supported
+])
+def test_fp8_append_validation(L, kw, code):
+    h = HostBuffers()
+    assert L.pa_append(ctypes.byref(_append_args(h, **kw)), None) == code

@@ -136,3 +136,34 @@ def test_fp8_pins_hold_on_the_fp32_build():
     for s in ((1.0, 1.0), (0.5, 0.25)):
         test_fp8_pages_equal_bf16_pages_holding_the_values(s, lib_path=lib32)
     test_fp8_stale_codes_are_ignored_bit_identically("nan", lib_path=lib32)
+
+
+def test_fp8_scatter_writes_hand_derived_codes_and_nothing_else():
+    """The write side with an fp8 pool: planted rows whose quotients by the
+    scale are exact values, ties, overflows and NaN land as the hand-derived
+    codes; every other byte of the pool is untouched; a negative slot skips
+    its token."""
+    from oracle.scatter import scatter_tokens_fp8
+    from workloads import f32_to_bf16_bits
+    P, H, ps, D = 3, 2, 4, 4
+    kp = np.full((P, H, ps, D), 0xAB, np.uint8)
+    vp = np.full((P, H, ps, D), 0xCD, np.uint8)
+    ks, vs = 0.5, 2.0
+    # key / ks and value / vs per element (all exact in bf16 and in fp32)
+    kq = np.array([[[1.0, 1.0625, 1.1875, -3.75], [2.0 ** -10, 3 * 2.0 ** -10, 448.0, 1e4]],
+                   [[0.0, -0.0, 0.5, 256.0], [-1e4, 15 * 2.0 ** -10, 1.125, -1.0]]], np.float32)
+    kcodes = [[[0x38, 0x38, 0x3A, 0xC7], [0x00, 0x02, 0x7E, 0x7E]],
+              [[0x00, 0x80, 0x30, 0x78], [0xFE, 0x08, 0x39, 0xB8]]]
+    key = f32_to_bf16_bits(kq * np.float32(ks))
+    value = f32_to_bf16_bits(np.full((2, H, D), 3.0, np.float32) * np.float32(vs))
+    value[1, 0, 2] = 0x7FC0                      # a bf16 NaN -> NaN code
+    slots = [1 * ps + 2, 2 * ps + 0]             # page 1 slot 2, page 2 slot 0
+    k2, v2 = scatter_tokens_fp8(kp, vp, key, value, slots, ks, vs)
+    assert k2[1, :, 2].tolist() == kcodes[0] and k2[2, :, 0].tolist() == kcodes[1]
+    assert (v2[1, :, 2] == 0x44).all()           # 3.0 = 1.5 * 2^1: e 8, m 4
+    assert v2[2, 0, 0].tolist() == [0x44, 0x44, 0x7F, 0x44] and (v2[2, 1, 0] == 0x44).all()
+    touched = np.zeros((P, H, ps, D), bool)
+    touched[1, :, 2] = touched[2, :, 0] = True
+    assert (k2[~touched] == 0xAB).all() and (v2[~touched] == 0xCD).all()
+    k3, _ = scatter_tokens_fp8(kp, vp, key, value, [-1, 2 * ps + 0], ks, vs)
+    assert (k3[1] == 0xAB).all() and k3[2, :, 0].tolist() == kcodes[1]

@@ -490,20 +490,24 @@ class AppendInputs:
         return int(self.slot_mapping.shape[0])
 
     def moved_bytes(self) -> int:
-        """Bytes an append reads plus writes for the tokens with a slot."""
+        """Bytes an append reads plus writes for the tokens with a slot (K and
+        V rows read in `dtype`, written in the pool's element type)."""
         p = self.paged
         live = int((self.slot_mapping >= 0).sum())
-        return live * p.H_kv * p.D * (4 if p.dtype == "f32" else 2) * 2 * 2
+        src = 4 if p.dtype == "f32" else 2
+        return live * p.H_kv * p.D * (src + p.kv_elem_bytes()) * 2
 
 
 def make_append(seed: int, *, B: int, H_kv: int, D: int, page_size: int,
                 ctx_old: Union[Sequence[int], tuple], n_new: Union[Sequence[int], tuple],
                 dtype: str = "bf16", pad_tokens: int = 0, extra_free_pages: int = 3,
-                garbage=GARBAGE_DEFAULT, name: str = "append") -> AppendInputs:
+                garbage=GARBAGE_DEFAULT, name: str = "append",
+                kv_dtype: Optional[str] = None, kv_scales=(0.5, 0.5)) -> AppendInputs:
     """Random write-path inputs.  Draw order: the paged pool of the grown
     contexts (make_random with this seed) -> old context lengths (when a
     range) -> new-token counts (when a range) -> pad positions -> K rows ->
-    V rows, from a child stream of the seed."""
+    V rows, from a child stream of the seed.  kv_dtype "fp8_e4m3": the pool
+    holds fp8 codes with scales kv_scales; the new rows stay in `dtype`."""
     rng = np.random.default_rng([seed, 1])
     old = ([int(v) for v in rng.integers(ctx_old[0], ctx_old[1] + 1, size=B)]
            if isinstance(ctx_old, tuple) else [int(v) for v in ctx_old])
@@ -513,7 +517,8 @@ def make_append(seed: int, *, B: int, H_kv: int, D: int, page_size: int,
     grown = [o + n for o, n in zip(old, new)]
     paged = make_random(seed, B=B, H_q=H_kv, H_kv=H_kv, L=1, D=D, page_size=page_size,
                         ctx=grown, dtype=dtype, causal=False,
-                        extra_free_pages=extra_free_pages, garbage=garbage, name=name)
+                        extra_free_pages=extra_free_pages, garbage=garbage, name=name,
+                        kv_dtype=kv_dtype, kv_scales=kv_scales)
     slots = []
     bt = paged.block_table
     for b in range(B):
