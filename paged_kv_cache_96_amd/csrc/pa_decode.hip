@@ -109,22 +109,21 @@ __device__ __forceinline__ uint32_t word(const Vec &v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-typedef float f32x2_v __attribute__((ext_vector_type(2)));
-
 // The elements of a lane's page load as bf16 pairs: pair j holds elements
 // 2j and 2j + 1.  bf16 pages: the loaded words.  fp8 pages: every code
-// widened exactly (an E4M3 value is a bf16 value) with the hardware
-// converter, whose results match the format's definition for all 256 codes.
+// widened exactly (an E4M3 value is a bf16 value) by the hardware converter
+// of two codes to a bf16 pair, with scale 1 (its results match the
+// format's definition for all 256 codes, checked on the device).
 template <typename KV>
 __device__ __forceinline__ void to_pairs(const Vec &v, uint32_t (&pr)[Elem<KV>::kPerVec / 2]) {
   if constexpr (sizeof(KV) == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t w = word(v, i);
-      const f32x2_v lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);  // bytes 0, 1
-      const f32x2_v hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);   // bytes 2, 3
-      pr[2 * i] = cvt_pk_bf16(lo[0], lo[1]);
-      pr[2 * i + 1] = cvt_pk_bf16(hi[0], hi[1]);
+      pr[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
+                                                   w, 1.0f, false));  // bytes 0, 1
+      pr[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
+                                                       w, 1.0f, true));  // bytes 2, 3
     }
   } else {
 #pragma unroll
