@@ -155,6 +155,37 @@ class Runner:
         torch.cuda.synchronize()
         return {"ms": np.array([e[0].elapsed_time(e[1]) for e in ev])}
 
+    def time_ragged(self, r, steps, warmup, flush=True):
+        """Times ONE pa_attention call over the packed rows of the ragged
+        batch `r` (decode kernel for its one-row requests, prefill kernel for
+        the rest, on one stream), workspace set up outside the timed region;
+        the last-level cache is flushed before each call."""
+        torch, api = self.torch, self.api
+        from tests._gpu import dev
+        qd = dev(r.query)
+        kp, vp = dev(r.key_pages), dev(r.value_pages)
+        bt, cl, ql = dev(r.block_table), dev(r.context_lens), dev(r.query_start_loc)
+        out = torch.empty_like(qd)
+        args = api.make_args(qd, kp, vp, bt, cl, out, scale=r.scale,
+                             mask="causal" if r.causal else "none", query_start_loc=ql,
+                             max_query_len=r.max_query_len)
+        ap = api.pa_attention_plan(args)
+        ws = api.attention_workspace(ap, args, qd)
+        for _ in range(warmup):
+            if flush:
+                self.flush()
+            api.pa_attention(args, ws)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for k in range(steps):
+            if flush:
+                self.flush()
+            ev[k][0].record()
+            api.pa_attention(args, ws)
+            ev[k][1].record()
+        torch.cuda.synchronize()
+        return {"ms": np.array([e[0].elapsed_time(e[1]) for e in ev]), "route": ap.route}
+
     def time_prefill(self, d, steps, warmup, flush=False, split=True):
         """Times pa_prefill; `split` passes the key-split workspace of the
         library's plan (allocated outside the timed region)."""
@@ -566,6 +597,15 @@ def main():
         sections["mixed_C5"]["roofline_decode"]["note"] = \
             "achieved on unique K/V bytes (shared prefix pages counted once)"
         del dd, dp, rd, rp
+        # the same 56 requests as ONE call over packed query rows
+        rr = run.time_ragged(W.pack_ragged(m), max(10, args.steps // 3), args.warmup)
+        om = float(np.mean(rr["ms"]))
+        log(f"[bench] mixed C5 as one ragged call: {om * 1e3:.1f} us "
+            f"(two calls {(sm + pm) * 1e3:.1f} us)")
+        sections["mixed_C5"]["one_call"] = {
+            "what": "one pa_attention call over packed rows (query_start_loc): the decode "
+                    "kernel for the 48 one-row requests, the prefill kernel for the 8 others",
+            **_stats(rr["ms"])}
     if "small" in only:
         # latency-bound decode: one to four requests over long contexts
         # (H 32/8, D 128, page 16), where the merge of many pieces per row

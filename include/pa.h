@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 8
+#define PA_ABI_VERSION 9
 
 typedef enum {
   PA_OK = 0,
@@ -129,6 +129,13 @@ typedef struct pa_args {
   int32_t kv_dtype;
   float k_scale;               /* fp8 pages: finite and > 0 (ignored otherwise) */
   float v_scale;               /* fp8 pages: finite and > 0 (ignored otherwise) */
+  /* Packed (ragged) query rows, or NULL.  When given, query and out are
+   * [T, H_q, D] with T = query_start_loc[batch]: request b owns rows
+   * query_start_loc[b] .. query_start_loc[b + 1] - 1 (0 = query_start_loc[0]
+   * <= ... nondecreasing), and no padding rows exist or are written.
+   * q_len is then an upper bound on every request's row count (it sizes
+   * tiles and plans), and query_lens must be NULL. */
+  const int32_t *query_start_loc;
 } pa_args;
 
 /* How pa_decode divides a call's keys among the waves of the GPU. */
@@ -182,6 +189,9 @@ typedef struct pa_workspace {
    * caller zeroes them once before first use; every call leaves them zero.
    * NULL: no run-time chunks, and pa_split_reduce merges. */
   uint32_t *counters;
+  /* Ragged route of pa_attention only: the key-split slots of its prefill
+   * part (0 otherwise). */
+  int32_t prefill_splits;
 } pa_workspace;
 
 /* Choose the plan of pa_decode for `args` (only the sizes in `args` are
@@ -250,11 +260,31 @@ pa_status pa_prefill(const pa_args *args, const pa_workspace *ws, void *stream);
  * the prefill path otherwise.  Measured on MI355X with 64 requests of
  * U[128, 4096] keys, H_q 32, H_kv 8, D 128, bf16: L = 1 decode 125 us vs
  * prefill 191 us; L = 2 149 vs 171; L = 4 298 vs 195; L = 8 627 vs 195. */
-typedef enum { PA_ROUTE_DECODE = 0, PA_ROUTE_PREFILL = 1 } pa_route;
+typedef enum { PA_ROUTE_DECODE = 0, PA_ROUTE_PREFILL = 1, PA_ROUTE_RAGGED = 2 } pa_route;
+
+/* Ragged batches (packed rows, query_start_loc given, q_len > 1): the shape
+ * decision is taken per request, in one call on one stream.  A request of
+ * one query row (G <= 8) takes the decode path, every other request the
+ * prefill path; pa_attention enqueues the decode kernel for the first kind
+ * and the prefill kernel for the second, each skipping the other's
+ * requests.  Route PA_ROUTE_RAGGED; its workspace holds both paths' parts,
+ * each in its own region:
+ *   partial_out  decode: num_splits * R * head_dim floats, then prefill:
+ *                prefill_splits * head_dim * 128 floats;
+ *   partial_lse  decode: num_splits * R floats rounded up to a multiple of
+ *                16, then prefill: prefill_splits * 512 floats;
+ *   counters     decode: batch * H_kv, then prefill: prefill_splits;
+ * with R the decode rows per block (the smallest of 1, 2, 4, 8 that holds G),
+ * num_splits the decode plan's piece slots (balanced schedule, merge fused)
+ * and prefill_splits the prefill plan's key-split slots.  The counters are
+ * zeroed once by the caller and left zero by every call. */
 
 /* The plan of pa_attention: *route (if not NULL) receives the path, and
  * `plan` / *workspace_bytes are those of pa_decode_plan (decode route;
- * plan->partition_tokens on input as there) or pa_prefill_plan. */
+ * plan->partition_tokens on input as there), pa_prefill_plan, or for the
+ * ragged route both (plan->num_splits, num_counters: the decode part;
+ * plan->prefill_splits: the prefill part; *workspace_bytes: all of
+ * partial_out and partial_lse). */
 pa_status pa_attention_plan(const pa_args *args, int32_t num_cus, pa_workspace *plan,
                             size_t *workspace_bytes, int32_t *route);
 

@@ -55,6 +55,7 @@ class PaArgs(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
+        ("query_start_loc", ctypes.c_void_p),
     ]
 
 
@@ -67,6 +68,7 @@ class PaWorkspace(ctypes.Structure):
         ("schedule", ctypes.c_int32),
         ("num_counters", ctypes.c_int32),
         ("counters", ctypes.c_void_p),
+        ("prefill_splits", ctypes.c_int32),
     ]
 
 
@@ -89,10 +91,11 @@ class PaAppendArgs(ctypes.Structure):
     ]
 
 
-ABI_VERSION = 8  # PA_ABI_VERSION of the structs below
+ABI_VERSION = 9  # PA_ABI_VERSION of the structs below
 
 ROUTE_DECODE = 0
 ROUTE_PREFILL = 1
+ROUTE_RAGGED = 2
 
 SCHEDULE_PARTITIONS = 0
 SCHEDULE_BALANCED = 1

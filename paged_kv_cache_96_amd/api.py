@@ -56,10 +56,22 @@ def make_args(query: torch.Tensor, key_pages: torch.Tensor, value_pages: torch.T
               query_lens: Optional[torch.Tensor] = None,
               debug_trace: Optional[torch.Tensor] = None,
               debug_visits: Optional[torch.Tensor] = None,
-              k_scale: Optional[float] = None, v_scale: Optional[float] = None) -> PaArgs:
+              k_scale: Optional[float] = None, v_scale: Optional[float] = None,
+              query_start_loc: Optional[torch.Tensor] = None,
+              max_query_len: Optional[int] = None) -> PaArgs:
     """Fill a pa_args from tensors (shapes as in include/pa.h).  uint8 pages
-    are fp8 E4M3 codes (PA_KV_FP8_E4M3) and need k_scale and v_scale."""
-    B, Hq, L, D = query.shape
+    are fp8 E4M3 codes (PA_KV_FP8_E4M3) and need k_scale and v_scale.  With
+    query_start_loc ([B + 1] int32) the query and out are packed rows
+    [T, H_q, D] and max_query_len bounds every request's rows."""
+    if query_start_loc is not None:
+        if query.dim() != 3 or max_query_len is None or query_lens is not None:
+            raise ValueError("packed rows: query [T, H_q, D], max_query_len, no query_lens")
+        T, Hq, D = query.shape
+        B, L = block_table.shape[0], int(max_query_len)
+        _int32(query_start_loc, "query_start_loc")
+        _shape(query_start_loc, (B + 1,), "query_start_loc")
+    else:
+        B, Hq, L, D = query.shape
     P, Hkv, ps, D2 = key_pages.shape
     if D2 != D or tuple(value_pages.shape) != tuple(key_pages.shape):
         raise ValueError("query / key_pages / value_pages head sizes disagree")
@@ -79,7 +91,8 @@ def make_args(query: torch.Tensor, key_pages: torch.Tensor, value_pages: torch.T
     _int32(debug_visits, "debug_visits")
     _same_gpu(query, key_pages=key_pages, value_pages=value_pages, block_table=block_table,
               context_lens=context_lens, out=out, query_lens=query_lens,
-              debug_trace=debug_trace, debug_visits=debug_visits)
+              debug_trace=debug_trace, debug_visits=debug_visits,
+              query_start_loc=query_start_loc)
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be [batch, max_pages]")
     cap = block_table.shape[1] * ps
@@ -105,6 +118,7 @@ def make_args(query: torch.Tensor, key_pages: torch.Tensor, value_pages: torch.T
     a.kv_dtype = _lib.PA_KV_FP8_E4M3 if fp8 else _lib.PA_KV_SAME
     a.k_scale = float(k_scale) if fp8 else 1.0
     a.v_scale = float(v_scale) if fp8 else 1.0
+    a.query_start_loc = _ptr(query_start_loc)
     return a
 
 
@@ -268,10 +282,45 @@ def pa_prefill(args: PaArgs, workspace: Optional[PrefillWorkspace] = None, strea
 
 
 class AttentionPlan(NamedTuple):
-    """pa_attention_plan's choice: the route (ROUTE_DECODE or ROUTE_PREFILL)
-    and the plan of that route's path."""
+    """pa_attention_plan's choice: the route (ROUTE_DECODE, ROUTE_PREFILL or
+    ROUTE_RAGGED) and the plan of that route's path."""
     route: int
-    plan: object  # DecodePlan or PrefillPlan
+    plan: object  # DecodePlan, PrefillPlan or RaggedPlan
+
+
+class RaggedPlan(NamedTuple):
+    """Both parts of a ragged call: the decode part's piece slots and
+    counters, the prefill part's key-split slots, and the bytes of
+    partial_out plus partial_lse (see include/pa.h, PA_ROUTE_RAGGED)."""
+    num_splits: int
+    num_counters: int
+    prefill_splits: int
+    workspace_bytes: int
+
+
+class RaggedWorkspace:
+    """Device buffers of a ragged plan, laid out as include/pa.h describes
+    for PA_ROUTE_RAGGED (torch owns the memory; counters zeroed once on
+    torch's current stream)."""
+
+    def __init__(self, plan: RaggedPlan, rows_per_block: int, D: int, device):
+        S, Sp = int(plan.num_splits), int(plan.prefill_splits)
+        lse_dec = -(-S * rows_per_block // 16) * 16
+        self.partial_out = torch.empty(S * rows_per_block * D + Sp * D * 128, dtype=torch.float32,
+                                       device=device)
+        self.partial_lse = torch.empty(lse_dec + Sp * 512, dtype=torch.float32, device=device)
+        self.counters = torch.zeros(int(plan.num_counters), dtype=torch.int32, device=device)
+        self.c = PaWorkspace()
+        self.c.partial_out = _ptr(self.partial_out)
+        self.c.partial_lse = _ptr(self.partial_lse)
+        self.c.counters = _ptr(self.counters)
+        self.c.num_splits = S
+        self.c.schedule = SCHEDULE_BALANCED
+        self.c.num_counters = int(plan.num_counters)
+        self.c.prefill_splits = Sp
+
+    def tensors(self):
+        return [self.partial_out, self.partial_lse, self.counters]
 
 
 def pa_attention_plan(args: PaArgs, *, num_cus: int = 0,
@@ -286,16 +335,34 @@ def pa_attention_plan(args: PaArgs, *, num_cus: int = 0,
     if route.value == _lib.ROUTE_DECODE:
         plan = DecodePlan(ws.num_splits, ws.partition_tokens, nbytes.value, ws.schedule,
                           ws.num_counters)
+    elif route.value == _lib.ROUTE_RAGGED:
+        plan = RaggedPlan(ws.num_splits, ws.num_counters, ws.prefill_splits, nbytes.value)
     else:
         plan = PrefillPlan(ws.num_splits, nbytes.value, ws.num_counters)
     return AttentionPlan(route.value, plan)
+
+
+def _rows_per_block(G: int) -> int:
+    for r in (1, 2, 4, 8):
+        if G <= r:
+            return r
+    return 8
 
 
 def attention_workspace(ap: AttentionPlan, args: PaArgs, query: torch.Tensor):
     """Device buffers for an AttentionPlan (decode: with arrival counters, so
     the merge runs inside pa_decode)."""
     if ap.route == _lib.ROUTE_DECODE:
+        if query.dim() == 3:  # packed rows: states per row block, not per row
+            return Workspace(args.batch, args.num_q_heads, 1, args.head_dim, ap.plan.num_splits,
+                             ap.plan.partition_tokens, query.device, schedule=ap.plan.schedule,
+                             block_rows=(ap.plan.workspace_bytes //
+                                         max(1, ap.plan.num_splits * (args.head_dim + 1) * 4)),
+                             num_counters=ap.plan.num_counters)
         return Workspace.for_plan(ap.plan, query, fused=True)
+    if ap.route == _lib.ROUTE_RAGGED:
+        G = args.num_q_heads // args.num_kv_heads
+        return RaggedWorkspace(ap.plan, _rows_per_block(G), args.head_dim, query.device)
     return PrefillWorkspace(ap.plan, args.head_dim, query.device)
 
 
@@ -310,7 +377,9 @@ def paged_attention(query: torch.Tensor, key_pages: torch.Tensor, value_pages: t
                     query_lens: Optional[torch.Tensor] = None, partition_tokens: int = 0,
                     out: Optional[torch.Tensor] = None, stream=None,
                     k_scale: Optional[float] = None,
-                    v_scale: Optional[float] = None) -> torch.Tensor:
+                    v_scale: Optional[float] = None,
+                    query_start_loc: Optional[torch.Tensor] = None,
+                    max_query_len: Optional[int] = None) -> torch.Tensor:
     """Convenience call through the library's router (pa_attention): the
     decode path when the query rows of one kv head fit a decode row block,
     the prefill path otherwise.  The workspace is allocated (and its
@@ -320,7 +389,8 @@ def paged_attention(query: torch.Tensor, key_pages: torch.Tensor, value_pages: t
     if out is None:
         out = torch.empty_like(query)
     args = make_args(query, key_pages, value_pages, block_table, context_lens, out, scale=scale,
-                     mask=mask, query_lens=query_lens, k_scale=k_scale, v_scale=v_scale)
+                     mask=mask, query_lens=query_lens, k_scale=k_scale, v_scale=v_scale,
+                     query_start_loc=query_start_loc, max_query_len=max_query_len)
     ap = pa_attention_plan(args, partition_tokens=partition_tokens)
     ws = attention_workspace(ap, args, query)
     if stream is not None:

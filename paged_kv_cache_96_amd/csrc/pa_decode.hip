@@ -188,7 +188,7 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
     const int h = g * G + (rho - i * G);
     valid[r] = rho < G * p.L && i < Lb;
     hi[r] = valid[r] ? (p.causal ? ctx - Lb + i + 1 : ctx) : 0;
-    qrow[r] = ((size_t)(b * p.Hq + h) * p.L + i);
+    qrow[r] = query_row(p, b, h, i);
     kmax = max(kmax, hi[r]);
     if (valid[r]) kmin = min(kmin, hi[r]);
   }
@@ -200,8 +200,9 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
   const T *qbase = reinterpret_cast<const T *>(p.q);
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
-    // rows past query_lens are in bounds (i < L): load unconditionally, then drop
-    const bool exists = rb * ROWS + r < G * p.L;
+    // padded rows past query_lens are in bounds (i < L): load unconditionally,
+    // then drop; packed rows past the request's own do not exist
+    const bool exists = p.qsl ? valid[r] : rb * ROWS + r < G * p.L;
 #pragma unroll
     for (int v = 0; v < kQVecs; ++v) {
       const Vec x = exists ? *reinterpret_cast<const Vec *>(qbase + qrow[r] * D + c * kElems +
@@ -490,6 +491,9 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
 
   // ---- merge the lane groups in registers, then write this partition
   T *out = reinterpret_cast<T *>(p.out);
+  // rows written: padded rows up to G * L (past query_lens as zeros); packed
+  // rows of the request only
+  const int rows_out = p.qsl ? G * Lb : G * p.L;
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
     const float M = stride_max<kLpt>(m[r]);
@@ -498,7 +502,7 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
 #pragma unroll
     for (int e = 0; e < kElems; ++e) acc[r][e] = stride_sum<kLpt>(acc[r][e] * f);
     const int rho = rb * ROWS + r;
-    if (rho >= G * p.L) continue;  // row outside the packed range
+    if (rho >= rows_out) continue;  // a row that does not exist (or is not written)
     const bool has = valid[r] && lt > 0.f;
     // fp8 pages: the values carry v_scale, applied once here
     const float inv = has ? (kFp8 ? p.v_scale / lt : 1.f / lt) : 0.f;
@@ -554,7 +558,7 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
       asm volatile("" ::: "memory");
       const size_t wi = (size_t)io.first * ROWS;
       merge_block<T, D, ROWS>(p.ws_lse + wi, p.ws_o + wi * D, io.pieces, valid, qrow,
-                              min(ROWS, G * p.L - rb * ROWS), out);
+                              min(ROWS, rows_out - rb * ROWS), out);
       if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -592,7 +596,8 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
     const int b = blockIdx.y;
     if (s >= p.num_splits) return;
     const int ctx = p.cl[b];
-    const int Lb = p.ql ? p.ql[b] : p.L;
+    const int Lb = query_rows(p, b);
+    if (!routed_here(p, Lb)) return;
     const int t0 = s * p.part_tokens;
     if (s > 0 && t0 >= ctx) return;  // never read by the merge
     const bool split = p.num_splits > 1;
@@ -616,9 +621,10 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
   for (int k = 0; k < per; ++k) {
     const int b = tid * per + k;
     if (b < B) {
-      const int ctx = p.cl[b];
+      // a request of another route counts as one without keys
+      const int ctx = routed_here(p, query_rows(p, b)) ? p.cl[b] : -1;
       s_ctx[b] = ctx;
-      const int n = (ctx + kStep - 1) / kStep;
+      const int n = ctx > 0 ? (ctx + kStep - 1) / kStep : 0;
       loc += (long long)U * (n > 0 ? n + kUnitSetupSteps : 0);
     }
   }
@@ -634,7 +640,7 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
   for (int k = 0; k < per; ++k) {
     const int b = tid * per + k;
     if (b < B) {
-      const int n = (s_ctx[b] + kStep - 1) / kStep;
+      const int n = s_ctx[b] > 0 ? (s_ctx[b] + kStep - 1) / kStep : 0;
       s_R[b] = run;
       run += (long long)U * (n > 0 ? n + kUnitSetupSteps : 0);
     }
@@ -657,12 +663,13 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
   const long long w = (long long)blockIdx.x * kWaves + wave;
   const int lane = threadIdx.x & 63;
   // A request without keys has no steps: wave (b mod grid waves) writes its
-  // (zero) output rows.
+  // (zero) output rows (a request of another route, marked -1, is left alone).
   {
-    const size_t row_elems = (size_t)p.Hq * p.L * D;
     for (int b = (int)w; b < B; b += (int)gridDim.x * kWaves) {
       if (uni(s_ctx[b]) != 0) continue;
-      uint4 *dst = reinterpret_cast<uint4 *>(reinterpret_cast<T *>(p.out) + (size_t)b * row_elems);
+      const size_t first = query_row(p, b, 0, 0) * D;
+      const size_t row_elems = (size_t)p.Hq * (p.qsl ? query_rows(p, b) : p.L) * D;
+      uint4 *dst = reinterpret_cast<uint4 *>(reinterpret_cast<T *>(p.out) + first);
       const size_t n16 = row_elems * sizeof(T) / 16;
       for (size_t i = lane; i < n16; i += 64) dst[i] = make_uint4(0, 0, 0, 0);
     }
@@ -699,7 +706,7 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
       const long long w1 = bs.wave_of(row0 + n - 1);
       const int g = u / row_blocks;
       const int rb = u - g * row_blocks;
-      const int Lb = p.ql ? p.ql[b] : p.L;
+      const int Lb = query_rows(p, b);
       const long long unit = (long long)b * U + u;  // row block over the call
       const ItemOut io{0, unit + v, unit + w0, (int)(w1 - w0 + 1), unit};
       decode_item<T, KV, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, (int)(j0 * kStep),

@@ -39,6 +39,7 @@ pa_status check_sizes(const pa_args *a) {
   if (a->batch > kMaxGridYZ) return PA_ERR_INVALID_ARG;
   if (a->dtype != PA_DTYPE_F32 && a->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
   if (a->head_dim != 64 && a->head_dim != 128) return PA_ERR_UNSUPPORTED;
+  if (a->query_start_loc && a->query_lens) return PA_ERR_INVALID_ARG;  // one or the other
   if (a->kv_dtype != PA_KV_SAME && a->kv_dtype != PA_KV_FP8_E4M3) return PA_ERR_INVALID_ARG;
   if (a->kv_dtype == PA_KV_FP8_E4M3) {
     if (!(a->k_scale > 0.f) || !isfinite(a->k_scale) || !(a->v_scale > 0.f) ||
@@ -171,6 +172,8 @@ pa::LaunchParams make_params(const pa_args *a, int32_t S, int32_t P, bool balanc
   p.kv_fp8 = kv_fp8(a) ? 1 : 0;
   p.k_scale = kv_fp8(a) ? a->k_scale : 1.f;
   p.v_scale = kv_fp8(a) ? a->v_scale : 1.f;
+  p.qsl = a->query_start_loc;
+  p.route = 0;
   if (balanced) p.grid_waves = pa::decode_balanced_waves(p, (pa::DType)a->dtype);
   return p;
 }
@@ -361,9 +364,37 @@ namespace {
 
 // pa_attention's route: decode when the query rows of one kv head fit one
 // decode row block (each K/V byte is then read once per kv head), else
-// prefill (K/V read once per 128-row tile).
-bool routes_to_decode(const pa_args *a) {
-  return (int64_t)(a->num_q_heads / a->num_kv_heads) * a->q_len <= 8;
+// prefill (K/V read once per 128-row tile); a packed ragged call with more
+// than one row bound routes each request (when some request can take the
+// decode path at all).
+int attention_route(const pa_args *a) {
+  const int64_t G = a->num_q_heads / a->num_kv_heads;
+  if (G * a->q_len <= 8) return PA_ROUTE_DECODE;
+  if (a->query_start_loc && G <= 8) return PA_ROUTE_RAGGED;
+  return PA_ROUTE_PREFILL;
+}
+
+// The decode part of a ragged call: the same call with one query row per
+// request (its requests have at most one).
+pa_args ragged_decode_args(const pa_args *a) {
+  pa_args d = *a;
+  d.q_len = 1;
+  return d;
+}
+
+size_t round16(size_t x) { return (x + 15) / 16 * 16; }
+
+// Plans of both parts of a ragged call.
+pa_status ragged_plans(const pa_args *a, int32_t num_cus, pa_workspace *dec, pa_workspace *pre,
+                       size_t *dec_bytes, size_t *pre_bytes) {
+  if (kv_fp8(a)) return PA_ERR_UNSUPPORTED;  // fp8 pages: decode path only
+  const pa_args d = ragged_decode_args(a);
+  memset(dec, 0, sizeof *dec);
+  memset(pre, 0, sizeof *pre);
+  pa_status st = pa_decode_plan(&d, num_cus, dec, dec_bytes);
+  if (st != PA_OK) return st;
+  if (dec->schedule != PA_SCHEDULE_BALANCED) return PA_ERR_UNSUPPORTED;  // batch above 2048
+  return pa_prefill_plan(a, num_cus, pre, pre_bytes);
 }
 
 }  // namespace
@@ -373,20 +404,87 @@ PA_EXPORT pa_status pa_attention_plan(const pa_args *args, int32_t num_cus, pa_w
   pa_status st = check_sizes(args);
   if (st != PA_OK) return st;
   if (!plan) return PA_ERR_INVALID_ARG;
-  const bool dec = routes_to_decode(args);
-  if (route) *route = dec ? PA_ROUTE_DECODE : PA_ROUTE_PREFILL;
-  return dec ? pa_decode_plan(args, num_cus, plan, workspace_bytes)
-             : pa_prefill_plan(args, num_cus, plan, workspace_bytes);
+  const int r = attention_route(args);
+  if (route) *route = r;
+  plan->prefill_splits = 0;
+  if (r == PA_ROUTE_DECODE) return pa_decode_plan(args, num_cus, plan, workspace_bytes);
+  if (r == PA_ROUTE_PREFILL) return pa_prefill_plan(args, num_cus, plan, workspace_bytes);
+  pa_workspace dec, pre;
+  size_t db = 0, pb = 0;
+  if ((st = ragged_plans(args, num_cus, &dec, &pre, &db, &pb)) != PA_OK) return st;
+  const pa_args d = ragged_decode_args(args);
+  const size_t rows = (size_t)decode_block_rows(&d);
+  plan->schedule = PA_SCHEDULE_BALANCED;
+  plan->partition_tokens = 0;
+  plan->num_splits = dec.num_splits;
+  plan->num_counters = dec.num_counters + pre.num_counters;
+  plan->prefill_splits = pre.num_splits;
+  if (workspace_bytes)
+    *workspace_bytes = ((size_t)dec.num_splits * rows * args->head_dim +
+                        round16((size_t)dec.num_splits * rows)) * sizeof(float) + pb;
+  return PA_OK;
 }
 
 PA_EXPORT pa_status pa_attention(const pa_args *args, const pa_workspace *ws, void *stream) {
   pa_status st = check_sizes(args);
   if (st != PA_OK) return st;
-  if (!routes_to_decode(args)) return pa_prefill(args, ws, stream);
-  if ((st = pa_decode(args, ws, stream)) != PA_OK) return st;
-  const bool merged = ws && ws->schedule == PA_SCHEDULE_BALANCED && ws->counters;
-  if (ws && ws->num_splits > 1 && !merged) return pa_split_reduce(args, ws, stream);
-  return PA_OK;
+  const int r = attention_route(args);
+  if (r == PA_ROUTE_PREFILL) return pa_prefill(args, ws, stream);
+  if (r == PA_ROUTE_DECODE) {
+    if ((st = pa_decode(args, ws, stream)) != PA_OK) return st;
+    const bool merged = ws && ws->schedule == PA_SCHEDULE_BALANCED && ws->counters;
+    if (ws && ws->num_splits > 1 && !merged) return pa_split_reduce(args, ws, stream);
+    return PA_OK;
+  }
+  // ragged: the decode part (requests of one row, merge fused) and the
+  // prefill part (the others), one launch each, on `stream`
+  if (args->batch == 0) return PA_OK;
+  if ((st = check_pointers(args)) != PA_OK) return st;
+  pa_workspace dec, pre;
+  size_t db = 0, pb = 0;
+  if ((st = ragged_plans(args, 0, &dec, &pre, &db, &pb)) != PA_OK) return st;
+  const pa_args d = ragged_decode_args(args);
+  const size_t rows = (size_t)decode_block_rows(&d);
+  const int64_t dec_counters = (int64_t)args->batch * decode_units(&d);
+  if (!ws || ws->schedule != PA_SCHEDULE_BALANCED || !ws->partial_out || !ws->partial_lse ||
+      !ws->counters || !aligned16(ws->partial_out) || !aligned16(ws->partial_lse) ||
+      (reinterpret_cast<uintptr_t>(ws->counters) & 3u) ||
+      (int64_t)ws->num_splits < dec_counters + 1 || ws->prefill_splits < 0 ||
+      (int64_t)ws->num_counters < dec_counters + ws->prefill_splits)
+    return PA_ERR_WORKSPACE;
+  pa_workspace wd;
+  memset(&wd, 0, sizeof wd);
+  wd.partial_out = ws->partial_out;
+  wd.partial_lse = ws->partial_lse;
+  wd.num_splits = ws->num_splits;
+  wd.schedule = PA_SCHEDULE_BALANCED;
+  wd.num_counters = (int32_t)dec_counters;
+  wd.counters = ws->counters;
+  int32_t S, P;
+  bool balanced;
+  if ((st = check_workspace(&d, &wd, &S, &P, &balanced)) != PA_OK) return st;
+  pa::LaunchParams pd = make_params(&d, S, P, balanced, &wd);
+  pd.route = 1;
+  hipError_t e = pa::launch_decode(pd, (pa::DType)args->dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return PA_ERR_HIP;
+  // the prefill part, with the key split in the workspace's second region
+  const int32_t cap = args->max_pages * args->page_size;
+  pa::LaunchParams pp = make_params(args, 1, cap, false, nullptr);
+  pp.route = 2;
+  if (ws->prefill_splits >= 2 && prefill_splits(args)) {
+    pp.ws_o = ws->partial_out + (size_t)ws->num_splits * rows * args->head_dim;
+    pp.ws_lse = ws->partial_lse + round16((size_t)ws->num_splits * rows);
+    pp.counters = ws->counters + dec_counters;
+    pp.num_splits = ws->prefill_splits;
+  }
+  if (args->dtype == PA_DTYPE_BF16) {
+    const int64_t tiles = prefill_tiles(args);
+    if (tiles * args->num_kv_heads * args->batch + ws_slots(pp) > INT32_MAX)
+      return PA_ERR_INVALID_ARG;
+    return hip_status(pa::launch_prefill_mfma(pp, (hipStream_t)stream));
+  }
+  if ((st = check_decode_grid(args, 1)) != PA_OK) return st;
+  return hip_status(pa::launch_decode(pp, (pa::DType)args->dtype, (hipStream_t)stream));
 }
 
 PA_EXPORT pa_status pa_append(const pa_append_args *args, void *stream) {

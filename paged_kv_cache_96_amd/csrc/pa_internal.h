@@ -34,7 +34,31 @@ struct LaunchParams {
   float scale_log2;         // scale * log2(e): scores are kept in base-2 units
   int32_t kv_fp8;           // 1: the pages hold fp8 E4M3 codes (query and out bf16)
   float k_scale, v_scale;   // fp8 pages: element value = code value * scale (else 1)
+  const int32_t *qsl;       // packed rows: query_start_loc [B + 1], or nullptr ([B, Hq, L])
+  int32_t route;            // 0: every request; ragged call: 1 its decode requests, 2 the rest
 };
+
+// Query rows of request b.
+__device__ __forceinline__ int query_rows(const LaunchParams &p, int b) {
+  return p.qsl ? p.qsl[b + 1] - p.qsl[b] : (p.ql ? p.ql[b] : p.L);
+}
+
+// Row index of query / output row (request b, head h, position i): packed
+// rows [T, Hq] (T = qsl[B]) or padded [B, Hq, L].
+__device__ __forceinline__ size_t query_row(const LaunchParams &p, int b, int h, int i) {
+  return p.qsl ? (size_t)(p.qsl[b] + i) * p.Hq + h : ((size_t)b * p.Hq + h) * p.L + i;
+}
+
+// Whether a request of Lb query rows takes the decode route of a ragged
+// call: one query row (or none) and a GQA group that one decode row block
+// holds.  Every other request takes the prefill route.
+__host__ __device__ inline bool ragged_decode_request(int G, int Lb) { return G <= 8 && Lb <= 1; }
+
+// Whether request b belongs to this launch.
+__device__ __forceinline__ bool routed_here(const LaunchParams &p, int Lb) {
+  if (p.route == 0) return true;
+  return (p.route == 1) == ragged_decode_request(p.Hq / p.Hkv, Lb);
+}
 
 // Vector-ALU paged decode kernel (also the fp32 prefill path, with S == 1).
 hipError_t launch_decode(const LaunchParams &p, DType dt, hipStream_t stream);

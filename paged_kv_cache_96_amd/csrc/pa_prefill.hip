@@ -186,7 +186,9 @@ __device__ void find_piece(const LaunchParams &p, int nt, int *s_ctx, int *s_ql,
   const int G = p.Hq / p.Hkv;
   for (int b = tid; b < p.B; b += 256) {
     s_ctx[b] = p.cl[b];
-    s_ql[b] = p.ql ? p.ql[b] : p.L;
+    // a request of another route has no rows here (no keys, one empty piece)
+    const int lb = query_rows(p, b);
+    s_ql[b] = routed_here(p, lb) ? lb : 0;
   }
   if (tid == 0) s_pc->found = 0;
   __syncthreads();
@@ -422,9 +424,12 @@ prefill_kernel(LaunchParams p, int num_tiles) {
 
   const int G = p.Hq / p.Hkv;
   const int ctx = p.cl[b];
-  const int Lb = p.ql ? p.ql[b] : p.L;
+  const int Lb = query_rows(p, b);
+  if (!routed_here(p, Lb)) return;  // block-uniform: a request of the other route
   const int rows_valid = G * Lb;
-  const int rows_all = G * p.L;
+  // rows written: padded rows up to G * L (past query_lens as zeros); packed
+  // rows of the request only
+  const int rows_all = p.qsl ? rows_valid : G * p.L;
   const int rho0 = tile * kBM;
 
   // ---- this lane's query rows (one per row block)
@@ -459,7 +464,7 @@ prefill_kernel(LaunchParams p, int num_tiles) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const uint16_t *qp = reinterpret_cast<const uint16_t *>(p.q) +
-                         ((size_t)(b * p.Hq + qh[rb]) * p.L + qi[rb]) * D + half * 8;
+                         query_row(p, b, qh[rb], qi[rb]) * D + half * 8;
 #pragma unroll
     for (int kk = 0; kk < TL::kKSteps; ++kk)
       q[rb][kk] = row_valid[rb] ? *reinterpret_cast<const uint4 *>(qp + kk * 16)
@@ -944,8 +949,7 @@ prefill_kernel(LaunchParams p, int num_tiles) {
     const float l_tot = pair_sum(l_run[rb]);  // uniform: every lane of the wave takes part
     if (rho[rb] < rows_all) {
       const float inv = (row_valid[rb] && l_tot > 0.f) ? 1.f / l_tot : 0.f;
-      uint16_t *op = reinterpret_cast<uint16_t *>(p.out) +
-                     ((size_t)(b * p.Hq + qh[rb]) * p.L + qi[rb]) * D;
+      uint16_t *op = reinterpret_cast<uint16_t *>(p.out) + query_row(p, b, qh[rb], qi[rb]) * D;
 #pragma unroll
       for (int mb = 0; mb < TL::kMBlocks; ++mb)
 #pragma unroll

@@ -30,7 +30,9 @@ __device__ void balanced_waves(const LaunchParams &p, int b, int u, int units, l
   const int lane = threadIdx.x & 63;
   long long tot = 0, before = 0;
   for (int c = lane; c < p.B; c += 64) {
-    const long long n = (p.cl[c] + kStep - 1) / kStep;
+    // requests of another route have no steps (as in the decode kernel)
+    const int ctx = routed_here(p, query_rows(p, c)) ? p.cl[c] : 0;
+    const long long n = (ctx + kStep - 1) / kStep;
     const long long steps = (long long)units * (n > 0 ? n + kUnitSetupSteps : 0);
     tot += steps;
     if (c < b) before += steps;
@@ -56,7 +58,11 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(LaunchParams p, int t
   const int i = row % p.L;
   const int b = row / (p.L * p.Hq);
   const int ctx = p.cl[b];
-  const int Lb = p.ql ? p.ql[b] : p.L;
+  const int Lb = query_rows(p, b);
+  if (!routed_here(p, Lb)) return;
+  if (p.qsl && i >= Lb) return;  // packed rows: no padding rows exist
+  // this row's index in the output (and in the partition states)
+  const size_t orow = query_row(p, b, (row / p.L) % p.Hq, i);
   const int S = p.num_splits;
   int n;
   // state s of this row: lse[s * stride], po[s * stride * D]
@@ -82,12 +88,12 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(LaunchParams p, int t
     stride = rows;
   } else {
     n = (i < Lb && ctx > 0) ? min(S, (ctx + p.part_tokens - 1) / p.part_tokens) : 0;
-    lse = p.ws_lse + (size_t)row * S;
-    po = p.ws_o + (size_t)row * S * D;
+    lse = p.ws_lse + orow * S;
+    po = p.ws_o + orow * S * D;
     stride = 1;
   }
 
-  merge_row<T, D>(lse, po, (int)stride, n, reinterpret_cast<T *>(p.out) + (size_t)row * D);
+  merge_row<T, D>(lse, po, (int)stride, n, reinterpret_cast<T *>(p.out) + orow * D);
 }
 
 template <typename T, int D, int KVB = (int)sizeof(T)>

@@ -41,7 +41,7 @@ def test_header_and_library_exports_agree(L):
     assert exported == declared
     for name in declared:
         assert hasattr(L, name)
-    assert L.pa_abi_version() == 8
+    assert L.pa_abi_version() == 9
 
 
 def test_status_strings(L):
@@ -406,3 +406,43 @@ def test_fp8_pages_are_decode_only(L):
 def test_fp8_append_validation(L, kw, code):
     h = HostBuffers()
     assert L.pa_append(ctypes.byref(_append_args(h, **kw)), None) == code
+
+
+def test_ragged_route_and_plan(L):
+    """Packed rows with a row bound above one: pa_attention routes per
+    request (PA_ROUTE_RAGGED) when some request can take the decode path
+    (G <= 8); the plan holds both parts and its byte count covers both
+    regions of partial_out and partial_lse."""
+    h = HostBuffers()
+    a = h.args(q_len=64, query_start_loc=h.p)
+    ws = PaWorkspace()
+    n = ctypes.c_size_t(0)
+    route = ctypes.c_int32(-1)
+    assert L.pa_attention_plan(ctypes.byref(a), 0, ctypes.byref(ws), ctypes.byref(n),
+                               ctypes.byref(route)) == 0
+    assert route.value == _lib.ROUTE_RAGGED
+    G = a.num_q_heads // a.num_kv_heads          # 4: rows per block 4
+    units = a.batch * a.num_kv_heads
+    assert ws.num_splits == units + 4 * 256 and ws.prefill_splits == 5 * 256
+    assert ws.num_counters == units + ws.prefill_splits
+    R, D, S, Sp = 4, a.head_dim, ws.num_splits, ws.prefill_splits
+    assert n.value == (S * R * D + -(-S * R // 16) * 16) * 4 + Sp * (D // 2 + 2) * 256 * 4
+    # G > 8: no request can take the decode path
+    b = h.args(q_len=64, query_start_loc=h.p, num_q_heads=32, num_kv_heads=2)
+    assert L.pa_attention_plan(ctypes.byref(b), 0, ctypes.byref(ws), ctypes.byref(n),
+                               ctypes.byref(route)) == 0
+    assert route.value == _lib.ROUTE_PREFILL
+    # one row bound: the decode route
+    c = h.args(q_len=1, query_start_loc=h.p)
+    assert L.pa_attention_plan(ctypes.byref(c), 0, ctypes.byref(ws), ctypes.byref(n),
+                               ctypes.byref(route)) == 0
+    assert route.value == _lib.ROUTE_DECODE
+    # packed rows and query_lens together are refused; fp8 pages have no prefill part
+    d = h.args(q_len=64, query_start_loc=h.p, query_lens=h.p)
+    assert L.pa_attention_plan(ctypes.byref(d), 0, ctypes.byref(ws), ctypes.byref(n),
+                               ctypes.byref(route)) == -1
+    e = h.args(q_len=64, query_start_loc=h.p, kv_dtype=1, k_scale=1.0, v_scale=1.0)
+    assert L.pa_attention_plan(ctypes.byref(e), 0, ctypes.byref(ws), ctypes.byref(n),
+                               ctypes.byref(route)) == -2
+    # a ragged call without its workspace is refused before any launch
+    assert L.pa_attention(ctypes.byref(a), None, None) == _lib.PA_ERR_WORKSPACE

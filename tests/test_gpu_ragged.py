@@ -1,0 +1,179 @@
+"""GPU parity of ragged batches in ONE call (packed query rows with
+query_start_loc) against the oracle, through the C ABI: pa_attention routes
+each request -- one query row: the decode kernel; more: the prefill kernel --
+on one stream, and pa_decode / pa_prefill also take packed rows.  The oracle
+sees the same requests in the padded layout.  Marked gpu."""
+import numpy as np
+import pytest
+
+import oracle
+from tests._gpu import DeviceInputs, assert_parity, dev, expected_visits, host_f64
+from workloads import make_c5, make_random, pack_ragged
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def api():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from paged_kv_cache_96_amd import api as a
+    a._lib.lib()
+    return a
+
+
+def _pack(x):
+    """Packed rows [T, H_q, D] and query_start_loc of padded inputs x (rows
+    past query_lens dropped)."""
+    lens = [int(v) for v in x.rows_valid()]
+    rows = [x.query[b, :, :n].transpose(1, 0, 2) for b, n in enumerate(lens)]
+    qsl = np.zeros(x.B + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum(lens)
+    T = int(qsl[-1])
+    q = (np.concatenate(rows, axis=0) if T else
+         np.zeros((0, x.H_q, x.D), dtype=x.query.dtype))
+    return np.ascontiguousarray(q), qsl
+
+
+def _unpack(packed, qsl, x):
+    out = np.zeros((x.B, x.H_q, x.L, x.D))
+    for b in range(x.B):
+        out[b, :, :qsl[b + 1] - qsl[b]] = packed[qsl[b]:qsl[b + 1]].transpose(1, 0, 2)
+    return out
+
+
+def _run(api, x, q, qsl, entry="attention", trace=False, num_cus=0):
+    """One call over packed rows; returns (packed output on the host, extras)."""
+    import torch
+    qd = dev(q)
+    kp, vp, bt, cl, ql = dev(x.key_pages), dev(x.value_pages), dev(x.block_table), \
+        dev(x.context_lens), dev(qsl)
+    out = torch.full_like(qd, float("nan"))
+    dbg_t = dbg_v = None
+    if trace:
+        cap = x.max_pages * x.page_size
+        dbg_t = torch.full((x.B, cap, 2), -1, dtype=torch.int32, device="cuda")
+        dbg_v = torch.zeros((x.B, x.H_kv, cap), dtype=torch.int32, device="cuda")
+    args = api.make_args(qd, kp, vp, bt, cl, out, scale=x.scale,
+                         mask="causal" if x.causal else "none", query_start_loc=ql,
+                         max_query_len=x.L, debug_trace=dbg_t, debug_visits=dbg_v)
+    ex = {}
+    if entry == "attention":
+        ap = api.pa_attention_plan(args, num_cus=num_cus)
+        ws = api.attention_workspace(ap, args, qd)
+        api.pa_attention(args, ws)
+        ex["route"] = ap.route
+        torch.cuda.synchronize()
+        ex["counters"] = ws.counters.cpu().numpy() if getattr(ws, "counters", None) is not None else None
+    elif entry == "decode":
+        plan = api.pa_decode_plan(args, num_cus=num_cus)
+        ws = api.Workspace(x.B, x.H_q, x.L, x.D, plan.num_splits, plan.partition_tokens, "cuda",
+                           schedule=plan.schedule,
+                           block_rows=plan.workspace_bytes // max(1, plan.num_splits * (x.D + 1) * 4),
+                           num_counters=plan.num_counters)
+        api.pa_decode(args, ws)
+        if plan.num_splits > 1 and ws.counters is None:
+            api.pa_split_reduce(args, ws)
+    else:
+        ws = api.PrefillWorkspace.for_args(args, "cuda", num_cus=num_cus)
+        api.pa_prefill(args, ws)
+    torch.cuda.synchronize()
+    if trace:
+        ex["trace"], ex["visits"] = dbg_t.cpu().numpy(), dbg_v.cpu().numpy()
+    return out, ex
+
+
+def test_c5_as_one_call(api):
+    """The mixed workload (48 one-row decode requests, 8 prefill requests of
+    64-256 rows, shared prefix pages) in one pa_attention call."""
+    m = make_c5()
+    r = pack_ragged(m)
+    print(f"[ragged C5] B={r.B} T={r.query.shape[0]} max rows {r.max_query_len}", flush=True)
+    import torch
+    qd = dev(r.query)
+    kp, vp = dev(r.key_pages), dev(r.value_pages)
+    bt, cl, ql = dev(r.block_table), dev(r.context_lens), dev(r.query_start_loc)
+    out = torch.full_like(qd, float("nan"))
+    args = api.make_args(qd, kp, vp, bt, cl, out, scale=r.scale, mask="causal",
+                         query_start_loc=ql, max_query_len=r.max_query_len)
+    ap = api.pa_attention_plan(args)
+    assert ap.route == api._lib.ROUTE_RAGGED
+    ws = api.attention_workspace(ap, args, qd)
+    for rep in range(2):
+        out.fill_(float("nan"))
+        api.pa_attention(args, ws)
+        torch.cuda.synchronize()
+        d_out, p_out = r.unpack(host_f64(out))
+        err_d = assert_parity(torch.from_numpy(d_out), oracle.attention_of(m.decode), "bf16",
+                              f"ragged C5 decode part rep {rep}")
+        err_p = assert_parity(torch.from_numpy(p_out), oracle.attention_of(m.prefill), "bf16",
+                              f"ragged C5 prefill part rep {rep}")
+        assert not ws.counters.any().item()
+        if rep == 0:
+            first = host_f64(out)
+        else:
+            assert np.array_equal(host_f64(out), first)
+    print(f"[ragged C5] max abs err decode {err_d:.3e} prefill {err_p:.3e}", flush=True)
+
+
+CASES = [
+    # seed, dtype, D, H_q, H_kv, L, ps, ctx, query_lens, causal
+    (1, "bf16", 128, 32, 8, 40, 16, [40, 900, 1, 0, 77, 300], [40, 1, 1, 0, 2, 33], True),
+    (2, "bf16", 128, 8, 8, 130, 16, [130, 5, 2000, 9], [130, 1, 129, 0], True),
+    (3, "bf16", 64, 12, 3, 20, 5, [20, 100, 1, 31], [20, 1, 1, 17], True),
+    (4, "f32", 128, 8, 2, 12, 16, [12, 50, 7, 40], [12, 1, 0, 9], True),
+    (5, "bf16", 128, 32, 2, 9, 32, [9, 300, 40], [9, 1, 5], False),   # G 16: all prefill
+    (6, "bf16", 128, 16, 4, 300, 128, [300, 5000, 129, 2049], [300, 1, 129, 1], True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"case{c[0]}" for c in CASES])
+def test_ragged_parity_trace_and_entry_points(api, case):
+    seed, dt, D, Hq, Hkv, L, ps, ctx, ql, causal = case
+    print(f"[ragged] seed={seed} {dt} D={D} Hq={Hq} Hkv={Hkv} L={L} ps={ps} ctx={ctx} ql={ql}",
+          flush=True)
+    x = make_random(seed, B=len(ctx), H_q=Hq, H_kv=Hkv, L=L, D=D, page_size=ps, ctx=ctx,
+                    dtype=dt, causal=causal, query_lens=ql, extra_free_pages=5)
+    q, qsl = _pack(x)
+    ref = oracle.attention_of(x)
+    out, ex = _run(api, x, q, qsl, "attention")
+    got = _unpack(host_f64(out), qsl, x)
+    assert_parity(torch_of(got), ref, dt, f"ragged case{seed}")
+    if ex["counters"] is not None:
+        assert not ex["counters"].any()
+    # the instrumented kernels of the same call trace every key of every request
+    t_out, tex = _run(api, x, q, qsl, "attention", trace=True)
+    tr = oracle.translate_of(x)
+    v = expected_visits(x)
+    for b in range(x.B):
+        if ql[b] == 0:
+            tr[b] = -1
+            v[b] = 0
+    assert np.array_equal(tex["trace"], tr)
+    assert np.array_equal(tex["visits"], v)
+    # the prefill entry point over all requests of the packed batch
+    if dt == "bf16" or L <= 64:
+        p_out, _ = _run(api, x, q, qsl, "prefill")
+        assert_parity(torch_of(_unpack(host_f64(p_out), qsl, x)), ref, dt, f"packed prefill {seed}")
+    # the decode entry point when every request fits it
+    if L <= 8:
+        d_out, _ = _run(api, x, q, qsl, "decode")
+        assert_parity(torch_of(_unpack(host_f64(d_out), qsl, x)), ref, dt, f"packed decode {seed}")
+
+
+def torch_of(a):
+    import torch
+    return torch.from_numpy(a)
+
+
+def test_packed_decode_all_requests_one_row(api):
+    """q_len 1 with packed rows: the router's decode route, partitions and
+    the balanced schedule."""
+    x = make_random(9, B=5, H_q=32, H_kv=8, L=1, D=128, page_size=16,
+                    ctx=[1, 300, 4096, 0, 77], dtype="bf16", causal=False, query_lens=[1, 1, 1, 0, 1])
+    q, qsl = _pack(x)
+    ref = oracle.attention_of(x)
+    out, ex = _run(api, x, q, qsl, "attention")
+    assert ex["route"] == api._lib.ROUTE_DECODE
+    assert_parity(torch_of(_unpack(host_f64(out), qsl, x)), ref, "bf16", "packed L=1")

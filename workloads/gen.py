@@ -455,6 +455,78 @@ def make_c5(seed: int = SEEDS["C5"]) -> MixedInputs:
     return MixedInputs(name="C5", seed=seed, decode=dec, prefill=pre, meta=meta)
 
 
+@dataclass
+class RaggedInputs:
+    """A ragged batch as ONE call over packed query rows: request b owns rows
+    query_start_loc[b] .. query_start_loc[b + 1] - 1 of query [T, H_q, D]
+    (token-major).  ``parts`` holds the same requests as padded inputs (the
+    decode requests first, then the prefill ones, in the order of the packed
+    batch), which is how the oracle sees them."""
+
+    name: str
+    seed: int
+    B: int
+    H_q: int
+    H_kv: int
+    D: int
+    page_size: int
+    num_pages: int
+    max_pages: int
+    scale: float
+    causal: bool
+    max_query_len: int
+    query: np.ndarray               # [T, H_q, D] uint16 (bf16 bits)
+    query_start_loc: np.ndarray     # [B + 1] int32
+    key_pages: np.ndarray
+    value_pages: np.ndarray
+    block_table: np.ndarray         # [B, max_pages]
+    context_lens: np.ndarray        # [B]
+    parts: MixedInputs
+
+    def unpack(self, packed: np.ndarray):
+        """Split packed output rows [T, H_q, D] into the padded layouts of the
+        decode part [B_dec, H_q, 1, D] and the prefill part [B_pre, H_q, L, D]
+        (rows past a request's own left at zero)."""
+        dec, pre = self.parts.decode, self.parts.prefill
+        out_d = np.zeros((dec.B, self.H_q, dec.L, self.D), dtype=packed.dtype)
+        out_p = np.zeros((pre.B, self.H_q, pre.L, self.D), dtype=packed.dtype)
+        qsl = self.query_start_loc
+        for b in range(self.B):
+            rows = packed[qsl[b]:qsl[b + 1]].transpose(1, 0, 2)   # [H_q, Lb, D]
+            if b < dec.B:
+                out_d[b, :, :rows.shape[1]] = rows
+            else:
+                out_p[b - dec.B, :, :rows.shape[1]] = rows
+        return out_d, out_p
+
+
+def pack_ragged(m: MixedInputs) -> RaggedInputs:
+    """The requests of a mixed workload (decode part, then prefill part) as
+    one batch of packed query rows over the same pool."""
+    dec, pre = m.decode, m.prefill
+    rows, lens = [], []
+    for b in range(dec.B):
+        n = int(dec.rows_valid()[b])
+        rows.append(dec.query[b, :, :n].transpose(1, 0, 2))
+        lens.append(n)
+    for b in range(pre.B):
+        n = int(pre.rows_valid()[b])
+        rows.append(pre.query[b, :, :n].transpose(1, 0, 2))
+        lens.append(n)
+    qsl = np.zeros(len(lens) + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum(lens)
+    assert dec.max_pages == pre.max_pages
+    return RaggedInputs(
+        name=m.name + "-ragged", seed=m.seed, B=dec.B + pre.B, H_q=dec.H_q, H_kv=dec.H_kv,
+        D=dec.D, page_size=dec.page_size, num_pages=dec.num_pages, max_pages=dec.max_pages,
+        scale=dec.scale, causal=dec.causal, max_query_len=max(lens),
+        query=np.ascontiguousarray(np.concatenate(rows, axis=0)), query_start_loc=qsl,
+        key_pages=dec.key_pages, value_pages=dec.value_pages,
+        block_table=np.ascontiguousarray(np.concatenate([dec.block_table, pre.block_table])),
+        context_lens=np.ascontiguousarray(np.concatenate([dec.context_lens, pre.context_lens])),
+        parts=m)
+
+
 BUILDERS = {"C1": make_c1, "C2": make_c2, "C3": make_c3, "C4": make_c4, "C5": make_c5}
 
 
