@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 9
+#define PA_ABI_VERSION 10
 
 typedef enum {
   PA_OK = 0,
@@ -294,6 +294,65 @@ pa_status pa_attention_plan(const pa_args *args, int32_t num_cus, pa_workspace *
  * without arrival counters), pa_split_reduce; the prefill route runs
  * pa_prefill.  Errors as for those calls. */
 pa_status pa_attention(const pa_args *args, const pa_workspace *ws, void *stream);
+
+/* ------------------------------------------------------- shared prefixes
+ * Block sharing across requests ("Reading vLLM's PagedAttention Kernel",
+ * section 1 "Intuition" and section 2 "Mental model": two block tables may
+ * name the same physical block, which is what prefix caching builds on).
+ * When the requests of a group share their first pages, pa_decode_shared
+ * reads those pages once for the whole group instead of once per request:
+ * a prefix launch (the bf16 matrix-core kernel, one request per group whose
+ * query rows are all the members' rows, no mask) leaves each member row's
+ * state over the prefix -- normalised output and log-sum-exp -- and the
+ * decode kernel walks each request's keys past the prefix and merges that
+ * state into the row's other partial states with the log-sum-exp rule
+ * (section 3.3).  The result is the same attention as pa_decode's, up to
+ * rounding order.
+ *
+ * Groups are consecutive ranges of requests that cover the batch: group k
+ * holds requests group_start[k] .. group_start[k + 1] - 1 (group_start[0] =
+ * 0, nondecreasing, group_start[num_groups] = batch); a request that shares
+ * nothing is a group of its own with prefix 0.  Group k shares its first
+ * P_k = prefix_lens[k] - prefix_lens[k] % page_size keys (whole pages only;
+ * a partial page is walked by each request).  Device-side contract, taken on
+ * trust like the block-table contract: every member's block table names the
+ * same physical pages as the group's first member for logical pages below
+ * P_k / page_size, and every member b with query rows has P_k <=
+ * context_lens[b] - (its query rows) (every row then sees the whole prefix);
+ * group k has at most max_group_size requests. */
+typedef struct pa_prefix_groups {
+  const int32_t *group_start; /* [num_groups + 1] int32, device */
+  const int32_t *prefix_lens; /* [num_groups] int32, device: shared keys of each group */
+  int32_t num_groups;         /* >= 1 (batch >= 1) */
+  int32_t max_group_size;     /* >= 1: bound on the requests of a group */
+} pa_prefix_groups;
+
+/* Plan of pa_decode_shared (sizes only; nothing runs on the GPU): the decode
+ * part's balanced plan with the merge fused (plan->num_splits piece slots,
+ * plan->num_counters = batch * U + prefill_splits counters) and the prefix
+ * launch's key split (plan->prefill_splits slots, 0: unsplit).  Workspace
+ * layout, each part in its own region:
+ *   partial_out  decode: num_splits * R * head_dim floats, then the prefix
+ *                states: batch * H_q * q_len * head_dim floats, then the key
+ *                split: prefill_splits * head_dim * 128 floats;
+ *   partial_lse  decode: num_splits * R floats rounded up to a multiple of
+ *                16, then batch * H_q * q_len rounded up to a multiple of 16,
+ *                then prefill_splits * 512 floats;
+ *   counters     decode: batch * U, then prefill_splits;
+ * R, U as for the balanced schedule.  *workspace_bytes is all of partial_out
+ * and partial_lse.  PA_ERR_UNSUPPORTED: dtype other than bf16, fp8 pages,
+ * debug outputs, or a batch the balanced schedule does not take. */
+pa_status pa_decode_shared_plan(const pa_args *args, const pa_prefix_groups *groups,
+                                int32_t num_cus, pa_workspace *plan, size_t *workspace_bytes);
+
+/* Decode (q_len <= 8, as pa_decode) with the shared prefixes of `groups`
+ * read once per group: the prefix launch, then the decode launch, both on
+ * `stream`, with the workspace of pa_decode_shared_plan (counters zeroed
+ * once by the caller, left zero by every call).  Errors as for pa_decode;
+ * PA_ERR_INVALID_ARG also for a NULL or misaligned group array or
+ * num_groups / max_group_size out of range. */
+pa_status pa_decode_shared(const pa_args *args, const pa_prefix_groups *groups,
+                           const pa_workspace *ws, void *stream);
 
 /* ---------------------------------------------------------------- write path
  * The K/V write that precedes attention on every step: each new token's key

@@ -27,7 +27,8 @@ PA_KV_FP8_E4M3 = 1
 
 EXPORTED = ("pa_decode_plan", "pa_decode", "pa_split_reduce", "pa_prefill_plan", "pa_prefill",
             "pa_attention_plan", "pa_attention", "pa_append", "pa_decode_noalloc",
-            "pa_status_string", "pa_abi_version")
+            "pa_decode_shared_plan", "pa_decode_shared", "pa_status_string",
+            "pa_abi_version")
 
 
 class PaArgs(ctypes.Structure):
@@ -91,7 +92,16 @@ class PaAppendArgs(ctypes.Structure):
     ]
 
 
-ABI_VERSION = 9  # PA_ABI_VERSION of the structs below
+class PaPrefixGroups(ctypes.Structure):
+    _fields_ = [
+        ("group_start", ctypes.c_void_p),
+        ("prefix_lens", ctypes.c_void_p),
+        ("num_groups", ctypes.c_int32),
+        ("max_group_size", ctypes.c_int32),
+    ]
+
+
+ABI_VERSION = 10  # PA_ABI_VERSION of the structs below
 
 ROUTE_DECODE = 0
 ROUTE_PREFILL = 1
@@ -140,6 +150,11 @@ def lib() -> ctypes.CDLL:
     L.pa_append.restype = ctypes.c_int
     L.pa_decode_noalloc.argtypes = [A, ctypes.c_void_p]
     L.pa_decode_noalloc.restype = ctypes.c_int
+    G = ctypes.POINTER(PaPrefixGroups)
+    L.pa_decode_shared_plan.argtypes = [A, G, ctypes.c_int32, W, ctypes.POINTER(ctypes.c_size_t)]
+    L.pa_decode_shared_plan.restype = ctypes.c_int
+    L.pa_decode_shared.argtypes = [A, G, W, ctypes.c_void_p]
+    L.pa_decode_shared.restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int32]
     L.pa_status_string.restype = ctypes.c_char_p
     L.pa_abi_version.argtypes = []

@@ -323,6 +323,82 @@ class RaggedWorkspace:
         return [self.partial_out, self.partial_lse, self.counters]
 
 
+def make_groups(group_start: torch.Tensor, prefix_lens: torch.Tensor,
+                max_group_size: Optional[int] = None) -> "_lib.PaPrefixGroups":
+    """Fill a pa_prefix_groups from device tensors: group_start [G + 1] and
+    prefix_lens [G] int32 (consecutive request ranges covering the batch).
+    max_group_size defaults to the largest group, read from group_start (a
+    device-to-host copy)."""
+    _int32(group_start, "group_start")
+    _int32(prefix_lens, "prefix_lens")
+    _same_gpu(group_start, prefix_lens=prefix_lens)
+    ng = prefix_lens.shape[0]
+    _shape(group_start, (ng + 1,), "group_start")
+    if max_group_size is None:
+        max_group_size = int((group_start[1:] - group_start[:-1]).max().item()) if ng else 1
+    g = _lib.PaPrefixGroups()
+    g.group_start = _ptr(group_start)
+    g.prefix_lens = _ptr(prefix_lens)
+    g.num_groups = int(ng)
+    g.max_group_size = int(max_group_size)
+    return g
+
+
+class SharedPlan(NamedTuple):
+    """pa_decode_shared_plan's choice: the decode part's piece slots, all
+    arrival counters, the prefix launch's key-split slots and the bytes of
+    partial_out plus partial_lse (layout in include/pa.h)."""
+    num_splits: int
+    num_counters: int
+    prefill_splits: int
+    workspace_bytes: int
+
+
+def pa_decode_shared_plan(args: PaArgs, groups, *, num_cus: int = 0) -> SharedPlan:
+    ws = PaWorkspace()
+    nbytes = ctypes.c_size_t(0)
+    _lib.check("pa_decode_shared_plan", _lib.lib().pa_decode_shared_plan(
+        ctypes.byref(args), ctypes.byref(groups), int(num_cus), ctypes.byref(ws),
+        ctypes.byref(nbytes)))
+    return SharedPlan(ws.num_splits, ws.num_counters, ws.prefill_splits, nbytes.value)
+
+
+class SharedWorkspace:
+    """Device buffers of a shared-prefix plan in the layout of include/pa.h
+    (torch owns the memory; counters zeroed once on torch's current
+    stream)."""
+
+    def __init__(self, plan: SharedPlan, args: PaArgs, device):
+        S, Sp, D = int(plan.num_splits), int(plan.prefill_splits), int(args.head_dim)
+        R = _rows_per_block(min(8, (args.num_q_heads // args.num_kv_heads) * args.q_len))
+        rows = args.batch * args.num_q_heads * args.q_len
+        r16 = lambda x: -(-x // 16) * 16  # noqa: E731
+        self.partial_out = torch.empty(S * R * D + rows * D + Sp * D * 128, dtype=torch.float32,
+                                       device=device)
+        self.partial_lse = torch.empty(r16(S * R) + r16(rows) + Sp * 512, dtype=torch.float32,
+                                       device=device)
+        if (self.partial_out.numel() + self.partial_lse.numel()) * 4 != plan.workspace_bytes:
+            raise ValueError("workspace size disagrees with the library's plan")
+        self.counters = torch.zeros(int(plan.num_counters), dtype=torch.int32, device=device)
+        self.c = PaWorkspace()
+        self.c.partial_out = _ptr(self.partial_out)
+        self.c.partial_lse = _ptr(self.partial_lse)
+        self.c.counters = _ptr(self.counters)
+        self.c.num_splits = S
+        self.c.schedule = SCHEDULE_BALANCED
+        self.c.num_counters = int(plan.num_counters)
+        self.c.prefill_splits = Sp
+
+    def tensors(self):
+        return [self.partial_out, self.partial_lse, self.counters]
+
+
+def pa_decode_shared(args: PaArgs, groups, workspace: SharedWorkspace, stream=None) -> None:
+    """Decode with each group's shared prefix pages read once per group."""
+    _lib.check("pa_decode_shared", _lib.lib().pa_decode_shared(
+        ctypes.byref(args), ctypes.byref(groups), ctypes.byref(workspace.c), _stream(stream)))
+
+
 def pa_attention_plan(args: PaArgs, *, num_cus: int = 0,
                       partition_tokens: int = 0) -> AttentionPlan:
     ws = PaWorkspace()

@@ -148,10 +148,12 @@ struct ItemOut {
 // With `split` it writes the state of that piece to the workspace (see
 // ItemOut), otherwise the piece is the whole row range and it writes the
 // output.
+// With `pre` (a request of a shared-prefix group; split then holds) the
+// fused merge starts every row from the row's prefix state.
 template <typename T, typename KV, int D, int ROWS, bool DEBUG, bool UNIFORM>
 __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g, int rb, int t0,
                                             int tend, const ItemOut &io, bool split, int ctx,
-                                            int Lb) {
+                                            int Lb, bool pre = false) {
   constexpr bool kFp8 = sizeof(KV) == 1;  // fp8 E4M3 pages (T: bf16)
   constexpr int kElems = Elem<KV>::kPerVec;  // page elements per 16-byte lane load
   constexpr int kLpt = D / kElems;      // lanes per key
@@ -558,7 +560,8 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
       asm volatile("" ::: "memory");
       const size_t wi = (size_t)io.first * ROWS;
       merge_block<T, D, ROWS>(p.ws_lse + wi, p.ws_o + wi * D, io.pieces, valid, qrow,
-                              min(ROWS, rows_out - rb * ROWS), out);
+                              min(ROWS, rows_out - rb * ROWS), out, pre ? p.pre_lse : nullptr,
+                              p.pre_o);
       if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -611,20 +614,60 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
   constexpr int kStep = decode_step_keys(D, (int)sizeof(KV));
   __shared__ long long s_R[kBalancedMaxBatch + 1];  // first step of request b
   __shared__ int s_ctx[kBalancedMaxBatch];
+  __shared__ int s_pre[kBalancedMaxBatch];  // shared-prefix keys of request b (0: none)
   __shared__ long long s_sum[256];
   const int B = p.B;
   const int U = p.Hkv * row_blocks;
   const int tid = threadIdx.x;
   // per-thread serial sums over a contiguous slice, then a block scan
   const int per = (B + 255) / 256;
+  const bool shared = p.grp_start != nullptr;
+  if (shared) {
+    // Shared prefixes: each non-empty group marks its first request, and an
+    // inclusive max scan of the marks over the requests names the group of
+    // every request (the groups are consecutive ranges covering the batch).
+    for (int b = tid; b < B; b += 256) s_pre[b] = -1;
+    __syncthreads();
+    for (int k = tid; k < p.num_groups; k += 256) {
+      const int first = p.grp_start[k];
+      if (first >= 0 && first < p.grp_start[k + 1] && first < B) s_pre[first] = k;  // distinct
+    }
+    __syncthreads();
+    long long mark = -1;
+    for (int k = 0; k < per; ++k) {
+      const int b = tid * per + k;
+      if (b < B) mark = max(mark, (long long)s_pre[b]);
+    }
+    s_sum[tid] = mark;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele max scan
+      const long long a = tid >= off ? s_sum[tid - off] : -1;
+      __syncthreads();
+      s_sum[tid] = max(s_sum[tid], a);
+      __syncthreads();
+    }
+    long long grp = tid > 0 ? s_sum[tid - 1] : -1;
+    for (int k = 0; k < per; ++k) {  // this thread's slice only: no other thread reads it
+      const int b = tid * per + k;
+      if (b < B) {
+        grp = max(grp, (long long)s_pre[b]);
+        s_pre[b] = grp >= 0 ? group_prefix_keys(p, (int)grp) : 0;
+      }
+    }
+    __syncthreads();  // s_sum is reused below
+  } else {
+    for (int b = tid; b < B; b += 256) s_pre[b] = 0;  // read after the scan's barriers
+  }
   long long loc = 0;
   for (int k = 0; k < per; ++k) {
     const int b = tid * per + k;
     if (b < B) {
-      // a request of another route counts as one without keys
+      // a request of another route counts as one without keys; a request of
+      // a shared-prefix group walks only its keys past the prefix
       const int ctx = routed_here(p, query_rows(p, b)) ? p.cl[b] : -1;
       s_ctx[b] = ctx;
-      const int n = ctx > 0 ? (ctx + kStep - 1) / kStep : 0;
+      const int keys = ctx - (shared ? s_pre[b] : 0);
+      const int n = keys > 0 ? (keys + kStep - 1) / kStep : 0;
       loc += (long long)U * (n > 0 ? n + kUnitSetupSteps : 0);
     }
   }
@@ -640,7 +683,8 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
   for (int k = 0; k < per; ++k) {
     const int b = tid * per + k;
     if (b < B) {
-      const int n = s_ctx[b] > 0 ? (s_ctx[b] + kStep - 1) / kStep : 0;
+      const int keys = s_ctx[b] - s_pre[b];
+      const int n = keys > 0 ? (keys + kStep - 1) / kStep : 0;
       s_R[b] = run;
       run += (long long)U * (n > 0 ? n + kUnitSetupSteps : 0);
     }
@@ -663,10 +707,12 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
   const long long w = (long long)blockIdx.x * kWaves + wave;
   const int lane = threadIdx.x & 63;
   // A request without keys has no steps: wave (b mod grid waves) writes its
-  // (zero) output rows (a request of another route, marked -1, is left alone).
+  // (zero) output rows (a request of another route, marked -1, is left alone;
+  // so is one with keys past a shared prefix).
   {
     for (int b = (int)w; b < B; b += (int)gridDim.x * kWaves) {
-      if (uni(s_ctx[b]) != 0) continue;
+      const int ctx = uni(s_ctx[b]);
+      if (ctx < 0 || ctx - uni(s_pre[b]) > 0) continue;
       const size_t first = query_row(p, b, 0, 0) * D;
       const size_t row_elems = (size_t)p.Hq * (p.qsl ? query_rows(p, b) : p.L) * D;
       uint4 *dst = reinterpret_cast<uint4 *>(reinterpret_cast<T *>(p.out) + first);
@@ -690,7 +736,8 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
       }
       const int b = uni(lo);
       const int ctx = uni(s_ctx[b]);
-      const long long n = (ctx + kStep - 1) / kStep;  // > 0: request b holds position t
+      const int pre = uni(s_pre[b]);  // keys below pre: the group's prefix state
+      const long long n = (ctx - pre + kStep - 1) / kStep;  // > 0: request b holds position t
       const long long nu = n + kUnitSetupSteps;       // positions per row block
       const long long Rb = uni64(s_R[b]);
       const long long rel = t - Rb;
@@ -709,8 +756,10 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
       const int Lb = query_rows(p, b);
       const long long unit = (long long)b * U + u;  // row block over the call
       const ItemOut io{0, unit + v, unit + w0, (int)(w1 - w0 + 1), unit};
-      decode_item<T, KV, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, (int)(j0 * kStep),
-                                                  (int)(j1 * kStep), io, w1 > w0, ctx, Lb);
+      // a row block with a prefix state always goes through the merge
+      decode_item<T, KV, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, pre + (int)(j0 * kStep),
+                                                  pre + (int)(j1 * kStep), io,
+                                                  w1 > w0 || pre > 0, ctx, Lb, pre > 0);
       t += j1 - j0;
     }
   };

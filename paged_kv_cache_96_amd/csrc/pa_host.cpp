@@ -487,6 +487,140 @@ PA_EXPORT pa_status pa_attention(const pa_args *args, const pa_workspace *ws, vo
   return hip_status(pa::launch_decode(pp, (pa::DType)args->dtype, (hipStream_t)stream));
 }
 
+// ------------------------------------------------------------ shared prefixes
+namespace {
+
+// The prefix launch of a shared-prefix decode as prefill arguments: one
+// request per group of max_group_size * q_len rows over the group's prefix
+// keys, no mask (the kernels take the rows, keys and table from the groups).
+pa_args prefix_launch_args(const pa_args *a, const pa_prefix_groups *g) {
+  pa_args v = *a;
+  v.batch = g->num_groups;
+  v.q_len = g->max_group_size * a->q_len;
+  v.query_lens = nullptr;
+  v.query_start_loc = nullptr;
+  v.mask = PA_MASK_NONE;
+  return v;
+}
+
+// Host-side checks of the groups (their contents are device data).
+pa_status check_groups(const pa_args *a, const pa_prefix_groups *g) {
+  if (!g) return PA_ERR_INVALID_ARG;
+  if (a->dtype != PA_DTYPE_BF16 || kv_fp8(a)) return PA_ERR_UNSUPPORTED;
+  if (a->debug_trace || a->debug_visits) return PA_ERR_UNSUPPORTED;
+  if (a->batch == 0) return PA_OK;
+  if (g->num_groups < 1 || g->num_groups > a->batch || g->max_group_size < 1 ||
+      g->max_group_size > a->batch)
+    return PA_ERR_INVALID_ARG;
+  if (!g->group_start || !g->prefix_lens ||
+      (reinterpret_cast<uintptr_t>(g->group_start) & 3u) ||
+      (reinterpret_cast<uintptr_t>(g->prefix_lens) & 3u))
+    return PA_ERR_INVALID_ARG;
+  return PA_OK;
+}
+
+// Rows of the prefix states: every row of the call (an upper bound for
+// packed rows).
+size_t state_rows(const pa_args *a) {
+  return (size_t)a->batch * a->num_q_heads * a->q_len;
+}
+
+}  // namespace
+
+PA_EXPORT pa_status pa_decode_shared_plan(const pa_args *args, const pa_prefix_groups *groups,
+                                          int32_t num_cus, pa_workspace *plan,
+                                          size_t *workspace_bytes) {
+  pa_status st = check_sizes(args);
+  if (st != PA_OK) return st;
+  if (!plan) return PA_ERR_INVALID_ARG;
+  if (args->q_len > 8) return PA_ERR_INVALID_ARG;
+  if ((st = check_groups(args, groups)) != PA_OK) return st;
+  pa_workspace dec, pre;
+  memset(&dec, 0, sizeof dec);
+  memset(&pre, 0, sizeof pre);
+  size_t db = 0, pb = 0;
+  if ((st = pa_decode_plan(args, num_cus, &dec, &db)) != PA_OK) return st;
+  if (dec.schedule != PA_SCHEDULE_BALANCED) return PA_ERR_UNSUPPORTED;  // batch above 2048
+  if (args->batch > 0) {
+    const pa_args v = prefix_launch_args(args, groups);
+    if ((st = pa_prefill_plan(&v, num_cus, &pre, &pb)) != PA_OK) return st;
+  }
+  const size_t R = (size_t)decode_block_rows(args);
+  const size_t rows = state_rows(args);
+  plan->schedule = PA_SCHEDULE_BALANCED;
+  plan->partition_tokens = 0;
+  plan->num_splits = dec.num_splits;
+  plan->num_counters = dec.num_counters + pre.num_counters;
+  plan->prefill_splits = pre.num_splits;
+  if (workspace_bytes)
+    *workspace_bytes = ((size_t)dec.num_splits * R * args->head_dim +
+                        round16((size_t)dec.num_splits * R) + rows * args->head_dim +
+                        round16(rows)) * sizeof(float) + pb;
+  return PA_OK;
+}
+
+PA_EXPORT pa_status pa_decode_shared(const pa_args *args, const pa_prefix_groups *groups,
+                                     const pa_workspace *ws, void *stream) {
+  pa_status st = check_sizes(args);
+  if (st != PA_OK) return st;
+  if (args->q_len > 8) return PA_ERR_INVALID_ARG;
+  if ((st = check_groups(args, groups)) != PA_OK) return st;
+  if (args->batch == 0) return PA_OK;
+  if ((st = check_pointers(args)) != PA_OK) return st;
+  const size_t R = (size_t)decode_block_rows(args);
+  const int64_t dec_counters = (int64_t)args->batch * decode_units(args);
+  if (!ws || ws->schedule != PA_SCHEDULE_BALANCED || !ws->partial_out || !ws->partial_lse ||
+      !ws->counters || !aligned16(ws->partial_out) || !aligned16(ws->partial_lse) ||
+      (reinterpret_cast<uintptr_t>(ws->counters) & 3u) ||
+      (int64_t)ws->num_splits < dec_counters + 1 || ws->prefill_splits < 0 ||
+      (int64_t)ws->num_counters < dec_counters + ws->prefill_splits)
+    return PA_ERR_WORKSPACE;
+  pa_workspace wd;
+  memset(&wd, 0, sizeof wd);
+  wd.partial_out = ws->partial_out;
+  wd.partial_lse = ws->partial_lse;
+  wd.num_splits = ws->num_splits;
+  wd.schedule = PA_SCHEDULE_BALANCED;
+  wd.num_counters = (int32_t)dec_counters;
+  wd.counters = ws->counters;
+  int32_t S, P;
+  bool balanced;
+  if ((st = check_workspace(args, &wd, &S, &P, &balanced)) != PA_OK) return st;
+  float *state_o = ws->partial_out + (size_t)S * R * args->head_dim;
+  float *state_lse = ws->partial_lse + round16((size_t)S * R);
+  const size_t rows = state_rows(args);
+  // the prefix launch: each group's member rows over its shared pages
+  const pa_args v = prefix_launch_args(args, groups);
+  const int32_t cap = args->max_pages * args->page_size;
+  pa::LaunchParams pp = make_params(&v, 1, cap, false, nullptr);
+  pp.grp_start = groups->group_start;
+  pp.grp_pre = groups->prefix_lens;
+  pp.num_groups = groups->num_groups;
+  pp.prefix_pass = 1;
+  pp.Lm = args->q_len;
+  pp.qsl = args->query_start_loc;  // member rows are addressed as in the call
+  pp.ql = args->query_lens;
+  pp.pre_o = state_o;
+  pp.pre_lse = state_lse;
+  if (ws->prefill_splits >= 2 && prefill_splits(&v)) {
+    pp.ws_o = state_o + rows * args->head_dim;
+    pp.ws_lse = state_lse + round16(rows);
+    pp.counters = ws->counters + dec_counters;
+    pp.num_splits = ws->prefill_splits;
+  }
+  const int64_t tiles = prefill_tiles(&v);
+  if (tiles * v.num_kv_heads * v.batch + ws_slots(pp) > INT32_MAX) return PA_ERR_INVALID_ARG;
+  if (pa::launch_prefill_mfma(pp, (hipStream_t)stream) != hipSuccess) return PA_ERR_HIP;
+  // the decode launch: keys past each request's prefix, merged with its state
+  pa::LaunchParams pd = make_params(args, S, P, balanced, &wd);
+  pd.grp_start = groups->group_start;
+  pd.grp_pre = groups->prefix_lens;
+  pd.num_groups = groups->num_groups;
+  pd.pre_o = state_o;
+  pd.pre_lse = state_lse;
+  return hip_status(pa::launch_decode(pd, (pa::DType)args->dtype, (hipStream_t)stream));
+}
+
 PA_EXPORT pa_status pa_append(const pa_append_args *args, void *stream) {
   if (!args) return PA_ERR_INVALID_ARG;
   const pa_append_args *a = args;

@@ -36,6 +36,20 @@ struct LaunchParams {
   float k_scale, v_scale;   // fp8 pages: element value = code value * scale (else 1)
   const int32_t *qsl;       // packed rows: query_start_loc [B + 1], or nullptr ([B, Hq, L])
   int32_t route;            // 0: every request; ragged call: 1 its decode requests, 2 the rest
+  // Shared prefixes (pa_decode_shared): request groups grp_start[k] ..
+  // grp_start[k + 1] - 1 read the same first grp_pre[k] keys (rounded down to
+  // whole pages).  Decode launch (prefix_pass 0): each request walks its keys
+  // past the prefix and merges the prefix state of its rows.  Prefix launch
+  // (prefix_pass 1, prefill kernel): virtual request k holds the query rows
+  // of the members of group k (Lm rows each, member-major) over the prefix
+  // keys of the group's first member, and writes each row's state.
+  const int32_t *grp_start; // [num_groups + 1], or nullptr (no shared prefixes)
+  const int32_t *grp_pre;   // [num_groups]
+  int32_t num_groups;
+  int32_t prefix_pass;
+  int32_t Lm;               // prefix launch: query rows per member (the call's q_len)
+  float *pre_o;             // prefix states by output row: normalised output fp32 [rows, D]
+  float *pre_lse;           // and natural-log log-sum-exp [rows] (-inf: no key)
 };
 
 // Query rows of request b.
@@ -47,6 +61,14 @@ __device__ __forceinline__ int query_rows(const LaunchParams &p, int b) {
 // rows [T, Hq] (T = qsl[B]) or padded [B, Hq, L].
 __device__ __forceinline__ size_t query_row(const LaunchParams &p, int b, int h, int i) {
   return p.qsl ? (size_t)(p.qsl[b] + i) * p.Hq + h : ((size_t)b * p.Hq + h) * p.L + i;
+}
+
+// Shared keys of group k: its prefix length rounded down to whole pages
+// (only whole pages are shared), within [0, max_pages * page_size] (so a
+// length beyond the contract never reads past a block-table row).
+__device__ __forceinline__ int group_prefix_keys(const LaunchParams &p, int k) {
+  const int n = min(p.grp_pre[k], p.max_pages * p.ps);
+  return n > 0 ? n - n % p.ps : 0;
 }
 
 // Whether a request of Lb query rows takes the decode route of a ragged

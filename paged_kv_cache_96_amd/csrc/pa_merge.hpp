@@ -102,10 +102,15 @@ namespace pa {
 // of up to 16 pieces are in flight together: the states are read past the
 // caches, and a row block split into many pieces (a small batch over long
 // contexts) would otherwise pay one memory round trip per piece.
+// With pre_lse (shared-prefix decode) every valid row starts from its prefix
+// state, pre_lse[row] and pre_o[row * D ...] at its output row index, which
+// an earlier launch on the stream wrote (ordinary loads see it).
 template <typename T, int D, int R>
 __device__ __forceinline__ void merge_block(const float *lse, const float *po, int n,
                                             const bool (&valid)[R], const size_t (&qrow)[R],
-                                            int rows_in_range, T *out) {
+                                            int rows_in_range, T *out,
+                                            const float *pre_lse = nullptr,
+                                            const float *pre_o = nullptr) {
   constexpr int kLanes = 64 / R;       // lanes per row
   constexpr int kE = D / kLanes;       // elements per lane
   static_assert(kLanes * R == 64 && kE * kLanes == D && kE % 4 == 0 || kE < 4, "layout");
@@ -113,17 +118,31 @@ __device__ __forceinline__ void merge_block(const float *lse, const float *po, i
   const int r = lane / kLanes;
   const int e0 = (lane % kLanes) * kE;
   bool ok = false;
+  size_t row = 0;
 #pragma unroll
   for (int i = 0; i < R; ++i)
-    if (i == r) ok = valid[i] && i < rows_in_range;
+    if (i == r) {
+      ok = valid[i] && i < rows_in_range;
+      row = qrow[i];
+    }
   const int cnt = ok ? n : 0;
   const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float *>(lse), (short)0, 0x7fffffff, kBufferRsrcWord3);
   const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float *>(po), (short)0, 0x7fffffff, kBufferRsrcWord3);
+  // state (m, l, acc): output acc / l, log-sum-exp m + ln l
   float m = kNegInf, l = 0.f, acc[kE];
 #pragma unroll
   for (int e = 0; e < kE; ++e) acc[e] = 0.f;
+  if (pre_lse != nullptr && ok) {
+    const float ls = pre_lse[row];
+    if (ls != kNegInf) {  // the prefix state: its normalised output with l = 1
+      m = ls;
+      l = 1.f;
+#pragma unroll
+      for (int e = 0; e < kE; ++e) acc[e] = pre_o[row * D + e0 + e];
+    }
+  }
 #pragma unroll 16
   for (int s = 0; s < cnt; ++s) {
     const float ls = __uint_as_float(
@@ -156,10 +175,6 @@ __device__ __forceinline__ void merge_block(const float *lse, const float *po, i
   }
   if (r >= rows_in_range) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  size_t row = 0;
-#pragma unroll
-  for (int i = 0; i < R; ++i)
-    if (i == r) row = qrow[i];
   T *dst = out + row * D + e0;
 #pragma unroll
   for (int e = 0; e < kE; ++e) {

@@ -145,6 +145,34 @@ __device__ __forceinline__ float wave_incl_scan_f(float x) {
   return x;
 }
 
+// Requests of a launch.  The prefix launch of a shared-prefix decode
+// (p.prefix_pass) runs one request per group: request b holds the query rows
+// of the group's members, p.Lm per member (member-major), over the group's
+// shared prefix keys, without a mask (every member row sees its whole
+// prefix).
+__device__ __forceinline__ int launch_ctx(const LaunchParams &p, int b) {
+  return p.prefix_pass ? group_prefix_keys(p, b) : p.cl[b];
+}
+__device__ __forceinline__ int launch_rows(const LaunchParams &p, int b) {
+  return p.prefix_pass ? (p.grp_start[b + 1] - p.grp_start[b]) * p.Lm : query_rows(p, b);
+}
+// Query/output row index of row i < launch_rows(p, b) of head h; `exists`
+// is false for a member's rows past its own query rows (prefix launch).
+__device__ __forceinline__ size_t launch_row(const LaunchParams &p, int b, int h, int i,
+                                             bool &exists) {
+  exists = true;
+  if (!p.prefix_pass) return query_row(p, b, h, i);
+  const int j = i / p.Lm;
+  const int pos = i - j * p.Lm;
+  const int m = p.grp_start[b] + j;  // the member request
+  if (p.qsl) {
+    exists = pos < p.qsl[m + 1] - p.qsl[m];
+    return (size_t)(p.qsl[m] + pos) * p.Hq + h;
+  }
+  exists = pos < (p.ql ? p.ql[m] : p.Lm);
+  return ((size_t)m * p.Hq + h) * p.Lm + pos;
+}
+
 // The piece of the key split that workgroup blockIdx.x walks.
 struct Piece {
   int tile, g, b;
@@ -185,9 +213,9 @@ __device__ void find_piece(const LaunchParams &p, int nt, int *s_ctx, int *s_ql,
   const int lane = tid & 63, wave = tid >> 6;
   const int G = p.Hq / p.Hkv;
   for (int b = tid; b < p.B; b += 256) {
-    s_ctx[b] = p.cl[b];
+    s_ctx[b] = launch_ctx(p, b);
     // a request of another route has no rows here (no keys, one empty piece)
-    const int lb = query_rows(p, b);
+    const int lb = launch_rows(p, b);
     s_ql[b] = routed_here(p, lb) ? lb : 0;
   }
   if (tid == 0) s_pc->found = 0;
@@ -423,13 +451,13 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   const int ln = lane & 31;         // query row of this lane within the wave
 
   const int G = p.Hq / p.Hkv;
-  const int ctx = p.cl[b];
-  const int Lb = query_rows(p, b);
+  const int ctx = launch_ctx(p, b);
+  const int Lb = launch_rows(p, b);
   if (!routed_here(p, Lb)) return;  // block-uniform: a request of the other route
   const int rows_valid = G * Lb;
   // rows written: padded rows up to G * L (past query_lens as zeros); packed
-  // rows of the request only
-  const int rows_all = p.qsl ? rows_valid : G * p.L;
+  // rows of the request only; states of existing member rows (prefix launch)
+  const int rows_all = (p.qsl || p.prefix_pass) ? rows_valid : G * p.L;
   const int rho0 = tile * kBM;
 
   // ---- this lane's query rows (one per row block)
@@ -441,6 +469,11 @@ prefill_kernel(LaunchParams p, int num_tiles) {
     qi[rb] = rho[rb] / G;
     qh[rb] = g * G + (rho[rb] - qi[rb] * G);
     row_valid[rb] = rho[rb] < rows_valid;
+    if (p.prefix_pass && row_valid[rb]) {
+      bool exists;
+      launch_row(p, b, qh[rb], qi[rb], exists);
+      row_valid[rb] = exists;
+    }
     lim[rb] = row_valid[rb] ? (p.causal ? ctx - Lb + qi[rb] + 1 : ctx) : 0;
   }
 
@@ -463,8 +496,9 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   uint4 q[RB][TL::kKSteps];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    const uint16_t *qp = reinterpret_cast<const uint16_t *>(p.q) +
-                         query_row(p, b, qh[rb], qi[rb]) * D + half * 8;
+    bool exists;
+    const size_t qr = row_valid[rb] ? launch_row(p, b, qh[rb], qi[rb], exists) : 0;
+    const uint16_t *qp = reinterpret_cast<const uint16_t *>(p.q) + qr * D + half * 8;
 #pragma unroll
     for (int kk = 0; kk < TL::kKSteps; ++kk)
       q[rb][kk] = row_valid[rb] ? *reinterpret_cast<const uint4 *>(qp + kk * 16)
@@ -474,7 +508,8 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   // ---- staging of one K/V tile: thread -> (key kr*KPR + tid / CH, chunk tid % CH)
   const uint16_t *kp = reinterpret_cast<const uint16_t *>(p.kp);
   const uint16_t *vp = reinterpret_cast<const uint16_t *>(p.vp);
-  const int32_t *bt = p.bt + (size_t)b * p.max_pages;
+  // the prefix launch reads the table of the group's first member
+  const int32_t *bt = p.bt + (size_t)(p.prefix_pass ? p.grp_start[b] : b) * p.max_pages;
   const int chunk = tid % TL::kChunks;
   const int key_in_round = tid / TL::kChunks;
   struct Stage {
@@ -919,6 +954,7 @@ prefill_kernel(LaunchParams p, int num_tiles) {
       // order: the result does not depend on which piece arrived last
       float M = kMinM;
       for (int s2 = 0; s2 < np; ++s2) M = fmaxf(M, ld(slot_m(s2), tid * 4));
+      m_ref[0] = M;  // the merged state's reference
       l_run[0] = 0.f;
 #pragma unroll
       for (int mb = 0; mb < TL::kMBlocks; ++mb)
@@ -941,6 +977,33 @@ prefill_kernel(LaunchParams p, int num_tiles) {
       }
       if (tid == 0) __hip_atomic_store(p.counters + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  }
+
+  // ---- prefix launch: the state of each member row, by its output row
+  // index: normalised output (fp32) and natural-log log-sum-exp
+  if (p.prefix_pass) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float l_tot = pair_sum(l_run[rb]);  // uniform: every lane of the wave takes part
+      if (!row_valid[rb]) continue;
+      bool exists;
+      const size_t orow = launch_row(p, b, qh[rb], qi[rb], exists);
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      float *po = p.pre_o + orow * D;
+#pragma unroll
+      for (int mb = 0; mb < TL::kMBlocks; ++mb)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d = mb * 32 + i4 * 8 + half * 4;
+          const f32x16_t &om = o[rb][mb];
+          *reinterpret_cast<float4 *>(po + d) =
+              make_float4(om[i4 * 4 + 0] * inv, om[i4 * 4 + 1] * inv, om[i4 * 4 + 2] * inv,
+                          om[i4 * 4 + 3] * inv);
+        }
+      if (half == 0)
+        p.pre_lse[orow] = l_tot > 0.f ? (m_ref[rb] + __log2f(l_tot)) * kLn2 : kNegInf;
+    }
+    return;
   }
 
   // ---- finalize: O = O^T / l, rounded to bf16; padding rows get zeros

@@ -41,7 +41,7 @@ def test_header_and_library_exports_agree(L):
     assert exported == declared
     for name in declared:
         assert hasattr(L, name)
-    assert L.pa_abi_version() == 9
+    assert L.pa_abi_version() == 10
 
 
 def test_status_strings(L):
@@ -446,3 +446,85 @@ def test_ragged_route_and_plan(L):
                                ctypes.byref(route)) == -2
     # a ragged call without its workspace is refused before any launch
     assert L.pa_attention(ctypes.byref(a), None, None) == _lib.PA_ERR_WORKSPACE
+
+
+def _groups(h, **kw):
+    g = _lib.PaPrefixGroups()
+    g.group_start = g.prefix_lens = h.p
+    g.num_groups, g.max_group_size = 1, 2
+    for k, v in kw.items():
+        setattr(g, k, v)
+    return g
+
+
+def _shared_plan(L, a, g, num_cus=0):
+    ws = PaWorkspace()
+    n = ctypes.c_size_t(0)
+    rc = L.pa_decode_shared_plan(ctypes.byref(a), ctypes.byref(g), num_cus, ctypes.byref(ws),
+                                 ctypes.byref(n))
+    return rc, ws, n.value
+
+
+def test_shared_prefix_plan_layout(L):
+    """The shared-prefix plan: the decode part's balanced plan, the prefix
+    launch's key split (one request per group of max_group_size * q_len
+    rows), and a byte count covering the three regions of partial_out and
+    partial_lse."""
+    h = HostBuffers()
+    a = h.args(batch=6)
+    rc, ws, n = _shared_plan(L, a, _groups(h, num_groups=3, max_group_size=4))
+    assert rc == 0 and ws.schedule == SCHEDULE_BALANCED
+    units = a.batch * a.num_kv_heads             # G = 4: one row block of 4 per kv head
+    assert ws.num_splits == units + 4 * 256 and ws.prefill_splits == 5 * 256
+    assert ws.num_counters == units + ws.prefill_splits
+    R, D, S, Sp = 4, a.head_dim, ws.num_splits, ws.prefill_splits
+    rows = a.batch * a.num_q_heads * a.q_len
+    r16 = lambda x: -(-x // 16) * 16  # noqa: E731
+    assert n == (S * R * D + r16(S * R) + rows * D + r16(rows)) * 4 + Sp * (D // 2 + 2) * 256 * 4
+    # more (group, tile) pairs than the key split plans over: the prefix
+    # launch runs unsplit and needs no split region
+    big = h.args(batch=2048, num_q_heads=64, num_kv_heads=1, q_len=8)
+    rc, ws, n = _shared_plan(L, big, _groups(h, num_groups=2048, max_group_size=1))
+    assert rc == 0 and ws.prefill_splits == 0
+
+
+@pytest.mark.parametrize("kw,gkw,code", [
+    ({}, {"num_groups": 0}, -1),
+    ({}, {"num_groups": 3}, -1),                  # more groups than requests
+    ({}, {"max_group_size": 0}, -1),
+    ({}, {"max_group_size": 3}, -1),              # larger than the batch
+    ({}, {"group_start": None}, -1),
+    ({}, {"prefix_lens": None}, -1),
+    ({"q_len": 9}, {}, -1),                       # decode rows only
+    ({"dtype": 0}, {}, -2),                       # the prefix launch is bf16 only
+    ({"kv_dtype": 1, "k_scale": 1.0, "v_scale": 1.0}, {}, -2),
+])
+def test_shared_prefix_validation(L, kw, gkw, code):
+    h = HostBuffers()
+    a = h.args(**kw)
+    g = _groups(h, **gkw)
+    assert _shared_plan(L, a, g)[0] == code
+    ws = PaWorkspace()
+    assert L.pa_decode_shared(ctypes.byref(a), ctypes.byref(g), ctypes.byref(ws), None) == code
+
+
+def test_shared_prefix_checks_before_launch(L):
+    h = HostBuffers()
+    a = h.args()
+    g = _groups(h)
+    ws = PaWorkspace()
+    # misaligned group arrays, debug outputs, no groups, no workspace
+    assert L.pa_decode_shared(ctypes.byref(a), ctypes.byref(_groups(h, group_start=h.p + 2)),
+                              ctypes.byref(ws), None) == -1
+    dbg = h.args(debug_trace=h.p)
+    assert L.pa_decode_shared(ctypes.byref(dbg), ctypes.byref(g), ctypes.byref(ws), None) == -2
+    assert L.pa_decode_shared(ctypes.byref(a), None, ctypes.byref(ws), None) == -1
+    assert L.pa_decode_shared(ctypes.byref(a), ctypes.byref(g), None, None) == -3
+    rc, plan, _ = _shared_plan(L, a, g)
+    assert rc == 0
+    plan.partial_out = plan.partial_lse = plan.counters = h.p
+    plan.num_counters -= 1                        # one counter short
+    assert L.pa_decode_shared(ctypes.byref(a), ctypes.byref(g), ctypes.byref(plan), None) == -3
+    # an empty batch is a no-op
+    z = h.args(batch=0)
+    assert L.pa_decode_shared(ctypes.byref(z), ctypes.byref(g), ctypes.byref(ws), None) == 0

@@ -68,3 +68,41 @@ def test_c5_shared_prefix_aliasing():
     assert len(ids) == len(set(ids)) and not set(ids) & set(shared)
     assert (m.prefill.query_lens >= 64).all() and (m.prefill.query_lens <= 256).all()
     assert 0.85 <= m.meta["used_pages"] / m.decode.num_pages <= 0.9
+
+
+def test_shared_groups_structure():
+    """make_shared: groups of consecutive requests cover the batch; members'
+    tables name the same physical pages below the group's prefix and distinct
+    ones after it; every member row sees the whole prefix."""
+    from workloads import make_shared
+    sizes, pages = [3, 1, 2, 4], [4, 0, 2, 3]
+    x, g = make_shared(21, H_q=8, H_kv=2, L=2, D=64, page_size=16, group_sizes=sizes,
+                       prefix_pages=pages, suffix=(2, 50), query_lens=[2, 1, 0, 2, 2, 1, 2, 2, 1, 2])
+    assert list(g.group_start) == [0, 3, 4, 6, 10] and g.max_group_size == 4
+    assert list(g.prefix_lens) == [p * 16 for p in pages]
+    for k in range(g.num_groups):
+        s, e, P = g.group_start[k], g.group_start[k + 1], pages[k]
+        for b in range(s, e):
+            assert np.array_equal(x.block_table[b, :P], x.block_table[s, :P])
+            assert x.context_lens[b] - x.rows_valid()[b] >= g.prefix_lens[k]
+    own = [set(x.block_table[b, pages[next(k for k in range(4) if g.group_start[k + 1] > b)]:
+                             (int(x.context_lens[b]) + 15) // 16].tolist()) for b in range(x.B)]
+    for i in range(x.B):
+        for j in range(i + 1, x.B):
+            assert not (own[i] & own[j])
+
+
+def test_c5_decode_grouped_is_a_permutation():
+    from workloads import c5_decode_grouped, make_c5
+    m = make_c5()
+    x, g, order = c5_decode_grouped(m)
+    dec = m.decode
+    assert sorted(order.tolist()) == list(range(dec.B))
+    assert np.array_equal(x.query, dec.query[order])
+    assert np.array_equal(x.block_table, dec.block_table[order])
+    assert np.array_equal(x.context_lens, dec.context_lens[order])
+    n = int(g.group_start[1])
+    assert n == sum(1 for b in m.meta["sharers"] if b < dec.B)
+    shared = m.meta["shared_page_ids"]
+    assert (x.block_table[:n, :len(shared)] == np.asarray(shared)).all()
+    assert g.group_start[-1] == dec.B and (g.prefix_lens[1:] == 0).all()

@@ -527,6 +527,116 @@ def pack_ragged(m: MixedInputs) -> RaggedInputs:
         parts=m)
 
 
+# ----------------------------------------------------------------------------
+# shared prefixes: groups of consecutive requests whose tables name the same
+# first pages (block sharing, as prefix caching produces it)
+# ----------------------------------------------------------------------------
+
+@dataclass
+class SharedGroups:
+    """Group k holds requests group_start[k] .. group_start[k + 1] - 1 and
+    shares its first prefix_lens[k] keys (whole pages); the groups cover the
+    batch, a request that shares nothing is a group of its own with 0."""
+
+    group_start: np.ndarray   # [G + 1] int32
+    prefix_lens: np.ndarray   # [G] int32
+
+    @property
+    def num_groups(self) -> int:
+        return int(self.prefix_lens.shape[0])
+
+    @property
+    def max_group_size(self) -> int:
+        return int(np.diff(self.group_start).max()) if self.num_groups else 1
+
+
+def make_shared(seed: int, *, H_q: int, H_kv: int, L: int, D: int, page_size: int,
+                group_sizes: Sequence[int], prefix_pages: Sequence[int],
+                suffix: tuple, dtype: str = "bf16", causal: bool = True,
+                query_lens: Optional[Sequence[int]] = None, extra_free_pages: int = 3,
+                garbage=GARBAGE_DEFAULT, name: str = "shared"):
+    """Requests in groups of consecutive requests: group k has
+    ``group_sizes[k]`` members whose first ``prefix_pages[k]`` block-table
+    entries name the same physical pages (complete pages), followed by pages
+    of their own; member context = prefix keys + a suffix of U{suffix[0]..
+    suffix[1]} keys (suffix[0] >= L, so every query row sees the whole
+    prefix).  Returns (PagedInputs, SharedGroups).
+
+    Draw order: suffix lengths -> physical-id permutation -> K -> V -> Q.
+    """
+    rng = np.random.default_rng(seed)
+    assert len(group_sizes) == len(prefix_pages) and suffix[0] >= L
+    B = int(sum(group_sizes))
+    suf = [int(v) for v in rng.integers(suffix[0], suffix[1] + 1, size=B)]
+    ctx, member_of = [], []
+    for k, n in enumerate(group_sizes):
+        for _ in range(n):
+            member_of.append(k)
+    for b in range(B):
+        ctx.append(prefix_pages[member_of[b]] * page_size + suf[b])
+    own = [_pages_needed(ctx[b], page_size) - prefix_pages[member_of[b]] for b in range(B)]
+    live = sum(prefix_pages) + sum(own)
+    num_pages = max(1, live + extra_free_pages)
+    perm = rng.permutation(num_pages)
+    cur = 0
+    shared_ids = []
+    for k in range(len(group_sizes)):
+        shared_ids.append([int(p) for p in perm[cur:cur + prefix_pages[k]]])
+        cur += prefix_pages[k]
+    order = [p for ids in shared_ids for p in ids]
+    slots = [page_size] * len(order)
+    ids = []
+    for b in range(B):
+        mine = [int(p) for p in perm[cur:cur + own[b]]]
+        cur += own[b]
+        ids.append(shared_ids[member_of[b]] + mine)
+        order.extend(mine)
+        vs = _valid_slots_per_page(ctx[b], page_size)
+        slots.extend(vs[len(vs) - len(mine):])
+    max_pages = max(_pages_needed(c, page_size) for c in ctx)
+    if query_lens is not None:
+        query_lens = np.asarray(query_lens, dtype=np.int32)
+    kp = _fill_pool(rng, dtype, num_pages, H_kv, page_size, D, order, slots, garbage)
+    vp = _fill_pool(rng, dtype, num_pages, H_kv, page_size, D, order, slots, garbage)
+    q = _queries(rng, dtype, B, H_q, L, D, query_lens, garbage)
+    bt = _tables_from_ids(ctx, page_size, max_pages, ids)
+    gs = np.zeros(len(group_sizes) + 1, dtype=np.int32)
+    gs[1:] = np.cumsum(group_sizes)
+    x = PagedInputs(
+        name=name, seed=seed, dtype=dtype, B=B, H_q=H_q, H_kv=H_kv, L=L, D=D,
+        page_size=page_size, num_pages=num_pages, max_pages=max_pages,
+        scale=1.0 / math.sqrt(D), causal=causal, query=q, key_pages=kp, value_pages=vp,
+        block_table=bt, context_lens=np.asarray(ctx, dtype=np.int32), query_lens=query_lens,
+        meta={"live_pages": live, "garbage": garbage})
+    return x, SharedGroups(gs, np.asarray([p * page_size for p in prefix_pages], dtype=np.int32))
+
+
+def c5_decode_grouped(m: MixedInputs):
+    """The decode part of a mixed workload with its prefix sharers moved to
+    the front as one group (the shared pages' keys as its prefix) and every
+    other request a group of its own.  Returns (PagedInputs, SharedGroups,
+    order): request i of the result is request order[i] of the decode part."""
+    dec = m.decode
+    sharers = [b for b in m.meta["sharers"] if b < dec.B]
+    rest = [b for b in range(dec.B) if b not in sharers]
+    order = np.asarray(sharers + rest, dtype=np.int64)
+    x = PagedInputs(
+        name=dec.name + "-grouped", seed=dec.seed, dtype=dec.dtype, B=dec.B, H_q=dec.H_q,
+        H_kv=dec.H_kv, L=dec.L, D=dec.D, page_size=dec.page_size, num_pages=dec.num_pages,
+        max_pages=dec.max_pages, scale=dec.scale, causal=dec.causal,
+        query=np.ascontiguousarray(dec.query[order]), key_pages=dec.key_pages,
+        value_pages=dec.value_pages, block_table=np.ascontiguousarray(dec.block_table[order]),
+        context_lens=np.ascontiguousarray(dec.context_lens[order]),
+        query_lens=None if dec.query_lens is None else
+        np.ascontiguousarray(dec.query_lens[order]), meta=dict(dec.meta))
+    n_shared = len(m.meta["shared_page_ids"])
+    sizes = ([len(sharers)] if sharers else []) + [1] * len(rest)
+    gs = np.zeros(len(sizes) + 1, dtype=np.int32)
+    gs[1:] = np.cumsum(sizes)
+    pre = ([n_shared * dec.page_size] if sharers else []) + [0] * len(rest)
+    return x, SharedGroups(gs, np.asarray(pre, dtype=np.int32)), order
+
+
 BUILDERS = {"C1": make_c1, "C2": make_c2, "C3": make_c3, "C4": make_c4, "C5": make_c5}
 
 
