@@ -186,6 +186,43 @@ class Runner:
         torch.cuda.synchronize()
         return {"ms": np.array([e[0].elapsed_time(e[1]) for e in ev]), "route": ap.route}
 
+    def time_shared_ab(self, d, groups, steps, warmup):
+        """Times pa_decode_shared over device inputs `d` with the request
+        groups `groups` (the prefix launch and the decode launch, one event
+        pair around both) and pa_decode over the same inputs, alternating
+        call by call so that both see the same clocks; workspaces and groups
+        set up outside the timed regions, the last-level cache flushed
+        before each call.  Returns (shared ms, unshared ms)."""
+        torch, api = self.torch, self.api
+        from tests._gpu import dev
+        x = d.x
+        out = torch.empty_like(d.q)
+        args = api.make_args(d.q, d.kp, d.vp, d.bt, d.cl, out, scale=x.scale, mask=d.mask,
+                             query_lens=d.ql)
+        gs, pl = dev(groups.group_start), dev(groups.prefix_lens)
+        g = api.PrefixGroups(gs, pl, groups.max_group_size)
+        plan = api.pa_decode_shared_plan(args, g)
+        ws = api.SharedWorkspace(plan, args, d.q.device)
+        dplan = api.pa_decode_plan(args)
+        dws = api.Workspace.for_plan(dplan, d.q, fused=True)
+        calls = (lambda: api.pa_decode_shared(args, g, ws), lambda: api.pa_decode(args, dws))
+        for _ in range(warmup):
+            for fn in calls:
+                self.flush()
+                fn()
+        ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(2)]
+              for _ in range(steps)]
+        torch.cuda.synchronize()
+        for k in range(steps):
+            for i, fn in enumerate(calls):
+                self.flush()
+                ev[k][i][0].record()
+                fn()
+                ev[k][i][1].record()
+        torch.cuda.synchronize()
+        ms = np.array([[e[i][0].elapsed_time(e[i][1]) for i in range(2)] for e in ev])
+        return ms[:, 0], ms[:, 1]
+
     def time_prefill(self, d, steps, warmup, flush=False, split=True):
         """Times pa_prefill; `split` passes the key-split workspace of the
         library's plan (allocated outside the timed region)."""
@@ -392,7 +429,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default="C2,C2fp8,C3,C4,C5,long,small,append",
                     help="sections to run (C2 is the headline; leaving it out leaves `value` "
-                         "null, for profiling runs): C2, C2fp8, C3, C4, C5, long (= long4096, "
+                         "null, for profiling runs): C2, C2fp8, C3, C4, C5, shared (the "
+                         "shared-prefix decode alone), long (= long4096, "
                          "long16384), small, threshold, append (all write shapes), "
                          "append_long, append_fp8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -434,6 +472,8 @@ def main():
     sha_dec = _source_sha("pa_decode.hip", "pa_common.hpp", "pa_merge.hpp", "pa_internal.h")
     sha_pre = _source_sha("pa_prefill.hip", "pa_common.hpp", "pa_merge.hpp", "pa_internal.h")
     sha_app = _source_sha("pa_append.hip", "pa_write.h")
+    sha_shared = _source_sha("pa_decode.hip", "pa_prefill.hip", "pa_common.hpp", "pa_merge.hpp",
+                             "pa_internal.h")
 
     def hbm_roofline(kernel, nbytes, ms, counters, sha):
         gbs = nbytes / (ms * 1e-3) / 1e9
@@ -606,6 +646,43 @@ def main():
             "what": "one pa_attention call over packed rows (query_start_loc): the decode "
                     "kernel for the 48 one-row requests, the prefill kernel for the 8 others",
             **_stats(rr["ms"])}
+    if "C5" in only or "shared" in only:
+        # shared-prefix decode (pa_decode_shared: one prefix launch reads each
+        # group's shared pages once, then the decode launch walks the rest and
+        # merges), against pa_decode on the same requests, interleaved call by
+        # call: the decode part of C5 (11 of 48 requests share 16 pages of
+        # 128 keys, moved to the front as one group) and a prefix-heavy batch
+        # (64 requests sharing a 16384-key prefix, own suffixes U[128,4096])
+        m5 = W.make_c5()
+        xg, g5, _ = W.c5_decode_grouped(m5)
+        xh, gh = W.make_shared(31, H_q=32, H_kv=8, L=1, D=128, page_size=16, group_sizes=[64],
+                               prefix_pages=[1024], suffix=(128, 4096))
+        n = max(10, args.steps // 3)
+        sh = []
+        for name, key, xx, gg in (
+                ("C5 decode part: 48 requests bf16 Hq32 Hkv8 D128 page128, 11 share a "
+                 "2048-key prefix (one group)", "decode_c5_shared", xg, g5),
+                ("prefix-heavy decode: 64 requests bf16 Hq32 Hkv8 D128 page16 sharing a "
+                 "16384-key prefix, own suffixes U[128,4096] seed31", "decode_prefix64_shared",
+                 xh, gh)):
+            dx = run.to_device(xx)
+            unique, logical = decode_kv_bytes(xx, unique=True), decode_kv_bytes(xx)
+            rs, ru = run.time_shared_ab(dx, gg, n, args.warmup)
+            shm, um = float(np.mean(rs)), float(np.mean(ru))
+            log(f"[bench] shared-prefix decode, {name.split(':')[0]}: shared {shm * 1e3:.1f} us "
+                f"({unique / shm / 1e6:.0f} GB/s unique), unshared {um * 1e3:.1f} us "
+                f"({unique / um / 1e6:.0f} GB/s unique)")
+            sh.append({
+                "workload": name, "groups": gg.num_groups,
+                "sharers": int(gg.group_start[-1]), "unique_kv_bytes": unique,
+                "logical_kv_bytes": logical, "gbs_unique": round(unique / shm / 1e6, 2),
+                **_stats(rs),
+                "unshared": {"gbs_unique": round(unique / um / 1e6, 2), **_stats(ru)},
+                "speedup": round(um / shm, 3),
+                "roofline": hbm_roofline("prefill_kernel (prefix launch) + decode_kernel, one "
+                                         "call", unique, shm, key, sha_shared)})
+            del dx
+        sections["decode_shared_prefix"] = sh
     if "small" in only:
         # latency-bound decode: one to four requests over long contexts
         # (H 32/8, D 128, page 16), where the merge of many pieces per row

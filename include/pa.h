@@ -309,10 +309,12 @@ pa_status pa_attention(const pa_args *args, const pa_workspace *ws, void *stream
  * (section 3.3).  The result is the same attention as pa_decode's, up to
  * rounding order.
  *
- * Groups are consecutive ranges of requests that cover the batch: group k
- * holds requests group_start[k] .. group_start[k + 1] - 1 (group_start[0] =
- * 0, nondecreasing, group_start[num_groups] = batch); a request that shares
- * nothing is a group of its own with prefix 0.  Group k shares its first
+ * Groups are consecutive ranges of requests from the start of the batch:
+ * group k holds requests group_start[k] .. group_start[k + 1] - 1
+ * (group_start[0] = 0, nondecreasing, group_start[num_groups] <= batch), and
+ * the requests from group_start[num_groups] on share nothing (a caller moves
+ * the sharers of each prefix next to each other, at the front).  num_groups
+ * 0 is a plain decode.  Group k shares its first
  * P_k = prefix_lens[k] - prefix_lens[k] % page_size keys (whole pages only;
  * a partial page is walked by each request).  Device-side contract, taken on
  * trust like the block-table contract: every member's block table names the
@@ -322,23 +324,27 @@ pa_status pa_attention(const pa_args *args, const pa_workspace *ws, void *stream
  * group k has at most max_group_size requests. */
 typedef struct pa_prefix_groups {
   const int32_t *group_start; /* [num_groups + 1] int32, device */
-  const int32_t *prefix_lens; /* [num_groups] int32, device: shared keys of each group */
-  int32_t num_groups;         /* >= 1 (batch >= 1) */
+  const int32_t *prefix_lens; /* [num_groups] int32, device: shared keys of each group
+                                 (may be NULL when num_groups is 0) */
+  int32_t num_groups;         /* 0 .. batch */
   int32_t max_group_size;     /* >= 1: bound on the requests of a group */
 } pa_prefix_groups;
 
 /* Plan of pa_decode_shared (sizes only; nothing runs on the GPU): the decode
  * part's balanced plan with the merge fused (plan->num_splits piece slots,
- * plan->num_counters = batch * U + prefill_splits counters) and the prefix
- * launch's key split (plan->prefill_splits slots, 0: unsplit).  Workspace
- * layout, each part in its own region:
+ * plan->num_counters = batch * U counters) and the slot count the prefix
+ * launch plans its key split with (plan->prefill_splits, 0: unsplit).  The
+ * prefix launch cuts each row tile's prefix keys into at most 16 pieces and
+ * every piece leaves its own state of each member row (no merge there: the
+ * decode launch folds a row's prefix states into the row's merge).
+ * Workspace layout, each part in its own region (N = batch * H_q * q_len
+ * rows, states by output row index):
  *   partial_out  decode: num_splits * R * head_dim floats, then the prefix
- *                states: batch * H_q * q_len * head_dim floats, then the key
- *                split: prefill_splits * head_dim * 128 floats;
+ *                states: N * 16 * head_dim floats;
  *   partial_lse  decode: num_splits * R floats rounded up to a multiple of
- *                16, then batch * H_q * q_len rounded up to a multiple of 16,
- *                then prefill_splits * 512 floats;
- *   counters     decode: batch * U, then prefill_splits;
+ *                16, then N * 16 log-sum-exps rounded up to a multiple of
+ *                16, then N int32 piece counts (rounded up to 16);
+ *   counters     decode: batch * U;
  * R, U as for the balanced schedule.  *workspace_bytes is all of partial_out
  * and partial_lse.  PA_ERR_UNSUPPORTED: dtype other than bf16, fp8 pages,
  * debug outputs, or a batch the balanced schedule does not take. */

@@ -119,6 +119,9 @@ def make_args(query: torch.Tensor, key_pages: torch.Tensor, value_pages: torch.T
     a.k_scale = float(k_scale) if fp8 else 1.0
     a.v_scale = float(v_scale) if fp8 else 1.0
     a.query_start_loc = _ptr(query_start_loc)
+    # the struct holds raw device addresses: keep the tensors alive with it
+    a._tensors = (query, key_pages, value_pages, block_table, context_lens, out, query_lens,
+                  debug_trace, debug_visits, query_start_loc)
     return a
 
 
@@ -323,25 +326,32 @@ class RaggedWorkspace:
         return [self.partial_out, self.partial_lse, self.counters]
 
 
-def make_groups(group_start: torch.Tensor, prefix_lens: torch.Tensor,
-                max_group_size: Optional[int] = None) -> "_lib.PaPrefixGroups":
-    """Fill a pa_prefix_groups from device tensors: group_start [G + 1] and
-    prefix_lens [G] int32 (consecutive request ranges covering the batch).
-    max_group_size defaults to the largest group, read from group_start (a
-    device-to-host copy)."""
-    _int32(group_start, "group_start")
-    _int32(prefix_lens, "prefix_lens")
-    _same_gpu(group_start, prefix_lens=prefix_lens)
-    ng = prefix_lens.shape[0]
-    _shape(group_start, (ng + 1,), "group_start")
-    if max_group_size is None:
-        max_group_size = int((group_start[1:] - group_start[:-1]).max().item()) if ng else 1
-    g = _lib.PaPrefixGroups()
-    g.group_start = _ptr(group_start)
-    g.prefix_lens = _ptr(prefix_lens)
-    g.num_groups = int(ng)
-    g.max_group_size = int(max_group_size)
-    return g
+class PrefixGroups:
+    """A pa_prefix_groups over device tensors group_start [G + 1] and
+    prefix_lens [G] int32 (consecutive request ranges from request 0); it
+    holds the tensors, so they live as long as the struct that points at
+    them.  max_group_size defaults to the largest group, read from
+    group_start (a device-to-host copy)."""
+
+    def __init__(self, group_start: torch.Tensor, prefix_lens: torch.Tensor,
+                 max_group_size: Optional[int] = None):
+        _int32(group_start, "group_start")
+        _int32(prefix_lens, "prefix_lens")
+        _same_gpu(group_start, prefix_lens=prefix_lens)
+        ng = prefix_lens.shape[0]
+        _shape(group_start, (ng + 1,), "group_start")
+        if max_group_size is None:
+            max_group_size = (int((group_start[1:] - group_start[:-1]).max().item())
+                              if ng else 1)
+        self.group_start, self.prefix_lens = group_start, prefix_lens
+        self.c = _lib.PaPrefixGroups()
+        self.c.group_start = _ptr(group_start)
+        self.c.prefix_lens = _ptr(prefix_lens) if ng else None
+        self.c.num_groups = int(ng)
+        self.c.max_group_size = int(max_group_size)
+
+
+PREFIX_PIECES = 16  # prefix states per row of a shared-prefix call (include/pa.h)
 
 
 class SharedPlan(NamedTuple):
@@ -354,11 +364,12 @@ class SharedPlan(NamedTuple):
     workspace_bytes: int
 
 
-def pa_decode_shared_plan(args: PaArgs, groups, *, num_cus: int = 0) -> SharedPlan:
+def pa_decode_shared_plan(args: PaArgs, groups: PrefixGroups, *,
+                          num_cus: int = 0) -> SharedPlan:
     ws = PaWorkspace()
     nbytes = ctypes.c_size_t(0)
     _lib.check("pa_decode_shared_plan", _lib.lib().pa_decode_shared_plan(
-        ctypes.byref(args), ctypes.byref(groups), int(num_cus), ctypes.byref(ws),
+        ctypes.byref(args), ctypes.byref(groups.c), int(num_cus), ctypes.byref(ws),
         ctypes.byref(nbytes)))
     return SharedPlan(ws.num_splits, ws.num_counters, ws.prefill_splits, nbytes.value)
 
@@ -373,10 +384,11 @@ class SharedWorkspace:
         R = _rows_per_block(min(8, (args.num_q_heads // args.num_kv_heads) * args.q_len))
         rows = args.batch * args.num_q_heads * args.q_len
         r16 = lambda x: -(-x // 16) * 16  # noqa: E731
-        self.partial_out = torch.empty(S * R * D + rows * D + Sp * D * 128, dtype=torch.float32,
+        n = PREFIX_PIECES
+        self.partial_out = torch.empty(S * R * D + rows * n * D, dtype=torch.float32,
                                        device=device)
-        self.partial_lse = torch.empty(r16(S * R) + r16(rows) + Sp * 512, dtype=torch.float32,
-                                       device=device)
+        self.partial_lse = torch.empty(r16(S * R) + r16(rows * n) + r16(rows),
+                                       dtype=torch.float32, device=device)
         if (self.partial_out.numel() + self.partial_lse.numel()) * 4 != plan.workspace_bytes:
             raise ValueError("workspace size disagrees with the library's plan")
         self.counters = torch.zeros(int(plan.num_counters), dtype=torch.int32, device=device)
@@ -393,10 +405,12 @@ class SharedWorkspace:
         return [self.partial_out, self.partial_lse, self.counters]
 
 
-def pa_decode_shared(args: PaArgs, groups, workspace: SharedWorkspace, stream=None) -> None:
+def pa_decode_shared(args: PaArgs, groups: PrefixGroups, workspace: SharedWorkspace,
+                     stream=None) -> None:
     """Decode with each group's shared prefix pages read once per group."""
     _lib.check("pa_decode_shared", _lib.lib().pa_decode_shared(
-        ctypes.byref(args), ctypes.byref(groups), ctypes.byref(workspace.c), _stream(stream)))
+        ctypes.byref(args), ctypes.byref(groups.c), ctypes.byref(workspace.c),
+        _stream(stream)))
 
 
 def pa_attention_plan(args: PaArgs, *, num_cus: int = 0,

@@ -561,7 +561,7 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
       const size_t wi = (size_t)io.first * ROWS;
       merge_block<T, D, ROWS>(p.ws_lse + wi, p.ws_o + wi * D, io.pieces, valid, qrow,
                               min(ROWS, rows_out - rb * ROWS), out, pre ? p.pre_lse : nullptr,
-                              p.pre_o);
+                              p.pre_o, p.pre_n);
       if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -623,14 +623,16 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
   const int per = (B + 255) / 256;
   const bool shared = p.grp_start != nullptr;
   if (shared) {
-    // Shared prefixes: each non-empty group marks its first request, and an
-    // inclusive max scan of the marks over the requests names the group of
-    // every request (the groups are consecutive ranges covering the batch).
+    // Shared prefixes: each non-empty group marks its first request, and the
+    // first request past the groups is marked num_groups (no group); the
+    // groups are consecutive ranges from request 0, so an inclusive max scan
+    // of the marks over the requests names the group of every request.
     for (int b = tid; b < B; b += 256) s_pre[b] = -1;
     __syncthreads();
-    for (int k = tid; k < p.num_groups; k += 256) {
+    for (int k = tid; k <= p.num_groups; k += 256) {
       const int first = p.grp_start[k];
-      if (first >= 0 && first < p.grp_start[k + 1] && first < B) s_pre[first] = k;  // distinct
+      const bool mark = k == p.num_groups || first < p.grp_start[k + 1];  // distinct positions
+      if (mark && first >= 0 && first < B) s_pre[first] = k;
     }
     __syncthreads();
     long long mark = -1;
@@ -651,7 +653,7 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
       const int b = tid * per + k;
       if (b < B) {
         grp = max(grp, (long long)s_pre[b]);
-        s_pre[b] = grp >= 0 ? group_prefix_keys(p, (int)grp) : 0;
+        s_pre[b] = grp >= 0 && grp < p.num_groups ? group_prefix_keys(p, (int)grp) : 0;
       }
     }
     __syncthreads();  // s_sum is reused below

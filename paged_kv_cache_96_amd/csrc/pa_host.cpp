@@ -450,7 +450,7 @@ PA_EXPORT pa_status pa_attention(const pa_args *args, const pa_workspace *ws, vo
       !ws->counters || !aligned16(ws->partial_out) || !aligned16(ws->partial_lse) ||
       (reinterpret_cast<uintptr_t>(ws->counters) & 3u) ||
       (int64_t)ws->num_splits < dec_counters + 1 || ws->prefill_splits < 0 ||
-      (int64_t)ws->num_counters < dec_counters + ws->prefill_splits)
+      (int64_t)ws->num_counters < dec_counters)
     return PA_ERR_WORKSPACE;
   pa_workspace wd;
   memset(&wd, 0, sizeof wd);
@@ -509,10 +509,10 @@ pa_status check_groups(const pa_args *a, const pa_prefix_groups *g) {
   if (a->dtype != PA_DTYPE_BF16 || kv_fp8(a)) return PA_ERR_UNSUPPORTED;
   if (a->debug_trace || a->debug_visits) return PA_ERR_UNSUPPORTED;
   if (a->batch == 0) return PA_OK;
-  if (g->num_groups < 1 || g->num_groups > a->batch || g->max_group_size < 1 ||
+  if (g->num_groups < 0 || g->num_groups > a->batch || g->max_group_size < 1 ||
       g->max_group_size > a->batch)
     return PA_ERR_INVALID_ARG;
-  if (!g->group_start || !g->prefix_lens ||
+  if (!g->group_start || (g->num_groups > 0 && !g->prefix_lens) ||
       (reinterpret_cast<uintptr_t>(g->group_start) & 3u) ||
       (reinterpret_cast<uintptr_t>(g->prefix_lens) & 3u))
     return PA_ERR_INVALID_ARG;
@@ -541,21 +541,23 @@ PA_EXPORT pa_status pa_decode_shared_plan(const pa_args *args, const pa_prefix_g
   size_t db = 0, pb = 0;
   if ((st = pa_decode_plan(args, num_cus, &dec, &db)) != PA_OK) return st;
   if (dec.schedule != PA_SCHEDULE_BALANCED) return PA_ERR_UNSUPPORTED;  // batch above 2048
-  if (args->batch > 0) {
+  if (args->batch > 0 && groups->num_groups > 0) {
     const pa_args v = prefix_launch_args(args, groups);
     if ((st = pa_prefill_plan(&v, num_cus, &pre, &pb)) != PA_OK) return st;
   }
+  (void)pb;  // the prefix launch plans pieces but merges none: no split workspace
   const size_t R = (size_t)decode_block_rows(args);
   const size_t rows = state_rows(args);
   plan->schedule = PA_SCHEDULE_BALANCED;
   plan->partition_tokens = 0;
   plan->num_splits = dec.num_splits;
-  plan->num_counters = dec.num_counters + pre.num_counters;
+  plan->num_counters = dec.num_counters;
   plan->prefill_splits = pre.num_splits;
   if (workspace_bytes)
     *workspace_bytes = ((size_t)dec.num_splits * R * args->head_dim +
-                        round16((size_t)dec.num_splits * R) + rows * args->head_dim +
-                        round16(rows)) * sizeof(float) + pb;
+                        round16((size_t)dec.num_splits * R) +
+                        rows * pa::kPrefixPieces * args->head_dim +
+                        round16(rows * pa::kPrefixPieces) + round16(rows)) * sizeof(float);
   return PA_OK;
 }
 
@@ -573,7 +575,7 @@ PA_EXPORT pa_status pa_decode_shared(const pa_args *args, const pa_prefix_groups
       !ws->counters || !aligned16(ws->partial_out) || !aligned16(ws->partial_lse) ||
       (reinterpret_cast<uintptr_t>(ws->counters) & 3u) ||
       (int64_t)ws->num_splits < dec_counters + 1 || ws->prefill_splits < 0 ||
-      (int64_t)ws->num_counters < dec_counters + ws->prefill_splits)
+      (int64_t)ws->num_counters < dec_counters)
     return PA_ERR_WORKSPACE;
   pa_workspace wd;
   memset(&wd, 0, sizeof wd);
@@ -586,31 +588,33 @@ PA_EXPORT pa_status pa_decode_shared(const pa_args *args, const pa_prefix_groups
   int32_t S, P;
   bool balanced;
   if ((st = check_workspace(args, &wd, &S, &P, &balanced)) != PA_OK) return st;
+  const size_t rows = state_rows(args);
   float *state_o = ws->partial_out + (size_t)S * R * args->head_dim;
   float *state_lse = ws->partial_lse + round16((size_t)S * R);
-  const size_t rows = state_rows(args);
+  int32_t *state_n = reinterpret_cast<int32_t *>(state_lse + round16(rows * pa::kPrefixPieces));
   // the prefix launch: each group's member rows over its shared pages
-  const pa_args v = prefix_launch_args(args, groups);
-  const int32_t cap = args->max_pages * args->page_size;
-  pa::LaunchParams pp = make_params(&v, 1, cap, false, nullptr);
-  pp.grp_start = groups->group_start;
-  pp.grp_pre = groups->prefix_lens;
-  pp.num_groups = groups->num_groups;
-  pp.prefix_pass = 1;
-  pp.Lm = args->q_len;
-  pp.qsl = args->query_start_loc;  // member rows are addressed as in the call
-  pp.ql = args->query_lens;
-  pp.pre_o = state_o;
-  pp.pre_lse = state_lse;
-  if (ws->prefill_splits >= 2 && prefill_splits(&v)) {
-    pp.ws_o = state_o + rows * args->head_dim;
-    pp.ws_lse = state_lse + round16(rows);
-    pp.counters = ws->counters + dec_counters;
-    pp.num_splits = ws->prefill_splits;
+  if (groups->num_groups > 0) {
+    const pa_args v = prefix_launch_args(args, groups);
+    const int32_t cap = args->max_pages * args->page_size;
+    pa::LaunchParams pp = make_params(&v, 1, cap, false, nullptr);
+    pp.grp_start = groups->group_start;
+    pp.grp_pre = groups->prefix_lens;
+    pp.num_groups = groups->num_groups;
+    pp.prefix_pass = 1;
+    pp.Lm = args->q_len;
+    pp.qsl = args->query_start_loc;  // member rows are addressed as in the call
+    pp.ql = args->query_lens;
+    pp.pre_o = state_o;
+    pp.pre_lse = state_lse;
+    pp.pre_n = state_n;
+    // the key split plans with prefill_splits slots; its pieces leave row
+    // states and merge nothing, so they need no split workspace
+    if (ws->prefill_splits >= 2 && prefill_splits(&v)) pp.num_splits = ws->prefill_splits;
+    const int64_t tiles = prefill_tiles(&v);
+    if (tiles * v.num_kv_heads * v.batch + pp.num_splits / 2 + 1 > INT32_MAX)
+      return PA_ERR_INVALID_ARG;
+    if (pa::launch_prefill_mfma(pp, (hipStream_t)stream) != hipSuccess) return PA_ERR_HIP;
   }
-  const int64_t tiles = prefill_tiles(&v);
-  if (tiles * v.num_kv_heads * v.batch + ws_slots(pp) > INT32_MAX) return PA_ERR_INVALID_ARG;
-  if (pa::launch_prefill_mfma(pp, (hipStream_t)stream) != hipSuccess) return PA_ERR_HIP;
   // the decode launch: keys past each request's prefix, merged with its state
   pa::LaunchParams pd = make_params(args, S, P, balanced, &wd);
   pd.grp_start = groups->group_start;
@@ -618,6 +622,7 @@ PA_EXPORT pa_status pa_decode_shared(const pa_args *args, const pa_prefix_groups
   pd.num_groups = groups->num_groups;
   pd.pre_o = state_o;
   pd.pre_lse = state_lse;
+  pd.pre_n = state_n;
   return hip_status(pa::launch_decode(pd, (pa::DType)args->dtype, (hipStream_t)stream));
 }
 

@@ -48,9 +48,20 @@ struct LaunchParams {
   int32_t num_groups;
   int32_t prefix_pass;
   int32_t Lm;               // prefix launch: query rows per member (the call's q_len)
-  float *pre_o;             // prefix states by output row: normalised output fp32 [rows, D]
-  float *pre_lse;           // and natural-log log-sum-exp [rows] (-inf: no key)
+  // Prefix states by output row: the prefix launch splits a group's prefix
+  // keys into at most kPrefixPieces pieces per row tile, and piece s of a
+  // row leaves its normalised output pre_o[(row * kPrefixPieces + s) * D ..]
+  // and natural-log log-sum-exp pre_lse[row * kPrefixPieces + s] (-inf: no
+  // key); pre_n[row] is the row's piece count.  The decode launch folds them
+  // into the row's merge.
+  float *pre_o;
+  float *pre_lse;
+  int32_t *pre_n;
 };
+
+// Most pieces the prefix launch cuts one row tile's prefix keys into (so a
+// row's prefix states fit one batch of loads of the decode merge).
+constexpr int kPrefixPieces = 16;
 
 // Query rows of request b.
 __device__ __forceinline__ int query_rows(const LaunchParams &p, int b) {

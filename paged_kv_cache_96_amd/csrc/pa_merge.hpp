@@ -9,6 +9,7 @@
 #pragma once
 
 #include "pa_common.hpp"
+#include "pa_internal.h"
 
 namespace pa {
 
@@ -102,15 +103,18 @@ namespace pa {
 // of up to 16 pieces are in flight together: the states are read past the
 // caches, and a row block split into many pieces (a small batch over long
 // contexts) would otherwise pay one memory round trip per piece.
-// With pre_lse (shared-prefix decode) every valid row starts from its prefix
-// state, pre_lse[row] and pre_o[row * D ...] at its output row index, which
-// an earlier launch on the stream wrote (ordinary loads see it).
+// With pre_lse (shared-prefix decode) every valid row first folds its
+// prefix states: pre_n[row] of them, state s at pre_lse[row * kPrefixPieces
+// + s] and pre_o[(row * kPrefixPieces + s) * D ...] by the row's output
+// index, which an earlier launch on the stream wrote (ordinary loads see
+// it).
 template <typename T, int D, int R>
 __device__ __forceinline__ void merge_block(const float *lse, const float *po, int n,
                                             const bool (&valid)[R], const size_t (&qrow)[R],
                                             int rows_in_range, T *out,
                                             const float *pre_lse = nullptr,
-                                            const float *pre_o = nullptr) {
+                                            const float *pre_o = nullptr,
+                                            const int32_t *pre_n = nullptr) {
   constexpr int kLanes = 64 / R;       // lanes per row
   constexpr int kE = D / kLanes;       // elements per lane
   static_assert(kLanes * R == 64 && kE * kLanes == D && kE % 4 == 0 || kE < 4, "layout");
@@ -134,13 +138,36 @@ __device__ __forceinline__ void merge_block(const float *lse, const float *po, i
   float m = kNegInf, l = 0.f, acc[kE];
 #pragma unroll
   for (int e = 0; e < kE; ++e) acc[e] = 0.f;
-  if (pre_lse != nullptr && ok) {
-    const float ls = pre_lse[row];
-    if (ls != kNegInf) {  // the prefix state: its normalised output with l = 1
-      m = ls;
-      l = 1.f;
+  // fold one state (log-sum-exp ls, normalised output v)
+  auto fold = [&](float ls, const float (&v)[kE]) {
+    const float mn = fmaxf(m, ls);
+    const bool none = mn == kNegInf;  // nothing seen yet: the state stays (-inf, 0, 0)
+    const float a = none ? 0.f : fast_exp2((m - mn) * kMergeLog2e);  // m = -inf -> 0
+    const float w = none ? 0.f : fast_exp2((ls - mn) * kMergeLog2e);
+    m = mn;
+    l = fmaf(l, a, w);
 #pragma unroll
-      for (int e = 0; e < kE; ++e) acc[e] = pre_o[row * D + e0 + e];
+    for (int e = 0; e < kE; ++e) acc[e] = none ? 0.f : fmaf(acc[e], a, w * v[e]);
+  };
+  if (pre_lse != nullptr && ok) {
+    // batches of kBatch slots, all loaded at once (every slot of the row
+    // lies in the buffer; slots past the count are loaded but not folded)
+    constexpr int kBatch = kE <= 4 ? 16 : kE <= 8 ? 8 : 4;
+    static_assert(kPrefixPieces % kBatch == 0, "batches");
+    const int npre = min(pre_n[row], kPrefixPieces);  // the same for every row of the block
+    const float *pl = pre_lse + row * kPrefixPieces;
+    const float *pv = pre_o + row * kPrefixPieces * D + e0;
+    for (int s0 = 0; s0 < npre; s0 += kBatch) {
+      float ls[kBatch], v[kBatch][kE];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        ls[k] = pl[s0 + k];
+#pragma unroll
+        for (int e = 0; e < kE; ++e) v[k][e] = pv[(s0 + k) * D + e];
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        if (s0 + k < npre) fold(ls[k], v[k]);
     }
   }
 #pragma unroll 16
@@ -164,14 +191,7 @@ __device__ __forceinline__ void merge_block(const float *lse, const float *po, i
         v[e] = __uint_as_float(
             (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(ro, base + e * 4, 0, kSysScope));
     }
-    const float mn = fmaxf(m, ls);
-    const bool none = mn == kNegInf;  // nothing seen yet: the state stays (-inf, 0, 0)
-    const float a = none ? 0.f : fast_exp2((m - mn) * kMergeLog2e);  // m = -inf -> 0
-    const float w = none ? 0.f : fast_exp2((ls - mn) * kMergeLog2e);
-    m = mn;
-    l = fmaf(l, a, w);
-#pragma unroll
-    for (int e = 0; e < kE; ++e) acc[e] = none ? 0.f : fmaf(acc[e], a, w * v[e]);
+    fold(ls, v);
   }
   if (r >= rows_in_range) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;

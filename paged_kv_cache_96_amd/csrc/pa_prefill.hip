@@ -61,6 +61,13 @@
 // arrive reads them all back, merges them in piece order (so the result
 // does not depend on the order of arrival) and writes the output.  No
 // workgroup waits for another.
+//
+// Prefix launch of a shared-prefix decode (p.prefix_pass): one request per
+// group of requests that share their first pages, holding the query rows
+// of all the members over the shared keys; its tiles are cut into at most
+// kPrefixPieces pieces, and each piece writes its own state of every member
+// row (normalised output and log-sum-exp) for the decode kernel's merge,
+// so nothing is merged here.
 #include <type_traits>
 
 #include "pa_common.hpp"
@@ -81,8 +88,10 @@ constexpr float kRefSlack = 16.0f; // largest row max above the reference (log2)
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= 8 (the eight loads of one
 // staging set may stay in flight), expcnt and lgkmcnt not waited for.
 constexpr int kWaitVmcntOlderThan8 = 8 | (0x7 << 4) | (0xF << 8);
-// Key split: shortest piece.
+// Key split: shortest piece (the prefix launch of a shared-prefix decode:
+// shorter, as its pieces are never merged here).
 constexpr int kMinPieceKeys = 4 * kBN;
+constexpr int kMinPrefixPieceKeys = 2 * kBN;
 
 template <int D>
 struct Tile {
@@ -255,7 +264,7 @@ __device__ void find_piece(const LaunchParams &p, int nt, int *s_ctx, int *s_ql,
   const float work = ((s_redf[0] + s_redf[1]) + (s_redf[2] + s_redf[3])) * (float)p.Hkv;
   const float target = 0.4f * (float)max(2, p.num_splits);
   const float blocks = fminf(ceilf(work / target), (float)(1 << 24));  // P / BN
-  const int P = max(kMinPieceKeys, (int)blocks * kBN);
+  const int P = max(p.prefix_pass ? kMinPrefixPieceKeys : kMinPieceKeys, (int)blocks * kBN);
   auto npieces = [&](int k, int len) { return k > len ? (k + len - 1) / len : 1; };
   auto cls = [&](int len) {
     return 4 * (long long)len >= 3LL * P ? 0 : 2 * (long long)len >= P ? 1
@@ -266,7 +275,8 @@ __device__ void find_piece(const LaunchParams &p, int nt, int *s_ctx, int *s_ql,
     const int k = s_keys[q];
     int len = k;
     if (k > P) {
-      const int n0 = (k + P - 1) / P;
+      // the prefix launch cuts a tile into kPrefixPieces pieces at most
+      const int n0 = min((k + P - 1) / P, p.prefix_pass ? kPrefixPieces : k);
       len = ((k + n0 - 1) / n0 + kBN - 1) / kBN * kBN;
     }
     s_len[q] = len;
@@ -426,7 +436,9 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   // ---- which keys of which tile: a piece of the key split (workspace
   // given), else the whole tile (heavy, late tiles first)
   int tile, g, b, k0 = 0, k1 = 0x7fffffff, np = 1, sp = 0, slot = 0;
-  if (p.ws_o != nullptr) {
+  // the prefix launch plans pieces without a merge workspace (each piece
+  // leaves its own row states)
+  if (p.ws_o != nullptr || (p.prefix_pass && p.num_splits > 1)) {
     Piece pc;
     find_piece(p, num_tiles, plan_a, plan_b, plan_c, plan_d, plan_s, &s_pc, pc);
     if (!pc.found) return;  // block-uniform
@@ -908,7 +920,7 @@ prefill_kernel(LaunchParams p, int num_tiles) {
 
   // ---- a piece of a split tile: publish this piece's state; the last piece
   // to arrive merges all of them and writes the output
-  if (np > 1) {
+  if (np > 1 && !p.prefix_pass) {
     if constexpr (RB == 1) {
       constexpr int kAcc = TL::kMBlocks * 16;  // accumulators per thread (D / 2)
       auto slot_o = [&](int s) {
@@ -921,9 +933,12 @@ prefill_kernel(LaunchParams p, int num_tiles) {
       };
       // [value / 4][thread][4]: every 16-byte store and load of a wave is
       // one coalesced 1 KiB row; written through to memory for the merging
-      // workgroup, which may run on another XCD
+      // workgroup, which may run on another XCD.  A wave whose rows all lie
+      // past the request's rows publishes and merges nothing (those rows
+      // are written as zeros, or not at all).
+      const bool live_w = rho_first_w < rows_valid;  // wave-uniform
       auto off4 = [&](int mb, int j) { return ((mb * 4 + j) * 256 + tid) * 16; };
-      {
+      if (live_w) {
         const auto ro = slot_o(sp);
         const auto rm = slot_m(sp);
 #pragma unroll
@@ -950,37 +965,50 @@ prefill_kernel(LaunchParams p, int num_tiles) {
       auto ld = [](__amdgpu_buffer_rsrc_t r, int off) {
         return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSysScope));
       };
-      // every piece, this one included, is read back and summed in piece
-      // order: the result does not depend on which piece arrived last
-      float M = kMinM;
-      for (int s2 = 0; s2 < np; ++s2) M = fmaxf(M, ld(slot_m(s2), tid * 4));
-      m_ref[0] = M;  // the merged state's reference
-      l_run[0] = 0.f;
+      // Every piece, this one included, is read back and summed in piece
+      // order: the result does not depend on which piece arrived last.  The
+      // maxima come first, 16 pieces per batch of loads in flight together
+      // (a slot past the last piece reads as empty: its offset lies outside
+      // the resource); then each piece costs one round trip to memory.
+      if (live_w) {
+        float M = kMinM;
+        for (int s0 = 0; s0 < np; s0 += 16) {
+          float ms[16];
 #pragma unroll
-      for (int mb = 0; mb < TL::kMBlocks; ++mb)
+          for (int k = 0; k < 16; ++k)
+            ms[k] = ld(slot_m(s0 + k), s0 + k < np ? tid * 4 : (int)0x80000000u);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[0][mb][i] = 0.f;
-      for (int s2 = 0; s2 < np; ++s2) {
-        const auto ro = slot_o(s2);
-        const auto rm = slot_m(s2);
-        const float f = fast_exp2(ld(rm, tid * 4) - M);
-        l_run[0] = fmaf(f, ld(rm, (256 + tid) * 4), l_run[0]);
+          for (int k = 0; k < 16; ++k) M = fmaxf(M, s0 + k < np ? ms[k] : kMinM);
+        }
+        m_ref[0] = M;  // the merged state's reference
+        l_run[0] = 0.f;
 #pragma unroll
         for (int mb = 0; mb < TL::kMBlocks; ++mb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(ro, off4(mb, j), 0, kSysScope);
+          for (int i = 0; i < 16; ++i) o[0][mb][i] = 0.f;
+        for (int s2 = 0; s2 < np; ++s2) {
+          const auto ro = slot_o(s2);
+          const auto rm = slot_m(s2);
+          const float f = fast_exp2(ld(rm, tid * 4) - M);
+          l_run[0] = fmaf(f, ld(rm, (256 + tid) * 4), l_run[0]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              o[0][mb][4 * j + e] = fmaf(f, __uint_as_float(v[e]), o[0][mb][4 * j + e]);
-          }
+          for (int mb = 0; mb < TL::kMBlocks; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(ro, off4(mb, j), 0, kSysScope);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                o[0][mb][4 * j + e] = fmaf(f, __uint_as_float(v[e]), o[0][mb][4 * j + e]);
+            }
+        }
       }
       if (tid == 0) __hip_atomic_store(p.counters + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
-  // ---- prefix launch: the state of each member row, by its output row
-  // index: normalised output (fp32) and natural-log log-sum-exp
+  // ---- prefix launch: this piece's state of each member row, by the
+  // row's output index: normalised output (fp32) and natural-log
+  // log-sum-exp, in piece slot sp of the row; piece 0 records the count
   if (p.prefix_pass) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -988,8 +1016,9 @@ prefill_kernel(LaunchParams p, int num_tiles) {
       if (!row_valid[rb]) continue;
       bool exists;
       const size_t orow = launch_row(p, b, qh[rb], qi[rb], exists);
+      const size_t ps_row = orow * kPrefixPieces + sp;
       const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      float *po = p.pre_o + orow * D;
+      float *po = p.pre_o + ps_row * D;
 #pragma unroll
       for (int mb = 0; mb < TL::kMBlocks; ++mb)
 #pragma unroll
@@ -1000,8 +1029,10 @@ prefill_kernel(LaunchParams p, int num_tiles) {
               make_float4(om[i4 * 4 + 0] * inv, om[i4 * 4 + 1] * inv, om[i4 * 4 + 2] * inv,
                           om[i4 * 4 + 3] * inv);
         }
-      if (half == 0)
-        p.pre_lse[orow] = l_tot > 0.f ? (m_ref[rb] + __log2f(l_tot)) * kLn2 : kNegInf;
+      if (half == 0) {
+        p.pre_lse[ps_row] = l_tot > 0.f ? (m_ref[rb] + __log2f(l_tot)) * kLn2 : kNegInf;
+        if (sp == 0) p.pre_n[orow] = np;
+      }
     }
     return;
   }
@@ -1034,8 +1065,9 @@ hipError_t launch_rb(const LaunchParams &p, hipStream_t stream) {
   const int tiles = (G * p.L + bm - 1) / bm;
   // key split: one workgroup per piece, at most one per tile plus half the
   // slots (see find_piece)
-  dim3 grid = p.ws_o ? dim3((unsigned)((long long)tiles * p.Hkv * p.B + max(1, p.num_splits / 2)))
-                     : dim3((unsigned)((long long)tiles * p.Hkv), p.B);
+  const bool split = p.ws_o != nullptr || (p.prefix_pass && p.num_splits > 1);
+  dim3 grid = split ? dim3((unsigned)((long long)tiles * p.Hkv * p.B + max(1, p.num_splits / 2)))
+                    : dim3((unsigned)((long long)tiles * p.Hkv), p.B);
   const long long pool = (long long)p.num_pages * p.Hkv * p.ps * D * 2;
   // the debug outputs select the instrumented build of the same staging mode
   const bool debug = p.dbg_trace || p.dbg_visits;

@@ -476,11 +476,11 @@ def test_shared_prefix_plan_layout(L):
     assert rc == 0 and ws.schedule == SCHEDULE_BALANCED
     units = a.batch * a.num_kv_heads             # G = 4: one row block of 4 per kv head
     assert ws.num_splits == units + 4 * 256 and ws.prefill_splits == 5 * 256
-    assert ws.num_counters == units + ws.prefill_splits
-    R, D, S, Sp = 4, a.head_dim, ws.num_splits, ws.prefill_splits
+    assert ws.num_counters == units
+    R, D, S = 4, a.head_dim, ws.num_splits
     rows = a.batch * a.num_q_heads * a.q_len
     r16 = lambda x: -(-x // 16) * 16  # noqa: E731
-    assert n == (S * R * D + r16(S * R) + rows * D + r16(rows)) * 4 + Sp * (D // 2 + 2) * 256 * 4
+    assert n == (S * R * D + r16(S * R) + rows * 16 * D + r16(rows * 16) + r16(rows)) * 4
     # more (group, tile) pairs than the key split plans over: the prefix
     # launch runs unsplit and needs no split region
     big = h.args(batch=2048, num_q_heads=64, num_kv_heads=1, q_len=8)
@@ -489,7 +489,7 @@ def test_shared_prefix_plan_layout(L):
 
 
 @pytest.mark.parametrize("kw,gkw,code", [
-    ({}, {"num_groups": 0}, -1),
+    ({}, {"num_groups": -1}, -1),
     ({}, {"num_groups": 3}, -1),                  # more groups than requests
     ({}, {"max_group_size": 0}, -1),
     ({}, {"max_group_size": 3}, -1),              # larger than the batch
@@ -525,6 +525,9 @@ def test_shared_prefix_checks_before_launch(L):
     plan.partial_out = plan.partial_lse = plan.counters = h.p
     plan.num_counters -= 1                        # one counter short
     assert L.pa_decode_shared(ctypes.byref(a), ctypes.byref(g), ctypes.byref(plan), None) == -3
+    # no groups: no prefix launch, so no key-split slots in the plan
+    rc, plan0, _ = _shared_plan(L, a, _groups(h, num_groups=0))
+    assert rc == 0 and plan0.prefill_splits == 0
     # an empty batch is a no-op
     z = h.args(batch=0)
     assert L.pa_decode_shared(ctypes.byref(z), ctypes.byref(g), ctypes.byref(ws), None) == 0

@@ -39,7 +39,7 @@ def _run_shared(api, x, groups, *, q=None, qsl=None, calls=1, prefix_lens=None, 
                          query_lens=d.ql if qsl is None else None, **kw)
     pl = groups.prefix_lens if prefix_lens is None else prefix_lens
     gs_d, pl_d = dev(groups.group_start), dev(np.asarray(pl, dtype=np.int32))
-    g = api.make_groups(gs_d, pl_d, groups.max_group_size)
+    g = api.PrefixGroups(gs_d, pl_d, groups.max_group_size)
     plan = api.pa_decode_shared_plan(args, g, num_cus=num_cus)
     ws = api.SharedWorkspace(plan, args, qd.device)
     for _ in range(calls):
@@ -94,6 +94,30 @@ def test_shared_equals_unshared_decode(api):
     assert d.max() <= 1.6e-2, d.max()
 
 
+def test_shared_prefix_read_through_first_member_only(api):
+    """The prefix pages are read once per group, through the first member's
+    table: with every other member's prefix entries pointed at a free page
+    of garbage, the shared path still gives the attention of the intact
+    inputs (a path that walked those entries would read the garbage)."""
+    x, groups = make_shared(18, H_q=8, H_kv=2, L=1, D=128, page_size=16,
+                            group_sizes=[4, 3, 2], prefix_pages=[6, 3, 2], suffix=(1, 80),
+                            extra_free_pages=2)
+    ref = oracle.attention_of(x)
+    used = set(x.block_table[x.block_table >= 0].tolist())
+    free = [p for p in range(x.num_pages) if p not in used]
+    assert free
+    bt = x.block_table.copy()
+    for k in range(groups.num_groups):
+        s, e = int(groups.group_start[k]), int(groups.group_start[k + 1])
+        P = int(groups.prefix_lens[k]) // x.page_size
+        bt[s + 1:e, :P] = free[0]
+    import dataclasses
+    bad = dataclasses.replace(x, block_table=bt)
+    out, counters = _run_shared(api, bad, groups)
+    assert_parity(out, ref, "bf16", "first member's prefix only")
+    assert not counters.any()
+
+
 def test_shared_repeated_calls(api):
     """Calls in a row reuse one workspace (counters left zero each time) and
     give identical outputs."""
@@ -121,6 +145,20 @@ def test_shared_all_singletons_no_prefix(api):
     x, groups = make_shared(14, H_q=8, H_kv=2, L=1, D=128, page_size=16,
                             group_sizes=[1] * 7, prefix_pages=[0] * 7, suffix=(1, 500))
     _check(api, x, groups, "singletons")
+
+
+def test_shared_groups_then_unshared_requests(api):
+    """Groups at the front, then requests in no group (group_start ends
+    before the batch does), and the same batch with no groups at all."""
+    x, groups = make_shared(17, H_q=8, H_kv=2, L=1, D=128, page_size=16,
+                            group_sizes=[3, 2, 1, 1, 1], prefix_pages=[5, 2, 0, 0, 0],
+                            suffix=(1, 90))
+    from workloads import SharedGroups
+    front = SharedGroups(groups.group_start[:3].copy(), groups.prefix_lens[:2].copy())
+    assert front.group_start[-1] == 5 < x.B
+    _check(api, x, front, "front groups")
+    none = SharedGroups(np.zeros(1, dtype=np.int32), np.zeros(0, dtype=np.int32))
+    _check(api, x, none, "no groups")
 
 
 def test_shared_many_requests(api):
@@ -160,5 +198,5 @@ def test_shared_c5_decode(api):
     whole output against the oracle."""
     m = make_c5()
     x, groups, _ = c5_decode_grouped(m)
-    assert groups.group_start[1] == 11 and groups.prefix_lens[0] == 2048
+    assert list(groups.group_start) == [0, 11] and list(groups.prefix_lens) == [2048]
     _check(api, x, groups, "C5 decode shared")

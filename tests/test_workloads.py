@@ -105,4 +105,4 @@ def test_c5_decode_grouped_is_a_permutation():
     assert n == sum(1 for b in m.meta["sharers"] if b < dec.B)
     shared = m.meta["shared_page_ids"]
     assert (x.block_table[:n, :len(shared)] == np.asarray(shared)).all()
-    assert g.group_start[-1] == dec.B and (g.prefix_lens[1:] == 0).all()
+    assert list(g.group_start) == [0, n] and list(g.prefix_lens) == [len(shared) * dec.page_size]

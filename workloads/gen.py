@@ -535,8 +535,9 @@ def pack_ragged(m: MixedInputs) -> RaggedInputs:
 @dataclass
 class SharedGroups:
     """Group k holds requests group_start[k] .. group_start[k + 1] - 1 and
-    shares its first prefix_lens[k] keys (whole pages); the groups cover the
-    batch, a request that shares nothing is a group of its own with 0."""
+    shares its first prefix_lens[k] keys (whole pages); the groups are
+    consecutive ranges from request 0, and requests past the last group share
+    nothing."""
 
     group_start: np.ndarray   # [G + 1] int32
     prefix_lens: np.ndarray   # [G] int32
@@ -613,8 +614,8 @@ def make_shared(seed: int, *, H_q: int, H_kv: int, L: int, D: int, page_size: in
 
 def c5_decode_grouped(m: MixedInputs):
     """The decode part of a mixed workload with its prefix sharers moved to
-    the front as one group (the shared pages' keys as its prefix) and every
-    other request a group of its own.  Returns (PagedInputs, SharedGroups,
+    the front as one group (the shared pages' keys as its prefix), the other
+    requests after it in no group.  Returns (PagedInputs, SharedGroups,
     order): request i of the result is request order[i] of the decode part."""
     dec = m.decode
     sharers = [b for b in m.meta["sharers"] if b < dec.B]
@@ -630,10 +631,8 @@ def c5_decode_grouped(m: MixedInputs):
         query_lens=None if dec.query_lens is None else
         np.ascontiguousarray(dec.query_lens[order]), meta=dict(dec.meta))
     n_shared = len(m.meta["shared_page_ids"])
-    sizes = ([len(sharers)] if sharers else []) + [1] * len(rest)
-    gs = np.zeros(len(sizes) + 1, dtype=np.int32)
-    gs[1:] = np.cumsum(sizes)
-    pre = ([n_shared * dec.page_size] if sharers else []) + [0] * len(rest)
+    gs = np.asarray([0, len(sharers)] if sharers else [0], dtype=np.int32)
+    pre = [n_shared * dec.page_size] if sharers else []
     return x, SharedGroups(gs, np.asarray(pre, dtype=np.int32)), order
 
 
