@@ -788,8 +788,10 @@ prefill_kernel(LaunchParams p, int num_tiles) {
     if constexpr (DMA) {
       // tile kt is in LDS once every wave's loads of it are done; after the
       // barrier no wave still reads tile kt - 1, whose buffers take tile
-      // kt + 1 (a whole tile of compute to arrive)
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // kt + 1 (the loads write LDS through the memory path, not in order
+      // with LDS reads, so every wave's reads are complete before it
+      // arrives: lgkmcnt(0))
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
       __syncthreads();
     } else if constexpr (kTwoSets) {
       if (UNIFORM || kt + 2 < kt_end) stage_load(kt + 2, ld);
