@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 10
+#define PA_ABI_VERSION 11
 
 typedef enum {
   PA_OK = 0,
@@ -136,6 +136,13 @@ typedef struct pa_args {
    * q_len is then an upper bound on every request's row count (it sizes
    * tiles and plans), and query_lens must be NULL. */
   const int32_t *query_start_loc;
+  /* Packed rows only: T = query_start_loc[batch] (the rows of query and
+   * out), or 0 if the caller does not give it; 0 <= num_tokens <= batch *
+   * q_len.  It only sizes the prefill grid (a ragged call of many one-row
+   * requests then launches no workgroups for their tiles); the kernels
+   * read the row counts from query_start_loc.  Taken on trust: a value
+   * below the true T leaves rows unwritten. */
+  int32_t num_tokens;
 } pa_args;
 
 /* How pa_decode divides a call's keys among the waves of the GPU. */

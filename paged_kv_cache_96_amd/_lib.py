@@ -57,6 +57,7 @@ class PaArgs(ctypes.Structure):
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
         ("query_start_loc", ctypes.c_void_p),
+        ("num_tokens", ctypes.c_int32),
     ]
 
 
@@ -101,7 +102,7 @@ class PaPrefixGroups(ctypes.Structure):
     ]
 
 
-ABI_VERSION = 10  # PA_ABI_VERSION of the structs below
+ABI_VERSION = 11  # PA_ABI_VERSION of the structs below
 
 ROUTE_DECODE = 0
 ROUTE_PREFILL = 1

@@ -119,6 +119,7 @@ def make_args(query: torch.Tensor, key_pages: torch.Tensor, value_pages: torch.T
     a.k_scale = float(k_scale) if fp8 else 1.0
     a.v_scale = float(v_scale) if fp8 else 1.0
     a.query_start_loc = _ptr(query_start_loc)
+    a.num_tokens = int(query.shape[0]) if query_start_loc is not None else 0
     # the struct holds raw device addresses: keep the tensors alive with it
     a._tensors = (query, key_pages, value_pages, block_table, context_lens, out, query_lens,
                   debug_trace, debug_visits, query_start_loc)

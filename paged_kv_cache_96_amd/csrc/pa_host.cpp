@@ -40,6 +40,9 @@ pa_status check_sizes(const pa_args *a) {
   if (a->dtype != PA_DTYPE_F32 && a->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
   if (a->head_dim != 64 && a->head_dim != 128) return PA_ERR_UNSUPPORTED;
   if (a->query_start_loc && a->query_lens) return PA_ERR_INVALID_ARG;  // one or the other
+  if (a->num_tokens < 0 ||
+      (a->query_start_loc && (int64_t)a->num_tokens > (int64_t)a->batch * a->q_len))
+    return PA_ERR_INVALID_ARG;
   if (a->kv_dtype != PA_KV_SAME && a->kv_dtype != PA_KV_FP8_E4M3) return PA_ERR_INVALID_ARG;
   if (a->kv_dtype == PA_KV_FP8_E4M3) {
     if (!(a->k_scale > 0.f) || !isfinite(a->k_scale) || !(a->v_scale > 0.f) ||
@@ -173,6 +176,7 @@ pa::LaunchParams make_params(const pa_args *a, int32_t S, int32_t P, bool balanc
   p.k_scale = kv_fp8(a) ? a->k_scale : 1.f;
   p.v_scale = kv_fp8(a) ? a->v_scale : 1.f;
   p.qsl = a->query_start_loc;
+  p.num_tokens = a->query_start_loc ? a->num_tokens : 0;
   p.route = 0;
   if (balanced) p.grid_waves = pa::decode_balanced_waves(p, (pa::DType)a->dtype);
   return p;
@@ -379,6 +383,7 @@ int attention_route(const pa_args *a) {
 pa_args ragged_decode_args(const pa_args *a) {
   pa_args d = *a;
   d.q_len = 1;
+  d.num_tokens = 0;  // sizes prefill grids only
   return d;
 }
 
@@ -499,6 +504,7 @@ pa_args prefix_launch_args(const pa_args *a, const pa_prefix_groups *g) {
   v.q_len = g->max_group_size * a->q_len;
   v.query_lens = nullptr;
   v.query_start_loc = nullptr;
+  v.num_tokens = 0;
   v.mask = PA_MASK_NONE;
   return v;
 }
@@ -603,6 +609,7 @@ PA_EXPORT pa_status pa_decode_shared(const pa_args *args, const pa_prefix_groups
     pp.prefix_pass = 1;
     pp.Lm = args->q_len;
     pp.qsl = args->query_start_loc;  // member rows are addressed as in the call
+    pp.num_tokens = 0;
     pp.ql = args->query_lens;
     pp.pre_o = state_o;
     pp.pre_lse = state_lse;

@@ -35,6 +35,7 @@ struct LaunchParams {
   int32_t kv_fp8;           // 1: the pages hold fp8 E4M3 codes (query and out bf16)
   float k_scale, v_scale;   // fp8 pages: element value = code value * scale (else 1)
   const int32_t *qsl;       // packed rows: query_start_loc [B + 1], or nullptr ([B, Hq, L])
+  int32_t num_tokens;       // packed rows: T = qsl[B] when the caller gives it, else 0
   int32_t route;            // 0: every request; ragged call: 1 its decode requests, 2 the rest
   // Shared prefixes (pa_decode_shared): request groups grp_start[k] ..
   // grp_start[k + 1] - 1 read the same first grp_pre[k] keys (rounded down to

@@ -213,8 +213,12 @@ __device__ __forceinline__ int div_small(int x, int d, float rcp) {
 // workspace slots in pair order.  All 256 threads take part: each owns a
 // contiguous slice of pairs, per-thread counts are scanned within waves
 // (DPP) and across the four waves (LDS), and the thread whose slice holds
-// this workgroup's piece publishes it in s_pc.  s_ctx, s_ql, s_len and
-// s_keys: kSplitMaxPairs ints each, s_red 32 ints of scratch; the block
+// this workgroup's piece publishes it in s_pc.  Pairs with no row to write
+// (packed rows: a tile past the request's rows, or a request of the other
+// route) form a fifth class after the four, so every piece with work has a
+// lower index than every piece without, and a grid sized for the pairs that
+// can have rows covers them all.  s_ctx, s_ql, s_len and s_keys:
+// kSplitMaxPairs ints each, s_red 32 ints of scratch; the block
 // synchronises before returning (the tables live in the staging buffers).
 __device__ void find_piece(const LaunchParams &p, int nt, int *s_ctx, int *s_ql, int *s_len,
                            int *s_keys, int *s_red, Piece *s_pc, Piece &pc) {
@@ -243,7 +247,9 @@ __device__ void find_piece(const LaunchParams &p, int nt, int *s_ctx, int *s_ql,
       const int rho0 = t * 128;
       const int last = min(rho0 + 128, G * Lb) - 1;
       const int k = last < rho0 ? 0 : (p.causal ? ctx - Lb + div_small(last, G, rcpG) + 1 : ctx);
-      s_keys[q] = k;
+      // -1: a tile with no row to write (packed rows and the prefix launch
+      // write only rows that exist; padded rows past query_lens are zeroed)
+      s_keys[q] = (last < rho0 && (p.qsl || p.prefix_pass)) ? -1 : k;
       w += (k + kBN - 1) / kBN;
       if (--t < 0 && q + 1 < q1) {
         t = nt - 1;
@@ -255,7 +261,7 @@ __device__ void find_piece(const LaunchParams &p, int nt, int *s_ctx, int *s_ql,
   }
   // total in fp32, summed in one fixed order (every workgroup gets the same
   // value; P only needs to be the same everywhere and about right)
-  float *s_redf = reinterpret_cast<float *>(s_red + 20);
+  float *s_redf = reinterpret_cast<float *>(s_red + 24);
   {
     const float ws = __shfl(wave_incl_scan_f((float)w), 63, 64);
     if (lane == 0) s_redf[wave] = ws;
@@ -270,9 +276,11 @@ __device__ void find_piece(const LaunchParams &p, int nt, int *s_ctx, int *s_ql,
     return 4 * (long long)len >= 3LL * P ? 0 : 2 * (long long)len >= P ? 1
            : 4 * (long long)len >= P ? 2 : 3;
   };
-  int cnt[5] = {0, 0, 0, 0, 0};  // widths of the four classes, split slots
+  // piece class of pair q: four by length, then the pairs with no row
+  auto pair_cls = [&](int q, int len) { return s_keys[q] < 0 ? 4 : cls(len); };
+  int cnt[6] = {0, 0, 0, 0, 0, 0};  // widths of the five classes, split slots
   for (int q = q0; q < q1; ++q) {
-    const int k = s_keys[q];
+    const int k = max(s_keys[q], 0);
     int len = k;
     if (k > P) {
       // the prefix launch cuts a tile into kPrefixPieces pieces at most
@@ -281,27 +289,28 @@ __device__ void find_piece(const LaunchParams &p, int nt, int *s_ctx, int *s_ql,
     }
     s_len[q] = len;
     const int n = npieces(k, len);
-    const int c = cls(len);
+    const int c = pair_cls(q, len);
     const int wdt = p.Hkv * n;
     cnt[0] += c == 0 ? wdt : 0;
     cnt[1] += c == 1 ? wdt : 0;
     cnt[2] += c == 2 ? wdt : 0;
     cnt[3] += c == 3 ? wdt : 0;
-    cnt[4] += n > 1 ? wdt : 0;
+    cnt[4] += c == 4 ? wdt : 0;
+    cnt[5] += n > 1 ? wdt : 0;
   }
   // exclusive prefix of each count over the block, and the class totals
-  int ex[5];
+  int ex[6];
 #pragma unroll
-  for (int v = 0; v < 5; ++v) {
+  for (int v = 0; v < 6; ++v) {
     const int inc = wave_incl_scan(cnt[v]);
     ex[v] = inc - cnt[v];
     if (lane == 63) s_red[v * 4 + wave] = inc;
   }
   __syncthreads();
-  int off[5];
+  int off[6];
   off[0] = 0;
 #pragma unroll
-  for (int v = 0; v < 5; ++v) {
+  for (int v = 0; v < 6; ++v) {
     int before = 0, tot = 0;
 #pragma unroll
     for (int w2 = 0; w2 < 4; ++w2) {
@@ -310,27 +319,27 @@ __device__ void find_piece(const LaunchParams &p, int nt, int *s_ctx, int *s_ql,
       tot += x;
     }
     ex[v] += before;
-    if (v < 4) off[v + 1] = off[v] + tot;
+    if (v < 5) off[v + 1] = off[v] + tot;
   }
   const int i = blockIdx.x;
   int c = 0;
-  while (c < 4 && i >= off[c + 1]) ++c;
-  if (c < 4) {
+  while (c < 5 && i >= off[c + 1]) ++c;
+  if (c < 5) {
     int cnt_c = 0, ex_c = 0;
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
+    for (int cc = 0; cc < 5; ++cc)
       if (cc == c) {
         cnt_c = cnt[cc];
         ex_c = ex[cc];
       }
     const int r = i - off[c];
     if (r >= ex_c && r < ex_c + cnt_c) {  // exactly one thread holds workgroup i
-      int acc = ex_c, sacc = ex[4];
+      int acc = ex_c, sacc = ex[5];
       for (int q = q0; q < q1; ++q) {
-        const int k = s_keys[q], len = s_len[q];
+        const int k = max(s_keys[q], 0), len = s_len[q];
         const int n = npieces(k, len);
         const int wdt = p.Hkv * n;
-        if (cls(len) == c) {
+        if (pair_cls(q, len) == c) {
           if (r < acc + wdt) {
             const int rr = r - acc;
             Piece x;
@@ -1068,7 +1077,18 @@ hipError_t launch_rb(const LaunchParams &p, hipStream_t stream) {
   // key split: one workgroup per piece, at most one per tile plus half the
   // slots (see find_piece)
   const bool split = p.ws_o != nullptr || (p.prefix_pass && p.num_splits > 1);
-  dim3 grid = split ? dim3((unsigned)((long long)tiles * p.Hkv * p.B + max(1, p.num_splits / 2)))
+  // pairs that can have rows: every (request, tile), or with packed rows of
+  // known total T at most floor(G T / bm) + (requests with rows): each such
+  // request adds at most one partial tile, and a request of the prefill
+  // route of a ragged call has two rows or more (the planner orders the
+  // pairs without rows last, so the workgroups cover the others)
+  long long pairs = (long long)tiles * p.B;
+  if (split && p.qsl && p.num_tokens > 0 && !p.prefix_pass) {
+    const long long T = p.num_tokens;
+    const long long with_rows = min((long long)p.B, p.route == 2 ? T / 2 : T);
+    pairs = min(pairs, (long long)G * T / bm + with_rows);
+  }
+  dim3 grid = split ? dim3((unsigned)(pairs * p.Hkv + max(1, p.num_splits / 2)))
                     : dim3((unsigned)((long long)tiles * p.Hkv), p.B);
   const long long pool = (long long)p.num_pages * p.Hkv * p.ps * D * 2;
   // the debug outputs select the instrumented build of the same staging mode

@@ -41,7 +41,7 @@ def test_header_and_library_exports_agree(L):
     assert exported == declared
     for name in declared:
         assert hasattr(L, name)
-    assert L.pa_abi_version() == 10
+    assert L.pa_abi_version() == 11
 
 
 def test_status_strings(L):
@@ -531,3 +531,21 @@ def test_shared_prefix_checks_before_launch(L):
     # an empty batch is a no-op
     z = h.args(batch=0)
     assert L.pa_decode_shared(ctypes.byref(z), ctypes.byref(g), ctypes.byref(ws), None) == 0
+
+
+def test_packed_row_total_is_validated_and_ragged_plan_accepts_it(L):
+    """num_tokens (packed rows' total, 0 = not given) must lie in [0, batch *
+    q_len]; a ragged call that gives it still plans both parts."""
+    h = HostBuffers()
+    ws = PaWorkspace()
+    n = ctypes.c_size_t(0)
+    route = ctypes.c_int32(-1)
+    ok = h.args(q_len=64, query_start_loc=h.p, num_tokens=2 * 64)
+    assert L.pa_attention_plan(ctypes.byref(ok), 0, ctypes.byref(ws), ctypes.byref(n),
+                               ctypes.byref(route)) == 0
+    assert route.value == _lib.ROUTE_RAGGED
+    for bad in (-1, 2 * 64 + 1):
+        a = h.args(q_len=64, query_start_loc=h.p, num_tokens=bad)
+        assert L.pa_attention_plan(ctypes.byref(a), 0, ctypes.byref(ws), ctypes.byref(n),
+                                   ctypes.byref(route)) == -1
+    assert _decode(L, h.args(num_tokens=-1)) == -1

@@ -25,16 +25,19 @@ def _constants():
 BN, MIN_PIECE = _constants()
 
 
-def plan(ctx, qlen, G, Hkv, causal, S):
+def plan(ctx, qlen, G, Hkv, causal, S, packed=False, L=None):
     """Pieces of one call: list of (workgroup order key, pair, head, piece,
-    k0, k1, split) and the grid size."""
-    nt = -(-(G * max(qlen)) // 128) if qlen else 0
-    keys = []
+    k0, k1, split) and the grid size.  With packed rows a tile with no row
+    to write is a pair of the fifth class (ordered after all others); L
+    bounds the rows of a request (default: the longest)."""
+    nt = -(-(G * (L or max(qlen))) // 128) if qlen else 0
+    keys, empty = [], []
     for b in range(len(ctx)):
         for tr in range(nt):
             t = nt - 1 - tr
             rho0, last = t * 128, min(t * 128 + 128, G * qlen[b]) - 1
             keys.append(0 if last < rho0 else (ctx[b] - qlen[b] + last // G + 1 if causal else ctx[b]))
+            empty.append(packed and last < rho0)
     work = np.float32(sum(-(-k // BN) for k in keys)) * np.float32(Hkv)
     target = np.float32(0.4) * np.float32(max(2, S))
     blocks = min(math.ceil(float(np.float32(work / target))), 1 << 24)
@@ -47,6 +50,8 @@ def plan(ctx, qlen, G, Hkv, causal, S):
             ln = (-(-k // n0) + BN - 1) // BN * BN
         n = -(-k // ln) if k > ln else 1
         cls = 0 if 4 * ln >= 3 * P else 1 if 2 * ln >= P else 2 if 4 * ln >= P else 3
+        if empty[q]:
+            cls = 4
         for g in range(Hkv):
             for sp in range(n):
                 pieces.append(((cls, q, g, sp), q, g, sp, sp * ln, min(k, sp * ln + ln), n > 1))
@@ -107,3 +112,37 @@ def test_c3_and_c5_like_plans_split_the_long_tiles():
     # one long prompt of 16384 rows: no tile is longer than P, nothing splits
     keys, P, pieces, slots, grid = plan([16384], [16384], 7, 4, True, 5 * 256)
     assert max(keys) <= P and slots == 0 and len(pieces) == len(keys) * 4
+
+
+def test_packed_grid_bound_covers_every_piece_with_rows():
+    """Packed rows of known total T: the grid of floor(G T / 128) + (requests
+    with rows) pairs per kv head plus half the slots (ragged prefill part:
+    requests of two rows or more) still reaches every piece that has rows,
+    because the pairs without rows are dispatched last."""
+    r = np.random.default_rng(7)
+    checked = 0
+    for _ in range(400):
+        B = int(r.integers(1, 64))
+        G = int(r.integers(1, 9))
+        Hkv = int(r.choice([1, 2, 4, 8]))
+        L = int(r.choice([2, 16, 100, 256, 600]))
+        ragged = r.random() < 0.5
+        # a ragged call's prefill part sees the one-row requests as rowless
+        qlen = [int(v) for v in r.integers(0, L + 1, B)]
+        if ragged:
+            qlen = [q if q >= 2 else 0 for q in qlen]
+        ctx = [q + int(r.integers(0, 5000)) for q in qlen]
+        S = int(r.choice([2, 10, 64, 5 * 256]))
+        nt = -(-(G * L) // 128)
+        if B * nt > 2048 or not any(qlen):
+            continue
+        keys, P, pieces, slots, grid = plan(ctx, qlen, G, Hkv, True, S, packed=True, L=L)
+        T = sum(qlen) + (sum(1 for q in qlen if q == 0) if ragged else 0)  # one-row requests
+        with_rows = min(B, T // 2 if ragged else T)
+        pairs = min(B * nt, G * T // 128 + with_rows)
+        bound = pairs * Hkv + max(1, S // 2)
+        order = sorted(pieces, key=lambda x: x[0])
+        with_work = [i for i, x in enumerate(order) if x[0][0] < 4]
+        assert not with_work or with_work[-1] < bound, (with_work[-1], bound)
+        checked += 1
+    assert checked > 200
