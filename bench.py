@@ -448,7 +448,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="C2,C2fp8,C3,C4,C5,long,small,append",
+    ap.add_argument("--only", default="C2,C2fp8,C3,C4,C5,shared,long,small,append",
                     help="sections to run (C2 is the headline; leaving it out leaves `value` "
                          "null, for profiling runs): C2, C2fp8, C3, C4, C5, shared (the "
                          "shared-prefix decode alone), long (= long4096, "
@@ -670,7 +670,7 @@ def main():
                     "timed alternately with pa_decode + pa_prefill back to back on one "
                     "stream (each flushed once)",
             **_stats(one), "two_calls_back_to_back": _stats(two)}
-    if "C5" in only or "shared" in only:
+    if "shared" in only:
         # shared-prefix decode (pa_decode_shared: one prefix launch reads each
         # group's shared pages once, then the decode launch walks the rest and
         # merges), against pa_decode on the same requests, interleaved call by
