@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define PA_ABI_VERSION 11
+#define PA_ABI_VERSION 12
 
 typedef enum {
   PA_OK = 0,
@@ -87,6 +87,21 @@ typedef enum { PA_MASK_NONE = 0, PA_MASK_CAUSAL = 1 } pa_mask;
  * element's value is its code's value times k_scale (keys) or v_scale
  * (values). */
 typedef enum { PA_KV_SAME = 0, PA_KV_FP8_E4M3 = 1 } pa_kv_dtype;
+
+/* Flags of the contract check (pa_args.debug_errors).  The kernels take the
+ * metadata on trust (tiny-llm "Week 3 Day 4", "What Must Hold, and What
+ * Breaks If It Doesn't": a page id outside the pool, or a context longer
+ * than its block-table row, reads memory that is not the request's). */
+typedef enum {
+  PA_DEBUG_BAD_PAGE = 1,    /* a block-table entry the call reads is outside [0, num_pages) */
+  PA_DEBUG_BAD_CONTEXT = 2, /* a context length < 0 or > max_pages * page_size */
+  PA_DEBUG_BAD_ROWS = 4,    /* query rows outside [0, q_len] (query_lens, or
+                               query_start_loc not 0 .. nondecreasing), or a
+                               causal request with keys but fewer keys than rows */
+  PA_DEBUG_BAD_GROUPS = 8   /* pa_decode_shared: groups or prefix lengths outside
+                               their contract, or a member's table that differs
+                               from its group's first member on the shared pages */
+} pa_debug_flag;
 
 typedef struct pa_args {
   const void *query;           /* [B, H_q, L, D] */
@@ -143,6 +158,20 @@ typedef struct pa_args {
    * read the row counts from query_start_loc.  Taken on trust: a value
    * below the true T leaves rows unwritten. */
   int32_t num_tokens;
+  /* Contract check (debug mode), or NULL.  When given: int32 [2] in device
+   * memory, which the caller zeroes.  Before its kernels, the call enqueues
+   * a check that reads only the metadata (every block-table entry j <
+   * ceil(min(context_lens[b], max_pages * page_size) / page_size) of every
+   * request, the context lengths, the query rows, and the groups of
+   * pa_decode_shared), ORs pa_debug_flag bits into debug_errors[0] and adds
+   * the number of out-of-pool entries to debug_errors[1].  Every kernel of
+   * the call reads debug_errors[0] first and, when it is nonzero, returns
+   * without reading K/V or writing any output, workspace or counter; the
+   * caller reads the word after synchronising.  Without it, a broken
+   * contract is undefined behaviour (a page id outside the pool reads
+   * outside the pool).  pa_append does not take it (its slots are checked
+   * in every call); pa_split_reduce reads it and checks nothing itself. */
+  int32_t *debug_errors;
 } pa_args;
 
 /* How pa_decode divides a call's keys among the waves of the GPU. */

@@ -24,6 +24,10 @@ PA_MASK_NONE = 0
 PA_MASK_CAUSAL = 1
 PA_KV_SAME = 0
 PA_KV_FP8_E4M3 = 1
+PA_DEBUG_BAD_PAGE = 1
+PA_DEBUG_BAD_CONTEXT = 2
+PA_DEBUG_BAD_ROWS = 4
+PA_DEBUG_BAD_GROUPS = 8
 
 EXPORTED = ("pa_decode_plan", "pa_decode", "pa_split_reduce", "pa_prefill_plan", "pa_prefill",
             "pa_attention_plan", "pa_attention", "pa_append", "pa_decode_noalloc",
@@ -58,6 +62,7 @@ class PaArgs(ctypes.Structure):
         ("v_scale", ctypes.c_float),
         ("query_start_loc", ctypes.c_void_p),
         ("num_tokens", ctypes.c_int32),
+        ("debug_errors", ctypes.c_void_p),
     ]
 
 
@@ -102,7 +107,7 @@ class PaPrefixGroups(ctypes.Structure):
     ]
 
 
-ABI_VERSION = 11  # PA_ABI_VERSION of the structs below
+ABI_VERSION = 12  # PA_ABI_VERSION of the structs below
 
 ROUTE_DECODE = 0
 ROUTE_PREFILL = 1

@@ -58,11 +58,14 @@ def make_args(query: torch.Tensor, key_pages: torch.Tensor, value_pages: torch.T
               debug_visits: Optional[torch.Tensor] = None,
               k_scale: Optional[float] = None, v_scale: Optional[float] = None,
               query_start_loc: Optional[torch.Tensor] = None,
-              max_query_len: Optional[int] = None) -> PaArgs:
+              max_query_len: Optional[int] = None,
+              debug_errors: Optional[torch.Tensor] = None) -> PaArgs:
     """Fill a pa_args from tensors (shapes as in include/pa.h).  uint8 pages
     are fp8 E4M3 codes (PA_KV_FP8_E4M3) and need k_scale and v_scale.  With
     query_start_loc ([B + 1] int32) the query and out are packed rows
-    [T, H_q, D] and max_query_len bounds every request's rows."""
+    [T, H_q, D] and max_query_len bounds every request's rows.
+    debug_errors ([2] int32, zeroed by the caller) turns on the contract
+    check of the calls made with these arguments."""
     if query_start_loc is not None:
         if query.dim() != 3 or max_query_len is None or query_lens is not None:
             raise ValueError("packed rows: query [T, H_q, D], max_query_len, no query_lens")
@@ -89,10 +92,11 @@ def make_args(query: torch.Tensor, key_pages: torch.Tensor, value_pages: torch.T
     _int32(query_lens, "query_lens")
     _int32(debug_trace, "debug_trace")
     _int32(debug_visits, "debug_visits")
+    _int32(debug_errors, "debug_errors")
     _same_gpu(query, key_pages=key_pages, value_pages=value_pages, block_table=block_table,
               context_lens=context_lens, out=out, query_lens=query_lens,
               debug_trace=debug_trace, debug_visits=debug_visits,
-              query_start_loc=query_start_loc)
+              query_start_loc=query_start_loc, debug_errors=debug_errors)
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be [batch, max_pages]")
     cap = block_table.shape[1] * ps
@@ -100,6 +104,7 @@ def make_args(query: torch.Tensor, key_pages: torch.Tensor, value_pages: torch.T
     _shape(query_lens, (B,), "query_lens")
     _shape(debug_trace, (B, cap, 2), "debug_trace")
     _shape(debug_visits, (B, Hkv, cap), "debug_visits")
+    _shape(debug_errors, (2,), "debug_errors")
     a = PaArgs()
     a.query = _ptr(query)
     a.key_pages = _ptr(key_pages)
@@ -120,9 +125,10 @@ def make_args(query: torch.Tensor, key_pages: torch.Tensor, value_pages: torch.T
     a.v_scale = float(v_scale) if fp8 else 1.0
     a.query_start_loc = _ptr(query_start_loc)
     a.num_tokens = int(query.shape[0]) if query_start_loc is not None else 0
+    a.debug_errors = _ptr(debug_errors)
     # the struct holds raw device addresses: keep the tensors alive with it
     a._tensors = (query, key_pages, value_pages, block_table, context_lens, out, query_lens,
-                  debug_trace, debug_visits, query_start_loc)
+                  debug_trace, debug_visits, query_start_loc, debug_errors)
     return a
 
 

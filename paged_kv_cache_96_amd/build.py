@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpa.so")
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["pa_decode.hip", "pa_reduce.hip", "pa_prefill.hip", "pa_append.hip", "pa_host.cpp"]
+SOURCES = ["pa_decode.hip", "pa_reduce.hip", "pa_prefill.hip", "pa_append.hip", "pa_validate.hip",
+           "pa_host.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -587,6 +587,7 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
 // output directly.
 template <typename T, typename KV, int D, int ROWS, bool DEBUG, bool UNIFORM>
 __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blocks) {
+  if (contract_broken(p)) return;
   constexpr int kWaves = 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (!p.balanced) {

@@ -62,7 +62,35 @@ pa_status check_pointers(const pa_args *a) {
   if (!aligned16(a->query) || !aligned16(a->key_pages) || !aligned16(a->value_pages) ||
       !aligned16(a->out))
     return PA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(a->debug_errors) & 3u) return PA_ERR_INVALID_ARG;
   return PA_OK;
+}
+
+// The contract check of a call, enqueued before its kernels when the caller
+// asks for it (pa_args.debug_errors); `groups` for pa_decode_shared.
+pa_status enqueue_check(const pa_args *a, const pa_prefix_groups *groups, hipStream_t stream) {
+  if (!a->debug_errors) return PA_OK;
+  pa::LaunchParams p;
+  memset(&p, 0, sizeof p);
+  p.bt = a->block_table;
+  p.cl = a->context_lens;
+  p.ql = a->query_lens;
+  p.qsl = a->query_start_loc;
+  p.B = a->batch;
+  p.L = a->q_len;
+  p.num_pages = a->num_pages;
+  p.ps = a->page_size;
+  p.max_pages = a->max_pages;
+  p.causal = a->mask == PA_MASK_CAUSAL;
+  int max_group = 0;
+  if (groups) {
+    p.grp_start = groups->group_start;
+    p.grp_pre = groups->prefix_lens;
+    p.num_groups = groups->num_groups;
+    max_group = groups->max_group_size;
+  }
+  return pa::launch_validate(p, a->debug_errors, max_group, stream) == hipSuccess ? PA_OK
+                                                                                 : PA_ERR_HIP;
 }
 
 // Bytes of one page element (the decode step depends on it).
@@ -157,6 +185,7 @@ pa::LaunchParams make_params(const pa_args *a, int32_t S, int32_t P, bool balanc
   p.ws_lse = (S > 1 && ws) ? ws->partial_lse : nullptr;
   p.dbg_trace = a->debug_trace;
   p.dbg_visits = a->debug_visits;
+  p.dbg_errors = a->debug_errors;
   p.counters = (balanced && ws) ? ws->counters : nullptr;
   p.B = a->batch;
   p.Hq = a->num_q_heads;
@@ -274,6 +303,7 @@ PA_EXPORT pa_status pa_decode(const pa_args *args, const pa_workspace *ws, void 
   if ((st = check_workspace(args, ws, &S, &P, &balanced)) != PA_OK) return st;
   if (!balanced && (st = check_decode_grid(args, S)) != PA_OK) return st;
   const pa::LaunchParams p = make_params(args, S, P, balanced, ws);
+  if ((st = enqueue_check(args, nullptr, (hipStream_t)stream)) != PA_OK) return st;
   return hip_status(pa::launch_decode(p, (pa::DType)args->dtype, (hipStream_t)stream));
 }
 
@@ -358,9 +388,11 @@ PA_EXPORT pa_status pa_prefill(const pa_args *args, const pa_workspace *ws, void
     const int64_t tiles = prefill_tiles(args);
     if (tiles * args->num_kv_heads > INT32_MAX) return PA_ERR_INVALID_ARG;
     if (tiles * args->num_kv_heads * args->batch + ws_slots(p) > INT32_MAX) return PA_ERR_INVALID_ARG;
+    if ((st = enqueue_check(args, nullptr, (hipStream_t)stream)) != PA_OK) return st;
     return hip_status(pa::launch_prefill_mfma(p, (hipStream_t)stream));
   }
   if ((st = check_decode_grid(args, 1)) != PA_OK) return st;
+  if ((st = enqueue_check(args, nullptr, (hipStream_t)stream)) != PA_OK) return st;
   return hip_status(pa::launch_decode(p, (pa::DType)args->dtype, (hipStream_t)stream));
 }
 
@@ -470,6 +502,15 @@ PA_EXPORT pa_status pa_attention(const pa_args *args, const pa_workspace *ws, vo
   if ((st = check_workspace(&d, &wd, &S, &P, &balanced)) != PA_OK) return st;
   pa::LaunchParams pd = make_params(&d, S, P, balanced, &wd);
   pd.route = 1;
+  if (args->dtype == PA_DTYPE_BF16) {
+    const int64_t tiles = prefill_tiles(args);
+    if (tiles * args->num_kv_heads * args->batch + ws->prefill_splits > INT32_MAX)
+      return PA_ERR_INVALID_ARG;
+  } else if ((st = check_decode_grid(args, 1)) != PA_OK) {
+    return st;
+  }
+  // one check of the whole call (its metadata is the decode part's too)
+  if ((st = enqueue_check(args, nullptr, (hipStream_t)stream)) != PA_OK) return st;
   hipError_t e = pa::launch_decode(pd, (pa::DType)args->dtype, (hipStream_t)stream);
   if (e != hipSuccess) return PA_ERR_HIP;
   // the prefill part, with the key split in the workspace's second region
@@ -620,7 +661,10 @@ PA_EXPORT pa_status pa_decode_shared(const pa_args *args, const pa_prefix_groups
     const int64_t tiles = prefill_tiles(&v);
     if (tiles * v.num_kv_heads * v.batch + pp.num_splits / 2 + 1 > INT32_MAX)
       return PA_ERR_INVALID_ARG;
+    if ((st = enqueue_check(args, groups, (hipStream_t)stream)) != PA_OK) return st;
     if (pa::launch_prefill_mfma(pp, (hipStream_t)stream) != hipSuccess) return PA_ERR_HIP;
+  } else if ((st = enqueue_check(args, groups, (hipStream_t)stream)) != PA_OK) {
+    return st;
   }
   // the decode launch: keys past each request's prefix, merged with its state
   pa::LaunchParams pd = make_params(args, S, P, balanced, &wd);

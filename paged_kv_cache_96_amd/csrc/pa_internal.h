@@ -24,6 +24,10 @@ struct LaunchParams {
                             // prefill key split: [S, 2, 256]
   int32_t *dbg_trace;       // nullptr unless instrumented
   int32_t *dbg_visits;      // nullptr unless instrumented
+  // Contract checks: nullptr, or the int32 [2] word the check kernel fills
+  // before the call's kernels, which then return at once when dbg_errors[0]
+  // is nonzero (debug_errors in pa.h).
+  const int32_t *dbg_errors;
   uint32_t *counters;       // balanced: per row block arrival counters (fused merge), or nullptr
   int32_t B, Hq, Hkv, L, D, num_pages, ps, max_pages;
   int32_t causal;
@@ -93,6 +97,20 @@ __device__ __forceinline__ bool routed_here(const LaunchParams &p, int Lb) {
   if (p.route == 0) return true;
   return (p.route == 1) == ragged_decode_request(p.Hq / p.Hkv, Lb);
 }
+
+// Whether the call's contract check found a violation: then a kernel of the
+// call reads no block-table entry and K/V element and writes nothing.  One
+// wave-uniform branch on a kernel argument when no check runs.
+__device__ __forceinline__ bool contract_broken(const LaunchParams &p) {
+  return p.dbg_errors != nullptr && p.dbg_errors[0] != 0;
+}
+
+// The contract check of a call (pa_validate.hip): checks on the device every
+// block-table entry the call's kernels would read, the context lengths, the
+// query rows and (max_group > 0) the shared-prefix groups, and ORs PA_DEBUG_*
+// flags into errors[0] and adds the count of bad entries to errors[1].
+hipError_t launch_validate(const LaunchParams &p, int32_t *errors, int max_group,
+                           hipStream_t stream);
 
 // Vector-ALU paged decode kernel (also the fp32 prefill path, with S == 1).
 hipError_t launch_decode(const LaunchParams &p, DType dt, hipStream_t stream);

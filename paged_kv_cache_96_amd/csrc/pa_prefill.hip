@@ -404,6 +404,7 @@ __global__ __launch_bounds__(256, (MODE == kStageDma || MODE == kStageDmaRun) ? 
                                   : RB == 1                                ? 2
                                                                            : 1) void
 prefill_kernel(LaunchParams p, int num_tiles) {
+  if (contract_broken(p)) return;
   constexpr bool UNIFORM = MODE != kStageLanes;
   constexpr bool DMA = MODE == kStageDma || MODE == kStageDmaRun;
   // keys per tile: DMA staging walks tiles of 32 keys (two 16 KiB buffers,

@@ -53,6 +53,7 @@ __device__ void balanced_waves(const LaunchParams &p, int b, int u, int units, l
 // depends on it).
 template <typename T, int D, int KVB>
 __global__ __launch_bounds__(256) void split_reduce_kernel(LaunchParams p, int total_rows) {
+  if (contract_broken(p)) return;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= total_rows) return;
   const int i = row % p.L;

@@ -41,7 +41,36 @@ def test_header_and_library_exports_agree(L):
     assert exported == declared
     for name in declared:
         assert hasattr(L, name)
-    assert L.pa_abi_version() == 11
+    assert L.pa_abi_version() == 12
+
+
+def _struct_fields(name):
+    """Field names of `typedef struct <name> { ... } <name>;` in the header,
+    in declaration order."""
+    with open(HEADER) as f:
+        text = f.read()
+    body = re.search(r"typedef struct %s \{(.*?)\} %s;" % (name, name), text, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = []
+    for decl in body.split(";"):
+        # "type a", "type *a" or "type a, b": the last word of each declarator
+        fields += [re.findall(r"(\w+)\s*$", d)[0] for d in decl.strip().split(",") if decl.strip()]
+    return fields
+
+
+def test_binding_structs_follow_the_header():
+    """The ctypes structures list the header's fields in the header's order
+    (the layout the library reads)."""
+    for name, cls in (("pa_args", PaArgs), ("pa_workspace", PaWorkspace),
+                      ("pa_append_args", PaAppendArgs), ("pa_prefix_groups", _lib.PaPrefixGroups)):
+        assert _struct_fields(name) == [f[0] for f in cls._fields_], name
+
+
+def test_misaligned_debug_errors_word_is_rejected(L):
+    h = HostBuffers()
+    a = h.args(debug_errors=h.p + 2)
+    assert _decode(L, a) == -1
+    assert L.pa_prefill(ctypes.byref(a), None, None) == -1
 
 
 def test_status_strings(L):
