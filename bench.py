@@ -588,7 +588,7 @@ def main():
         fl3 = prefill_flops(x3)
     if "C3" in only:
         d3 = run.to_device(x3)
-        r3 = run.time_prefill(d3, args.steps, args.warmup)
+        r3 = run.time_prefill(d3, args.steps, args.warmup, flush=True)
         ms = float(np.mean(r3["ms"]))
         log(f"[bench] prefill C3: {ms * 1e3:.1f} us, {fl3 / ms / 1e9:.1f} TFLOP/s")
         sections["prefill_C3"] = {
@@ -604,7 +604,7 @@ def main():
                            dtype="bf16", causal=True, extra_free_pages=16)
         dl = run.to_device(xl)
         fl = prefill_flops(xl)
-        rl = run.time_prefill(dl, max(5, args.steps // 6), 2)
+        rl = run.time_prefill(dl, max(5, args.steps // 6), 2, flush=True)
         ms = float(np.mean(rl["ms"]))
         tf = fl / (ms * 1e-3) / 1e12
         log(f"[bench] long prefill L={L}: {ms * 1e3:.1f} us, {tf:.1f} TFLOP/s")
