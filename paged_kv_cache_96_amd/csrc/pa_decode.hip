@@ -131,6 +131,29 @@ __device__ __forceinline__ void to_pairs(const Vec &v, uint32_t (&pr)[Elem<KV>::
   }
 }
 
+// Scan of v over the 256 threads of a workgroup in thread order with the
+// associative `op` (identity `id`): lane shifts within each wave, then the
+// four wave totals through s_w (one barrier).  Returns the inclusive value
+// and sets *excl to the exclusive one.  s_w may be reused once every thread
+// has passed a later barrier.
+template <typename Op>
+__device__ __forceinline__ long long block_scan(long long v, long long id, Op op, long long *s_w,
+                                                long long *excl) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long n = __shfl_up(v, off, 64);
+    if (lane >= off) v = op(v, n);
+  }
+  if (lane == 63) s_w[wv] = v;
+  __syncthreads();
+  long long pre = id;
+  for (int k = 0; k < wv; ++k) pre = op(pre, s_w[k]);
+  const long long up = __shfl_up(v, 1, 64);
+  *excl = op(pre, lane > 0 ? up : id);
+  return op(pre, v);
+}
+
 // Where a work item's state goes.  Partition schedule: slot `slot` of each
 // row.  Balanced schedule: piece slot `piece` of the row block, whose
 // `pieces` pieces occupy slots first, first + 1, ...; with arrival counters
@@ -616,7 +639,7 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
   __shared__ long long s_R[kBalancedMaxBatch + 1];  // first step of request b
   __shared__ int s_ctx[kBalancedMaxBatch];
   __shared__ int s_pre[kBalancedMaxBatch];  // shared-prefix keys of request b (0: none)
-  __shared__ long long s_sum[256];
+  __shared__ long long s_wsum[4];  // wave totals of the prologue's scans
   const int B = p.B;
   const int U = p.Hkv * row_blocks;
   const int tid = threadIdx.x;
@@ -641,15 +664,8 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
       const int b = tid * per + k;
       if (b < B) mark = max(mark, (long long)s_pre[b]);
     }
-    s_sum[tid] = mark;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele max scan
-      const long long a = tid >= off ? s_sum[tid - off] : -1;
-      __syncthreads();
-      s_sum[tid] = max(s_sum[tid], a);
-      __syncthreads();
-    }
-    long long grp = tid > 0 ? s_sum[tid - 1] : -1;
+    long long grp;  // exclusive max scan of the marks
+    block_scan(mark, -1ll, [](long long x, long long y) { return x > y ? x : y; }, s_wsum, &grp);
     for (int k = 0; k < per; ++k) {  // this thread's slice only: no other thread reads it
       const int b = tid * per + k;
       if (b < B) {
@@ -657,7 +673,7 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
         s_pre[b] = grp >= 0 && grp < p.num_groups ? group_prefix_keys(p, (int)grp) : 0;
       }
     }
-    __syncthreads();  // s_sum is reused below
+    __syncthreads();  // s_wsum is reused below
   } else {
     for (int b = tid; b < B; b += 256) s_pre[b] = 0;  // read after the scan's barriers
   }
@@ -674,15 +690,9 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
       loc += (long long)U * (n > 0 ? n + kUnitSetupSteps : 0);
     }
   }
-  s_sum[tid] = loc;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {  // inclusive Hillis-Steele scan
-    const long long a = tid >= off ? s_sum[tid - off] : 0;
-    __syncthreads();
-    s_sum[tid] += a;
-    __syncthreads();
-  }
-  long long run = tid > 0 ? s_sum[tid - 1] : 0;
+  long long run;  // exclusive sum scan of the step positions
+  const long long total =
+      block_scan(loc, 0ll, [](long long x, long long y) { return x + y; }, s_wsum, &run);
   for (int k = 0; k < per; ++k) {
     const int b = tid * per + k;
     if (b < B) {
@@ -692,7 +702,7 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
       run += (long long)U * (n > 0 ? n + kUnitSetupSteps : 0);
     }
   }
-  if (tid == 255) s_R[B] = s_sum[255];
+  if (tid == 255) s_R[B] = total;
   __syncthreads();
 
   // Values read from LDS are per-lane to the compiler; everything that shapes
