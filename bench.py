@@ -74,11 +74,16 @@ class Runner:
     def __init__(self, torch, api, flush: bool):
         self.torch = torch
         self.api = api
-        self.flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda") if flush else None
+        self.flush_buf = None
+        if flush:
+            self.flush_buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
 
     def flush(self):
+        """Evict the last-level cache by reading 1 GiB: the cache then holds
+        clean lines of another buffer, so the timed call pays its own cold
+        misses and no write-back of someone else's dirty lines."""
         if self.flush_buf is not None:
-            self.flush_buf.fill_(1.0)
+            self.flush_sink = self.flush_buf.sum()
 
     def to_device(self, x, pages=None):
         from tests._gpu import DeviceInputs
