@@ -223,7 +223,7 @@ typedef struct pa_workspace {
   /* Balanced only, optional: uint32 [num_counters] counters in device
    * memory (one arrival counter per row block).  The
    * caller zeroes them once before first use; every call leaves them zero.
-   * NULL: no run-time chunks, and pa_split_reduce merges. */
+   * NULL: pa_decode leaves the pieces' states and pa_split_reduce merges. */
   uint32_t *counters;
   /* Ragged route of pa_attention only: the key-split slots of its prefill
    * part (0 otherwise). */

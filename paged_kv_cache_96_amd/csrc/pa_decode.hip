@@ -751,7 +751,7 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
     }
   }
 
-  // The steps of virtual wave v (its static run, or dynamic chunk v - Wa),
+  // The steps of the run of wave v (positions [begin(v), begin(v + 1))),
   // piece by piece: a piece is the part of one row block inside the run.
   // Positions of the step order: each row block with keys is kUnitSetupSteps
   // setup positions (no work) followed by its n steps.
