@@ -176,7 +176,7 @@ struct ItemOut {
 template <typename T, typename KV, int D, int ROWS, bool DEBUG, bool UNIFORM>
 __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g, int rb, int t0,
                                             int tend, const ItemOut &io, bool split, int ctx,
-                                            int Lb, bool pre = false) {
+                                            int Lb, int q0, bool pre = false) {
   constexpr bool kFp8 = sizeof(KV) == 1;  // fp8 E4M3 pages (T: bf16)
   constexpr int kElems = Elem<KV>::kPerVec;  // page elements per 16-byte lane load
   constexpr int kLpt = D / kElems;      // lanes per key
@@ -213,7 +213,8 @@ __device__ __forceinline__ void decode_item(const LaunchParams &p, int b, int g,
     const int h = g * G + (rho - i * G);
     valid[r] = rho < G * p.L && i < Lb;
     hi[r] = valid[r] ? (p.causal ? ctx - Lb + i + 1 : ctx) : 0;
-    qrow[r] = query_row(p, b, h, i);
+    // packed rows: q0 is the request's first row (query_start_loc[b])
+    qrow[r] = p.qsl ? (size_t)(q0 + i) * p.Hq + h : query_row(p, b, h, i);
     kmax = max(kmax, hi[r]);
     if (valid[r]) kmin = min(kmin, hi[r]);
   }
@@ -647,7 +648,7 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
     const bool split = p.num_splits > 1;
     const ItemOut io{s, -1, 0, 0, 0};
     decode_item<T, KV, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, t0, split ? t0 + p.part_tokens : ctx,
-                                                io, split, ctx, Lb);
+                                                io, split, ctx, Lb, p.qsl ? p.qsl[b] : 0);
     return;
   }
 
@@ -656,6 +657,9 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
   __shared__ long long s_R[kBalancedMaxBatch + 1];  // first step of request b
   __shared__ int s_ctx[kBalancedMaxBatch];
   __shared__ int s_pre[kBalancedMaxBatch];  // shared-prefix keys of request b (0: none)
+  // query rows of request b and (packed rows) its first row: read once here
+  // rather than by every piece's setup, where they would add a round trip
+  __shared__ int s_rows[kBalancedMaxBatch], s_q0[kBalancedMaxBatch];
   __shared__ long long s_wsum[4];  // wave totals of the prologue's scans
   const int B = p.B;
   const int U = p.Hkv * row_blocks;
@@ -700,8 +704,11 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
     if (b < B) {
       // a request of another route counts as one without keys; a request of
       // a shared-prefix group walks only its keys past the prefix
-      const int ctx = routed_here(p, query_rows(p, b)) ? p.cl[b] : -1;
+      const int lb = query_rows(p, b);
+      const int ctx = routed_here(p, lb) ? p.cl[b] : -1;
       s_ctx[b] = ctx;
+      s_rows[b] = lb;
+      s_q0[b] = p.qsl ? p.qsl[b] : 0;
       const int keys = ctx - (shared ? s_pre[b] : 0);
       const int n = keys > 0 ? (keys + kStep - 1) / kStep : 0;
       loc += (long long)U * (n > 0 ? n + kUnitSetupSteps : 0);
@@ -783,13 +790,14 @@ __global__ __launch_bounds__(256) void decode_kernel(LaunchParams p, int row_blo
       const long long w1 = bs.wave_of(row0 + n - 1);
       const int g = u / row_blocks;
       const int rb = u - g * row_blocks;
-      const int Lb = query_rows(p, b);
+      const int Lb = uni(s_rows[b]);
       const long long unit = (long long)b * U + u;  // row block over the call
       const ItemOut io{0, unit + v, unit + w0, (int)(w1 - w0 + 1), unit};
       // a row block with a prefix state always goes through the merge
       decode_item<T, KV, D, ROWS, DEBUG, UNIFORM>(p, b, g, rb, pre + (int)(j0 * kStep),
                                                   pre + (int)(j1 * kStep), io,
-                                                  w1 > w0 || pre > 0, ctx, Lb, pre > 0);
+                                                  w1 > w0 || pre > 0, ctx, Lb, uni(s_q0[b]),
+                                                  pre > 0);
       t += j1 - j0;
     }
   };
