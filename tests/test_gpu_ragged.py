@@ -177,3 +177,31 @@ def test_packed_decode_all_requests_one_row(api):
     out, ex = _run(api, x, q, qsl, "attention")
     assert ex["route"] == api._lib.ROUTE_DECODE
     assert_parity(torch_of(_unpack(host_f64(out), qsl, x)), ref, "bf16", "packed L=1")
+
+
+def test_ragged_many_requests(api):
+    """More than 256 requests of packed rows in one call: the decode
+    prologue keeps each request's row count and first row from a scan over
+    several requests per thread; one-row requests go to the decode kernel,
+    the others to the prefill kernel."""
+    rng = np.random.default_rng(21)
+    B = 300
+    ql = [int(v) for v in rng.choice([1, 1, 1, 0, 2, 5, 12], size=B)]
+    ctx = [q + int(rng.integers(0, 180)) for q in ql]
+    x = make_random(22, B=B, H_q=8, H_kv=2, L=12, D=128, page_size=16, ctx=ctx, dtype="bf16",
+                    causal=True, query_lens=ql, extra_free_pages=5)
+    q, qsl = _pack(x)
+    ref = oracle.attention_of(x)
+    out, ex = _run(api, x, q, qsl, "attention")
+    assert ex["route"] == api._lib.ROUTE_RAGGED
+    assert_parity(torch_of(_unpack(host_f64(out), qsl, x)), ref, "bf16", "ragged B=300")
+    assert not ex["counters"].any()
+    # every request of one row or none: the decode entry point takes them all
+    ql1 = [min(v, 1) for v in ql]
+    x1 = make_random(23, B=B, H_q=8, H_kv=2, L=1, D=128, page_size=16,
+                     ctx=[max(c, v) for c, v in zip(ctx, ql1)], dtype="bf16", causal=True,
+                     query_lens=ql1, extra_free_pages=5)
+    q1, qsl1 = _pack(x1)
+    d_out, _ = _run(api, x1, q1, qsl1, "decode")
+    assert_parity(torch_of(_unpack(host_f64(d_out), qsl1, x1)), oracle.attention_of(x1), "bf16",
+                  "packed decode B=300")
