@@ -337,7 +337,7 @@ def sample_clocks(busy, samples=3, timeout_s=30.0, gap_s=1.0):
     """Clocks of the GPU while it runs a workload: keeps calling `busy()`
     (which enqueues work and synchronises) throughout, and reads the clocks
     with amd-smi `samples` times, each after `gap_s` more seconds of work
-    (the tool reports a snapshot that the driver refreshes; readings taken
+    (the tool reports a snapshot that the amdgpu kernel driver refreshes; readings taken
     back to back repeat it).  Each reading is the gfx clock of every XCD and
     the memory clock in MHz.  None where amd-smi is missing or fails, or
     under a profiler (the child would be profiled too)."""
@@ -471,7 +471,7 @@ def main():
                          "byte count that scales the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
@@ -524,8 +524,8 @@ def main():
         "roofline": None,
     }
     clocks = {"source": "amd-smi metric -c, three readings one second apart while the "
-                        "workload runs back to back (outside the timed regions); driver "
-                        "snapshots, context only"}
+                        "workload runs back to back (outside the timed regions); amdgpu "
+                        "driver snapshots, context only"}
 
     # ---- headline: C2 GQA decode
     x2 = W.make_c2()

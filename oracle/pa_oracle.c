@@ -188,7 +188,7 @@ static int row_limit(const or_args *a, int b, int i) {
   return ctx - qlen_of(a, b) + i + 1;
 }
 
-/* Shared driver: for every (b, g) gather densely, then for every query row of
+/* Shared loop: for every (b, g) gather densely, then for every query row of
  * the group compute either the full result (P <= 0) or S partition states. */
 static int run(const or_args *a, int P, int S, double *out, double *part_o,
                double *part_lse, int nthreads, int *threads_used) {
