@@ -74,3 +74,76 @@ def test_decode_and_prefill_replay_in_a_graph(api):
         assert torch.equal(_bits(out_p), _bits(ref_p)), f"prefill replay {rep}"
         assert not ws_d.counters.any().item() and not ws_p.counters.any().item()
     del g
+
+
+def test_ragged_shared_and_checked_calls_replay_in_a_graph(api):
+    """The ragged one call (two kernels), the shared-prefix decode (two
+    kernels) and a decode call with the contract check (a check kernel before
+    the decode) captured together; every replay equals the eager result."""
+    import torch
+    from tests._gpu import dev
+    from workloads import make_shared
+    xr = make_random(503, B=6, H_q=8, H_kv=2, L=24, D=128, page_size=16,
+                     ctx=[500, 64, 210, 30, 1200, 90], dtype="bf16", causal=True,
+                     query_lens=[1, 24, 1, 7, 1, 3], extra_free_pages=4)
+    lens = [int(v) for v in xr.rows_valid()]
+    rows = [xr.query[b, :, :n].transpose(1, 0, 2) for b, n in enumerate(lens)]
+    qsl = np.zeros(xr.B + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum(lens)
+    qr = dev(np.ascontiguousarray(np.concatenate(rows, axis=0)))
+    out_r = torch.empty_like(qr)
+    args_r = api.make_args(qr, dev(xr.key_pages), dev(xr.value_pages), dev(xr.block_table),
+                           dev(xr.context_lens), out_r, scale=xr.scale, mask="causal",
+                           query_start_loc=dev(qsl), max_query_len=xr.L)
+    ws_r = api.attention_workspace(api.pa_attention_plan(args_r), args_r, qr)
+
+    xs, gs = make_shared(504, H_q=8, H_kv=2, L=1, D=128, page_size=16, group_sizes=[4, 2, 1],
+                         prefix_pages=[6, 3, 0], suffix=(1, 120))
+    ds = DeviceInputs(xs)
+    out_s = torch.empty_like(ds.q)
+    args_s = api.make_args(ds.q, ds.kp, ds.vp, ds.bt, ds.cl, out_s, scale=xs.scale, mask=ds.mask)
+    groups = api.PrefixGroups(dev(gs.group_start), dev(gs.prefix_lens), gs.max_group_size)
+    ws_s = api.SharedWorkspace(api.pa_decode_shared_plan(args_s, groups), args_s, ds.q.device)
+
+    xc = make_random(505, B=8, H_q=32, H_kv=8, L=1, D=128, page_size=16, ctx=(16, 2000),
+                     dtype="bf16", causal=True)
+    dc = DeviceInputs(xc)
+    out_c = torch.empty_like(dc.q)
+    err = torch.zeros(2, dtype=torch.int32, device=dc.q.device)
+    args_c = api.make_args(dc.q, dc.kp, dc.vp, dc.bt, dc.cl, out_c, scale=xc.scale, mask=dc.mask,
+                           debug_errors=err)
+    ws_c = api.Workspace.for_plan(api.pa_decode_plan(args_c), dc.q, fused=True)
+
+    def calls():
+        api.pa_attention(args_r, ws_r)
+        api.pa_decode_shared(args_s, groups, ws_s)
+        api.pa_decode(args_c, ws_c)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    refs = [out_r.clone(), out_s.clone(), out_c.clone()]
+    assert_parity(refs[1], oracle.attention_of(xs), "bf16", "graph shared (eager)")
+    assert_parity(refs[2], oracle.attention_of(xc), "bf16", "graph checked decode (eager)")
+    assert err.tolist() == [0, 0]
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        calls()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in (out_r, out_s, out_c):
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"[graph] ragged/shared/checked replay {rep}", flush=True)
+        for name, o, r in zip(("ragged", "shared", "checked"), (out_r, out_s, out_c), refs):
+            assert torch.equal(_bits(o), _bits(r)), f"{name} replay {rep}"
+        for w in (ws_r, ws_s, ws_c):
+            assert not w.counters.any().item()
+        assert err.tolist() == [0, 0]
+    del g
