@@ -149,7 +149,8 @@ typedef struct pa_args {
    * query_start_loc[b] .. query_start_loc[b + 1] - 1 (0 = query_start_loc[0]
    * <= ... nondecreasing), and no padding rows exist or are written.
    * q_len is then an upper bound on every request's row count (it sizes
-   * tiles and plans), and query_lens must be NULL. */
+   * tiles and plans), and query_lens must be NULL.  A call with no row at
+   * all (T = 0) passes NULL query and out and does nothing. */
   const int32_t *query_start_loc;
   /* Packed rows only: T = query_start_loc[batch] (the rows of query and
    * out), or 0 if the caller does not give it; 0 <= num_tokens <= batch *

@@ -55,6 +55,12 @@ pa_status check_sizes(const pa_args *a) {
 
 bool kv_fp8(const pa_args *a) { return a->kv_dtype == PA_KV_FP8_E4M3; }
 
+// A call with nothing to compute: no requests, or packed rows with no row at
+// all (T = 0), which the caller states by passing NULL query and out.
+bool nothing_to_do(const pa_args *a) {
+  return a->batch == 0 || (a->query_start_loc && !a->query && !a->out);
+}
+
 pa_status check_pointers(const pa_args *a) {
   if (!a->query || !a->key_pages || !a->value_pages || !a->block_table || !a->context_lens ||
       !a->out)
@@ -296,7 +302,7 @@ PA_EXPORT pa_status pa_decode(const pa_args *args, const pa_workspace *ws, void 
   pa_status st = check_sizes(args);
   if (st != PA_OK) return st;
   if (args->q_len > 8) return PA_ERR_INVALID_ARG;
-  if (args->batch == 0) return PA_OK;
+  if (nothing_to_do(args)) return PA_OK;
   if ((st = check_pointers(args)) != PA_OK) return st;
   int32_t S, P;
   bool balanced;
@@ -311,7 +317,7 @@ PA_EXPORT pa_status pa_split_reduce(const pa_args *args, const pa_workspace *ws,
   pa_status st = check_sizes(args);
   if (st != PA_OK) return st;
   if (args->q_len > 8) return PA_ERR_INVALID_ARG;
-  if (args->batch == 0) return PA_OK;
+  if (nothing_to_do(args)) return PA_OK;
   if ((st = check_pointers(args)) != PA_OK) return st;
   int32_t S, P;
   bool balanced;
@@ -365,7 +371,7 @@ PA_EXPORT pa_status pa_prefill(const pa_args *args, const pa_workspace *ws, void
   pa_status st = check_sizes(args);
   if (st != PA_OK) return st;
   if (kv_fp8(args)) return PA_ERR_UNSUPPORTED;  // fp8 pages: decode path only
-  if (args->batch == 0) return PA_OK;
+  if (nothing_to_do(args)) return PA_OK;
   if ((st = check_pointers(args)) != PA_OK) return st;
   const int32_t cap = args->max_pages * args->page_size;
   pa::LaunchParams p = make_params(args, 1, cap, false, nullptr);
@@ -475,7 +481,7 @@ PA_EXPORT pa_status pa_attention(const pa_args *args, const pa_workspace *ws, vo
   }
   // ragged: the decode part (requests of one row, merge fused) and the
   // prefill part (the others), one launch each, on `stream`
-  if (args->batch == 0) return PA_OK;
+  if (nothing_to_do(args)) return PA_OK;
   if ((st = check_pointers(args)) != PA_OK) return st;
   pa_workspace dec, pre;
   size_t db = 0, pb = 0;
@@ -614,7 +620,7 @@ PA_EXPORT pa_status pa_decode_shared(const pa_args *args, const pa_prefix_groups
   if (st != PA_OK) return st;
   if (args->q_len > 8) return PA_ERR_INVALID_ARG;
   if ((st = check_groups(args, groups)) != PA_OK) return st;
-  if (args->batch == 0) return PA_OK;
+  if (nothing_to_do(args)) return PA_OK;
   if ((st = check_pointers(args)) != PA_OK) return st;
   const size_t R = (size_t)decode_block_rows(args);
   const int64_t dec_counters = (int64_t)args->batch * decode_units(args);
@@ -775,7 +781,7 @@ PA_EXPORT pa_status pa_decode_noalloc(const pa_args *args, void *stream) {
   pa_status st = check_sizes(args);
   if (st != PA_OK) return st;
   if (args->q_len > 8) return PA_ERR_INVALID_ARG;
-  if (args->batch == 0) return PA_OK;
+  if (nothing_to_do(args)) return PA_OK;
   if ((st = check_pointers(args)) != PA_OK) return st;
   pa_workspace ws;
   memset(&ws, 0, sizeof ws);

@@ -170,6 +170,22 @@ def test_batch_zero_is_a_no_op(L):
     assert L.pa_prefill(ctypes.byref(a), None, None) == 0
 
 
+def test_packed_call_without_rows_is_a_no_op(L):
+    """Packed rows with T = 0 (NULL query and out): every entry point returns
+    ok and launches nothing (the host buffers stand in for device memory and
+    are never read); a NULL query with a non-NULL out stays an error."""
+    h = HostBuffers()
+    a = h.args(q_len=16, query=None, out=None, query_start_loc=h.p)
+    assert _decode(L, a) == -1  # q_len 16 is past the decode path whatever the rows
+    assert L.pa_prefill(ctypes.byref(a), None, None) == 0
+    assert L.pa_attention(ctypes.byref(a), None, None) == 0
+    d = h.args(q_len=1, query=None, out=None, query_start_loc=h.p)
+    assert _decode(L, d) == 0
+    assert L.pa_decode_noalloc(ctypes.byref(d), None) == 0
+    half = h.args(q_len=1, query=None, query_start_loc=h.p)
+    assert _decode(L, half) == -1
+
+
 def test_prefill_accepts_long_queries_but_checks_sizes(L):
     h = HostBuffers()
     assert L.pa_prefill(ctypes.byref(h.args(q_len=0)), None, None) == -1

@@ -205,3 +205,17 @@ def test_ragged_many_requests(api):
     d_out, _ = _run(api, x1, q1, qsl1, "decode")
     assert_parity(torch_of(_unpack(host_f64(d_out), qsl1, x1)), oracle.attention_of(x1), "bf16",
                   "packed decode B=300")
+
+
+def test_packed_batch_without_rows(api):
+    """Requests with context but no query row at all (T = 0): the call does
+    nothing and succeeds, on the ragged route and on the decode route."""
+    import torch
+    for L in (130, 1):
+        x = make_random(24, B=2, H_q=12, H_kv=2, L=L, D=128, page_size=128, ctx=[161, 623],
+                        dtype="bf16", causal=True, query_lens=[0, 0], extra_free_pages=2)
+        q, qsl = _pack(x)
+        assert q.shape[0] == 0
+        out, ex = _run(api, x, q, qsl, "attention")
+        assert out.numel() == 0
+        assert ex["route"] == (api._lib.ROUTE_RAGGED if L > 1 else api._lib.ROUTE_DECODE)
