@@ -137,10 +137,9 @@ typedef struct pa_args {
   int32_t *debug_trace;
   int32_t *debug_visits;
   /* Page element type (pa_kv_dtype; 0 = PA_KV_SAME).  PA_KV_FP8_E4M3 needs
-   * dtype PA_DTYPE_BF16 (query and out) and head_dim 128, and is served by
-   * the decode path only (pa_decode, pa_split_reduce, pa_decode_noalloc,
-   * and pa_attention on its decode route); pa_prefill returns
-   * PA_ERR_UNSUPPORTED for it. */
+   * dtype PA_DTYPE_BF16 (query and out) and head_dim 128.  pa_decode,
+   * pa_split_reduce, pa_decode_noalloc, pa_prefill and pa_attention (every
+   * route) take it; pa_decode_shared returns PA_ERR_UNSUPPORTED for it. */
   int32_t kv_dtype;
   float k_scale;               /* fp8 pages: finite and > 0 (ignored otherwise) */
   float v_scale;               /* fp8 pages: finite and > 0 (ignored otherwise) */

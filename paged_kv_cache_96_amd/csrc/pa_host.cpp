@@ -347,7 +347,6 @@ PA_EXPORT pa_status pa_prefill_plan(const pa_args *args, int32_t num_cus, pa_wor
   pa_status st = check_sizes(args);
   if (st != PA_OK) return st;
   if (!plan) return PA_ERR_INVALID_ARG;
-  if (kv_fp8(args)) return PA_ERR_UNSUPPORTED;  // fp8 pages: decode path only
   plan->schedule = PA_SCHEDULE_KEY_SPLIT;
   plan->partition_tokens = 0;
   plan->num_splits = 0;
@@ -370,7 +369,6 @@ PA_EXPORT pa_status pa_prefill_plan(const pa_args *args, int32_t num_cus, pa_wor
 PA_EXPORT pa_status pa_prefill(const pa_args *args, const pa_workspace *ws, void *stream) {
   pa_status st = check_sizes(args);
   if (st != PA_OK) return st;
-  if (kv_fp8(args)) return PA_ERR_UNSUPPORTED;  // fp8 pages: decode path only
   if (nothing_to_do(args)) return PA_OK;
   if ((st = check_pointers(args)) != PA_OK) return st;
   const int32_t cap = args->max_pages * args->page_size;
@@ -430,7 +428,6 @@ size_t round16(size_t x) { return (x + 15) / 16 * 16; }
 // Plans of both parts of a ragged call.
 pa_status ragged_plans(const pa_args *a, int32_t num_cus, pa_workspace *dec, pa_workspace *pre,
                        size_t *dec_bytes, size_t *pre_bytes) {
-  if (kv_fp8(a)) return PA_ERR_UNSUPPORTED;  // fp8 pages: decode path only
   const pa_args d = ragged_decode_args(a);
   memset(dec, 0, sizeof *dec);
   memset(pre, 0, sizeof *pre);

@@ -108,6 +108,21 @@ struct Tile {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Eight E4M3 codes (two words, element 0 in the low byte) as eight bf16
+// values: every E4M3 value is a bf16 value, and the hardware converter of
+// two codes to a bf16 pair (scale 1) gives it exactly.
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  auto lo = [](uint32_t w) {  // bytes 0, 1
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  };
+  auto hi = [](uint32_t w) {  // bytes 2, 3
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+  };
+  return make_uint4(lo(w0), hi(w0), lo(w1), hi(w1));
+}
+
 
 // max(a, b, c) in one instruction, without the operand quieting that
 // fmaxf adds (the scores are finite or -inf).
@@ -399,7 +414,7 @@ __device__ __forceinline__ int dma_pos(int r, int c) {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <int D, bool DEBUG, int MODE, int RB>
+template <int D, bool DEBUG, int MODE, int RB, bool FP8>
 __global__ __launch_bounds__(256, (MODE == kStageDma || MODE == kStageDmaRun) ? 3
                                   : RB == 1                                ? 2
                                                                            : 1) void
@@ -407,6 +422,10 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   if (contract_broken(p)) return;
   constexpr bool UNIFORM = MODE != kStageLanes;
   constexpr bool DMA = MODE == kStageDma || MODE == kStageDmaRun;
+  // fp8 (E4M3) pages: register staging only, each code widened to bf16 on
+  // its way into LDS (the direct-to-LDS loads cannot convert)
+  static_assert(!FP8 || (D == 128 && !DMA), "fp8 pages: D = 128, register staging");
+  constexpr int EB = FP8 ? 1 : 2;  // bytes of a page element
   // keys per tile: DMA staging walks tiles of 32 keys (two 16 KiB buffers,
   // three workgroups per compute unit); the split plan's 64-key grid is a
   // multiple of it
@@ -530,6 +549,8 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   // ---- staging of one K/V tile: thread -> (key kr*KPR + tid / CH, chunk tid % CH)
   const uint16_t *kp = reinterpret_cast<const uint16_t *>(p.kp);
   const uint16_t *vp = reinterpret_cast<const uint16_t *>(p.vp);
+  const uint8_t *kp8 = reinterpret_cast<const uint8_t *>(p.kp);  // fp8 pages
+  const uint8_t *vp8 = reinterpret_cast<const uint8_t *>(p.vp);
   // the prefix launch reads the table of the group's first member
   const int32_t *bt = p.bt + (size_t)(p.prefix_pass ? p.grp_start[b] : b) * p.max_pages;
   const int chunk = tid % TL::kChunks;
@@ -543,7 +564,7 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   typedef const __attribute__((address_space(4))) int32_t *const_i32_ptr;
   const const_i32_ptr btc = (const_i32_ptr)bt;
   // page-uniform rounds: per-thread byte offset within a 16-key run of a page
-  const int run_off = (key_in_round * D + chunk * 8) * 2;
+  const int run_off = (key_in_round * D + chunk * 8) * EB;
   // Every load is issued unconditionally: a run past the workgroup's last
   // key gets a resource of size 0 (its loads return zeros without touching
   // memory), so no register is ever written conditionally and the compiler's
@@ -551,8 +572,8 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   // Runs are loaded strictly in key order, so the run's logical page and
   // slot are advanced incrementally (scalar registers): a new block-table
   // entry is read only when a run starts a page.
-  const long long page_bytes = (long long)p.Hkv * p.ps * D * 2;
-  const long long head_bytes = (long long)g * p.ps * D * 2;
+  const long long page_bytes = (long long)p.Hkv * p.ps * D * EB;
+  const long long head_bytes = (long long)g * p.ps * D * EB;
   const char *kp_bytes = reinterpret_cast<const char *>(p.kp);
   const char *vp_bytes = reinterpret_cast<const char *>(p.vp);
   int run_j0 = 0, run_lp = 0, run_slot = 0, run_page = 0;
@@ -564,10 +585,10 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   // arithmetic.  The visit is counted under the kv head the offset points at.
   auto record = [&](int j, long long byte) {
     if constexpr (DEBUG) {
-      const long long head_row = (long long)p.ps * D * 2;  // bytes of one page of one head
-      if (counts && pass == 0 && j < kend_wg && byte % (D * 2) == 0) {
-        const long long ph = byte / head_row;              // page * H_kv + head
-        const int slot = (int)((byte - ph * head_row) / (D * 2));
+      const long long head_row = (long long)p.ps * D * EB;  // bytes of one page of one head
+      if (counts && pass == 0 && j < kend_wg && byte % (D * EB) == 0) {
+        const long long ph = byte / head_row;               // page * H_kv + head
+        const int slot = (int)((byte - ph * head_row) / (D * EB));
         const int page = (int)(ph / p.Hkv);
         const int head = (int)(ph - (long long)page * p.Hkv);
         const size_t cap = (size_t)p.max_pages * p.ps;
@@ -658,13 +679,20 @@ prefill_kernel(LaunchParams p, int num_tiles) {
       const bool live = run_j0 < kend_wg;                 // wave-uniform
       if (run_slot == 0) run_page = live ? btc[min(run_lp, p.max_pages - 1)] : 0;
       if constexpr (MODE == kStagePool) {
-        const int soff = run_page * (int)page_bytes + (int)head_bytes + run_slot * (D * 2);
+        const int soff = run_page * (int)page_bytes + (int)head_bytes + run_slot * (D * EB);
         const int voff = run_j0 + key_in_round < kend_wg ? run_off : (int)0x80000000u;
-        const u32x4_t kv = __builtin_amdgcn_raw_buffer_load_b128(pool_k, voff, soff, 0);
-        const u32x4_t vv = __builtin_amdgcn_raw_buffer_load_b128(pool_v, voff, soff, 0);
+        if constexpr (FP8) {
+          const u32x2_t kv = __builtin_amdgcn_raw_buffer_load_b64(pool_k, voff, soff, 0);
+          const u32x2_t vv = __builtin_amdgcn_raw_buffer_load_b64(pool_v, voff, soff, 0);
+          st.k[r] = fp8x8_to_bf16x8(kv[0], kv[1]);
+          st.v[r] = fp8x8_to_bf16x8(vv[0], vv[1]);
+        } else {
+          const u32x4_t kv = __builtin_amdgcn_raw_buffer_load_b128(pool_k, voff, soff, 0);
+          const u32x4_t vv = __builtin_amdgcn_raw_buffer_load_b128(pool_v, voff, soff, 0);
+          st.k[r] = make_uint4(kv[0], kv[1], kv[2], kv[3]);
+          st.v[r] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+        }
         if (live && voff >= 0) record(run_j0 + key_in_round, (long long)soff + voff);
-        st.k[r] = make_uint4(kv[0], kv[1], kv[2], kv[3]);
-        st.v[r] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
         run_j0 += TL::kKeysPerRound;
         run_slot += TL::kKeysPerRound;
         if (run_slot == p.ps) {
@@ -673,19 +701,26 @@ prefill_kernel(LaunchParams p, int num_tiles) {
         }
         continue;
       }
-      const long long off = (long long)run_page * page_bytes + head_bytes + run_slot * (D * 2);
-      const int nrec = live ? (p.ps - run_slot) * D * 2 : 0;
+      const long long off = (long long)run_page * page_bytes + head_bytes + run_slot * (D * EB);
+      const int nrec = live ? (p.ps - run_slot) * D * EB : 0;
       const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<char *>(kp_bytes + off), (short)0, nrec, kBufferRsrcWord3);
       const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<char *>(vp_bytes + off), (short)0, nrec, kBufferRsrcWord3);
       // keys at or past kend_wg read as zeros (offset past the resource)
       const int voff = run_j0 + key_in_round < kend_wg ? run_off : 0x40000000;
-      const u32x4_t kv = __builtin_amdgcn_raw_buffer_load_b128(rk, voff, 0, 0);
-      const u32x4_t vv = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0);
+      if constexpr (FP8) {
+        const u32x2_t kv = __builtin_amdgcn_raw_buffer_load_b64(rk, voff, 0, 0);
+        const u32x2_t vv = __builtin_amdgcn_raw_buffer_load_b64(rv, voff, 0, 0);
+        st.k[r] = fp8x8_to_bf16x8(kv[0], kv[1]);
+        st.v[r] = fp8x8_to_bf16x8(vv[0], vv[1]);
+      } else {
+        const u32x4_t kv = __builtin_amdgcn_raw_buffer_load_b128(rk, voff, 0, 0);
+        const u32x4_t vv = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0);
+        st.k[r] = make_uint4(kv[0], kv[1], kv[2], kv[3]);
+        st.v[r] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
+      }
       if (live && voff != 0x40000000) record(run_j0 + key_in_round, off + voff);
-      st.k[r] = make_uint4(kv[0], kv[1], kv[2], kv[3]);
-      st.v[r] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
       run_j0 += TL::kKeysPerRound;
       run_slot += TL::kKeysPerRound;
       if (run_slot == p.ps) {
@@ -707,9 +742,16 @@ prefill_kernel(LaunchParams p, int num_tiles) {
         const int page = bt[lp];
         const int slot = j - lp * p.ps;
         const size_t off = (((size_t)page * p.Hkv + g) * p.ps + slot) * D + chunk * 8;
-        st.k[r] = *reinterpret_cast<const uint4 *>(kp + off);
-        st.v[r] = *reinterpret_cast<const uint4 *>(vp + off);
-        record(j, (long long)off * 2);
+        if constexpr (FP8) {
+          const uint2 kw = *reinterpret_cast<const uint2 *>(kp8 + off);
+          const uint2 vw = *reinterpret_cast<const uint2 *>(vp8 + off);
+          st.k[r] = fp8x8_to_bf16x8(kw.x, kw.y);
+          st.v[r] = fp8x8_to_bf16x8(vw.x, vw.y);
+        } else {
+          st.k[r] = *reinterpret_cast<const uint4 *>(kp + off);
+          st.v[r] = *reinterpret_cast<const uint4 *>(vp + off);
+        }
+        record(j, (long long)off * EB);
       } else {
         st.k[r] = make_uint4(0, 0, 0, 0);  // never loaded: zeros keep masked math finite
         st.v[r] = make_uint4(0, 0, 0, 0);
@@ -735,7 +777,8 @@ prefill_kernel(LaunchParams p, int num_tiles) {
     m_ref[rb] = kMinM;
     m_seen[rb] = kMinM;
   }
-  const float c = p.scale_log2;
+  // score multiplier in base-2 units (fp8 pages: times k_scale)
+  const float c = FP8 ? p.scale_log2 * p.k_scale : p.scale_log2;
 
   // Register staging: with one row block per wave, two sets (set A holds
   // even tiles, set B odd ones) so that loads run two tiles ahead; with two
@@ -1029,7 +1072,7 @@ prefill_kernel(LaunchParams p, int num_tiles) {
       bool exists;
       const size_t orow = launch_row(p, b, qh[rb], qi[rb], exists);
       const size_t ps_row = orow * kPrefixPieces + sp;
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      const float inv = l_tot > 0.f ? (FP8 ? p.v_scale : 1.f) / l_tot : 0.f;
       float *po = p.pre_o + ps_row * D;
 #pragma unroll
       for (int mb = 0; mb < TL::kMBlocks; ++mb)
@@ -1054,7 +1097,8 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   for (int rb = 0; rb < RB; ++rb) {
     const float l_tot = pair_sum(l_run[rb]);  // uniform: every lane of the wave takes part
     if (rho[rb] < rows_all) {
-      const float inv = (row_valid[rb] && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+      // fp8 pages: the values carry v_scale, applied once here
+      const float inv = (row_valid[rb] && l_tot > 0.f) ? (FP8 ? p.v_scale : 1.f) / l_tot : 0.f;
       uint16_t *op = reinterpret_cast<uint16_t *>(p.out) + query_row(p, b, qh[rb], qi[rb]) * D;
 #pragma unroll
       for (int mb = 0; mb < TL::kMBlocks; ++mb)
@@ -1091,34 +1135,50 @@ hipError_t launch_rb(const LaunchParams &p, hipStream_t stream) {
   }
   dim3 grid = split ? dim3((unsigned)(pairs * p.Hkv + max(1, p.num_splits / 2)))
                     : dim3((unsigned)((long long)tiles * p.Hkv), p.B);
-  const long long pool = (long long)p.num_pages * p.Hkv * p.ps * D * 2;
   // the debug outputs select the instrumented build of the same staging mode
   const bool debug = p.dbg_trace || p.dbg_visits;
-  auto go = [&](auto dbg) {
+  auto go = [&](auto dbg, auto fp8) {
     constexpr bool DBG = decltype(dbg)::value;
+    constexpr bool F8 = decltype(fp8)::value;
+    // direct-to-LDS staging: bf16 pages with D = 128 (fp8 codes are widened
+    // in registers)
+    constexpr bool kDma = D == 128 && RB == 1 && !F8;
+    const long long pool = (long long)p.num_pages * p.Hkv * p.ps * D * (F8 ? 1 : 2);
     if (p.ps % Tile<D>::kKeysPerRound != 0) {  // runs would straddle pages
-      hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageLanes, RB>), grid, dim3(256), 0, stream, p,
-                         tiles);
+      hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageLanes, RB, F8>), grid, dim3(256), 0,
+                         stream, p, tiles);
     } else if (pool < (1ll << 31)) {
-      if constexpr (D == 128 && RB == 1)
-        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageDma, RB>), grid, dim3(256), 0, stream, p,
-                           tiles);
+      if constexpr (kDma)
+        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageDma, RB, F8>), grid, dim3(256), 0,
+                           stream, p, tiles);
       else
-        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStagePool, RB>), grid, dim3(256), 0, stream,
-                           p, tiles);
+        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStagePool, RB, F8>), grid, dim3(256), 0,
+                           stream, p, tiles);
     } else {
-      if constexpr (D == 128 && RB == 1)
-        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageDmaRun, RB>), grid, dim3(256), 0, stream,
-                           p, tiles);
+      if constexpr (kDma)
+        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageDmaRun, RB, F8>), grid, dim3(256), 0,
+                           stream, p, tiles);
       else
-        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageRun, RB>), grid, dim3(256), 0, stream, p,
-                           tiles);
+        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageRun, RB, F8>), grid, dim3(256), 0,
+                           stream, p, tiles);
     }
   };
-  if (debug)
-    go(std::integral_constant<bool, true>());
-  else
-    go(std::integral_constant<bool, false>());
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+  if (p.kv_fp8) {
+    if constexpr (D == 128) {  // fp8 pages come with D = 128 only
+      if (debug)
+        go(yes(), yes());
+      else
+        go(no(), yes());
+    } else {
+      return hipErrorInvalidValue;
+    }
+  } else if (debug) {
+    go(yes(), no());
+  } else {
+    go(no(), no());
+  }
   return hipGetLastError();
 }
 

@@ -98,7 +98,8 @@ def run_prefill(api, d: DeviceInputs, *, trace=False, split=True, num_cus=0):
         dbg_t = torch.full((x.B, cap, 2), -1, dtype=torch.int32, device=d.q.device)
         dbg_v = torch.zeros((x.B, x.H_kv, cap), dtype=torch.int32, device=d.q.device)
     args = api.make_args(d.q, d.kp, d.vp, d.bt, d.cl, out, scale=x.scale, mask=d.mask,
-                         query_lens=d.ql, debug_trace=dbg_t, debug_visits=dbg_v)
+                         query_lens=d.ql, debug_trace=dbg_t, debug_visits=dbg_v,
+                         **kv_scales(x))
     ws = api.PrefillWorkspace.for_args(args, d.q.device, num_cus=num_cus) if split else None
     api.pa_prefill(args, ws)
     torch.cuda.synchronize()

@@ -422,23 +422,32 @@ def test_fp8_pages_validation(L, kw, code):
     assert _decode(L, h.args(**kw)) == code
 
 
-def test_fp8_pages_are_decode_only(L):
-    """fp8 pages go through the decode path (and the router's decode route);
-    the prefill path refuses them before any launch."""
+def test_fp8_pages_plans(L):
+    """fp8 pages are planned like bf16 pages by the decode path (with 32-key
+    steps), the prefill path (same key-split slots) and the router (every
+    route); the shared-prefix decode refuses them before any launch."""
     h = HostBuffers()
+    ws, wb = PaWorkspace(), PaWorkspace()
+    n, nb = ctypes.c_size_t(0), ctypes.c_size_t(0)
     a = h.args(kv_dtype=1, k_scale=0.5, v_scale=0.5, q_len=64)
-    assert L.pa_prefill(ctypes.byref(a), None, None) == -2
-    ws = PaWorkspace()
-    n = ctypes.c_size_t(0)
-    assert L.pa_prefill_plan(ctypes.byref(a), 0, ctypes.byref(ws), ctypes.byref(n)) == -2
-    assert L.pa_attention(ctypes.byref(a), None, None) == -2
+    b = h.args(q_len=64)
+    assert L.pa_prefill_plan(ctypes.byref(a), 0, ctypes.byref(ws), ctypes.byref(n)) == 0
+    assert L.pa_prefill_plan(ctypes.byref(b), 0, ctypes.byref(wb), ctypes.byref(nb)) == 0
+    assert (ws.schedule, ws.num_splits, ws.num_counters, n.value) == \
+        (wb.schedule, wb.num_splits, wb.num_counters, nb.value)
+    route = ctypes.c_int32(-1)
+    assert L.pa_attention_plan(ctypes.byref(a), 0, ctypes.byref(ws), ctypes.byref(n),
+                               ctypes.byref(route)) == 0
+    assert route.value == _lib.ROUTE_PREFILL
+    g = _groups(h)
+    assert L.pa_decode_shared_plan(ctypes.byref(h.args(kv_dtype=1, k_scale=0.5, v_scale=0.5)),
+                                   ctypes.byref(g), 0, ctypes.byref(ws), ctypes.byref(n)) == -2
     a.q_len = 1
     assert L.pa_decode_plan(ctypes.byref(a), 0, ctypes.byref(ws), ctypes.byref(n)) == 0
     assert ws.schedule == SCHEDULE_BALANCED
     # a bf16 call with the same step budget: fp8 steps hold 32 keys, not 16
     b = h.args(q_len=1)
-    wb = PaWorkspace()
-    assert L.pa_decode_plan(ctypes.byref(b), 0, ctypes.byref(wb), ctypes.byref(n)) == 0
+    assert L.pa_decode_plan(ctypes.byref(b), 0, ctypes.byref(wb), ctypes.byref(nb)) == 0
     assert wb.num_splits == ws.num_splits
 
 
@@ -482,13 +491,17 @@ def test_ragged_route_and_plan(L):
     assert L.pa_attention_plan(ctypes.byref(c), 0, ctypes.byref(ws), ctypes.byref(n),
                                ctypes.byref(route)) == 0
     assert route.value == _lib.ROUTE_DECODE
-    # packed rows and query_lens together are refused; fp8 pages have no prefill part
+    # packed rows and query_lens together are refused
     d = h.args(q_len=64, query_start_loc=h.p, query_lens=h.p)
     assert L.pa_attention_plan(ctypes.byref(d), 0, ctypes.byref(ws), ctypes.byref(n),
                                ctypes.byref(route)) == -1
+    # fp8 pages: the same ragged plan as bf16 pages (the decode part's steps
+    # hold 32 keys, so its splits follow the fp8 step budget)
     e = h.args(q_len=64, query_start_loc=h.p, kv_dtype=1, k_scale=1.0, v_scale=1.0)
-    assert L.pa_attention_plan(ctypes.byref(e), 0, ctypes.byref(ws), ctypes.byref(n),
-                               ctypes.byref(route)) == -2
+    we = PaWorkspace()
+    assert L.pa_attention_plan(ctypes.byref(e), 0, ctypes.byref(we), ctypes.byref(n),
+                               ctypes.byref(route)) == 0
+    assert route.value == _lib.ROUTE_RAGGED and we.prefill_splits == 5 * 256
     # a ragged call without its workspace is refused before any launch
     assert L.pa_attention(ctypes.byref(a), None, None) == _lib.PA_ERR_WORKSPACE
 
