@@ -10,7 +10,8 @@ once) divided by the mean HIP-event time of the step (pa_decode +
 pa_split_reduce), with the inputs resident in HBM and the 256 MB last-level
 cache flushed before every step.  ``roofline`` is for the dominant kernel
 (the decode kernel alone, timed by its own event pair).  Secondary sections
-report the same decode with fp8 (E4M3) pages, the chunked prefill,
+report the same decode with fp8 (E4M3) pages, the chunked prefill (bf16
+and fp8 pages),
 long-context decode, mixed batch and a long-prompt prefill sweep, each with
 its own roofline (``traffic`` is the HBM bytes per launch from the committed
 rocprofv3 counter summary of that section while its kernel source is
@@ -255,8 +256,10 @@ class Runner:
         torch, api = self.torch, self.api
         x = d.x
         out = torch.empty_like(d.q)
+        fp8 = getattr(x, "kv_dtype", None) == "fp8_e4m3"
         args = api.make_args(d.q, d.kp, d.vp, d.bt, d.cl, out, scale=x.scale, mask=d.mask,
-                             query_lens=d.ql)
+                             query_lens=d.ql,
+                             **(dict(k_scale=x.k_scale, v_scale=x.v_scale) if fp8 else {}))
         ws = api.PrefillWorkspace.for_args(args, d.q.device) if split else None
         for _ in range(warmup):
             if flush:
@@ -453,9 +456,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", default="C2,C2fp8,C3,C4,C5,shared,long,small,append",
+    ap.add_argument("--only", default="C2,C2fp8,C3,C3fp8,C4,C5,shared,long,small,append",
                     help="sections to run (C2 is the headline; leaving it out leaves `value` "
-                         "null, for profiling runs): C2, C2fp8, C3, C4, C5, shared (the "
+                         "null, for profiling runs): C2, C2fp8, C3, C3fp8, C4, C5, shared (the "
                          "shared-prefix decode alone), long (= long4096, "
                          "long16384), small, threshold, append (all write shapes), "
                          "append_long, append_fp8")
@@ -601,6 +604,21 @@ def main():
             "flops": fl3, "tflops": round(fl3 / ms / 1e9, 2), **_stats(r3["ms"]),
             "roofline": mfma_roofline(fl3, ms, "prefill_c3")}
         del d3, r3
+    if "C3fp8" in only:
+        # the same chunked prefill over fp8 (E4M3) pages: the codes are
+        # widened to bf16 on their way into LDS, so the flops are the same
+        x3f = W.make_c3_fp8()
+        fl3f = prefill_flops(x3f)
+        d3f = run.to_device(x3f)
+        r3f = run.time_prefill(d3f, args.steps, args.warmup, flush=True)
+        ms = float(np.mean(r3f["ms"]))
+        log(f"[bench] prefill C3 fp8: {ms * 1e3:.1f} us, {fl3f / ms / 1e9:.1f} TFLOP/s")
+        sections["prefill_C3_fp8"] = {
+            "workload": "chunked causal prefill bf16 query, fp8 e4m3 K/V pages (k/v scale 0.5) "
+                        "B4 Hq28 Hkv4 D128 L512 prefix U[0,2048] page16 seed3",
+            "flops": fl3f, "tflops": round(fl3f / ms / 1e9, 2), **_stats(r3f["ms"]),
+            "roofline": mfma_roofline(fl3f, ms, "prefill_c3_fp8")}
+        del d3f, r3f, x3f
     long = []
     for L in (4096, 16384):
         if f"long{L}" not in only:

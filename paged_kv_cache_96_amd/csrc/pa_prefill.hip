@@ -415,7 +415,7 @@ __device__ __forceinline__ int dma_pos(int r, int c) {
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 template <int D, bool DEBUG, int MODE, int RB, bool FP8>
-__global__ __launch_bounds__(256, (MODE == kStageDma || MODE == kStageDmaRun) ? 3
+__global__ __launch_bounds__(256, (MODE == kStageDma || MODE == kStageDmaRun || FP8) ? 3
                                   : RB == 1                                ? 2
                                                                            : 1) void
 prefill_kernel(LaunchParams p, int num_tiles) {
@@ -429,7 +429,7 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   // keys per tile: DMA staging walks tiles of 32 keys (two 16 KiB buffers,
   // three workgroups per compute unit); the split plan's 64-key grid is a
   // multiple of it
-  constexpr int BN = DMA ? 32 : kBN;
+  constexpr int BN = (DMA || FP8) ? 32 : kBN;
   constexpr int NBLK = BN / 32;    // 32-key blocks per tile
   constexpr int kRW = 32 * RB;     // packed rows per wave
   constexpr int kBM = 4 * kRW;     // packed rows per workgroup
@@ -441,8 +441,8 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   constexpr int kKS = DMA ? D : TL::kKStride;   // shorts per K row
   constexpr int kVS = DMA ? D : TL::kVStride;   // shorts per V row
   constexpr int kPadBuf = DMA ? 1 : 2;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kPadBuf][DMA ? 8 : kBN * kKS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kPadBuf][DMA ? 8 : kBN * kVS];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kPadBuf][DMA ? 8 : BN * kKS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kPadBuf][DMA ? 8 : BN * kVS];
   __shared__ __attribute__((aligned(16))) uint16_t kd0[DMA ? BN * D : 8], kd1[DMA ? BN * D : 8];
   __shared__ __attribute__((aligned(16))) uint16_t vd0[DMA ? BN * D : 8], vd1[DMA ? BN * D : 8];
   __shared__ int s_plan_red[DMA ? 32 : 1];
@@ -555,8 +555,13 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   const int32_t *bt = p.bt + (size_t)(p.prefix_pass ? p.grp_start[b] : b) * p.max_pages;
   const int chunk = tid % TL::kChunks;
   const int key_in_round = tid / TL::kChunks;
+  // one staged K/V tile in registers: 8 bf16 elements per lane and round,
+  // or for fp8 pages their 8 codes, widened only when stored to LDS (a
+  // conversion next to the load would wait for it at once)
+  using StageWord = typename std::conditional<FP8, uint2, uint4>::type;
+  constexpr int kRounds = BN / TL::kKeysPerRound;  // staging rounds per tile
   struct Stage {
-    uint4 k[DMA ? 1 : TL::kRounds], v[DMA ? 1 : TL::kRounds];
+    StageWord k[DMA ? 1 : kRounds], v[DMA ? 1 : kRounds];
   };
 
   // The block table is read-only for the whole call: reading it through the
@@ -675,7 +680,7 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   auto stage_load_uniform = [&](int kt, Stage &st) {
     (void)kt;  // runs follow run_j0, which tracks kt * BN
 #pragma unroll
-    for (int r = 0; r < TL::kRounds; ++r) {
+    for (int r = 0; r < kRounds; ++r) {
       const bool live = run_j0 < kend_wg;                 // wave-uniform
       if (run_slot == 0) run_page = live ? btc[min(run_lp, p.max_pages - 1)] : 0;
       if constexpr (MODE == kStagePool) {
@@ -684,8 +689,8 @@ prefill_kernel(LaunchParams p, int num_tiles) {
         if constexpr (FP8) {
           const u32x2_t kv = __builtin_amdgcn_raw_buffer_load_b64(pool_k, voff, soff, 0);
           const u32x2_t vv = __builtin_amdgcn_raw_buffer_load_b64(pool_v, voff, soff, 0);
-          st.k[r] = fp8x8_to_bf16x8(kv[0], kv[1]);
-          st.v[r] = fp8x8_to_bf16x8(vv[0], vv[1]);
+          st.k[r] = make_uint2(kv[0], kv[1]);
+          st.v[r] = make_uint2(vv[0], vv[1]);
         } else {
           const u32x4_t kv = __builtin_amdgcn_raw_buffer_load_b128(pool_k, voff, soff, 0);
           const u32x4_t vv = __builtin_amdgcn_raw_buffer_load_b128(pool_v, voff, soff, 0);
@@ -712,8 +717,8 @@ prefill_kernel(LaunchParams p, int num_tiles) {
       if constexpr (FP8) {
         const u32x2_t kv = __builtin_amdgcn_raw_buffer_load_b64(rk, voff, 0, 0);
         const u32x2_t vv = __builtin_amdgcn_raw_buffer_load_b64(rv, voff, 0, 0);
-        st.k[r] = fp8x8_to_bf16x8(kv[0], kv[1]);
-        st.v[r] = fp8x8_to_bf16x8(vv[0], vv[1]);
+        st.k[r] = make_uint2(kv[0], kv[1]);
+        st.v[r] = make_uint2(vv[0], vv[1]);
       } else {
         const u32x4_t kv = __builtin_amdgcn_raw_buffer_load_b128(rk, voff, 0, 0);
         const u32x4_t vv = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0);
@@ -735,7 +740,7 @@ prefill_kernel(LaunchParams p, int num_tiles) {
       return;
     }
 #pragma unroll
-    for (int r = 0; r < TL::kRounds; ++r) {
+    for (int r = 0; r < kRounds; ++r) {
       const int j = kt * BN + r * TL::kKeysPerRound + key_in_round;
       if (j < kend_wg) {
         const int lp = j / p.ps;
@@ -743,28 +748,33 @@ prefill_kernel(LaunchParams p, int num_tiles) {
         const int slot = j - lp * p.ps;
         const size_t off = (((size_t)page * p.Hkv + g) * p.ps + slot) * D + chunk * 8;
         if constexpr (FP8) {
-          const uint2 kw = *reinterpret_cast<const uint2 *>(kp8 + off);
-          const uint2 vw = *reinterpret_cast<const uint2 *>(vp8 + off);
-          st.k[r] = fp8x8_to_bf16x8(kw.x, kw.y);
-          st.v[r] = fp8x8_to_bf16x8(vw.x, vw.y);
+          st.k[r] = *reinterpret_cast<const uint2 *>(kp8 + off);
+          st.v[r] = *reinterpret_cast<const uint2 *>(vp8 + off);
         } else {
           st.k[r] = *reinterpret_cast<const uint4 *>(kp + off);
           st.v[r] = *reinterpret_cast<const uint4 *>(vp + off);
         }
         record(j, (long long)off * EB);
       } else {
-        st.k[r] = make_uint4(0, 0, 0, 0);  // never loaded: zeros keep masked math finite
-        st.v[r] = make_uint4(0, 0, 0, 0);
+        st.k[r] = StageWord{};  // never loaded: zeros keep masked math finite
+        st.v[r] = StageWord{};
       }
     }
   };
   auto stage_store = [&](uint16_t *kdst, uint16_t *vdst, const Stage &st) {
     if constexpr (!DMA) {
 #pragma unroll
-      for (int r = 0; r < TL::kRounds; ++r) {
+      for (int r = 0; r < kRounds; ++r) {
         const int key = r * TL::kKeysPerRound + key_in_round;
-        *reinterpret_cast<uint4 *>(&kdst[key * kKS + chunk * 8]) = st.k[r];
-        *reinterpret_cast<uint4 *>(&vdst[key * kVS + chunk * 8]) = st.v[r];
+        if constexpr (FP8) {
+          *reinterpret_cast<uint4 *>(&kdst[key * kKS + chunk * 8]) =
+              fp8x8_to_bf16x8(st.k[r].x, st.k[r].y);
+          *reinterpret_cast<uint4 *>(&vdst[key * kVS + chunk * 8]) =
+              fp8x8_to_bf16x8(st.v[r].x, st.v[r].y);
+        } else {
+          *reinterpret_cast<uint4 *>(&kdst[key * kKS + chunk * 8]) = st.k[r];
+          *reinterpret_cast<uint4 *>(&vdst[key * kVS + chunk * 8]) = st.v[r];
+        }
       }
     }
   };

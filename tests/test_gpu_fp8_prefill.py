@@ -169,3 +169,24 @@ def test_fp8_ragged_one_call(api, case):
         if trace:
             assert np.array_equal(dbg_t.cpu().numpy(), tr)
             assert np.array_equal(dbg_v.cpu().numpy(), v)
+
+
+def test_fp8_c3_full_size(api):
+    """The chunked prefill workload (4 requests x 512 rows after prefixes of
+    up to 2048 keys, H_q 28, H_kv 4) over fp8 pages: whole output against the
+    oracle in fp32 and fp64, split and unsplit, and the address trace."""
+    from workloads import make_c3_fp8
+    x = make_c3_fp8()
+    print(f"[C3-fp8] seed={x.seed} ctx={x.context_lens.tolist()}", flush=True)
+    ref = oracle.attention_of(x)
+    ref64 = oracle.attention_of(x, precision="f64")
+    tr, v = _expect_trace_visits(x)
+    d = DeviceInputs(x)
+    for kw in (dict(), dict(split=False)):
+        out, ex = run_prefill(api, d, **kw)
+        err = assert_parity(out, ref, "bf16", f"C3-fp8 {kw}")
+        assert_parity(out, ref64, "bf16", f"C3-fp8 {kw} (fp64 oracle)")
+        assert "counters" not in ex or not ex["counters"].any()
+        print(f"[C3-fp8] {kw} max abs err {err:.3e}", flush=True)
+        _, tex = run_prefill(api, d, trace=True, **kw)
+        assert np.array_equal(tex["trace"], tr) and np.array_equal(tex["visits"], v)

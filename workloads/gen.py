@@ -378,6 +378,19 @@ def make_c3(seed: int = SEEDS["C3"]) -> PagedInputs:
     return x
 
 
+def make_c3_fp8(seed: int = SEEDS["C3"]) -> PagedInputs:
+    """The chunked prefill workload with fp8 (E4M3) K/V pages: the shape,
+    prefixes and pool of C3 (same seed, same draw order), page elements
+    drawn as fp8 codes (_draw_fp8_codes), k_scale = v_scale = 0.5; query and
+    output bf16."""
+    x = _uniform_pool_config("C3-fp8", seed, B=4, H_q=28, H_kv=4, D=128, L=512, ps=16,
+                             ctx_lo=None, ctx_hi=None, free_frac=0.10,
+                             prefix_lo=0, prefix_hi=2048, kv_dtype="fp8_e4m3")
+    x.meta["workload"] = ("chunked causal prefill bf16 query, fp8 e4m3 pages, B4 Hq28 Hkv4 D128 "
+                          "L512 prefix U[0,2048] ps16")
+    return x
+
+
 def make_c4(seed: int = SEEDS["C4"]) -> PagedInputs:
     """Long-context split-KV decode, bf16: B=8, H_q=32, H_kv=8, D=128, L=1,
     context_lens ~ U{32768..131072}, page_size=16, pool = live + 10% free."""
