@@ -137,9 +137,8 @@ typedef struct pa_args {
   int32_t *debug_trace;
   int32_t *debug_visits;
   /* Page element type (pa_kv_dtype; 0 = PA_KV_SAME).  PA_KV_FP8_E4M3 needs
-   * dtype PA_DTYPE_BF16 (query and out) and head_dim 128.  pa_decode,
-   * pa_split_reduce, pa_decode_noalloc, pa_prefill and pa_attention (every
-   * route) take it; pa_decode_shared returns PA_ERR_UNSUPPORTED for it. */
+   * dtype PA_DTYPE_BF16 (query and out) and head_dim 128; every read entry
+   * point takes it. */
   int32_t kv_dtype;
   float k_scale;               /* fp8 pages: finite and > 0 (ignored otherwise) */
   float v_scale;               /* fp8 pages: finite and > 0 (ignored otherwise) */
@@ -382,8 +381,8 @@ typedef struct pa_prefix_groups {
  *                16, then N int32 piece counts (rounded up to 16);
  *   counters     decode: batch * U;
  * R, U as for the balanced schedule.  *workspace_bytes is all of partial_out
- * and partial_lse.  PA_ERR_UNSUPPORTED: dtype other than bf16, fp8 pages,
- * debug outputs, or a batch the balanced schedule does not take. */
+ * and partial_lse.  PA_ERR_UNSUPPORTED: dtype other than bf16, debug
+ * outputs, or a batch the balanced schedule does not take. */
 pa_status pa_decode_shared_plan(const pa_args *args, const pa_prefix_groups *groups,
                                 int32_t num_cus, pa_workspace *plan, size_t *workspace_bytes);
 

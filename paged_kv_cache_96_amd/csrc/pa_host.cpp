@@ -556,7 +556,7 @@ pa_args prefix_launch_args(const pa_args *a, const pa_prefix_groups *g) {
 // Host-side checks of the groups (their contents are device data).
 pa_status check_groups(const pa_args *a, const pa_prefix_groups *g) {
   if (!g) return PA_ERR_INVALID_ARG;
-  if (a->dtype != PA_DTYPE_BF16 || kv_fp8(a)) return PA_ERR_UNSUPPORTED;
+  if (a->dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
   if (a->debug_trace || a->debug_visits) return PA_ERR_UNSUPPORTED;
   if (a->batch == 0) return PA_OK;
   if (g->num_groups < 0 || g->num_groups > a->batch || g->max_group_size < 1 ||

@@ -424,8 +424,8 @@ def test_fp8_pages_validation(L, kw, code):
 
 def test_fp8_pages_plans(L):
     """fp8 pages are planned like bf16 pages by the decode path (with 32-key
-    steps), the prefill path (same key-split slots) and the router (every
-    route); the shared-prefix decode refuses them before any launch."""
+    steps), the prefill path (same key-split slots), the router (every
+    route) and the shared-prefix decode."""
     h = HostBuffers()
     ws, wb = PaWorkspace(), PaWorkspace()
     n, nb = ctypes.c_size_t(0), ctypes.c_size_t(0)
@@ -441,7 +441,10 @@ def test_fp8_pages_plans(L):
     assert route.value == _lib.ROUTE_PREFILL
     g = _groups(h)
     assert L.pa_decode_shared_plan(ctypes.byref(h.args(kv_dtype=1, k_scale=0.5, v_scale=0.5)),
-                                   ctypes.byref(g), 0, ctypes.byref(ws), ctypes.byref(n)) == -2
+                                   ctypes.byref(g), 0, ctypes.byref(ws), ctypes.byref(n)) == 0
+    assert L.pa_decode_shared_plan(ctypes.byref(h.args()), ctypes.byref(g), 0,
+                                   ctypes.byref(wb), ctypes.byref(nb)) == 0
+    assert ws.prefill_splits == wb.prefill_splits and ws.num_counters == wb.num_counters
     a.q_len = 1
     assert L.pa_decode_plan(ctypes.byref(a), 0, ctypes.byref(ws), ctypes.byref(n)) == 0
     assert ws.schedule == SCHEDULE_BALANCED
@@ -555,7 +558,8 @@ def test_shared_prefix_plan_layout(L):
     ({}, {"prefix_lens": None}, -1),
     ({"q_len": 9}, {}, -1),                       # decode rows only
     ({"dtype": 0}, {}, -2),                       # the prefix launch is bf16 only
-    ({"kv_dtype": 1, "k_scale": 1.0, "v_scale": 1.0}, {}, -2),
+    ({"kv_dtype": 1, "k_scale": 1.0, "v_scale": 1.0, "head_dim": 64}, {}, -2),  # fp8: D 128
+    ({"kv_dtype": 1, "k_scale": 0.0, "v_scale": 1.0}, {}, -1),                  # fp8 scales
 ])
 def test_shared_prefix_validation(L, kw, gkw, code):
     h = HostBuffers()

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests._gpu import DeviceInputs, assert_parity, dev, host_f64, run_decode
+from tests._gpu import DeviceInputs, assert_parity, dev, host_f64, kv_scales, run_decode
 from workloads import c5_decode_grouped, make_c5, make_shared
 
 pytestmark = pytest.mark.gpu
@@ -36,7 +36,7 @@ def _run_shared(api, x, groups, *, q=None, qsl=None, calls=1, prefix_lens=None, 
     if qsl is not None:
         kw = dict(query_start_loc=dev(qsl), max_query_len=x.L)
     args = api.make_args(qd, d.kp, d.vp, d.bt, d.cl, out, scale=x.scale, mask=d.mask,
-                         query_lens=d.ql if qsl is None else None, **kw)
+                         query_lens=d.ql if qsl is None else None, **kw, **kv_scales(x))
     pl = groups.prefix_lens if prefix_lens is None else prefix_lens
     gs_d, pl_d = dev(groups.group_start), dev(np.asarray(pl, dtype=np.int32))
     g = api.PrefixGroups(gs_d, pl_d, groups.max_group_size)
@@ -81,6 +81,36 @@ def test_shared_matches_oracle(api, seed, case):
                             query_lens=qlens)
     print(f"shared case {name}: B={x.B} groups={groups.num_groups}", flush=True)
     _check(api, x, groups, name)
+
+
+FP8_CASES = [c for c in CASES if c[4] == 128]  # fp8 pages: head_dim 128
+
+
+@pytest.mark.parametrize("seed,case", list(enumerate(FP8_CASES, start=200)),
+                         ids=[c[0] for c in FP8_CASES])
+def test_shared_fp8_pages_match_oracle(api, seed, case):
+    """fp8 (E4M3) pages with per-tensor scales: the prefix launch (the
+    prefill kernel's fp8 build) and the decode launch both read the codes;
+    their row states carry v_scale alike, so the merge is unchanged."""
+    name, H_q, H_kv, L, D, ps, sizes, pages, suffix, qlens = case
+    x, groups = make_shared(seed, H_q=H_q, H_kv=H_kv, L=L, D=D, page_size=ps,
+                            group_sizes=sizes, prefix_pages=pages, suffix=suffix,
+                            query_lens=qlens, kv_dtype="fp8_e4m3", kv_scales=(0.37, 1.7))
+    print(f"shared fp8 case {name}: B={x.B} groups={groups.num_groups}", flush=True)
+    _check(api, x, groups, f"fp8 {name}")
+
+
+def test_shared_fp8_partial_page_prefix_and_unshared_agree(api):
+    """fp8 pages, a prefix that ends inside a page, and the same inputs
+    through pa_decode: both within the bar of the oracle, and of each other."""
+    x, groups = make_shared(19, H_q=8, H_kv=2, L=1, D=128, page_size=16,
+                            group_sizes=[3, 2, 4], prefix_pages=[4, 2, 9], suffix=(9, 150),
+                            kv_dtype="fp8_e4m3", kv_scales=(0.6, 0.45))
+    pl = groups.prefix_lens + np.asarray([7, 15, 3], dtype=np.int32)
+    out_s, _, ref = _check(api, x, groups, "fp8 partial page", prefix_lens=pl)
+    out_u, _ = run_decode(api, DeviceInputs(x))
+    assert_parity(out_u, ref, "bf16", "fp8 unshared")
+    assert np.abs(host_f64(out_s) - host_f64(out_u)).max() <= 1.6e-2
 
 
 def test_shared_equals_unshared_decode(api):

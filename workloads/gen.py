@@ -568,13 +568,16 @@ def make_shared(seed: int, *, H_q: int, H_kv: int, L: int, D: int, page_size: in
                 group_sizes: Sequence[int], prefix_pages: Sequence[int],
                 suffix: tuple, dtype: str = "bf16", causal: bool = True,
                 query_lens: Optional[Sequence[int]] = None, extra_free_pages: int = 3,
-                garbage=GARBAGE_DEFAULT, name: str = "shared"):
+                garbage=GARBAGE_DEFAULT, name: str = "shared", kv_dtype: Optional[str] = None,
+                kv_scales=(0.5, 0.5)):
     """Requests in groups of consecutive requests: group k has
     ``group_sizes[k]`` members whose first ``prefix_pages[k]`` block-table
     entries name the same physical pages (complete pages), followed by pages
     of their own; member context = prefix keys + a suffix of U{suffix[0]..
     suffix[1]} keys (suffix[0] >= L, so every query row sees the whole
-    prefix).  Returns (PagedInputs, SharedGroups).
+    prefix).  ``kv_dtype="fp8_e4m3"``: the pages hold fp8 codes (as in
+    make_random) with k_scale, v_scale = ``kv_scales``.  Returns
+    (PagedInputs, SharedGroups).
 
     Draw order: suffix lengths -> physical-id permutation -> K -> V -> Q.
     """
@@ -610,10 +613,12 @@ def make_shared(seed: int, *, H_q: int, H_kv: int, L: int, D: int, page_size: in
     max_pages = max(_pages_needed(c, page_size) for c in ctx)
     if query_lens is not None:
         query_lens = np.asarray(query_lens, dtype=np.int32)
-    kp = _fill_pool(rng, dtype, num_pages, H_kv, page_size, D, order, slots, garbage)
-    vp = _fill_pool(rng, dtype, num_pages, H_kv, page_size, D, order, slots, garbage)
+    pdt = kv_dtype or dtype
+    kp = _fill_pool(rng, pdt, num_pages, H_kv, page_size, D, order, slots, garbage)
+    vp = _fill_pool(rng, pdt, num_pages, H_kv, page_size, D, order, slots, garbage)
     q = _queries(rng, dtype, B, H_q, L, D, query_lens, garbage)
     bt = _tables_from_ids(ctx, page_size, max_pages, ids)
+    fp8 = kv_dtype == "fp8_e4m3"
     gs = np.zeros(len(group_sizes) + 1, dtype=np.int32)
     gs[1:] = np.cumsum(group_sizes)
     x = PagedInputs(
@@ -621,7 +626,8 @@ def make_shared(seed: int, *, H_q: int, H_kv: int, L: int, D: int, page_size: in
         page_size=page_size, num_pages=num_pages, max_pages=max_pages,
         scale=1.0 / math.sqrt(D), causal=causal, query=q, key_pages=kp, value_pages=vp,
         block_table=bt, context_lens=np.asarray(ctx, dtype=np.int32), query_lens=query_lens,
-        meta={"live_pages": live, "garbage": garbage})
+        meta={"live_pages": live, "garbage": garbage}, kv_dtype=kv_dtype,
+        k_scale=float(kv_scales[0]) if fp8 else 1.0, v_scale=float(kv_scales[1]) if fp8 else 1.0)
     return x, SharedGroups(gs, np.asarray([p * page_size for p in prefix_pages], dtype=np.int32))
 
 
