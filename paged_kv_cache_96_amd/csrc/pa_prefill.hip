@@ -793,7 +793,9 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   // Register staging: with one row block per wave, two sets (set A holds
   // even tiles, set B odd ones) so that loads run two tiles ahead; with two
   // row blocks a tile is long enough for loads one tile ahead, in one set.
-  constexpr bool kTwoSets = RB == 1;
+  // fp8 codes take one set too: at three workgroups per CU a second set
+  // spills, and loads one 32-key tile ahead measured faster than that.
+  constexpr bool kTwoSets = RB == 1 && !FP8;
   Stage sa, sb;
  for (; pass < 2; ++pass) {
 #pragma unroll
