@@ -45,7 +45,7 @@ def _traced_prefill_matches(api, d, x, out, **kw):
     visit per key under the kv head that address points at: both equal the
     oracle's translation exactly.  The LDS-load staging gives the same
     output bits traced and untraced (and call after call); the register
-    staging modes (D 64, and page sizes that are not a multiple of 16) are
+    staging modes (D 64, page sizes that are not a multiple of 16, fp8 pages) are
     not bitwise repeatable from call to call (1-ulp bf16 differences in a
     few rows whose tile walks two or more key tiles), so there the traced
     output is held to the oracle instead."""
