@@ -190,3 +190,62 @@ def test_fp8_c3_full_size(api):
         print(f"[C3-fp8] {kw} max abs err {err:.3e}", flush=True)
         _, tex = run_prefill(api, d, trace=True, **kw)
         assert np.array_equal(tex["trace"], tr) and np.array_equal(tex["visits"], v)
+
+
+def test_fp8_packed_rows_through_pa_prefill(api):
+    """Packed query rows (query_start_loc) of fp8 pages through pa_prefill
+    itself, with and without the key split."""
+    import torch
+    x = _fp8(91, [300, 45, 900, 130], H_q=16, H_kv=4, L=130, page_size=16, causal=True,
+             query_lens=[130, 45, 2, 0], kv_scales=(0.6, 1.2))
+    q, qsl = _pack(x)
+    ref = oracle.attention_of(x)
+    qd = dev(q)
+    for split in (True, False):
+        out = torch.full_like(qd, float("nan"))
+        args = api.make_args(qd, dev(x.key_pages), dev(x.value_pages), dev(x.block_table),
+                             dev(x.context_lens), out, scale=x.scale, mask="causal",
+                             query_start_loc=dev(qsl), max_query_len=x.L, k_scale=x.k_scale,
+                             v_scale=x.v_scale)
+        ws = api.PrefillWorkspace.for_args(args, qd.device) if split else None
+        api.pa_prefill(args, ws)
+        torch.cuda.synchronize()
+        got = host_f64(out)
+        full = np.zeros((x.B, x.H_q, x.L, x.D))
+        for b in range(x.B):
+            full[b, :, :qsl[b + 1] - qsl[b]] = got[qsl[b]:qsl[b + 1]].transpose(1, 0, 2)
+        assert_parity(torch.from_numpy(full), ref, "bf16", f"fp8 packed prefill split={split}")
+        if ws is not None and ws.counters is not None:
+            assert not ws.counters.any().item()
+
+
+def test_fp8_checked_call_flags_out_of_pool_pages(api):
+    """The contract check with fp8 pages: an out-of-pool entry is flagged
+    (PA_DEBUG_BAD_PAGE, one count per call), the output stays untouched, and
+    the same call on valid metadata gives the oracle's result with the
+    error word zero."""
+    import dataclasses
+    import torch
+    x = _fp8(92, [300, 41, 900], H_q=8, H_kv=2, L=40, page_size=16, causal=True,
+             kv_scales=(0.5, 0.5))
+    bt = x.block_table.copy()
+    bt[2, 3] = x.num_pages
+    bad = dataclasses.replace(x, block_table=bt)
+    for inputs, want in ((bad, [1, 1]), (x, [0, 0])):
+        err = torch.zeros(2, dtype=torch.int32, device="cuda")
+        qd = dev(inputs.query)
+        out = torch.full_like(qd, float("nan"))
+        args = api.make_args(qd, dev(inputs.key_pages), dev(inputs.value_pages),
+                             dev(inputs.block_table), dev(inputs.context_lens), out,
+                             scale=inputs.scale, mask="causal", debug_errors=err,
+                             k_scale=inputs.k_scale, v_scale=inputs.v_scale)
+        ws = api.PrefillWorkspace.for_args(args, qd.device)
+        api.pa_prefill(args, ws)
+        torch.cuda.synchronize()
+        assert err.cpu().tolist() == want
+        if want[0]:
+            assert torch.isnan(out).all()
+        else:
+            assert_parity(out, oracle.attention_of(x), "bf16", "fp8 checked prefill")
+        if ws.counters is not None:
+            assert not ws.counters.any().item()
