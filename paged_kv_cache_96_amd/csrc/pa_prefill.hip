@@ -1,4 +1,5 @@
-// bf16 paged prefill kernel on gfx950 matrix cores.
+// bf16 paged prefill kernel on gfx950 matrix cores (pages of bf16 values or
+// of fp8 E4M3 codes with per-tensor scales).
 //
 // Work: one workgroup (4 waves) owns BM = 128 * RB packed query rows of one
 // (request b, kv head g); packed row rho is position rho / G of head
@@ -22,9 +23,14 @@
 //      computed; no staging registers and no LDS stores, so a workgroup
 //      needs 33 KiB of LDS and fits three waves per SIMD (the launch
 //      bounds ask for three workgroups per compute unit); the tile layout
-//      (dma_pos) keeps the operand reads conflict-free.  Otherwise 64-key tiles: every thread loads the
-//      tile TWO ahead into one of two register sets and stores the set
-//      loaded one tile earlier to the other LDS buffer;
+//      (dma_pos) keeps the operand reads conflict-free.  fp8 codes take the
+//      same loads into a tile of half the bytes (fp8_pos), and each operand
+//      read widens its 8 codes to bf16 (the transposed V read is the 8-bit
+//      one; the key rows of the score product are permuted so that a lane's
+//      PV keys are consecutive, fp8_key_perm).  Otherwise (page sizes that
+//      are not a multiple of 16, or D = 64) 64-key tiles: every thread
+//      loads the tile TWO ahead into one of two register sets and stores the
+//      set loaded one tile earlier to the other LDS buffer;
 //   2. S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: K from LDS is the A
 //      operand, Q (kept in registers for the whole walk) the B operand.  The
 //      result gives every lane the scores of ONE query row (lane % 32) against
@@ -412,7 +418,23 @@ __device__ __forceinline__ int dma_pos(int r, int c) {
   return (r >> 4) * 2048 + b * 512 + (16 * (c >> 2) + 4 * (r & 3) + ((c & 3) ^ b)) * 8;
 }
 
+// LDS tile layout of the fp8 LDS-load staging (32 rows x 8 chunks of 16
+// codes, D = 128): row r at byte 128 r, chunk c in slot c ^ ((r / 2) % 8).
+// A K operand read (32 rows, one chunk, 8 bytes per lane) then touches every
+// bank pair twice, the least that 512 bytes can.
+__device__ __forceinline__ int fp8_pos(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }
+
+// The fp8 staging feeds the score product with key rows in the order pi(m)
+// = 16 (m / 16) + 8 ((m / 4) % 2) + 4 ((m / 8) % 2) + m % 4 (bits 2 and 3
+// of m swapped): then the 8 keys of a lane's k slot in the PV product are
+// consecutive, which is what an 8-bit transposed read delivers.
+__device__ __forceinline__ int fp8_key_perm(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
 
 template <int D, bool DEBUG, int MODE, int RB, bool FP8>
 __global__ __launch_bounds__(256, (MODE == kStageDma || MODE == kStageDmaRun || FP8) ? 3
@@ -422,9 +444,10 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   if (contract_broken(p)) return;
   constexpr bool UNIFORM = MODE != kStageLanes;
   constexpr bool DMA = MODE == kStageDma || MODE == kStageDmaRun;
-  // fp8 (E4M3) pages: register staging only, each code widened to bf16 on
-  // its way into LDS (the direct-to-LDS loads cannot convert)
-  static_assert(!FP8 || (D == 128 && !DMA), "fp8 pages: D = 128, register staging");
+  // fp8 (E4M3) pages, D = 128: with LDS loads the codes land in LDS as they
+  // are and each operand read widens them to bf16; register staging widens
+  // them on their way into LDS
+  static_assert(!FP8 || D == 128, "fp8 pages: D = 128");
   constexpr int EB = FP8 ? 1 : 2;  // bytes of a page element
   // keys per tile: DMA staging walks tiles of 32 keys (two 16 KiB buffers,
   // three workgroups per compute unit); the split plan's 64-key grid is a
@@ -617,13 +640,22 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   // (see dma_pos).  The per-lane offsets are fixed for the whole walk; the
   // run's page and slot are advanced by BN keys per tile.
   constexpr int kDmaRows = BN / 4;          // keys per wave and tile
-  constexpr int kDmaBlocks = kDmaRows / 4;  // load instructions per wave, K and V each
-  const int dma_row = (lane >> 2) & 3;
+  // load instructions per wave, K and V each: 4 rows of bf16 or 8 rows of
+  // fp8 codes per 1 KiB
+  constexpr int kDmaRowsPerLoad = FP8 ? 8 : 4;
+  constexpr int kDmaBlocks = kDmaRows / kDmaRowsPerLoad;
+  const int dma_row = FP8 ? lane >> 3 : (lane >> 2) & 3;
   int dma_voff[kDmaBlocks];
 #pragma unroll
   for (int j = 0; j < kDmaBlocks; ++j) {
-    const int blk4 = (kDmaBlocks * wave + j) & 3;
-    dma_voff[j] = (4 * j + dma_row) * (D * 2) + (4 * (lane >> 4) + ((lane & 3) ^ blk4)) * 16;
+    if constexpr (FP8) {
+      // lane l fills slot l % 8 of row l / 8 of the wave's 8 rows (fp8_pos)
+      const int r = kDmaRows * wave + dma_row;
+      dma_voff[j] = dma_row * D + 16 * ((lane & 7) ^ ((r >> 1) & 7));
+    } else {
+      const int blk4 = (kDmaBlocks * wave + j) & 3;
+      dma_voff[j] = (4 * j + dma_row) * (D * 2) + (4 * (lane >> 4) + ((lane & 3) ^ blk4)) * 16;
+    }
   }
   int dma_lp = 0, dma_slot = 0;
   auto dma_tile = [&](int T, uint16_t *kdst, uint16_t *vdst) {
@@ -636,14 +668,14 @@ prefill_kernel(LaunchParams p, int num_tiles) {
     int soff = 0;
     if constexpr (MODE == kStageDmaRun) {
       const long long off =
-          (long long)page * page_bytes + head_bytes + (long long)dma_slot * (D * 2);
-      const int nrec = live ? kDmaRows * D * 2 : 0;
+          (long long)page * page_bytes + head_bytes + (long long)dma_slot * (D * EB);
+      const int nrec = live ? kDmaRows * D * EB : 0;
       rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(kp_bytes + off), (short)0, nrec,
                                              kBufferRsrcWord3);
       rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(vp_bytes + off), (short)0, nrec,
                                              kBufferRsrcWord3);
     } else {
-      soff = page * (int)page_bytes + (int)head_bytes + dma_slot * (D * 2);
+      soff = page * (int)page_bytes + (int)head_bytes + dma_slot * (D * EB);
     }
     auto load = [&](int j, int voff) {
       const int dst = (kDmaBlocks * wave + j) * 512;
@@ -657,8 +689,8 @@ prefill_kernel(LaunchParams p, int num_tiles) {
         // the lane offset
         long long base = soff;
         if constexpr (MODE == kStageDmaRun)
-          base = (long long)page * page_bytes + head_bytes + (long long)dma_slot * (D * 2);
-        if (live && voff >= 0) record(run0 + 4 * j + dma_row, base + voff);
+          base = (long long)page * page_bytes + head_bytes + (long long)dma_slot * (D * EB);
+        if (live && voff >= 0) record(run0 + kDmaRowsPerLoad * j + dma_row, base + voff);
       }
     };
     if (run0 + kDmaRows <= kend_wg) {  // wave-uniform: the whole run is live
@@ -669,7 +701,7 @@ prefill_kernel(LaunchParams p, int num_tiles) {
       // hold anything, NaN included)
 #pragma unroll
       for (int j = 0; j < kDmaBlocks; ++j)
-        load(j, run0 + 4 * j + dma_row < kend_wg ? dma_voff[j] : (int)0x80000000u);
+        load(j, run0 + kDmaRowsPerLoad * j + dma_row < kend_wg ? dma_voff[j] : (int)0x80000000u);
     }
     dma_slot += BN;
     while (dma_slot >= p.ps) {
@@ -837,7 +869,18 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   // (2 kk + half), V rows kb .. kb + 3 and kb + 8 .. kb + 11 of the
   // transposed reads; every other read adds a constant (see dma_pos)
   int k_dma[2] = {0, 0}, v_dma[2] = {0, 0};
-  if constexpr (DMA) {
+  // fp8 LDS loads: K row pi(lane % 32) and its chunk slot key; V rows for
+  // the 8-bit transposed reads (lane 2j + c of a 16-lane group points at
+  // 8 codes of row j of its 8 keys, columns + 8 c) and their slot key
+  int k8_row = 0, k8_key = 0, v8_off = 0, v8_key = 0;
+  if constexpr (DMA && FP8) {
+    const int kr = fp8_key_perm(ln);
+    k8_row = kr * 128 + 8 * half;
+    k8_key = (kr >> 1) & 7;
+    const int rv = ((lane & 15) >> 1) + 8 * (lane >> 5);  // key within the 16-key step
+    v8_off = rv * 128 + 8 * (lane & 1);
+    v8_key = (rv >> 1) & 7;                            // rows 16 hf + rv share it
+  } else if constexpr (DMA) {
     k_dma[0] = dma_pos(ln, half);
     k_dma[1] = dma_pos(ln, 2 + half);
     const int src = lane & 15;
@@ -880,9 +923,16 @@ prefill_kernel(LaunchParams p, int num_tiles) {
         const uint16_t *krow = kc + (blk * 32 + ln) * kKS;
 #pragma unroll
         for (int kk = 0; kk < TL::kKSteps; ++kk) {
-          const uint16_t *ka = DMA ? kc + k_dma[kk & 1] + blk * 4096 + (kk >> 1) * 128
-                                   : krow + kk * 16 + half * 8;
-          const uint4 a = *reinterpret_cast<const uint4 *>(ka);
+          uint4 a;
+          if constexpr (DMA && FP8) {
+            const uint8_t *kb8 = reinterpret_cast<const uint8_t *>(kc);
+            const uint2 w = *reinterpret_cast<const uint2 *>(kb8 + k8_row + 16 * (kk ^ k8_key));
+            a = fp8x8_to_bf16x8(w.x, w.y);
+          } else {
+            const uint16_t *ka = DMA ? kc + k_dma[kk & 1] + blk * 4096 + (kk >> 1) * 128
+                                     : krow + kk * 16 + half * 8;
+            a = *reinterpret_cast<const uint4 *>(ka);
+          }
 #pragma unroll
           for (int rb = 0; rb < RB; ++rb)
             s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(q[rb][kk]),
@@ -897,7 +947,9 @@ prefill_kernel(LaunchParams p, int num_tiles) {
           for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const int key = kt * BN + blk * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+              const int key =
+                  DMA && FP8 ? kt * BN + blk * 32 + fp8_key_perm((i >> 2) * 8 + half * 4 + (i & 3))
+                             : kt * BN + blk * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
               if (key >= lim[rb]) s[rb][i] = kNegInf;
             }
         }
@@ -943,16 +995,26 @@ prefill_kernel(LaunchParams p, int num_tiles) {
           for (int mb = 0; mb < TL::kMBlocks; ++mb) {
             const int d0 = mb * 32 + ((lane >> 4) & 1) * 16 + 4 * (src & 3);
             const int vr = kb + (src >> 2);
-            const int vo = blk * 4096 + hf * 2048 + mb * 128;  // kStageDma
-            const uint16_t *r1 = DMA ? vc + v_dma[0] + vo : vc + vr * kVS + d0;
-            const uint16_t *r2 = DMA ? vc + v_dma[1] + vo : vc + (vr + 8) * kVS + d0;
-            const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)r1);
-            const s16x4_t t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)r2);
-            const uint4 aop = make_uint4(
-                (uint32_t)(uint16_t)t1[0] | ((uint32_t)(uint16_t)t1[1] << 16),
-                (uint32_t)(uint16_t)t1[2] | ((uint32_t)(uint16_t)t1[3] << 16),
-                (uint32_t)(uint16_t)t2[0] | ((uint32_t)(uint16_t)t2[1] << 16),
-                (uint32_t)(uint16_t)t2[2] | ((uint32_t)(uint16_t)t2[3] << 16));
+            uint4 aop;
+            if constexpr (DMA && FP8) {
+              // 8 codes of the lane's column for keys 16 hf + 8 half .. + 7
+              // (chunk 2 mb + (lane / 16) % 2 of their rows), widened to bf16
+              const uint8_t *vb8 = reinterpret_cast<const uint8_t *>(vc);
+              const int c8 = 2 * mb + ((lane >> 4) & 1);
+              const i32x2_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                  (lds_i32x2_t *)(vb8 + hf * 16 * 128 + v8_off + 16 * (c8 ^ v8_key)));
+              aop = fp8x8_to_bf16x8((uint32_t)t[0], (uint32_t)t[1]);
+            } else {
+              const int vo = blk * 4096 + hf * 2048 + mb * 128;  // kStageDma
+              const uint16_t *r1 = DMA ? vc + v_dma[0] + vo : vc + vr * kVS + d0;
+              const uint16_t *r2 = DMA ? vc + v_dma[1] + vo : vc + (vr + 8) * kVS + d0;
+              const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)r1);
+              const s16x4_t t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t *)r2);
+              aop = make_uint4((uint32_t)(uint16_t)t1[0] | ((uint32_t)(uint16_t)t1[1] << 16),
+                               (uint32_t)(uint16_t)t1[2] | ((uint32_t)(uint16_t)t1[3] << 16),
+                               (uint32_t)(uint16_t)t2[0] | ((uint32_t)(uint16_t)t2[1] << 16),
+                               (uint32_t)(uint16_t)t2[2] | ((uint32_t)(uint16_t)t2[3] << 16));
+            }
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
               o[rb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -1152,9 +1214,9 @@ hipError_t launch_rb(const LaunchParams &p, hipStream_t stream) {
   auto go = [&](auto dbg, auto fp8) {
     constexpr bool DBG = decltype(dbg)::value;
     constexpr bool F8 = decltype(fp8)::value;
-    // direct-to-LDS staging: bf16 pages with D = 128 (fp8 codes are widened
-    // in registers)
-    constexpr bool kDma = D == 128 && RB == 1 && !F8;
+    // direct-to-LDS staging with D = 128 (fp8 codes are widened at the
+    // operand reads)
+    constexpr bool kDma = D == 128 && RB == 1;
     const long long pool = (long long)p.num_pages * p.Hkv * p.ps * D * (F8 ? 1 : 2);
     if (p.ps % Tile<D>::kKeysPerRound != 0) {  // runs would straddle pages
       hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageLanes, RB, F8>), grid, dim3(256), 0,

@@ -1,12 +1,13 @@
 """GPU parity of the prefill path over fp8 (E4M3) K/V pages against the
 oracle, through the C ABI.  The kv-cache dtype with per-tensor k/v scales
 ("Reading vLLM's PagedAttention Kernel", section 3.2) applies to every read
-of the pages: pa_prefill (key split and unsplit; 16-key runs through one
-pool-wide buffer resource, per-run resources for pools past 2 GiB, per-lane
-walks for page sizes that are not a multiple of 16) and pa_attention's
-ragged route, whose decode part and prefill part both read the codes.  The
-address trace of the instrumented build is bit-exact; outputs are held to
-the bf16 bar.  Marked gpu."""
+of the pages: pa_prefill (key split and unsplit; codes loaded into LDS
+with one pool-wide buffer resource or, for pools past 2 GiB, one per run,
+and widened at the operand reads; per-lane register staging for page sizes
+that are not a multiple of 16) and pa_attention's ragged route, whose
+decode part and prefill part both read the codes.  The address trace of
+the instrumented build is bit-exact; outputs are held to the bf16 bar, and
+the LDS-load staging repeats bit for bit.  Marked gpu."""
 import numpy as np
 import pytest
 
@@ -249,3 +250,18 @@ def test_fp8_checked_call_flags_out_of_pool_pages(api):
             assert_parity(out, oracle.attention_of(x), "bf16", "fp8 checked prefill")
         if ws.counters is not None:
             assert not ws.counters.any().item()
+
+
+def test_fp8_lds_load_staging_repeats_bit_for_bit(api):
+    """Page sizes that are a multiple of 16: the codes go straight into LDS,
+    and calls in a row (split or not) and the instrumented build give the
+    same output bits."""
+    import torch
+    from workloads import make_c3_fp8
+    x = make_c3_fp8()
+    d = DeviceInputs(x)
+    for kw in (dict(), dict(split=False)):
+        outs = [run_prefill(api, d, **kw)[0] for _ in range(3)]
+        outs.append(run_prefill(api, d, trace=True, **kw)[0])
+        for o in outs[1:]:
+            assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16)), kw
