@@ -276,8 +276,9 @@ pa_status pa_prefill_plan(const pa_args *args, int32_t num_cus, pa_workspace *pl
  * bf16 matrix cores, fp32 statistics); fp32 runs on a vector-ALU kernel.
  * fp8 pages (bf16 query) run on the MFMA kernel too: the codes are loaded
  * into LDS as they are and widened exactly to bf16 by the operand reads
- * (page sizes that are a multiple of 16; other page sizes widen them on
- * their way into LDS), k_scale scales the scores and v_scale the output.
+ * (pools of 2 GiB and more with a page size that is not a multiple of 16
+ * widen them on their way into LDS), k_scale scales the scores and v_scale
+ * the output.
  * `ws` is NULL (no split) or a workspace of pa_prefill_plan: partial_out
  * fp32 [num_splits, D / 8, 256, 4] and partial_lse fp32 [num_splits, 2, 256]
  * (the state of a piece: the accumulators, reference maxima and row sums of

@@ -398,7 +398,18 @@ __device__ void find_piece(const LaunchParams &p, int nt, int *s_ctx, int *s_ql,
 // LDS by the loads (no staging registers, no LDS stores): D = 128 only.
 // kStageDmaRun: the same with one buffer resource per run (pools of 2 GiB
 // and more, as kStageRun).
-enum StageMode { kStageLanes = 0, kStageRun = 1, kStagePool = 2, kStageDma = 3, kStageDmaRun = 4 };
+// kStageDmaLanes: the LDS loads of kStageDma for page sizes that are not a
+// multiple of 16 (pools under 2 GiB): a wave's 8-key run may straddle pages,
+// so each lane resolves its own row's page from the run's block-table
+// entries and puts the whole pool offset in its own vector offset.
+enum StageMode {
+  kStageLanes = 0,
+  kStageRun = 1,
+  kStagePool = 2,
+  kStageDma = 3,
+  kStageDmaRun = 4,
+  kStageDmaLanes = 5
+};
 
 // LDS tile layout of kStageDma (64 rows x 16 chunks of 16 bytes, D = 128).
 // Rows come in blocks of 4 (b = (r / 4) % 4 within a 16-row group); a block
@@ -437,13 +448,15 @@ typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
 
 template <int D, bool DEBUG, int MODE, int RB, bool FP8>
-__global__ __launch_bounds__(256, (MODE == kStageDma || MODE == kStageDmaRun || FP8) ? 3
+__global__ __launch_bounds__(256, (MODE == kStageDma || MODE == kStageDmaRun ||
+                                   MODE == kStageDmaLanes || FP8)
+                                      ? 3
                                   : RB == 1                                ? 2
                                                                            : 1) void
 prefill_kernel(LaunchParams p, int num_tiles) {
   if (contract_broken(p)) return;
   constexpr bool UNIFORM = MODE != kStageLanes;
-  constexpr bool DMA = MODE == kStageDma || MODE == kStageDmaRun;
+  constexpr bool DMA = MODE == kStageDma || MODE == kStageDmaRun || MODE == kStageDmaLanes;
   // fp8 (E4M3) pages, D = 128: with LDS loads the codes land in LDS as they
   // are and each operand read widens them to bf16; register staging widens
   // them on their way into LDS
@@ -661,6 +674,38 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   auto dma_tile = [&](int T, uint16_t *kdst, uint16_t *vdst) {
     const int run0 = T * BN + kDmaRows * wave;  // first key of this wave's run
     const bool live = run0 < kend_wg;           // wave-uniform
+    if constexpr (MODE == kStageDmaLanes) {
+      // the run's keys lie on at most kDmaRows pages from its first one on;
+      // lane row r (run0 + r) is q = (s0 + r) / ps pages further
+      const int lp0 = run0 / p.ps;
+      const int s0 = run0 - lp0 * p.ps;
+      int ent[kDmaRows];
+#pragma unroll
+      for (int i = 0; i < kDmaRows; ++i) ent[i] = live ? btc[min(lp0 + i, p.max_pages - 1)] : 0;
+#pragma unroll
+      for (int j = 0; j < kDmaBlocks; ++j) {
+        const int r = kDmaRowsPerLoad * j + dma_row;
+        int q = 0;
+#pragma unroll
+        for (int m = 1; m < kDmaRows; ++m) q += s0 + r >= m * p.ps ? 1 : 0;
+        int pg = ent[0];
+#pragma unroll
+        for (int m = 1; m < kDmaRows; ++m) pg = q == m ? ent[m] : pg;
+        const int slot = s0 + r - q * p.ps;
+        const int coff = dma_voff[j] - r * (D * EB);  // the lane's chunk within the row
+        const int voff = run0 + r < kend_wg
+                             ? pg * (int)page_bytes + (int)head_bytes + slot * (D * EB) + coff
+                             : (int)0x80000000u;
+        const int dst = (kDmaBlocks * wave + j) * 512;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_k, (lds_void_t *)(kdst + dst), 16, voff, 0,
+                                                 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(pool_v, (lds_void_t *)(vdst + dst), 16, voff, 0,
+                                                 0, 0);
+        if constexpr (DEBUG)
+          if (voff >= 0) record(run0 + r, voff);
+      }
+      return;
+    }
     const int page = live ? btc[min(dma_lp, p.max_pages - 1)] : 0;
     // pool-wide resources with the run in the scalar offset, or (pools of
     // 2 GiB and more) resources of the run itself, empty past the last key
@@ -1219,6 +1264,13 @@ hipError_t launch_rb(const LaunchParams &p, hipStream_t stream) {
     constexpr bool kDma = D == 128 && RB == 1;
     const long long pool = (long long)p.num_pages * p.Hkv * p.ps * D * (F8 ? 1 : 2);
     if (p.ps % Tile<D>::kKeysPerRound != 0) {  // runs would straddle pages
+      if constexpr (kDma) {
+        if (pool < (1ll << 31)) {
+          hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageDmaLanes, RB, F8>), grid, dim3(256), 0,
+                             stream, p, tiles);
+          return;
+        }
+      }
       hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageLanes, RB, F8>), grid, dim3(256), 0,
                          stream, p, tiles);
     } else if (pool < (1ll << 31)) {

@@ -2,9 +2,10 @@
 oracle, through the C ABI.  The kv-cache dtype with per-tensor k/v scales
 ("Reading vLLM's PagedAttention Kernel", section 3.2) applies to every read
 of the pages: pa_prefill (key split and unsplit; codes loaded into LDS
-with one pool-wide buffer resource or, for pools past 2 GiB, one per run,
-and widened at the operand reads; per-lane register staging for page sizes
-that are not a multiple of 16) and pa_attention's ragged route, whose
+with one pool-wide buffer resource, per-row page offsets for page sizes
+that are not a multiple of 16, or one resource per run for pools past
+2 GiB, and widened at the operand reads; per-lane register staging for
+pools past 2 GiB with such page sizes) and pa_attention's ragged route, whose
 decode part and prefill part both read the codes.  The address trace of
 the instrumented build is bit-exact; outputs are held to the bf16 bar, and
 the LDS-load staging repeats bit for bit.  Marked gpu."""
@@ -252,13 +253,15 @@ def test_fp8_checked_call_flags_out_of_pool_pages(api):
             assert not ws.counters.any().item()
 
 
-def test_fp8_lds_load_staging_repeats_bit_for_bit(api):
-    """Page sizes that are a multiple of 16: the codes go straight into LDS,
-    and calls in a row (split or not) and the instrumented build give the
-    same output bits."""
+@pytest.mark.parametrize("ps", [16, 5])
+def test_fp8_lds_load_staging_repeats_bit_for_bit(api, ps):
+    """The codes go straight into LDS (16-key runs in a page, or rows that
+    resolve their own page): calls in a row (split or not) and the
+    instrumented build give the same output bits."""
     import torch
     from workloads import make_c3_fp8
-    x = make_c3_fp8()
+    x = make_c3_fp8() if ps == 16 else _fp8(93, [700, 200, 1500], H_q=28, H_kv=4, L=200,
+                                            page_size=ps, causal=True, kv_scales=(0.5, 0.5))
     d = DeviceInputs(x)
     for kw in (dict(), dict(split=False)):
         outs = [run_prefill(api, d, **kw)[0] for _ in range(3)]
