@@ -147,3 +147,84 @@ def test_ragged_shared_and_checked_calls_replay_in_a_graph(api):
             assert not w.counters.any().item()
         assert err.tolist() == [0, 0]
     del g
+
+
+def test_fp8_calls_replay_in_a_graph(api):
+    """fp8 pages: the key-split prefill (LDS-load staging, 16- and 8-key
+    pages), the ragged one call and the shared-prefix decode captured
+    together; every replay equals the eager result bit for bit."""
+    import torch
+    from tests._gpu import dev, kv_scales
+    from workloads import make_shared
+    F = dict(dtype="bf16", kv_dtype="fp8_e4m3", kv_scales=(0.45, 1.3))
+    xs16 = make_random(511, B=3, H_q=28, H_kv=4, L=200, D=128, page_size=16,
+                       ctx=[2000, 200, 900], causal=True, **F)
+    xs8 = make_random(512, B=3, H_q=28, H_kv=4, L=200, D=128, page_size=8,
+                      ctx=[1500, 300, 700], causal=True, **F)
+    pre = []
+    for x in (xs16, xs8):
+        d = DeviceInputs(x)
+        out = torch.empty_like(d.q)
+        args = api.make_args(d.q, d.kp, d.vp, d.bt, d.cl, out, scale=x.scale, mask=d.mask,
+                             **kv_scales(x))
+        pre.append((x, out, args, api.PrefillWorkspace.for_args(args, d.q.device, num_cus=512), d))
+
+    xr = make_random(513, B=5, H_q=8, H_kv=2, L=24, D=128, page_size=16,
+                     ctx=[500, 64, 210, 30, 1200], causal=True, query_lens=[1, 24, 1, 7, 2], **F)
+    lens = [int(v) for v in xr.rows_valid()]
+    rows = [xr.query[b, :, :n].transpose(1, 0, 2) for b, n in enumerate(lens)]
+    qsl = np.zeros(xr.B + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum(lens)
+    qr = dev(np.ascontiguousarray(np.concatenate(rows, axis=0)))
+    out_r = torch.empty_like(qr)
+    args_r = api.make_args(qr, dev(xr.key_pages), dev(xr.value_pages), dev(xr.block_table),
+                           dev(xr.context_lens), out_r, scale=xr.scale, mask="causal",
+                           query_start_loc=dev(qsl), max_query_len=xr.L, **kv_scales(xr))
+    ws_r = api.attention_workspace(api.pa_attention_plan(args_r), args_r, qr)
+
+    xs, gs = make_shared(514, H_q=8, H_kv=2, L=1, D=128, page_size=16, group_sizes=[4, 2, 1],
+                         prefix_pages=[6, 3, 0], suffix=(1, 120), kv_dtype="fp8_e4m3",
+                         kv_scales=(0.45, 1.3))
+    ds = DeviceInputs(xs)
+    out_s = torch.empty_like(ds.q)
+    args_s = api.make_args(ds.q, ds.kp, ds.vp, ds.bt, ds.cl, out_s, scale=xs.scale, mask=ds.mask,
+                           **kv_scales(xs))
+    groups = api.PrefixGroups(dev(gs.group_start), dev(gs.prefix_lens), gs.max_group_size)
+    ws_s = api.SharedWorkspace(api.pa_decode_shared_plan(args_s, groups), args_s, ds.q.device)
+
+    outs = [p[1] for p in pre] + [out_r, out_s]
+
+    def calls():
+        for _, _, args, ws, _ in pre:
+            api.pa_prefill(args, ws)
+        api.pa_attention(args_r, ws_r)
+        api.pa_decode_shared(args_s, groups, ws_s)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    refs = [o.clone() for o in outs]
+    for (x, out, _, _, _), ref in zip(pre, refs):
+        assert_parity(ref, oracle.attention_of(x), "bf16", f"graph fp8 prefill ps {x.page_size}")
+    assert_parity(refs[3], oracle.attention_of(xs), "bf16", "graph fp8 shared (eager)")
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        calls()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"[graph fp8] replay {rep}", flush=True)
+        for i, (o, ref) in enumerate(zip(outs, refs)):
+            assert torch.equal(_bits(o), _bits(ref)), f"fp8 output {i}, replay {rep}"
+        for ws in [p[3] for p in pre] + [ws_r, ws_s]:
+            if getattr(ws, "counters", None) is not None:
+                assert not ws.counters.any().item()
+    del g
