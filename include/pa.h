@@ -276,7 +276,7 @@ pa_status pa_prefill_plan(const pa_args *args, int32_t num_cus, pa_workspace *pl
  * bf16 matrix cores, fp32 statistics); fp32 runs on a vector-ALU kernel.
  * fp8 pages (bf16 query) run on the MFMA kernel too: the codes are loaded
  * into LDS as they are and widened exactly to bf16 by the operand reads
- * (pools of 2 GiB and more with a page size that is not a multiple of 16
+ * (pools of 2 GiB and more with a page size that is not a multiple of 8
  * widen them on their way into LDS), k_scale scales the scores and v_scale
  * the output.
  * `ws` is NULL (no split) or a workspace of pa_prefill_plan: partial_out

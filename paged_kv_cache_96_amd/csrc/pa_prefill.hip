@@ -13,12 +13,13 @@
 //
 // Per key tile:
 //   1. staging, with two LDS buffers and one barrier per tile.  When
-//      page_size is a multiple of 16, each 16-key run of a tile lies in one
-//      page: its block-table entry is a scalar load (SGPR) and the run is
-//      read with buffer loads from that page at per-lane offsets fixed for
-//      the whole walk, so staging costs no per-lane address arithmetic.
-//      With D = 128 the loads write LDS directly (kStageDma; kStageDmaRun
-//      for pools of 2 GiB and more, with one buffer resource per run): 32-key tiles, wave w loads keys 8w .. 8w + 7 of the next
+//      page_size is a multiple of 8, each wave's 8-key run of a tile lies in
+//      one page: its block-table entry is a scalar load (SGPR) and the run
+//      is read with buffer loads from that page at per-lane offsets fixed
+//      for the whole walk, so staging costs no per-lane address arithmetic.
+//      The loads write LDS directly (kStageDma; kStageDmaRun for pools of
+//      2 GiB and more, with one buffer resource per run): 32-key tiles,
+//      wave w loads keys 8w .. 8w + 7 of the next
 //      tile into the other buffer once the current tile's scores are
 //      computed; no staging registers and no LDS stores, so a workgroup
 //      needs 33 KiB of LDS and fits three waves per SIMD (the launch
@@ -27,10 +28,13 @@
 //      same loads into a tile of half the bytes (fp8_pos), and each operand
 //      read widens its 8 codes to bf16 (the transposed V read is the 8-bit
 //      one; the key rows of the score product are permuted so that a lane's
-//      PV keys are consecutive, fp8_key_perm).  Otherwise (page sizes that
-//      are not a multiple of 16, or D = 64) 64-key tiles: every thread
-//      loads the tile TWO ahead into one of two register sets and stores the
-//      set loaded one tile earlier to the other LDS buffer;
+//      PV keys are consecutive, fp8_key_perm); bf16 rows of D = 64 are 128
+//      bytes as well and take that layout.  Page sizes that are not a
+//      multiple of 8 take the same loads with each row's page resolved per
+//      lane (kStageDmaLanes).  Register staging remains for such page sizes
+//      on pools of 2 GiB and more: every thread loads the next tile into
+//      registers and stores the set loaded one tile earlier to the other
+//      LDS buffer;
 //   2. S^T = K . Q^T with v_mfma_f32_32x32x16_bf16: K from LDS is the A
 //      operand, Q (kept in registers for the whole walk) the B operand.  The
 //      result gives every lane the scores of ONE query row (lane % 32) against
@@ -470,7 +474,11 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   constexpr int kRW = 32 * RB;     // packed rows per wave
   constexpr int kBM = 4 * kRW;     // packed rows per workgroup
   using TL = Tile<D>;
-  static_assert(!DMA || (D == 128 && RB == 1), "DMA staging: D = 128, one row block per wave");
+  static_assert(!DMA || ((D == 128 || D == 64) && RB == 1),
+                "LDS-load staging: D = 128 or 64, one row block per wave");
+  // rows of 128 bytes (fp8 codes with D = 128, bf16 with D = 64): the tile
+  // layout of fp8_pos; rows of 256 bytes (bf16, D = 128): dma_pos
+  constexpr bool ROW128 = D * EB == 128;
   // Tile buffers: padded [key][dim] rows (register staging), or four
   // separate unpadded, swizzled arrays (DMA staging: separate arrays let the
   // compiler see that a load into one buffer never feeds reads of the other).
@@ -479,8 +487,10 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   constexpr int kPadBuf = DMA ? 1 : 2;
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[kPadBuf][DMA ? 8 : BN * kKS];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[kPadBuf][DMA ? 8 : BN * kVS];
-  __shared__ __attribute__((aligned(16))) uint16_t kd0[DMA ? BN * D : 8], kd1[DMA ? BN * D : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t vd0[DMA ? BN * D : 8], vd1[DMA ? BN * D : 8];
+  // (4096 shorts at least: the planner's tables live there)
+  constexpr int kDmaBuf = DMA ? (BN * D > 4096 ? BN * D : 4096) : 8;
+  __shared__ __attribute__((aligned(16))) uint16_t kd0[kDmaBuf], kd1[kDmaBuf];
+  __shared__ __attribute__((aligned(16))) uint16_t vd0[kDmaBuf], vd1[kDmaBuf];
   __shared__ int s_plan_red[DMA ? 32 : 1];
   __shared__ uint32_t s_arrived;
   __shared__ Piece s_pc;
@@ -655,16 +665,16 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   constexpr int kDmaRows = BN / 4;          // keys per wave and tile
   // load instructions per wave, K and V each: 4 rows of bf16 or 8 rows of
   // fp8 codes per 1 KiB
-  constexpr int kDmaRowsPerLoad = FP8 ? 8 : 4;
+  constexpr int kDmaRowsPerLoad = ROW128 ? 8 : 4;
   constexpr int kDmaBlocks = kDmaRows / kDmaRowsPerLoad;
-  const int dma_row = FP8 ? lane >> 3 : (lane >> 2) & 3;
+  const int dma_row = ROW128 ? lane >> 3 : (lane >> 2) & 3;
   int dma_voff[kDmaBlocks];
 #pragma unroll
   for (int j = 0; j < kDmaBlocks; ++j) {
-    if constexpr (FP8) {
+    if constexpr (ROW128) {
       // lane l fills slot l % 8 of row l / 8 of the wave's 8 rows (fp8_pos)
       const int r = kDmaRows * wave + dma_row;
-      dma_voff[j] = dma_row * D + 16 * ((lane & 7) ^ ((r >> 1) & 7));
+      dma_voff[j] = dma_row * (D * EB) + 16 * ((lane & 7) ^ ((r >> 1) & 7));
     } else {
       const int blk4 = (kDmaBlocks * wave + j) & 3;
       dma_voff[j] = (4 * j + dma_row) * (D * 2) + (4 * (lane >> 4) + ((lane & 3) ^ blk4)) * 16;
@@ -918,6 +928,19 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   // the 8-bit transposed reads (lane 2j + c of a 16-lane group points at
   // 8 codes of row j of its 8 keys, columns + 8 c) and their slot key
   int k8_row = 0, k8_key = 0, v8_off = 0, v8_key = 0;
+  // bf16 rows of 128 bytes (D = 64): K row lane % 32, chunk 2 kk + half; V
+  // rows of the two 16-bit transposed reads and their chunk slot keys
+  int k64_row = 0, k64_key = 0, v64_off = 0, v64_c = 0, v64_key1 = 0, v64_key2 = 0;
+  if constexpr (DMA && ROW128 && !FP8) {
+    k64_row = ln * 128;
+    k64_key = (ln >> 1) & 7;
+    const int src = lane & 15;
+    const int r1 = half * 4 + (src >> 2);  // the second read: row r1 + 8
+    v64_off = r1 * 128 + 8 * (src & 1);
+    v64_c = 2 * ((lane >> 4) & 1) + ((src & 3) >> 1);
+    v64_key1 = (r1 >> 1) & 7;
+    v64_key2 = ((r1 + 8) >> 1) & 7;
+  }
   if constexpr (DMA && FP8) {
     const int kr = fp8_key_perm(ln);
     k8_row = kr * 128 + 8 * half;
@@ -973,6 +996,10 @@ prefill_kernel(LaunchParams p, int num_tiles) {
             const uint8_t *kb8 = reinterpret_cast<const uint8_t *>(kc);
             const uint2 w = *reinterpret_cast<const uint2 *>(kb8 + k8_row + 16 * (kk ^ k8_key));
             a = fp8x8_to_bf16x8(w.x, w.y);
+          } else if constexpr (DMA && ROW128) {
+            const uint8_t *kb8 = reinterpret_cast<const uint8_t *>(kc);
+            a = *reinterpret_cast<const uint4 *>(kb8 + k64_row +
+                                                 16 * ((2 * kk + half) ^ k64_key));
           } else {
             const uint16_t *ka = DMA ? kc + k_dma[kk & 1] + blk * 4096 + (kk >> 1) * 128
                                      : krow + kk * 16 + half * 8;
@@ -1049,6 +1076,19 @@ prefill_kernel(LaunchParams p, int num_tiles) {
               const i32x2_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                   (lds_i32x2_t *)(vb8 + hf * 16 * 128 + v8_off + 16 * (c8 ^ v8_key)));
               aop = fp8x8_to_bf16x8((uint32_t)t[0], (uint32_t)t[1]);
+            } else if constexpr (DMA && ROW128) {
+              // keys 16 hf + 4 half + 0..3 and + 8, columns mb * 32 + 16 (lane /
+              // 16 % 2) + 4 (lane % 4) of the lane's transposed reads
+              const uint8_t *vb8 = reinterpret_cast<const uint8_t *>(vc);
+              const int c = 4 * mb + v64_c;
+              const s16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_s16x4_t *)(vb8 + hf * 2048 + v64_off + 16 * (c ^ v64_key1)));
+              const s16x4_t t2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_s16x4_t *)(vb8 + hf * 2048 + v64_off + 1024 + 16 * (c ^ v64_key2)));
+              aop = make_uint4((uint32_t)(uint16_t)t1[0] | ((uint32_t)(uint16_t)t1[1] << 16),
+                               (uint32_t)(uint16_t)t1[2] | ((uint32_t)(uint16_t)t1[3] << 16),
+                               (uint32_t)(uint16_t)t2[0] | ((uint32_t)(uint16_t)t2[1] << 16),
+                               (uint32_t)(uint16_t)t2[2] | ((uint32_t)(uint16_t)t2[3] << 16));
             } else {
               const int vo = blk * 4096 + hf * 2048 + mb * 128;  // kStageDma
               const uint16_t *r1 = DMA ? vc + v_dma[0] + vo : vc + vr * kVS + d0;
@@ -1259,34 +1299,37 @@ hipError_t launch_rb(const LaunchParams &p, hipStream_t stream) {
   auto go = [&](auto dbg, auto fp8) {
     constexpr bool DBG = decltype(dbg)::value;
     constexpr bool F8 = decltype(fp8)::value;
-    // direct-to-LDS staging with D = 128 (fp8 codes are widened at the
-    // operand reads)
-    constexpr bool kDma = D == 128 && RB == 1;
+    // LDS-load staging (one row block per wave): 8-key runs inside a page
+    // with the page in a scalar offset (or, pools of 2 GiB and more, one
+    // resource per run); other page sizes resolve each row's page, and on
+    // pools of 2 GiB and more stage through registers
+    constexpr bool kDma = (D == 128 || D == 64) && RB == 1;
     const long long pool = (long long)p.num_pages * p.Hkv * p.ps * D * (F8 ? 1 : 2);
-    if (p.ps % Tile<D>::kKeysPerRound != 0) {  // runs would straddle pages
-      if constexpr (kDma) {
-        if (pool < (1ll << 31)) {
-          hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageDmaLanes, RB, F8>), grid, dim3(256), 0,
+    const bool runs = p.ps % 8 == 0;
+    if constexpr (kDma) {
+      if (pool < (1ll << 31)) {
+        if (runs)
+          hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageDma, RB, F8>), grid, dim3(256), 0,
                              stream, p, tiles);
-          return;
-        }
+        else
+          hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageDmaLanes, RB, F8>), grid, dim3(256),
+                             0, stream, p, tiles);
+      } else if (runs) {
+        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageDmaRun, RB, F8>), grid, dim3(256), 0,
+                           stream, p, tiles);
+      } else {
+        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageLanes, RB, F8>), grid, dim3(256), 0,
+                           stream, p, tiles);
       }
+    } else if (p.ps % Tile<D>::kKeysPerRound != 0) {  // register runs would straddle pages
       hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageLanes, RB, F8>), grid, dim3(256), 0,
                          stream, p, tiles);
     } else if (pool < (1ll << 31)) {
-      if constexpr (kDma)
-        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageDma, RB, F8>), grid, dim3(256), 0,
-                           stream, p, tiles);
-      else
-        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStagePool, RB, F8>), grid, dim3(256), 0,
-                           stream, p, tiles);
+      hipLaunchKernelGGL((prefill_kernel<D, DBG, kStagePool, RB, F8>), grid, dim3(256), 0,
+                         stream, p, tiles);
     } else {
-      if constexpr (kDma)
-        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageDmaRun, RB, F8>), grid, dim3(256), 0,
-                           stream, p, tiles);
-      else
-        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageRun, RB, F8>), grid, dim3(256), 0,
-                           stream, p, tiles);
+      hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageRun, RB, F8>), grid, dim3(256), 0, stream,
+                         p, tiles);
     }
   };
   using yes = std::integral_constant<bool, true>;
