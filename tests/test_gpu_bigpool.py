@@ -26,15 +26,20 @@ def api():
 
 def _big(x, extra=512):
     """Device pools of more than 2 GiB each holding x's pages at the top, and
-    the block table relabelled to match."""
+    the block table relabelled to match (fp8 pools: NaN codes elsewhere)."""
     import torch
-    page_bytes = x.H_kv * x.page_size * x.D * 2
+    fp8 = getattr(x, "kv_dtype", None) == "fp8_e4m3"
+    page_bytes = x.H_kv * x.page_size * x.D * (1 if fp8 else 2)
     n_big = (1 << 31) // page_bytes + extra
     assert n_big * page_bytes > (1 << 31)
     ids = np.arange(n_big - x.num_pages, n_big)          # compact page i -> ids[i]
-    garbage = torch.tensor([9984.0], dtype=torch.bfloat16).item()
-    kp = torch.full((n_big, x.H_kv, x.page_size, x.D), garbage, dtype=torch.bfloat16, device="cuda")
-    vp = torch.full_like(kp, garbage)
+    if fp8:
+        kp = torch.full((n_big, x.H_kv, x.page_size, x.D), 0x7F, dtype=torch.uint8, device="cuda")
+    else:
+        garbage = torch.tensor([9984.0], dtype=torch.bfloat16).item()
+        kp = torch.full((n_big, x.H_kv, x.page_size, x.D), garbage, dtype=torch.bfloat16,
+                        device="cuda")
+    vp = torch.full_like(kp, kp.flatten()[0].item())
     idx = torch.from_numpy(ids).to("cuda")
     kp[idx] = dev(x.key_pages)
     vp[idx] = dev(x.value_pages)
@@ -53,6 +58,29 @@ def test_prefill_pool_past_2gib(api, split):
     d, _ = _big(x)
     out, _ = run_prefill(api, d, split=split)
     assert_parity(out, oracle.attention_of(x), "bf16", "prefill, pool past 2 GiB")
+
+
+@pytest.mark.parametrize("shape", [
+    dict(seed=64, D=128, page_size=5, kv=None),     # per-lane register staging
+    dict(seed=65, D=128, page_size=5, kv="fp8_e4m3"),
+    dict(seed=66, D=64, page_size=16, kv=None),     # one buffer resource per 8-key run
+])
+def test_prefill_pool_past_2gib_other_shapes(api, shape):
+    """Pools past 2 GiB with a page size that is not a multiple of 8 (the
+    only calls that still stage through registers, bf16 and fp8) and with
+    D = 64 (per-run resources): against the oracle, split and unsplit."""
+    kv = shape["kv"]
+    x = make_random(shape["seed"], B=3, H_q=8, H_kv=2, L=40, D=shape["D"],
+                    page_size=shape["page_size"], ctx=[40, 170, 333], dtype="bf16", causal=True,
+                    name="bigpool_prefill_other", kv_dtype=kv, kv_scales=(0.45, 1.3))
+    d, _ = _big(x)
+    ref = oracle.attention_of(x)
+    for split in (False, True):
+        out, _ = run_prefill(api, d, split=split)
+        assert_parity(out, ref, "bf16", f"prefill past 2 GiB {shape} split={split}")
+    del d
+    import torch
+    torch.cuda.empty_cache()
 
 
 def test_decode_pool_past_2gib(api):
