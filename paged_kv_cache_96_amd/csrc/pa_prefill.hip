@@ -392,28 +392,22 @@ __device__ void find_piece(const LaunchParams &p, int nt, int *s_ctx, int *s_ql,
 }
 
 // Staging modes (each also has an instrumented build that records the
-// page and slot of every key from the address its load uses).  kStageLanes:
-// every lane resolves its own key (any page size).  kStageRun: page_size a multiple of the run length, one
-// buffer resource per run.  kStagePool: the same runs, with one resource for
-// the whole K (V) pool and the run's position in the SGPR offset (pools
-// under 2 GiB, so that offsets stay below 2^31 and an offset of 2^31 is
-// always out of range).
-// kStageDma: the runs of kStagePool with the K/V rows written straight into
-// LDS by the loads (no staging registers, no LDS stores): D = 128 only.
+// page and slot of every key from the address its load uses).
+// kStageDma: each wave's 8-key run of a tile lies in one page (page_size a
+// multiple of 8); the K/V rows are written straight into LDS by the loads
+// (no staging registers, no LDS stores), with one resource for the whole K
+// (V) pool and the run's position in the SGPR offset (pools under 2 GiB, so
+// that offsets stay below 2^31 and an offset of 2^31 is always out of
+// range).
 // kStageDmaRun: the same with one buffer resource per run (pools of 2 GiB
-// and more, as kStageRun).
+// and more).
 // kStageDmaLanes: the LDS loads of kStageDma for page sizes that are not a
-// multiple of 16 (pools under 2 GiB): a wave's 8-key run may straddle pages,
+// multiple of 8 (pools under 2 GiB): a wave's 8-key run may straddle pages,
 // so each lane resolves its own row's page from the run's block-table
 // entries and puts the whole pool offset in its own vector offset.
-enum StageMode {
-  kStageLanes = 0,
-  kStageRun = 1,
-  kStagePool = 2,
-  kStageDma = 3,
-  kStageDmaRun = 4,
-  kStageDmaLanes = 5
-};
+// kStageLanes: register staging, every lane resolving its own key (page
+// sizes that are not a multiple of 8 on pools of 2 GiB and more).
+enum StageMode { kStageLanes = 0, kStageDma = 3, kStageDmaRun = 4, kStageDmaLanes = 5 };
 
 // LDS tile layout of kStageDma (64 rows x 16 chunks of 16 bytes, D = 128).
 // Rows come in blocks of 4 (b = (r / 4) % 4 within a 16-row group); a block
@@ -459,7 +453,6 @@ __global__ __launch_bounds__(256, (MODE == kStageDma || MODE == kStageDmaRun ||
                                                                            : 1) void
 prefill_kernel(LaunchParams p, int num_tiles) {
   if (contract_broken(p)) return;
-  constexpr bool UNIFORM = MODE != kStageLanes;
   constexpr bool DMA = MODE == kStageDma || MODE == kStageDmaRun || MODE == kStageDmaLanes;
   // fp8 (E4M3) pages, D = 128: with LDS loads the codes land in LDS as they
   // are and each operand read widens them to bf16; register staging widens
@@ -614,20 +607,10 @@ prefill_kernel(LaunchParams p, int num_tiles) {
   // constant address space lets wave-uniform entries come in by scalar loads.
   typedef const __attribute__((address_space(4))) int32_t *const_i32_ptr;
   const const_i32_ptr btc = (const_i32_ptr)bt;
-  // page-uniform rounds: per-thread byte offset within a 16-key run of a page
-  const int run_off = (key_in_round * D + chunk * 8) * EB;
-  // Every load is issued unconditionally: a run past the workgroup's last
-  // key gets a resource of size 0 (its loads return zeros without touching
-  // memory), so no register is ever written conditionally and the compiler's
-  // wait counts only ever wait for the set that is about to be stored.
-  // Runs are loaded strictly in key order, so the run's logical page and
-  // slot are advanced incrementally (scalar registers): a new block-table
-  // entry is read only when a run starts a page.
   const long long page_bytes = (long long)p.Hkv * p.ps * D * EB;
   const long long head_bytes = (long long)g * p.ps * D * EB;
   const char *kp_bytes = reinterpret_cast<const char *>(p.kp);
   const char *vp_bytes = reinterpret_cast<const char *>(p.vp);
-  int run_j0 = 0, run_lp = 0, run_slot = 0, run_page = 0;
   int pass = 0;  // 1: the walk again with exact row maxima
   // Debug record of logical key j, decoded from the byte offset into the
   // pool that this thread's load of the key's first 16-byte chunk actually
@@ -651,7 +634,7 @@ prefill_kernel(LaunchParams p, int num_tiles) {
       }
     }
   };
-  const int pool_bytes = (int)((long long)p.num_pages * page_bytes);  // kStagePool only
+  const int pool_bytes = (int)((long long)p.num_pages * page_bytes);  // pools under 2 GiB
   const __amdgpu_buffer_rsrc_t pool_k = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char *>(kp_bytes), (short)0, pool_bytes, kBufferRsrcWord3);
   const __amdgpu_buffer_rsrc_t pool_v = __builtin_amdgcn_make_buffer_rsrc(
@@ -764,68 +747,7 @@ prefill_kernel(LaunchParams p, int num_tiles) {
       ++dma_lp;
     }
   };
-  auto stage_load_uniform = [&](int kt, Stage &st) {
-    (void)kt;  // runs follow run_j0, which tracks kt * BN
-#pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
-      const bool live = run_j0 < kend_wg;                 // wave-uniform
-      if (run_slot == 0) run_page = live ? btc[min(run_lp, p.max_pages - 1)] : 0;
-      if constexpr (MODE == kStagePool) {
-        const int soff = run_page * (int)page_bytes + (int)head_bytes + run_slot * (D * EB);
-        const int voff = run_j0 + key_in_round < kend_wg ? run_off : (int)0x80000000u;
-        if constexpr (FP8) {
-          const u32x2_t kv = __builtin_amdgcn_raw_buffer_load_b64(pool_k, voff, soff, 0);
-          const u32x2_t vv = __builtin_amdgcn_raw_buffer_load_b64(pool_v, voff, soff, 0);
-          st.k[r] = make_uint2(kv[0], kv[1]);
-          st.v[r] = make_uint2(vv[0], vv[1]);
-        } else {
-          const u32x4_t kv = __builtin_amdgcn_raw_buffer_load_b128(pool_k, voff, soff, 0);
-          const u32x4_t vv = __builtin_amdgcn_raw_buffer_load_b128(pool_v, voff, soff, 0);
-          st.k[r] = make_uint4(kv[0], kv[1], kv[2], kv[3]);
-          st.v[r] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
-        }
-        if (live && voff >= 0) record(run_j0 + key_in_round, (long long)soff + voff);
-        run_j0 += TL::kKeysPerRound;
-        run_slot += TL::kKeysPerRound;
-        if (run_slot == p.ps) {
-          run_slot = 0;
-          ++run_lp;
-        }
-        continue;
-      }
-      const long long off = (long long)run_page * page_bytes + head_bytes + run_slot * (D * EB);
-      const int nrec = live ? (p.ps - run_slot) * D * EB : 0;
-      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<char *>(kp_bytes + off), (short)0, nrec, kBufferRsrcWord3);
-      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<char *>(vp_bytes + off), (short)0, nrec, kBufferRsrcWord3);
-      // keys at or past kend_wg read as zeros (offset past the resource)
-      const int voff = run_j0 + key_in_round < kend_wg ? run_off : 0x40000000;
-      if constexpr (FP8) {
-        const u32x2_t kv = __builtin_amdgcn_raw_buffer_load_b64(rk, voff, 0, 0);
-        const u32x2_t vv = __builtin_amdgcn_raw_buffer_load_b64(rv, voff, 0, 0);
-        st.k[r] = make_uint2(kv[0], kv[1]);
-        st.v[r] = make_uint2(vv[0], vv[1]);
-      } else {
-        const u32x4_t kv = __builtin_amdgcn_raw_buffer_load_b128(rk, voff, 0, 0);
-        const u32x4_t vv = __builtin_amdgcn_raw_buffer_load_b128(rv, voff, 0, 0);
-        st.k[r] = make_uint4(kv[0], kv[1], kv[2], kv[3]);
-        st.v[r] = make_uint4(vv[0], vv[1], vv[2], vv[3]);
-      }
-      if (live && voff != 0x40000000) record(run_j0 + key_in_round, off + voff);
-      run_j0 += TL::kKeysPerRound;
-      run_slot += TL::kKeysPerRound;
-      if (run_slot == p.ps) {
-        run_slot = 0;
-        ++run_lp;
-      }
-    }
-  };
   auto stage_load = [&](int kt, Stage &st) {
-    if constexpr (UNIFORM) {
-      stage_load_uniform(kt, st);
-      return;
-    }
 #pragma unroll
     for (int r = 0; r < kRounds; ++r) {
       const int j = kt * BN + r * TL::kKeysPerRound + key_in_round;
@@ -893,9 +815,6 @@ prefill_kernel(LaunchParams p, int num_tiles) {
       for (int i = 0; i < 16; ++i) o[rb][mb][i] = 0.f;
     l_run[rb] = 0.f;
   }
-  run_j0 = k0;
-  run_lp = k0 / p.ps;
-  run_slot = k0 - run_lp * p.ps;
   if constexpr (DMA) {
     // tile kt0 goes to buffer 0; the first step waits for it (no load is
     // issued that the walk does not wait for: LDS must not be written after
@@ -904,14 +823,11 @@ prefill_kernel(LaunchParams p, int num_tiles) {
     dma_slot = (k0 + kDmaRows * wave) - dma_lp * p.ps;
     if (ntiles > 0) dma_tile(kt0, kbuf0, vbuf0);
   } else {
-    // a piece may start inside a page: its first entry is read here (later
-    // ones when a run starts a page)
-    if constexpr (UNIFORM) run_page = run_j0 < kend_wg ? btc[min(run_lp, p.max_pages - 1)] : 0;
     if (ntiles > 0) {
       stage_load(kt0, sa);
       stage_store(kbuf0, vbuf0, sa);
     }
-    if (kTwoSets && (UNIFORM || ntiles > 1)) stage_load(kt0 + 1, sb);
+    if (kTwoSets && ntiles > 1) stage_load(kt0 + 1, sb);
     // the query and tile-0 loads are complete here; tile 1 stays in flight
     __builtin_amdgcn_s_waitcnt(kWaitVmcntOlderThan8);
     __syncthreads();
@@ -970,9 +886,9 @@ prefill_kernel(LaunchParams p, int num_tiles) {
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
       __syncthreads();
     } else if constexpr (kTwoSets) {
-      if (UNIFORM || kt + 2 < kt_end) stage_load(kt + 2, ld);
+      if (kt + 2 < kt_end) stage_load(kt + 2, ld);
     } else {
-      if (UNIFORM || more) stage_load(kt + 1, ld);
+      if (more) stage_load(kt + 1, ld);
     }
 
     if (kt * BN < kend_w) {
@@ -1303,33 +1219,22 @@ hipError_t launch_rb(const LaunchParams &p, hipStream_t stream) {
     // with the page in a scalar offset (or, pools of 2 GiB and more, one
     // resource per run); other page sizes resolve each row's page, and on
     // pools of 2 GiB and more stage through registers
-    constexpr bool kDma = (D == 128 || D == 64) && RB == 1;
+    static_assert((D == 128 || D == 64) && RB == 1, "LDS-load staging");
     const long long pool = (long long)p.num_pages * p.Hkv * p.ps * D * (F8 ? 1 : 2);
     const bool runs = p.ps % 8 == 0;
-    if constexpr (kDma) {
-      if (pool < (1ll << 31)) {
-        if (runs)
-          hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageDma, RB, F8>), grid, dim3(256), 0,
-                             stream, p, tiles);
-        else
-          hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageDmaLanes, RB, F8>), grid, dim3(256),
-                             0, stream, p, tiles);
-      } else if (runs) {
-        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageDmaRun, RB, F8>), grid, dim3(256), 0,
+    if (pool < (1ll << 31)) {
+      if (runs)
+        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageDma, RB, F8>), grid, dim3(256), 0,
                            stream, p, tiles);
-      } else {
-        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageLanes, RB, F8>), grid, dim3(256), 0,
+      else
+        hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageDmaLanes, RB, F8>), grid, dim3(256), 0,
                            stream, p, tiles);
-      }
-    } else if (p.ps % Tile<D>::kKeysPerRound != 0) {  // register runs would straddle pages
-      hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageLanes, RB, F8>), grid, dim3(256), 0,
-                         stream, p, tiles);
-    } else if (pool < (1ll << 31)) {
-      hipLaunchKernelGGL((prefill_kernel<D, DBG, kStagePool, RB, F8>), grid, dim3(256), 0,
+    } else if (runs) {
+      hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageDmaRun, RB, F8>), grid, dim3(256), 0,
                          stream, p, tiles);
     } else {
-      hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageRun, RB, F8>), grid, dim3(256), 0, stream,
-                         p, tiles);
+      hipLaunchKernelGGL((prefill_kernel<D, DBG, kStageLanes, RB, F8>), grid, dim3(256), 0,
+                         stream, p, tiles);
     }
   };
   using yes = std::integral_constant<bool, true>;
